@@ -1,0 +1,369 @@
+"""Pins for the CPU oracle: each function returns an error magnitude that is ~0 for a correct
+oracle and large when a plausible mistake is planted in it (a dropped term, a wrong sign or
+index, a transposed operand). test_oracle.py asserts the errors are small; test_oracle_mutants.py
+plants mistakes in the oracle (on the CPU) and asserts that some pin catches each of them.
+
+The independent sides are library routines (torch's scaled_dot_product_attention, softmax and
+logsumexp in float64 on the CPU), closed forms, invariants, and hand-derived fixtures under
+tests/golden/.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _t(x):
+    return torch.from_numpy(np.ascontiguousarray(x))
+
+
+def rand_qkv(n=512, d=16, seed=0, nv=None, runs=1):
+    """Random q, k, v [n, d] fp64; with runs > 1, k and v are constant within runs."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((n, d))
+    k = rng.standard_normal((n // runs, d)).repeat(runs, axis=0)
+    v = rng.standard_normal((n // runs, d)).repeat(runs, axis=0)
+    if nv is not None:
+        q[nv:] = 0
+        k[nv:] = 0
+        v[nv:] = 0
+    return q, k, v
+
+
+def sdpa(q, k, v, mask_bool, scale):
+    """torch SDPA (fp64, CPU) on [n, d] rows with a [n_q, n_k] boolean keep-mask."""
+    o = torch.nn.functional.scaled_dot_product_attention(
+        _t(q)[None, None], _t(k)[None, None], _t(v)[None, None],
+        attn_mask=_t(mask_bool)[None, None], scale=scale)
+    return o[0, 0].numpy()
+
+
+def torch_lse(q, k, mask_bool, scale, bias=None):
+    z = scale * (_t(q) @ _t(k).T)
+    if bias is not None:
+        z = z + _t(bias)
+    z = z.masked_fill(~_t(mask_bool), float("-inf"))
+    return torch.logsumexp(z, dim=-1).numpy()
+
+
+# ---------------------------------------------------------------------------------------
+# P1: an all-level-0 map is dense softmax attention (also with padding and causal).
+# ---------------------------------------------------------------------------------------
+def pin_all_l0_dense(causal=False, nv=512):
+    n, d = 512, 16
+    p = oracle.Problem(seq_len=n, seq_valid=nv, head_dim=d, block_q=64, block_k=64,
+                       causal=causal)
+    q, k, v = rand_qkv(n, d, seed=1, nv=nv)
+    lm = np.zeros((p.n_qblocks, p.n_kblocks), dtype=np.int8)
+    o, lse = oracle.attention_head(q, k, v, lm, p)
+    i = np.arange(n)
+    keep = (i[None, :] < nv) & np.ones((n, 1), dtype=bool)
+    if causal:
+        keep = keep & (i[None, :] <= i[:, None])
+    s = 1.0 / math.sqrt(d)
+    ref = sdpa(q, k, v, keep, s)
+    ref_lse = torch_lse(q, k, keep, s)
+    rows = slice(0, nv)
+    err = max(np.abs(o[rows] - ref[rows]).max(), np.abs(lse[rows] - ref_lse[rows]).max())
+    pad_ok = np.all(o[nv:] == 0) and np.all(np.isneginf(lse[nv:]))
+    return err if pad_ok else np.inf
+
+
+# ---------------------------------------------------------------------------------------
+# P2: a map with only {L0, skip} is block-sparse attention with a binary block mask.
+# ---------------------------------------------------------------------------------------
+def pin_binary_block_sparse():
+    n, d, bq, bk = 512, 16, 128, 64
+    p = oracle.Problem(seq_len=n, seq_valid=n, head_dim=d, block_q=bq, block_k=bk)
+    q, k, v = rand_qkv(n, d, seed=2)
+    rng = np.random.default_rng(3)
+    lm = np.where(rng.random((p.n_qblocks, p.n_kblocks)) < 0.5, 0, -1).astype(np.int8)
+    lm[:, 0] = 0
+    keep = np.repeat(np.repeat(lm == 0, bq, axis=0), bk, axis=1)
+    o, lse = oracle.attention_head(q, k, v, lm, p)
+    s = 1.0 / math.sqrt(d)
+    ref = sdpa(q, k, v, keep, s)
+    return max(np.abs(o - ref).max(), np.abs(lse - torch_lse(q, k, keep, s)).max())
+
+
+# ---------------------------------------------------------------------------------------
+# P3: nearest-neighbour upsampling of each pooled block back to full length, then standard
+# attention, equals the level-weighted formulation (pins the 2**l weight).
+# ---------------------------------------------------------------------------------------
+def _upsampled_row(k, v, row_levels, bk):
+    ks, vs, keep = [], [], []
+    for kb, l in enumerate(row_levels):
+        blk = slice(kb * bk, (kb + 1) * bk)
+        if l < 0:
+            ks.append(k[blk])
+            vs.append(v[blk])
+            keep.append(np.zeros(bk, dtype=bool))
+            continue
+        f = 1 << int(l)
+        kp = k[blk].reshape(bk // f, f, -1).mean(axis=1)
+        vp = v[blk].reshape(bk // f, f, -1).mean(axis=1)
+        ks.append(np.repeat(kp, f, axis=0))
+        vs.append(np.repeat(vp, f, axis=0))
+        keep.append(np.ones(bk, dtype=bool))
+    return np.concatenate(ks), np.concatenate(vs), np.concatenate(keep)
+
+
+def pin_upsample_equivalence(seed=4):
+    n, d, bq, bk = 512, 16, 64, 64
+    p = oracle.Problem(seq_len=n, seq_valid=n, head_dim=d, block_q=bq, block_k=bk)
+    q, k, v = rand_qkv(n, d, seed=seed)
+    rng = np.random.default_rng(seed + 1)
+    lm = rng.choice(np.array([0, 1, 2, 3, -1], dtype=np.int8), size=(p.n_qblocks, p.n_kblocks))
+    lm[:, 0] = 3
+    o, lse = oracle.attention_head(q, k, v, lm, p)
+    err = 0.0
+    for qb in range(p.n_qblocks):
+        qi = slice(qb * bq, (qb + 1) * bq)
+        ku, vu, keep = _upsampled_row(k, v, lm[qb], bk)
+        km = np.broadcast_to(keep, (bq, n))
+        ref = sdpa(q[qi], ku, vu, km, 1.0 / math.sqrt(d))
+        ref_lse = torch_lse(q[qi], ku, km, 1.0 / math.sqrt(d))
+        err = max(err, np.abs(o[qi] - ref).max(), np.abs(lse[qi] - ref_lse).max())
+    return err
+
+
+# ---------------------------------------------------------------------------------------
+# P4: K, V constant within runs of 2**l: level l gives the same output as level 0.
+# ---------------------------------------------------------------------------------------
+def pin_constant_runs(level=3):
+    n, d = 512, 16
+    p = oracle.Problem(seq_len=n, seq_valid=n, head_dim=d, block_q=64, block_k=64)
+    q, k, v = rand_qkv(n, d, seed=5, runs=1 << level)
+    rng = np.random.default_rng(6)
+    base = np.where(rng.random((p.n_qblocks, p.n_kblocks)) < 0.3, -1, 0).astype(np.int8)
+    base[:, 1] = 0
+    pooled = base.copy()
+    sel = (base == 0) & (rng.random(base.shape) < 0.6)
+    pooled[sel] = level
+    o0, l0 = oracle.attention_head(q, k, v, base, p)
+    o1, l1 = oracle.attention_head(q, k, v, pooled, p)
+    return max(np.abs(o0 - o1).max(), np.abs(l0 - l1).max())
+
+
+# ---------------------------------------------------------------------------------------
+# P5: an all-skip row gives o = 0 and lse = -inf; other rows are unaffected.
+# ---------------------------------------------------------------------------------------
+def pin_all_skip_row():
+    n, d = 256, 8
+    p = oracle.Problem(seq_len=n, seq_valid=n, head_dim=d, block_q=64, block_k=64)
+    q, k, v = rand_qkv(n, d, seed=7)
+    lm = np.zeros((4, 4), dtype=np.int8)
+    lm[2] = -1
+    o, lse = oracle.attention_head(q, k, v, lm, p)
+    ok = np.all(o[128:192] == 0) and np.all(np.isneginf(lse[128:192]))
+    full, fl = oracle.attention_head(q, k, v, np.zeros((4, 4), dtype=np.int8), p)
+    other = np.r_[0:128, 192:256]
+    return np.abs(o[other] - full[other]).max() if ok else np.inf
+
+
+# ---------------------------------------------------------------------------------------
+# P6: per-row weights sum to 1 including the 2**l multiplicity: the weight of a pooled
+# token equals the summed weights of its 2**l upsampled copies under standard softmax.
+# ---------------------------------------------------------------------------------------
+def pin_weight_multiplicity():
+    n, d, bk = 256, 8, 64
+    p = oracle.Problem(seq_len=n, seq_valid=n, head_dim=d, block_q=64, block_k=bk)
+    q, k, v = rand_qkv(n, d, seed=8)
+    row_levels = np.array([0, 1, 2, 3], dtype=np.int8)
+    lk, lv = oracle.pyramid(k), oracle.pyramid(v)
+    Kb, Vb, lvl, last = oracle.psa_oracle.gather_row_keys(lk, lv, row_levels, p)
+    qi = np.arange(64)
+    w = oracle.psa_oracle.attention_weights_row(q[qi], qi, Kb, lvl, last, p, p.scale)
+    ku, _, _ = _upsampled_row(k, v, row_levels, bk)
+    wu = torch.softmax((_t(q[qi]) @ _t(ku).T) / math.sqrt(d), dim=-1).numpy()
+    # fold the upsampled weights back onto pooled tokens
+    folded = []
+    for kb, l in enumerate(row_levels):
+        f = 1 << int(l)
+        blk = wu[:, kb * bk:(kb + 1) * bk]
+        folded.append(blk.reshape(64, bk // f, f).sum(axis=-1))
+    folded = np.concatenate(folded, axis=1)
+    return max(np.abs(w - folded).max(), np.abs(w.sum(axis=1) - 1).max())
+
+
+# ---------------------------------------------------------------------------------------
+# P7: pyramid. 2**l * sum(level l) == sum(level 0) per block; mean of a constant is that
+# constant; progressive pooling equals direct pooling; brute-force mean on a tiny input;
+# packed layout offsets.
+# ---------------------------------------------------------------------------------------
+def pin_pyramid():
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((256, 8))
+    err = 0.0
+    for l in (1, 2, 3):
+        pl = oracle.pool(x, l)
+        f = 1 << l
+        err = max(err, np.abs(f * pl.reshape(4, 64 // f, 8).sum(1)
+                              - x.reshape(4, 64, 8).sum(1)).max())
+    err = max(err, np.abs(oracle.pool(oracle.pool(x, 1), 1) - oracle.pool(x, 2)).max())
+    err = max(err, np.abs(oracle.pool(oracle.pool(oracle.pool(x, 1), 1), 1)
+                          - oracle.pool(x, 3)).max())
+    c = np.full((64, 3), 1.25)
+    for l in (1, 2, 3):
+        err = max(err, np.abs(oracle.pool(c, l) - 1.25).max())
+    tiny = rng.standard_normal((16, 2))
+    p3 = oracle.pool(tiny, 3)
+    for j in range(2):
+        for e in range(2):
+            s = 0.0
+            for t in range(8):
+                s += tiny[8 * j + t, e]
+            err = max(err, abs(p3[j, e] - s / 8))
+    packed = oracle.pack_pyramid(x)
+    n = x.shape[0]
+    for l in (1, 2, 3):
+        off = oracle.packed_level_offset(n, l)
+        err = max(err, np.abs(packed[off:off + (n >> l)] - oracle.pool(x, l)).max())
+    if packed.shape[0] != 7 * n // 8:
+        return np.inf
+    return err
+
+
+# ---------------------------------------------------------------------------------------
+# P8: scoring reductions. Sampling every row (S = BQ) gives the dense softmax block mass
+# averaged over the rows; antidiagonal scoring with stride 1 gives the same; stride-S
+# antidiagonal orientation and the sum (not mean) of the S products; similarity special
+# cases and a pure-Python pairwise brute force.
+# ---------------------------------------------------------------------------------------
+def _dense_block_mass(q, k, p, rows_per_block=None):
+    z = (_t(q) @ _t(k).T) / math.sqrt(q.shape[1])
+    n = q.shape[0]
+    i = torch.arange(n)
+    keep = (i[None, :] < p.seq_valid).expand(n, n)
+    if p.causal:
+        keep = keep & (i[None, :] <= i[:, None])
+    pr = torch.softmax(z.masked_fill(~keep, float("-inf")), dim=-1).numpy()
+    mass = pr.reshape(n, p.n_kblocks, p.block_k).sum(-1)
+    return mass.reshape(p.n_qblocks, p.block_q, p.n_kblocks).mean(axis=1)
+
+
+def pin_sampling_all_rows(causal=False):
+    n, d = 512, 16
+    p = oracle.Problem(seq_len=n, seq_valid=n, head_dim=d, block_q=64, block_k=64,
+                       causal=causal)
+    q, k, _ = rand_qkv(n, d, seed=10)
+    M = oracle.mask_scores_sampling(q, k, p, samples=64)
+    ref = _dense_block_mass(q, k, p)
+    return max(np.abs(M - ref).max(), np.abs(M.sum(1) - 1).max())
+
+
+def pin_antidiag_stride1(causal=False):
+    n, d = 512, 16
+    p = oracle.Problem(seq_len=n, seq_valid=n, head_dim=d, block_q=64, block_k=64,
+                       causal=causal)
+    q, k, _ = rand_qkv(n, d, seed=11)
+    M = oracle.mask_scores_antidiag(q, k, p, stride=1)
+    return np.abs(M - _dense_block_mass(q, k, p)).max()
+
+
+def pin_antidiag_orientation_and_sum():
+    """Stride 4. (a) Only q[4r+3] and k[4c] non-zero: the antidiagonal pairs exactly these
+    (t = 0 term), the main diagonal would pair nothing. (b) q and k constant inside each
+    4-row group: the compressed logit is 4x the token logit (a sum, not a mean)."""
+    n, d, S = 256, 8, 4
+    p = oracle.Problem(seq_len=n, seq_valid=n, head_dim=d, block_q=64, block_k=64)
+    rng = np.random.default_rng(12)
+    R = n // S
+    qa, ka = np.zeros((n, d)), np.zeros((n, d))
+    qa[S - 1::S] = rng.standard_normal((R, d))
+    ka[0::S] = rng.standard_normal((R, d))
+    Ma = oracle.mask_scores_antidiag(qa, ka, p, stride=S)
+    za = (_t(qa[S - 1::S]) @ _t(ka[0::S]).T) / math.sqrt(d)
+    pa = torch.softmax(za, -1).numpy()
+    ref_a = pa.reshape(R, p.n_kblocks, 64 // S).sum(-1).reshape(p.n_qblocks, 64 // S, -1).mean(1)
+    qg = rng.standard_normal((R, d)).repeat(S, axis=0)
+    kg = rng.standard_normal((R, d)).repeat(S, axis=0)
+    Mb = oracle.mask_scores_antidiag(qg, kg, p, stride=S)
+    zb = S * (_t(qg[::S]) @ _t(kg[::S]).T) / math.sqrt(d)
+    pb = torch.softmax(zb, -1).numpy()
+    ref_b = pb.reshape(R, p.n_kblocks, 64 // S).sum(-1).reshape(p.n_qblocks, 64 // S, -1).mean(1)
+    return max(np.abs(Ma - ref_a).max(), np.abs(Mb - ref_b).max())
+
+
+def pin_cossim():
+    d = 80
+    p = oracle.Problem(seq_len=64, seq_valid=64, head_dim=d, block_q=64, block_k=64)
+    rng = np.random.default_rng(13)
+    err = 0.0
+    same = np.tile(rng.standard_normal((1, d)), (64, 1)) * rng.uniform(0.5, 2, (64, 1))
+    err = max(err, abs(oracle.block_cossim(same, p)[0] - 1.0))
+    eye = np.eye(d)[:64] * 3.0
+    err = max(err, abs(oracle.block_cossim(eye, p)[0] - 0.0))
+    x = rng.standard_normal((1, d))
+    anti = np.concatenate([np.tile(x, (32, 1)), np.tile(-x, (32, 1))])
+    err = max(err, abs(oracle.block_cossim(anti, p)[0] - (-1.0 / 63.0)))
+    # pure-Python brute force over ordered pairs on a small block (BK = 8), one zero key
+    p8 = oracle.Problem(seq_len=16, seq_valid=16, head_dim=3, block_q=8, block_k=8)
+    y = rng.standard_normal((16, 3))
+    y[5] = 0.0
+    got = oracle.block_cossim(y, p8)
+    for kb in range(2):
+        tot = 0.0
+        for i in range(8):
+            for j in range(8):
+                if i == j:
+                    continue
+                a, b = y[kb * 8 + i], y[kb * 8 + j]
+                na = math.sqrt(sum(t * t for t in a))
+                nb = math.sqrt(sum(t * t for t in b))
+                if na > 0 and nb > 0:
+                    tot += sum(s * t for s, t in zip(a, b)) / (na * nb)
+        err = max(err, abs(got[kb] - tot / 56.0))
+    return err
+
+
+def pin_sample_offsets():
+    ok = (oracle.sample_offsets(128, 8) == [0, 16, 32, 48, 64, 80, 96, 112]
+          and oracle.sample_offsets(112, 8) == [0, 14, 28, 42, 56, 70, 84, 98]
+          and oracle.sample_offsets(0, 8) == [])
+    return 0.0 if ok else np.inf
+
+
+# ---------------------------------------------------------------------------------------
+# P9: threshold assignment against hand-derived golden rows.
+# ---------------------------------------------------------------------------------------
+def golden_assign_cases():
+    with open(os.path.join(GOLDEN, "assign_cases.json")) as f:
+        return json.load(f)["cases"]
+
+
+def pin_assign_case(case):
+    n = case["seq_len"]
+    p = oracle.Problem(seq_len=n, seq_valid=n, head_dim=8, block_q=case["block_q"],
+                       block_k=64, causal=case["causal"])
+    a = oracle.AssignParams(tuple(case["thresholds"]), case.get("cos_sim_min", 0.0),
+                            case.get("force_diag_l0", False), case.get("force_begin", 0),
+                            case.get("force_end", 0))
+    sim = None
+    if "sim" in case:
+        sim = np.asarray(case["sim"], dtype=np.float32).astype(np.float64)
+    M = np.asarray(case["M"], dtype=np.float32).astype(np.float64)
+    row = oracle.assign_row(M, sim, p, a, case["qb"])
+    return int(np.sum(row != np.asarray(case["expected"])))
+
+
+def pin_build_index(seed=14):
+    rng = np.random.default_rng(seed)
+    lm = rng.choice(np.array([0, 1, 2, 3, -1], dtype=np.int8), size=(2, 3, 5, 37))
+    rp, ci = oracle.build_index(lm)
+    rows = lm.reshape(-1, 37)
+    bad = 0
+    for r in range(rows.shape[0]):
+        for l in range(4):
+            ref = np.flatnonzero(rows[r] == l)
+            got = ci[rp[r * 4 + l]:rp[r * 4 + l + 1]]
+            bad += int(not np.array_equal(ref, got))
+    return bad

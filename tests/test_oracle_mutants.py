@@ -1,0 +1,92 @@
+"""Plant plausible mistakes in the CPU oracle (on the CPU, in a private copy of its source)
+and check that at least one pin catches each one. This guards the pins themselves: a pin set
+that a dropped term, a flipped sign, a wrong index or a transposed operand slips through is
+not pinning the oracle."""
+import importlib.util
+import os
+import sys
+import types
+
+import numpy as np
+import pytest
+
+import pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "psa_oracle.py")
+
+ALL_PINS = {
+    "p1": lambda: max(pins.pin_all_l0_dense(False, 512), pins.pin_all_l0_dense(False, 488),
+                      pins.pin_all_l0_dense(True, 512)),
+    "p2": pins.pin_binary_block_sparse,
+    "p3": pins.pin_upsample_equivalence,
+    "p4": lambda: max(pins.pin_constant_runs(l) for l in (1, 2, 3)),
+    "p5": pins.pin_all_skip_row,
+    "p6": pins.pin_weight_multiplicity,
+    "p7": pins.pin_pyramid,
+    "p8s": lambda: max(pins.pin_sampling_all_rows(False), pins.pin_sampling_all_rows(True)),
+    "p8a": lambda: max(pins.pin_antidiag_stride1(False), pins.pin_antidiag_stride1(True),
+                       pins.pin_antidiag_orientation_and_sum()),
+    "p8c": pins.pin_cossim,
+    "p9": lambda: sum(pins.pin_assign_case(c) for c in pins.golden_assign_cases()),
+    "idx": pins.pin_build_index,
+}
+
+MUTANTS = [
+    ("bias_sign", "lv[None, :] * LN2\n        vis", "lv[None, :] * -LN2\n        vis"),
+    ("bias_dropped", "lv[None, :] * LN2\n        vis", "lv[None, :] * 0.0\n        vis"),
+    ("scale_dropped", "return 1.0 / math.sqrt(self.head_dim)", "return 1.0"),
+    ("pv_uses_keys", "o[qi] = w @ Vb", "o[qi] = w @ Kb"),
+    ("last_token_off_by_one", "return (np.asarray(rows) + 1) * (1 << level) - 1",
+     "return (np.asarray(rows) + 1) * (1 << level)"),
+    ("pool_wrong_axis", "n // f, f, x.shape[-1]).mean(axis=-2)",
+     "n // f, f, x.shape[-1]).mean(axis=-1)[..., None].repeat(x.shape[-1], -1)"),
+    ("pad_keys_visible", "vis = last[None, :] < p.seq_valid\n        if p.causal",
+     "vis = last[None, :] < p.seq_len\n        if p.causal"),
+    ("antidiag_no_reverse", "qs = q.reshape(R, S, d)[:, ::-1, :]", "qs = q.reshape(R, S, d)[:, :, :]"),
+    ("antidiag_mean", "A = p.scale * (qs @ ks.T)", "A = p.scale * (qs @ ks.T) / S"),
+    ("sampling_no_causal", "vis = vis & (keys[None, :] <= rows[:, None])", "vis = vis"),
+    ("cossim_keeps_diagonal", "sim[kb] = cos[off].sum()", "sim[kb] = cos.sum()"),
+    ("assign_le", "if c < t[l]:", "if c <= t[l]:"),
+    ("assign_tie_reversed", "key=lambda kb: (-float(M[kb]), kb)", "key=lambda kb: (-float(M[kb]), -kb)"),
+    ("assign_inclusive_cumsum", "for kb in order:\n        lvl = SKIP",
+     "for kb in order:\n        c += float(M[kb])\n        lvl = SKIP"),
+    ("cos_fallback_inclusive", "float(sim[kb]) < float(np.float32(a.cos_sim_min))",
+     "float(sim[kb]) <= float(np.float32(a.cos_sim_min))"),
+    ("index_descending", "sel = [kb for kb in range(nkb) if rows[r, kb] == l]",
+     "sel = [kb for kb in reversed(range(nkb)) if rows[r, kb] == l]"),
+]
+
+
+def _mutant_module(old, new, monkeypatch):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor not found exactly once: {old!r}"
+    mod = types.ModuleType("psa_oracle_mutant")
+    mod.__file__ = SRC
+    monkeypatch.setitem(sys.modules, "psa_oracle_mutant", mod)
+    exec(compile(src.replace(old, new), SRC, "exec"), mod.__dict__)
+    mod.psa_oracle = mod
+    return mod
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_some_pin_catches_mutant(monkeypatch, name, old, new):
+    mod = _mutant_module(old, new, monkeypatch)
+    monkeypatch.setattr(pins, "oracle", mod)
+    caught = []
+    for pin, fn in ALL_PINS.items():
+        try:
+            with np.errstate(all="ignore"):
+                err = fn()
+        except Exception:
+            err = np.inf
+        if not (err < 1e-9):
+            caught.append(pin)
+    assert caught, f"mutant {name} passed every pin"
+
+
+def test_unmutated_copy_passes_every_pin(monkeypatch):
+    mod = _mutant_module("SKIP = -1\n", "SKIP = -1\n", monkeypatch)
+    monkeypatch.setattr(pins, "oracle", mod)
+    for pin, fn in ALL_PINS.items():
+        assert fn() < 1e-9, pin
