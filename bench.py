@@ -1,0 +1,353 @@
+#!/usr/bin/env python3
+"""Benchmark of the Pyramid Sparse Attention forward path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step = the whole path on one batch of synthetic, seeded input already resident in HBM:
+psa_build_pyramid, psa_mask (block scores, cosine check if any, threshold assignment),
+psa_build_index and the level-weighted attention kernel. The default workload is the
+Wan2.1-1.3B-like 32k self-attention layer (12 heads, d 128, 32760 tokens padded to 32768,
+query/KV blocks 128/64, sampling-mode mask with thresholds 0.5/0.7/0.8/0.9).
+
+Prints one JSON line. `value` is whole-step throughput: executed level-weighted attention
+FLOPs (4*d per executed (valid query, visible pooled key) pair) per second of step time.
+`attn` gives the attention kernel alone (ms/layer, TFLOP/s, % of the 2.5 PFLOP/s dense bf16
+MFMA peak, speedup over the same kernel on an all-level-0 map). `roofline` is for that
+kernel, timed with HIP events on the stream it runs on. `cpu_baseline` times the CPU oracle
+(fp64 numpy) on a bounded sample of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, GB/s
+METRIC = "psa_attn_fwd ms/layer + effective TFLOP/s (% bf16 MFMA peak), Wan-like 32k"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_fwd_bf16_traffic.txt")
+ATTN_SOURCE = os.path.join(ROOT, "video_transformers_amd", "csrc", "psa_attn.hip")
+
+
+# ---------------------------------------------------------------------------------------
+# work accounting (host side, from the level map)
+# ---------------------------------------------------------------------------------------
+def executed_pairs(level_map: np.ndarray, wl: W.Workload) -> int:
+    """Number of (valid query, visible pooled key) pairs the level map executes: a pooled row j
+    of level l stands for tokens [j*2^l, (j+1)*2^l) and is visible to query i iff its last
+    token is < seq_valid and, when causal, <= i."""
+    B, H, nqb, nkb = level_map.shape
+    nv, bq = wl.seq_valid, wl.block_q
+    total = 0
+    kb = np.arange(nkb)
+    # visible pooled rows per (kb, level) for non-causal attention
+    vis = np.stack([np.clip(nv // (1 << l) - kb * (64 >> l), 0, 64 >> l) for l in range(4)], 1)
+    nq = np.clip(nv - np.arange(nqb) * bq, 0, bq)
+    if not wl.causal:
+        for l in range(4):
+            sel = (level_map == l)
+            total += int(np.einsum("bhqk,k,q->", sel.astype(np.int64), vis[:, l], nq))
+        return total
+    for b in range(B):
+        for h in range(H):
+            for qb in range(nqb):
+                row = level_map[b, h, qb]
+                lasts = []
+                for l in range(4):
+                    for k in np.flatnonzero(row == l):
+                        j = np.arange(k * (64 >> l), (k + 1) * (64 >> l))
+                        lasts.append((j + 1) * (1 << l) - 1)
+                if not lasts:
+                    continue
+                lasts = np.sort(np.concatenate(lasts))
+                qi = np.arange(qb * bq, qb * bq + nq[qb])
+                lim = np.minimum(qi, nv - 1)
+                total += int(np.searchsorted(lasts, lim, side="right").sum())
+    return total
+
+
+def dense_pairs(wl: W.Workload) -> int:
+    nv = wl.seq_valid
+    per_head = nv * (nv + 1) // 2 if wl.causal else nv * nv
+    return wl.batch * wl.heads_q * per_head
+
+
+# ---------------------------------------------------------------------------------------
+# CPU baseline: the oracle, bounded sample, host cores
+# ---------------------------------------------------------------------------------------
+_G = {}
+
+
+def _oracle_row(qb):
+    import oracle
+    from threadpoolctl import threadpool_limits
+    g = _G
+    with threadpool_limits(limits=1):
+        t = time.perf_counter()
+        oracle.attention_head(g["q"], g["k"], g["v"], g["lm"], g["p"], qblocks=[qb])
+        return time.perf_counter() - t
+
+
+def cpu_baseline(wl: W.Workload, budget_s: float = 15.0) -> dict:
+    """Times the oracle's attention on query blocks of head 0 (its own level map for that
+    head) with a fork pool of one single-threaded worker per available core (at most 16)."""
+    import multiprocessing as mp
+
+    import oracle
+    p = oracle.Problem.of(wl)
+    q = oracle.as_f64(W.make_q(wl, [0]))[0, 0]
+    k = oracle.as_f64(W.make_k(wl, [0]))[0, 0]
+    v = oracle.as_f64(W.make_v(wl, [0]))[0, 0]
+    if wl.map_source in ("iid", "fixed_frac"):
+        lm = W.make_map(wl, [0])[0, 0]
+    else:
+        a = oracle.AssignParams(tuple(wl.thresholds), wl.cos_sim_min, wl.force_diag_l0,
+                                wl.text_begin, wl.text_end)
+        if wl.mask_mode == "sampling":
+            M = oracle.mask_scores_sampling(q, k, p, wl.samples_per_qblock)
+        else:
+            M = oracle.mask_scores_antidiag(q, k, p, wl.antidiag_stride)
+        sim = oracle.block_cossim(k, p) if wl.cos_sim_min > 0 else None
+        lm = oracle.assign_levels(M, sim, p, a)
+    _G.update(q=q, k=k, v=v, lm=lm, p=p)
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    t_one = _oracle_row(0)
+    n_rows = int(min(wl.n_qblocks, max(workers, budget_s * workers / max(t_one, 1e-3))))
+    rows = list(range(n_rows))
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(workers) as pool:
+        pool.map(_oracle_row, rows, chunksize=1)
+    wall = time.perf_counter() - t0
+    pairs = executed_pairs(lm[None, None, :n_rows], wl.replace(heads_q=1, batch=1))
+    flops = 4.0 * wl.head_dim * pairs
+    return {"value": round(flops / wall / 1e12, 6), "unit": "TFLOP/s", "cores": workers,
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle attention over query blocks 0..{n_rows - 1} of head 0 "
+                      f"(of {wl.heads_q} heads x {wl.n_qblocks} blocks), its own level map; "
+                      f"{pairs} executed pairs in {wall:.2f} s on {workers} single-threaded "
+                      f"processes"}
+
+
+# ---------------------------------------------------------------------------------------
+# GPU run
+# ---------------------------------------------------------------------------------------
+def _traffic_from_profile():
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary, or None if
+    the attention kernel source changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.lstrip().startswith("#"):
+            key, val = line.split(":", 1)
+            kv[key.strip()] = val.strip()
+    sha = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
+    if kv.get("attn_source_sha256") != sha:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def run(args) -> dict:
+    import torch
+    import video_transformers_amd as psa
+
+    wl = W.BY_NAME[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = (t.to(dev) for t in W.make_qkv(wl))
+    prob = psa.make_problem(q, k, v, block_q=wl.block_q, block_k=wl.block_k,
+                            causal=wl.causal, seq_valid=wl.seq_valid)
+    params = psa.MaskParams(mode=wl.mask_mode or "sampling",
+                            thresholds=tuple(wl.thresholds) or (0.5, 0.7, 0.8, 0.9),
+                            samples_per_qblock=wl.samples_per_qblock,
+                            antidiag_stride=wl.antidiag_stride, cos_sim_min=wl.cos_sim_min,
+                            force_diag_l0=wl.force_diag_l0, force_l0_begin=wl.text_begin,
+                            force_l0_end=wl.text_end)
+    computed_map = wl.map_source == "mask"
+    drawn = None if computed_map else torch.from_numpy(W.make_map(wl)).to(dev)
+    B, H, N, d = q.shape
+    nqb, nkb = wl.n_qblocks, wl.n_kblocks
+
+    # outputs and scratch allocated once
+    kp = torch.empty((B, wl.heads_kv, psa.pooled_rows(prob), d), dtype=q.dtype, device=dev)
+    vp = torch.empty_like(kp)
+    lm_buf = torch.empty((B, H, nqb, nkb), dtype=torch.int8, device=dev)
+    mass = torch.empty((B, H, nqb, nkb), dtype=torch.float32, device=dev)
+    sim = (torch.empty((B, wl.heads_kv, nkb), dtype=torch.float32, device=dev)
+           if wl.cos_sim_min > 0 else None)
+    row_ptr = torch.empty(B * H * nqb * 4 + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(B * H * nqb * nkb, dtype=torch.int32, device=dev)
+    dev_err = torch.empty(1, dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    L = psa.lib()
+    import ctypes
+    cp = params.c()
+    ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    st = ctypes.c_void_p(stream.cuda_stream)
+
+    def check(rc, what):
+        if rc != 0:
+            raise psa.PsaError(rc, what)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        check(L.psa_build_pyramid(prob.ref(), ptr(k), ptr(v), ptr(kp), ptr(vp), st), "pyramid")
+        if ev:
+            ev[1].record(stream)
+        if computed_map:
+            check(L.psa_mask(prob.ref(), ctypes.byref(cp), ptr(q), ptr(k), ptr(lm_buf), ptr(mass),
+                             ptr(sim), None, 0, st), "mask")
+            lm = lm_buf
+        else:
+            lm = drawn
+        if ev:
+            ev[2].record(stream)
+        check(L.psa_build_index(prob.ref(), ptr(lm), ptr(row_ptr), ptr(col_idx), ptr(dev_err), st),
+              "index")
+        if ev:
+            ev[3].record(stream)
+        check(L.psa_attn_fwd_indexed(prob.ref(), ctypes.c_float(0.0), ptr(q), ptr(k), ptr(v),
+                                     ptr(kp), ptr(vp), ptr(row_ptr), ptr(col_idx), ptr(o),
+                                     ptr(lse), st), "attn")
+        if ev:
+            ev[4].record(stream)
+        return lm
+
+    # a plain copy of known size, for scaling the HBM byte counters of a profiled run
+    copy_bytes = 256 << 20
+    cs = torch.empty(copy_bytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    cd = torch.empty_like(cs)
+    cd.copy_(cs)
+    del cs, cd
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if int(dev_err.item()) != 0:
+        raise RuntimeError("level map held invalid entries")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)]
+                      for i in range(args.steps)])
+    st_ms = stage.mean(axis=0)
+    attn_ms = float(np.median(stage[:, 3]))
+    attn_ms_mean = float(st_ms[3])
+
+    lm_host = (lm_buf if computed_map else drawn).cpu().numpy()
+    pairs = executed_pairs(lm_host, wl)
+    flops = 4.0 * d * pairs
+    dpairs = dense_pairs(wl)
+    lv, cnt = np.unique(lm_host, return_counts=True)
+    frac = {("skip" if int(a) < 0 else f"L{int(a)}"): round(float(c) / lm_host.size, 4)
+            for a, c in zip(lv, cnt)}
+
+    # same kernel, all-level-0 map (causal: the lower triangle)
+    dense = torch.zeros((B, H, nqb, nkb), dtype=torch.int8, device=dev)
+    if wl.causal:
+        qb_i = torch.arange(nqb, device=dev)[:, None]
+        kb_i = torch.arange(nkb, device=dev)[None, :]
+        dense[:, :, kb_i.expand(nqb, nkb) * 64 > (qb_i + 1) * wl.block_q - 1] = -1
+    rp_d = torch.empty_like(row_ptr)
+    ci_d = torch.empty_like(col_idx)
+    check(L.psa_build_index(prob.ref(), ptr(dense), ptr(rp_d), ptr(ci_d), ptr(dev_err), st), "index")
+    de = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    times = []
+    for i in range(3):
+        de[0].record(stream)
+        check(L.psa_attn_fwd_indexed(prob.ref(), ctypes.c_float(0.0), ptr(q), ptr(k), ptr(v),
+                                     ptr(kp), ptr(vp), ptr(rp_d), ptr(ci_d), ptr(o), ptr(lse), st),
+              "attn dense")
+        de[1].record(stream)
+        torch.cuda.synchronize()
+        times.append(de[0].elapsed_time(de[1]))
+    dense_ms = float(np.median(times[1:]))
+
+    ms_per_step = wall * 1e3 / args.steps
+    attn_tflops = flops / (attn_ms_mean * 1e-3) / 1e12
+    traffic = _traffic_from_profile()
+    out = {
+        "metric": METRIC,
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; clustered keys, no weights or videos)",
+        "config": {"workload": wl.name, "batch": B, "heads_q": H, "heads_kv": wl.heads_kv,
+                   "seq_len": N, "seq_valid": wl.seq_valid, "head_dim": d,
+                   "block_q": wl.block_q, "block_k": wl.block_k, "causal": wl.causal,
+                   "map": (f"psa_mask {wl.mask_mode} thresholds {list(wl.thresholds)}"
+                           if computed_map else f"drawn ({wl.map_source})")},
+        "attn": {"ms_per_layer_median": round(attn_ms, 4), "ms_per_layer_mean": round(attn_ms_mean, 4),
+                 "tflops_executed": round(attn_tflops, 2),
+                 "pct_bf16_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
+                 "dense_same_kernel_ms": round(dense_ms, 3),
+                 "speedup_vs_dense": round(dense_ms / attn_ms_mean, 2),
+                 "dense_tflops": round(4.0 * d * dpairs / (dense_ms * 1e-3) / 1e12, 2),
+                 "executed_pairs": pairs,
+                 "effective_sparsity": round(1.0 - pairs / dpairs, 4),
+                 "level_fractions": frac},
+        "stages_ms": {"build_pyramid": round(float(st_ms[0]), 4), "mask": round(float(st_ms[1]), 4),
+                      "build_index": round(float(st_ms[2]), 4), "attn_kernel": round(float(st_ms[3]), 4)},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic,
+                     "kernel": "k_attn_fwd_bf16" if wl.dtype == "bf16" else "k_attn_fwd_f32",
+                     "per_launch": f"{flops:.4e} executed FLOP (4*d per executed pair)"},
+    }
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=W.WAN13B_32K.name, choices=sorted(W.BY_NAME))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(every (batch, head) is independent; see the sharding notes). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    wl = W.BY_NAME[args.workload]
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_budget)      # before the GPU is touched (fork pool)
+    out = run(args)
+    out["cpu_baseline"] = cpu
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

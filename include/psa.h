@@ -1,0 +1,209 @@
+/*
+ * psa.h - C ABI of libpsa: the Pyramid Sparse Attention (PSA) forward path, written in HIP
+ * for AMD Instinct MI355X (gfx950, CDNA4).
+ *
+ * PSA (arXiv 2512.04025; summary article at rg.mbintangr.com, section "Method") replaces the
+ * keep/drop decision of block-sparse attention with a level per (query block, KV block) pair:
+ * level 0 reads the block's full-resolution keys/values, levels 1/2/3 read them 1D mean-pooled
+ * by 2/4/8, and the least important pairs are skipped. The path has three calls:
+ *   psa_build_pyramid  - the mean-pooled levels 1..3 of K and V;
+ *   psa_mask           - block importance (sampling or antidiagonal scoring, optional
+ *                        intra-block cosine check) and threshold assignment of levels;
+ *   psa_attn_fwd       - the level-weighted flash-style attention.
+ * plus psa_mask_assign and psa_build_index, the mask's and the attention's integer stages,
+ * exported on their own.
+ *
+ * Conventions shared by every call
+ *  - Pointers named q, k, v, o, k_pooled, v_pooled, level_map, block_mass, block_sim, lse,
+ *    row_ptr, col_idx, dev_err and ws are DEVICE pointers owned by the caller; the library
+ *    never allocates or frees device memory and keeps no state between calls. psa_problem and
+ *    psa_mask_params are HOST pointers, read during the call only.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). Work is only
+ *    enqueued: no call synchronises except psa_check_status.
+ *  - Arguments are checked on the host before anything is enqueued. A failed check returns a
+ *    negative psa_status and enqueues nothing. No C++ exception crosses this interface.
+ *  - All calls are reentrant; calls on different streams may run concurrently provided their
+ *    output and workspace buffers do not overlap.
+ *
+ * Tensor layouts (element counts, row-major):
+ *   Q, O      [batch, heads_q,  seq_len, head_dim]  with strides q_stride / o_stride
+ *   K, V      [batch, heads_kv, seq_len, head_dim]  with strides k_stride / v_stride
+ *   k_pooled, v_pooled  [batch, heads_kv, 7*seq_len/8, head_dim], contiguous, same dtype as K:
+ *             level l (1..3) occupies rows [seq_len - 2*seq_len/2^l, seq_len - seq_len/2^l),
+ *             i.e. level 1 at row 0, level 2 at seq_len/2, level 3 at 3*seq_len/4.
+ *   level_map [batch, heads_q, seq_len/block_q, seq_len/block_k] int8, contiguous;
+ *             0..3 = level, -1 = skip.
+ *   block_mass [batch, heads_q, NQB, NKB] float32; block_sim [batch, heads_kv, NKB] float32.
+ *   lse       [batch, heads_q, seq_len] float32 (natural-log logsumexp of the logits).
+ * Strides are in elements for the (batch, head, token) axes; head_dim is contiguous. Strides
+ * must be positive multiples of 8 and base pointers 16-byte aligned.
+ * GQA: query head h reads KV head h / (heads_q / heads_kv).
+ *
+ * Supported domain (anything else returns PSA_ERR_UNSUPPORTED): dtype f32 or bf16;
+ * head_dim 64 or 128; block_k 64; block_q 64 or 128; seq_len a multiple of block_q;
+ * 0 <= seq_valid <= seq_len with (seq_len - seq_valid) a multiple of 8 (so that every pooled
+ * token is either wholly valid or wholly padding).
+ */
+#ifndef PSA_H_
+#define PSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define PSA_OK 0
+#define PSA_ERR_INVALID_ARG (-1)   /* null pointer, negative size, inconsistent shape/stride */
+#define PSA_ERR_UNSUPPORTED (-2)   /* valid request outside the supported domain above */
+#define PSA_ERR_WORKSPACE (-3)     /* workspace null or smaller than the *_workspace_bytes query */
+#define PSA_ERR_HIP (-4)           /* a HIP runtime call or kernel launch failed; see psa_last_hip_error */
+#define PSA_ERR_BAD_LEVEL_MAP (-5) /* a level map entry outside {-1,0,1,2,3} was seen on the device */
+
+/* Element types. */
+#define PSA_F32 0
+#define PSA_BF16 1
+
+#define PSA_SKIP (-1)
+#define PSA_NUM_LEVELS 4
+
+/* Mask generator modes (summary article, "Method": sampling-based for generation, antidiagonal
+ * scoring with an intra-block similarity check for understanding). */
+#define PSA_MASK_SAMPLING 0
+#define PSA_MASK_ANTIDIAG 1
+
+typedef struct psa_problem {
+    int32_t batch, heads_q, heads_kv;
+    int32_t seq_len;    /* padded length N */
+    int32_t seq_valid;  /* valid tokens Nv; keys >= Nv are never attended, queries >= Nv give 0 */
+    int32_t head_dim;
+    int32_t block_q, block_k;
+    int32_t causal;     /* nonzero: query i sees full-resolution key j iff j <= i */
+    int32_t dtype;      /* PSA_F32 or PSA_BF16, for Q, K, V, O and the pooled levels */
+    int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3];
+} psa_problem;
+
+typedef struct psa_mask_params {
+    int32_t mode;                 /* PSA_MASK_SAMPLING or PSA_MASK_ANTIDIAG */
+    float thresholds[4];          /* cumulative-mass thresholds t0 <= t1 <= t2 <= t3, in (0, 1] */
+    int32_t samples_per_qblock;   /* sampling mode: rows per query block; 1, 2, 4, .., 32 */
+    int32_t antidiag_stride;      /* antidiagonal mode: stride S in {2, 4, 8}, block_q/S <= 32 */
+    float cos_sim_min;            /* pooled levels need block similarity >= this; <= 0 disables */
+    int32_t force_diag_l0;        /* nonzero: blocks overlapping the query block's tokens are L0 */
+    int32_t force_l0_begin;       /* token span [begin, end) forced to L0 in both directions; */
+    int32_t force_l0_end;         /* empty if begin >= end */
+} psa_mask_params;
+
+/* Rows per (batch, KV head) of the packed pooled tensors: 7*seq_len/8; -1 on a bad problem. */
+int64_t psa_pooled_rows(const psa_problem* prob);
+
+/*
+ * Levels 1..3 of K and V (summary article, "Method": a pyramid built by progressive 1D mean
+ * pooling; skill summary at skillsmp.com, "Implementation": level l pools by 2^l).
+ * k_pooled/v_pooled row j of level l = mean of full-resolution rows [j*2^l, (j+1)*2^l).
+ * Accumulation is a pairwise float32 tree (each level is the pairwise mean of the one
+ * below), which equals the direct mean up to one rounding; bf16 outputs are rounded to
+ * nearest-even. Level 0 is not copied: the attention reads K and V directly.
+ */
+int psa_build_pyramid(const psa_problem* prob, const void* k, const void* v,
+                      void* k_pooled, void* v_pooled, void* stream);
+
+/* Device workspace psa_mask needs for `params`; 0 on a bad argument. */
+size_t psa_mask_workspace_bytes(const psa_problem* prob, const psa_mask_params* params);
+
+/*
+ * Multi-level mask generator (summary article, "Method" and "Results").
+ *  Sampling mode: for each query block, S = samples_per_qblock rows r_s = floor(s*R/S) of its
+ *   R valid rows are scored against every valid level-0 key of its KV head (softmax of
+ *   q.k/sqrt(d), keys >= seq_valid masked, causal keys after the row masked);
+ *   block_mass[qb][kb] = mean over the S rows of the probability mass of KV block kb.
+ *  Antidiagonal mode, stride S: compressed logits
+ *   A[r][c] = (1/sqrt(d)) * sum_{t<S} q[r*S+S-1-t] . k[c*S+t], softmax over valid c
+ *   (causal: c <= r), block_mass[qb][kb] = mass of kb's columns averaged over qb's valid rows.
+ *  If cos_sim_min > 0, block_sim[b][hkv][kb] = mean cosine similarity over ordered pairs of
+ *   distinct valid level-0 keys of the block (written; block_sim must then be non-null).
+ *  Then psa_mask_assign's rule turns block_mass (and block_sim) into level_map.
+ * block_mass is required (it is an output). Workspace: psa_mask_workspace_bytes.
+ * Scoring runs bf16 MFMA: psa_mask needs dtype PSA_BF16 (PSA_ERR_UNSUPPORTED otherwise);
+ * psa_mask_assign takes masses of any origin.
+ */
+int psa_mask(const psa_problem* prob, const psa_mask_params* params, const void* q,
+             const void* k, int8_t* level_map, float* block_mass, float* block_sim,
+             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Threshold assignment (summary article, "Results": threshold-based levels with a cosine
+ * constraint on pooling). Per (batch, head, query block) row, over the candidate blocks
+ * (all; causal: those overlapping tokens <= the block's last token):
+ *   sort by block_mass descending (ties: lower kb first); exclusive running sum c in float64
+ *   in that order; level = min{l : c < thresholds[l]}, otherwise skip.
+ * Then: causal non-candidates -> skip; forced L0 (force_diag_l0: blocks overlapping the query
+ * block's tokens; the forced span in either direction) -> 0; a pooled level on a block with
+ * block_sim < cos_sim_min (when cos_sim_min > 0) -> 0. A query block with no valid query row is
+ * all skip. block_sim may be null when cos_sim_min <= 0. Integer output, deterministic.
+ */
+int psa_mask_assign(const psa_problem* prob, const psa_mask_params* params,
+                    const float* block_mass, const float* block_sim, int8_t* level_map,
+                    void* stream);
+
+/*
+ * Block index: a CSR over (row, level) keys, rows r = (b*heads_q + h)*NQB + qb.
+ * row_ptr[R*4+1] int32: col_idx[row_ptr[r*4+l] .. row_ptr[r*4+l+1]) lists, in ascending
+ * order, the kb with level_map == l. col_idx needs capacity R*NKB int32. Entries outside
+ * {-1..3} are treated as skip and set *dev_err (device int32) to PSA_ERR_BAD_LEVEL_MAP;
+ * the call clears *dev_err first.
+ */
+int psa_build_index(const psa_problem* prob, const int8_t* level_map, int32_t* row_ptr,
+                    int32_t* col_idx, int32_t* dev_err, void* stream);
+
+/* Device workspace psa_attn_fwd needs; 0 on a bad problem. */
+size_t psa_attn_workspace_bytes(const psa_problem* prob);
+
+/*
+ * Adaptive Pyramid Attention forward (summary article, "Method": each KV block is fetched at
+ * its level and a scaling factor keeps the probabilities consistent; news summary at
+ * euno.news, "Methodology" item 4: equivalent to upsampling the pooled block and running
+ * standard scaled dot-product attention). For every valid query i of query block qb:
+ *   z_j = softmax_scale * q_i . Kbar_j + l_j * ln 2
+ * over the pooled rows j of every block listed for (b, h, qb) at its level l_j (weight 2^l_j
+ * per pooled token), a pooled token being visible iff its last full-resolution token is
+ * < seq_valid and (causal) <= i; o_i = sum_j softmax(z)_j Vbar_j, lse_i = logsumexp_j z_j.
+ * A query with no visible key, and every query >= seq_valid, gets o = 0 and lse = -inf.
+ * softmax_scale <= 0 selects 1/sqrt(head_dim). lse may be null. k_pooled/v_pooled come from
+ * psa_build_pyramid on the same K, V. The block index is built inside the call (into ws).
+ * bf16 runs MFMA in bf16 with float32 accumulation and softmax; f32 runs float32 MFMA.
+ */
+int psa_attn_fwd(const psa_problem* prob, float softmax_scale, const void* q, const void* k,
+                 const void* v, const void* k_pooled, const void* v_pooled,
+                 const int8_t* level_map, void* o, float* lse, void* ws, size_t ws_bytes,
+                 void* stream);
+
+/*
+ * psa_attn_fwd on a block index already built by psa_build_index (row_ptr, col_idx) for the
+ * same problem, e.g. a map reused across layers or denoising steps. Same math and outputs;
+ * no workspace. The index must describe a map of this problem's shape.
+ */
+int psa_attn_fwd_indexed(const psa_problem* prob, float softmax_scale, const void* q,
+                         const void* k, const void* v, const void* k_pooled,
+                         const void* v_pooled, const int32_t* row_ptr, const int32_t* col_idx,
+                         void* o, float* lse, void* stream);
+
+/*
+ * Waits for `stream`, then reports device-side errors recorded in `ws` by the last
+ * psa_attn_fwd that used it: PSA_OK or PSA_ERR_BAD_LEVEL_MAP (or PSA_ERR_HIP).
+ */
+int psa_check_status(const void* ws, void* stream);
+
+/* Static string for a status code. */
+const char* psa_status_string(int status);
+
+/* The hipError_t of the last PSA_ERR_HIP returned on this thread (0 if none). */
+int psa_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PSA_H_ */

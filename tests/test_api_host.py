@@ -1,0 +1,119 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every function that
+include/psa.h declares, and rejects bad arguments with the documented status before touching
+the device."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import video_transformers_amd as psa
+from video_transformers_amd import psa as P
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "psa.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(psa_[a-z_0-9]+)\s*\(",
+                                 src, flags=re.M)))
+
+
+def test_header_lists_the_binding_exports():
+    assert declared_functions() == sorted(psa.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = psa.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def _prob(**kw):
+    q = torch.zeros(1, 2, 1024, 64)
+    p = psa.make_problem(q, q, q, block_q=64)
+    for k, v in kw.items():
+        setattr(p.c, k, v)
+    return p
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 96, P.PSA_ERR_UNSUPPORTED),
+    ("block_k", 32, P.PSA_ERR_UNSUPPORTED),
+    ("block_q", 256, P.PSA_ERR_UNSUPPORTED),
+    ("dtype", 7, P.PSA_ERR_UNSUPPORTED),
+    ("seq_valid", 1020, P.PSA_ERR_UNSUPPORTED),     # padding not a multiple of 8
+    ("seq_valid", 2000, P.PSA_ERR_INVALID_ARG),     # beyond seq_len
+    ("seq_len", 1088 + 8, P.PSA_ERR_UNSUPPORTED),   # not a multiple of block_q
+    ("heads_kv", 3, P.PSA_ERR_INVALID_ARG),         # heads_q % heads_kv
+    ("heads_q", 0, P.PSA_ERR_INVALID_ARG),
+])
+def test_problem_checks(field, value, status):
+    p = _prob(**{field: value})
+    L = psa.lib()
+    assert L.psa_pooled_rows(p.ref()) == -1
+    assert L.psa_attn_workspace_bytes(p.ref()) == 0
+    dummy = ctypes.c_void_p(256)
+    rc = L.psa_attn_fwd(p.ref(), 0.0, dummy, dummy, dummy, dummy, dummy, dummy, dummy, None,
+                        dummy, 1 << 20, None)
+    assert rc == status
+    assert L.psa_build_pyramid(p.ref(), dummy, dummy, dummy, dummy, None) == status
+
+
+def test_bad_stride_rejected():
+    p = _prob()
+    p.c.k_stride[2] = 60   # not a multiple of 8
+    assert psa.lib().psa_pooled_rows(p.ref()) == -1
+
+
+def test_null_pointer_and_workspace_checks():
+    p = _prob()
+    L = psa.lib()
+    d = ctypes.c_void_p(256)
+    assert L.psa_attn_fwd(p.ref(), 0.0, None, d, d, d, d, d, d, None, d, 1 << 20, None) == P.PSA_ERR_INVALID_ARG
+    need = L.psa_attn_workspace_bytes(p.ref())
+    assert need > 0
+    assert L.psa_attn_fwd(p.ref(), 0.0, d, d, d, d, d, d, d, None, d, need - 1, None) == P.PSA_ERR_WORKSPACE
+    assert L.psa_attn_fwd(p.ref(), 0.0, d, d, d, d, d, d, d, None, None, need, None) == P.PSA_ERR_WORKSPACE
+    misaligned = ctypes.c_void_p(264)
+    assert L.psa_attn_fwd(p.ref(), 0.0, misaligned, d, d, d, d, d, d, None, d, need, None) == P.PSA_ERR_INVALID_ARG
+    assert L.psa_build_index(p.ref(), None, d, d, d, None) == P.PSA_ERR_INVALID_ARG
+    assert L.psa_check_status(None, None) == P.PSA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(thresholds=(0.5, 0.4, 0.8, 0.9)), P.PSA_ERR_INVALID_ARG),   # decreasing
+    (dict(thresholds=(0.0, 0.7, 0.8, 0.9)), P.PSA_ERR_INVALID_ARG),   # t0 <= 0
+    (dict(thresholds=(0.5, 0.7, 0.8, 1.5)), P.PSA_ERR_INVALID_ARG),   # > 1
+    (dict(samples_per_qblock=0), P.PSA_ERR_INVALID_ARG),
+    (dict(samples_per_qblock=65), P.PSA_ERR_INVALID_ARG),             # > block_q (64)
+    (dict(samples_per_qblock=12), P.PSA_ERR_UNSUPPORTED),             # not a power of two
+    (dict(samples_per_qblock=64), P.PSA_ERR_UNSUPPORTED),             # > 32
+    (dict(mode="antidiag", antidiag_stride=3), P.PSA_ERR_UNSUPPORTED),
+    (dict(mode="antidiag", antidiag_stride=16), P.PSA_ERR_UNSUPPORTED),
+    (dict(force_l0_begin=10, force_l0_end=5000), P.PSA_ERR_INVALID_ARG),
+])
+def test_mask_param_checks(kw, status):
+    p = _prob(dtype=P.PSA_BF16)
+    mp = psa.MaskParams(**kw).c()
+    L = psa.lib()
+    d = ctypes.c_void_p(256)
+    assert L.psa_mask_workspace_bytes(p.ref(), ctypes.byref(mp)) == 0
+    assert L.psa_mask(p.ref(), ctypes.byref(mp), d, d, d, d, d, d, 1 << 20, None) == status
+    assert L.psa_mask_assign(p.ref(), ctypes.byref(mp), d, d, d, None) == status
+
+
+def test_mask_needs_bf16():
+    p = _prob()   # float32 problem
+    mp = psa.MaskParams().c()
+    d = ctypes.c_void_p(256)
+    assert psa.lib().psa_mask(p.ref(), ctypes.byref(mp), d, d, d, d, d, d, 0, None) == P.PSA_ERR_UNSUPPORTED
+
+
+def test_status_strings():
+    L = psa.lib()
+    for code in (0, -1, -2, -3, -4, -5):
+        assert L.psa_status_string(code).startswith(b"PSA_")
+    assert L.psa_last_hip_error() == 0

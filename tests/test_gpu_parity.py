@@ -1,0 +1,271 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on seeded inputs.
+
+Reduced copies of the five workloads (same block sizes, mask mode, padding, GQA, causality,
+text span) are checked element by element; they span several tiles and end in a ragged tail.
+Integer outputs (block index, level maps, threshold assignment) are compared bit-exactly;
+floating-point outputs against the bars in gpu_util.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+import video_transformers_amd as psa
+from gpu_util import (DEV, announce, assign_params, check_attention, fragile_entries,
+                      mask_params, need_gpu, oracle_map, oracle_problem, problem_for)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [W.small(w) for w in W.ALL]
+IDS = [w.name for w in SMALL]
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+    yield
+    torch.cuda.synchronize()
+
+
+def _inputs(wl):
+    q, k, v = W.make_qkv(wl)
+    return q, k, v, q.to(DEV), k.to(DEV), v.to(DEV)
+
+
+# ---------------------------------------------------------------------------------------
+# pyramid
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("wl", SMALL, ids=IDS)
+def test_pyramid_parity(wl):
+    announce(f"pyramid {wl.name}")
+    q, k, v, qd, kd, vd = _inputs(wl)
+    prob = problem_for(wl, qd, kd, vd)
+    kp, vp = psa.build_pyramid(kd, vd, prob)
+    torch.cuda.synchronize()
+    for name, x, xp in (("k", k, kp), ("v", v, vp)):
+        ref = oracle.pack_pyramid(oracle.as_f64(x))
+        got = xp.double().cpu().numpy()
+        if wl.dtype == "f32":
+            d = np.abs(got - ref)
+            assert d.max() <= 1e-5 * np.abs(ref).max(), name
+            assert np.linalg.norm(got - ref) <= 1e-5 * np.linalg.norm(ref), name
+        else:
+            # bf16 output: the correctly rounded mean, within one bf16 ulp of the exact mean
+            ref_bf = torch.from_numpy(ref).to(torch.float32).to(torch.bfloat16).double().numpy()
+            exact = np.mean(got == ref_bf)
+            ulp = np.abs(ref) * 2.0 ** -7 + 1e-30
+            assert np.all(np.abs(got - ref) <= ulp), name
+            assert exact > 0.999, f"{name}: only {exact:.5f} of pooled values equal RNE(mean)"
+
+
+# ---------------------------------------------------------------------------------------
+# block index
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("shape", [(1, 3, 16, 16), (2, 5, 65, 130), (1, 1, 1, 1), (1, 4, 33, 66)])
+def test_build_index_exact(shape):
+    announce(f"build_index {shape}")
+    rng = np.random.default_rng(sum(shape))
+    lm = rng.choice(np.array([0, 1, 2, 3, -1], dtype=np.int8), size=shape,
+                    p=[0.1, 0.15, 0.2, 0.05, 0.5])
+    if shape[2] > 2:
+        lm[0, 0, 1] = -1      # an all-skip row
+        lm[0, 0, 2] = 2       # a full row at one level
+    B, H, nqb, nkb = shape
+    N = nkb * 64
+    bq = N // nqb if N % nqb == 0 and (N // nqb) in (64, 128) else None
+    if bq is None:
+        pytest.skip("shape not expressible as a problem")
+    q = torch.zeros((B, H, N, 64), device=DEV, dtype=torch.bfloat16)
+    prob = psa.make_problem(q, q, q, block_q=bq)
+    row_ptr, col_idx, err = psa.build_index(torch.from_numpy(lm).to(DEV), prob)
+    rp_ref, ci_ref = oracle.build_index(lm)
+    rp = row_ptr.cpu().numpy()
+    assert np.array_equal(rp, rp_ref)
+    assert np.array_equal(col_idx.cpu().numpy()[:rp[-1]], ci_ref)
+    assert err.item() == 0
+
+
+def test_build_index_flags_bad_entries():
+    announce("build_index bad entries")
+    lm = np.zeros((1, 2, 16, 16), dtype=np.int8)
+    lm[0, 1, 3, 5] = 7
+    lm[0, 0, 0, 0] = -2
+    q = torch.zeros((1, 2, 1024, 64), device=DEV, dtype=torch.bfloat16)
+    prob = psa.make_problem(q, q, q, block_q=64)
+    row_ptr, col_idx, err = psa.build_index(torch.from_numpy(lm).to(DEV), prob)
+    assert err.item() == psa.psa.PSA_ERR_BAD_LEVEL_MAP
+    clean = np.where((lm < -1) | (lm > 3), -1, lm).astype(np.int8)
+    rp_ref, ci_ref = oracle.build_index(clean)
+    assert np.array_equal(row_ptr.cpu().numpy(), rp_ref)
+    assert np.array_equal(col_idx.cpu().numpy()[:rp_ref[-1]], ci_ref)
+
+
+def test_attn_reports_bad_level_map():
+    announce("attn bad level map")
+    wl = W.TINY_F32
+    q, k, v, qd, kd, vd = _inputs(wl)
+    prob = problem_for(wl, qd, kd, vd)
+    kp, vp = psa.build_pyramid(kd, vd, prob)
+    lm = torch.from_numpy(W.make_map(wl)).to(DEV)
+    ws = psa.attn_workspace(prob, DEV)
+    psa.attn_fwd(qd, kd, vd, kp, vp, lm, prob, ws=ws)
+    psa.check_status(ws)
+    lm[0, 0, 0, 1] = 9
+    psa.attn_fwd(qd, kd, vd, kp, vp, lm, prob, ws=ws)
+    with pytest.raises(psa.PsaError):
+        psa.check_status(ws)
+
+
+# ---------------------------------------------------------------------------------------
+# attention on the oracle's maps
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("wl", SMALL, ids=IDS)
+def test_attention_parity(wl):
+    announce(f"attention {wl.name}")
+    q, k, v, qd, kd, vd = _inputs(wl)
+    lm = oracle_map(wl, q, k)
+    prob = problem_for(wl, qd, kd, vd)
+    kp, vp = psa.build_pyramid(kd, vd, prob)
+    o, lse = psa.attn_fwd(qd, kd, vd, kp, vp, torch.from_numpy(lm).to(DEV), prob)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention(q, k, v, lm, oracle_problem(wl))
+    check_attention(o, lse, o_ref, lse_ref, wl.seq_valid, wl.dtype == "f32", wl.name)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d,bq", [(64, 64), (128, 128), (64, 128), (128, 64)])
+def test_attention_shapes(causal, dtype, d, bq):
+    """Every kernel instantiation, with padding, GQA and maps holding every level, including
+    pooled levels on causal diagonal blocks and all-skip rows."""
+    announce(f"attention d={d} bq={bq} {dtype} causal={causal}")
+    wl = W.Workload(name="shape", seed=77, batch=2, heads_q=4, heads_kv=2, head_dim=d,
+                    seq_len=1024, seq_valid=1000, block_q=bq, causal=causal, dtype=dtype,
+                    k_dist="clustered", map_source="iid", map_probs=(0.2, 0.2, 0.2, 0.2, 0.2))
+    q, k, v, qd, kd, vd = _inputs(wl)
+    lm = W.make_map(wl)
+    lm[0, 1, 2] = -1
+    prob = problem_for(wl, qd, kd, vd)
+    kp, vp = psa.build_pyramid(kd, vd, prob)
+    o, lse = psa.attn_fwd(qd, kd, vd, kp, vp, torch.from_numpy(lm).to(DEV), prob)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention(q, k, v, lm, oracle_problem(wl))
+    check_attention(o, lse, o_ref, lse_ref, wl.seq_valid, dtype == "f32", f"shape d{d} bq{bq}")
+
+
+def test_attention_all_l0_matches_sdpa():
+    """An all-L0 map is dense attention: compare with torch SDPA (float32, on the GPU)."""
+    announce("attention all-L0 vs SDPA")
+    wl = W.small(W.WAN13B_32K).replace(seq_valid=2048)
+    q, k, v, qd, kd, vd = _inputs(wl)
+    prob = problem_for(wl, qd, kd, vd)
+    kp, vp = psa.build_pyramid(kd, vd, prob)
+    lm = torch.zeros((1, wl.heads_q, wl.n_qblocks, wl.n_kblocks), dtype=torch.int8, device=DEV)
+    o, _ = psa.attn_fwd(qd, kd, vd, kp, vp, lm, prob)
+    ref = torch.nn.functional.scaled_dot_product_attention(qd.float(), kd.float(), vd.float())
+    err = (o.float() - ref).abs().max().item()
+    assert err < 2e-2, err
+
+
+def test_attention_pad_keys_do_not_leak():
+    """Large values in the pad rows of K and V must not reach any output."""
+    announce("attention pad leak")
+    wl = W.small(W.WAN14B_720P_75K)
+    q, k, v = W.make_qkv(wl)
+    k2, v2 = k.clone(), v.clone()
+    k2[..., wl.seq_valid:, :] = 1e3
+    v2[..., wl.seq_valid:, :] = 1e3
+    lm = W.make_map(wl)
+    qd = q.to(DEV)
+    outs = []
+    for kk, vv in ((k, v), (k2, v2)):
+        kd, vd = kk.to(DEV), vv.to(DEV)
+        prob = problem_for(wl, qd, kd, vd)
+        kp, vp = psa.build_pyramid(kd, vd, prob)
+        o, _ = psa.attn_fwd(qd, kd, vd, kp, vp, torch.from_numpy(lm).to(DEV), prob)
+        outs.append(o)
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_attention_deterministic():
+    announce("attention determinism")
+    wl = W.small(W.QWEN25VL_32K)
+    q, k, v, qd, kd, vd = _inputs(wl)
+    lm = torch.from_numpy(W.make_map(wl.replace(map_source="iid",
+                                                map_probs=(.3, .2, .2, .1, .2)))).to(DEV)
+    prob = problem_for(wl, qd, kd, vd)
+    kp, vp = psa.build_pyramid(kd, vd, prob)
+    o1, l1 = psa.attn_fwd(qd, kd, vd, kp, vp, lm, prob)
+    o2, l2 = psa.attn_fwd(qd, kd, vd, kp, vp, lm, prob)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ---------------------------------------------------------------------------------------
+# threshold assignment, exact
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("causal,force_diag,span,cos,nv", [
+    (False, False, (0, 0), 0.0, 4096),
+    (True, True, (0, 0), 0.8, 4096),
+    (False, True, (3000, 3300), 0.8, 4096),
+    (False, False, (0, 0), 0.0, 3712),     # last query block all padding
+    (True, False, (100, 900), 0.5, 4096),
+])
+def test_mask_assign_exact(causal, force_diag, span, cos, nv):
+    """Dyadic masses (multiples of 2^-20 summing to 1, with ties) make every running sum exact,
+    so the level maps must agree bit for bit."""
+    announce(f"mask_assign causal={causal} diag={force_diag} span={span} cos={cos} nv={nv}")
+    B, H, Hkv, N, bq = 1, 4, 2, 4096, 128
+    nqb, nkb = N // bq, N // 64
+    rng = np.random.default_rng(5)
+    counts = np.stack([rng.multinomial(1 << 20, rng.dirichlet(np.full(nkb, 0.3)))
+                       for _ in range(B * H * nqb)])
+    M = (counts / float(1 << 20)).astype(np.float32).reshape(B, H, nqb, nkb)
+    sim = rng.integers(0, 1 << 10, size=(B, Hkv, nkb)).astype(np.float32) / (1 << 10)
+    sim[..., ::7] = np.float32(0.8)                          # exactly at the bound
+    thr = (0.5, 0.7, 0.8, 0.9)
+    p = oracle.Problem(seq_len=N, seq_valid=nv, head_dim=64, block_q=bq, causal=causal)
+    a = oracle.AssignParams(thr, cos, force_diag, span[0], span[1])
+    ref = np.stack([np.stack([oracle.assign_levels(M[b, h].astype(np.float64),
+                                                   sim[b, h // (H // Hkv)].astype(np.float64) if cos > 0 else None,
+                                                   p, a) for h in range(H)]) for b in range(B)])
+    qd = torch.zeros((B, H, N, 64), device=DEV, dtype=torch.bfloat16)
+    kd = torch.zeros((B, Hkv, N, 64), device=DEV, dtype=torch.bfloat16)
+    prob = psa.make_problem(qd, kd, kd, block_q=bq, causal=causal, seq_valid=nv)
+    mp = psa.MaskParams(thresholds=thr, cos_sim_min=cos, force_diag_l0=force_diag,
+                        force_l0_begin=span[0], force_l0_end=span[1])
+    got = psa.mask_assign(torch.from_numpy(M).to(DEV), torch.from_numpy(sim).to(DEV), prob, mp)
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
+# ---------------------------------------------------------------------------------------
+# mask generator end to end
+# ---------------------------------------------------------------------------------------
+MASKED = [w for w in SMALL if w.map_source == "mask"]
+
+
+@pytest.mark.parametrize("wl", MASKED, ids=[w.name for w in MASKED])
+def test_mask_parity(wl):
+    announce(f"mask {wl.name}")
+    q, k, v, qd, kd, vd = _inputs(wl)
+    p = oracle_problem(wl)
+    a = assign_params(wl)
+    lm_ref, M_ref, sim_ref = oracle.mask(q, k, p, wl.mask_mode, a, samples=wl.samples_per_qblock,
+                                         stride=wl.antidiag_stride)
+    prob = problem_for(wl, qd, kd, vd)
+    lm, M, sim = psa.mask(qd, kd, prob, mask_params(wl))
+    torch.cuda.synchronize()
+    Mg = M.double().cpu().numpy()
+    dM = np.abs(Mg - M_ref)
+    print(f"[{wl.name}] mass max abs diff {dM.max():.3e}", flush=True)
+    assert dM.max() <= 2e-6
+    if sim_ref is not None:
+        ds = np.abs(sim.double().cpu().numpy() - sim_ref)
+        print(f"[{wl.name}] sim max abs diff {ds.max():.3e}", flush=True)
+        assert ds.max() <= 1e-6
+    got = lm.cpu().numpy()
+    diff = got != lm_ref
+    frag = fragile_entries(M_ref, sim_ref, p, a)
+    print(f"[{wl.name}] map entries differing {int(diff.sum())}, fragile {int(frag.sum())} "
+          f"of {diff.size}", flush=True)
+    assert not np.any(diff & ~frag)

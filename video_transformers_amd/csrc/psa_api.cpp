@@ -1,0 +1,276 @@
+// Host side of the C ABI declared in include/psa.h: argument checks (before anything is
+// enqueued), workspace layout, and dispatch to the kernel launchers. No exception crosses the
+// interface; HIP failures map to PSA_ERR_HIP with the hipError_t kept per thread.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "psa.h"
+#include "psa_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return PSA_OK;
+    g_last_hip_error = static_cast<int>(e);
+    return PSA_ERR_HIP;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks a problem and fills the internal shape. Returns PSA_OK or a negative status.
+int check_problem(const psa_problem* p, psa::Shape* s) {
+    if (p == nullptr) return PSA_ERR_INVALID_ARG;
+    if (p->batch < 0 || p->heads_q <= 0 || p->heads_kv <= 0 || p->seq_len < 0 ||
+        p->seq_valid < 0 || p->head_dim <= 0 || p->block_q <= 0 || p->block_k <= 0)
+        return PSA_ERR_INVALID_ARG;
+    if (p->heads_q % p->heads_kv != 0) return PSA_ERR_INVALID_ARG;
+    if (p->seq_valid > p->seq_len) return PSA_ERR_INVALID_ARG;
+    if (p->dtype != PSA_F32 && p->dtype != PSA_BF16) return PSA_ERR_UNSUPPORTED;
+    if (p->head_dim != 64 && p->head_dim != 128) return PSA_ERR_UNSUPPORTED;
+    if (p->block_k != 64) return PSA_ERR_UNSUPPORTED;
+    if (p->block_q != 64 && p->block_q != 128) return PSA_ERR_UNSUPPORTED;
+    if (p->seq_len % p->block_q != 0) return PSA_ERR_UNSUPPORTED;
+    if ((p->seq_len - p->seq_valid) % 8 != 0) return PSA_ERR_UNSUPPORTED;
+    const int64_t* strides[4] = {p->q_stride, p->k_stride, p->v_stride, p->o_stride};
+    for (auto st : strides)
+        for (int i = 0; i < 3; ++i)
+            if (st[i] <= 0 || st[i] % 8 != 0) return PSA_ERR_INVALID_ARG;
+    if (p->q_stride[2] < p->head_dim || p->k_stride[2] < p->head_dim ||
+        p->v_stride[2] < p->head_dim || p->o_stride[2] < p->head_dim)
+        return PSA_ERR_INVALID_ARG;
+    // every index the kernels form per (batch, head) row stays in int32 range
+    const int64_t R = static_cast<int64_t>(p->batch) * p->heads_q * (p->seq_len / p->block_q);
+    if (R * 4 + 1 > INT32_MAX || R * (p->seq_len / 64) > INT32_MAX) return PSA_ERR_UNSUPPORTED;
+    if (s != nullptr) {
+        s->B = p->batch;
+        s->H = p->heads_q;
+        s->Hkv = p->heads_kv;
+        s->N = p->seq_len;
+        s->Nv = p->seq_valid;
+        s->D = p->head_dim;
+        s->BQ = p->block_q;
+        s->BK = p->block_k;
+        s->causal = p->causal != 0;
+        s->dtype = p->dtype;
+        s->NQB = p->seq_len / p->block_q;
+        s->NKB = p->seq_len / p->block_k;
+        for (int i = 0; i < 3; ++i) {
+            s->qs[i] = p->q_stride[i];
+            s->ks[i] = p->k_stride[i];
+            s->vs[i] = p->v_stride[i];
+            s->os[i] = p->o_stride[i];
+        }
+        s->pooled_rows = static_cast<int64_t>(p->seq_len) / 8 * 7;
+    }
+    return PSA_OK;
+}
+
+int check_mask_params(const psa_problem* p, const psa_mask_params* m) {
+    if (m == nullptr) return PSA_ERR_INVALID_ARG;
+    if (m->mode != PSA_MASK_SAMPLING && m->mode != PSA_MASK_ANTIDIAG) return PSA_ERR_INVALID_ARG;
+    float prev = 0.f;
+    for (int i = 0; i < 4; ++i) {
+        const float t = m->thresholds[i];
+        if (!std::isfinite(t) || t <= 0.f || t > 1.f || t < prev) return PSA_ERR_INVALID_ARG;
+        prev = t;
+    }
+    if (!std::isfinite(m->cos_sim_min)) return PSA_ERR_INVALID_ARG;
+    if (m->force_l0_begin < 0 || m->force_l0_end < 0) return PSA_ERR_INVALID_ARG;
+    if (m->force_l0_begin < m->force_l0_end && m->force_l0_end > p->seq_len)
+        return PSA_ERR_INVALID_ARG;
+    if (m->mode == PSA_MASK_SAMPLING) {
+        const int S = m->samples_per_qblock;
+        if (S < 1 || S > p->block_q) return PSA_ERR_INVALID_ARG;
+        // the sampled rows of one query block are reduced inside one half-wave
+        if (S > 32 || (S & (S - 1)) != 0) return PSA_ERR_UNSUPPORTED;
+    } else {
+        const int S = m->antidiag_stride;
+        if (S < 1 || S > 64) return PSA_ERR_INVALID_ARG;
+        // a KV block must span whole 8-column groups and a query block's compressed rows
+        // must fit one half-wave
+        if ((S != 2 && S != 4 && S != 8) || p->block_q / S > 32) return PSA_ERR_UNSUPPORTED;
+    }
+    return PSA_OK;
+}
+
+struct AttnWs {
+    int32_t* dev_err;
+    int32_t* row_ptr;
+    int32_t* col_idx;
+    size_t bytes;
+};
+
+AttnWs attn_ws_layout(const psa::Shape& s, void* base) {
+    const size_t R = static_cast<size_t>(s.B) * s.H * s.NQB;
+    AttnWs w;
+    char* p = static_cast<char*>(base);
+    size_t off = 0;
+    w.dev_err = reinterpret_cast<int32_t*>(p + off);
+    off += kAlign;
+    w.row_ptr = reinterpret_cast<int32_t*>(p + off);
+    off += align_up((R * 4 + 1) * sizeof(int32_t));
+    w.col_idx = reinterpret_cast<int32_t*>(p + off);
+    off += align_up(R * s.NKB * sizeof(int32_t));
+    w.bytes = off;
+    return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t psa_pooled_rows(const psa_problem* prob) {
+    if (check_problem(prob, nullptr) != PSA_OK) return -1;
+    return static_cast<int64_t>(prob->seq_len) / 8 * 7;
+}
+
+int psa_build_pyramid(const psa_problem* prob, const void* k, const void* v, void* k_pooled,
+                      void* v_pooled, void* stream) {
+    psa::Shape s;
+    int rc = check_problem(prob, &s);
+    if (rc != PSA_OK) return rc;
+    if (!k || !v || !k_pooled || !v_pooled) return PSA_ERR_INVALID_ARG;
+    if (!aligned16(k) || !aligned16(v) || !aligned16(k_pooled) || !aligned16(v_pooled))
+        return PSA_ERR_INVALID_ARG;
+    return hip_status(psa::launch_pyramid(s, k, v, k_pooled, v_pooled,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+size_t psa_mask_workspace_bytes(const psa_problem* prob, const psa_mask_params* params) {
+    psa::Shape s;
+    if (check_problem(prob, &s) != PSA_OK || check_mask_params(prob, params) != PSA_OK) return 0;
+    return psa::mask_workspace_bytes(s, *params);
+}
+
+int psa_mask(const psa_problem* prob, const psa_mask_params* params, const void* q,
+             const void* k, int8_t* level_map, float* block_mass, float* block_sim, void* ws,
+             size_t ws_bytes, void* stream) {
+    psa::Shape s;
+    int rc = check_problem(prob, &s);
+    if (rc != PSA_OK) return rc;
+    if ((rc = check_mask_params(prob, params)) != PSA_OK) return rc;
+    if (s.dtype != PSA_BF16) return PSA_ERR_UNSUPPORTED;
+    if (!q || !k || !level_map || !block_mass) return PSA_ERR_INVALID_ARG;
+    if (params->cos_sim_min > 0.f && block_sim == nullptr) return PSA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k)) return PSA_ERR_INVALID_ARG;
+    const size_t need = psa::mask_workspace_bytes(s, *params);
+    if (need > 0 && (ws == nullptr || ws_bytes < need)) return PSA_ERR_WORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    psa::MaskBufs mb{block_mass, block_sim, ws, ws_bytes};
+    hipError_t e = psa::launch_mask_scores(s, *params, q, k, mb, st);
+    if (e != hipSuccess) return hip_status(e);
+    const bool use_sim = params->cos_sim_min > 0.f;
+    if (use_sim) {
+        e = psa::launch_block_sim(s, k, block_sim, st);
+        if (e != hipSuccess) return hip_status(e);
+    }
+    return hip_status(psa::launch_mask_assign(s, *params, block_mass,
+                                              use_sim ? block_sim : nullptr, level_map, st));
+}
+
+int psa_mask_assign(const psa_problem* prob, const psa_mask_params* params,
+                    const float* block_mass, const float* block_sim, int8_t* level_map,
+                    void* stream) {
+    psa::Shape s;
+    int rc = check_problem(prob, &s);
+    if (rc != PSA_OK) return rc;
+    if ((rc = check_mask_params(prob, params)) != PSA_OK) return rc;
+    if (!block_mass || !level_map) return PSA_ERR_INVALID_ARG;
+    const bool use_sim = params->cos_sim_min > 0.f;
+    if (use_sim && block_sim == nullptr) return PSA_ERR_INVALID_ARG;
+    return hip_status(psa::launch_mask_assign(s, *params, block_mass, use_sim ? block_sim : nullptr,
+                                              level_map, static_cast<hipStream_t>(stream)));
+}
+
+int psa_build_index(const psa_problem* prob, const int8_t* level_map, int32_t* row_ptr,
+                    int32_t* col_idx, int32_t* dev_err, void* stream) {
+    psa::Shape s;
+    int rc = check_problem(prob, &s);
+    if (rc != PSA_OK) return rc;
+    if (!level_map || !row_ptr || !col_idx || !dev_err) return PSA_ERR_INVALID_ARG;
+    psa::IndexBufs ib{row_ptr, col_idx, dev_err};
+    return hip_status(psa::launch_build_index(s, level_map, ib, static_cast<hipStream_t>(stream)));
+}
+
+size_t psa_attn_workspace_bytes(const psa_problem* prob) {
+    psa::Shape s;
+    if (check_problem(prob, &s) != PSA_OK) return 0;
+    return attn_ws_layout(s, nullptr).bytes;
+}
+
+int psa_attn_fwd(const psa_problem* prob, float softmax_scale, const void* q, const void* k,
+                 const void* v, const void* k_pooled, const void* v_pooled,
+                 const int8_t* level_map, void* o, float* lse, void* ws, size_t ws_bytes,
+                 void* stream) {
+    psa::Shape s;
+    int rc = check_problem(prob, &s);
+    if (rc != PSA_OK) return rc;
+    if (!q || !k || !v || !k_pooled || !v_pooled || !level_map || !o) return PSA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_pooled) ||
+        !aligned16(v_pooled) || !aligned16(o))
+        return PSA_ERR_INVALID_ARG;
+    if (!std::isfinite(softmax_scale)) return PSA_ERR_INVALID_ARG;
+    const size_t need = attn_ws_layout(s, nullptr).bytes;
+    if (ws == nullptr || ws_bytes < need) return PSA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return PSA_ERR_WORKSPACE;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(s.D));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    AttnWs w = attn_ws_layout(s, ws);
+    psa::IndexBufs ib{w.row_ptr, w.col_idx, w.dev_err};
+    hipError_t e = psa::launch_build_index(s, level_map, ib, st);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(psa::launch_attn_fwd(s, scale, q, k, v, k_pooled, v_pooled, w.row_ptr,
+                                           w.col_idx, o, lse, st));
+}
+
+int psa_attn_fwd_indexed(const psa_problem* prob, float softmax_scale, const void* q,
+                         const void* k, const void* v, const void* k_pooled,
+                         const void* v_pooled, const int32_t* row_ptr, const int32_t* col_idx,
+                         void* o, float* lse, void* stream) {
+    psa::Shape s;
+    int rc = check_problem(prob, &s);
+    if (rc != PSA_OK) return rc;
+    if (!q || !k || !v || !k_pooled || !v_pooled || !row_ptr || !col_idx || !o)
+        return PSA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_pooled) ||
+        !aligned16(v_pooled) || !aligned16(o))
+        return PSA_ERR_INVALID_ARG;
+    if (!std::isfinite(softmax_scale)) return PSA_ERR_INVALID_ARG;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(s.D));
+    return hip_status(psa::launch_attn_fwd(s, scale, q, k, v, k_pooled, v_pooled, row_ptr,
+                                           col_idx, o, lse, static_cast<hipStream_t>(stream)));
+}
+
+int psa_check_status(const void* ws, void* stream) {
+    if (ws == nullptr) return PSA_ERR_INVALID_ARG;
+    hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_status(e);
+    int32_t flag = 0;
+    e = hipMemcpy(&flag, ws, sizeof(flag), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_status(e);
+    return flag == 0 ? PSA_OK : PSA_ERR_BAD_LEVEL_MAP;
+}
+
+const char* psa_status_string(int status) {
+    switch (status) {
+        case PSA_OK: return "PSA_OK";
+        case PSA_ERR_INVALID_ARG: return "PSA_ERR_INVALID_ARG: invalid argument";
+        case PSA_ERR_UNSUPPORTED: return "PSA_ERR_UNSUPPORTED: outside the supported domain";
+        case PSA_ERR_WORKSPACE: return "PSA_ERR_WORKSPACE: workspace missing, misaligned or too small";
+        case PSA_ERR_HIP: return "PSA_ERR_HIP: HIP runtime or launch failure";
+        case PSA_ERR_BAD_LEVEL_MAP: return "PSA_ERR_BAD_LEVEL_MAP: level map entry outside {-1,0,1,2,3}";
+        default: return "unknown psa status";
+    }
+}
+
+int psa_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

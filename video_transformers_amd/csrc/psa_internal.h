@@ -1,0 +1,60 @@
+// Internal interface between the host API (psa_api.cpp) and the kernel translation units.
+// Everything here is in the library's private namespace; only include/psa.h is public.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "psa.h"
+
+namespace psa {
+
+// Shapes and strides of one problem, already validated by the host API.
+struct Shape {
+    int B, H, Hkv, N, Nv, D, BQ, BK, causal, dtype;
+    int NQB, NKB;
+    int64_t qs[3], ks[3], vs[3], os[3];
+    int64_t pooled_rows;  // 7N/8
+};
+
+struct IndexBufs {
+    int32_t* row_ptr;  // [R*4 + 1]
+    int32_t* col_idx;  // [R*NKB]
+    int32_t* dev_err;  // [1]
+};
+
+// ---- launchers (each returns the launch's hipError_t) ----
+
+hipError_t launch_pyramid(const Shape& s, const void* k, const void* v, void* kp, void* vp,
+                          hipStream_t st);
+
+hipError_t launch_build_index(const Shape& s, const int8_t* level_map, const IndexBufs& ib,
+                              hipStream_t st);
+
+hipError_t launch_attn_fwd(const Shape& s, float scale, const void* q, const void* k,
+                           const void* v, const void* kp, const void* vp,
+                           const int32_t* row_ptr, const int32_t* col_idx, void* o, float* lse,
+                           hipStream_t st);
+
+struct MaskBufs {
+    float* block_mass;   // [B,H,NQB,NKB]
+    float* block_sim;    // [B,Hkv,NKB] or null
+    void* ws;
+    size_t ws_bytes;
+};
+
+size_t mask_workspace_bytes(const Shape& s, const psa_mask_params& mp);
+
+hipError_t launch_mask_scores(const Shape& s, const psa_mask_params& mp, const void* q,
+                              const void* k, const MaskBufs& mb, hipStream_t st);
+
+hipError_t launch_block_sim(const Shape& s, const void* k, float* block_sim, hipStream_t st);
+
+hipError_t launch_mask_assign(const Shape& s, const psa_mask_params& mp, const float* block_mass,
+                              const float* block_sim, int8_t* level_map, hipStream_t st);
+
+// Clears one int32 on the device with a kernel (no memset node, so the call stays safe to
+// capture in a graph).
+hipError_t launch_clear_i32(int32_t* p, int n, hipStream_t st);
+
+}  // namespace psa

@@ -1,0 +1,495 @@
+// Multi-level mask generator (PSA summary article at rg.mbintangr.com, "Method": block
+// importance from a sampling-based strategy for generation, antidiagonal scoring with an
+// intra-block similarity check for understanding; "Results": threshold-based assignment and a
+// cosine-similarity constraint on pooling).
+//
+// k_mask_scores  block_mass[b,h,qb,kb]. Rows of a scoring GEMM are either sampled query rows
+//                (sampling mode, S rows per query block) or compressed query rows (antidiagonal
+//                mode, stride S: row r pairs q[rS+S-1-t] with k[cS+t], t < S, summed). One
+//                workgroup owns 128 rows of one (batch, head); it sweeps all 64-column key
+//                tiles twice: pass 0 the row max and sum (online), pass 1 the probabilities,
+//                summed per KV block in-lane and across the rows of each query block with
+//                shuffles. Logits come from v_mfma_f32_32x32x16_bf16 exactly as in the
+//                attention kernel (keys on M, rows on N). No workspace, no atomics.
+// k_block_sim    mean pairwise cosine similarity of each KV block's valid keys, via
+//                sum_{i!=j} khat_i.khat_j = |sum khat|^2 - sum |khat|^2, in float64.
+// k_mask_assign  one workgroup per row: bitonic sort of (mass desc, kb asc) in LDS, then one
+//                lane walks the sorted row with a float64 exclusive running sum (the same
+//                order and precision as a sequential reference), then overrides.
+#include <math.h>
+
+#include "psa_device.h"
+#include "psa_internal.h"
+
+namespace psa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kScoreWaves = 4;
+constexpr int kScoreThreads = 64 * kScoreWaves;
+
+struct ScoreArgs {
+    const bf16_bits* q;
+    const bf16_bits* k;
+    float* M;
+    int H, Hkv, N, Nv, BQ, NQB, NKB, causal;
+    int64_t qs0, qs1, qs2, ks0, ks1, ks2;
+    int rows_per_head;  // sampling: NQB*S; antidiag: N/S
+    int RQ;             // rows per query block: sampling S, antidiag BQ/S
+    int wg_per_head;
+    float c;            // scale * log2(e)
+};
+
+// MODE 0: sampling with S samples per query block; MODE 1: antidiagonal with stride S.
+template <int MODE, int D, int S>
+__global__ void __launch_bounds__(kScoreThreads) k_mask_scores(ScoreArgs a) {
+    constexpr int SI = MODE == 1 ? S : 1;          // inner chunks of D
+    constexpr int CPK = MODE == 1 ? 64 / S : 64;   // columns per KV block
+    constexpr int KT = 64 / CPK;                   // KV blocks per 64-column tile
+    constexpr int KSTR = D + 8;
+    constexpr int KCH = 64 * (D / 8) / kScoreThreads;
+    static_assert(KCH >= 1, "tile");
+    __shared__ __attribute__((aligned(16))) bf16_bits Ks[64 * KSTR];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+    const int bh = blockIdx.x / a.wg_per_head;
+    const int wg = blockIdx.x % a.wg_per_head;
+    const int h = bh % a.H;
+    const int b = bh / a.H;
+    const int hk = h / (a.H / a.Hkv);
+
+    const int r = wg * 128 + wave * 32 + l32;  // 128 rows per workgroup
+    const int r_first = wg * 128;
+    const int r_last = r_first + 127;
+    bool row_ok;
+    int tok = 0;  // sampling: the sampled token
+    if (MODE == 0) {
+        const int qb = r / S;
+        const int s = r % S;
+        const int rv = qb < a.NQB ? min(max(a.Nv - qb * a.BQ, 0), a.BQ) : 0;
+        row_ok = rv > 0;
+        tok = rv > 0 ? qb * a.BQ + (s * rv) / S : 0;
+    } else {
+        row_ok = r < a.rows_per_head && (r * S + S - 1) < a.Nv;
+    }
+
+    const bf16_bits* qbase = a.q + b * a.qs0 + h * a.qs1;
+    const bf16_bits* kbase = a.k + b * a.ks0 + hk * a.ks1;
+
+    bf16x8 qf[D / 16];
+    auto load_q = [&](int t) {
+        const int qt = MODE == 0 ? tok : (row_ok ? r * S + S - 1 - t : 0);
+        const bf16_bits* qp = qbase + static_cast<int64_t>(qt) * a.qs2;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk)
+            qf[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16 + hi * 8);
+    };
+    if (MODE == 0) load_q(0);
+
+    const int ncols = MODE == 0 ? a.N : a.N / S;
+    const int ntiles = ncols / 64;
+    // causal antidiagonal: columns beyond the workgroup's last row are all masked
+    int tiles_needed = ntiles;
+    if (MODE == 1 && a.causal) tiles_needed = min(ntiles, r_last / 64 + 1);
+    if (MODE == 0 && a.causal) {
+        // last sampled token of the workgroup bounds the visible keys
+        const int qb_last = min(r_last / S, a.NQB - 1);
+        tiles_needed = min(ntiles, (qb_last * a.BQ + a.BQ - 1) / 64 + 1);
+    }
+
+    u32x4 kreg[KCH];
+    auto load_k = [&](int j, int t) {
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int cidx = tid + i * kScoreThreads;
+            const int row = cidx / (D / 8);
+            const int col = (cidx % (D / 8)) * 8;
+            const int64_t key = MODE == 0 ? static_cast<int64_t>(j) * 64 + row
+                                          : (static_cast<int64_t>(j) * 64 + row) * S + t;
+            kreg[i] = *reinterpret_cast<const u32x4*>(kbase + key * a.ks2 + col);
+        }
+    };
+    auto store_k = [&]() {
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int cidx = tid + i * kScoreThreads;
+            const int row = cidx / (D / 8);
+            const int col = (cidx % (D / 8)) * 8;
+            *reinterpret_cast<u32x4*>(&Ks[row * KSTR + col]) = kreg[i];
+        }
+    };
+
+    float m_run = -INFINITY, l_run = 0.f, m_ref = 0.f, inv_l = 0.f;
+
+    for (int pass = 0; pass < 2; ++pass) {
+        if (pass == 1) {
+            l_run = pair32_sum(l_run);
+            m_ref = m_run == -INFINITY ? 0.f : m_run;
+            inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
+        }
+        if (tiles_needed > 0) load_k(0, 0);
+        for (int j = 0; j < ntiles; ++j) {
+            if (j >= tiles_needed) {
+                // fully masked tile: contributes nothing; pass 1 still writes its zeros
+                if (pass == 1 && hi == 0 && (l32 % a.RQ) == 0) {
+                    const int qb = r / a.RQ;
+                    if (qb < a.NQB && r < a.rows_per_head) {
+                        float* Mrow = a.M + (static_cast<int64_t>(bh) * a.NQB + qb) * a.NKB;
+#pragma unroll
+                        for (int kt = 0; kt < KT; ++kt) Mrow[j * KT + kt] = 0.f;
+                    }
+                }
+                continue;
+            }
+            f32x16 sacc[2];
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) sacc[kh][e] = 0.f;
+            for (int t = 0; t < SI; ++t) {
+                __syncthreads();
+                store_k();
+                __syncthreads();
+                // prefetch the next (tile, chunk) step
+                {
+                    int nj = j, nt = t + 1;
+                    if (nt == SI) {
+                        nt = 0;
+                        ++nj;
+                    }
+                    if (nj < tiles_needed) load_k(nj, nt);
+                }
+                if (MODE == 1) load_q(t);
+#pragma unroll
+                for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+                    for (int kh = 0; kh < 2; ++kh) {
+                        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
+                            &Ks[(kh * 32 + l32) * KSTR + kk * 16 + hi * 8]);
+                        sacc[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], sacc[kh], 0, 0, 0);
+                    }
+            }
+            // mask
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int cc = j * 64 + kh * 32 + (e >> 2) * 8 + hi * 4 + (e & 3);
+                    bool ok;
+                    if (MODE == 0)
+                        ok = row_ok && cc < a.Nv && (!a.causal || cc <= tok);
+                    else
+                        ok = row_ok && (cc * S + S - 1) < a.Nv && (!a.causal || cc <= r);
+                    if (!ok) sacc[kh][e] = -INFINITY;
+                }
+            if (pass == 0) {
+                float mt = -INFINITY;
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[kh][e]);
+                mt = pair32_max(mt);
+                const float m_new = fmaxf(m_run, mt * a.c);
+                const float mr = m_new == -INFINITY ? 0.f : m_new;
+                l_run *= fast_exp2(m_run - mr);
+                m_run = m_new;
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) l_run += fast_exp2(fmaf(sacc[kh][e], a.c, -mr));
+            } else {
+                float part[KT];
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt) part[kt] = 0.f;
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int kt = (kh * 32 + (e >> 2) * 8) / CPK;
+                        part[kt] += fast_exp2(fmaf(sacc[kh][e], a.c, -m_ref)) * inv_l;
+                    }
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt) {
+                    float x = pair32_sum(part[kt]);
+                    for (int o = 1; o < a.RQ; o <<= 1) x += __shfl_xor(x, o, 64);
+                    part[kt] = x;
+                }
+                if (hi == 0 && (l32 % a.RQ) == 0) {
+                    const int qb = r / a.RQ;
+                    if (qb < a.NQB && r < a.rows_per_head) {
+                        int den;
+                        if (MODE == 0)
+                            den = min(max(a.Nv - qb * a.BQ, 0), a.BQ) > 0 ? S : 0;
+                        else
+                            den = min(max(a.Nv / S - qb * a.RQ, 0), a.RQ);
+                        const float invd = den > 0 ? 1.f / static_cast<float>(den) : 0.f;
+                        float* Mrow = a.M + (static_cast<int64_t>(bh) * a.NQB + qb) * a.NKB;
+#pragma unroll
+                        for (int kt = 0; kt < KT; ++kt) Mrow[j * KT + kt] = part[kt] * invd;
+                    }
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Intra-block key similarity, one wave per (batch, KV head, KV block).
+// ---------------------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256)
+    k_block_sim(const bf16_bits* __restrict__ k, int64_t ks0, int64_t ks1, int64_t ks2, int Hkv,
+                int NKB, int Nv, int64_t items, float* __restrict__ sim) {
+    const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (item >= items) return;
+    const int kb = static_cast<int>(item % NKB);
+    const int bh = static_cast<int>(item / NKB);
+    const int h = bh % Hkv;
+    const int b = bh / Hkv;
+    const int lo = kb * 64;
+    const int nv = min(max(Nv - lo, 0), 64);
+    if (nv < 2) {
+        if (lane == 0) sim[item] = 1.f;
+        return;
+    }
+    // lane t owns key lo + t: its norm, then every lane accumulates head-dim slices of the
+    // normalised sum. Keys >= nv contribute nothing.
+    const bf16_bits* kp = k + b * ks0 + h * ks1;
+    double nrm2 = 0.0;
+    if (lane < nv) {
+        const bf16_bits* row = kp + static_cast<int64_t>(lo + lane) * ks2;
+        for (int e = 0; e < D; ++e) {
+            const double x = bf16_to_f32(row[e]);
+            nrm2 += x * x;
+        }
+    }
+    const double inv = (lane < nv && nrm2 > 0.0) ? 1.0 / sqrt(nrm2) : 0.0;
+    const double self = (lane < nv && nrm2 > 0.0) ? nrm2 * inv * inv : 0.0;
+    const double self_sum = wave_sum_f64(self);
+    // |sum_i khat_i|^2, head-dim element e handled by lane e % 64 over keys
+    double sq = 0.0;
+    for (int e = lane; e < D; e += 64) {
+        double s = 0.0;
+        for (int t = 0; t < nv; ++t) {
+            const double it = __shfl(inv, t, 64);
+            s += static_cast<double>(bf16_to_f32(kp[static_cast<int64_t>(lo + t) * ks2 + e])) * it;
+        }
+        sq += s * s;
+    }
+    sq = wave_sum_f64(sq);
+    if (lane == 0) sim[item] = static_cast<float>((sq - self_sum) / (static_cast<double>(nv) * (nv - 1)));
+}
+
+// ---------------------------------------------------------------------------------------
+// Threshold assignment, one workgroup per (batch, head, query block) row.
+// ---------------------------------------------------------------------------------------
+constexpr int kAssignThreads = 256;
+
+struct AssignArgs {
+    const float* M;
+    const float* sim;
+    int8_t* map;
+    int H, Hkv, N, Nv, BQ, BK, NQB, NKB, causal;
+    int P;  // sort length: power of two >= NKB
+    double t[4];
+    float cos_min;
+    int force_diag, force_lo, force_hi;
+};
+
+__device__ __forceinline__ uint32_t float_order(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__global__ void __launch_bounds__(kAssignThreads) k_mask_assign(AssignArgs a) {
+    extern __shared__ uint64_t keys[];  // P sort keys, then NKB int8 levels
+    int8_t* lvl = reinterpret_cast<int8_t*>(keys + a.P);
+    const int64_t row = blockIdx.x;
+    const int qb = static_cast<int>(row % a.NQB);
+    const int bh = static_cast<int>(row / a.NQB);
+    const int h = bh % a.H;
+    const int b = bh / a.H;
+    const int hk = h / (a.H / a.Hkv);
+    const int tid = threadIdx.x;
+    const float* Mrow = a.M + row * a.NKB;
+    int8_t* out = a.map + row * a.NKB;
+
+    const int qlo = qb * a.BQ, qhi = qlo + a.BQ;
+    const bool any_valid = qlo < a.Nv;
+    const int last = a.causal ? min((qhi - 1) / a.BK, a.NKB - 1) : a.NKB - 1;
+    const int ncand = last + 1;
+
+    for (int i = tid; i < a.P; i += kAssignThreads) {
+        uint64_t key = ~0ull;
+        if (i < ncand) key = (static_cast<uint64_t>(~float_order(Mrow[i])) << 32) | static_cast<uint32_t>(i);
+        keys[i] = key;
+    }
+    for (int i = tid; i < a.NKB; i += kAssignThreads) lvl[i] = -1;
+    __syncthreads();
+    // bitonic sort, ascending keys = mass descending, kb ascending
+    for (int size = 2; size <= a.P; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = tid; i < a.P / 2; i += kAssignThreads) {
+                const int lo = 2 * i - (i & (stride - 1));
+                const int hi = lo + stride;
+                const bool up = ((lo & size) == 0);
+                const uint64_t x = keys[lo], y = keys[hi];
+                if ((x > y) == up) {
+                    keys[lo] = y;
+                    keys[hi] = x;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    if (tid == 0 && any_valid) {
+        double c = 0.0;
+        for (int i = 0; i < ncand; ++i) {
+            const int kb = static_cast<int>(keys[i] & 0xffffffffu);
+            int8_t L = -1;
+            if (c < a.t[0]) L = 0;
+            else if (c < a.t[1]) L = 1;
+            else if (c < a.t[2]) L = 2;
+            else if (c < a.t[3]) L = 3;
+            lvl[kb] = L;
+            c += static_cast<double>(Mrow[kb]);
+        }
+    }
+    __syncthreads();
+    for (int kb = tid; kb < a.NKB; kb += kAssignThreads) {
+        int8_t L = any_valid ? lvl[kb] : static_cast<int8_t>(-1);
+        if (any_valid && kb <= last) {
+            const int klo = kb * a.BK, khi = klo + a.BK;
+            bool forced = a.force_diag && klo < qhi && qlo < khi;
+            if (a.force_lo < a.force_hi &&
+                ((qlo < a.force_hi && a.force_lo < qhi) || (klo < a.force_hi && a.force_lo < khi)))
+                forced = true;
+            if (forced)
+                L = 0;
+            else if (a.sim != nullptr && L > 0 &&
+                     a.sim[(static_cast<int64_t>(b) * a.Hkv + hk) * a.NKB + kb] < a.cos_min)
+                L = 0;
+        }
+        out[kb] = L;
+    }
+}
+
+template <int MODE, int D, int S>
+hipError_t launch_scores(const ScoreArgs& a, int blocks, hipStream_t st) {
+    hipLaunchKernelGGL((k_mask_scores<MODE, D, S>), dim3(blocks), dim3(kScoreThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int MODE, int S>
+hipError_t launch_scores_d(const ScoreArgs& a, int D, int blocks, hipStream_t st) {
+    return D == 128 ? launch_scores<MODE, 128, S>(a, blocks, st)
+                    : launch_scores<MODE, 64, S>(a, blocks, st);
+}
+
+}  // namespace
+
+size_t mask_workspace_bytes(const Shape&, const psa_mask_params&) { return 0; }
+
+hipError_t launch_mask_scores(const Shape& s, const psa_mask_params& mp, const void* q,
+                              const void* k, const MaskBufs& mb, hipStream_t st) {
+    if (s.dtype != PSA_BF16) return hipErrorNotSupported;
+    ScoreArgs a;
+    a.q = static_cast<const bf16_bits*>(q);
+    a.k = static_cast<const bf16_bits*>(k);
+    a.M = mb.block_mass;
+    a.H = s.H;
+    a.Hkv = s.Hkv;
+    a.N = s.N;
+    a.Nv = s.Nv;
+    a.BQ = s.BQ;
+    a.NQB = s.NQB;
+    a.NKB = s.NKB;
+    a.causal = s.causal;
+    a.qs0 = s.qs[0]; a.qs1 = s.qs[1]; a.qs2 = s.qs[2];
+    a.ks0 = s.ks[0]; a.ks1 = s.ks[1]; a.ks2 = s.ks[2];
+    a.c = (1.0f / sqrtf(static_cast<float>(s.D))) * kLog2e;
+    const int S = mp.mode == PSA_MASK_SAMPLING ? mp.samples_per_qblock : mp.antidiag_stride;
+    if (mp.mode == PSA_MASK_SAMPLING) {
+        a.rows_per_head = s.NQB * S;
+        a.RQ = S;
+    } else {
+        a.rows_per_head = s.N / S;
+        a.RQ = s.BQ / S;
+    }
+    a.wg_per_head = (a.rows_per_head + 127) / 128;
+    const int blocks = s.B * s.H * a.wg_per_head;
+    if (blocks == 0) return hipSuccess;
+    if (mp.mode == PSA_MASK_SAMPLING) {
+        switch (S) {
+            case 1: return launch_scores_d<0, 1>(a, s.D, blocks, st);
+            case 2: return launch_scores_d<0, 2>(a, s.D, blocks, st);
+            case 4: return launch_scores_d<0, 4>(a, s.D, blocks, st);
+            case 8: return launch_scores_d<0, 8>(a, s.D, blocks, st);
+            case 16: return launch_scores_d<0, 16>(a, s.D, blocks, st);
+            case 32: return launch_scores_d<0, 32>(a, s.D, blocks, st);
+            default: return hipErrorNotSupported;
+        }
+    }
+    if (a.RQ > 32 || a.RQ < 1) return hipErrorNotSupported;
+    switch (S) {
+        case 2: return launch_scores_d<1, 2>(a, s.D, blocks, st);
+        case 4: return launch_scores_d<1, 4>(a, s.D, blocks, st);
+        case 8: return launch_scores_d<1, 8>(a, s.D, blocks, st);
+        default: return hipErrorNotSupported;
+    }
+}
+
+hipError_t launch_block_sim(const Shape& s, const void* k, float* block_sim, hipStream_t st) {
+    if (s.dtype != PSA_BF16) return hipErrorNotSupported;
+    const int64_t items = static_cast<int64_t>(s.B) * s.Hkv * s.NKB;
+    if (items == 0) return hipSuccess;
+    const unsigned blocks = static_cast<unsigned>((items + 3) / 4);
+    if (s.D == 128)
+        hipLaunchKernelGGL(k_block_sim<128>, dim3(blocks), dim3(256), 0, st,
+                           static_cast<const bf16_bits*>(k), s.ks[0], s.ks[1], s.ks[2], s.Hkv,
+                           s.NKB, s.Nv, items, block_sim);
+    else
+        hipLaunchKernelGGL(k_block_sim<64>, dim3(blocks), dim3(256), 0, st,
+                           static_cast<const bf16_bits*>(k), s.ks[0], s.ks[1], s.ks[2], s.Hkv,
+                           s.NKB, s.Nv, items, block_sim);
+    return hipGetLastError();
+}
+
+hipError_t launch_mask_assign(const Shape& s, const psa_mask_params& mp, const float* block_mass,
+                              const float* block_sim, int8_t* level_map, hipStream_t st) {
+    AssignArgs a;
+    a.M = block_mass;
+    a.sim = mp.cos_sim_min > 0.f ? block_sim : nullptr;
+    a.map = level_map;
+    a.H = s.H;
+    a.Hkv = s.Hkv;
+    a.N = s.N;
+    a.Nv = s.Nv;
+    a.BQ = s.BQ;
+    a.BK = s.BK;
+    a.NQB = s.NQB;
+    a.NKB = s.NKB;
+    a.causal = s.causal;
+    int P = 1;
+    while (P < s.NKB) P <<= 1;
+    a.P = P;
+    for (int i = 0; i < 4; ++i) a.t[i] = static_cast<double>(mp.thresholds[i]);
+    a.cos_min = mp.cos_sim_min;
+    a.force_diag = mp.force_diag_l0 != 0;
+    a.force_lo = mp.force_l0_begin;
+    a.force_hi = mp.force_l0_end;
+    const int64_t rows = static_cast<int64_t>(s.B) * s.H * s.NQB;
+    if (rows == 0) return hipSuccess;
+    const size_t lds = static_cast<size_t>(P) * sizeof(uint64_t) + static_cast<size_t>(s.NKB);
+    if (lds > 64 * 1024) return hipErrorNotSupported;
+    hipLaunchKernelGGL(k_mask_assign, dim3(static_cast<unsigned>(rows)), dim3(kAssignThreads),
+                       lds, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace psa

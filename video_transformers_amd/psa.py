@@ -1,0 +1,286 @@
+"""Thin ctypes binding of libpsa (include/psa.h): argument marshalling only.
+
+Every step of the Pyramid Sparse Attention forward path runs in the library's HIP kernels;
+torch supplies device memory and the current HIP stream and nothing else. If the library is
+not built, every entry point raises (there is no fallback).
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpsa.so")
+
+PSA_OK = 0
+PSA_ERR_INVALID_ARG = -1
+PSA_ERR_UNSUPPORTED = -2
+PSA_ERR_WORKSPACE = -3
+PSA_ERR_HIP = -4
+PSA_ERR_BAD_LEVEL_MAP = -5
+PSA_F32 = 0
+PSA_BF16 = 1
+PSA_MASK_SAMPLING = 0
+PSA_MASK_ANTIDIAG = 1
+SKIP = -1
+
+# every symbol include/psa.h declares
+EXPORTS = ("psa_pooled_rows", "psa_build_pyramid", "psa_mask_workspace_bytes", "psa_mask",
+           "psa_mask_assign", "psa_build_index", "psa_attn_workspace_bytes", "psa_attn_fwd",
+           "psa_attn_fwd_indexed", "psa_check_status", "psa_status_string", "psa_last_hip_error")
+
+
+class PsaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().psa_status_string(status).decode()
+        if status == PSA_ERR_HIP:
+            msg += f" (hipError_t {lib().psa_last_hip_error()})"
+        super().__init__(f"{where}: {msg}")
+
+
+class CProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32),
+                ("heads_kv", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("seq_valid", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32),
+                ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
+                ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3)]
+
+
+class CMaskParams(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("thresholds", ctypes.c_float * 4),
+                ("samples_per_qblock", ctypes.c_int32), ("antidiag_stride", ctypes.c_int32),
+                ("cos_sim_min", ctypes.c_float), ("force_diag_l0", ctypes.c_int32),
+                ("force_l0_begin", ctypes.c_int32), ("force_l0_end", ctypes.c_int32)]
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libpsa.so once (after torch, so both bind the same HIP runtime)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m video_transformers_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, V, I32, I64, SZ = (ctypes.POINTER(CProblem), ctypes.c_void_p, ctypes.c_int,
+                              ctypes.c_int64, ctypes.c_size_t)
+        MP = ctypes.POINTER(CMaskParams)
+        L.psa_pooled_rows.argtypes, L.psa_pooled_rows.restype = [P], I64
+        L.psa_build_pyramid.argtypes, L.psa_build_pyramid.restype = [P, V, V, V, V, V], I32
+        L.psa_mask_workspace_bytes.argtypes, L.psa_mask_workspace_bytes.restype = [P, MP], SZ
+        L.psa_mask.argtypes, L.psa_mask.restype = [P, MP, V, V, V, V, V, V, SZ, V], I32
+        L.psa_mask_assign.argtypes, L.psa_mask_assign.restype = [P, MP, V, V, V, V], I32
+        L.psa_build_index.argtypes, L.psa_build_index.restype = [P, V, V, V, V, V], I32
+        L.psa_attn_workspace_bytes.argtypes, L.psa_attn_workspace_bytes.restype = [P], SZ
+        L.psa_attn_fwd.argtypes = [P, ctypes.c_float, V, V, V, V, V, V, V, V, V, SZ, V]
+        L.psa_attn_fwd.restype = I32
+        L.psa_attn_fwd_indexed.argtypes = [P, ctypes.c_float, V, V, V, V, V, V, V, V, V, V]
+        L.psa_attn_fwd_indexed.restype = I32
+        L.psa_check_status.argtypes, L.psa_check_status.restype = [V, V], I32
+        L.psa_status_string.argtypes, L.psa_status_string.restype = [I32], ctypes.c_char_p
+        L.psa_last_hip_error.argtypes, L.psa_last_hip_error.restype = [], I32
+        _LIB = L
+    return _LIB
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != PSA_OK:
+        raise PsaError(rc, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return PSA_BF16
+    if dt == torch.float32:
+        return PSA_F32
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+@dataclasses.dataclass
+class Problem:
+    """A psa_problem built from Q [B,H,N,d], K/V [B,Hkv,N,d] (and O) tensors."""
+    c: CProblem
+
+    @property
+    def n_qblocks(self) -> int:
+        return self.c.seq_len // self.c.block_q
+
+    @property
+    def n_kblocks(self) -> int:
+        return self.c.seq_len // self.c.block_k
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def make_problem(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                 o: Optional[torch.Tensor] = None, *, block_q: int, block_k: int = 64,
+                 causal: bool = False, seq_valid: Optional[int] = None) -> Problem:
+    for name, t in (("q", q), ("k", k), ("v", v)) + ((("o", o),) if o is not None else ()):
+        if t.dim() != 4 or t.stride(-1) != 1:
+            raise ValueError(f"{name} must be [batch, heads, tokens, head_dim] with a contiguous head_dim")
+    B, H, N, d = q.shape
+    o = q if o is None else o
+    c = CProblem()
+    c.batch, c.heads_q, c.heads_kv, c.seq_len = B, H, k.shape[1], N
+    c.seq_valid = N if seq_valid is None else int(seq_valid)
+    c.head_dim, c.block_q, c.block_k = d, block_q, block_k
+    c.causal = 1 if causal else 0
+    c.dtype = _dtype_code(q.dtype)
+    for arr, t in ((c.q_stride, q), (c.k_stride, k), (c.v_stride, v), (c.o_stride, o)):
+        arr[0], arr[1], arr[2] = t.stride(0), t.stride(1), t.stride(2)
+    return Problem(c)
+
+
+@dataclasses.dataclass
+class MaskParams:
+    mode: str = "sampling"                 # "sampling" | "antidiag"
+    thresholds: Sequence[float] = (0.5, 0.7, 0.8, 0.9)
+    samples_per_qblock: int = 8
+    antidiag_stride: int = 8
+    cos_sim_min: float = 0.0
+    force_diag_l0: bool = False
+    force_l0_begin: int = 0
+    force_l0_end: int = 0
+
+    def c(self) -> CMaskParams:
+        m = CMaskParams()
+        m.mode = PSA_MASK_SAMPLING if self.mode == "sampling" else PSA_MASK_ANTIDIAG
+        for i, t in enumerate(self.thresholds):
+            m.thresholds[i] = float(t)
+        m.samples_per_qblock = self.samples_per_qblock
+        m.antidiag_stride = self.antidiag_stride
+        m.cos_sim_min = float(self.cos_sim_min)
+        m.force_diag_l0 = 1 if self.force_diag_l0 else 0
+        m.force_l0_begin = self.force_l0_begin
+        m.force_l0_end = self.force_l0_end
+        return m
+
+
+def pooled_rows(prob: Problem) -> int:
+    n = lib().psa_pooled_rows(prob.ref())
+    if n < 0:
+        raise PsaError(PSA_ERR_INVALID_ARG, "psa_pooled_rows")
+    return n
+
+
+def build_pyramid(k: torch.Tensor, v: torch.Tensor, prob: Problem,
+                  out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None, stream=None):
+    """Levels 1..3 of K and V packed as [B, Hkv, 7N/8, d] (level l at row N - 2N/2^l)."""
+    B, Hkv, _, d = k.shape
+    if out is None:
+        shape = (B, Hkv, pooled_rows(prob), d)
+        out = (torch.empty(shape, dtype=k.dtype, device=k.device),
+               torch.empty(shape, dtype=v.dtype, device=v.device))
+    kp, vp = out
+    _check(lib().psa_build_pyramid(prob.ref(), _ptr(k), _ptr(v), _ptr(kp), _ptr(vp),
+                                   _stream(stream)), "psa_build_pyramid")
+    return kp, vp
+
+
+def mask(q: torch.Tensor, k: torch.Tensor, prob: Problem, params: MaskParams, stream=None):
+    """Returns (level_map int8 [B,H,NQB,NKB], block_mass f32 [B,H,NQB,NKB], block_sim or None)."""
+    B, H = q.shape[:2]
+    Hkv = k.shape[1]
+    nqb, nkb = prob.n_qblocks, prob.n_kblocks
+    cp = params.c()
+    lm = torch.empty((B, H, nqb, nkb), dtype=torch.int8, device=q.device)
+    mass = torch.empty((B, H, nqb, nkb), dtype=torch.float32, device=q.device)
+    sim = (torch.empty((B, Hkv, nkb), dtype=torch.float32, device=q.device)
+           if params.cos_sim_min > 0 else None)
+    nbytes = lib().psa_mask_workspace_bytes(prob.ref(), ctypes.byref(cp))
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().psa_mask(prob.ref(), ctypes.byref(cp), _ptr(q), _ptr(k), _ptr(lm), _ptr(mass),
+                          _ptr(sim), _ptr(ws), nbytes, _stream(stream)), "psa_mask")
+    return lm, mass, sim
+
+
+def mask_assign(block_mass: torch.Tensor, block_sim: Optional[torch.Tensor], prob: Problem,
+                params: MaskParams, stream=None) -> torch.Tensor:
+    cp = params.c()
+    lm = torch.empty(block_mass.shape, dtype=torch.int8, device=block_mass.device)
+    _check(lib().psa_mask_assign(prob.ref(), ctypes.byref(cp), _ptr(block_mass), _ptr(block_sim),
+                                 _ptr(lm), _stream(stream)), "psa_mask_assign")
+    return lm
+
+
+def build_index(level_map: torch.Tensor, prob: Problem, stream=None):
+    """Returns (row_ptr int32 [R*4+1], col_idx int32 [R*NKB] (prefix valid), dev_err int32 [1])."""
+    rows = level_map.numel() // prob.n_kblocks
+    dev = level_map.device
+    row_ptr = torch.empty(rows * 4 + 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(max(rows * prob.n_kblocks, 1), dtype=torch.int32, device=dev)
+    dev_err = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(lib().psa_build_index(prob.ref(), _ptr(level_map), _ptr(row_ptr), _ptr(col_idx),
+                                 _ptr(dev_err), _stream(stream)), "psa_build_index")
+    return row_ptr, col_idx, dev_err
+
+
+def attn_workspace(prob: Problem, device) -> torch.Tensor:
+    n = lib().psa_attn_workspace_bytes(prob.ref())
+    if n == 0:
+        raise PsaError(PSA_ERR_INVALID_ARG, "psa_attn_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def attn_fwd(q, k, v, k_pooled, v_pooled, level_map, prob: Problem, *, scale: float = 0.0,
+             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+             want_lse: bool = True, ws: Optional[torch.Tensor] = None, stream=None):
+    """Level-weighted attention. Returns (o, lse or None). `out` must match the problem's
+    o_stride (make_problem(..., o=out)); by default o is allocated like q."""
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = attn_workspace(prob, q.device)
+    _check(lib().psa_attn_fwd(prob.ref(), ctypes.c_float(scale), _ptr(q), _ptr(k), _ptr(v),
+                              _ptr(k_pooled), _ptr(v_pooled), _ptr(level_map), _ptr(out),
+                              _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)), "psa_attn_fwd")
+    return out, lse
+
+
+def attn_fwd_indexed(q, k, v, k_pooled, v_pooled, row_ptr, col_idx, prob: Problem, *,
+                     scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                     lse: Optional[torch.Tensor] = None, want_lse: bool = True, stream=None):
+    """attn_fwd on an index from build_index. Returns (o, lse or None)."""
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    _check(lib().psa_attn_fwd_indexed(prob.ref(), ctypes.c_float(scale), _ptr(q), _ptr(k),
+                                      _ptr(v), _ptr(k_pooled), _ptr(v_pooled), _ptr(row_ptr),
+                                      _ptr(col_idx), _ptr(out), _ptr(lse), _stream(stream)),
+           "psa_attn_fwd_indexed")
+    return out, lse
+
+
+def check_status(ws: torch.Tensor, stream=None) -> None:
+    _check(lib().psa_check_status(_ptr(ws), _stream(stream)), "psa_check_status")
+
+
+def forward(q, k, v, *, block_q: int, params: MaskParams, causal: bool = False,
+            seq_valid: Optional[int] = None, scale: float = 0.0):
+    """The whole path: pyramid, mask, attention. Returns (o, lse, level_map)."""
+    prob = make_problem(q, k, v, block_q=block_q, causal=causal, seq_valid=seq_valid)
+    kp, vp = build_pyramid(k, v, prob)
+    lm, _, _ = mask(q, k, prob, params)
+    o, lse = attn_fwd(q, k, v, kp, vp, lm, prob, scale=scale)
+    return o, lse, lm
