@@ -20,8 +20,9 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpsa.so")
 
-SOURCES = ["psa_api.cpp", "psa_pyramid.hip", "psa_index.hip", "psa_attn.hip", "psa_mask.hip"]
-HEADERS = ["psa_internal.h", "psa_device.h"]
+SOURCES = ["psa_api.cpp", "psa_pyramid.hip", "psa_index.hip", "psa_attn.hip", "psa_attn_bf16.hip",
+           "psa_mask.hip"]
+HEADERS = ["psa_internal.h", "psa_device.h", "psa_attn_common.h"]
 
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are disabled for every device compile: the compiler then never
@@ -29,6 +30,13 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-result"] + DEVICE_FLAGS
+# Per-source extras. The bf16 attention kernel keeps its MFMA accumulators in VGPRs (the
+# online-softmax rescale is VALU work on them; AGPRs then only hold spilled operands), and
+# is compiled without NaN semantics so that max reductions of MFMA results need no
+# canonicalisation (the kernel masks with -inf, never with NaN; infinities keep their meaning).
+EXTRA = {
+    "psa_attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
+}
 
 
 def hipcc() -> str:
@@ -41,7 +49,7 @@ def hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + CFLAGS
+    cmd = [hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + CFLAGS + EXTRA.get(src, [])
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

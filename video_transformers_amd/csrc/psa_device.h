@@ -29,9 +29,20 @@ __device__ __forceinline__ bf16_bits f32_to_bf16(float f) {
     return static_cast<bf16_bits>(u >> 16);
 }
 
-// Two floats -> two packed bf16 (RNE) in one dword, low half = a.
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> two packed bf16 in one dword, low half = a: one v_cvt_pk_bf16_f32
+// (round to nearest even).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_hw));
+}
+
+// acc + lo(x) + hi(x) for a dword holding two bf16 values (one v_dot2c_f32_bf16 with 1.0).
+__device__ __forceinline__ float add_bf16x2(uint32_t x, float acc) {
+    const bf16x2_hw one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_hw, x), one, acc, false);
 }
 
 // max / sum of a value across lane l and lane l^32 of the wave: after v_permlane32_swap of
