@@ -36,7 +36,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, GB/s
 METRIC = "psa_attn_fwd ms/layer + effective TFLOP/s (% bf16 MFMA peak), Wan-like 32k"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_fwd_bf16_traffic.txt")
-ATTN_SOURCE = os.path.join(ROOT, "video_transformers_amd", "csrc", "psa_attn.hip")
+ATTN_SOURCE = os.path.join(ROOT, "video_transformers_amd", "csrc", "psa_attn_bf16.hip")
 
 
 # ---------------------------------------------------------------------------------------
@@ -265,6 +265,21 @@ def run(args) -> dict:
             for a, c in zip(lv, cnt)}
 
     # same kernel, all-level-0 map (causal: the lower triangle)
+    dense_ms = float("nan")
+    if not args.no_dense:
+        dense_ms = _dense_run(args, wl, prob, L, ptr, st, check, q, k, v, kp, vp, o, lse,
+                              row_ptr, col_idx, dev_err, stream)
+    return _report(args, wl, flops, pairs, dpairs, frac, d, B, H, N, computed_map, attn_ms,
+                   attn_ms_mean, st_ms, dense_ms, wall)
+
+
+def _dense_run(args, wl, prob, L, ptr, st, check, q, k, v, kp, vp, o, lse, row_ptr, col_idx,
+               dev_err, stream):
+    import ctypes
+    import torch
+    B, H, N, d = q.shape
+    nqb, nkb = wl.n_qblocks, wl.n_kblocks
+    dev = q.device
     dense = torch.zeros((B, H, nqb, nkb), dtype=torch.int8, device=dev)
     if wl.causal:
         qb_i = torch.arange(nqb, device=dev)[:, None]
@@ -283,8 +298,11 @@ def run(args) -> dict:
         de[1].record(stream)
         torch.cuda.synchronize()
         times.append(de[0].elapsed_time(de[1]))
-    dense_ms = float(np.median(times[1:]))
+    return float(np.median(times[1:]))
 
+
+def _report(args, wl, flops, pairs, dpairs, frac, d, B, H, N, computed_map, attn_ms,
+            attn_ms_mean, st_ms, dense_ms, wall):
     ms_per_step = wall * 1e3 / args.steps
     attn_tflops = flops / (attn_ms_mean * 1e-3) / 1e12
     traffic = _traffic_from_profile()
@@ -309,9 +327,10 @@ def run(args) -> dict:
         "attn": {"ms_per_layer_median": round(attn_ms, 4), "ms_per_layer_mean": round(attn_ms_mean, 4),
                  "tflops_executed": round(attn_tflops, 2),
                  "pct_bf16_peak": round(100 * attn_tflops / PEAK_BF16_TFLOPS, 2),
-                 "dense_same_kernel_ms": round(dense_ms, 3),
-                 "speedup_vs_dense": round(dense_ms / attn_ms_mean, 2),
-                 "dense_tflops": round(4.0 * d * dpairs / (dense_ms * 1e-3) / 1e12, 2),
+                 "dense_same_kernel_ms": None if dense_ms != dense_ms else round(dense_ms, 3),
+                 "speedup_vs_dense": None if dense_ms != dense_ms else round(dense_ms / attn_ms_mean, 2),
+                 "dense_tflops": (None if dense_ms != dense_ms
+                                  else round(4.0 * d * dpairs / (dense_ms * 1e-3) / 1e12, 2)),
                  "executed_pairs": pairs,
                  "effective_sparsity": round(1.0 - pairs / dpairs, 4),
                  "level_fractions": frac},
@@ -333,6 +352,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=W.WAN13B_32K.name, choices=sorted(W.BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the all-level-0 comparison run (for profiling the PSA launches alone)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

@@ -46,6 +46,12 @@ int check_problem(const psa_problem* p, psa::Shape* s) {
     if (p->q_stride[2] < p->head_dim || p->k_stride[2] < p->head_dim ||
         p->v_stride[2] < p->head_dim || p->o_stride[2] < p->head_dim)
         return PSA_ERR_INVALID_ARG;
+    // byte offsets inside one (batch, head) of K, V or one pooled level stay below 2^31
+    const int64_t elem = p->dtype == PSA_BF16 ? 2 : 4;
+    if ((static_cast<int64_t>(p->seq_len) * p->k_stride[2] + p->head_dim) * elem >= (int64_t(1) << 31) ||
+        (static_cast<int64_t>(p->seq_len) * p->v_stride[2] + p->head_dim) * elem >= (int64_t(1) << 31) ||
+        static_cast<int64_t>(p->seq_len) * p->head_dim * elem >= (int64_t(1) << 31))
+        return PSA_ERR_UNSUPPORTED;
     // every index the kernels form per (batch, head) row stays in int32 range
     const int64_t R = static_cast<int64_t>(p->batch) * p->heads_q * (p->seq_len / p->block_q);
     if (R * 4 + 1 > INT32_MAX || R * (p->seq_len / 64) > INT32_MAX) return PSA_ERR_UNSUPPORTED;

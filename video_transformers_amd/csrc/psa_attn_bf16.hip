@@ -17,9 +17,11 @@
 //
 // Math per wave (queries on the MFMA N axis, so each lane owns one query):
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = Q (registers, whole
-//    row). K rows are stored in LDS with bits 2 and 3 of the row index swapped; then the 16
+//    row). A-operand row r reads the tile key sigma(r) (bits 2 and 3 of r swapped); then the 16
 //    accumulator values a lane holds for MFMA j of the P V product are 8 consecutive keys,
-//    16j + 8*(lane/32) + e, so P needs no shuffling.
+//    16j + 8*(lane/32) + e, so P needs no shuffling. K and V sit in LDS in natural key order,
+//    so every 1 KB direct load covers consecutive keys of one logical block: its block offset
+//    is wave-uniform (an SGPR base) and each lane's offset inside it is fixed per kernel.
 //  * Online softmax in the exp2 domain, per lane (one query) plus one v_permlane32_swap; the
 //    level term folds into the exp2 offset: p = exp2(s*c + (l - m)). The running max is
 //    refreshed lazily: the accumulators are rescaled only when a tile's max exceeds the one in
@@ -29,6 +31,8 @@
 //    Both query groups of a wave share every K and V operand read (64 FLOP per LDS byte).
 //  * LDS tiles are XOR-swizzled per row at 16-byte granularity so the operand reads are free of
 //    bank conflicts.
+#include <stdlib.h>
+
 #include "psa_attn_common.h"
 
 namespace psa {
@@ -74,7 +78,7 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
         : "memory");
 }
 
-// K tile row r holds tile key sigma(r): bits 2 and 3 of r swapped.
+// The K tile row that MFMA A-operand row r reads: bits 2 and 3 of r swapped.
 __device__ __forceinline__ int sigma(int r) {
     return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
@@ -86,18 +90,20 @@ struct Tile {
     int cnt;   // blocks present in the tile (<= 2^l)
 };
 
-template <int D, int BQ>
-__global__ void __launch_bounds__(BQ) k_attn_fwd_bf16(AttnArgs a, int total_rows) {
-    constexpr int NW = BQ / 64;
+// G: query groups of 32 per wave (1 or 2). G = 2 shares every LDS operand read between two
+// groups at one wave per SIMD; G = 1 halves the registers so two waves share each SIMD.
+template <int D, int BQ, int G>
+__global__ void __launch_bounds__(2 * BQ / G, 3 - G) k_attn_fwd_bf16(AttnArgs a, int total_rows) {
+    constexpr int NW = BQ / (32 * G);
     using LY = Lay<D>;
     constexpr int IPW = LY::INSTR / NW;  // direct-load instructions per wave per tensor
     __shared__ __attribute__((aligned(1024))) bf16_bits Kt[2][64 * D];
     __shared__ __attribute__((aligned(1024))) bf16_bits Vt[2][64 * D];
-    extern __shared__ int cols[];
+    extern __shared__ int cols[];   // the row's block list (LDS reads do not wait on vmcnt)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps tile math scalar
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 
@@ -126,36 +132,40 @@ __global__ void __launch_bounds__(BQ) k_attn_fwd_bf16(AttnArgs a, int total_rows
     for (int i = tid; i < lb4; i += BQ) cols[i] = a.col_idx[r0 + i];
 
     const int blk_first = qb * BQ;
-    const int qbase = blk_first + wave * 64;
+    const int qbase = blk_first + wave * 32 * G;
     const int min_limit = a.causal ? min(blk_first, a.Nv - 1) : a.Nv - 1;
     const bool any_valid_query = blk_first < a.Nv;
 
     // ---- Q fragments: two groups of 32 queries ----
-    bf16x8 qf[2][D / 16];
+    bf16x8 qf[G][D / 16];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    for (int g = 0; g < G; ++g) {
         const bf16_bits* qp = Q + b * a.qs0 + h * a.qs1 +
                               static_cast<int64_t>(qbase + g * 32 + l32) * a.qs2;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk)
             qf[g][kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16 + hi * 8);
     }
-    int limit[2];
+    int limit[G];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    for (int g = 0; g < G; ++g) {
         const int qt = qbase + g * 32 + l32;
         limit[g] = a.causal ? min(qt, a.Nv - 1) : a.Nv - 1;
     }
 
-    f32x16 oacc[2][D / 32];
+    f32x16 oacc[G][D / 32];
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+    for (int g = 0; g < G; ++g)
 #pragma unroll
         for (int i = 0; i < D / 32; ++i)
 #pragma unroll
             for (int e = 0; e < 16; ++e) oacc[g][i][e] = 0.f;
-    float m_use[2] = {-INFINITY, -INFINITY};
-    float l_run[2] = {0.f, 0.f};
+    float m_use[G], l_run[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        m_use[g] = -INFINITY;
+        l_run[g] = 0.f;
+    }
 
     const int64_t kbase = b * a.ks0 + hk * a.ks1;
     const int64_t vbase = b * a.vs0 + hk * a.vs1;
@@ -183,52 +193,65 @@ __global__ void __launch_bounds__(BQ) k_attn_fwd_bf16(AttnArgs a, int total_rows
         return n;
     };
 
-    // Issue the direct loads of tile t into buffer `buf`. Per tile the source base and row
-    // stride are uniform (level 0 reads K/V, levels 1..3 the packed pooled tensors); per lane
-    // only the block of its row (one LDS read of the list) and the row offset vary.
+    // Issue the direct loads of tile t into buffer `buf`. Instruction m fills LDS rows
+    // [m*RPI, (m+1)*RPI): consecutive keys of one logical block, so its block offset is
+    // uniform and folds into the SGPR base; the lane offsets (row inside the instruction,
+    // swizzled chunk) depend only on the row stride (level 0 or pooled) and, for K, on m.
+    constexpr int KVAR = D == 128 ? 4 : 2;   // distinct K chunk swizzles across instructions
+    static_assert(IPW % KVAR == 0, "instruction m and its index inside the wave agree mod KVAR");
+    uint32_t lpk[2][KVAR], lpv[2];
+    {
+        const uint32_t st[2] = {static_cast<uint32_t>(a.ks2) * 2u, static_cast<uint32_t>(D) * 2u};
+        const uint32_t sv[2] = {static_cast<uint32_t>(a.vs2) * 2u, static_cast<uint32_t>(D) * 2u};
+        const int rr = lane / LY::CH;   // row inside the instruction
+        const int p = lane % LY::CH;    // LDS chunk position
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+#pragma unroll
+            for (int q = 0; q < KVAR; ++q)
+                lpk[i][q] = rr * st[i] + static_cast<uint32_t>((p ^ LY::fk(q * LY::RPI + rr)) << 4);
+            lpv[i] = rr * sv[i] + static_cast<uint32_t>((p ^ LY::fv(rr)) << 4);
+        }
+    }
     // LDS byte offsets of the tile buffers (32-bit local-address-space pointers)
-    const uint32_t lds_k[2] = {static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Kt[0][0])),
-                               static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Kt[1][0]))};
-    const uint32_t lds_v[2] = {static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Vt[0][0])),
-                               static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Vt[1][0]))};
+    const uint32_t lds_k0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Kt[0][0]));
+    const uint32_t lds_v0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Vt[0][0]));
+    constexpr uint32_t kBufBytes = 64 * D * 2;
     auto issue = [&](const Tile& t, int buf) {
         const int l = t.l;
         const int rs = 64 >> l;
         const int sh = 6 - l;
+        const int pooled = l > 0 ? 1 : 0;
         const int64_t lvl_off = static_cast<int64_t>(a.N) - (static_cast<int64_t>(a.N) >> (l > 0 ? l - 1 : 0));
-        const bf16_bits* kb_base = l == 0 ? K + kbase : KP + pbase + lvl_off * D;
-        const bf16_bits* vb_base = l == 0 ? V + vbase : VP + pbase + lvl_off * D;
+        const char* kb_base = reinterpret_cast<const char*>(l == 0 ? K + kbase : KP + pbase + lvl_off * D);
+        const char* vb_base = reinterpret_cast<const char*>(l == 0 ? V + vbase : VP + pbase + lvl_off * D);
+        // byte offsets inside one (batch, head) of one level fit 32 bits (checked on the host)
         const uint32_t kstride = static_cast<uint32_t>(l == 0 ? a.ks2 : D) * 2u;  // bytes per row
         const uint32_t vstride = static_cast<uint32_t>(l == 0 ? a.vs2 : D) * 2u;
-        const uint32_t kblk = kstride * rs;  // bytes per logical block
-        const uint32_t vblk = vstride * rs;
-        const int cbase = t.base;
+        const uint32_t kblk = kstride * static_cast<uint32_t>(rs);  // bytes per logical block
+        const uint32_t vblk = vstride * static_cast<uint32_t>(rs);
         const int clast = t.cnt - 1;
-        const uint32_t lk = buf ? lds_k[1] : lds_k[0];
-        const uint32_t lv = buf ? lds_v[1] : lds_v[0];
-        int kbk[IPW], kbv[IPW];
+        const uint32_t lk = lds_k0 + (buf ? kBufBytes : 0u);
+        const uint32_t lv = lds_v0 + (buf ? kBufBytes : 0u);
+        uint32_t lk_lane[KVAR];
+#pragma unroll
+        for (int q = 0; q < KVAR; ++q) lk_lane[q] = pooled ? lpk[1][q] : lpk[0][q];
+        const uint32_t lv_lane = pooled ? lpv[1] : lpv[0];
+        // every block index first (LDS reads + readfirstlane), then the loads
+        int kbs[IPW];
 #pragma unroll
         for (int mi = 0; mi < IPW; ++mi) {
-            const int r = (wave * IPW + mi) * LY::RPI + lane / LY::CH;
-            kbk[mi] = cols[cbase + min(sigma(r) >> sh, clast)];
-            kbv[mi] = cols[cbase + min(r >> sh, clast)];
+            const int key0 = (wave * IPW + mi) * LY::RPI;   // first tile key of the instruction
+            const int s = min(key0 >> sh, clast);           // its logical block (absent -> last)
+            kbs[mi] = __builtin_amdgcn_readfirstlane(cols[t.base + s]);
         }
 #pragma unroll
         for (int mi = 0; mi < IPW; ++mi) {
             const int m = wave * IPW + mi;
-            const int r = m * LY::RPI + lane / LY::CH;   // LDS row this lane fills
-            const int p = lane % LY::CH;                 // LDS chunk position
-            // K: row r holds tile key sigma(r); position p holds logical chunk p ^ fk(r)
-            const int tk = sigma(r);
-            const uint32_t ko = static_cast<uint32_t>(kbk[mi]) * kblk +
-                                static_cast<uint32_t>(tk & (rs - 1)) * kstride +
-                                static_cast<uint32_t>((p ^ LY::fk(r)) << 4);
-            dma16(kb_base, ko, lk + m * 1024);
-            // V: row r holds tile key r; position p holds logical chunk p ^ fv(r)
-            const uint32_t vo = static_cast<uint32_t>(kbv[mi]) * vblk +
-                                static_cast<uint32_t>(r & (rs - 1)) * vstride +
-                                static_cast<uint32_t>((p ^ LY::fv(r)) << 4);
-            dma16(vb_base, vo, lv + m * 1024);
+            const uint32_t rin = static_cast<uint32_t>((m * LY::RPI) & (rs - 1));
+            const uint32_t kb = static_cast<uint32_t>(kbs[mi]);
+            dma16(kb_base + (kb * kblk + rin * kstride), lk_lane[mi % KVAR], lk + m * 1024);
+            dma16(vb_base + (kb * vblk + rin * vstride), lv_lane, lv + m * 1024);
         }
     };
 
@@ -257,9 +280,9 @@ __global__ void __launch_bounds__(BQ) k_attn_fwd_bf16(AttnArgs a, int total_rows
         const bf16_bits* Vb = Vt[buf];
 
         // ---- S^T = K Q^T for both query groups ----
-        f32x16 sacc[2][2];
+        f32x16 sacc[G][2];
 #pragma unroll
-        for (int g = 0; g < 2; ++g)
+        for (int g = 0; g < G; ++g)
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
@@ -268,11 +291,12 @@ __global__ void __launch_bounds__(BQ) k_attn_fwd_bf16(AttnArgs a, int total_rows
         for (int kk = 0; kk < D / 16; ++kk) {
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
-                const int r = kh * 32 + l32;
+                const int r = sigma(kh * 32 + l32);
                 const int pos = (2 * kk + hi) ^ LY::fk(r);
                 const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Kb[r * D + pos * 8]);
-                sacc[0][kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[0][kk], sacc[0][kh], 0, 0, 0);
-                sacc[1][kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[1][kk], sacc[1][kh], 0, 0, 0);
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    sacc[g][kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[g][kk], sacc[g][kh], 0, 0, 0);
             }
         }
 
@@ -295,7 +319,7 @@ __global__ void __launch_bounds__(BQ) k_attn_fwd_bf16(AttnArgs a, int total_rows
                     for (int i = 0; i < 4; ++i) {
                         const int last = last0 + (i << lvl);
 #pragma unroll
-                        for (int g = 0; g < 2; ++g)
+                        for (int g = 0; g < G; ++g)
                             if (last > limit[g]) sacc[g][kh][gi * 4 + i] = -INFINITY;
                     }
                 }
@@ -303,9 +327,9 @@ __global__ void __launch_bounds__(BQ) k_attn_fwd_bf16(AttnArgs a, int total_rows
 
         // ---- online softmax (exp2 domain, lazy rescale) ----
         const float flvl = static_cast<float>(lvl);
-        float mt[2];
+        float mt[G];
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
+        for (int g = 0; g < G; ++g) {
             float x = sacc[g][0][0];
 #pragma unroll
             for (int e = 1; e < 31; e += 2)
@@ -313,12 +337,14 @@ __global__ void __launch_bounds__(BQ) k_attn_fwd_bf16(AttnArgs a, int total_rows
             x = fmaxf(x, sacc[g][1][15]);
             mt[g] = fmaf(pair32_max(x), a.c, flvl);   // tile max of z in log2 units
         }
-        const bool grow = (mt[0] > m_use[0] + kLazyRescale) || (mt[1] > m_use[1] + kLazyRescale);
+        bool grow = false;
+#pragma unroll
+        for (int g = 0; g < G; ++g) grow |= mt[g] > m_use[g] + kLazyRescale;
         if (__builtin_expect(__ballot(grow) != 0ull, 0)) {
             // rare (lazy max): the accumulators leave the AGPRs only here
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int g = 0; g < 2; ++g) {
+            for (int g = 0; g < G; ++g) {
                 const float m_new = fmaxf(m_use[g], mt[g]);
                 const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_use[g] - m_new);
                 m_use[g] = m_new;
@@ -329,18 +355,20 @@ __global__ void __launch_bounds__(BQ) k_attn_fwd_bf16(AttnArgs a, int total_rows
                     for (int e = 0; e < 16; ++e) oacc[g][i][e] *= alpha;
             }
         }
-        float off[2], psum[2] = {0.f, 0.f};
+        float off[G], psum[G];
 #pragma unroll
-        for (int g = 0; g < 2; ++g) off[g] = flvl - (m_use[g] == -INFINITY ? 0.f : m_use[g]);
+        for (int g = 0; g < G; ++g) psum[g] = 0.f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) off[g] = flvl - (m_use[g] == -INFINITY ? 0.f : m_use[g]);
 
         // ---- O^T += V^T P^T; P for 16 keys is formed just before its MFMAs ----
         const int grp = lane >> 4;   // 16-lane group: d half (grp & 1), key half (grp >> 1)
         const int jj = lane & 15;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            bf16x8 pf[2];
+            bf16x8 pf[G];
 #pragma unroll
-            for (int g = 0; g < 2; ++g) {
+            for (int g = 0; g < G; ++g) {
                 union {
                     bf16x8 v;
                     uint32_t u[4];
@@ -369,19 +397,20 @@ __global__ void __launch_bounds__(BQ) k_attn_fwd_bf16(AttnArgs a, int total_rows
                 } va;
                 va.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)pA);
                 va.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)pB);
-                oacc[0][dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va.v, pf[0], oacc[0][dblk], 0, 0, 0);
-                oacc[1][dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va.v, pf[1], oacc[1][dblk], 0, 0, 0);
+#pragma unroll
+                for (int g = 0; g < G; ++g)
+                    oacc[g][dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va.v, pf[g], oacc[g][dblk], 0, 0, 0);
             }
         }
-        l_run[0] += psum[0];
-        l_run[1] += psum[1];
+#pragma unroll
+        for (int g = 0; g < G; ++g) l_run[g] += psum[g];
         cur = nxt;
         buf ^= 1;
     }
 
     // ---- epilogue ----
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    for (int g = 0; g < G; ++g) {
         const int qt = qbase + g * 32 + l32;
         const float l_tot = pair32_sum(l_run[g]);
         const bool valid_q = qt < a.Nv && l_tot > 0.f;
@@ -404,22 +433,34 @@ __global__ void __launch_bounds__(BQ) k_attn_fwd_bf16(AttnArgs a, int total_rows
     }
 }
 
-template <int D, int BQ>
+template <int D, int BQ, int G>
 hipError_t launch_one(const Shape& s, const AttnArgs& a, hipStream_t st) {
     const int rows = s.B * s.H * s.NQB;
     const int nper = (rows + 7) / 8;
     const size_t dyn = static_cast<size_t>(s.NKB) * sizeof(int);
-    hipLaunchKernelGGL((k_attn_fwd_bf16<D, BQ>), dim3(8 * nper), dim3(BQ), dyn, st, a, rows);
+    hipLaunchKernelGGL((k_attn_fwd_bf16<D, BQ, G>), dim3(8 * nper), dim3(2 * BQ / G), dyn, st, a, rows);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_bf16(const Shape& s, const AttnArgs& a, hipStream_t st) {
-    if (s.D == 128 && s.BQ == 128) return launch_one<128, 128>(s, a, st);
-    if (s.D == 128 && s.BQ == 64) return launch_one<128, 64>(s, a, st);
-    if (s.D == 64 && s.BQ == 128) return launch_one<64, 128>(s, a, st);
-    if (s.D == 64 && s.BQ == 64) return launch_one<64, 64>(s, a, st);
+    // query groups per wave: PSA_ATTN_GROUPS=1|2 overrides the default (tuning runs)
+    static const int groups = [] {
+        const char* e = getenv("PSA_ATTN_GROUPS");
+        return (e != nullptr && e[0] == '2') ? 2 : 1;
+    }();
+    if (groups == 1) {
+        if (s.D == 128 && s.BQ == 128) return launch_one<128, 128, 1>(s, a, st);
+        if (s.D == 128 && s.BQ == 64) return launch_one<128, 64, 1>(s, a, st);
+        if (s.D == 64 && s.BQ == 128) return launch_one<64, 128, 1>(s, a, st);
+        if (s.D == 64 && s.BQ == 64) return launch_one<64, 64, 1>(s, a, st);
+    } else {
+        if (s.D == 128 && s.BQ == 128) return launch_one<128, 128, 2>(s, a, st);
+        if (s.D == 128 && s.BQ == 64) return launch_one<128, 64, 2>(s, a, st);
+        if (s.D == 64 && s.BQ == 128) return launch_one<64, 128, 2>(s, a, st);
+        if (s.D == 64 && s.BQ == 64) return launch_one<64, 64, 2>(s, a, st);
+    }
     return hipErrorInvalidValue;
 }
 
