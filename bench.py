@@ -162,6 +162,8 @@ def _traffic_from_profile():
 
 
 def run(args) -> dict:
+    import ctypes
+
     import torch
     import video_transformers_amd as psa
 
@@ -189,6 +191,9 @@ def run(args) -> dict:
     mass = torch.empty((B, H, nqb, nkb), dtype=torch.float32, device=dev)
     sim = (torch.empty((B, wl.heads_kv, nkb), dtype=torch.float32, device=dev)
            if wl.cos_sim_min > 0 else None)
+    cp0 = params.c()
+    mask_ws_bytes = psa.lib().psa_mask_workspace_bytes(prob.ref(), ctypes.byref(cp0)) if computed_map else 0
+    mask_ws = torch.empty(max(mask_ws_bytes, 256), dtype=torch.uint8, device=dev)
     row_ptr = torch.empty(B * H * nqb * 4 + 1, dtype=torch.int32, device=dev)
     col_idx = torch.empty(B * H * nqb * nkb, dtype=torch.int32, device=dev)
     dev_err = torch.empty(1, dtype=torch.int32, device=dev)
@@ -213,7 +218,7 @@ def run(args) -> dict:
             ev[1].record(stream)
         if computed_map:
             check(L.psa_mask(prob.ref(), ctypes.byref(cp), ptr(q), ptr(k), ptr(lm_buf), ptr(mass),
-                             ptr(sim), None, 0, st), "mask")
+                             ptr(sim), ptr(mask_ws), mask_ws.numel(), st), "mask")
             lm = lm_buf
         else:
             lm = drawn

@@ -18,6 +18,8 @@
 //                order and precision as a sequential reference), then overrides.
 #include <math.h>
 
+#include <algorithm>
+
 #include "psa_device.h"
 #include "psa_internal.h"
 
@@ -32,16 +34,23 @@ struct ScoreArgs {
     const bf16_bits* q;
     const bf16_bits* k;
     float* M;
+    float2* part;       // [row groups * 128][nsplit] running (max, sum) per key split, log2 units
     int H, Hkv, N, Nv, BQ, NQB, NKB, causal;
     int64_t qs0, qs1, qs2, ks0, ks1, ks2;
     int rows_per_head;  // sampling: NQB*S; antidiag: N/S
     int RQ;             // rows per query block: sampling S, antidiag BQ/S
-    int wg_per_head;
+    int wg_per_head;    // row groups of 128 per (batch, head)
+    int nsplit;         // key-tile splits per row group
+    int tiles_per_split;
     float c;            // scale * log2(e)
 };
 
 // MODE 0: sampling with S samples per query block; MODE 1: antidiagonal with stride S.
-template <int MODE, int D, int S>
+// PASS 0: per split, the online (max, sum) of each row over the split's key tiles.
+// PASS 1: merge the splits into the row's logsumexp, then the probabilities of the split's
+//         tiles, summed per KV block and over the rows of each query block -> block_mass.
+// Workgroup = 128 rows x one split; grid = B*H*wg_per_head*nsplit.
+template <int MODE, int D, int S, int PASS>
 __global__ void __launch_bounds__(kScoreThreads) k_mask_scores(ScoreArgs a) {
     constexpr int SI = MODE == 1 ? S : 1;          // inner chunks of D
     constexpr int CPK = MODE == 1 ? 64 / S : 64;   // columns per KV block
@@ -56,15 +65,16 @@ __global__ void __launch_bounds__(kScoreThreads) k_mask_scores(ScoreArgs a) {
     const int wave = tid >> 6;
     const int l32 = lane & 31;
     const int hi = lane >> 5;
-    const int bh = blockIdx.x / a.wg_per_head;
-    const int wg = blockIdx.x % a.wg_per_head;
+    const int split = blockIdx.x % a.nsplit;
+    const int rg = blockIdx.x / a.nsplit;      // row group over all (batch, head)
+    const int bh = rg / a.wg_per_head;
+    const int wg = rg % a.wg_per_head;
     const int h = bh % a.H;
     const int b = bh / a.H;
     const int hk = h / (a.H / a.Hkv);
 
     const int r = wg * 128 + wave * 32 + l32;  // 128 rows per workgroup
-    const int r_first = wg * 128;
-    const int r_last = r_first + 127;
+    const int r_last = wg * 128 + 127;
     bool row_ok;
     int tok = 0;  // sampling: the sampled token
     if (MODE == 0) {
@@ -76,6 +86,8 @@ __global__ void __launch_bounds__(kScoreThreads) k_mask_scores(ScoreArgs a) {
     } else {
         row_ok = r < a.rows_per_head && (r * S + S - 1) < a.Nv;
     }
+    const int64_t slot = static_cast<int64_t>(rg) * 128 + wave * 32 + l32;  // workspace row
+    const bool row_in = r < a.rows_per_head;
 
     const bf16_bits* qbase = a.q + b * a.qs0 + h * a.qs1;
     const bf16_bits* kbase = a.k + b * a.ks0 + hk * a.ks1;
@@ -92,14 +104,16 @@ __global__ void __launch_bounds__(kScoreThreads) k_mask_scores(ScoreArgs a) {
 
     const int ncols = MODE == 0 ? a.N : a.N / S;
     const int ntiles = ncols / 64;
-    // causal antidiagonal: columns beyond the workgroup's last row are all masked
+    // tiles past the causal frontier of the workgroup's rows are fully masked
     int tiles_needed = ntiles;
     if (MODE == 1 && a.causal) tiles_needed = min(ntiles, r_last / 64 + 1);
     if (MODE == 0 && a.causal) {
-        // last sampled token of the workgroup bounds the visible keys
         const int qb_last = min(r_last / S, a.NQB - 1);
         tiles_needed = min(ntiles, (qb_last * a.BQ + a.BQ - 1) / 64 + 1);
     }
+    const int j_lo = split * a.tiles_per_split;
+    const int j_hi = min(ntiles, j_lo + a.tiles_per_split);
+    const int j_end = min(j_hi, tiles_needed);   // tiles [j_lo, j_end) are computed
 
     u32x4 kreg[KCH];
     auto load_k = [&](int j, int t) {
@@ -124,116 +138,126 @@ __global__ void __launch_bounds__(kScoreThreads) k_mask_scores(ScoreArgs a) {
     };
 
     float m_run = -INFINITY, l_run = 0.f, m_ref = 0.f, inv_l = 0.f;
-
-    for (int pass = 0; pass < 2; ++pass) {
-        if (pass == 1) {
-            l_run = pair32_sum(l_run);
-            m_ref = m_run == -INFINITY ? 0.f : m_run;
-            inv_l = l_run > 0.f ? 1.f / l_run : 0.f;
-        }
-        if (tiles_needed > 0) load_k(0, 0);
-        for (int j = 0; j < ntiles; ++j) {
-            if (j >= tiles_needed) {
-                // fully masked tile: contributes nothing; pass 1 still writes its zeros
-                if (pass == 1 && hi == 0 && (l32 % a.RQ) == 0) {
-                    const int qb = r / a.RQ;
-                    if (qb < a.NQB && r < a.rows_per_head) {
-                        float* Mrow = a.M + (static_cast<int64_t>(bh) * a.NQB + qb) * a.NKB;
-#pragma unroll
-                        for (int kt = 0; kt < KT; ++kt) Mrow[j * KT + kt] = 0.f;
-                    }
-                }
-                continue;
+    if (PASS == 1) {
+        // merge the splits: lse in log2 units is m + log2(l); here p = exp2(s*c - m) / l
+        float m = -INFINITY;
+        for (int sp = 0; sp < a.nsplit; ++sp) m = fmaxf(m, a.part[slot * a.nsplit + sp].x);
+        float l = 0.f;
+        if (m != -INFINITY)
+            for (int sp = 0; sp < a.nsplit; ++sp) {
+                const float2 pr = a.part[slot * a.nsplit + sp];
+                if (pr.y > 0.f) l += pr.y * fast_exp2(pr.x - m);
             }
-            f32x16 sacc[2];
+        m_ref = m == -INFINITY ? 0.f : m;
+        inv_l = (row_ok && l > 0.f) ? 1.f / l : 0.f;
+    }
+    auto write_zero_tile = [&](int j) {
+        if (hi == 0 && (l32 % a.RQ) == 0) {
+            const int qb = r / a.RQ;
+            if (qb < a.NQB && row_in) {
+                float* Mrow = a.M + (static_cast<int64_t>(bh) * a.NQB + qb) * a.NKB;
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt) Mrow[j * KT + kt] = 0.f;
+            }
+        }
+    };
+
+    if (j_lo < j_end) load_k(j_lo, 0);
+    for (int j = j_lo; j < j_end; ++j) {
+        f32x16 sacc[2];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sacc[kh][e] = 0.f;
+        for (int t = 0; t < SI; ++t) {
+            __syncthreads();
+            store_k();
+            __syncthreads();
+            {   // prefetch the next (tile, chunk) step
+                int nj = j, nt = t + 1;
+                if (nt == SI) {
+                    nt = 0;
+                    ++nj;
+                }
+                if (nj < j_end) load_k(nj, nt);
+            }
+            if (MODE == 1) load_q(t);
+#pragma unroll
+            for (int kk = 0; kk < D / 16; ++kk)
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh) {
+                    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
+                        &Ks[(kh * 32 + l32) * KSTR + kk * 16 + hi * 8]);
+                    sacc[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], sacc[kh], 0, 0, 0);
+                }
+        }
+        // mask
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int cc = j * 64 + kh * 32 + (e >> 2) * 8 + hi * 4 + (e & 3);
+                bool ok;
+                if (MODE == 0)
+                    ok = row_ok && cc < a.Nv && (!a.causal || cc <= tok);
+                else
+                    ok = row_ok && (cc * S + S - 1) < a.Nv && (!a.causal || cc <= r);
+                if (!ok) sacc[kh][e] = -INFINITY;
+            }
+        if (PASS == 0) {
+            float mt = -INFINITY;
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) sacc[kh][e] = 0.f;
-            for (int t = 0; t < SI; ++t) {
-                __syncthreads();
-                store_k();
-                __syncthreads();
-                // prefetch the next (tile, chunk) step
-                {
-                    int nj = j, nt = t + 1;
-                    if (nt == SI) {
-                        nt = 0;
-                        ++nj;
-                    }
-                    if (nj < tiles_needed) load_k(nj, nt);
-                }
-                if (MODE == 1) load_q(t);
+                for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[kh][e]);
+            mt = pair32_max(mt);
+            const float m_new = fmaxf(m_run, mt * a.c);
+            const float mr = m_new == -INFINITY ? 0.f : m_new;
+            l_run *= fast_exp2(m_run - mr);
+            m_run = m_new;
 #pragma unroll
-                for (int kk = 0; kk < D / 16; ++kk)
+            for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-                    for (int kh = 0; kh < 2; ++kh) {
-                        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
-                            &Ks[(kh * 32 + l32) * KSTR + kk * 16 + hi * 8]);
-                        sacc[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], sacc[kh], 0, 0, 0);
-                    }
-            }
-            // mask
+                for (int e = 0; e < 16; ++e) l_run += fast_exp2(fmaf(sacc[kh][e], a.c, -mr));
+        } else {
+            float part[KT];
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) part[kt] = 0.f;
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const int cc = j * 64 + kh * 32 + (e >> 2) * 8 + hi * 4 + (e & 3);
-                    bool ok;
+                    const int kt = (kh * 32 + (e >> 2) * 8) / CPK;
+                    part[kt] += fast_exp2(fmaf(sacc[kh][e], a.c, -m_ref)) * inv_l;
+                }
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+                float x = pair32_sum(part[kt]);
+                for (int o = 1; o < a.RQ; o <<= 1) x += __shfl_xor(x, o, 64);
+                part[kt] = x;
+            }
+            if (hi == 0 && (l32 % a.RQ) == 0) {
+                const int qb = r / a.RQ;
+                if (qb < a.NQB && row_in) {
+                    int den;
                     if (MODE == 0)
-                        ok = row_ok && cc < a.Nv && (!a.causal || cc <= tok);
+                        den = min(max(a.Nv - qb * a.BQ, 0), a.BQ) > 0 ? S : 0;
                     else
-                        ok = row_ok && (cc * S + S - 1) < a.Nv && (!a.causal || cc <= r);
-                    if (!ok) sacc[kh][e] = -INFINITY;
-                }
-            if (pass == 0) {
-                float mt = -INFINITY;
+                        den = min(max(a.Nv / S - qb * a.RQ, 0), a.RQ);
+                    const float invd = den > 0 ? 1.f / static_cast<float>(den) : 0.f;
+                    float* Mrow = a.M + (static_cast<int64_t>(bh) * a.NQB + qb) * a.NKB;
 #pragma unroll
-                for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[kh][e]);
-                mt = pair32_max(mt);
-                const float m_new = fmaxf(m_run, mt * a.c);
-                const float mr = m_new == -INFINITY ? 0.f : m_new;
-                l_run *= fast_exp2(m_run - mr);
-                m_run = m_new;
-#pragma unroll
-                for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) l_run += fast_exp2(fmaf(sacc[kh][e], a.c, -mr));
-            } else {
-                float part[KT];
-#pragma unroll
-                for (int kt = 0; kt < KT; ++kt) part[kt] = 0.f;
-#pragma unroll
-                for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int kt = (kh * 32 + (e >> 2) * 8) / CPK;
-                        part[kt] += fast_exp2(fmaf(sacc[kh][e], a.c, -m_ref)) * inv_l;
-                    }
-#pragma unroll
-                for (int kt = 0; kt < KT; ++kt) {
-                    float x = pair32_sum(part[kt]);
-                    for (int o = 1; o < a.RQ; o <<= 1) x += __shfl_xor(x, o, 64);
-                    part[kt] = x;
-                }
-                if (hi == 0 && (l32 % a.RQ) == 0) {
-                    const int qb = r / a.RQ;
-                    if (qb < a.NQB && r < a.rows_per_head) {
-                        int den;
-                        if (MODE == 0)
-                            den = min(max(a.Nv - qb * a.BQ, 0), a.BQ) > 0 ? S : 0;
-                        else
-                            den = min(max(a.Nv / S - qb * a.RQ, 0), a.RQ);
-                        const float invd = den > 0 ? 1.f / static_cast<float>(den) : 0.f;
-                        float* Mrow = a.M + (static_cast<int64_t>(bh) * a.NQB + qb) * a.NKB;
-#pragma unroll
-                        for (int kt = 0; kt < KT; ++kt) Mrow[j * KT + kt] = part[kt] * invd;
-                    }
+                    for (int kt = 0; kt < KT; ++kt) Mrow[j * KT + kt] = part[kt] * invd;
                 }
             }
         }
+    }
+    if (PASS == 0) {
+        l_run = pair32_sum(l_run);
+        if (hi == 0) a.part[slot * a.nsplit + split] = make_float2(m_run, l_run);
+    } else {
+        // fully masked tiles of this split (past the causal frontier) still get their zeros
+        for (int j = max(j_lo, j_end); j < j_hi; ++j) write_zero_tile(j);
     }
 }
 
@@ -381,7 +405,10 @@ __global__ void __launch_bounds__(kAssignThreads) k_mask_assign(AssignArgs a) {
 
 template <int MODE, int D, int S>
 hipError_t launch_scores(const ScoreArgs& a, int blocks, hipStream_t st) {
-    hipLaunchKernelGGL((k_mask_scores<MODE, D, S>), dim3(blocks), dim3(kScoreThreads), 0, st, a);
+    hipLaunchKernelGGL((k_mask_scores<MODE, D, S, 0>), dim3(blocks), dim3(kScoreThreads), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_mask_scores<MODE, D, S, 1>), dim3(blocks), dim3(kScoreThreads), 0, st, a);
     return hipGetLastError();
 }
 
@@ -391,9 +418,35 @@ hipError_t launch_scores_d(const ScoreArgs& a, int D, int blocks, hipStream_t st
                     : launch_scores<MODE, 64, S>(a, blocks, st);
 }
 
+// Row groups, key-tile splits and their workspace for a problem.
+struct ScoreGeom {
+    int rows_per_head, RQ, wg_per_head, ntiles, nsplit, tiles_per_split;
+    size_t ws_bytes;
+};
+
+ScoreGeom score_geom(const Shape& s, const psa_mask_params& mp) {
+    ScoreGeom g;
+    const bool sampling = mp.mode == PSA_MASK_SAMPLING;
+    const int S = sampling ? mp.samples_per_qblock : mp.antidiag_stride;
+    g.rows_per_head = sampling ? s.NQB * S : s.N / S;
+    g.RQ = sampling ? S : s.BQ / S;
+    g.wg_per_head = (g.rows_per_head + 127) / 128;
+    g.ntiles = (sampling ? s.N : s.N / S) / 64;
+    // enough workgroups to fill the chip several times over; at least 4 tiles per split
+    const int64_t groups = static_cast<int64_t>(s.B) * s.H * g.wg_per_head;
+    int64_t want = groups > 0 ? (2048 + groups - 1) / groups : 1;
+    want = std::max<int64_t>(1, std::min<int64_t>(want, std::max(1, g.ntiles / 4)));
+    g.tiles_per_split = (g.ntiles + static_cast<int>(want) - 1) / static_cast<int>(want);
+    g.nsplit = g.tiles_per_split > 0 ? (g.ntiles + g.tiles_per_split - 1) / g.tiles_per_split : 1;
+    g.ws_bytes = static_cast<size_t>(groups) * 128 * g.nsplit * sizeof(float2);
+    return g;
+}
+
 }  // namespace
 
-size_t mask_workspace_bytes(const Shape&, const psa_mask_params&) { return 0; }
+size_t mask_workspace_bytes(const Shape& s, const psa_mask_params& mp) {
+    return score_geom(s, mp).ws_bytes;
+}
 
 hipError_t launch_mask_scores(const Shape& s, const psa_mask_params& mp, const void* q,
                               const void* k, const MaskBufs& mb, hipStream_t st) {
@@ -414,15 +467,15 @@ hipError_t launch_mask_scores(const Shape& s, const psa_mask_params& mp, const v
     a.ks0 = s.ks[0]; a.ks1 = s.ks[1]; a.ks2 = s.ks[2];
     a.c = (1.0f / sqrtf(static_cast<float>(s.D))) * kLog2e;
     const int S = mp.mode == PSA_MASK_SAMPLING ? mp.samples_per_qblock : mp.antidiag_stride;
-    if (mp.mode == PSA_MASK_SAMPLING) {
-        a.rows_per_head = s.NQB * S;
-        a.RQ = S;
-    } else {
-        a.rows_per_head = s.N / S;
-        a.RQ = s.BQ / S;
-    }
-    a.wg_per_head = (a.rows_per_head + 127) / 128;
-    const int blocks = s.B * s.H * a.wg_per_head;
+    const ScoreGeom g = score_geom(s, mp);
+    if (mb.ws == nullptr || mb.ws_bytes < g.ws_bytes) return hipErrorInvalidValue;
+    a.part = static_cast<float2*>(mb.ws);
+    a.rows_per_head = g.rows_per_head;
+    a.RQ = g.RQ;
+    a.wg_per_head = g.wg_per_head;
+    a.nsplit = g.nsplit;
+    a.tiles_per_split = g.tiles_per_split;
+    const int blocks = s.B * s.H * a.wg_per_head * a.nsplit;
     if (blocks == 0) return hipSuccess;
     if (mp.mode == PSA_MASK_SAMPLING) {
         switch (S) {
