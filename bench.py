@@ -142,9 +142,10 @@ def cpu_baseline(wl: W.Workload, budget_s: float = 15.0) -> dict:
 # ---------------------------------------------------------------------------------------
 # GPU run
 # ---------------------------------------------------------------------------------------
-def _traffic_from_profile():
+def _traffic_from_profile(workload: str):
     """HBM bytes per attention launch from the committed rocprofv3 counter summary, or None if
-    the attention kernel source changed since the counters were taken."""
+    the attention kernel source changed since the counters were taken or they were taken on
+    another workload."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
@@ -153,7 +154,7 @@ def _traffic_from_profile():
             key, val = line.split(":", 1)
             kv[key.strip()] = val.strip()
     sha = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
-    if kv.get("attn_source_sha256") != sha:
+    if kv.get("attn_source_sha256") != sha or kv.get("workload") != workload:
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -310,7 +311,7 @@ def _report(args, wl, flops, pairs, dpairs, frac, d, B, H, N, computed_map, attn
             attn_ms_mean, st_ms, dense_ms, wall):
     ms_per_step = wall * 1e3 / args.steps
     attn_tflops = flops / (attn_ms_mean * 1e-3) / 1e12
-    traffic = _traffic_from_profile()
+    traffic = _traffic_from_profile(wl.name)
     out = {
         "metric": METRIC,
         "value": round(flops / (ms_per_step * 1e-3) / 1e12, 3),

@@ -106,18 +106,20 @@ def check_attention(o_gpu, lse_gpu, o_ref, lse_ref, valid_rows, f32: bool, what:
 
 
 def fragile_entries(M_ref: np.ndarray, sim_ref, p: oracle.Problem, a: oracle.AssignParams,
-                    eps_m: float = 2e-6, eps_c: float = 2e-5, eps_s: float = 1e-6):
+                    eps_m: float = 2e-6, eps_c: float = 2e-5, eps_s: float = 1e-6,
+                    qblocks=None):
     """Boolean mask [.., NQB, NKB] of level decisions that an error of `eps` in the block
     masses (or similarities) could flip, judged on the oracle's own values: running sums within
     eps_c of a threshold, masses within eps_m of each other straddling a level change,
-    similarities within eps_s of the cosine bound. Used to excuse float-rounding differences in end-to-end maps."""
+    similarities within eps_s of the cosine bound. Used to excuse float-rounding differences in
+    end-to-end maps. `qblocks` restricts the scan to those query blocks (others stay False)."""
     t = np.array([float(np.float32(x)) for x in a.thresholds])
     B, H, nqb, nkb = M_ref.shape
     frag = np.zeros(M_ref.shape, dtype=bool)
     g = H // (sim_ref.shape[1] if sim_ref is not None else H)
     for b in range(B):
         for h in range(H):
-            for qb in range(nqb):
+            for qb in (range(nqb) if qblocks is None else qblocks):
                 Mr = M_ref[b, h, qb]
                 last = oracle.kb_diag(p, qb) if p.causal else nkb - 1
                 cand = np.arange(last + 1)
