@@ -4,16 +4,25 @@
 // from the hardware tile size while staying flash-attention compatible).
 //
 // Work decomposition
-//  * One workgroup per (batch, head, query block) row; 64 queries per wave (block_q / 64
-//    waves). Workgroups are remapped so that each XCD walks a contiguous range of rows (one
-//    head's K/V stays in that XCD's L2).
+//  * One workgroup per (batch, head, query block) row, 32 queries per wave (block_q / 32
+//    waves), two workgroups per CU (two waves per SIMD). Workgroups are remapped so that each
+//    XCD walks a contiguous range of rows.
 //  * The row's block list (its slice of the CSR) is copied to LDS once; the walk visits level
 //    0 tiles first, then 1, 2, 3. A 64-row hardware tile at level l packs 2^l logical pooled
 //    blocks of 64 / 2^l rows (decoupled block-tile); a level's partial last tile repeats its
 //    first block and masks the absent rows. Skipped blocks are never loaded.
-//  * K and V tiles travel HBM/L2 -> LDS with global_load_lds_dwordx4 (no VGPR staging), two
-//    LDS buffers per tensor: the loads of tile t+1 are in flight while tile t is computed; one
-//    barrier per tile.
+//  * K and V tiles travel HBM/L2 -> LDS with global_load_lds_dwordx4 (no VGPR staging). K:
+//    two 64-row buffers. V: a ring of four 32-row slots (half tile u lives in slot u mod 4),
+//    because the O product of a half runs one half behind its S product. One barrier per
+//    tile; the next tile's direct loads are issued from inside the MFMA stream.
+//
+// Software pipeline (per wave), in steps of 32 keys (half tiles u = 2t + h):
+//    S(u) = K(u) Q^T                       8 MFMAs (d = 128), K reads three MFMAs ahead
+//    P(u-1) = exp2(S(u-1) - m) -> bf16      VALU, one slice after each S MFMA
+//    O += V(u-1)^T P(u-1)                  8 MFMAs, interleaved with the second half of S(u)
+//    row max of S(u)                       VALU, beside the last O MFMAs
+//    (tiles that need it) mask, max again; lazy rescale check
+//  A scheduling barrier after every MFMA keeps this issue order.
 //
 // Math per wave (queries on the MFMA N axis, so each lane owns one query):
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: A = K rows from LDS, B = Q (registers, whole
@@ -28,10 +37,11 @@
 //    use by more than 8 (p <= 2^8 otherwise, exact after the final 1/l).
 //  * O^T = V^T P^T: A = V^T read from the row-major V tile with ds_read_b64_tr_b16 (each
 //    16-lane group reads a 4x16 block and receives it transposed), B = P^T from registers.
-//    Both query groups of a wave share every K and V operand read (64 FLOP per LDS byte).
 //  * LDS tiles are XOR-swizzled per row at 16-byte granularity so the operand reads are free of
 //    bank conflicts.
 #include <stdlib.h>
+
+#include <type_traits>
 
 #include "psa_attn_common.h"
 
@@ -40,8 +50,8 @@ namespace {
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) const void gbl_cvoid;
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 
 constexpr float kLazyRescale = 8.0f;  // log2-domain headroom before the accumulators rescale
 // s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their no-wait maxima
@@ -90,13 +100,18 @@ struct Tile {
     int cnt;   // blocks present in the tile (<= 2^l)
 };
 
-// G: query groups of 32 per wave (1 or 2). G = 2 shares every LDS operand read between two
-// groups at one wave per SIMD; G = 1 halves the registers so two waves share each SIMD.
-template <int D, int BQ, int G>
-__global__ void __launch_bounds__(2 * BQ / G, 3 - G) k_attn_fwd_bf16(AttnArgs a, int total_rows) {
-    constexpr int NW = BQ / (32 * G);
+template <int P>
+using IC = std::integral_constant<int, P>;
+
+// CONTIG: K and V rows are D elements apart (level 0 and the pooled levels share the lane
+// offsets of the direct loads).
+template <int D, int BQ, bool CONTIG>
+__global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int total_rows) {
+    constexpr int NW = BQ / 32;
     using LY = Lay<D>;
     constexpr int IPW = LY::INSTR / NW;  // direct-load instructions per wave per tensor
+    constexpr int KK = D / 16;           // k-steps of the S product
+    constexpr int DB = D / 32;           // 32-wide d blocks of the O product
     __shared__ __attribute__((aligned(1024))) bf16_bits Kt[2][64 * D];
     __shared__ __attribute__((aligned(1024))) bf16_bits Vt[2][64 * D];
     extern __shared__ int cols[];   // the row's block list (LDS reads do not wait on vmcnt)
@@ -129,49 +144,35 @@ __global__ void __launch_bounds__(2 * BQ / G, 3 - G) k_attn_fwd_bf16(AttnArgs a,
     const int lb1 = rp[1] - r0, lb2 = rp[2] - r0, lb3 = rp[3] - r0, lb4 = rp[4] - r0;
     // list offset of level l (l = 0..4), by selects: nothing is indexed dynamically
     auto lb = [&](int l) { return l <= 0 ? 0 : l == 1 ? lb1 : l == 2 ? lb2 : l == 3 ? lb3 : lb4; };
-    for (int i = tid; i < lb4; i += BQ) cols[i] = a.col_idx[r0 + i];
+    for (int i = tid; i < lb4; i += BQ * 2) cols[i] = a.col_idx[r0 + i];
 
     const int blk_first = qb * BQ;
-    const int qbase = blk_first + wave * 32 * G;
+    const int qt = blk_first + wave * 32 + l32;   // this lane's query
     const int min_limit = a.causal ? min(blk_first, a.Nv - 1) : a.Nv - 1;
     const bool any_valid_query = blk_first < a.Nv;
+    const int limit = a.causal ? min(qt, a.Nv - 1) : a.Nv - 1;
 
-    // ---- Q fragments: two groups of 32 queries ----
-    bf16x8 qf[G][D / 16];
+    // ---- Q fragments (B operand of S^T = K Q^T) ----
+    bf16x8 qf[KK];
+    {
+        const bf16_bits* qp = Q + b * a.qs0 + h * a.qs1 + static_cast<int64_t>(qt) * a.qs2;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const bf16_bits* qp = Q + b * a.qs0 + h * a.qs1 +
-                              static_cast<int64_t>(qbase + g * 32 + l32) * a.qs2;
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk)
-            qf[g][kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16 + hi * 8);
-    }
-    int limit[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const int qt = qbase + g * 32 + l32;
-        limit[g] = a.causal ? min(qt, a.Nv - 1) : a.Nv - 1;
+        for (int kk = 0; kk < KK; ++kk)
+            qf[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16 + hi * 8);
     }
 
-    f32x16 oacc[G][D / 32];
+    f32x16 oacc[DB];
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int i = 0; i < DB; ++i)
 #pragma unroll
-        for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) oacc[g][i][e] = 0.f;
-    float m_use[G], l_run[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-        m_use[g] = -INFINITY;
-        l_run[g] = 0.f;
-    }
+        for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
+    float m_use = -INFINITY, l_run = 0.f;
 
     const int64_t kbase = b * a.ks0 + hk * a.ks1;
     const int64_t vbase = b * a.vs0 + hk * a.vs1;
     const int64_t pbase = (static_cast<int64_t>(b) * a.Hkv + hk) * a.pooled_rows * D;
 
-    // walk state (uniform): first tile, then next() per tile; level changes are rare
+    // walk state (uniform): first tile, then next_tile() per tile; level changes are rare
     auto enter_level = [&](Tile& t) {   // t.l set, list position at the level's start
         while (t.l < 4 && lb(t.l + 1) == lb(t.l)) ++t.l;
         if (t.l < 4) {
@@ -193,7 +194,7 @@ __global__ void __launch_bounds__(2 * BQ / G, 3 - G) k_attn_fwd_bf16(AttnArgs a,
         return n;
     };
 
-    // Issue the direct loads of tile t into buffer `buf`. Instruction m fills LDS rows
+    // Direct loads of one tensor of tile t into buffer `buf`. Instruction m fills LDS rows
     // [m*RPI, (m+1)*RPI): consecutive keys of one logical block, so its block offset is
     // uniform and folds into the SGPR base; the lane offsets (row inside the instruction,
     // swizzled chunk) depend only on the row stride (level 0 or pooled) and, for K, on m.
@@ -201,8 +202,10 @@ __global__ void __launch_bounds__(2 * BQ / G, 3 - G) k_attn_fwd_bf16(AttnArgs a,
     static_assert(IPW % KVAR == 0, "instruction m and its index inside the wave agree mod KVAR");
     uint32_t lpk[2][KVAR], lpv[2];
     {
-        const uint32_t st[2] = {static_cast<uint32_t>(a.ks2) * 2u, static_cast<uint32_t>(D) * 2u};
-        const uint32_t sv[2] = {static_cast<uint32_t>(a.vs2) * 2u, static_cast<uint32_t>(D) * 2u};
+        const uint32_t st[2] = {CONTIG ? static_cast<uint32_t>(D) * 2u : static_cast<uint32_t>(a.ks2) * 2u,
+                                static_cast<uint32_t>(D) * 2u};
+        const uint32_t sv[2] = {CONTIG ? static_cast<uint32_t>(D) * 2u : static_cast<uint32_t>(a.vs2) * 2u,
+                                static_cast<uint32_t>(D) * 2u};
         const int rr = lane / LY::CH;   // row inside the instruction
         const int p = lane % LY::CH;    // LDS chunk position
 #pragma unroll
@@ -217,42 +220,305 @@ __global__ void __launch_bounds__(2 * BQ / G, 3 - G) k_attn_fwd_bf16(AttnArgs a,
     const uint32_t lds_k0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Kt[0][0]));
     const uint32_t lds_v0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Vt[0][0]));
     constexpr uint32_t kBufBytes = 64 * D * 2;
-    auto issue = [&](const Tile& t, int buf) {
+    // Direct loads of rows [r0, r0 + NR) of tile t (one tensor) to LDS address lds_dst (row r0
+    // lands at lds_dst). Instruction m (RPI rows, m*RPI >= r0) covers consecutive keys of one
+    // logical block, so its block offset is uniform and folds into the SGPR base; the lane
+    // offsets (row inside the instruction, swizzled chunk) depend only on the row stride (level
+    // 0 or pooled) and, for K, on m. prep() resolves the tile's addresses (scalar work), fire()
+    // issues one instruction; the loop spreads both over the MFMA slots of a step.
+    struct Dma {
+        const char* base;
+        uint32_t stride, blk, lds;
+        int rsm1;
+        int kb[8];
+    };
+    auto prep = [&](const Tile& t, uint32_t lds_dst, bool is_v, auto R0, auto NR) {
+        constexpr int r0 = decltype(R0)::value;
+        constexpr int ipw = decltype(NR)::value / LY::RPI / NW;   // instructions per wave
+        static_assert(ipw <= 8, "Dma::kb holds 8 instructions");
+        Dma d;
         const int l = t.l;
-        const int rs = 64 >> l;
         const int sh = 6 - l;
-        const int pooled = l > 0 ? 1 : 0;
-        const int64_t lvl_off = static_cast<int64_t>(a.N) - (static_cast<int64_t>(a.N) >> (l > 0 ? l - 1 : 0));
-        const char* kb_base = reinterpret_cast<const char*>(l == 0 ? K + kbase : KP + pbase + lvl_off * D);
-        const char* vb_base = reinterpret_cast<const char*>(l == 0 ? V + vbase : VP + pbase + lvl_off * D);
+        // pooled level l starts at row N - N / 2^(l-1) (0 for l = 1 and, by the same formula
+        // with shift 0, for l = 0); the level-0 / pooled tensor choice is a mask, not a branch
+        const uint32_t lvl_off = static_cast<uint32_t>(a.N - (a.N >> max(l - 1, 0)));
+        const uint64_t l0 = reinterpret_cast<uint64_t>(is_v ? V + vbase : K + kbase);
+        const uint64_t pl = reinterpret_cast<uint64_t>(is_v ? VP + pbase : KP + pbase);
+        const uint64_t m0 = 0ull - static_cast<uint64_t>(l == 0);
+        d.base = reinterpret_cast<const char*>(((l0 & m0) | (pl & ~m0)) + static_cast<uint64_t>(lvl_off * (D * 2u)));
         // byte offsets inside one (batch, head) of one level fit 32 bits (checked on the host)
-        const uint32_t kstride = static_cast<uint32_t>(l == 0 ? a.ks2 : D) * 2u;  // bytes per row
-        const uint32_t vstride = static_cast<uint32_t>(l == 0 ? a.vs2 : D) * 2u;
-        const uint32_t kblk = kstride * static_cast<uint32_t>(rs);  // bytes per logical block
-        const uint32_t vblk = vstride * static_cast<uint32_t>(rs);
+        d.stride = static_cast<uint32_t>(l == 0 && !CONTIG ? (is_v ? a.vs2 : a.ks2) : D) * 2u;
+        d.blk = d.stride * static_cast<uint32_t>(64 >> l);   // bytes per logical block
+        d.rsm1 = (64 >> l) - 1;
+        d.lds = lds_dst;
         const int clast = t.cnt - 1;
-        const uint32_t lk = lds_k0 + (buf ? kBufBytes : 0u);
-        const uint32_t lv = lds_v0 + (buf ? kBufBytes : 0u);
-        uint32_t lk_lane[KVAR];
 #pragma unroll
-        for (int q = 0; q < KVAR; ++q) lk_lane[q] = pooled ? lpk[1][q] : lpk[0][q];
-        const uint32_t lv_lane = pooled ? lpv[1] : lpv[0];
-        // every block index first (LDS reads + readfirstlane), then the loads
-        int kbs[IPW];
-#pragma unroll
-        for (int mi = 0; mi < IPW; ++mi) {
-            const int key0 = (wave * IPW + mi) * LY::RPI;   // first tile key of the instruction
-            const int s = min(key0 >> sh, clast);           // its logical block (absent -> last)
-            kbs[mi] = __builtin_amdgcn_readfirstlane(cols[t.base + s]);
+        for (int mi = 0; mi < ipw; ++mi) {
+            const int key0 = r0 + (wave * ipw + mi) * LY::RPI;   // first tile key of the instruction
+            const int sblk = min(key0 >> sh, clast);             // its logical block (absent -> last)
+            d.kb[mi] = __builtin_amdgcn_readfirstlane(cols[t.base + sblk]);
         }
+        return d;
+    };
+    auto fire = [&](const Dma& d, bool is_v, int pooled, auto R0, auto NR, int mi) {
+        constexpr int r0 = decltype(R0)::value;
+        constexpr int ipw = decltype(NR)::value / LY::RPI / NW;
+        const int mrel = wave * ipw + mi;
+        const int key0 = r0 + mrel * LY::RPI;
+        const uint32_t rin = static_cast<uint32_t>(key0 & d.rsm1);
+        const bool p1 = CONTIG || pooled;
+        // K swizzle variant of instruction m = key0 / RPI: (r0/RPI + mi) mod KVAR (wave * ipw
+        // is a multiple of KVAR)
+        const int q = (r0 / LY::RPI + mi) % KVAR;
+        const uint32_t lane_off = is_v ? (p1 ? lpv[1] : lpv[0]) : (p1 ? lpk[1][q] : lpk[0][q]);
+        dma16(d.base + (static_cast<uint32_t>(d.kb[mi]) * d.blk + rin * d.stride), lane_off, d.lds + mrel * 1024);
+    };
+    auto issue = [&](const Tile& t, uint32_t lds_dst, bool is_v, auto R0, auto NR) {
+        constexpr int ipw = decltype(NR)::value / LY::RPI / NW;
+        const Dma d = prep(t, lds_dst, is_v, R0, NR);
 #pragma unroll
-        for (int mi = 0; mi < IPW; ++mi) {
-            const int m = wave * IPW + mi;
-            const uint32_t rin = static_cast<uint32_t>((m * LY::RPI) & (rs - 1));
-            const uint32_t kb = static_cast<uint32_t>(kbs[mi]);
-            dma16(kb_base + (kb * kblk + rin * kstride), lk_lane[mi % KVAR], lk + m * 1024);
-            dma16(vb_base + (kb * vblk + rin * vstride), lv_lane, lv + m * 1024);
+        for (int mi = 0; mi < ipw; ++mi) fire(d, is_v, t.l > 0, R0, NR, mi);
+    };
+    constexpr uint32_t kSlotBytes = 32 * D * 2;   // one 32-row V slot
+    constexpr int IPWK = 64 / LY::RPI / NW;       // K instructions per wave per tile
+    constexpr int IPWV = 32 / LY::RPI / NW;       // V instructions per wave per half tile
+    auto issue_k = [&](const Tile& t, int buf) {
+        issue(t, lds_k0 + (buf ? kBufBytes : 0u), false, IC<0>{}, IC<64>{});
+    };
+    auto issue_vh = [&](const Tile& t, int half, int slot) {
+        if (half == 0)
+            issue(t, lds_v0 + slot * kSlotBytes, true, IC<0>{}, IC<32>{});
+        else
+            issue(t, lds_v0 + slot * kSlotBytes, true, IC<32>{}, IC<32>{});
+    };
+
+    // Loop-invariant per-lane LDS byte addresses of the operand reads (buffer 0; buffer 1 and
+    // the kh / j steps are instruction immediates).
+    // K: chunk position (2kk + hi) ^ fk(r) -> byte address ka_base ^ (32 kk): the row start and
+    // the hi / low-swizzle chunk bit occupy other bits than 32 kk (rows are D*2 >= 128 bytes).
+    uint32_t ka_base;
+    {
+        const int r = sigma(l32);          // kh = 1 adds 32 rows: an immediate
+        const int f = LY::fk(r);
+        ka_base = lds_k0 + static_cast<uint32_t>(r * D * 2 + 16 * ((hi ^ f) & 1) + 16 * (f & ~1));
+    }
+    const int grp = lane >> 4;   // 16-lane group: d half (grp & 1), key half (grp >> 1)
+    const int jj = lane & 15;
+    uint32_t va_addr[DB];
+#pragma unroll
+    for (int dblk = 0; dblk < DB; ++dblk) {
+        const int d = dblk * 32 + 16 * (grp & 1) + 4 * (jj & 3);
+        const int c = d >> 3;
+        const int half = d & 7;  // 0 or 4 elements
+        const int rA = 8 * (grp >> 1) + (jj >> 2);   // j adds 16 rows, B adds 4: immediates
+        va_addr[dblk] = lds_v0 + static_cast<uint32_t>((rA * D + ((c ^ LY::fv(rA)) << 3) + half) * 2);
+    }
+
+    f32x16 sacc[2];   // S of two consecutive 32-key half tiles (index: the half)
+    float psum0 = 0.f, psum1 = 0.f;
+
+    // S^T of half H of the K tile at LDS byte offset kbuf (0 or one buffer) into sacc[H]
+    auto compute_s = [&](auto H, uint32_t kbuf) {
+        constexpr int hh = decltype(H)::value;
+        constexpr uint32_t boff = hh * 32 * D * 2;
+        // the buffer offset (bit 14 and up) and the XOR of 32 kk (bits 5..7) do not interact;
+        // the per-k-step addresses stay inside the loop (one XOR each) instead of KK registers
+        uint32_t kb_opaque = ka_base + kbuf;
+        asm volatile("" : "+v"(kb_opaque));
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[hh][e] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const uint32_t kaddr = kb_opaque ^ static_cast<uint32_t>(32 * kk);
+            const bf16x8 ka = *(const lds_bf16x8*)(uintptr_t)(kaddr + boff);
+            sacc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], sacc[hh], 0, 0, 0);
         }
+    };
+    // P fragment j (0/1) of sacc[H]: 16 keys 16j + 8*hi + e of that half; exp2 offset `off`
+    auto make_p = [&](auto H, int j, float off) {
+        constexpr int hh = decltype(H)::value;
+        union {
+            bf16x8 v;
+            uint32_t u[4];
+        } pk;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float p0 = fast_exp2(fmaf(sacc[hh][j * 8 + 2 * t], a.c, off));
+            const float p1 = fast_exp2(fmaf(sacc[hh][j * 8 + 2 * t + 1], a.c, off));
+            pk.u[t] = pack_bf16x2(p0, p1);
+            if (t & 1)
+                psum1 = add_bf16x2(pk.u[t], psum1);
+            else
+                psum0 = add_bf16x2(pk.u[t], psum0);
+        }
+        return pk.v;
+    };
+    // O^T += V^T(j) P^T(j) for the 16 keys j (0/1) of the V slot at LDS byte offset vslot
+    auto pv = [&](uint32_t vslot, int j, const bf16x8& pf) {
+#pragma unroll
+        for (int dblk = 0; dblk < DB; ++dblk) {
+            const uint32_t pa = va_addr[dblk] + vslot + j * 16 * D * 2;
+            union {
+                bf16x8 v;
+                v4i16 h[2];
+            } va;
+            va.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)pa);
+            va.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)(pa + 4 * D * 2));
+            oacc[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va.v, pf, oacc[dblk], 0, 0, 0);
+        }
+    };
+    // mask (partial tiles, padding, causal diagonal) of half H of tile t in sacc[H]
+    auto apply_mask = [&](auto H, const Tile& t) {
+        constexpr int hh = decltype(H)::value;
+        const int lvl = t.l;
+        // A lane's 16 accumulator slots are 4 runs of 4 consecutive tile keys tk0 + i; a run
+        // lies inside one logical block (>= 8 rows), so one list read per run.
+        const int rs = 64 >> lvl;
+        const int sh = 6 - lvl;
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+            const int tk0 = hh * 32 + 16 * (gi >> 1) + 8 * hi + 4 * (gi & 1);
+            const int s = tk0 >> sh;
+            const int kb = cols[t.base + (s < t.cnt ? s : 0)];
+            const int last0 = s < t.cnt ? ((kb * rs + (tk0 & (rs - 1)) + 1) << lvl) - 1
+                                        : 0x7fffffff - (3 << 3);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int last = last0 + (i << lvl);
+                if (last > limit) sacc[hh][gi * 4 + i] = -INFINITY;
+            }
+        }
+    };
+    // row max over the 16 values of sacc[H] in two chains (max3 each): part 0 / part 1 / final
+    auto half_max_part = [&](auto H, int part) {
+        constexpr int hh = decltype(H)::value;
+        const int e0 = part * 8;
+        return fmaxf(fmaxf(fmaxf(sacc[hh][e0], sacc[hh][e0 + 1]), fmaxf(sacc[hh][e0 + 2], sacc[hh][e0 + 3])),
+                     fmaxf(fmaxf(sacc[hh][e0 + 4], sacc[hh][e0 + 5]), fmaxf(sacc[hh][e0 + 6], sacc[hh][e0 + 7])));
+    };
+    auto half_max = [&](float x0, float x1, int lvl) {
+        return fmaf(pair32_max(fmaxf(x0, x1)), a.c, static_cast<float>(lvl));  // log2 units
+    };
+    // lazy running max: rescale the O accumulators and row sums only when the max in use is
+    // exceeded by more than kLazyRescale (after the O products issued so far)
+    auto update_max = [&](float mt) {
+        if (__builtin_expect(__ballot(mt > m_use + kLazyRescale) != 0ull, 0)) {
+            const float m_new = fmaxf(m_use, mt);
+            const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_use - m_new);
+            m_use = m_new;
+            psum0 *= alpha;
+            psum1 *= alpha;
+#pragma unroll
+            for (int i = 0; i < DB; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
+        }
+    };
+    auto tile_needs_mask = [&](const Tile& t) {
+        const int kb_max = cols[t.base + t.cnt - 1];
+        return (t.cnt < (1 << t.l)) || ((kb_max + 1) * 64 - 1 > min_limit);
+    };
+    auto exp_off = [&](int lvl) { return static_cast<float>(lvl) - (m_use == -INFINITY ? 0.f : m_use); };
+    auto wait_publish = [&]() {
+        // this wave's direct loads landed (vmcnt), then the barrier publishes every wave's and
+        // retires every wave's reads of the buffers about to be refilled
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        __syncthreads();
+    };
+    // exp chunk c (of KK) of the P fragments of sacc[H]: 8 / KK * 4 ... pairs of keys
+    auto exp_chunk = [&](auto H, int c, float off, uint32_t (&pk)[8]) {
+        constexpr int hh = decltype(H)::value;
+        constexpr int PAIRS = 8 / KK;   // key pairs per chunk (1 for D = 128, 2 for D = 64)
+#pragma unroll
+        for (int q = 0; q < PAIRS; ++q) {
+            const int pr = c * PAIRS + q;   // pair 0..7: fragment pr / 4, dword pr % 4
+            const float p0 = fast_exp2(fmaf(sacc[hh][2 * pr], a.c, off));
+            const float p1 = fast_exp2(fmaf(sacc[hh][2 * pr + 1], a.c, off));
+            pk[pr] = pack_bf16x2(p0, p1);
+            if (pr & 1)
+                psum1 = add_bf16x2(pk[pr], psum1);
+            else
+                psum0 = add_bf16x2(pk[pr], psum0);
+        }
+    };
+    auto read_k = [&](uint32_t base, int kk) {
+        return *(const lds_bf16x8*)(uintptr_t)(base ^ static_cast<uint32_t>(32 * kk));
+    };
+    auto read_v = [&](uint32_t vslot, int j, int dblk) {
+        const uint32_t pa = va_addr[dblk] + vslot + j * 16 * D * 2;
+        union {
+            bf16x8 v;
+            v4i16 h[2];
+        } va;
+        va.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)pa);
+        va.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)(pa + 4 * D * 2));
+        return va.v;
+    };
+    // One pipeline step, in a fixed issue order (a scheduling barrier after each MFMA):
+    //   S(h) MFMAs 0..KK-1, K reads three MFMAs ahead; after each, 1/KK of the exp work of the
+    //   previous half (sacc[H^1], level lvl_p); from MFMA KK/2 on, the O MFMAs of its first 16
+    //   keys alternate with them; then the O MFMAs of its last 16 keys, alongside the row max
+    //   of S(h).
+    // Returns the half's unmasked max (log2 units).
+    auto step = [&](auto H, uint32_t kbuf, uint32_t vslot, int lvl_p, int lvl_h, auto&& dma) {
+        constexpr int hh = decltype(H)::value;
+        const float off = exp_off(lvl_p);
+        uint32_t kaddr = ka_base + kbuf + hh * 32 * D * 2;   // no carry into the XORed bits
+        asm volatile("" : "+v"(kaddr));
+        uint32_t pk[8];
+        bf16x8 kr[KK];
+        bf16x8 vr0[DB], vr1[DB];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 3 && i < KK; ++i) kr[i] = read_k(kaddr, i);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[hh][e] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            if (kk + 3 < KK) kr[kk + 3] = read_k(kaddr, kk + 3);
+            if (kk == 0)
+#pragma unroll
+                for (int d = 0; d < DB; ++d) vr0[d] = read_v(vslot, 0, d);
+            if (kk == KK / 2)
+#pragma unroll
+                for (int d = 0; d < DB; ++d) vr1[d] = read_v(vslot, 1, d);
+            sacc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[kk], qf[kk], sacc[hh], 0, 0, 0);
+            exp_chunk(IC<hh ^ 1>{}, kk, off, pk);
+            dma(kk);   // the next tiles' direct loads ride along with the MFMAs
+            if (kk >= KK / 2) {
+                const int d = kk - KK / 2;
+                const bf16x8 p0 = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+                oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr0[d], p0, oacc[d], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        float x0 = -INFINITY, x1 = -INFINITY;
+#pragma unroll
+        for (int d = 0; d < DB; ++d) {
+            const bf16x8 p1 = __builtin_bit_cast(bf16x8, u32x4{pk[4], pk[5], pk[6], pk[7]});
+            oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vr1[d], p1, oacc[d], 0, 0, 0);
+            // (the empty asm pins each partial max to its slot; the compiler would sink it)
+            if (d == 0) {
+                x0 = half_max_part(H, 0);
+                asm volatile("" : "+v"(x0));
+            }
+            if (d == (DB > 1 ? 1 : 0)) {
+                x1 = half_max_part(H, 1);
+                asm volatile("" : "+v"(x1));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        return half_max(x0, x1, lvl_h);
+    };
+    // step, then (tiles that need it) the mask and the max again, then the lazy max update
+    auto step_max = [&](auto H, bool need, uint32_t kbuf, uint32_t vslot, int lvl_p, const Tile& t,
+                        auto&& dma) {
+        float mt = step(H, kbuf, vslot, lvl_p, t.l, dma);
+        if (need) {
+            apply_mask(H, t);
+            mt = half_max(half_max_part(H, 0), half_max_part(H, 1), t.l);
+        }
+        update_max(mt);
     };
 
     __syncthreads();  // cols[] visible
@@ -261,206 +527,124 @@ __global__ void __launch_bounds__(2 * BQ / G, 3 - G) k_attn_fwd_bf16(AttnArgs a,
     enter_level(cur);
     set_cnt(cur);
     if (!any_valid_query) cur.l = 4;
-    if (cur.l < 4) issue(cur, 0);
 
-    int buf = 0;
-    while (cur.l < 4) {
-        const Tile nxt = next_tile(cur);
-        const int lvl = cur.l;
-        const int kb_max = cols[cur.base + cur.cnt - 1];
-        const bool need_mask = (cur.cnt < (1 << lvl)) || ((kb_max + 1) * 64 - 1 > min_limit);
-
-        // tile `cur` landed in `buf`: each wave waits for its own direct loads (vmcnt), then
-        // the barrier publishes them and retires every wave's reads of the other buffer
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        __syncthreads();
-        if (nxt.l < 4) issue(nxt, buf ^ 1);
-
-        const bf16_bits* Kb = Kt[buf];
-        const bf16_bits* Vb = Vt[buf];
-
-        // ---- S^T = K Q^T for both query groups ----
-        f32x16 sacc[G][2];
-#pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) sacc[g][kh][e] = 0.f;
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh) {
-                const int r = sigma(kh * 32 + l32);
-                const int pos = (2 * kk + hi) ^ LY::fk(r);
-                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Kb[r * D + pos * 8]);
-#pragma unroll
-                for (int g = 0; g < G; ++g)
-                    sacc[g][kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[g][kk], sacc[g][kh], 0, 0, 0);
-            }
-        }
-
-        // ---- mask (partial tiles, padding, causal diagonal) ----
-        // A lane's 32 accumulator slots per query group are 8 runs of 4 consecutive tile keys
-        // tk0 + i; a run lies inside one logical block (>= 8 rows), so one list read per run.
-        if (need_mask) {
-            const int rs = 64 >> lvl;
-            const int sh = 6 - lvl;
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                for (int gi = 0; gi < 4; ++gi) {
-                    const int tk0 = kh * 32 + 16 * (gi >> 1) + 8 * hi + 4 * (gi & 1);
-                    const int s = tk0 >> sh;
-                    const int kb = cols[cur.base + (s < cur.cnt ? s : 0)];
-                    const int last0 = s < cur.cnt ? ((kb * rs + (tk0 & (rs - 1)) + 1) << lvl) - 1
-                                                  : 0x7fffffff - (3 << 3);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int last = last0 + (i << lvl);
-#pragma unroll
-                        for (int g = 0; g < G; ++g)
-                            if (last > limit[g]) sacc[g][kh][gi * 4 + i] = -INFINITY;
-                    }
-                }
-        }
-
-        // ---- online softmax (exp2 domain, lazy rescale) ----
-        const float flvl = static_cast<float>(lvl);
-        float mt[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            float x = sacc[g][0][0];
-#pragma unroll
-            for (int e = 1; e < 31; e += 2)
-                x = fmaxf(x, fmaxf(sacc[g][e >> 4][e & 15], sacc[g][(e + 1) >> 4][(e + 1) & 15]));
-            x = fmaxf(x, sacc[g][1][15]);
-            mt[g] = fmaf(pair32_max(x), a.c, flvl);   // tile max of z in log2 units
-        }
-        bool grow = false;
-#pragma unroll
-        for (int g = 0; g < G; ++g) grow |= mt[g] > m_use[g] + kLazyRescale;
-        if (__builtin_expect(__ballot(grow) != 0ull, 0)) {
-            // rare (lazy max): the accumulators leave the AGPRs only here
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const float m_new = fmaxf(m_use[g], mt[g]);
-                const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_use[g] - m_new);
-                m_use[g] = m_new;
-                l_run[g] *= alpha;
-#pragma unroll
-                for (int i = 0; i < D / 32; ++i)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) oacc[g][i][e] *= alpha;
-            }
-        }
-        float off[G], psum[G];
-#pragma unroll
-        for (int g = 0; g < G; ++g) psum[g] = 0.f;
-#pragma unroll
-        for (int g = 0; g < G; ++g) off[g] = flvl - (m_use[g] == -INFINITY ? 0.f : m_use[g]);
-
-        // ---- O^T += V^T P^T; P for 16 keys is formed just before its MFMAs ----
-        const int grp = lane >> 4;   // 16-lane group: d half (grp & 1), key half (grp >> 1)
-        const int jj = lane & 15;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            bf16x8 pf[G];
-#pragma unroll
-            for (int g = 0; g < G; ++g) {
-                union {
-                    bf16x8 v;
-                    uint32_t u[4];
-                } pk;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const float p0 = fast_exp2(fmaf(sacc[g][j >> 1][(j & 1) * 8 + 2 * t], a.c, off[g]));
-                    const float p1 = fast_exp2(fmaf(sacc[g][j >> 1][(j & 1) * 8 + 2 * t + 1], a.c, off[g]));
-                    pk.u[t] = pack_bf16x2(p0, p1);
-                    psum[g] = add_bf16x2(pk.u[t], psum[g]);
-                }
-                pf[g] = pk.v;
-            }
-#pragma unroll
-            for (int dblk = 0; dblk < D / 32; ++dblk) {
-                const int d = dblk * 32 + 16 * (grp & 1) + 4 * (jj & 3);
-                const int c = d >> 3;
-                const int half = (d & 7);  // 0 or 4 elements
-                const int rA = 16 * j + 8 * (grp >> 1) + (jj >> 2);
-                const int rB = rA + 4;
-                const bf16_bits* pA = &Vb[rA * D + ((c ^ LY::fv(rA)) << 3) + half];
-                const bf16_bits* pB = &Vb[rB * D + ((c ^ LY::fv(rB)) << 3) + half];
-                union {
-                    bf16x8 v;
-                    v4i16 h[2];
-                } va;
-                va.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)pA);
-                va.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)pB);
-#pragma unroll
-                for (int g = 0; g < G; ++g)
-                    oacc[g][dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va.v, pf[g], oacc[g][dblk], 0, 0, 0);
-            }
-        }
-#pragma unroll
-        for (int g = 0; g < G; ++g) l_run[g] += psum[g];
+    if (cur.l < 4) {
+        // ---- tile 0: K(0) and V half 0 first; S of half 0 alone, then step(half 1) ----
+        issue_k(cur, 0);
+        issue_vh(cur, 0, 0);
+        Tile nxt = next_tile(cur);
+        wait_publish();
+        if (nxt.l < 4) issue_k(nxt, 1);
+        issue_vh(cur, 1, 1);
+        if (nxt.l < 4) issue_vh(nxt, 0, 2);
+        bool nm = tile_needs_mask(cur);
+        compute_s(IC<0>{}, 0u);
+        if (nm) apply_mask(IC<0>{}, cur);
+        update_max(half_max(half_max_part(IC<0>{}, 0), half_max_part(IC<0>{}, 1), cur.l));
+        step_max(IC<1>{}, nm, 0u, 0u, cur.l, cur, [](int) {});
+        int lvl_prev = cur.l;
         cur = nxt;
-        buf ^= 1;
+        int T = 1;   // parity of the tile index
+
+        // ---- tile t >= 1 (T = t & 1): K(t) in buffer T; V half u = 2t + h in slot u & 3 ----
+        // (one loop body with the parity in a scalar: two copies of the body make the register
+        // allocator split the accumulators)
+        while (cur.l < 4) {
+            const Tile nx = next_tile(cur);
+            wait_publish();
+            const bool has_nx = nx.l < 4;
+            const bool need = tile_needs_mask(cur);
+            const uint32_t kbuf = T ? kBufBytes : 0u;
+            // slot s of the K-tile steps fires the instructions mi with mi % (KK - 1) == s - 1
+            // (slot 0 resolves the addresses)
+            // after the row's last tile the "next" loads repeat the current tile into buffers
+            // that are never read again: no branches inside the steps
+            const Tile nsrc = has_nx ? nx : cur;
+            Dma dk{}, dv1{}, dv0{};
+            auto dma_k = [&](int sl) {
+                if (sl == 0) {
+                    dk = prep(nsrc, lds_k0 + (T ? 0u : kBufBytes), false, IC<0>{}, IC<64>{});
+                } else {
+#pragma unroll
+                    for (int mi = 0; mi < IPWK; ++mi)
+                        if (mi % (KK - 1) == sl - 1) fire(dk, false, nsrc.l > 0, IC<0>{}, IC<64>{}, mi);
+                }
+            };
+            auto dma_v = [&](int sl) {
+                if (sl == 0) {
+                    dv1 = prep(cur, lds_v0 + static_cast<uint32_t>(2 * T + 1) * kSlotBytes, true, IC<32>{}, IC<32>{});
+                    dv0 = prep(nsrc, lds_v0 + static_cast<uint32_t>((2 * T + 2) & 3) * kSlotBytes, true, IC<0>{}, IC<32>{});
+                } else {
+#pragma unroll
+                    for (int mi = 0; mi < 2 * IPWV; ++mi)
+                        if (mi % (KK - 1) == sl - 1) {
+                            if (mi < IPWV)
+                                fire(dv1, true, cur.l > 0, IC<32>{}, IC<32>{}, mi);
+                            else
+                                fire(dv0, true, nsrc.l > 0, IC<0>{}, IC<32>{}, mi - IPWV);
+                        }
+                }
+            };
+            // half 0: P of the previous tile's half 1 (slot 2t-1 = 2T+3 mod 4)
+            step_max(IC<0>{}, need, kbuf, static_cast<uint32_t>((2 * T + 3) & 3) * kSlotBytes, lvl_prev, cur, dma_k);
+            // half 1: P of this tile's half 0 (slot 2T)
+            step_max(IC<1>{}, need, kbuf, static_cast<uint32_t>(2 * T) * kSlotBytes, cur.l, cur, dma_v);
+            lvl_prev = cur.l;
+            cur = nx;
+            T ^= 1;
+        }
+        // ---- after the last tile (parity T ^ 1): P and O of its half 1 (slot 2(T^1)+1) ----
+        wait_publish();
+        {
+            const float off = exp_off(lvl_prev);
+            const bf16x8 p0 = make_p(IC<1>{}, 0, off);
+            const bf16x8 p1 = make_p(IC<1>{}, 1, off);
+            const uint32_t vslot = static_cast<uint32_t>(2 * (T ^ 1) + 1) * kSlotBytes;
+            pv(vslot, 0, p0);
+            pv(vslot, 1, p1);
+        }
     }
+    l_run += psum0 + psum1;
 
     // ---- epilogue ----
+    const float l_tot = pair32_sum(l_run);
+    const bool valid_q = qt < a.Nv && l_tot > 0.f;
+    const float inv = valid_q ? 1.f / l_tot : 0.f;
+    bf16_bits* O = static_cast<bf16_bits*>(a.o) + b * a.os0 + h * a.os1 + static_cast<int64_t>(qt) * a.os2;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-        const int qt = qbase + g * 32 + l32;
-        const float l_tot = pair32_sum(l_run[g]);
-        const bool valid_q = qt < a.Nv && l_tot > 0.f;
-        const float inv = valid_q ? 1.f / l_tot : 0.f;
-        bf16_bits* O = static_cast<bf16_bits*>(a.o) + b * a.os0 + h * a.os1 +
-                       static_cast<int64_t>(qt) * a.os2;
+    for (int dblk = 0; dblk < DB; ++dblk)
 #pragma unroll
-        for (int dblk = 0; dblk < D / 32; ++dblk)
-#pragma unroll
-            for (int gg = 0; gg < 4; ++gg) {
-                u32x2 w;
-                w[0] = pack_bf16x2(oacc[g][dblk][4 * gg] * inv, oacc[g][dblk][4 * gg + 1] * inv);
-                w[1] = pack_bf16x2(oacc[g][dblk][4 * gg + 2] * inv, oacc[g][dblk][4 * gg + 3] * inv);
-                *reinterpret_cast<u32x2*>(O + dblk * 32 + gg * 8 + hi * 4) = w;
-            }
-        if (a.lse != nullptr && hi == 0) {
-            const float lse = valid_q ? (m_use[g] + log2f(l_tot)) * kLn2 : -INFINITY;
-            a.lse[(static_cast<int64_t>(b) * a.H + h) * a.N + qt] = lse;
+        for (int gg = 0; gg < 4; ++gg) {
+            u32x2 w;
+            w[0] = pack_bf16x2(oacc[dblk][4 * gg] * inv, oacc[dblk][4 * gg + 1] * inv);
+            w[1] = pack_bf16x2(oacc[dblk][4 * gg + 2] * inv, oacc[dblk][4 * gg + 3] * inv);
+            *reinterpret_cast<u32x2*>(O + dblk * 32 + gg * 8 + hi * 4) = w;
         }
+    if (a.lse != nullptr && hi == 0) {
+        const float lse = valid_q ? (m_use + log2f(l_tot)) * kLn2 : -INFINITY;
+        a.lse[(static_cast<int64_t>(b) * a.H + h) * a.N + qt] = lse;
     }
 }
 
-template <int D, int BQ, int G>
+template <int D, int BQ>
 hipError_t launch_one(const Shape& s, const AttnArgs& a, hipStream_t st) {
     const int rows = s.B * s.H * s.NQB;
     const int nper = (rows + 7) / 8;
     const size_t dyn = static_cast<size_t>(s.NKB) * sizeof(int);
-    hipLaunchKernelGGL((k_attn_fwd_bf16<D, BQ, G>), dim3(8 * nper), dim3(2 * BQ / G), dyn, st, a, rows);
+    if (a.ks2 == D && a.vs2 == D)
+        hipLaunchKernelGGL((k_attn_fwd_bf16<D, BQ, true>), dim3(8 * nper), dim3(2 * BQ), dyn, st, a, rows);
+    else
+        hipLaunchKernelGGL((k_attn_fwd_bf16<D, BQ, false>), dim3(8 * nper), dim3(2 * BQ), dyn, st, a, rows);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_bf16(const Shape& s, const AttnArgs& a, hipStream_t st) {
-    // query groups per wave: PSA_ATTN_GROUPS=1|2 overrides the default (tuning runs)
-    static const int groups = [] {
-        const char* e = getenv("PSA_ATTN_GROUPS");
-        return (e != nullptr && e[0] == '2') ? 2 : 1;
-    }();
-    if (groups == 1) {
-        if (s.D == 128 && s.BQ == 128) return launch_one<128, 128, 1>(s, a, st);
-        if (s.D == 128 && s.BQ == 64) return launch_one<128, 64, 1>(s, a, st);
-        if (s.D == 64 && s.BQ == 128) return launch_one<64, 128, 1>(s, a, st);
-        if (s.D == 64 && s.BQ == 64) return launch_one<64, 64, 1>(s, a, st);
-    } else {
-        if (s.D == 128 && s.BQ == 128) return launch_one<128, 128, 2>(s, a, st);
-        if (s.D == 128 && s.BQ == 64) return launch_one<128, 64, 2>(s, a, st);
-        if (s.D == 64 && s.BQ == 128) return launch_one<64, 128, 2>(s, a, st);
-        if (s.D == 64 && s.BQ == 64) return launch_one<64, 64, 2>(s, a, st);
-    }
+    if (s.D == 128 && s.BQ == 128) return launch_one<128, 128>(s, a, st);
+    if (s.D == 128 && s.BQ == 64) return launch_one<128, 64>(s, a, st);
+    if (s.D == 64 && s.BQ == 128) return launch_one<64, 128>(s, a, st);
+    if (s.D == 64 && s.BQ == 64) return launch_one<64, 64>(s, a, st);
     return hipErrorInvalidValue;
 }
 
