@@ -178,8 +178,7 @@ int psa_mask(const psa_problem* prob, const psa_mask_params* params, const void*
         e = psa::launch_block_sim(s, k, block_sim, st);
         if (e != hipSuccess) return hip_status(e);
     }
-    return hip_status(psa::launch_mask_assign(s, *params, block_mass,
-                                              use_sim ? block_sim : nullptr, level_map, st));
+    return hip_status(psa::launch_mask_assign_logmass(s, *params, mb, level_map, st));
 }
 
 int psa_mask_assign(const psa_problem* prob, const psa_mask_params* params,

@@ -53,6 +53,10 @@ hipError_t launch_block_sim(const Shape& s, const void* k, float* block_sim, hip
 hipError_t launch_mask_assign(const Shape& s, const psa_mask_params& mp, const float* block_mass,
                               const float* block_sim, int8_t* level_map, hipStream_t st);
 
+// Assignment from the scoring pass's log-masses in mb.ws; writes mb.block_mass and the map.
+hipError_t launch_mask_assign_logmass(const Shape& s, const psa_mask_params& mp, const MaskBufs& mb,
+                                      int8_t* level_map, hipStream_t st);
+
 // Clears one int32 on the device with a kernel (no memset node, so the call stays safe to
 // capture in a graph).
 hipError_t launch_clear_i32(int32_t* p, int n, hipStream_t st);

@@ -3,19 +3,23 @@
 // intra-block similarity check for understanding; "Results": threshold-based assignment and a
 // cosine-similarity constraint on pooling).
 //
-// k_mask_scores  block_mass[b,h,qb,kb]. Rows of a scoring GEMM are either sampled query rows
-//                (sampling mode, S rows per query block) or compressed query rows (antidiagonal
-//                mode, stride S: row r pairs q[rS+S-1-t] with k[cS+t], t < S, summed). One
-//                workgroup owns 128 rows of one (batch, head); it sweeps all 64-column key
-//                tiles twice: pass 0 the row max and sum (online), pass 1 the probabilities,
-//                summed per KV block in-lane and across the rows of each query block with
-//                shuffles. Logits come from v_mfma_f32_32x32x16_bf16 exactly as in the
-//                attention kernel (keys on M, rows on N). No workspace, no atomics.
+// k_mask_logmass per scoring row and KV block, the log2 of the row's unnormalised softmax
+//                mass on the block: L = m + log2(sum_t exp2(z_t c - m)), m the block's max of
+//                z c (z the logits, c = scale * log2 e). Rows of the scoring GEMM are either
+//                sampled query rows (sampling mode, S rows per query block) or compressed query
+//                rows (antidiagonal mode, stride S: row r pairs q[rS+S-1-t] with k[cS+t], t < S,
+//                summed). One workgroup owns 128 rows of one (batch, head) and a range of
+//                64-column key tiles; logits come from v_mfma_f32_32x32x16_bf16 as in the
+//                attention kernel (keys on M, rows on N). One pass, no cross-workgroup state:
+//                the normalisation is left to the assignment.
 // k_block_sim    mean pairwise cosine similarity of each KV block's valid keys, via
 //                sum_{i!=j} khat_i.khat_j = |sum khat|^2 - sum |khat|^2, in float64.
-// k_mask_assign  one workgroup per row: bitonic sort of (mass desc, kb asc) in LDS, then one
-//                lane walks the sorted row with a float64 exclusive running sum (the same
-//                order and precision as a sequential reference), then overrides.
+// k_mask_assign  one workgroup per (batch, head, query block) row. From log-masses: each
+//                scoring row's logsumexp over the KV blocks, block_mass[kb] = the mean over the
+//                query block's valid rows of exp2(L - lse) (written out). Then a bitonic sort of
+//                (mass desc, kb asc) in LDS and one lane walks the sorted row with a float64
+//                exclusive running sum (the same order and precision as a sequential
+//                reference), then the overrides. psa_mask_assign enters with given masses.
 #include <math.h>
 
 #include <algorithm>
@@ -33,31 +37,28 @@ constexpr int kScoreThreads = 64 * kScoreWaves;
 struct ScoreArgs {
     const bf16_bits* q;
     const bf16_bits* k;
-    float* M;
-    float2* part;       // [row groups * 128][nsplit] running (max, sum) per key split, log2 units
+    float* L;           // [B*H][NKB][rows_per_head] log2 masses
     int H, Hkv, N, Nv, BQ, NQB, NKB, causal;
     int64_t qs0, qs1, qs2, ks0, ks1, ks2;
     int rows_per_head;  // sampling: NQB*S; antidiag: N/S
     int RQ;             // rows per query block: sampling S, antidiag BQ/S
     int wg_per_head;    // row groups of 128 per (batch, head)
-    int nsplit;         // key-tile splits per row group
+    int nsplit;         // key-tile ranges per row group
     int tiles_per_split;
     float c;            // scale * log2(e)
 };
 
 // MODE 0: sampling with S samples per query block; MODE 1: antidiagonal with stride S.
-// PASS 0: per split, the online (max, sum) of each row over the split's key tiles.
-// PASS 1: merge the splits into the row's logsumexp, then the probabilities of the split's
-//         tiles, summed per KV block and over the rows of each query block -> block_mass.
-// Workgroup = 128 rows x one split; grid = B*H*wg_per_head*nsplit.
-template <int MODE, int D, int S, int PASS>
-__global__ void __launch_bounds__(kScoreThreads) k_mask_scores(ScoreArgs a) {
+// Workgroup = 128 rows x one range of key tiles; grid = B*H*wg_per_head*nsplit.
+template <int MODE, int D, int S>
+__global__ void __launch_bounds__(kScoreThreads) k_mask_logmass(ScoreArgs a) {
     constexpr int SI = MODE == 1 ? S : 1;          // inner chunks of D
     constexpr int CPK = MODE == 1 ? 64 / S : 64;   // columns per KV block
     constexpr int KT = 64 / CPK;                   // KV blocks per 64-column tile
     constexpr int KSTR = D + 8;
     constexpr int KCH = 64 * (D / 8) / kScoreThreads;
     static_assert(KCH >= 1, "tile");
+    static_assert(CPK >= 8, "a KV block's columns are whole runs of 4 in each lane half");
     __shared__ __attribute__((aligned(16))) bf16_bits Ks[64 * KSTR];
 
     const int tid = threadIdx.x;
@@ -86,8 +87,10 @@ __global__ void __launch_bounds__(kScoreThreads) k_mask_scores(ScoreArgs a) {
     } else {
         row_ok = r < a.rows_per_head && (r * S + S - 1) < a.Nv;
     }
-    const int64_t slot = static_cast<int64_t>(rg) * 128 + wave * 32 + l32;  // workspace row
     const bool row_in = r < a.rows_per_head;
+    // log-mass of (row r, block kb) lives at Lh[kb * rows_per_head + r]: the 32 rows of a wave
+    // store one contiguous 128-byte run per block
+    float* Lh = a.L + static_cast<int64_t>(bh) * a.NKB * a.rows_per_head;
 
     const bf16_bits* qbase = a.q + b * a.qs0 + h * a.qs1;
     const bf16_bits* kbase = a.k + b * a.ks0 + hk * a.ks1;
@@ -137,31 +140,6 @@ __global__ void __launch_bounds__(kScoreThreads) k_mask_scores(ScoreArgs a) {
         }
     };
 
-    float m_run = -INFINITY, l_run = 0.f, m_ref = 0.f, inv_l = 0.f;
-    if (PASS == 1) {
-        // merge the splits: lse in log2 units is m + log2(l); here p = exp2(s*c - m) / l
-        float m = -INFINITY;
-        for (int sp = 0; sp < a.nsplit; ++sp) m = fmaxf(m, a.part[slot * a.nsplit + sp].x);
-        float l = 0.f;
-        if (m != -INFINITY)
-            for (int sp = 0; sp < a.nsplit; ++sp) {
-                const float2 pr = a.part[slot * a.nsplit + sp];
-                if (pr.y > 0.f) l += pr.y * fast_exp2(pr.x - m);
-            }
-        m_ref = m == -INFINITY ? 0.f : m;
-        inv_l = (row_ok && l > 0.f) ? 1.f / l : 0.f;
-    }
-    auto write_zero_tile = [&](int j) {
-        if (hi == 0 && (l32 % a.RQ) == 0) {
-            const int qb = r / a.RQ;
-            if (qb < a.NQB && row_in) {
-                float* Mrow = a.M + (static_cast<int64_t>(bh) * a.NQB + qb) * a.NKB;
-#pragma unroll
-                for (int kt = 0; kt < KT; ++kt) Mrow[j * KT + kt] = 0.f;
-            }
-        }
-    };
-
     if (j_lo < j_end) load_k(j_lo, 0);
     for (int j = j_lo; j < j_end; ++j) {
         f32x16 sacc[2];
@@ -191,7 +169,7 @@ __global__ void __launch_bounds__(kScoreThreads) k_mask_scores(ScoreArgs a) {
                     sacc[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], sacc[kh], 0, 0, 0);
                 }
         }
-        // mask
+        // mask: lane value e of half kh is column j*64 + kh*32 + (e/4)*8 + hi*4 + e%4
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
@@ -204,61 +182,43 @@ __global__ void __launch_bounds__(kScoreThreads) k_mask_scores(ScoreArgs a) {
                     ok = row_ok && (cc * S + S - 1) < a.Nv && (!a.causal || cc <= r);
                 if (!ok) sacc[kh][e] = -INFINITY;
             }
-        if (PASS == 0) {
-            float mt = -INFINITY;
+        // per KV block of the tile: max, then the sum of exp2 relative to it (the block's
+        // columns are whole 8-column groups, half in each lane of a lane pair)
+        float Lk[KT];
 #pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
+        for (int kt = 0; kt < KT; ++kt) {
+            constexpr int G8 = CPK / 8;   // 8-column groups per block
+            float m = -INFINITY;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) mt = fmaxf(mt, sacc[kh][e]);
-            mt = pair32_max(mt);
-            const float m_new = fmaxf(m_run, mt * a.c);
-            const float mr = m_new == -INFINITY ? 0.f : m_new;
-            l_run *= fast_exp2(m_run - mr);
-            m_run = m_new;
+            for (int g = 0; g < G8; ++g) {
+                const int gg = kt * G8 + g;   // group 0..7 of the tile: half gg/4, e = (gg%4)*4 + i
 #pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) l_run += fast_exp2(fmaf(sacc[kh][e], a.c, -mr));
-        } else {
-            float part[KT];
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt) part[kt] = 0.f;
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int kt = (kh * 32 + (e >> 2) * 8) / CPK;
-                    part[kt] += fast_exp2(fmaf(sacc[kh][e], a.c, -m_ref)) * inv_l;
-                }
-#pragma unroll
-            for (int kt = 0; kt < KT; ++kt) {
-                float x = pair32_sum(part[kt]);
-                for (int o = 1; o < a.RQ; o <<= 1) x += __shfl_xor(x, o, 64);
-                part[kt] = x;
+                for (int i = 0; i < 4; ++i) m = fmaxf(m, sacc[gg >> 2][(gg & 3) * 4 + i]);
             }
-            if (hi == 0 && (l32 % a.RQ) == 0) {
-                const int qb = r / a.RQ;
-                if (qb < a.NQB && row_in) {
-                    int den;
-                    if (MODE == 0)
-                        den = min(max(a.Nv - qb * a.BQ, 0), a.BQ) > 0 ? S : 0;
-                    else
-                        den = min(max(a.Nv / S - qb * a.RQ, 0), a.RQ);
-                    const float invd = den > 0 ? 1.f / static_cast<float>(den) : 0.f;
-                    float* Mrow = a.M + (static_cast<int64_t>(bh) * a.NQB + qb) * a.NKB;
+            m = pair32_max(m);
+            const float mc = m * a.c;
+            float sum = 0.f;
+            if (m != -INFINITY) {
 #pragma unroll
-                    for (int kt = 0; kt < KT; ++kt) Mrow[j * KT + kt] = part[kt] * invd;
+                for (int g = 0; g < G8; ++g) {
+                    const int gg = kt * G8 + g;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) sum += fast_exp2(fmaf(sacc[gg >> 2][(gg & 3) * 4 + i], a.c, -mc));
                 }
             }
+            sum = pair32_sum(sum);
+            Lk[kt] = sum > 0.f ? mc + __builtin_amdgcn_logf(sum) : -INFINITY;
+        }
+        if (hi == 0 && row_in) {
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) Lh[static_cast<int64_t>(j * KT + kt) * a.rows_per_head + r] = Lk[kt];
         }
     }
-    if (PASS == 0) {
-        l_run = pair32_sum(l_run);
-        if (hi == 0) a.part[slot * a.nsplit + split] = make_float2(m_run, l_run);
-    } else {
-        // fully masked tiles of this split (past the causal frontier) still get their zeros
-        for (int j = max(j_lo, j_end); j < j_hi; ++j) write_zero_tile(j);
-    }
+    // tiles of this range past the causal frontier: no mass
+    if (hi == 0 && row_in)
+        for (int j = max(j_lo, j_end); j < j_hi; ++j)
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) Lh[static_cast<int64_t>(j * KT + kt) * a.rows_per_head + r] = -INFINITY;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -315,11 +275,14 @@ __global__ void __launch_bounds__(256)
 constexpr int kAssignThreads = 256;
 
 struct AssignArgs {
-    const float* M;
+    const float* M;     // given masses [rows][NKB] (psa_mask_assign), or null
+    const float* L;     // log2 masses [B*H][NKB][rows_per_head] (psa_mask), or null
+    float* M_out;       // masses computed from L, written here
     const float* sim;
     int8_t* map;
     int H, Hkv, N, Nv, BQ, BK, NQB, NKB, causal;
     int P;  // sort length: power of two >= NKB
+    int RQ, rows_per_head, sampling, S;   // scoring rows per query block (L path)
     double t[4];
     float cos_min;
     int force_diag, force_lo, force_hi;
@@ -331,8 +294,10 @@ __device__ __forceinline__ uint32_t float_order(float f) {
 }
 
 __global__ void __launch_bounds__(kAssignThreads) k_mask_assign(AssignArgs a) {
-    extern __shared__ uint64_t keys[];  // P sort keys, then NKB int8 levels
-    int8_t* lvl = reinterpret_cast<int8_t*>(keys + a.P);
+    extern __shared__ uint64_t keys[];  // P sort keys, then NKB masses, then NKB int8 levels
+    float* Ms = reinterpret_cast<float*>(keys + a.P);
+    int8_t* lvl = reinterpret_cast<int8_t*>(Ms + a.NKB);
+    __shared__ float lse[32];           // per scoring row of the query block (L path)
     const int64_t row = blockIdx.x;
     const int qb = static_cast<int>(row % a.NQB);
     const int bh = static_cast<int>(row / a.NQB);
@@ -340,7 +305,8 @@ __global__ void __launch_bounds__(kAssignThreads) k_mask_assign(AssignArgs a) {
     const int b = bh / a.H;
     const int hk = h / (a.H / a.Hkv);
     const int tid = threadIdx.x;
-    const float* Mrow = a.M + row * a.NKB;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     int8_t* out = a.map + row * a.NKB;
 
     const int qlo = qb * a.BQ, qhi = qlo + a.BQ;
@@ -348,9 +314,49 @@ __global__ void __launch_bounds__(kAssignThreads) k_mask_assign(AssignArgs a) {
     const int last = a.causal ? min((qhi - 1) / a.BK, a.NKB - 1) : a.NKB - 1;
     const int ncand = last + 1;
 
+    if (a.L != nullptr) {
+        // masses from log-masses: row i of the query block's scoring rows has logsumexp
+        // lse_i = log2 sum_kb exp2(L_i,kb); mass_kb = mean over the valid rows of
+        // exp2(L_i,kb - lse_i). Rows with no visible key have L = -inf everywhere.
+        const float* Lh = a.L + static_cast<int64_t>(bh) * a.NKB * a.rows_per_head + qb * a.RQ;
+        for (int i = wave; i < a.RQ; i += kAssignThreads / 64) {
+            float m = -INFINITY;
+            for (int kb = lane; kb < a.NKB; kb += 64) m = fmaxf(m, Lh[static_cast<int64_t>(kb) * a.rows_per_head + i]);
+            m = wave_max(m);
+            float sum = 0.f;
+            if (m != -INFINITY)
+                for (int kb = lane; kb < a.NKB; kb += 64)
+                    sum += fast_exp2(Lh[static_cast<int64_t>(kb) * a.rows_per_head + i] - m);
+            sum = wave_sum(sum);
+            if (lane == 0) lse[i] = m == -INFINITY ? -INFINITY : m + __builtin_amdgcn_logf(sum);
+        }
+        __syncthreads();
+        int den;
+        if (a.sampling)
+            den = min(max(a.Nv - qb * a.BQ, 0), a.BQ) > 0 ? a.RQ : 0;
+        else
+            den = min(max(a.Nv / a.S - qb * a.RQ, 0), a.RQ);
+        const float invd = den > 0 ? 1.f / static_cast<float>(den) : 0.f;
+        float* Mo = a.M_out + row * a.NKB;
+        for (int kb = tid; kb < a.NKB; kb += kAssignThreads) {
+            float acc = 0.f;
+            for (int i = 0; i < a.RQ; ++i) {
+                const float li = lse[i];
+                if (li != -INFINITY) acc += fast_exp2(Lh[static_cast<int64_t>(kb) * a.rows_per_head + i] - li);
+            }
+            acc *= invd;
+            Ms[kb] = acc;
+            Mo[kb] = acc;
+        }
+    } else {
+        const float* Mrow = a.M + row * a.NKB;
+        for (int kb = tid; kb < a.NKB; kb += kAssignThreads) Ms[kb] = Mrow[kb];
+    }
+    __syncthreads();
+
     for (int i = tid; i < a.P; i += kAssignThreads) {
         uint64_t key = ~0ull;
-        if (i < ncand) key = (static_cast<uint64_t>(~float_order(Mrow[i])) << 32) | static_cast<uint32_t>(i);
+        if (i < ncand) key = (static_cast<uint64_t>(~float_order(Ms[i])) << 32) | static_cast<uint32_t>(i);
         keys[i] = key;
     }
     for (int i = tid; i < a.NKB; i += kAssignThreads) lvl[i] = -1;
@@ -381,7 +387,7 @@ __global__ void __launch_bounds__(kAssignThreads) k_mask_assign(AssignArgs a) {
             else if (c < a.t[2]) L = 2;
             else if (c < a.t[3]) L = 3;
             lvl[kb] = L;
-            c += static_cast<double>(Mrow[kb]);
+            c += static_cast<double>(Ms[kb]);
         }
     }
     __syncthreads();
@@ -403,43 +409,68 @@ __global__ void __launch_bounds__(kAssignThreads) k_mask_assign(AssignArgs a) {
     }
 }
 
-template <int MODE, int D, int S>
-hipError_t launch_scores(const ScoreArgs& a, int blocks, hipStream_t st) {
-    hipLaunchKernelGGL((k_mask_scores<MODE, D, S, 0>), dim3(blocks), dim3(kScoreThreads), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_mask_scores<MODE, D, S, 1>), dim3(blocks), dim3(kScoreThreads), 0, st, a);
+template <int MODE, int S>
+hipError_t launch_scores_d(const ScoreArgs& a, int D, int blocks, hipStream_t st) {
+    if (D == 128)
+        hipLaunchKernelGGL((k_mask_logmass<MODE, 128, S>), dim3(blocks), dim3(kScoreThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((k_mask_logmass<MODE, 64, S>), dim3(blocks), dim3(kScoreThreads), 0, st, a);
     return hipGetLastError();
 }
 
-template <int MODE, int S>
-hipError_t launch_scores_d(const ScoreArgs& a, int D, int blocks, hipStream_t st) {
-    return D == 128 ? launch_scores<MODE, 128, S>(a, blocks, st)
-                    : launch_scores<MODE, 64, S>(a, blocks, st);
-}
-
-// Row groups, key-tile splits and their workspace for a problem.
+// Row groups, key-tile ranges and the log-mass workspace for a problem.
 struct ScoreGeom {
-    int rows_per_head, RQ, wg_per_head, ntiles, nsplit, tiles_per_split;
+    int S, rows_per_head, RQ, wg_per_head, ntiles, nsplit, tiles_per_split;
     size_t ws_bytes;
 };
 
 ScoreGeom score_geom(const Shape& s, const psa_mask_params& mp) {
     ScoreGeom g;
     const bool sampling = mp.mode == PSA_MASK_SAMPLING;
-    const int S = sampling ? mp.samples_per_qblock : mp.antidiag_stride;
-    g.rows_per_head = sampling ? s.NQB * S : s.N / S;
-    g.RQ = sampling ? S : s.BQ / S;
+    g.S = sampling ? mp.samples_per_qblock : mp.antidiag_stride;
+    g.rows_per_head = sampling ? s.NQB * g.S : s.N / g.S;
+    g.RQ = sampling ? g.S : s.BQ / g.S;
     g.wg_per_head = (g.rows_per_head + 127) / 128;
-    g.ntiles = (sampling ? s.N : s.N / S) / 64;
-    // enough workgroups to fill the chip several times over; at least 4 tiles per split
+    g.ntiles = (sampling ? s.N : s.N / g.S) / 64;
+    // enough workgroups to fill the chip several times over; at least 4 tiles per range
     const int64_t groups = static_cast<int64_t>(s.B) * s.H * g.wg_per_head;
     int64_t want = groups > 0 ? (2048 + groups - 1) / groups : 1;
     want = std::max<int64_t>(1, std::min<int64_t>(want, std::max(1, g.ntiles / 4)));
     g.tiles_per_split = (g.ntiles + static_cast<int>(want) - 1) / static_cast<int>(want);
     g.nsplit = g.tiles_per_split > 0 ? (g.ntiles + g.tiles_per_split - 1) / g.tiles_per_split : 1;
-    g.ws_bytes = static_cast<size_t>(groups) * 128 * g.nsplit * sizeof(float2);
+    g.ws_bytes = static_cast<size_t>(s.B) * s.H * s.NKB * g.rows_per_head * sizeof(float);
     return g;
+}
+
+AssignArgs assign_args(const Shape& s, const psa_mask_params& mp) {
+    AssignArgs a{};
+    a.H = s.H;
+    a.Hkv = s.Hkv;
+    a.N = s.N;
+    a.Nv = s.Nv;
+    a.BQ = s.BQ;
+    a.BK = s.BK;
+    a.NQB = s.NQB;
+    a.NKB = s.NKB;
+    a.causal = s.causal;
+    int P = 1;
+    while (P < s.NKB) P <<= 1;
+    a.P = P;
+    for (int i = 0; i < 4; ++i) a.t[i] = static_cast<double>(mp.thresholds[i]);
+    a.cos_min = mp.cos_sim_min;
+    a.force_diag = mp.force_diag_l0 != 0;
+    a.force_lo = mp.force_l0_begin;
+    a.force_hi = mp.force_l0_end;
+    return a;
+}
+
+hipError_t launch_assign(const Shape& s, const AssignArgs& a, hipStream_t st) {
+    const int64_t rows = static_cast<int64_t>(s.B) * s.H * s.NQB;
+    if (rows == 0) return hipSuccess;
+    const size_t lds = static_cast<size_t>(a.P) * sizeof(uint64_t) + static_cast<size_t>(s.NKB) * (sizeof(float) + 1);
+    if (lds > 64 * 1024) return hipErrorNotSupported;
+    hipLaunchKernelGGL(k_mask_assign, dim3(static_cast<unsigned>(rows)), dim3(kAssignThreads), lds, st, a);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -454,7 +485,6 @@ hipError_t launch_mask_scores(const Shape& s, const psa_mask_params& mp, const v
     ScoreArgs a;
     a.q = static_cast<const bf16_bits*>(q);
     a.k = static_cast<const bf16_bits*>(k);
-    a.M = mb.block_mass;
     a.H = s.H;
     a.Hkv = s.Hkv;
     a.N = s.N;
@@ -466,10 +496,9 @@ hipError_t launch_mask_scores(const Shape& s, const psa_mask_params& mp, const v
     a.qs0 = s.qs[0]; a.qs1 = s.qs[1]; a.qs2 = s.qs[2];
     a.ks0 = s.ks[0]; a.ks1 = s.ks[1]; a.ks2 = s.ks[2];
     a.c = (1.0f / sqrtf(static_cast<float>(s.D))) * kLog2e;
-    const int S = mp.mode == PSA_MASK_SAMPLING ? mp.samples_per_qblock : mp.antidiag_stride;
     const ScoreGeom g = score_geom(s, mp);
     if (mb.ws == nullptr || mb.ws_bytes < g.ws_bytes) return hipErrorInvalidValue;
-    a.part = static_cast<float2*>(mb.ws);
+    a.L = static_cast<float*>(mb.ws);
     a.rows_per_head = g.rows_per_head;
     a.RQ = g.RQ;
     a.wg_per_head = g.wg_per_head;
@@ -478,7 +507,7 @@ hipError_t launch_mask_scores(const Shape& s, const psa_mask_params& mp, const v
     const int blocks = s.B * s.H * a.wg_per_head * a.nsplit;
     if (blocks == 0) return hipSuccess;
     if (mp.mode == PSA_MASK_SAMPLING) {
-        switch (S) {
+        switch (g.S) {
             case 1: return launch_scores_d<0, 1>(a, s.D, blocks, st);
             case 2: return launch_scores_d<0, 2>(a, s.D, blocks, st);
             case 4: return launch_scores_d<0, 4>(a, s.D, blocks, st);
@@ -489,12 +518,28 @@ hipError_t launch_mask_scores(const Shape& s, const psa_mask_params& mp, const v
         }
     }
     if (a.RQ > 32 || a.RQ < 1) return hipErrorNotSupported;
-    switch (S) {
+    switch (g.S) {
         case 2: return launch_scores_d<1, 2>(a, s.D, blocks, st);
         case 4: return launch_scores_d<1, 4>(a, s.D, blocks, st);
         case 8: return launch_scores_d<1, 8>(a, s.D, blocks, st);
         default: return hipErrorNotSupported;
     }
+}
+
+hipError_t launch_mask_assign_logmass(const Shape& s, const psa_mask_params& mp, const MaskBufs& mb,
+                                      int8_t* level_map, hipStream_t st) {
+    const ScoreGeom g = score_geom(s, mp);
+    if (mb.ws == nullptr || mb.ws_bytes < g.ws_bytes) return hipErrorInvalidValue;
+    AssignArgs a = assign_args(s, mp);
+    a.L = static_cast<const float*>(mb.ws);
+    a.M_out = mb.block_mass;
+    a.sim = mp.cos_sim_min > 0.f ? mb.block_sim : nullptr;
+    a.map = level_map;
+    a.RQ = g.RQ;
+    a.rows_per_head = g.rows_per_head;
+    a.sampling = mp.mode == PSA_MASK_SAMPLING;
+    a.S = g.S;
+    return launch_assign(s, a, st);
 }
 
 hipError_t launch_block_sim(const Shape& s, const void* k, float* block_sim, hipStream_t st) {
@@ -515,34 +560,11 @@ hipError_t launch_block_sim(const Shape& s, const void* k, float* block_sim, hip
 
 hipError_t launch_mask_assign(const Shape& s, const psa_mask_params& mp, const float* block_mass,
                               const float* block_sim, int8_t* level_map, hipStream_t st) {
-    AssignArgs a;
+    AssignArgs a = assign_args(s, mp);
     a.M = block_mass;
     a.sim = mp.cos_sim_min > 0.f ? block_sim : nullptr;
     a.map = level_map;
-    a.H = s.H;
-    a.Hkv = s.Hkv;
-    a.N = s.N;
-    a.Nv = s.Nv;
-    a.BQ = s.BQ;
-    a.BK = s.BK;
-    a.NQB = s.NQB;
-    a.NKB = s.NKB;
-    a.causal = s.causal;
-    int P = 1;
-    while (P < s.NKB) P <<= 1;
-    a.P = P;
-    for (int i = 0; i < 4; ++i) a.t[i] = static_cast<double>(mp.thresholds[i]);
-    a.cos_min = mp.cos_sim_min;
-    a.force_diag = mp.force_diag_l0 != 0;
-    a.force_lo = mp.force_l0_begin;
-    a.force_hi = mp.force_l0_end;
-    const int64_t rows = static_cast<int64_t>(s.B) * s.H * s.NQB;
-    if (rows == 0) return hipSuccess;
-    const size_t lds = static_cast<size_t>(P) * sizeof(uint64_t) + static_cast<size_t>(s.NKB);
-    if (lds > 64 * 1024) return hipErrorNotSupported;
-    hipLaunchKernelGGL(k_mask_assign, dim3(static_cast<unsigned>(rows)), dim3(kAssignThreads),
-                       lds, st, a);
-    return hipGetLastError();
+    return launch_assign(s, a, st);
 }
 
 }  // namespace psa
