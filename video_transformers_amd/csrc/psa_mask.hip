@@ -17,9 +17,10 @@
 // k_mask_assign  one workgroup per (batch, head, query block) row. From log-masses: each
 //                scoring row's logsumexp over the KV blocks, block_mass[kb] = the mean over the
 //                query block's valid rows of exp2(L - lse) (written out). Then a bitonic sort of
-//                (mass desc, kb asc) in LDS and one lane walks the sorted row with a float64
-//                exclusive running sum (the same order and precision as a sequential
-//                reference), then the overrides. psa_mask_assign enters with given masses.
+//                (mass desc, kb asc) in LDS, a float64 exclusive block scan of the sorted
+//                masses (equal to a left-to-right float64 sum up to float64 rounding) gives
+//                each block its level, then the overrides. psa_mask_assign enters with given
+//                masses.
 #include <math.h>
 
 #include <algorithm>
@@ -293,10 +294,15 @@ __device__ __forceinline__ uint32_t float_order(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+__device__ __forceinline__ float float_from_order(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
 __global__ void __launch_bounds__(kAssignThreads) k_mask_assign(AssignArgs a) {
-    extern __shared__ uint64_t keys[];  // P sort keys, then NKB masses, then NKB int8 levels
+    // P sort keys, NKB masses, (log-mass path) NKB * RQ staged log-masses, NKB int8 levels
+    extern __shared__ uint64_t keys[];
     float* Ms = reinterpret_cast<float*>(keys + a.P);
-    int8_t* lvl = reinterpret_cast<int8_t*>(Ms + a.NKB);
+    int8_t* lvl = reinterpret_cast<int8_t*>(Ms + a.NKB + (a.L != nullptr ? a.NKB * a.RQ : 0));
     __shared__ float lse[32];           // per scoring row of the query block (L path)
     const int64_t row = blockIdx.x;
     const int qb = static_cast<int>(row % a.NQB);
@@ -315,38 +321,71 @@ __global__ void __launch_bounds__(kAssignThreads) k_mask_assign(AssignArgs a) {
     const int ncand = last + 1;
 
     if (a.L != nullptr) {
-        // masses from log-masses: row i of the query block's scoring rows has logsumexp
-        // lse_i = log2 sum_kb exp2(L_i,kb); mass_kb = mean over the valid rows of
-        // exp2(L_i,kb - lse_i). Rows with no visible key have L = -inf everywhere.
-        const float* Lh = a.L + static_cast<int64_t>(bh) * a.NKB * a.rows_per_head + qb * a.RQ;
-        for (int i = wave; i < a.RQ; i += kAssignThreads / 64) {
-            float m = -INFINITY;
-            for (int kb = lane; kb < a.NKB; kb += 64) m = fmaxf(m, Lh[static_cast<int64_t>(kb) * a.rows_per_head + i]);
-            m = wave_max(m);
-            float sum = 0.f;
-            if (m != -INFINITY)
-                for (int kb = lane; kb < a.NKB; kb += 64)
-                    sum += fast_exp2(Lh[static_cast<int64_t>(kb) * a.rows_per_head + i] - m);
-            sum = wave_sum(sum);
-            if (lane == 0) lse[i] = m == -INFINITY ? -INFINITY : m + __builtin_amdgcn_logf(sum);
+        // masses from log-masses: scoring row i of the query block has logsumexp
+        // lse_i = log2 sum_kb exp2(L[kb][i]); mass_kb = mean over the valid rows of
+        // exp2(L[kb][i] - lse_i). Rows with no visible key have L = -inf everywhere.
+        // The RQ rows of one block are contiguous in the workspace: the block's values are
+        // staged in LDS (Ls[kb * RQ + i]) with independent loads, thread t taking row
+        // i = t % RQ of blocks t / RQ + k * (256 / RQ).
+        const int RQ = a.RQ;   // power of two <= 32
+        const int i = tid & (RQ - 1);
+        const int kstep = kAssignThreads / RQ;
+        float* Ls = Ms + a.NKB;   // NKB * RQ floats, after the masses
+        {
+            const float* Lh = a.L + static_cast<int64_t>(bh) * a.NKB * a.rows_per_head + qb * RQ + i;
+#pragma unroll 8
+            for (int kb = tid / RQ; kb < a.NKB; kb += kstep)
+                Ls[kb * RQ + i] = Lh[static_cast<int64_t>(kb) * a.rows_per_head];
+        }
+        __syncthreads();
+        float m = -INFINITY, sum = 0.f;   // online logsumexp of this thread's values
+        for (int kb = tid / RQ; kb < a.NKB; kb += kstep) {
+            const float v = Ls[kb * RQ + i];
+            const float mn = fmaxf(m, v);
+            if (mn != -INFINITY) sum = sum * fast_exp2(m - mn) + fast_exp2(v - mn);
+            m = mn;
+        }
+        // merge across the lanes of the same row (lane xor RQ, 2 RQ, ... 32), then the waves
+        for (int o = RQ; o < 64; o <<= 1) {
+            const float mo = __shfl_xor(m, o, 64);
+            const float so = __shfl_xor(sum, o, 64);
+            const float mn = fmaxf(m, mo);
+            sum = mn == -INFINITY ? 0.f : sum * fast_exp2(m - mn) + so * fast_exp2(mo - mn);
+            m = mn;
+        }
+        __shared__ float wm[kAssignThreads / 64][32], ws[kAssignThreads / 64][32];
+        if (lane < RQ) {
+            wm[wave][lane] = m;
+            ws[wave][lane] = sum;
+        }
+        __syncthreads();
+        if (tid < RQ) {
+            float mm = -INFINITY, ss = 0.f;
+            for (int w = 0; w < kAssignThreads / 64; ++w) {
+                const float mo = wm[w][tid], so = ws[w][tid];
+                const float mn = fmaxf(mm, mo);
+                ss = mn == -INFINITY ? 0.f : ss * fast_exp2(mm - mn) + so * fast_exp2(mo - mn);
+                mm = mn;
+            }
+            lse[tid] = (mm == -INFINITY || ss <= 0.f) ? -INFINITY : mm + __builtin_amdgcn_logf(ss);
         }
         __syncthreads();
         int den;
         if (a.sampling)
-            den = min(max(a.Nv - qb * a.BQ, 0), a.BQ) > 0 ? a.RQ : 0;
+            den = min(max(a.Nv - qb * a.BQ, 0), a.BQ) > 0 ? RQ : 0;
         else
-            den = min(max(a.Nv / a.S - qb * a.RQ, 0), a.RQ);
+            den = min(max(a.Nv / a.S - qb * RQ, 0), RQ);
         const float invd = den > 0 ? 1.f / static_cast<float>(den) : 0.f;
         float* Mo = a.M_out + row * a.NKB;
         for (int kb = tid; kb < a.NKB; kb += kAssignThreads) {
             float acc = 0.f;
-            for (int i = 0; i < a.RQ; ++i) {
-                const float li = lse[i];
-                if (li != -INFINITY) acc += fast_exp2(Lh[static_cast<int64_t>(kb) * a.rows_per_head + i] - li);
+            for (int r = 0; r < RQ; ++r) {
+                const float lr = lse[r];
+                if (lr != -INFINITY) acc += fast_exp2(Ls[kb * RQ + r] - lr);
             }
-            acc *= invd;
-            Ms[kb] = acc;
-            Mo[kb] = acc;
+            const float mass = acc * invd;
+            Ms[kb] = mass;
+            Mo[kb] = mass;
         }
     } else {
         const float* Mrow = a.M + row * a.NKB;
@@ -377,17 +416,44 @@ __global__ void __launch_bounds__(kAssignThreads) k_mask_assign(AssignArgs a) {
             __syncthreads();
         }
     }
-    if (tid == 0 && any_valid) {
-        double c = 0.0;
-        for (int i = 0; i < ncand; ++i) {
-            const int kb = static_cast<int>(keys[i] & 0xffffffffu);
-            int8_t L = -1;
-            if (c < a.t[0]) L = 0;
-            else if (c < a.t[1]) L = 1;
-            else if (c < a.t[2]) L = 2;
-            else if (c < a.t[3]) L = 3;
-            lvl[kb] = L;
-            c += static_cast<double>(Ms[kb]);
+    // Exclusive running sum of the sorted masses in float64 (a block scan; the summation
+    // order differs from a left-to-right loop only in float64 rounding, ~1e-16 relative),
+    // then each sorted entry's level from its exclusive sum. The mass comes back out of the
+    // sort key.
+    {
+        const int per = a.P / kAssignThreads > 0 ? a.P / kAssignThreads : 1;   // entries per thread
+        const int i0 = tid * per;
+        double loc = 0.0;
+        for (int u = 0; u < per; ++u) {
+            const int i = i0 + u;
+            if (i < ncand) loc += static_cast<double>(float_from_order(~static_cast<uint32_t>(keys[i] >> 32)));
+        }
+        // inclusive scan of the per-thread totals: within the wave, then across the waves
+        double inc = loc;
+        for (int o = 1; o < 64; o <<= 1) {
+            const double y = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += y;
+        }
+        __shared__ double wsum[kAssignThreads / 64];
+        if (lane == 63) wsum[wave] = inc;
+        __syncthreads();
+        double base = 0.0;
+        for (int w = 0; w < wave; ++w) base += wsum[w];
+        double c = base + inc - loc;   // exclusive sum before entry i0
+        if (any_valid) {
+            for (int u = 0; u < per; ++u) {
+                const int i = i0 + u;
+                if (i >= ncand) break;
+                const uint64_t key = keys[i];
+                const int kb = static_cast<int>(key & 0xffffffffu);
+                int8_t L = -1;
+                if (c < a.t[0]) L = 0;
+                else if (c < a.t[1]) L = 1;
+                else if (c < a.t[2]) L = 2;
+                else if (c < a.t[3]) L = 3;
+                lvl[kb] = L;
+                c += static_cast<double>(float_from_order(~static_cast<uint32_t>(key >> 32)));
+            }
         }
     }
     __syncthreads();
@@ -467,7 +533,10 @@ AssignArgs assign_args(const Shape& s, const psa_mask_params& mp) {
 hipError_t launch_assign(const Shape& s, const AssignArgs& a, hipStream_t st) {
     const int64_t rows = static_cast<int64_t>(s.B) * s.H * s.NQB;
     if (rows == 0) return hipSuccess;
-    const size_t lds = static_cast<size_t>(a.P) * sizeof(uint64_t) + static_cast<size_t>(s.NKB) * (sizeof(float) + 1);
+    // sort keys, masses, (log-mass path) the staged log-masses, levels
+    const size_t lds = static_cast<size_t>(a.P) * sizeof(uint64_t) + static_cast<size_t>(s.NKB) * sizeof(float) +
+                       (a.L != nullptr ? static_cast<size_t>(s.NKB) * a.RQ * sizeof(float) : 0) +
+                       static_cast<size_t>(s.NKB);
     if (lds > 64 * 1024) return hipErrorNotSupported;
     hipLaunchKernelGGL(k_mask_assign, dim3(static_cast<unsigned>(rows)), dim3(kAssignThreads), lds, st, a);
     return hipGetLastError();
