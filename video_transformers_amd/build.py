@@ -30,12 +30,13 @@ ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-result"] + DEVICE_FLAGS
-# Per-source extras. The bf16 attention kernel keeps its MFMA accumulators in VGPRs (the
-# online-softmax rescale is VALU work on them; AGPRs then only hold spilled operands), and
-# is compiled without NaN semantics so that max reductions of MFMA results need no
+# Per-source extras. The bf16 attention and mask-scoring kernels keep their MFMA accumulators
+# in VGPRs (the softmax work reads them with VALU instructions; from AGPRs each value would
+# first need a v_accvgpr_read), and the attention kernel is compiled without NaN semantics so that max reductions of MFMA results need no
 # canonicalisation (the kernel masks with -inf, never with NaN; infinities keep their meaning).
 EXTRA = {
     "psa_attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
+    "psa_mask.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

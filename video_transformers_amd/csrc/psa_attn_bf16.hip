@@ -68,26 +68,6 @@ struct Lay {
     static __device__ __forceinline__ int fv(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
-// One 1 KB direct load: lane i's 16 bytes at global address sbase + voff go to LDS bytes
-// [lds + 16 i, lds + 16 i + 16). Written in asm so the compiler does not treat every later
-// LDS read as a possible alias of the in-flight write (it would wait for it); the kernel
-// waits for these loads itself (vmcnt(0) before the barrier that publishes a tile). The
-// instruction has no destination registers; its address operands are read at issue.
-__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
-    // every operand but voff is wave-uniform: pin them to SGPRs
-    // (readfirstlane returns int: widen each half through uint32_t, never by sign extension)
-    const uint64_t b = reinterpret_cast<uint64_t>(sbase);
-    const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(b & 0xffffffffu)));
-    const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(b >> 32)));
-    const uint64_t bs = (static_cast<uint64_t>(hi) << 32) | static_cast<uint64_t>(lo);
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "global_load_lds_dwordx4 %1, %2"
-        :
-        : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(bs)
-        : "memory");
-}
-
 // The K tile row that MFMA A-operand row r reads: bits 2 and 3 of r swapped.
 __device__ __forceinline__ int sigma(int r) {
     return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);

@@ -39,7 +39,7 @@ struct ScoreArgs {
     const bf16_bits* q;
     const bf16_bits* k;
     float* L;           // [B*H][NKB][rows_per_head] log2 masses
-    int H, Hkv, N, Nv, BQ, NQB, NKB, causal;
+    int B, H, Hkv, N, Nv, BQ, NQB, NKB, causal;
     int64_t qs0, qs1, qs2, ks0, ks1, ks2;
     int rows_per_head;  // sampling: NQB*S; antidiag: N/S
     int RQ;             // rows per query block: sampling S, antidiag BQ/S
@@ -220,6 +220,181 @@ __global__ void __launch_bounds__(kScoreThreads) k_mask_logmass(ScoreArgs a) {
         for (int j = max(j_lo, j_end); j < j_hi; ++j)
 #pragma unroll
             for (int kt = 0; kt < KT; ++kt) Lh[static_cast<int64_t>(j * KT + kt) * a.rows_per_head + r] = -INFINITY;
+}
+
+// Sampling mode, the fast path: 64 rows per wave (two groups of 32 sharing every K operand
+// read), 256 rows per workgroup; K tiles move HBM/L2 -> LDS with direct loads into two
+// XOR-swizzled buffers (no VGPR staging), one barrier per tile. Same outputs as
+// k_mask_logmass<0, D, S>.
+constexpr int kSampRows = 256;
+
+template <int D, int S>
+__global__ void __launch_bounds__(kScoreThreads) k_mask_logmass_sampling(ScoreArgs a) {
+    constexpr int KK = D / 16;
+    constexpr int CH = D / 8;                 // 16-byte chunks per K row
+    constexpr int RPI = 1024 / (2 * D);       // K rows per 1 KB direct load
+    constexpr int IPW = 64 / RPI / kScoreWaves;   // direct loads per wave per tile
+    constexpr int KVAR = D == 128 ? 4 : 2;    // distinct chunk swizzles across instructions
+    static_assert(IPW % KVAR == 0, "instruction and its index inside the wave agree mod KVAR");
+    constexpr uint32_t kBuf = 64 * D * 2;
+    __shared__ __attribute__((aligned(1024))) bf16_bits Kt[2][64 * D];
+    auto fk = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+    // XCD-aware order: workgroup i runs on XCD i % 8; each XCD takes a contiguous range of
+    // (head, key range, row group) items, row group fastest, so the workgroups resident on an
+    // XCD read the same K tiles (one head's key ranges) from its L2.
+    const int total = a.B * a.H * a.wg_per_head * a.nsplit;
+    const int nper = (total + 7) >> 3;
+    const int item = (blockIdx.x & 7) * nper + (blockIdx.x >> 3);
+    if (item >= total) return;
+    const int wg = item % a.wg_per_head;
+    const int split = (item / a.wg_per_head) % a.nsplit;
+    const int bh = item / (a.wg_per_head * a.nsplit);
+    const int h = bh % a.H;
+    const int b = bh / a.H;
+    const int hk = h / (a.H / a.Hkv);
+
+    const int r0 = wg * kSampRows + wave * 64;   // group g holds rows r0 + 32 g + l32
+    int tok[2];
+    bool row_ok[2], row_in[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        const int r = r0 + 32 * g + l32;
+        const int qb = r / S;
+        const int rv = qb < a.NQB ? min(max(a.Nv - qb * a.BQ, 0), a.BQ) : 0;
+        row_ok[g] = rv > 0;
+        row_in[g] = r < a.rows_per_head;
+        tok[g] = rv > 0 ? qb * a.BQ + ((r % S) * rv) / S : 0;
+    }
+    float* Lh = a.L + static_cast<int64_t>(bh) * a.NKB * a.rows_per_head;
+
+    bf16x8 qf[2][KK];
+    {
+        const bf16_bits* qbase = a.q + b * a.qs0 + h * a.qs1;
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const bf16_bits* qp = qbase + static_cast<int64_t>(tok[g]) * a.qs2;
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) qf[g][kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16 + hi * 8);
+        }
+    }
+
+    const int ntiles = a.N / 64;
+    int tiles_needed = ntiles;
+    const int r_last = min(wg * kSampRows + kSampRows, a.rows_per_head) - 1;
+    if (a.causal) {
+        const int qb_last = min(r_last / S, a.NQB - 1);
+        tiles_needed = min(ntiles, (qb_last * a.BQ + a.BQ - 1) / 64 + 1);
+    }
+    const int j_lo = split * a.tiles_per_split;
+    const int j_hi = min(ntiles, j_lo + a.tiles_per_split);
+    const int j_end = min(j_hi, tiles_needed);
+    // the smallest sampled token of the workgroup: tiles entirely at or below it and below Nv
+    // need no mask
+    const int tok_min = (wg * kSampRows / S) * a.BQ;
+
+    // direct-load lane offsets: row inside the instruction, swizzled source chunk
+    const bf16_bits* kbase = a.k + b * a.ks0 + hk * a.ks1;
+    const uint32_t kstride = static_cast<uint32_t>(a.ks2) * 2u;
+    uint32_t lpk[KVAR];
+    {
+        const int rr = lane / CH;
+        const int p = lane % CH;
+#pragma unroll
+        for (int q = 0; q < KVAR; ++q)
+            lpk[q] = rr * kstride + static_cast<uint32_t>((p ^ fk(q * RPI + rr)) << 4);
+    }
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)&Kt[0][0]));
+    auto issue = [&](int j, int buf) {
+        // tile j = keys [64 j, 64 j + 64); instruction m covers rows [m RPI, m RPI + RPI)
+        const char* tb = reinterpret_cast<const char*>(kbase) + static_cast<uint32_t>(j * 64) * kstride;
+#pragma unroll
+        for (int mi = 0; mi < IPW; ++mi) {
+            const int m = wave * IPW + mi;
+            dma16(tb + static_cast<uint32_t>(m * RPI) * kstride, lpk[mi % KVAR], lds0 + buf * kBuf + m * 1024);
+        }
+    };
+    // A-operand address of row kh*32 + l32, chunk 2kk + hi: base ^ (32 kk) (see the attention
+    // kernel: the XOR only touches the chunk bits)
+    uint32_t ka_base;
+    {
+        const int r = l32;
+        const int f = fk(r);
+        ka_base = lds0 + static_cast<uint32_t>(r * D * 2 + 16 * ((hi ^ f) & 1) + 16 * (f & ~1));
+    }
+
+    if (j_lo < j_end) issue(j_lo, 0);
+    int buf = 0;
+    for (int j = j_lo; j < j_end; ++j) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's loads of tile j landed
+        __syncthreads();                       // everyone's landed; buffer buf^1 free
+        if (j + 1 < j_end) issue(j + 1, buf ^ 1);
+        f32x16 sacc[2][2];
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) sacc[g][kh][e] = 0.f;
+        const uint32_t kb0 = ka_base + (buf ? kBuf : 0u);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const uint32_t ad = kb0 ^ static_cast<uint32_t>(32 * kk);
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                const bf16x8 ka = *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(ad + kh * 32 * D * 2);
+#pragma unroll
+                for (int g = 0; g < 2; ++g)
+                    sacc[g][kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[g][kk], sacc[g][kh], 0, 0, 0);
+            }
+        }
+        // lane value e of half kh is key 64 j + 32 kh + (e / 4) * 8 + 4 hi + e % 4
+        const bool need_mask = (j * 64 + 63 >= a.Nv) || (a.causal && j * 64 + 63 > tok_min);
+        if (need_mask) {
+            asm volatile("");   // keeps the branch: if-converted, the mask would run on every tile
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int cc = j * 64 + kh * 32 + (e >> 2) * 8 + hi * 4 + (e & 3);
+                        if (!(cc < a.Nv && (!a.causal || cc <= tok[g]))) sacc[g][kh][e] = -INFINITY;
+                    }
+        }
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            // two max chains and four partial sums: short dependency chains
+            float m0 = fmaxf(sacc[g][0][0], sacc[g][0][1]), m1 = fmaxf(sacc[g][1][0], sacc[g][1][1]);
+#pragma unroll
+            for (int e = 2; e < 16; e += 2) {
+                m0 = fmaxf(fmaxf(m0, sacc[g][0][e]), sacc[g][0][e + 1]);
+                m1 = fmaxf(fmaxf(m1, sacc[g][1][e]), sacc[g][1][e + 1]);
+            }
+            const float m = pair32_max(fmaxf(m0, m1));
+            const float mc = m * a.c;
+            float s4[4] = {0.f, 0.f, 0.f, 0.f};
+            if (m != -INFINITY) {
+#pragma unroll
+                for (int e = 0; e < 32; ++e) s4[e & 3] += fast_exp2(fmaf(sacc[g][e >> 4][e & 15], a.c, -mc));
+            }
+            const float sum = pair32_sum((s4[0] + s4[1]) + (s4[2] + s4[3]));
+            const float Lv = (row_ok[g] && sum > 0.f) ? mc + __builtin_amdgcn_logf(sum) : -INFINITY;
+            if (hi == 0 && row_in[g]) Lh[static_cast<int64_t>(j) * a.rows_per_head + r0 + 32 * g + l32] = Lv;
+        }
+        buf ^= 1;
+    }
+    // tiles of this range past the causal frontier: no mass
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+        if (hi == 0 && row_in[g])
+            for (int j = max(j_lo, j_end); j < j_hi; ++j)
+                Lh[static_cast<int64_t>(j) * a.rows_per_head + r0 + 32 * g + l32] = -INFINITY;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -484,9 +659,18 @@ hipError_t launch_scores_d(const ScoreArgs& a, int D, int blocks, hipStream_t st
     return hipGetLastError();
 }
 
+template <int S>
+hipError_t launch_sampling(const ScoreArgs& a, int D, int blocks, hipStream_t st) {
+    if (D == 128)
+        hipLaunchKernelGGL((k_mask_logmass_sampling<128, S>), dim3(blocks), dim3(kScoreThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((k_mask_logmass_sampling<64, S>), dim3(blocks), dim3(kScoreThreads), 0, st, a);
+    return hipGetLastError();
+}
+
 // Row groups, key-tile ranges and the log-mass workspace for a problem.
 struct ScoreGeom {
-    int S, rows_per_head, RQ, wg_per_head, ntiles, nsplit, tiles_per_split;
+    int S, rows_per_head, RQ, rows_per_wg, wg_per_head, ntiles, nsplit, tiles_per_split;
     size_t ws_bytes;
 };
 
@@ -496,7 +680,8 @@ ScoreGeom score_geom(const Shape& s, const psa_mask_params& mp) {
     g.S = sampling ? mp.samples_per_qblock : mp.antidiag_stride;
     g.rows_per_head = sampling ? s.NQB * g.S : s.N / g.S;
     g.RQ = sampling ? g.S : s.BQ / g.S;
-    g.wg_per_head = (g.rows_per_head + 127) / 128;
+    g.rows_per_wg = sampling ? kSampRows : 128;
+    g.wg_per_head = (g.rows_per_head + g.rows_per_wg - 1) / g.rows_per_wg;
     g.ntiles = (sampling ? s.N : s.N / g.S) / 64;
     // enough workgroups to fill the chip several times over; at least 4 tiles per range
     const int64_t groups = static_cast<int64_t>(s.B) * s.H * g.wg_per_head;
@@ -554,6 +739,7 @@ hipError_t launch_mask_scores(const Shape& s, const psa_mask_params& mp, const v
     ScoreArgs a;
     a.q = static_cast<const bf16_bits*>(q);
     a.k = static_cast<const bf16_bits*>(k);
+    a.B = s.B;
     a.H = s.H;
     a.Hkv = s.Hkv;
     a.N = s.N;
@@ -576,13 +762,15 @@ hipError_t launch_mask_scores(const Shape& s, const psa_mask_params& mp, const v
     const int blocks = s.B * s.H * a.wg_per_head * a.nsplit;
     if (blocks == 0) return hipSuccess;
     if (mp.mode == PSA_MASK_SAMPLING) {
+        const int grid = 8 * ((blocks + 7) / 8);   // the kernel remaps blocks XCD-wise
+        // direct loads: K rows 16-byte aligned (the host checks strides), 32-bit offsets
         switch (g.S) {
-            case 1: return launch_scores_d<0, 1>(a, s.D, blocks, st);
-            case 2: return launch_scores_d<0, 2>(a, s.D, blocks, st);
-            case 4: return launch_scores_d<0, 4>(a, s.D, blocks, st);
-            case 8: return launch_scores_d<0, 8>(a, s.D, blocks, st);
-            case 16: return launch_scores_d<0, 16>(a, s.D, blocks, st);
-            case 32: return launch_scores_d<0, 32>(a, s.D, blocks, st);
+            case 1: return launch_sampling<1>(a, s.D, grid, st);
+            case 2: return launch_sampling<2>(a, s.D, grid, st);
+            case 4: return launch_sampling<4>(a, s.D, grid, st);
+            case 8: return launch_sampling<8>(a, s.D, grid, st);
+            case 16: return launch_sampling<16>(a, s.D, grid, st);
+            case 32: return launch_sampling<32>(a, s.D, grid, st);
             default: return hipErrorNotSupported;
         }
     }
