@@ -12,7 +12,8 @@ query/KV blocks 128/64, sampling-mode mask with thresholds 0.5/0.7/0.8/0.9).
 Prints one JSON line. `value` is whole-step throughput: executed level-weighted attention
 FLOPs (4*d per executed (valid query, visible pooled key) pair) per second of step time.
 `attn` gives the attention kernel alone (ms/layer, TFLOP/s, % of the 2.5 PFLOP/s dense bf16
-MFMA peak, speedup over the same kernel on an all-level-0 map). `roofline` is for that
+MFMA peak, speedup over the same kernel on an all-level-0 map, and over the unpacked layout
+with one logical block per hardware tile on the same map). `roofline` is for that
 kernel, timed with HIP events on the stream it runs on. `cpu_baseline` times the CPU oracle
 (fp64 numpy) on a bounded sample of the same workload on this host's cores.
 """
@@ -275,8 +276,26 @@ def run(args) -> dict:
     if not args.no_dense:
         dense_ms = _dense_run(args, wl, prob, L, ptr, st, check, q, k, v, kp, vp, o, lse,
                               row_ptr, col_idx, dev_err, stream)
-    return _report(args, wl, flops, pairs, dpairs, frac, d, B, H, N, computed_map, attn_ms,
-                   attn_ms_mean, st_ms, dense_ms, wall)
+    # same map, same index, one logical block per hardware tile (the unpacked ablation)
+    unpacked_ms = float("nan")
+    if not args.no_unpacked and wl.dtype == "bf16":
+        ue = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        times = []
+        for i in range(4):
+            ue[0].record(stream)
+            check(L.psa_attn_fwd_unpacked(prob.ref(), ctypes.c_float(0.0), ptr(q), ptr(k), ptr(v),
+                                          ptr(kp), ptr(vp), ptr(row_ptr), ptr(col_idx), ptr(o),
+                                          ptr(lse), st), "attn unpacked")
+            ue[1].record(stream)
+            torch.cuda.synchronize()
+            times.append(ue[0].elapsed_time(ue[1]))
+        unpacked_ms = float(np.median(times[1:]))
+    out = _report(args, wl, flops, pairs, dpairs, frac, d, B, H, N, computed_map, attn_ms,
+                  attn_ms_mean, st_ms, dense_ms, wall)
+    out["attn"]["unpacked_same_map_ms"] = None if unpacked_ms != unpacked_ms else round(unpacked_ms, 3)
+    out["attn"]["speedup_vs_unpacked"] = (None if unpacked_ms != unpacked_ms
+                                          else round(unpacked_ms / attn_ms_mean, 2))
+    return out
 
 
 def _dense_run(args, wl, prob, L, ptr, st, check, q, k, v, kp, vp, o, lse, row_ptr, col_idx,
@@ -360,6 +379,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the all-level-0 comparison run (for profiling the PSA launches alone)")
+    ap.add_argument("--no-unpacked", action="store_true",
+                    help="skip the unpacked-layout comparison run (one logical block per tile)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

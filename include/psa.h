@@ -191,6 +191,18 @@ int psa_attn_fwd_indexed(const psa_problem* prob, float softmax_scale, const voi
                          void* o, float* lse, void* stream);
 
 /*
+ * psa_attn_fwd_indexed without the decoupled block-tile packing (summary article, "Results":
+ * the block-tile kernel against a naive implementation): every 64-row hardware tile holds ONE
+ * logical block, so a level-l tile carries 64/2^l pooled rows and masks the rest. Same math
+ * and outputs as psa_attn_fwd_indexed; it exists as the ablation baseline that the packed
+ * kernel is measured against. dtype PSA_BF16 only (PSA_ERR_UNSUPPORTED otherwise).
+ */
+int psa_attn_fwd_unpacked(const psa_problem* prob, float softmax_scale, const void* q,
+                          const void* k, const void* v, const void* k_pooled,
+                          const void* v_pooled, const int32_t* row_ptr, const int32_t* col_idx,
+                          void* o, float* lse, void* stream);
+
+/*
  * Waits for `stream`, then reports device-side errors recorded in `ws` by the last
  * psa_attn_fwd that used it: PSA_OK or PSA_ERR_BAD_LEVEL_MAP (or PSA_ERR_HIP).
  */

@@ -133,6 +133,37 @@ def test_attention_parity(wl):
     check_attention(o, lse, o_ref, lse_ref, wl.seq_valid, wl.dtype == "f32", wl.name)
 
 
+BF16_SMALL = [w for w in SMALL if w.dtype == "bf16"]
+
+
+@pytest.mark.parametrize("wl", BF16_SMALL, ids=[w.name for w in BF16_SMALL])
+def test_unpacked_attention_parity(wl):
+    """The ablation layout (one logical block per hardware tile) computes the same attention."""
+    announce(f"unpacked attention {wl.name}")
+    q, k, v, qd, kd, vd = _inputs(wl)
+    lm = oracle_map(wl, q, k)
+    prob = problem_for(wl, qd, kd, vd)
+    kp, vp = psa.build_pyramid(kd, vd, prob)
+    row_ptr, col_idx, err = psa.build_index(torch.from_numpy(lm).to(DEV), prob)
+    o, lse = psa.attn_fwd_unpacked(qd, kd, vd, kp, vp, row_ptr, col_idx, prob)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    o_ref, lse_ref = oracle.attention(q, k, v, lm, oracle_problem(wl))
+    check_attention(o, lse, o_ref, lse_ref, wl.seq_valid, False, wl.name + " unpacked")
+
+
+def test_unpacked_attention_rejects_f32():
+    announce("unpacked attention f32")
+    wl = W.TINY_F32
+    q, k, v, qd, kd, vd = _inputs(wl)
+    prob = problem_for(wl, qd, kd, vd)
+    kp, vp = psa.build_pyramid(kd, vd, prob)
+    row_ptr, col_idx, err = psa.build_index(torch.from_numpy(W.make_map(wl)).to(DEV), prob)
+    with pytest.raises(psa.PsaError) as ei:
+        psa.attn_fwd_unpacked(qd, kd, vd, kp, vp, row_ptr, col_idx, prob)
+    assert ei.value.status == psa.psa.PSA_ERR_UNSUPPORTED
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("d,bq", [(64, 64), (128, 128), (64, 128), (128, 64)])

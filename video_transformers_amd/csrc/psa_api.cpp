@@ -233,13 +233,15 @@ int psa_attn_fwd(const psa_problem* prob, float softmax_scale, const void* q, co
     hipError_t e = psa::launch_build_index(s, level_map, ib, st);
     if (e != hipSuccess) return hip_status(e);
     return hip_status(psa::launch_attn_fwd(s, scale, q, k, v, k_pooled, v_pooled, w.row_ptr,
-                                           w.col_idx, o, lse, st));
+                                           w.col_idx, o, lse, true, st));
 }
 
-int psa_attn_fwd_indexed(const psa_problem* prob, float softmax_scale, const void* q,
-                         const void* k, const void* v, const void* k_pooled,
-                         const void* v_pooled, const int32_t* row_ptr, const int32_t* col_idx,
-                         void* o, float* lse, void* stream) {
+namespace {
+
+int attn_indexed(const psa_problem* prob, float softmax_scale, const void* q, const void* k,
+                 const void* v, const void* k_pooled, const void* v_pooled,
+                 const int32_t* row_ptr, const int32_t* col_idx, void* o, float* lse,
+                 bool pack, void* stream) {
     psa::Shape s;
     int rc = check_problem(prob, &s);
     if (rc != PSA_OK) return rc;
@@ -250,8 +252,27 @@ int psa_attn_fwd_indexed(const psa_problem* prob, float softmax_scale, const voi
         return PSA_ERR_INVALID_ARG;
     if (!std::isfinite(softmax_scale)) return PSA_ERR_INVALID_ARG;
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(s.D));
+    if (!pack && s.dtype != PSA_BF16) return PSA_ERR_UNSUPPORTED;
     return hip_status(psa::launch_attn_fwd(s, scale, q, k, v, k_pooled, v_pooled, row_ptr,
-                                           col_idx, o, lse, static_cast<hipStream_t>(stream)));
+                                           col_idx, o, lse, pack, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+int psa_attn_fwd_indexed(const psa_problem* prob, float softmax_scale, const void* q,
+                         const void* k, const void* v, const void* k_pooled,
+                         const void* v_pooled, const int32_t* row_ptr, const int32_t* col_idx,
+                         void* o, float* lse, void* stream) {
+    return attn_indexed(prob, softmax_scale, q, k, v, k_pooled, v_pooled, row_ptr, col_idx, o,
+                        lse, true, stream);
+}
+
+int psa_attn_fwd_unpacked(const psa_problem* prob, float softmax_scale, const void* q,
+                          const void* k, const void* v, const void* k_pooled,
+                          const void* v_pooled, const int32_t* row_ptr, const int32_t* col_idx,
+                          void* o, float* lse, void* stream) {
+    return attn_indexed(prob, softmax_scale, q, k, v, k_pooled, v_pooled, row_ptr, col_idx, o,
+                        lse, false, stream);
 }
 
 int psa_check_status(const void* ws, void* stream) {

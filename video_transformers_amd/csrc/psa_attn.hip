@@ -220,7 +220,7 @@ hipError_t launch(Kern kern, int threads, const AttnArgs& a, int64_t rows, hipSt
 hipError_t launch_attn_fwd(const Shape& s, float scale, const void* q, const void* k,
                            const void* v, const void* kp, const void* vp,
                            const int32_t* row_ptr, const int32_t* col_idx, void* o, float* lse,
-                           hipStream_t st) {
+                           bool pack, hipStream_t st) {
     AttnArgs a;
     a.q = q;
     a.k = k;
@@ -246,8 +246,9 @@ hipError_t launch_attn_fwd(const Shape& s, float scale, const void* q, const voi
     const int64_t rows = static_cast<int64_t>(s.B) * s.H * s.NQB;
     if (rows == 0) return hipSuccess;
     if (s.dtype == PSA_BF16) {
-        return launch_attn_bf16(s, a, st);
+        return launch_attn_bf16(s, a, pack, st);
     } else {
+        if (!pack) return hipErrorNotSupported;
         if (s.D == 128 && s.BQ == 128) return launch(k_attn_fwd_f32<128, 128>, 256, a, rows, st);
         if (s.D == 128 && s.BQ == 64) return launch(k_attn_fwd_f32<128, 64>, 128, a, rows, st);
         if (s.D == 64 && s.BQ == 128) return launch(k_attn_fwd_f32<64, 128>, 256, a, rows, st);

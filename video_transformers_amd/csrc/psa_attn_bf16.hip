@@ -85,7 +85,10 @@ using IC = std::integral_constant<int, P>;
 
 // CONTIG: K and V rows are D elements apart (level 0 and the pooled levels share the lane
 // offsets of the direct loads).
-template <int D, int BQ, bool CONTIG>
+// PACK: a tile packs 2^l logical blocks of level l (the decoupled block-tile). Without it
+// every tile holds one logical block and its other rows are masked: the naive layout, kept
+// as the ablation baseline the packing is measured against.
+template <int D, int BQ, bool CONTIG, bool PACK>
 __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int total_rows) {
     constexpr int NW = BQ / 32;
     using LY = Lay<D>;
@@ -161,11 +164,11 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
         }
     };
     auto set_cnt = [&](Tile& t) {
-        if (t.l < 4) t.cnt = min(t.lend - t.base, 1 << t.l);
+        if (t.l < 4) t.cnt = min(t.lend - t.base, PACK ? 1 << t.l : 1);
     };
     auto next_tile = [&](const Tile& t) {
         Tile n = t;
-        n.base += 1 << t.l;
+        n.base += PACK ? 1 << t.l : 1;
         if (n.base >= n.lend) {
             ++n.l;
             enter_level(n);
@@ -606,26 +609,31 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
     }
 }
 
-template <int D, int BQ>
+template <int D, int BQ, bool PACK>
 hipError_t launch_one(const Shape& s, const AttnArgs& a, hipStream_t st) {
     const int rows = s.B * s.H * s.NQB;
     const int nper = (rows + 7) / 8;
     const size_t dyn = static_cast<size_t>(s.NKB) * sizeof(int);
     if (a.ks2 == D && a.vs2 == D)
-        hipLaunchKernelGGL((k_attn_fwd_bf16<D, BQ, true>), dim3(8 * nper), dim3(2 * BQ), dyn, st, a, rows);
+        hipLaunchKernelGGL((k_attn_fwd_bf16<D, BQ, true, PACK>), dim3(8 * nper), dim3(2 * BQ), dyn, st, a, rows);
     else
-        hipLaunchKernelGGL((k_attn_fwd_bf16<D, BQ, false>), dim3(8 * nper), dim3(2 * BQ), dyn, st, a, rows);
+        hipLaunchKernelGGL((k_attn_fwd_bf16<D, BQ, false, PACK>), dim3(8 * nper), dim3(2 * BQ), dyn, st, a, rows);
     return hipGetLastError();
+}
+
+template <bool PACK>
+hipError_t launch_packed(const Shape& s, const AttnArgs& a, hipStream_t st) {
+    if (s.D == 128 && s.BQ == 128) return launch_one<128, 128, PACK>(s, a, st);
+    if (s.D == 128 && s.BQ == 64) return launch_one<128, 64, PACK>(s, a, st);
+    if (s.D == 64 && s.BQ == 128) return launch_one<64, 128, PACK>(s, a, st);
+    if (s.D == 64 && s.BQ == 64) return launch_one<64, 64, PACK>(s, a, st);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_attn_bf16(const Shape& s, const AttnArgs& a, hipStream_t st) {
-    if (s.D == 128 && s.BQ == 128) return launch_one<128, 128>(s, a, st);
-    if (s.D == 128 && s.BQ == 64) return launch_one<128, 64>(s, a, st);
-    if (s.D == 64 && s.BQ == 128) return launch_one<64, 128>(s, a, st);
-    if (s.D == 64 && s.BQ == 64) return launch_one<64, 64>(s, a, st);
-    return hipErrorInvalidValue;
+hipError_t launch_attn_bf16(const Shape& s, const AttnArgs& a, bool pack, hipStream_t st) {
+    return pack ? launch_packed<true>(s, a, st) : launch_packed<false>(s, a, st);
 }
 
 }  // namespace psa

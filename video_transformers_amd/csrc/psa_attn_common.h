@@ -98,6 +98,7 @@ __device__ __forceinline__ RowSrc tile_row(const AttnArgs& a, const TileWalk& tw
 }
 
 
-hipError_t launch_attn_bf16(const Shape& s, const AttnArgs& a, hipStream_t st);
+// pack = false: one logical block per hardware tile (the unpacked ablation baseline).
+hipError_t launch_attn_bf16(const Shape& s, const AttnArgs& a, bool pack, hipStream_t st);
 
 }  // namespace psa

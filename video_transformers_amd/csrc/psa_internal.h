@@ -31,10 +31,11 @@ hipError_t launch_pyramid(const Shape& s, const void* k, const void* v, void* kp
 hipError_t launch_build_index(const Shape& s, const int8_t* level_map, const IndexBufs& ib,
                               hipStream_t st);
 
+// pack = false selects the unpacked ablation layout (bf16 only; hipErrorNotSupported for f32)
 hipError_t launch_attn_fwd(const Shape& s, float scale, const void* q, const void* k,
                            const void* v, const void* kp, const void* vp,
                            const int32_t* row_ptr, const int32_t* col_idx, void* o, float* lse,
-                           hipStream_t st);
+                           bool pack, hipStream_t st);
 
 struct MaskBufs {
     float* block_mass;   // [B,H,NQB,NKB]

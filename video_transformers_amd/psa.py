@@ -31,7 +31,8 @@ SKIP = -1
 # every symbol include/psa.h declares
 EXPORTS = ("psa_pooled_rows", "psa_build_pyramid", "psa_mask_workspace_bytes", "psa_mask",
            "psa_mask_assign", "psa_build_index", "psa_attn_workspace_bytes", "psa_attn_fwd",
-           "psa_attn_fwd_indexed", "psa_check_status", "psa_status_string", "psa_last_hip_error")
+           "psa_attn_fwd_indexed", "psa_attn_fwd_unpacked", "psa_check_status", "psa_status_string",
+           "psa_last_hip_error")
 
 
 class PsaError(RuntimeError):
@@ -84,6 +85,8 @@ def lib() -> ctypes.CDLL:
         L.psa_attn_fwd.restype = I32
         L.psa_attn_fwd_indexed.argtypes = [P, ctypes.c_float, V, V, V, V, V, V, V, V, V, V]
         L.psa_attn_fwd_indexed.restype = I32
+        L.psa_attn_fwd_unpacked.argtypes = [P, ctypes.c_float, V, V, V, V, V, V, V, V, V, V]
+        L.psa_attn_fwd_unpacked.restype = I32
         L.psa_check_status.argtypes, L.psa_check_status.restype = [V, V], I32
         L.psa_status_string.argtypes, L.psa_status_string.restype = [I32], ctypes.c_char_p
         L.psa_last_hip_error.argtypes, L.psa_last_hip_error.restype = [], I32
@@ -269,6 +272,22 @@ def attn_fwd_indexed(q, k, v, k_pooled, v_pooled, row_ptr, col_idx, prob: Proble
                                       _ptr(v), _ptr(k_pooled), _ptr(v_pooled), _ptr(row_ptr),
                                       _ptr(col_idx), _ptr(out), _ptr(lse), _stream(stream)),
            "psa_attn_fwd_indexed")
+    return out, lse
+
+
+def attn_fwd_unpacked(q, k, v, k_pooled, v_pooled, row_ptr, col_idx, prob: Problem, *,
+                      scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                      lse: Optional[torch.Tensor] = None, want_lse: bool = True, stream=None):
+    """attn_fwd_indexed with one logical block per hardware tile (the ablation baseline of the
+    block-tile packing). Returns (o, lse or None)."""
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    _check(lib().psa_attn_fwd_unpacked(prob.ref(), ctypes.c_float(scale), _ptr(q), _ptr(k),
+                                       _ptr(v), _ptr(k_pooled), _ptr(v_pooled), _ptr(row_ptr),
+                                       _ptr(col_idx), _ptr(out), _ptr(lse), _stream(stream)),
+           "psa_attn_fwd_unpacked")
     return out, lse
 
 
