@@ -273,6 +273,10 @@ def test_mask_assign_exact(causal, force_diag, span, cos, nv):
 # mask generator end to end
 # ---------------------------------------------------------------------------------------
 MASKED = [w for w in SMALL if w.map_source == "mask"]
+# the antidiagonal scorer's general path (compressed columns not a whole number of 128-column
+# tiles) next to its fast path above
+MASKED.append(W.small(W.QWEN25VL_32K).replace(name="qwen2.5-vl-7b-small-1536", seq_len=1536,
+                                                  seq_valid=1536))
 
 
 @pytest.mark.parametrize("wl", MASKED, ids=[w.name for w in MASKED])

@@ -397,6 +397,187 @@ __global__ void __launch_bounds__(kScoreThreads) k_mask_logmass_sampling(ScoreAr
                 Lh[static_cast<int64_t>(j) * a.rows_per_head + r0 + 32 * g + l32] = -INFINITY;
 }
 
+// Antidiagonal mode, the fast path. The compressed logit A[r][c] = sum_t q[rS+S-1-t].k[cS+t]
+// is a GEMM with contraction S*D. A workgroup owns 128 compressed rows (32 per wave) and a
+// range of 128-column tiles; per (tile, chunk t) step the K chunk (keys cS+t of the tile's
+// columns) moves HBM/L2 -> LDS by direct loads into two XOR-swizzled buffers while each wave's
+// Q chunk (q[rS+S-1-t] of its rows) is prefetched into registers one step ahead. After the S
+// chunks of a tile the per-block log-masses of its columns are reduced and stored. Same
+// outputs as k_mask_logmass<1, D, S>.
+constexpr int kAdCols = 128;
+
+template <int D, int S>
+__global__ void __launch_bounds__(kScoreThreads) k_mask_logmass_antidiag(ScoreArgs a) {
+    constexpr int KK = D / 16;
+    constexpr int CH = D / 8;
+    constexpr int RPI = 1024 / (2 * D);          // columns per 1 KB direct load
+    constexpr int IPW = kAdCols / RPI / kScoreWaves;
+    constexpr int KVAR = D == 128 ? 4 : 2;
+    static_assert(IPW % KVAR == 0, "instruction and its index inside the wave agree mod KVAR");
+    constexpr uint32_t kBuf = kAdCols * D * 2;
+    constexpr int CPK = 64 / S;                  // compressed columns per KV block
+    constexpr int KT = kAdCols / CPK;            // KV blocks per column tile
+    static_assert(CPK >= 8, "a KV block's columns are whole runs of 4 in each lane half");
+    __shared__ __attribute__((aligned(1024))) bf16_bits Kt[2][kAdCols * D];
+    auto fk = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;
+    const int hi = lane >> 5;
+    // XCD-aware order as in the sampling kernel: row group fastest within a key range
+    const int total = a.B * a.H * a.wg_per_head * a.nsplit;
+    const int nper = (total + 7) >> 3;
+    const int item = (blockIdx.x & 7) * nper + (blockIdx.x >> 3);
+    if (item >= total) return;
+    const int wg = item % a.wg_per_head;
+    const int split = (item / a.wg_per_head) % a.nsplit;
+    const int bh = item / (a.wg_per_head * a.nsplit);
+    const int h = bh % a.H;
+    const int b = bh / a.H;
+    const int hk = h / (a.H / a.Hkv);
+
+    const int r = wg * 128 + wave * 32 + l32;
+    const bool row_in = r < a.rows_per_head;
+    const bool row_ok = row_in && (r * S + S - 1) < a.Nv;
+    float* Lh = a.L + static_cast<int64_t>(bh) * a.NKB * a.rows_per_head;
+
+    const int ncols = a.N / S;
+    const int ntiles = ncols / kAdCols;
+    int tiles_needed = ntiles;
+    if (a.causal) tiles_needed = min(ntiles, (min(wg * 128 + 127, a.rows_per_head - 1)) / kAdCols + 1);
+    const int j_lo = split * a.tiles_per_split;
+    const int j_hi = min(ntiles, j_lo + a.tiles_per_split);
+    const int j_end = min(j_hi, tiles_needed);
+
+    const bf16_bits* kbase = a.k + b * a.ks0 + hk * a.ks1;
+    // the row's last token; chunk t reads S-1-t rows before it (rows without a valid token
+    // read tokens 0..S-1, in bounds, and are masked)
+    const bf16_bits* qrow = a.q + b * a.qs0 + h * a.qs1 + static_cast<int64_t>(row_ok ? r * S + S - 1 : S - 1) * a.qs2;
+    const uint32_t kstride = static_cast<uint32_t>(a.ks2) * 2u;
+    uint32_t lpk[KVAR];
+    {
+        const int rr = lane / CH;
+        const int p = lane % CH;
+#pragma unroll
+        for (int q = 0; q < KVAR; ++q)
+            lpk[q] = rr * (S * kstride) + static_cast<uint32_t>((p ^ fk(q * RPI + rr)) << 4);
+    }
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)&Kt[0][0]));
+    // step u = (tile j_lo + u / S, chunk t = u % S)
+    auto issue = [&](int u, int buf) {
+        const int j = j_lo + u / S;
+        const int t = u % S;
+        const char* tb = reinterpret_cast<const char*>(kbase) +
+                         static_cast<uint32_t>(j * kAdCols * S + t) * kstride;
+#pragma unroll
+        for (int mi = 0; mi < IPW; ++mi) {
+            const int m = wave * IPW + mi;
+            dma16(tb + static_cast<uint32_t>(m * RPI * S) * kstride, lpk[mi % KVAR], lds0 + buf * kBuf + m * 1024);
+        }
+    };
+    bf16x8 qf[KK], qn[KK];
+    auto load_q = [&](int u, bf16x8 (&dst)[KK]) {
+        const int t = u % S;
+        const bf16_bits* qp = qrow - static_cast<int64_t>(t) * a.qs2;   // q[rS + S-1-t]
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) dst[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16 + hi * 8);
+    };
+    uint32_t ka_base;
+    {
+        const int f = fk(l32);
+        ka_base = lds0 + static_cast<uint32_t>(l32 * D * 2 + 16 * ((hi ^ f) & 1) + 16 * (f & ~1));
+    }
+
+    const int steps = (j_end - j_lo) * S;
+    f32x16 sacc[4];
+#pragma unroll
+    for (int kh = 0; kh < 4; ++kh)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[kh][e] = 0.f;
+    if (steps > 0) {
+        issue(0, 0);
+        load_q(0, qf);
+    }
+    int buf = 0;
+    for (int u = 0; u < steps; ++u) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's K loads and Q chunk landed
+        __syncthreads();                       // everyone's landed; buffer buf^1 free
+        if (u + 1 < steps) {
+            issue(u + 1, buf ^ 1);
+            load_q(u + 1, qn);
+        }
+        const uint32_t kb0 = ka_base + (buf ? kBuf : 0u);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const uint32_t ad = kb0 ^ static_cast<uint32_t>(32 * kk);
+#pragma unroll
+            for (int kh = 0; kh < 4; ++kh) {
+                const bf16x8 ka = *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(ad + kh * 32 * D * 2);
+                sacc[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], sacc[kh], 0, 0, 0);
+            }
+        }
+        if (u % S == S - 1) {
+            // tile complete: lane value e of group kh is column 128 j + 32 kh + (e/4)*8 + 4 hi + e%4
+            const int j = j_lo + u / S;
+            const bool need_mask = !row_ok || ((j * kAdCols + kAdCols - 1) * S + S - 1 >= a.Nv) ||
+                                   (a.causal && j * kAdCols + kAdCols - 1 > wg * 128);
+            if (need_mask) {
+                asm volatile("");   // keeps the branch (see the sampling kernel)
+#pragma unroll
+                for (int kh = 0; kh < 4; ++kh)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int cc = j * kAdCols + kh * 32 + (e >> 2) * 8 + hi * 4 + (e & 3);
+                        if (!(row_ok && (cc * S + S - 1) < a.Nv && (!a.causal || cc <= r))) sacc[kh][e] = -INFINITY;
+                    }
+            }
+            float Lk[KT];
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) {
+                constexpr int G8 = CPK / 8;
+                float m = -INFINITY;
+#pragma unroll
+                for (int g = 0; g < G8; ++g) {
+                    const int gg = kt * G8 + g;   // 8-column group of the tile: kh = gg / 4, e = (gg % 4) * 4 + i
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) m = fmaxf(m, sacc[gg >> 2][(gg & 3) * 4 + i]);
+                }
+                m = pair32_max(m);
+                const float mc = m * a.c;
+                float sum = 0.f;
+                if (m != -INFINITY) {
+#pragma unroll
+                    for (int g = 0; g < G8; ++g) {
+                        const int gg = kt * G8 + g;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) sum += fast_exp2(fmaf(sacc[gg >> 2][(gg & 3) * 4 + i], a.c, -mc));
+                    }
+                }
+                sum = pair32_sum(sum);
+                Lk[kt] = sum > 0.f ? mc + __builtin_amdgcn_logf(sum) : -INFINITY;
+            }
+            if (hi == 0 && row_in) {
+#pragma unroll
+                for (int kt = 0; kt < KT; ++kt) Lh[static_cast<int64_t>(j * KT + kt) * a.rows_per_head + r] = Lk[kt];
+            }
+#pragma unroll
+            for (int kh = 0; kh < 4; ++kh)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) sacc[kh][e] = 0.f;
+        }
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) qf[kk] = qn[kk];
+        buf ^= 1;
+    }
+    // tiles of this range past the causal frontier: no mass
+    if (hi == 0 && row_in)
+        for (int j = max(j_lo, j_end); j < j_hi; ++j)
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt) Lh[static_cast<int64_t>(j * KT + kt) * a.rows_per_head + r] = -INFINITY;
+}
+
 // ---------------------------------------------------------------------------------------
 // Intra-block key similarity, one wave per (batch, KV head, KV block).
 // ---------------------------------------------------------------------------------------
@@ -668,6 +849,18 @@ hipError_t launch_sampling(const ScoreArgs& a, int D, int blocks, hipStream_t st
     return hipGetLastError();
 }
 
+// The antidiagonal fast path needs whole 128-column tiles of compressed columns.
+bool antidiag_fast(const Shape& s, int S) { return (s.N / S) % kAdCols == 0 && 64 / S >= 8; }
+
+template <int S>
+hipError_t launch_antidiag(const ScoreArgs& a, int D, int blocks, hipStream_t st) {
+    if (D == 128)
+        hipLaunchKernelGGL((k_mask_logmass_antidiag<128, S>), dim3(blocks), dim3(kScoreThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((k_mask_logmass_antidiag<64, S>), dim3(blocks), dim3(kScoreThreads), 0, st, a);
+    return hipGetLastError();
+}
+
 // Row groups, key-tile ranges and the log-mass workspace for a problem.
 struct ScoreGeom {
     int S, rows_per_head, RQ, rows_per_wg, wg_per_head, ntiles, nsplit, tiles_per_split;
@@ -682,7 +875,8 @@ ScoreGeom score_geom(const Shape& s, const psa_mask_params& mp) {
     g.RQ = sampling ? g.S : s.BQ / g.S;
     g.rows_per_wg = sampling ? kSampRows : 128;
     g.wg_per_head = (g.rows_per_head + g.rows_per_wg - 1) / g.rows_per_wg;
-    g.ntiles = (sampling ? s.N : s.N / g.S) / 64;
+    // column tiles: 64 columns (sampling), 128 compressed columns (antidiagonal fast path)
+    g.ntiles = sampling ? s.N / 64 : (s.N / g.S) / (antidiag_fast(s, g.S) ? kAdCols : 64);
     // enough workgroups to fill the chip several times over; at least 4 tiles per range
     const int64_t groups = static_cast<int64_t>(s.B) * s.H * g.wg_per_head;
     int64_t want = groups > 0 ? (2048 + groups - 1) / groups : 1;
@@ -775,6 +969,15 @@ hipError_t launch_mask_scores(const Shape& s, const psa_mask_params& mp, const v
         }
     }
     if (a.RQ > 32 || a.RQ < 1) return hipErrorNotSupported;
+    if (antidiag_fast(s, g.S)) {
+        const int grid = 8 * ((blocks + 7) / 8);   // the kernel remaps blocks XCD-wise
+        switch (g.S) {
+            case 2: return launch_antidiag<2>(a, s.D, grid, st);
+            case 4: return launch_antidiag<4>(a, s.D, grid, st);
+            case 8: return launch_antidiag<8>(a, s.D, grid, st);
+            default: return hipErrorNotSupported;
+        }
+    }
     switch (g.S) {
         case 2: return launch_scores_d<1, 2>(a, s.D, blocks, st);
         case 4: return launch_scores_d<1, 4>(a, s.D, blocks, st);
