@@ -116,6 +116,8 @@ def cpu_baseline(wl: W.Workload, budget_s: float = 15.0) -> dict:
                                 wl.text_begin, wl.text_end)
         if wl.mask_mode == "sampling":
             M = oracle.mask_scores_sampling(q, k, p, wl.samples_per_qblock)
+        elif wl.mask_mode == "meankey":
+            M = oracle.mask_scores_meankey(q, k, p)
         else:
             M = oracle.mask_scores_antidiag(q, k, p, wl.antidiag_stride)
         sim = oracle.block_cossim(k, p) if wl.cos_sim_min > 0 else None
@@ -163,13 +165,20 @@ def _traffic_from_profile(workload: str):
         return None
 
 
+def _workload(args) -> W.Workload:
+    wl = W.BY_NAME[args.workload]
+    if args.mask_mode and wl.map_source == "mask":
+        wl = wl.replace(mask_mode=args.mask_mode)
+    return wl
+
+
 def run(args) -> dict:
     import ctypes
 
     import torch
     import video_transformers_amd as psa
 
-    wl = W.BY_NAME[args.workload]
+    wl = _workload(args)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     q, k, v = (t.to(dev) for t in W.make_qkv(wl))
@@ -381,6 +390,8 @@ def main():
                     help="skip the all-level-0 comparison run (for profiling the PSA launches alone)")
     ap.add_argument("--no-unpacked", action="store_true",
                     help="skip the unpacked-layout comparison run (one logical block per tile)")
+    ap.add_argument("--mask-mode", choices=("sampling", "antidiag", "meankey"), default=None,
+                    help="score with this psa_mask mode instead of the workload's own")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -388,7 +399,7 @@ def main():
               "(every (batch, head) is independent; see the sharding notes). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
-    wl = W.BY_NAME[args.workload]
+    wl = _workload(args)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, args.cpu_budget)      # before the GPU is touched (fork pool)

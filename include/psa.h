@@ -73,6 +73,9 @@ extern "C" {
  * scoring with an intra-block similarity check for understanding). */
 #define PSA_MASK_SAMPLING 0
 #define PSA_MASK_ANTIDIAG 1
+/* Block-mean scoring (skill summary at skillsmp.com, "Implementation": a query against each KV
+ * block's mean key): the cheapest estimator, one score per (query block, KV block). */
+#define PSA_MASK_MEANKEY 2
 
 typedef struct psa_problem {
     int32_t batch, heads_q, heads_kv;
@@ -86,7 +89,7 @@ typedef struct psa_problem {
 } psa_problem;
 
 typedef struct psa_mask_params {
-    int32_t mode;                 /* PSA_MASK_SAMPLING or PSA_MASK_ANTIDIAG */
+    int32_t mode;                 /* PSA_MASK_SAMPLING, PSA_MASK_ANTIDIAG or PSA_MASK_MEANKEY */
     float thresholds[4];          /* cumulative-mass thresholds t0 <= t1 <= t2 <= t3, in (0, 1] */
     int32_t samples_per_qblock;   /* sampling mode: rows per query block; 1, 2, 4, .., 32 */
     int32_t antidiag_stride;      /* antidiagonal mode: stride S in {2, 4, 8}, block_q/S <= 32 */
@@ -122,6 +125,10 @@ size_t psa_mask_workspace_bytes(const psa_problem* prob, const psa_mask_params* 
  *  Antidiagonal mode, stride S: compressed logits
  *   A[r][c] = (1/sqrt(d)) * sum_{t<S} q[r*S+S-1-t] . k[c*S+t], softmax over valid c
  *   (causal: c <= r), block_mass[qb][kb] = mass of kb's columns averaged over qb's valid rows.
+ *  Block-mean mode: q_bar = mean of the query block's valid rows, k_bar = mean of the KV
+ *   block's n valid keys, block_mass[qb][kb] = softmax over the candidate blocks of
+ *   q_bar.k_bar/sqrt(d) + ln(n) (causal: blocks up to the last one overlapping the query
+ *   block); samples_per_qblock and antidiag_stride are ignored.
  *  If cos_sim_min > 0, block_sim[b][hkv][kb] = mean cosine similarity over ordered pairs of
  *   distinct valid level-0 keys of the block (written; block_sim must then be non-null).
  *  Then psa_mask_assign's rule turns block_mass (and block_sim) into level_map.

@@ -17,7 +17,8 @@ Where the pages leave a step open, the reading taken is stated in the function's
 (and listed with the rest of the design notes). Pins that tie each function to something other
 than itself live in tests/test_oracle.py. Functions whose definition is this project's own
 reading with no closed form or special case on the pages to pin against say so:
-  mask_scores_sampling, mask_scores_antidiag, block_cossim, assign_levels — pinned only by
+  mask_scores_sampling, mask_scores_antidiag, mask_scores_meankey, block_cossim,
+  assign_levels — pinned only by
   reductions and hand-computed special cases of our own readings ("parity unpinned" against
   the pages, which print no worked example for the mask generator).
 
@@ -206,6 +207,41 @@ def mask_scores_antidiag(q: np.ndarray, k: np.ndarray, p: Problem, stride: int,
             continue
         colmass = P[rows].sum(axis=0).reshape(nkb, ck).sum(axis=-1)
         M[qb] = colmass / nv
+    return M
+
+
+def mask_scores_meankey(q: np.ndarray, k: np.ndarray, p: Problem,
+                        qblocks: Optional[Iterable[int]] = None) -> np.ndarray:
+    """Block importance M[qb, kb] for one (batch, head) from block means.
+
+    [SKILL] "Implementation" (block importance scoring): a query is scored against the mean
+    key of each KV block. Our reading, turned into the block masses the threshold rule needs:
+    q_bar = mean of the query block's valid rows, k_bar = mean of the KV block's valid keys,
+    z_kb = s * q_bar . k_bar + ln(n_kb) with n_kb the block's valid keys (a block of n
+    identical keys k_bar carries n times the weight of one), M[qb] = softmax of z over the
+    candidate blocks (causal: kb up to the last block overlapping the query block). A query
+    block with no valid rows gets M = 0. When every query block's rows are equal and every
+    KV block's keys are equal, this is exactly the sampling-mode mass (non-causal).
+    """
+    nqb, nkb = p.n_qblocks, p.n_kblocks
+    M = np.zeros((nqb, nkb), dtype=np.float64)
+    nv = np.clip(p.seq_valid - np.arange(nkb) * p.block_k, 0, p.block_k)
+    kbar = np.zeros((nkb, k.shape[1]))
+    for kb in range(nkb):
+        if nv[kb] > 0:
+            kbar[kb] = k[kb * p.block_k: kb * p.block_k + nv[kb]].mean(axis=0)
+    qbs = range(nqb) if qblocks is None else qblocks
+    for qb in qbs:
+        rv = _valid_rows_in_qblock(p, qb)
+        if rv == 0:
+            continue
+        qbar = q[qb * p.block_q: qb * p.block_q + rv].mean(axis=0)
+        last = kb_diag(p, qb) if p.causal else nkb - 1
+        cand = np.arange(nkb) <= last
+        ok = cand & (nv > 0)
+        z = np.full(nkb, -np.inf)
+        z[ok] = p.scale * (kbar[ok] @ qbar) + np.log(nv[ok])
+        M[qb] = _softmax_rows(z[None, :])[0]
     return M
 
 
@@ -461,6 +497,8 @@ def mask(q, k, p: Problem, mode: str, a: AssignParams, samples: int = 8, stride:
                 M[b, h] = mask_scores_sampling(q[b, h], k[b, h // g], p, samples)
             elif mode == "antidiag":
                 M[b, h] = mask_scores_antidiag(q[b, h], k[b, h // g], p, stride)
+            elif mode == "meankey":
+                M[b, h] = mask_scores_meankey(q[b, h], k[b, h // g], p)
             else:
                 raise ValueError(mode)
             lm[b, h] = assign_levels(M[b, h], None if sim is None else sim[b, h // g], p, a)

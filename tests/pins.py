@@ -269,6 +269,41 @@ def pin_antidiag_stride1(causal=False):
     return np.abs(M - _dense_block_mass(q, k, p)).max()
 
 
+def _block_constant_qk(n, d, bq, bk, seed):
+    rng = np.random.default_rng(seed)
+    q = np.repeat(rng.standard_normal((n // bq, d)), bq, axis=0)
+    k = np.repeat(2.0 * rng.standard_normal((n // bk, d)), bk, axis=0)
+    return q, k
+
+
+def pin_meankey_constant_blocks():
+    """Query rows constant per query block and keys constant per KV block: the block-mean
+    scores are the exact attention block masses (torch softmax over all valid keys, averaged
+    over the query block's rows), padded keys included in the count."""
+    n, d = 512, 16
+    p = oracle.Problem(seq_len=n, seq_valid=n - 24, head_dim=d, block_q=128, block_k=64)
+    q, k = _block_constant_qk(n, d, 128, 64, seed=21)
+    M = oracle.mask_scores_meankey(q, k, p)
+    ref = _dense_block_mass(q, k, p)
+    return max(np.abs(M - ref).max(), np.abs(M.sum(1) - 1).max())
+
+
+def pin_meankey_causal_blocks():
+    """Causal: the candidates are the KV blocks up to the last one overlapping the query
+    block; with block-constant inputs the masses equal dense attention under a block-level
+    causal mask (torch)."""
+    n, d, bq, bk = 512, 16, 128, 64
+    p = oracle.Problem(seq_len=n, seq_valid=n, head_dim=d, block_q=bq, block_k=bk, causal=True)
+    q, k = _block_constant_qk(n, d, bq, bk, seed=22)
+    M = oracle.mask_scores_meankey(q, k, p)
+    z = (_t(q) @ _t(k).T) / math.sqrt(d)
+    i = torch.arange(n)
+    keep = (i[None, :] // bk) <= (((i[:, None] // bq) + 1) * bq - 1) // bk
+    pr = torch.softmax(z.masked_fill(~keep, float("-inf")), dim=-1).numpy()
+    ref = pr.reshape(n, n // bk, bk).sum(-1).reshape(n // bq, bq, n // bk).mean(axis=1)
+    return np.abs(M - ref).max()
+
+
 def pin_antidiag_orientation_and_sum():
     """Stride 4. (a) Only q[4r+3] and k[4c] non-zero: the antidiagonal pairs exactly these
     (t = 0 term), the main diagonal would pair nothing. (b) q and k constant inside each

@@ -105,6 +105,24 @@ def test_mask_param_checks(kw, status):
     assert L.psa_mask_assign(p.ref(), ctypes.byref(mp), d, d, d, None) == status
 
 
+def test_mask_workspace_per_mode():
+    """Every scoring mode is accepted and sizes its workspace: the log-masses (scoring rows x
+    blocks, float32) plus, for block means, the query and key means."""
+    p = _prob(dtype=P.PSA_BF16)
+    L = psa.lib()
+    B, H, Hkv, N, D = 1, 2, 2, 1024, 64   # the _prob() shape
+    nqb, nkb = N // 64, N // 64
+    sizes = {}
+    for mode in ("sampling", "antidiag", "meankey"):
+        mp = psa.MaskParams(mode=mode, samples_per_qblock=8, antidiag_stride=8).c()
+        sizes[mode] = L.psa_mask_workspace_bytes(p.ref(), ctypes.byref(mp))
+    assert sizes["sampling"] == B * H * nkb * nqb * 8 * 4
+    assert sizes["antidiag"] == B * H * nkb * (N // 8) * 4
+    assert sizes["meankey"] >= B * H * nkb * nqb * 4 + B * H * nqb * D * 4 + B * Hkv * nkb * D * 4
+    with pytest.raises(ValueError):
+        psa.MaskParams(mode="bogus").c()
+
+
 def test_mask_needs_bf16():
     p = _prob()   # float32 problem
     mp = psa.MaskParams().c()

@@ -63,7 +63,11 @@ def _run_path(wl, qd, kd, vd):
     return kp, vp, lm, M, sim, o, lse
 
 
-@pytest.mark.parametrize("wl", W.ALL, ids=[w.name for w in W.ALL])
+# the five workloads, plus block-mean scoring on the Wan-like 32k layer
+FULL = list(W.ALL) + [W.WAN13B_32K.replace(name="wan2.1-1.3b_32k-meankey", mask_mode="meankey")]
+
+
+@pytest.mark.parametrize("wl", FULL, ids=[w.name for w in FULL])
 def test_fullsize_sampled_parity(wl):
     announce(f"full size {wl.name}: B{wl.batch} H{wl.heads_q}/{wl.heads_kv} N{wl.seq_len} "
              f"d{wl.head_dim}")
@@ -101,6 +105,8 @@ def test_fullsize_sampled_parity(wl):
         if wl.map_source == "mask":
             if wl.mask_mode == "sampling":
                 Mr = oracle.mask_scores_sampling(qh, kh, p, wl.samples_per_qblock, qblocks=qbs)
+            elif wl.mask_mode == "meankey":
+                Mr = oracle.mask_scores_meankey(qh, kh, p, qblocks=qbs)
             else:
                 Mr = oracle.mask_scores_antidiag(qh, kh, p, wl.antidiag_stride, qblocks=qbs)
             simr = oracle.block_cossim(kh, p) if wl.cos_sim_min > 0 else None

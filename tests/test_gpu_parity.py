@@ -277,6 +277,9 @@ MASKED = [w for w in SMALL if w.map_source == "mask"]
 # tiles) next to its fast path above
 MASKED.append(W.small(W.QWEN25VL_32K).replace(name="qwen2.5-vl-7b-small-1536", seq_len=1536,
                                                   seq_valid=1536))
+# block-mean scoring on the sampling workloads' inputs, non-causal with padding and causal
+MASKED.append(W.small(W.WAN13B_32K).replace(name="wan2.1-1.3b-small-meankey", mask_mode="meankey"))
+MASKED.append(W.small(W.QWEN25VL_32K).replace(name="qwen2.5-vl-7b-small-meankey", mask_mode="meankey"))
 
 
 @pytest.mark.parametrize("wl", MASKED, ids=[w.name for w in MASKED])

@@ -53,6 +53,14 @@ def test_p8_antidiag_orientation_and_sum():
     assert pins.pin_antidiag_orientation_and_sum() < TOL
 
 
+def test_p8_meankey_constant_blocks():
+    assert pins.pin_meankey_constant_blocks() < TOL
+
+
+def test_p8_meankey_causal_blocks():
+    assert pins.pin_meankey_causal_blocks() < TOL
+
+
 def test_p8_cossim():
     assert pins.pin_cossim() < TOL
 

@@ -28,6 +28,7 @@ ALL_PINS = {
     "p8a": lambda: max(pins.pin_antidiag_stride1(False), pins.pin_antidiag_stride1(True),
                        pins.pin_antidiag_orientation_and_sum()),
     "p8c": pins.pin_cossim,
+    "p8m": lambda: max(pins.pin_meankey_constant_blocks(), pins.pin_meankey_causal_blocks()),
     "p9": lambda: sum(pins.pin_assign_case(c) for c in pins.golden_assign_cases()),
     "idx": pins.pin_build_index,
 }
@@ -47,6 +48,11 @@ MUTANTS = [
     ("antidiag_mean", "A = p.scale * (qs @ ks.T)", "A = p.scale * (qs @ ks.T) / S"),
     ("sampling_no_causal", "vis = vis & (keys[None, :] <= rows[:, None])", "vis = vis"),
     ("cossim_keeps_diagonal", "sim[kb] = cos[off].sum()", "sim[kb] = cos.sum()"),
+    ("meankey_no_count", "p.scale * (kbar[ok] @ qbar) + np.log(nv[ok])", "p.scale * (kbar[ok] @ qbar)"),
+    ("meankey_key_sum", "kbar[kb] = k[kb * p.block_k: kb * p.block_k + nv[kb]].mean(axis=0)",
+     "kbar[kb] = k[kb * p.block_k: kb * p.block_k + nv[kb]].sum(axis=0)"),
+    ("meankey_no_causal", "last = kb_diag(p, qb) if p.causal else nkb - 1\n        cand",
+     "last = nkb - 1\n        cand"),
     ("assign_le", "if c < t[l]:", "if c <= t[l]:"),
     ("assign_tie_reversed", "key=lambda kb: (-float(M[kb]), kb)", "key=lambda kb: (-float(M[kb]), -kb)"),
     ("assign_inclusive_cumsum", "for kb in order:\n        lvl = SKIP",

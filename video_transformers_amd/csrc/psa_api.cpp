@@ -81,7 +81,8 @@ int check_problem(const psa_problem* p, psa::Shape* s) {
 
 int check_mask_params(const psa_problem* p, const psa_mask_params* m) {
     if (m == nullptr) return PSA_ERR_INVALID_ARG;
-    if (m->mode != PSA_MASK_SAMPLING && m->mode != PSA_MASK_ANTIDIAG) return PSA_ERR_INVALID_ARG;
+    if (m->mode != PSA_MASK_SAMPLING && m->mode != PSA_MASK_ANTIDIAG && m->mode != PSA_MASK_MEANKEY)
+        return PSA_ERR_INVALID_ARG;
     float prev = 0.f;
     for (int i = 0; i < 4; ++i) {
         const float t = m->thresholds[i];
@@ -97,7 +98,7 @@ int check_mask_params(const psa_problem* p, const psa_mask_params* m) {
         if (S < 1 || S > p->block_q) return PSA_ERR_INVALID_ARG;
         // the sampled rows of one query block are reduced inside one half-wave
         if (S > 32 || (S & (S - 1)) != 0) return PSA_ERR_UNSUPPORTED;
-    } else {
+    } else if (m->mode == PSA_MASK_ANTIDIAG) {
         const int S = m->antidiag_stride;
         if (S < 1 || S > 64) return PSA_ERR_INVALID_ARG;
         // a KV block must span whole 8-column groups and a query block's compressed rows

@@ -579,6 +579,127 @@ __global__ void __launch_bounds__(kScoreThreads) k_mask_logmass_antidiag(ScoreAr
 }
 
 // ---------------------------------------------------------------------------------------
+// Block-mean scoring: k_block_means writes the mean of each query block's valid rows and of
+// each KV block's valid keys (float32); k_meankey_logmass scores 16 query blocks of one
+// (batch, head) per workgroup against every KV block mean (float64 dots) and writes the
+// log-masses z*log2(e) + log2(n) for the assignment (one scoring row per query block).
+// ---------------------------------------------------------------------------------------
+struct MeanArgs {
+    const bf16_bits* q;
+    const bf16_bits* k;
+    float* qbar;   // [B*H][NQB][D]
+    float* kbar;   // [B*Hkv][NKB][D]
+    int B, H, Hkv, N, Nv, D, BQ, BK, NQB, NKB;
+    int64_t qs0, qs1, qs2, ks0, ks1, ks2;
+};
+
+__global__ void __launch_bounds__(256) k_block_means(MeanArgs a) {
+    // 16-byte loads: thread t reads 8 columns (t % (D/8)) of rows t / (D/8), t / (D/8) + 256/(D/8), ..
+    __shared__ float part[256 * 8];
+    const int64_t nq = static_cast<int64_t>(a.B) * a.H * a.NQB;
+    const int64_t item = blockIdx.x;
+    const bool is_q = item < nq;
+    int b, h, blk, len;
+    if (is_q) {
+        blk = static_cast<int>(item % a.NQB);
+        const int bh = static_cast<int>(item / a.NQB);
+        h = bh % a.H;
+        b = bh / a.H;
+        len = a.BQ;
+    } else {
+        const int64_t it = item - nq;
+        blk = static_cast<int>(it % a.NKB);
+        const int bh = static_cast<int>(it / a.NKB);
+        h = bh % a.Hkv;
+        b = bh / a.Hkv;
+        len = a.BK;
+    }
+    const int lo = blk * len;
+    const int rows = min(max(a.Nv - lo, 0), len);
+    const bf16_bits* src = is_q ? a.q + b * a.qs0 + h * a.qs1 + static_cast<int64_t>(lo) * a.qs2
+                                : a.k + b * a.ks0 + h * a.ks1 + static_cast<int64_t>(lo) * a.ks2;
+    const int64_t rs = is_q ? a.qs2 : a.ks2;
+    const int cpr = a.D / 8;                 // 16-byte chunks per row
+    const int phases = 256 / cpr;
+    const int ch = threadIdx.x % cpr;
+    const int ph = threadIdx.x / cpr;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int r = ph; r < rows; r += phases) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(r) * rs + ch * 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += __uint_as_float(w[i] << 16);
+            acc[2 * i + 1] += __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) part[threadIdx.x * 8 + i] = acc[i];
+    __syncthreads();
+    if (threadIdx.x < a.D) {
+        const int e = threadIdx.x;
+        float sum = 0.f;
+        for (int p = 0; p < phases; ++p) sum += part[(p * cpr + e / 8) * 8 + e % 8];
+        const float mean = rows > 0 ? sum / static_cast<float>(rows) : 0.f;
+        float* dst = is_q ? a.qbar + item * a.D : a.kbar + (item - nq) * a.D;
+        dst[e] = mean;
+    }
+}
+
+struct MeanKeyArgs {
+    const float* qbar;
+    const float* kbar;
+    float* L;        // [B*H][NKB][NQB]
+    int H, Hkv, N, Nv, D, BQ, BK, NQB, NKB, causal;
+    double c;        // scale * log2(e)
+};
+
+constexpr int kMeanRows = 16;   // query blocks per workgroup
+constexpr int kMeanCols = 64;   // KV blocks per workgroup
+
+__global__ void __launch_bounds__(256) k_meankey_logmass(MeanKeyArgs a) {
+    // 16 query blocks x 64 KV blocks of one (batch, head): both sets of means staged in LDS,
+    // thread t takes KV block t % 64 against query blocks t / 64 + 4 i (float64 dots)
+    extern __shared__ float sm[];
+    const int ksd = a.D + 1;                 // padded row: the 64 lanes read 64 rows at once
+    float* qs = sm;                          // [kMeanRows][D]
+    float* ks = sm + kMeanRows * a.D;        // [kMeanCols][D + 1]
+    const int rchunks = (a.NQB + kMeanRows - 1) / kMeanRows;
+    const int cchunks = (a.NKB + kMeanCols - 1) / kMeanCols;
+    const int per_bh = rchunks * cchunks;
+    const int bh = blockIdx.x / per_bh;
+    const int qb0 = ((blockIdx.x % per_bh) / cchunks) * kMeanRows;
+    const int kb0 = (blockIdx.x % cchunks) * kMeanCols;
+    const int h = bh % a.H;
+    const int b = bh / a.H;
+    const int hk = h / (a.H / a.Hkv);
+    const int nr = min(kMeanRows, a.NQB - qb0);
+    const int nc = min(kMeanCols, a.NKB - kb0);
+    for (int i = threadIdx.x; i < nr * a.D; i += 256)
+        qs[i] = a.qbar[(static_cast<int64_t>(bh) * a.NQB + qb0) * a.D + i];
+    for (int i = threadIdx.x; i < nc * a.D; i += 256)
+        ks[(i / a.D) * ksd + i % a.D] = a.kbar[(static_cast<int64_t>(b * a.Hkv + hk) * a.NKB + kb0) * a.D + i];
+    __syncthreads();
+    float* Lh = a.L + static_cast<int64_t>(bh) * a.NKB * a.NQB;
+    const int c = threadIdx.x % kMeanCols;
+    const int r0 = threadIdx.x / kMeanCols;   // 0..3
+    if (c >= nc) return;
+    const int kb = kb0 + c;
+    const int nv = min(max(a.Nv - kb * a.BK, 0), a.BK);
+    const float* kr = ks + c * ksd;
+    for (int i = r0; i < nr; i += 256 / kMeanCols) {
+        const float* qr = qs + i * a.D;
+        double dot = 0.0;
+        for (int e = 0; e < a.D; ++e) dot += static_cast<double>(kr[e]) * static_cast<double>(qr[e]);
+        const int qb = qb0 + i;
+        const int qlo = qb * a.BQ;
+        const int last = a.causal ? min((qlo + a.BQ - 1) / a.BK, a.NKB - 1) : a.NKB - 1;
+        float L = -INFINITY;
+        if (qlo < a.Nv && nv > 0 && kb <= last) L = static_cast<float>(dot * a.c + log2(static_cast<double>(nv)));
+        Lh[static_cast<int64_t>(kb) * a.NQB + qb] = L;
+    }
+}
+
+// ---------------------------------------------------------------------------------------
 // Intra-block key similarity, one wave per (batch, KV head, KV block).
 // ---------------------------------------------------------------------------------------
 template <int D>
@@ -865,10 +986,30 @@ hipError_t launch_antidiag(const ScoreArgs& a, int D, int blocks, hipStream_t st
 struct ScoreGeom {
     int S, rows_per_head, RQ, rows_per_wg, wg_per_head, ntiles, nsplit, tiles_per_split;
     size_t ws_bytes;
+    size_t qbar_off = 0, kbar_off = 0;   // block-mean mode: offsets of the means in the workspace
 };
 
 ScoreGeom score_geom(const Shape& s, const psa_mask_params& mp) {
     ScoreGeom g;
+    if (mp.mode == PSA_MASK_MEANKEY) {
+        // one scoring row per query block; workspace: log-masses, query and key block means
+        g.S = 1;
+        g.rows_per_head = s.NQB;
+        g.RQ = 1;
+        g.rows_per_wg = kMeanRows;
+        g.wg_per_head = (s.NQB + kMeanRows - 1) / kMeanRows;
+        g.ntiles = 0;
+        g.nsplit = 1;
+        g.tiles_per_split = 0;
+        g.ws_bytes = static_cast<size_t>(s.B) * s.H * s.NKB * s.NQB * sizeof(float);
+        g.ws_bytes = (g.ws_bytes + 255) & ~static_cast<size_t>(255);
+        g.qbar_off = g.ws_bytes;
+        g.ws_bytes += static_cast<size_t>(s.B) * s.H * s.NQB * s.D * sizeof(float);
+        g.ws_bytes = (g.ws_bytes + 255) & ~static_cast<size_t>(255);
+        g.kbar_off = g.ws_bytes;
+        g.ws_bytes += static_cast<size_t>(s.B) * s.Hkv * s.NKB * s.D * sizeof(float);
+        return g;
+    }
     const bool sampling = mp.mode == PSA_MASK_SAMPLING;
     g.S = sampling ? mp.samples_per_qblock : mp.antidiag_stride;
     g.rows_per_head = sampling ? s.NQB * g.S : s.N / g.S;
@@ -947,6 +1088,35 @@ hipError_t launch_mask_scores(const Shape& s, const psa_mask_params& mp, const v
     a.c = (1.0f / sqrtf(static_cast<float>(s.D))) * kLog2e;
     const ScoreGeom g = score_geom(s, mp);
     if (mb.ws == nullptr || mb.ws_bytes < g.ws_bytes) return hipErrorInvalidValue;
+    if (mp.mode == PSA_MASK_MEANKEY) {
+        char* ws = static_cast<char*>(mb.ws);
+        MeanArgs m;
+        m.q = a.q;
+        m.k = a.k;
+        m.qbar = reinterpret_cast<float*>(ws + g.qbar_off);
+        m.kbar = reinterpret_cast<float*>(ws + g.kbar_off);
+        m.B = s.B; m.H = s.H; m.Hkv = s.Hkv; m.N = s.N; m.Nv = s.Nv; m.D = s.D;
+        m.BQ = s.BQ; m.BK = s.BK; m.NQB = s.NQB; m.NKB = s.NKB;
+        m.qs0 = s.qs[0]; m.qs1 = s.qs[1]; m.qs2 = s.qs[2];
+        m.ks0 = s.ks[0]; m.ks1 = s.ks[1]; m.ks2 = s.ks[2];
+        const int64_t items = static_cast<int64_t>(s.B) * (s.H * s.NQB + s.Hkv * s.NKB);
+        if (items == 0) return hipSuccess;
+        hipLaunchKernelGGL(k_block_means, dim3(static_cast<unsigned>(items)), dim3(256), 0, st, m);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        MeanKeyArgs k;
+        k.qbar = m.qbar;
+        k.kbar = m.kbar;
+        k.L = static_cast<float*>(mb.ws);
+        k.H = s.H; k.Hkv = s.Hkv; k.N = s.N; k.Nv = s.Nv; k.D = s.D; k.BQ = s.BQ; k.BK = s.BK;
+        k.NQB = s.NQB; k.NKB = s.NKB; k.causal = s.causal;
+        k.c = (1.0 / std::sqrt(static_cast<double>(s.D))) * 1.4426950408889634;
+        const int blocks = s.B * s.H * g.wg_per_head * ((s.NKB + kMeanCols - 1) / kMeanCols);
+        hipLaunchKernelGGL(k_meankey_logmass, dim3(blocks), dim3(256),
+                           (static_cast<size_t>(kMeanRows) * s.D + static_cast<size_t>(kMeanCols) * (s.D + 1)) *
+                               sizeof(float), st, k);
+        return hipGetLastError();
+    }
     a.L = static_cast<float*>(mb.ws);
     a.rows_per_head = g.rows_per_head;
     a.RQ = g.RQ;
@@ -997,7 +1167,8 @@ hipError_t launch_mask_assign_logmass(const Shape& s, const psa_mask_params& mp,
     a.map = level_map;
     a.RQ = g.RQ;
     a.rows_per_head = g.rows_per_head;
-    a.sampling = mp.mode == PSA_MASK_SAMPLING;
+    // block-mean mode: one row per query block, counted like a sampled row
+    a.sampling = mp.mode != PSA_MASK_ANTIDIAG;
     a.S = g.S;
     return launch_assign(s, a, st);
 }

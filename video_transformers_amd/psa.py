@@ -26,6 +26,8 @@ PSA_F32 = 0
 PSA_BF16 = 1
 PSA_MASK_SAMPLING = 0
 PSA_MASK_ANTIDIAG = 1
+PSA_MASK_MEANKEY = 2
+_MODES = {"sampling": PSA_MASK_SAMPLING, "antidiag": PSA_MASK_ANTIDIAG, "meankey": PSA_MASK_MEANKEY}
 SKIP = -1
 
 # every symbol include/psa.h declares
@@ -154,7 +156,7 @@ def make_problem(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
 
 @dataclasses.dataclass
 class MaskParams:
-    mode: str = "sampling"                 # "sampling" | "antidiag"
+    mode: str = "sampling"                 # "sampling" | "antidiag" | "meankey"
     thresholds: Sequence[float] = (0.5, 0.7, 0.8, 0.9)
     samples_per_qblock: int = 8
     antidiag_stride: int = 8
@@ -165,7 +167,9 @@ class MaskParams:
 
     def c(self) -> CMaskParams:
         m = CMaskParams()
-        m.mode = PSA_MASK_SAMPLING if self.mode == "sampling" else PSA_MASK_ANTIDIAG
+        if self.mode not in _MODES:
+            raise ValueError(f"unknown mask mode {self.mode!r}")
+        m.mode = _MODES[self.mode]
         for i, t in enumerate(self.thresholds):
             m.thresholds[i] = float(t)
         m.samples_per_qblock = self.samples_per_qblock

@@ -51,7 +51,7 @@ class Workload:
     map_probs: tuple = ()   # iid: P(L0..L3, skip); fixed_frac: fractions of L0..L3 per row
     force_diag_l0: bool = False
     # mask parameters (map_source == "mask")
-    mask_mode: Optional[str] = None   # "sampling" | "antidiag"
+    mask_mode: Optional[str] = None   # "sampling" | "antidiag" | "meankey"
     thresholds: tuple = ()
     samples_per_qblock: int = 8
     antidiag_stride: int = 8
