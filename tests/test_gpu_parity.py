@@ -185,6 +185,43 @@ def test_attention_shapes(causal, dtype, d, bq):
     check_attention(o, lse, o_ref, lse_ref, wl.seq_valid, dtype == "f32", f"shape d{d} bq{bq}")
 
 
+TOKEN_MAJOR = [W.small(W.WAN13B_32K), W.small(W.QWEN25VL_32K)]
+
+
+@pytest.mark.parametrize("wl", TOKEN_MAJOR, ids=[w.name for w in TOKEN_MAJOR])
+def test_path_on_token_major_layout(wl):
+    """Q, K, V as [batch, tokens, heads, d] storage viewed as [batch, heads, tokens, d] (token
+    stride heads*d): the pyramid, the mask and the attention (the general-stride kernels)."""
+    announce(f"path on a token-major layout {wl.name}")
+    q, k, v = W.make_qkv(wl)
+    def token_major(t):
+        return t.permute(0, 2, 1, 3).contiguous().to(DEV).permute(0, 2, 1, 3)
+    qd, kd, vd = token_major(q), token_major(k), token_major(v)
+    assert qd.stride(2) == wl.heads_q * wl.head_dim and kd.stride(2) == wl.heads_kv * wl.head_dim
+    prob = problem_for(wl, qd, kd, vd)
+    kp, vp = psa.build_pyramid(kd, vd, prob)
+    lm, M, sim = psa.mask(qd, kd, prob, mask_params(wl))
+    o, lse = psa.attn_fwd(qd, kd, vd, kp, vp, lm, prob)
+    torch.cuda.synchronize()
+    assert o.stride() == qd.stride()
+    p = oracle_problem(wl)
+    lm_ref, M_ref, sim_ref = oracle.mask(q, k, p, wl.mask_mode, assign_params(wl),
+                                         samples=wl.samples_per_qblock, stride=wl.antidiag_stride)
+    assert np.abs(M.double().cpu().numpy() - M_ref).max() <= 2e-6
+    frag = fragile_entries(M_ref, sim_ref, p, assign_params(wl))
+    diff = lm.cpu().numpy() != lm_ref
+    assert not np.any(diff & ~frag)
+    o_ref, lse_ref = oracle.attention(q, k, v, lm.cpu().numpy(), p)
+    check_attention(o, lse, o_ref, lse_ref, wl.seq_valid, False, f"{wl.name} token-major")
+    # the attention on this layout equals the attention on the contiguous copies
+    qc, kc, vc = qd.contiguous(), kd.contiguous(), vd.contiguous()
+    prob_c = problem_for(wl, qc, kc, vc)
+    kpc, vpc = psa.build_pyramid(kc, vc, prob_c)
+    assert torch.equal(kpc, kp) and torch.equal(vpc, vp)
+    oc, _ = psa.attn_fwd(qc, kc, vc, kpc, vpc, lm, prob_c)
+    assert torch.equal(oc, o.contiguous())
+
+
 def test_attention_all_l0_matches_sdpa():
     """An all-L0 map is dense attention: compare with torch SDPA (float32, on the GPU)."""
     announce("attention all-L0 vs SDPA")

@@ -251,9 +251,9 @@ def attn_fwd(q, k, v, k_pooled, v_pooled, level_map, prob: Problem, *, scale: fl
              out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
              want_lse: bool = True, ws: Optional[torch.Tensor] = None, stream=None):
     """Level-weighted attention. Returns (o, lse or None). `out` must match the problem's
-    o_stride (make_problem(..., o=out)); by default o is allocated like q."""
+    o_stride (make_problem(..., o=out)); by default o is allocated with q's strides."""
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     if ws is None:
@@ -269,7 +269,7 @@ def attn_fwd_indexed(q, k, v, k_pooled, v_pooled, row_ptr, col_idx, prob: Proble
                      lse: Optional[torch.Tensor] = None, want_lse: bool = True, stream=None):
     """attn_fwd on an index from build_index. Returns (o, lse or None)."""
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     _check(lib().psa_attn_fwd_indexed(prob.ref(), ctypes.c_float(scale), _ptr(q), _ptr(k),
@@ -285,7 +285,7 @@ def attn_fwd_unpacked(q, k, v, k_pooled, v_pooled, row_ptr, col_idx, prob: Probl
     """attn_fwd_indexed with one logical block per hardware tile (the ablation baseline of the
     block-tile packing). Returns (o, lse or None)."""
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     _check(lib().psa_attn_fwd_unpacked(prob.ref(), ctypes.c_float(scale), _ptr(q), _ptr(k),
