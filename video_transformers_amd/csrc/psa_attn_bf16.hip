@@ -14,7 +14,9 @@
 //  * K and V tiles travel HBM/L2 -> LDS with global_load_lds_dwordx4 (no VGPR staging). K:
 //    two 64-row buffers. V: a ring of four 32-row slots (half tile u lives in slot u mod 4),
 //    because the O product of a half runs one half behind its S product. One barrier per
-//    tile; the next tile's direct loads are issued from inside the MFMA stream.
+//    tile; the next tile's direct loads are issued from inside the first step's MFMA stream.
+//    The tile loop has one body per buffer parity, so LDS operand addresses are loop
+//    invariants plus instruction immediates.
 //
 // Software pipeline (per wave), in steps of 32 keys (half tiles u = 2t + h):
 //    S(u) = K(u) Q^T                       8 MFMAs (d = 128), K reads three MFMAs ahead
@@ -177,94 +179,99 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
         return n;
     };
 
-    // Direct loads of one tensor of tile t into buffer `buf`. Instruction m fills LDS rows
-    // [m*RPI, (m+1)*RPI): consecutive keys of one logical block, so its block offset is
-    // uniform and folds into the SGPR base; the lane offsets (row inside the instruction,
-    // swizzled chunk) depend only on the row stride (level 0 or pooled) and, for K, on m.
+    // Direct loads of one tensor of tile t. Instruction m of the tile covers RPI consecutive
+    // tile rows; a wave issues ipw consecutive instructions. Logical blocks hold 8 rows or
+    // more, so every run of 8 rows (an aligned group of 8 / RPI instructions) lies in one
+    // block: group j of the wave reads from SGPR base b[j], which points at the group's
+    // first row minus the rows of the instructions before it. Instruction mi's lane offsets
+    // (row inside the instruction, swizzled 16-byte chunk, plus mi instructions of rows) are
+    // then loop invariants, and no per-instruction address work remains but the LDS
+    // destination in M0.
     constexpr int KVAR = D == 128 ? 4 : 2;   // distinct K chunk swizzles across instructions
     static_assert(IPW % KVAR == 0, "instruction m and its index inside the wave agree mod KVAR");
-    uint32_t lpk[2][KVAR], lpv[2];
+    constexpr int IPWK = 64 / LY::RPI / NW;       // K instructions per wave per tile
+    constexpr int IPWV = 32 / LY::RPI / NW;       // V instructions per wave per half tile
+    constexpr int IPG = 8 / LY::RPI;              // instructions per 8-row group
+    static_assert(IPWK % KVAR == 0 && IPWV % IPG == 0 && IPWK / IPG <= 4, "direct-load groups");
+    constexpr int NSTR = CONTIG ? 1 : 2;          // lane offset sets: pooled stride (and level 0)
+    uint32_t lok[NSTR][IPWK], lov[NSTR][IPWV];
     {
-        const uint32_t st[2] = {CONTIG ? static_cast<uint32_t>(D) * 2u : static_cast<uint32_t>(a.ks2) * 2u,
-                                static_cast<uint32_t>(D) * 2u};
-        const uint32_t sv[2] = {CONTIG ? static_cast<uint32_t>(D) * 2u : static_cast<uint32_t>(a.vs2) * 2u,
-                                static_cast<uint32_t>(D) * 2u};
         const int rr = lane / LY::CH;   // row inside the instruction
         const int p = lane % LY::CH;    // LDS chunk position
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < NSTR; ++i) {
+            const uint32_t sk = i == 1 ? static_cast<uint32_t>(a.ks2) * 2u : static_cast<uint32_t>(D) * 2u;
+            const uint32_t sv = i == 1 ? static_cast<uint32_t>(a.vs2) * 2u : static_cast<uint32_t>(D) * 2u;
 #pragma unroll
-            for (int q = 0; q < KVAR; ++q)
-                lpk[i][q] = rr * st[i] + static_cast<uint32_t>((p ^ LY::fk(q * LY::RPI + rr)) << 4);
-            lpv[i] = rr * sv[i] + static_cast<uint32_t>((p ^ LY::fv(rr)) << 4);
+            for (int mi = 0; mi < IPWK; ++mi)
+                lok[i][mi] = (rr + mi * LY::RPI) * sk + static_cast<uint32_t>((p ^ LY::fk((mi % KVAR) * LY::RPI + rr)) << 4);
+#pragma unroll
+            for (int mi = 0; mi < IPWV; ++mi)
+                lov[i][mi] = (rr + mi * LY::RPI) * sv + static_cast<uint32_t>((p ^ LY::fv(rr)) << 4);
         }
     }
     // LDS byte offsets of the tile buffers (32-bit local-address-space pointers)
     const uint32_t lds_k0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Kt[0][0]));
     const uint32_t lds_v0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Vt[0][0]));
     constexpr uint32_t kBufBytes = 64 * D * 2;
-    // Direct loads of rows [r0, r0 + NR) of tile t (one tensor) to LDS address lds_dst (row r0
-    // lands at lds_dst). Instruction m (RPI rows, m*RPI >= r0) covers consecutive keys of one
-    // logical block, so its block offset is uniform and folds into the SGPR base; the lane
-    // offsets (row inside the instruction, swizzled chunk) depend only on the row stride (level
-    // 0 or pooled) and, for K, on m. prep() resolves the tile's addresses (scalar work), fire()
-    // issues one instruction; the loop spreads both over the MFMA slots of a step.
     struct Dma {
-        const char* base;
-        uint32_t stride, blk, lds;
-        int rsm1;
-        int kb[8];
+        uint64_t b[4];   // SGPR bases of the wave's 8-row groups
+        uint32_t lds;    // LDS byte address of the wave's first instruction
     };
-    auto prep = [&](const Tile& t, uint32_t lds_dst, bool is_v, auto R0, auto NR) {
-        constexpr int r0 = decltype(R0)::value;
-        constexpr int ipw = decltype(NR)::value / LY::RPI / NW;   // instructions per wave
-        static_assert(ipw <= 8, "Dma::kb holds 8 instructions");
-        Dma d;
+    // the list entries (logical blocks) of the wave's groups: LDS reads, issued one pipeline
+    // slot before their values are used
+    struct Pend {
+        int c[4];
+    };
+    auto pend = [&](const Tile& t, auto R0, auto NR) {
+        constexpr int ipw = decltype(NR)::value / LY::RPI / NW;
+        const int sh = 6 - t.l;
+        const int clast = t.cnt - 1;
+        const int key0 = decltype(R0)::value + wave * ipw * LY::RPI;
+        // an absent block of a level's partial last tile is replaced by the last one (masked)
+        Pend pd;
+#pragma unroll
+        for (int j = 0; j < ipw / IPG; ++j) pd.c[j] = cols[t.base + min((key0 + 8 * j) >> sh, clast)];
+        return pd;
+    };
+    auto resolve = [&](const Tile& t, const Pend& pd, uint32_t lds_dst, bool is_v, auto R0, auto NR) {
+        constexpr int ipw = decltype(NR)::value / LY::RPI / NW;
         const int l = t.l;
         const int sh = 6 - l;
+        const int rsm1 = (1 << sh) - 1;   // rows per logical block - 1
         // pooled level l starts at row N - N / 2^(l-1) (0 for l = 1 and, by the same formula
         // with shift 0, for l = 0); the level-0 / pooled tensor choice is a mask, not a branch
         const uint32_t lvl_off = static_cast<uint32_t>(a.N - (a.N >> max(l - 1, 0)));
         const uint64_t l0 = reinterpret_cast<uint64_t>(is_v ? V + vbase : K + kbase);
         const uint64_t pl = reinterpret_cast<uint64_t>(is_v ? VP + pbase : KP + pbase);
         const uint64_t m0 = 0ull - static_cast<uint64_t>(l == 0);
-        d.base = reinterpret_cast<const char*>(((l0 & m0) | (pl & ~m0)) + static_cast<uint64_t>(lvl_off * (D * 2u)));
+        const uint64_t base = ((l0 & m0) | (pl & ~m0)) + static_cast<uint64_t>(lvl_off * (D * 2u));
         // byte offsets inside one (batch, head) of one level fit 32 bits (checked on the host)
-        d.stride = static_cast<uint32_t>(l == 0 && !CONTIG ? (is_v ? a.vs2 : a.ks2) : D) * 2u;
-        d.blk = d.stride * static_cast<uint32_t>(64 >> l);   // bytes per logical block
-        d.rsm1 = (64 >> l) - 1;
-        d.lds = lds_dst;
-        const int clast = t.cnt - 1;
+        const uint32_t stride = static_cast<uint32_t>(l == 0 && !CONTIG ? (is_v ? a.vs2 : a.ks2) : D) * 2u;
+        const int key0 = decltype(R0)::value + wave * ipw * LY::RPI;
+        Dma d;
 #pragma unroll
-        for (int mi = 0; mi < ipw; ++mi) {
-            const int key0 = r0 + (wave * ipw + mi) * LY::RPI;   // first tile key of the instruction
-            const int sblk = min(key0 >> sh, clast);             // its logical block (absent -> last)
-            d.kb[mi] = __builtin_amdgcn_readfirstlane(cols[t.base + sblk]);
+        for (int j = 0; j < ipw / IPG; ++j) {
+            const uint32_t r = (static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(pd.c[j])) << sh) +
+                               static_cast<uint32_t>((key0 + 8 * j) & rsm1);
+            d.b[j] = base + static_cast<uint64_t>(r * stride) - static_cast<uint64_t>(8 * j * stride);
         }
+        d.lds = lds_dst + static_cast<uint32_t>(wave * ipw) * 1024u;
         return d;
     };
-    auto fire = [&](const Dma& d, bool is_v, int pooled, auto R0, auto NR, int mi) {
-        constexpr int r0 = decltype(R0)::value;
-        constexpr int ipw = decltype(NR)::value / LY::RPI / NW;
-        const int mrel = wave * ipw + mi;
-        const int key0 = r0 + mrel * LY::RPI;
-        const uint32_t rin = static_cast<uint32_t>(key0 & d.rsm1);
-        const bool p1 = CONTIG || pooled;
-        // K swizzle variant of instruction m = key0 / RPI: (r0/RPI + mi) mod KVAR (wave * ipw
-        // is a multiple of KVAR)
-        const int q = (r0 / LY::RPI + mi) % KVAR;
-        const uint32_t lane_off = is_v ? (p1 ? lpv[1] : lpv[0]) : (p1 ? lpk[1][q] : lpk[0][q]);
-        dma16(d.base + (static_cast<uint32_t>(d.kb[mi]) * d.blk + rin * d.stride), lane_off, d.lds + mrel * 1024);
+    // instruction mi of the wave (level-0 / pooled lane offsets by `pooled`)
+    auto fire = [&](const Dma& d, bool is_v, int pooled, int mi) {
+        const int s = CONTIG ? 0 : (pooled ? 0 : 1);
+        const uint32_t lo = is_v ? lov[s][mi] : lok[s][mi];
+        dma16(reinterpret_cast<const void*>(d.b[mi / IPG]), lo, d.lds + static_cast<uint32_t>(mi) * 1024u);
     };
     auto issue = [&](const Tile& t, uint32_t lds_dst, bool is_v, auto R0, auto NR) {
         constexpr int ipw = decltype(NR)::value / LY::RPI / NW;
-        const Dma d = prep(t, lds_dst, is_v, R0, NR);
+        const Dma d = resolve(t, pend(t, R0, NR), lds_dst, is_v, R0, NR);
 #pragma unroll
-        for (int mi = 0; mi < ipw; ++mi) fire(d, is_v, t.l > 0, R0, NR, mi);
+        for (int mi = 0; mi < ipw; ++mi) fire(d, is_v, t.l > 0, mi);
     };
     constexpr uint32_t kSlotBytes = 32 * D * 2;   // one 32-row V slot
-    constexpr int IPWK = 64 / LY::RPI / NW;       // K instructions per wave per tile
-    constexpr int IPWV = 32 / LY::RPI / NW;       // V instructions per wave per half tile
     auto issue_k = [&](const Tile& t, int buf) {
         issue(t, lds_k0 + (buf ? kBufBytes : 0u), false, IC<0>{}, IC<64>{});
     };
@@ -424,8 +431,14 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
                 psum0 = add_bf16x2(pk[pr], psum0);
         }
     };
-    auto read_k = [&](uint32_t base, int kk) {
-        return *(const lds_bf16x8*)(uintptr_t)(base ^ static_cast<uint32_t>(32 * kk));
+    // K operand address of k-step kk: a loop-invariant register per k-step plus an immediate
+    // (buffer and half); every operand read of the loop then takes its offset from the
+    // instruction
+    uint32_t kx[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) kx[kk] = ka_base ^ static_cast<uint32_t>(32 * kk);
+    auto read_kx = [&](int kk, uint32_t off) {
+        return *(const lds_bf16x8*)(uintptr_t)(kx[kk] + off);
     };
     auto read_v = [&](uint32_t vslot, int j, int dblk) {
         const uint32_t pa = va_addr[dblk] + vslot + j * 16 * D * 2;
@@ -446,19 +459,18 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
     auto step = [&](auto H, uint32_t kbuf, uint32_t vslot, int lvl_p, int lvl_h, auto&& dma) {
         constexpr int hh = decltype(H)::value;
         const float off = exp_off(lvl_p);
-        uint32_t kaddr = ka_base + kbuf + hh * 32 * D * 2;   // no carry into the XORed bits
-        asm volatile("" : "+v"(kaddr));
+        const uint32_t koff = kbuf + hh * 32 * D * 2;   // an immediate: no carry into the XORed bits
         uint32_t pk[8];
         bf16x8 kr[KK];
         bf16x8 vr0[DB], vr1[DB];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 3 && i < KK; ++i) kr[i] = read_k(kaddr, i);
+        for (int i = 0; i < 3 && i < KK; ++i) kr[i] = read_kx(i, koff);
 #pragma unroll
         for (int e = 0; e < 16; ++e) sacc[hh][e] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            if (kk + 3 < KK) kr[kk + 3] = read_k(kaddr, kk + 3);
+            if (kk + 3 < KK) kr[kk + 3] = read_kx(kk + 3, koff);
             if (kk == 0)
 #pragma unroll
                 for (int d = 0; d < DB; ++d) vr0[d] = read_v(vslot, 0, d);
@@ -527,62 +539,75 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
         step_max(IC<1>{}, nm, 0u, 0u, cur.l, cur, [](int) {});
         int lvl_prev = cur.l;
         cur = nxt;
-        int T = 1;   // parity of the tile index
+        int last_parity = 0;   // parity of the row's last tile
 
         // ---- tile t >= 1 (T = t & 1): K(t) in buffer T; V half u = 2t + h in slot u & 3 ----
-        // (one loop body with the parity in a scalar: two copies of the body make the register
-        // allocator split the accumulators)
-        while (cur.l < 4) {
+        // Two copies of the body, one per parity, so that every buffer and slot offset is an
+        // instruction immediate.
+        auto tile_body = [&](auto TT) -> bool {   // false after the row's last tile
+            constexpr int T = decltype(TT)::value;
             const Tile nx = next_tile(cur);
             wait_publish();
             const bool has_nx = nx.l < 4;
             const bool need = tile_needs_mask(cur);
             const uint32_t kbuf = T ? kBufBytes : 0u;
-            // slot s of the K-tile steps fires the instructions mi with mi % (KK - 1) == s - 1
-            // (slot 0 resolves the addresses)
-            // after the row's last tile the "next" loads repeat the current tile into buffers
-            // that are never read again: no branches inside the steps
+            // All of the next direct loads ride along with the first step, so each has about
+            // one and a half steps to land before the barrier that publishes it: K(t+1) into
+            // the other K buffer, V halves 2t+1 and 2t+2 into ring slots whose previous halves
+            // (2t-3, 2t-2) were consumed before this tile's barrier. Slot 0 reads the list
+            // entries, slot 1 resolves the addresses, slot s >= 2 fires the instructions i
+            // (K, then V half 2t+1, then V half 2t+2) with i % (KK - 2) == s - 2.
+            // After the row's last tile the "next" loads repeat the current tile into buffers
+            // that are never read again: no branches inside the steps.
             const Tile nsrc = has_nx ? nx : cur;
+            Pend pk{}, pv1{}, pv0{};
             Dma dk{}, dv1{}, dv0{};
-            auto dma_k = [&](int sl) {
+            auto dma = [&](int sl) {
                 if (sl == 0) {
-                    dk = prep(nsrc, lds_k0 + (T ? 0u : kBufBytes), false, IC<0>{}, IC<64>{});
+                    pk = pend(nsrc, IC<0>{}, IC<64>{});
+                    pv1 = pend(cur, IC<32>{}, IC<32>{});
+                    pv0 = pend(nsrc, IC<0>{}, IC<32>{});
+                } else if (sl == 1) {
+                    dk = resolve(nsrc, pk, lds_k0 + (T ? 0u : kBufBytes), false, IC<0>{}, IC<64>{});
+                    dv1 = resolve(cur, pv1, lds_v0 + static_cast<uint32_t>(2 * T + 1) * kSlotBytes, true, IC<32>{}, IC<32>{});
+                    dv0 = resolve(nsrc, pv0, lds_v0 + static_cast<uint32_t>((2 * T + 2) & 3) * kSlotBytes, true, IC<0>{}, IC<32>{});
                 } else {
 #pragma unroll
-                    for (int mi = 0; mi < IPWK; ++mi)
-                        if (mi % (KK - 1) == sl - 1) fire(dk, false, nsrc.l > 0, IC<0>{}, IC<64>{}, mi);
-                }
-            };
-            auto dma_v = [&](int sl) {
-                if (sl == 0) {
-                    dv1 = prep(cur, lds_v0 + static_cast<uint32_t>(2 * T + 1) * kSlotBytes, true, IC<32>{}, IC<32>{});
-                    dv0 = prep(nsrc, lds_v0 + static_cast<uint32_t>((2 * T + 2) & 3) * kSlotBytes, true, IC<0>{}, IC<32>{});
-                } else {
-#pragma unroll
-                    for (int mi = 0; mi < 2 * IPWV; ++mi)
-                        if (mi % (KK - 1) == sl - 1) {
-                            if (mi < IPWV)
-                                fire(dv1, true, cur.l > 0, IC<32>{}, IC<32>{}, mi);
+                    for (int i = 0; i < IPWK + 2 * IPWV; ++i)
+                        if (i % (KK - 2) == sl - 2) {
+                            if (i < IPWK)
+                                fire(dk, false, nsrc.l > 0, i);
+                            else if (i < IPWK + IPWV)
+                                fire(dv1, true, cur.l > 0, i - IPWK);
                             else
-                                fire(dv0, true, nsrc.l > 0, IC<0>{}, IC<32>{}, mi - IPWV);
+                                fire(dv0, true, nsrc.l > 0, i - IPWK - IPWV);
                         }
                 }
             };
             // half 0: P of the previous tile's half 1 (slot 2t-1 = 2T+3 mod 4)
-            step_max(IC<0>{}, need, kbuf, static_cast<uint32_t>((2 * T + 3) & 3) * kSlotBytes, lvl_prev, cur, dma_k);
+            step_max(IC<0>{}, need, kbuf, static_cast<uint32_t>((2 * T + 3) & 3) * kSlotBytes, lvl_prev, cur, dma);
             // half 1: P of this tile's half 0 (slot 2T)
-            step_max(IC<1>{}, need, kbuf, static_cast<uint32_t>(2 * T) * kSlotBytes, cur.l, cur, dma_v);
+            step_max(IC<1>{}, need, kbuf, static_cast<uint32_t>(2 * T) * kSlotBytes, cur.l, cur, [](int) {});
             lvl_prev = cur.l;
             cur = nx;
-            T ^= 1;
+            return cur.l < 4;
+        };
+        if (cur.l < 4) {
+            for (;;) {
+                if (!tile_body(IC<1>{})) {
+                    last_parity = 1;
+                    break;
+                }
+                if (!tile_body(IC<0>{})) break;
+            }
         }
-        // ---- after the last tile (parity T ^ 1): P and O of its half 1 (slot 2(T^1)+1) ----
+        // ---- after the last tile (parity P): P and O of its half 1 (slot 2P+1) ----
         wait_publish();
         {
             const float off = exp_off(lvl_prev);
             const bf16x8 p0 = make_p(IC<1>{}, 0, off);
             const bf16x8 p1 = make_p(IC<1>{}, 1, off);
-            const uint32_t vslot = static_cast<uint32_t>(2 * (T ^ 1) + 1) * kSlotBytes;
+            const uint32_t vslot = static_cast<uint32_t>(2 * last_parity + 1) * kSlotBytes;
             pv(vslot, 0, p0);
             pv(vslot, 1, p1);
         }
