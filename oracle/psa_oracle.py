@@ -1,4 +1,4 @@
-"""CPU oracle for the Pyramid Sparse Attention (PSA) forward path — fp64, numpy.
+"""CPU oracle for the Pyramid Sparse Attention (PSA) path, forward and backward — fp64, numpy.
 
 TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU-baseline leg may
 import this module. The product path (the HIP library and its Python binding) never imports,
@@ -463,6 +463,71 @@ def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, level_map: np.nd
 
 
 # ----------------------------------------------------------------------------------------
+# 6. Backward of the Adaptive Pyramid Attention
+# ----------------------------------------------------------------------------------------
+
+def attention_backward_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, level_map: np.ndarray,
+                            do: np.ndarray, p: Problem, scale: Optional[float] = None):
+    """Gradients of the PSA forward of one (batch, head) with respect to q, k and v (level 0),
+    given the output gradient do [N, d]. Returns (dq [N, d], dk [N, d], dv [N, d]) in fp64.
+
+    [NEWS] "Methodology" item 4: pooling is deterministic, so gradients flow through every
+    level and the whole layer trains end to end. This function is the chain rule of
+    attention_head written out, one query block at a time:
+      P = softmax(z) over the gathered pooled keys (z as in attention_head),
+      dV̄ = P^T dO,  dP = dO V̄^T,  D_i = sum_j P_ij dP_ij,  dz = P * (dP - D),
+      dq = s dz K̄,  dK̄ = s dz^T q;
+    each gathered pooled row's gradient is added to its level's pooled row, and a pooled row
+    of level l, the mean of 2**l consecutive tokens, hands 2**-l of its gradient to each of
+    them. Pad query rows and rows with no visible key have a constant output (zero): they
+    contribute nothing.
+    """
+    sc = p.scale if scale is None else scale
+    lk, lvv = pyramid(k), pyramid(v)
+    n, d = q.shape
+    gk = {l: np.zeros_like(lk[l]) for l in range(NUM_LEVELS)}
+    gv = {l: np.zeros_like(lvv[l]) for l in range(NUM_LEVELS)}
+    dq = np.zeros((n, d))
+    for qb in range(p.n_qblocks):
+        qi = np.arange(qb * p.block_q, (qb + 1) * p.block_q)
+        qi = qi[qi < p.seq_valid]
+        if qi.size == 0:
+            continue
+        Kb, Vb, lv, last = gather_row_keys(lk, lvv, level_map[qb], p)
+        if Kb.shape[0] == 0:
+            continue
+        # which pooled row of which level each gathered key is
+        src_l, src_r = [], []
+        for kb in range(p.n_kblocks):
+            l = int(level_map[qb, kb])
+            if l < 0:
+                continue
+            per = p.block_k >> l
+            src_l.append(np.full(per, l))
+            src_r.append(np.arange(kb * per, (kb + 1) * per))
+        src_l, src_r = np.concatenate(src_l), np.concatenate(src_r)
+        P = attention_weights_row(q[qi], qi, Kb, lv, last, p, sc)
+        dO = do[qi]
+        dP = dO @ Vb.T
+        D = np.sum(P * dP, axis=1)
+        dz = P * (dP - D[:, None])
+        dq[qi] = sc * (dz @ Kb)
+        dKb = sc * (dz.T @ q[qi])
+        dVb = P.T @ dO
+        for l in range(NUM_LEVELS):
+            sel = src_l == l
+            np.add.at(gk[l], src_r[sel], dKb[sel])
+            np.add.at(gv[l], src_r[sel], dVb[sel])
+    dk = np.zeros((n, d))
+    dv = np.zeros((n, d))
+    for l in range(NUM_LEVELS):
+        tok = np.arange(n)
+        dk += gk[l][tok >> l] * 2.0 ** -l
+        dv += gv[l][tok >> l] * 2.0 ** -l
+    return dq, dk, dv
+
+
+# ----------------------------------------------------------------------------------------
 # Whole-tensor wrappers ([B, H, N, d] inputs, GQA: KV head = h // (H / Hkv))
 # ----------------------------------------------------------------------------------------
 
@@ -477,6 +542,25 @@ def attention(q, k, v, level_map, p: Problem, scale: Optional[float] = None):
             o[b, h], lse[b, h] = attention_head(q[b, h], k[b, h // g], v[b, h // g],
                                                 level_map[b, h], p, scale)
     return o, lse
+
+
+def attention_backward(q, k, v, level_map, do, p: Problem, scale: Optional[float] = None):
+    """(dq [B,H,N,d], dk [B,Hkv,N,d], dv [B,Hkv,N,d]): per-head gradients; a KV head's gradient
+    is the sum over the query heads that share it."""
+    q, k, v, do = as_f64(q), as_f64(k), as_f64(v), as_f64(do)
+    B, H = q.shape[:2]
+    g = H // k.shape[1]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            a, bk, bv = attention_backward_head(q[b, h], k[b, h // g], v[b, h // g],
+                                                level_map[b, h], do[b, h], p, scale)
+            dq[b, h] = a
+            dk[b, h // g] += bk
+            dv[b, h // g] += bv
+    return dq, dk, dv
 
 
 def mask(q, k, p: Problem, mode: str, a: AssignParams, samples: int = 8, stride: int = 8):

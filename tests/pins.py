@@ -402,3 +402,90 @@ def pin_build_index(seed=14):
             got = ci[rp[r * 4 + l]:rp[r * 4 + l + 1]]
             bad += int(not np.array_equal(ref, got))
     return bad
+
+
+# ---------------------------------------------------------------------------------------
+# Backward pins. The gradient the oracle writes out by the chain rule is checked against
+# (a) central finite differences of the oracle's own forward (the forward is pinned above;
+# the difference quotient shares none of the backward's formulas), with mixed levels,
+# padding, causal masking and a shared KV head; (b) torch autograd of dense masked attention
+# (float64, CPU) on an all-level-0 map; (c) K, V constant within runs of 2**l: level l and
+# level 0 give the same dq and the same gradient summed over each run.
+# ---------------------------------------------------------------------------------------
+def _bwd_problem(causal, nv, n=128, d=8):
+    return oracle.Problem(seq_len=n, seq_valid=nv, head_dim=d, block_q=64, block_k=64,
+                          causal=causal)
+
+
+def pin_bwd_finite_difference(causal=False, nv=120, H=2, Hkv=1, seed=30, samples=12):
+    n, d = 128, 8
+    p = _bwd_problem(causal, nv, n, d)
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((1, H, n, d))
+    k = rng.standard_normal((1, Hkv, n, d))
+    v = rng.standard_normal((1, Hkv, n, d))
+    do = rng.standard_normal((1, H, n, d))
+    lm = rng.choice(np.array([0, 1, 2, 3, -1], dtype=np.int8), size=(1, H, p.n_qblocks, p.n_kblocks))
+    lm[..., 0, 0] = 1
+    lm[..., 1, 1] = 3
+    lm[..., 1, 0] = 2
+
+    def loss(q_, k_, v_):
+        o, _ = oracle.attention(q_, k_, v_, lm, p)
+        return float(np.sum(np.where(np.isfinite(o), o, 0.0) * do))
+
+    dq, dk, dv = oracle.attention_backward(q, k, v, lm, do, p)
+    eps = 1e-5
+    err = 0.0
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        flat = rng.choice(x.size, size=samples, replace=False)
+        for f in flat:
+            idx = np.unravel_index(f, x.shape)
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+            args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            err = max(err, abs(fd - g[idx]) / max(1.0, abs(fd)))
+    return err
+
+
+def pin_bwd_all_l0_autograd(causal=False, nv=256):
+    n, d = 256, 16
+    p = oracle.Problem(seq_len=n, seq_valid=nv, head_dim=d, block_q=64, block_k=64,
+                       causal=causal)
+    q, k, v = rand_qkv(n, d, seed=31, nv=nv)
+    do = np.random.default_rng(32).standard_normal((n, d))
+    do[nv:] = 0.0
+    lm = np.zeros((p.n_qblocks, p.n_kblocks), dtype=np.int8)
+    dq, dk, dv = oracle.attention_backward_head(q, k, v, lm, do, p)
+    i = np.arange(n)
+    keep = (i[None, :] < nv) & np.ones((n, 1), dtype=bool)
+    if causal:
+        keep = keep & (i[None, :] <= i[:, None])
+    tq, tk, tv = (_t(x).clone().requires_grad_(True) for x in (q, k, v))
+    z = (tq @ tk.T) / math.sqrt(d)
+    z = z.masked_fill(~_t(keep), float("-inf"))
+    o = torch.softmax(z, dim=-1) @ tv
+    (o * _t(do)).sum().backward()
+    return max(np.abs(dq - tq.grad.numpy()).max(), np.abs(dk - tk.grad.numpy()).max(),
+               np.abs(dv - tv.grad.numpy()).max())
+
+
+def pin_bwd_constant_runs(level=2):
+    n, d = 256, 8
+    f = 1 << level
+    p = oracle.Problem(seq_len=n, seq_valid=n, head_dim=d, block_q=64, block_k=64)
+    q, k, v = rand_qkv(n, d, seed=33, runs=f)
+    do = np.random.default_rng(34).standard_normal((n, d))
+    rng = np.random.default_rng(35)
+    base = np.where(rng.random((p.n_qblocks, p.n_kblocks)) < 0.3, -1, 0).astype(np.int8)
+    base[:, 0] = 0
+    pooled = base.copy()
+    pooled[(base == 0) & (rng.random(base.shape) < 0.6)] = level
+    g0 = oracle.attention_backward_head(q, k, v, base, do, p)
+    g1 = oracle.attention_backward_head(q, k, v, pooled, do, p)
+    runsum = lambda x: x.reshape(n // f, f, d).sum(axis=1)
+    return max(np.abs(g0[0] - g1[0]).max(), np.abs(runsum(g0[1]) - runsum(g1[1])).max(),
+               np.abs(runsum(g0[2]) - runsum(g1[2])).max())

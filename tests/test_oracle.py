@@ -116,3 +116,18 @@ def test_causal_pooled_visibility_uses_last_token():
     o, lse = oracle.attention_head(q, k, v, np.array([[3]], dtype=np.int8), p)
     assert np.all(np.isneginf(lse[:7])) and np.all(o[:7] == 0)
     assert np.allclose(o[7], v[:8].mean(0), atol=1e-14)
+
+
+@pytest.mark.parametrize("causal,nv,H,Hkv", [(False, 120, 2, 1), (True, 128, 2, 2), (True, 112, 1, 1)])
+def test_pbwd_finite_difference(causal, nv, H, Hkv):
+    assert pins.pin_bwd_finite_difference(causal, nv, H, Hkv) < 1e-6
+
+
+@pytest.mark.parametrize("causal,nv", [(False, 256), (False, 232), (True, 256)])
+def test_pbwd_all_l0_is_dense_autograd(causal, nv):
+    assert pins.pin_bwd_all_l0_autograd(causal, nv) < 1e-10
+
+
+@pytest.mark.parametrize("level", [1, 2, 3])
+def test_pbwd_constant_runs(level):
+    assert pins.pin_bwd_constant_runs(level) < 1e-10
