@@ -1,5 +1,5 @@
 /*
- * psa.h - C ABI of libpsa: the Pyramid Sparse Attention (PSA) forward path, written in HIP
+ * psa.h - C ABI of libpsa: the Pyramid Sparse Attention (PSA) path, written in HIP
  * for AMD Instinct MI355X (gfx950, CDNA4).
  *
  * PSA (arXiv 2512.04025; summary article at rg.mbintangr.com, section "Method") replaces the
@@ -9,15 +9,16 @@
  *   psa_build_pyramid  - the mean-pooled levels 1..3 of K and V;
  *   psa_mask           - block importance (sampling or antidiagonal scoring, optional
  *                        intra-block cosine check) and threshold assignment of levels;
- *   psa_attn_fwd       - the level-weighted flash-style attention.
+ *   psa_attn_fwd       - the level-weighted flash-style attention;
+ *   psa_attn_bwd       - its backward (dq, dk, dv through every pyramid level).
  * plus psa_mask_assign and psa_build_index, the mask's and the attention's integer stages,
  * exported on their own.
  *
  * Conventions shared by every call
  *  - Pointers named q, k, v, o, k_pooled, v_pooled, level_map, block_mass, block_sim, lse,
- *    row_ptr, col_idx, dev_err and ws are DEVICE pointers owned by the caller; the library
- *    never allocates or frees device memory and keeps no state between calls. psa_problem and
- *    psa_mask_params are HOST pointers, read during the call only.
+ *    row_ptr, col_idx, dev_err, dout, dq, dk, dv and ws are DEVICE pointers owned by the
+ *    caller; the library never allocates or frees device memory and keeps no state between
+ *    calls. psa_problem and psa_mask_params are HOST pointers, read during the call only.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). Work is only
  *    enqueued: no call synchronises except psa_check_status.
  *  - Arguments are checked on the host before anything is enqueued. A failed check returns a
@@ -209,9 +210,36 @@ int psa_attn_fwd_unpacked(const psa_problem* prob, float softmax_scale, const vo
                           const void* v_pooled, const int32_t* row_ptr, const int32_t* col_idx,
                           void* o, float* lse, void* stream);
 
+/* Device workspace psa_attn_bwd needs; 0 on a bad problem. */
+size_t psa_attn_bwd_workspace_bytes(const psa_problem* prob);
+
+/*
+ * Backward of psa_attn_fwd (news summary at euno.news, "Methodology" item 4: pooling is
+ * deterministic, so gradients flow through every pyramid level and the layer trains end to
+ * end). Given the forward's o and lse for the same problem, map and softmax_scale, and the
+ * output gradient dout, writes
+ *   dq = dL/dq,  dk = dL/dk,  dv = dL/dv   (L with dL/do = dout)
+ * for the level-0 q, k, v: with P the forward's softmax weights over the gathered pooled rows,
+ * dVbar = P^T dO, dS = P * (dO Vbar^T - rowsum(dO * o)), dq = s dS Kbar, dKbar = s dS^T q, and a
+ * pooled row of level l hands 2^-l of its gradient to each of its 2^l tokens. A KV head's
+ * gradient sums over the query heads that share it. Pad query rows and rows with no visible
+ * key contribute nothing and get dq = 0; pad tokens get dk = dv = 0.
+ * Layouts: dout and o use o_stride, dq uses q_stride, dk uses k_stride, dv uses v_stride (all
+ * in the problem's dtype); lse is the forward's [batch, heads_q, seq_len] float32 output (not
+ * null). The block index is built inside the call (into ws); invalid map entries are
+ * recorded for psa_check_status as in psa_attn_fwd.
+ * dtype PSA_BF16 only (bf16 MFMA, f32 accumulation; P and dS enter the products rounded to
+ * bf16); seq_len/block_q < 4096 and (heads_q/heads_kv) * seq_len/block_q <= 16384.
+ * Anything else returns PSA_ERR_UNSUPPORTED.
+ */
+int psa_attn_bwd(const psa_problem* prob, float softmax_scale, const void* q, const void* k,
+                 const void* v, const void* k_pooled, const void* v_pooled,
+                 const int8_t* level_map, const void* o, const float* lse, const void* dout,
+                 void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream);
+
 /*
  * Waits for `stream`, then reports device-side errors recorded in `ws` by the last
- * psa_attn_fwd that used it: PSA_OK or PSA_ERR_BAD_LEVEL_MAP (or PSA_ERR_HIP).
+ * psa_attn_fwd or psa_attn_bwd that used it: PSA_OK or PSA_ERR_BAD_LEVEL_MAP (or PSA_ERR_HIP).
  */
 int psa_check_status(const void* ws, void* stream);
 

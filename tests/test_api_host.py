@@ -135,3 +135,29 @@ def test_status_strings():
     for code in (0, -1, -2, -3, -4, -5):
         assert L.psa_status_string(code).startswith(b"PSA_")
     assert L.psa_last_hip_error() == 0
+
+
+def test_attn_bwd_host_checks():
+    L = psa.lib()
+    d = ctypes.c_void_p(256)
+    args13 = lambda **o: [o.get(n, d) for n in ("q", "k", "v", "kp", "vp", "map", "o", "lse",
+                                                 "do", "dq", "dk", "dv", "ws")]
+    # f32 problems have no backward
+    p32 = _prob()
+    need32 = L.psa_attn_bwd_workspace_bytes(p32.ref())
+    assert need32 > L.psa_attn_workspace_bytes(p32.ref())
+    assert L.psa_attn_bwd(p32.ref(), 0.0, *args13(), need32, None) == P.PSA_ERR_UNSUPPORTED
+    p = _prob(dtype=P.PSA_BF16)
+    need = L.psa_attn_bwd_workspace_bytes(p.ref())
+    # per-row lse2 and D, and the f32 gradients of all N + 7N/8 rows of K and V
+    rows, grows = 2 * 1024, 2 * (1024 + 896)
+    assert need >= 2 * rows * 4 + 2 * grows * 64 * 4 + L.psa_attn_workspace_bytes(p.ref())
+    assert L.psa_attn_bwd(p.ref(), 0.0, *args13(), need - 1, None) == P.PSA_ERR_WORKSPACE
+    assert L.psa_attn_bwd(p.ref(), 0.0, *args13(ws=None), need, None) == P.PSA_ERR_WORKSPACE
+    for name in ("q", "lse", "do", "dq", "dk", "dv", "map"):
+        assert L.psa_attn_bwd(p.ref(), 0.0, *args13(**{name: None}), need, None) == P.PSA_ERR_INVALID_ARG, name
+    assert L.psa_attn_bwd(p.ref(), 0.0, *args13(dk=ctypes.c_void_p(264)), need, None) == P.PSA_ERR_INVALID_ARG
+    assert L.psa_attn_bwd(p.ref(), float("nan"), *args13(), need, None) == P.PSA_ERR_INVALID_ARG
+    # the key-side kernel's row list: at most 16384 (query head, query block) rows per KV head
+    big = _prob(dtype=P.PSA_BF16, heads_q=64, heads_kv=1, seq_len=32768, seq_valid=32768)
+    assert L.psa_attn_bwd(big.ref(), 0.0, *args13(), 1 << 40, None) == P.PSA_ERR_UNSUPPORTED

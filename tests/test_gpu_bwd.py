@@ -1,0 +1,137 @@
+"""GPU parity of psa_attn_bwd (through the C ABI) against the CPU oracle's backward.
+
+The forward runs on the GPU (its o and lse feed the backward, as in training); the oracle
+recomputes everything in float64 from the same bf16 inputs, map and output gradient.
+
+Tolerance. The kernels round P and dS to bf16 before the products that use them (relative
+error <= 2^-9 each) and take D_i = dO_i . o_i from the bf16 forward output; everything else is
+bf16 inputs (exact in both) with float32 accumulation. Those roundings are independent across
+the terms of each sum, so the gradient's relative L2 error is a few times 2^-9 ~ 2e-3: the
+bar is rel-L2 <= 1e-2 per tensor, and max-abs <= 2e-2 of the tensor's largest magnitude.
+Pad query rows get dq = 0 and pad tokens dk = dv = 0 exactly; two runs are bit-identical.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+import video_transformers_amd as psa
+from gpu_util import DEV, announce, need_gpu, oracle_map, oracle_problem, problem_for
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 1e-2
+MAX_REL = 2e-2
+
+BWD = [W.small(w) for w in W.ALL if w.dtype == "bf16"]
+BWD.append(W.small(W.QWEN25VL_32K).replace(name="qwen2.5-vl-7b-small-bq64", block_q=64))
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+    yield
+    torch.cuda.synchronize()
+
+
+def _run(wl, q, k, v, lm, dout):
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    prob = problem_for(wl, qd, kd, vd)
+    kp, vp = psa.build_pyramid(kd, vd, prob)
+    lmd = torch.from_numpy(lm).to(DEV)
+    o, lse = psa.attn_fwd(qd, kd, vd, kp, vp, lmd, prob)
+    do = dout.to(DEV)
+    bprob = psa.make_problem(qd, kd, vd, o, block_q=wl.block_q, block_k=wl.block_k,
+                             causal=wl.causal, seq_valid=wl.seq_valid)
+    ws = psa.attn_bwd_workspace(bprob, DEV)
+    dq, dk, dv = psa.attn_bwd(qd, kd, vd, kp, vp, lmd, o, lse, do, bprob, ws=ws)
+    psa.check_status(ws)
+    return dq, dk, dv
+
+
+def _compare(name, got, ref):
+    g = got.double().cpu().numpy()
+    diff = g - ref
+    scale = max(np.abs(ref).max(), 1e-30)
+    rel = float(np.linalg.norm(diff) / max(np.linalg.norm(ref), 1e-30))
+    mx = float(np.abs(diff).max() / scale)
+    print(f"  {name}: rel_l2={rel:.3e} max_abs/max|ref|={mx:.3e} max|ref|={scale:.3e}", flush=True)
+    assert rel <= REL_L2, f"{name}: rel L2 {rel}"
+    assert mx <= MAX_REL, f"{name}: max abs {mx} of max|ref|"
+
+
+@pytest.mark.parametrize("wl", BWD, ids=[w.name for w in BWD])
+def test_bwd_parity(wl):
+    announce(f"backward {wl.name}: H{wl.heads_q}/{wl.heads_kv} N{wl.seq_len} d{wl.head_dim} "
+             f"bq{wl.block_q} causal={wl.causal}")
+    q, k, v = W.make_qkv(wl)
+    lm = oracle_map(wl, q, k)
+    dout = W.make_dout(wl)
+    dq, dk, dv = _run(wl, q, k, v, lm, dout)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_backward(q, k, v, lm, dout, oracle_problem(wl))
+    _compare("dq", dq, rq)
+    _compare("dk", dk, rk)
+    _compare("dv", dv, rv)
+    nv = wl.seq_valid
+    assert torch.count_nonzero(dq[..., nv:, :]).item() == 0
+    assert torch.count_nonzero(dk[..., nv:, :]).item() == 0
+    assert torch.count_nonzero(dv[..., nv:, :]).item() == 0
+
+
+def test_bwd_deterministic():
+    wl = W.small(W.QWEN25VL_32K)
+    announce(f"backward determinism {wl.name}")
+    q, k, v = W.make_qkv(wl)
+    lm = oracle_map(wl, q, k)
+    dout = W.make_dout(wl)
+    a = _run(wl, q, k, v, lm, dout)
+    b = _run(wl, q, k, v, lm, dout)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_bwd_all_l0_matches_autograd():
+    """An all-level-0 map is dense attention: the gradients match torch autograd of dense
+    masked attention (float32 on the GPU) to the same bars."""
+    wl = W.small(W.WAN13B_32K)
+    announce(f"backward all-L0 vs autograd {wl.name}")
+    q, k, v = W.make_qkv(wl)
+    lm = np.zeros((wl.batch, wl.heads_q, wl.n_qblocks, wl.n_kblocks), dtype=np.int8)
+    dout = W.make_dout(wl)
+    dq, dk, dv = _run(wl, q, k, v, lm, dout)
+    nv = wl.seq_valid
+    tq, tk, tv = (x.to(DEV).float().requires_grad_(True) for x in (q, k, v))
+    keep = torch.arange(wl.seq_len, device=DEV)[None, :] < nv
+    z = (tq @ tk.transpose(-1, -2).contiguous()) / (wl.head_dim ** 0.5)
+    z = z.masked_fill(~keep, float("-inf"))
+    o = torch.softmax(z, dim=-1) @ tv
+    rows = (torch.arange(wl.seq_len, device=DEV) < nv)[:, None]
+    (o * dout.to(DEV).float() * rows).sum().backward()
+    _compare("dq", dq, tq.grad.double().cpu().numpy())
+    _compare("dk", dk, tk.grad.double().cpu().numpy())
+    _compare("dv", dv, tv.grad.double().cpu().numpy())
+
+
+def test_bwd_token_major_layout():
+    """Q, K, V, O, dO and the gradients on [batch, tokens, heads, d] storage."""
+    wl = W.small(W.QWEN25VL_32K)
+    announce(f"backward token-major {wl.name}")
+    q, k, v = W.make_qkv(wl)
+    lm = oracle_map(wl, q, k)
+    dout = W.make_dout(wl)
+    tm = lambda t: t.permute(0, 2, 1, 3).contiguous().to(DEV).permute(0, 2, 1, 3)
+    qd, kd, vd, dod = tm(q), tm(k), tm(v), tm(dout)
+    prob = problem_for(wl, qd, kd, vd)
+    kp, vp = psa.build_pyramid(kd, vd, prob)
+    lmd = torch.from_numpy(lm).to(DEV)
+    o = torch.empty_strided(qd.shape, qd.stride(), dtype=qd.dtype, device=DEV)
+    oprob = psa.make_problem(qd, kd, vd, o, block_q=wl.block_q, causal=wl.causal,
+                             seq_valid=wl.seq_valid)
+    o, lse = psa.attn_fwd(qd, kd, vd, kp, vp, lmd, oprob, out=o)
+    dq, dk, dv = psa.attn_bwd(qd, kd, vd, kp, vp, lmd, o, lse, dod, oprob)
+    assert dq.stride() == qd.stride() and dk.stride() == kd.stride()
+    ref = _run(wl, q, k, v, lm, dout)
+    for x, y in zip((dq, dk, dv), ref):
+        assert torch.equal(x.contiguous(), y)

@@ -21,8 +21,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpsa.so")
 
 SOURCES = ["psa_api.cpp", "psa_pyramid.hip", "psa_index.hip", "psa_attn.hip", "psa_attn_bf16.hip",
-           "psa_mask.hip"]
-HEADERS = ["psa_internal.h", "psa_device.h", "psa_attn_common.h"]
+           "psa_attn_bwd.hip", "psa_mask.hip"]
+HEADERS = ["psa_internal.h", "psa_device.h", "psa_attn_common.h", "psa_bf16_tile.h"]
 
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are disabled for every device compile: the compiler then never
@@ -37,6 +37,7 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
 EXTRA = {
     "psa_attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
     "psa_mask.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "psa_attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

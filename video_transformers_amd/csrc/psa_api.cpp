@@ -276,6 +276,48 @@ int psa_attn_fwd_unpacked(const psa_problem* prob, float softmax_scale, const vo
                         lse, false, stream);
 }
 
+size_t psa_attn_bwd_workspace_bytes(const psa_problem* prob) {
+    psa::Shape s;
+    if (check_problem(prob, &s) != PSA_OK) return 0;
+    return attn_ws_layout(s, nullptr).bytes + align_up(psa::attn_bwd_scratch_bytes(s));
+}
+
+int psa_attn_bwd(const psa_problem* prob, float softmax_scale, const void* q, const void* k,
+                 const void* v, const void* k_pooled, const void* v_pooled,
+                 const int8_t* level_map, const void* o, const float* lse, const void* dout,
+                 void* dq, void* dk, void* dv, void* ws, size_t ws_bytes, void* stream) {
+    psa::Shape s;
+    int rc = check_problem(prob, &s);
+    if (rc != PSA_OK) return rc;
+    if (s.dtype != PSA_BF16) return PSA_ERR_UNSUPPORTED;
+    // the key-side kernel lists (query head, query block) rows in LDS: 12-bit query block
+    // index, at most 16384 rows per KV head
+    const int g = s.H / s.Hkv;
+    if (s.NQB >= 4096 || static_cast<int64_t>(g) * s.NQB > 16384) return PSA_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !k_pooled || !v_pooled || !level_map || !o || !lse || !dout || !dq ||
+        !dk || !dv)
+        return PSA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_pooled) ||
+        !aligned16(v_pooled) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+        !aligned16(dk) || !aligned16(dv))
+        return PSA_ERR_INVALID_ARG;
+    if (!std::isfinite(softmax_scale)) return PSA_ERR_INVALID_ARG;
+    const AttnWs w0 = attn_ws_layout(s, nullptr);
+    const size_t need = w0.bytes + align_up(psa::attn_bwd_scratch_bytes(s));
+    if (ws == nullptr || ws_bytes < need) return PSA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return PSA_ERR_WORKSPACE;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(s.D));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    AttnWs w = attn_ws_layout(s, ws);
+    psa::IndexBufs ib{w.row_ptr, w.col_idx, w.dev_err};
+    hipError_t e = psa::launch_build_index(s, level_map, ib, st);
+    if (e != hipSuccess) return hip_status(e);
+    void* scratch = static_cast<char*>(ws) + w0.bytes;
+    return hip_status(psa::launch_attn_bwd(s, scale, q, k, v, k_pooled, v_pooled, level_map,
+                                           w.row_ptr, w.col_idx, o, lse, dout, dq, dk, dv,
+                                           scratch, st));
+}
+
 int psa_check_status(const void* ws, void* stream) {
     if (ws == nullptr) return PSA_ERR_INVALID_ARG;
     hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));

@@ -46,34 +46,12 @@
 #include <type_traits>
 
 #include "psa_attn_common.h"
+#include "psa_bf16_tile.h"
 
 namespace psa {
 namespace {
 
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
-
 constexpr float kLazyRescale = 8.0f;  // log2-domain headroom before the accumulators rescale
-// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their no-wait maxima
-// (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
-constexpr int kWaitVmcnt0 = 0x0F70;
-
-template <int D>
-struct Lay {
-    static constexpr int CH = D / 8;                 // 16-byte chunks per row
-    static constexpr int RPI = 1024 / (2 * D);       // rows per 1 KB direct-load instruction
-    static constexpr int INSTR = 64 * D * 2 / 1024;  // instructions per 64-row tile
-    // chunk swizzles (conflict-free operand reads, see the header)
-    static __device__ __forceinline__ int fk(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
-    static __device__ __forceinline__ int fv(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
-};
-
-// The K tile row that MFMA A-operand row r reads: bits 2 and 3 of r swapped.
-__device__ __forceinline__ int sigma(int r) {
-    return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
-}
 
 struct Tile {
     int l;     // level (4 = walk finished)
@@ -81,9 +59,6 @@ struct Tile {
     int lend;  // end of the current level's list
     int cnt;   // blocks present in the tile (<= 2^l)
 };
-
-template <int P>
-using IC = std::integral_constant<int, P>;
 
 // CONTIG: K and V rows are D elements apart (level 0 and the pooled levels share the lane
 // offsets of the direct loads).

@@ -37,6 +37,15 @@ hipError_t launch_attn_fwd(const Shape& s, float scale, const void* q, const voi
                            const int32_t* row_ptr, const int32_t* col_idx, void* o, float* lse,
                            bool pack, hipStream_t st);
 
+// Backward (bf16 only; hipErrorNotSupported otherwise). `scratch` holds
+// attn_bwd_scratch_bytes(s): per-row lse2 and D, and the f32 gradients of every level's rows.
+size_t attn_bwd_scratch_bytes(const Shape& s);
+hipError_t launch_attn_bwd(const Shape& s, float scale, const void* q, const void* k,
+                           const void* v, const void* kp, const void* vp, const int8_t* level_map,
+                           const int32_t* row_ptr, const int32_t* col_idx, const void* o,
+                           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                           void* scratch, hipStream_t st);
+
 struct MaskBufs {
     float* block_mass;   // [B,H,NQB,NKB]
     float* block_sim;    // [B,Hkv,NKB] or null

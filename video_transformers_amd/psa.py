@@ -33,8 +33,8 @@ SKIP = -1
 # every symbol include/psa.h declares
 EXPORTS = ("psa_pooled_rows", "psa_build_pyramid", "psa_mask_workspace_bytes", "psa_mask",
            "psa_mask_assign", "psa_build_index", "psa_attn_workspace_bytes", "psa_attn_fwd",
-           "psa_attn_fwd_indexed", "psa_attn_fwd_unpacked", "psa_check_status", "psa_status_string",
-           "psa_last_hip_error")
+           "psa_attn_fwd_indexed", "psa_attn_fwd_unpacked", "psa_attn_bwd_workspace_bytes",
+           "psa_attn_bwd", "psa_check_status", "psa_status_string", "psa_last_hip_error")
 
 
 class PsaError(RuntimeError):
@@ -89,6 +89,10 @@ def lib() -> ctypes.CDLL:
         L.psa_attn_fwd_indexed.restype = I32
         L.psa_attn_fwd_unpacked.argtypes = [P, ctypes.c_float, V, V, V, V, V, V, V, V, V, V]
         L.psa_attn_fwd_unpacked.restype = I32
+        L.psa_attn_bwd_workspace_bytes.argtypes = [P]
+        L.psa_attn_bwd_workspace_bytes.restype = SZ
+        L.psa_attn_bwd.argtypes = [P, ctypes.c_float] + [V] * 13 + [SZ, V]
+        L.psa_attn_bwd.restype = I32
         L.psa_check_status.argtypes, L.psa_check_status.restype = [V, V], I32
         L.psa_status_string.argtypes, L.psa_status_string.restype = [I32], ctypes.c_char_p
         L.psa_last_hip_error.argtypes, L.psa_last_hip_error.restype = [], I32
@@ -293,6 +297,36 @@ def attn_fwd_unpacked(q, k, v, k_pooled, v_pooled, row_ptr, col_idx, prob: Probl
                                        _ptr(col_idx), _ptr(out), _ptr(lse), _stream(stream)),
            "psa_attn_fwd_unpacked")
     return out, lse
+
+
+def attn_bwd_workspace(prob: Problem, device) -> torch.Tensor:
+    n = lib().psa_attn_bwd_workspace_bytes(prob.ref())
+    if n == 0:
+        raise PsaError(PSA_ERR_INVALID_ARG, "psa_attn_bwd_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def attn_bwd(q, k, v, k_pooled, v_pooled, level_map, o, lse, dout, prob: Problem, *,
+             scale: float = 0.0, dq: Optional[torch.Tensor] = None,
+             dk: Optional[torch.Tensor] = None, dv: Optional[torch.Tensor] = None,
+             ws: Optional[torch.Tensor] = None, stream=None):
+    """Backward of attn_fwd: returns (dq, dk, dv). o and dout share the problem's o_stride
+    (make_problem(..., o=o)); dq/dk/dv default to q's/k's/v's strides."""
+    if dout.stride() != o.stride():
+        raise ValueError("dout must have the same strides as o")
+    if dq is None:
+        dq = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    if dk is None:
+        dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=k.device)
+    if dv is None:
+        dv = torch.empty_strided(v.shape, v.stride(), dtype=v.dtype, device=v.device)
+    if ws is None:
+        ws = attn_bwd_workspace(prob, q.device)
+    _check(lib().psa_attn_bwd(prob.ref(), ctypes.c_float(scale), _ptr(q), _ptr(k), _ptr(v),
+                              _ptr(k_pooled), _ptr(v_pooled), _ptr(level_map), _ptr(o),
+                              _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
+                              ws.numel(), _stream(stream)), "psa_attn_bwd")
+    return dq, dk, dv
 
 
 def check_status(ws: torch.Tensor, stream=None) -> None:

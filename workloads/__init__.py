@@ -28,7 +28,7 @@ import torch
 SKIP = -1
 
 # tensor codes for the per-slice streams
-_T_Q, _T_K, _T_V, _T_MAP = 1, 2, 3, 4
+_T_Q, _T_K, _T_V, _T_MAP, _T_DO = 1, 2, 3, 4, 5
 
 
 @dataclasses.dataclass(frozen=True)
@@ -158,6 +158,17 @@ def make_v(wl: Workload, heads: Optional[Sequence[int]] = None) -> torch.Tensor:
 
 def make_qkv(wl: Workload):
     return make_q(wl), make_k(wl), make_v(wl)
+
+
+def make_dout_head(wl: Workload, b: int, h: int) -> torch.Tensor:
+    """The output gradient dO[b, h] ~ N(0, 1), shape [N, d] (pad rows zero)."""
+    rng = _rng(wl.seed, _T_DO, b, h)
+    return _finish(rng.standard_normal((wl.seq_len, wl.head_dim), dtype=np.float32), wl)
+
+
+def make_dout(wl: Workload, heads: Optional[Sequence[int]] = None) -> torch.Tensor:
+    """dO as [B, H, N, d], for the backward."""
+    return _stack(wl, make_dout_head, wl.heads_q, heads)
 
 
 def diag_blocks(wl: Workload, qb: int) -> range:
