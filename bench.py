@@ -14,7 +14,8 @@ FLOPs (4*d per executed (valid query, visible pooled key) pair) per second of st
 `attn` gives the attention kernel alone (ms/layer, TFLOP/s, % of the 2.5 PFLOP/s dense bf16
 MFMA peak, speedup over the same kernel on an all-level-0 map, and over the unpacked layout
 with one logical block per hardware tile on the same map). `roofline` is for that
-kernel, timed with HIP events on the stream it runs on. `cpu_baseline` times the CPU oracle
+kernel, timed with HIP events on the stream it runs on. `bwd` times psa_attn_bwd on the same
+map with a seeded output gradient (not part of `value`). `cpu_baseline` times the CPU oracle
 (fp64 numpy) on a bounded sample of the same workload on this host's cores.
 """
 from __future__ import annotations
@@ -299,12 +300,55 @@ def run(args) -> dict:
             torch.cuda.synchronize()
             times.append(ue[0].elapsed_time(ue[1]))
         unpacked_ms = float(np.median(times[1:]))
+    bwd = None
+    if not args.no_bwd and wl.dtype == "bf16":
+        bwd = _bwd_run(wl, prob, L, ptr, st, check, q, k, v, kp, vp, lm_host, o, lse, stream, flops)
     out = _report(args, wl, flops, pairs, dpairs, frac, d, B, H, N, computed_map, attn_ms,
                   attn_ms_mean, st_ms, dense_ms, wall)
+    if bwd is not None:
+        out["bwd"] = bwd
     out["attn"]["unpacked_same_map_ms"] = None if unpacked_ms != unpacked_ms else round(unpacked_ms, 3)
     out["attn"]["speedup_vs_unpacked"] = (None if unpacked_ms != unpacked_ms
                                           else round(unpacked_ms / attn_ms_mean, 2))
     return out
+
+
+def _bwd_run(wl, prob, L, ptr, st, check, q, k, v, kp, vp, lm_host, o, lse, stream, fwd_flops):
+    """psa_attn_bwd on the step's map, o and lse with a seeded output gradient: median of 5
+    timed launches (the call builds its block index and runs its four kernels). Work is
+    counted as 2.5x the forward's executed FLOPs (recomputed S, then dP, dV, dK, dQ: 10*d per
+    executed pair)."""
+    import ctypes
+    import torch
+    dev = q.device
+    dout = W.make_dout(wl).to(dev)
+    lm = torch.from_numpy(lm_host).to(dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    n = L.psa_attn_bwd_workspace_bytes(prob.ref())
+    ws = torch.empty(n, dtype=torch.uint8, device=dev)
+
+    def call():
+        check(L.psa_attn_bwd(prob.ref(), ctypes.c_float(0.0), ptr(q), ptr(k), ptr(v), ptr(kp),
+                             ptr(vp), ptr(lm), ptr(o), ptr(lse), ptr(dout), ptr(dq), ptr(dk),
+                             ptr(dv), ptr(ws), n, st), "attn bwd")
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    times = []
+    for _ in range(5):
+        ev[0].record(stream)
+        call()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        times.append(ev[0].elapsed_time(ev[1]))
+    check(L.psa_check_status(ptr(ws), st), "attn bwd status")
+    ms = float(np.median(times))
+    tf = 2.5 * fwd_flops / (ms * 1e-3) / 1e12
+    return {"ms_per_layer_median": round(ms, 4), "tflops_algorithmic": round(tf, 2),
+            "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+            "work": "2.5x the forward's executed FLOP (10*d per executed pair)",
+            "workspace_bytes": n}
 
 
 def _dense_run(args, wl, prob, L, ptr, st, check, q, k, v, kp, vp, o, lse, row_ptr, col_idx,
@@ -390,6 +434,8 @@ def main():
                     help="skip the all-level-0 comparison run (for profiling the PSA launches alone)")
     ap.add_argument("--no-unpacked", action="store_true",
                     help="skip the unpacked-layout comparison run (one logical block per tile)")
+    ap.add_argument("--no-bwd", action="store_true",
+                    help="skip the psa_attn_bwd timing (reported beside the forward metric)")
     ap.add_argument("--mask-mode", choices=("sampling", "antidiag", "meankey"), default=None,
                     help="score with this psa_mask mode instead of the workload's own")
     ap.add_argument("--cpu-budget", type=float, default=15.0)

@@ -229,7 +229,7 @@ size_t psa_attn_bwd_workspace_bytes(const psa_problem* prob);
  * null). The block index is built inside the call (into ws); invalid map entries are
  * recorded for psa_check_status as in psa_attn_fwd.
  * dtype PSA_BF16 only (bf16 MFMA, f32 accumulation; P and dS enter the products rounded to
- * bf16); seq_len/block_q < 4096 and (heads_q/heads_kv) * seq_len/block_q <= 16384.
+ * bf16); seq_len/block_q < 4096 and (heads_q/heads_kv) * seq_len/block_q <= 7680.
  * Anything else returns PSA_ERR_UNSUPPORTED.
  */
 int psa_attn_bwd(const psa_problem* prob, float softmax_scale, const void* q, const void* k,

@@ -158,6 +158,6 @@ def test_attn_bwd_host_checks():
         assert L.psa_attn_bwd(p.ref(), 0.0, *args13(**{name: None}), need, None) == P.PSA_ERR_INVALID_ARG, name
     assert L.psa_attn_bwd(p.ref(), 0.0, *args13(dk=ctypes.c_void_p(264)), need, None) == P.PSA_ERR_INVALID_ARG
     assert L.psa_attn_bwd(p.ref(), float("nan"), *args13(), need, None) == P.PSA_ERR_INVALID_ARG
-    # the key-side kernel's row list: at most 16384 (query head, query block) rows per KV head
-    big = _prob(dtype=P.PSA_BF16, heads_q=64, heads_kv=1, seq_len=32768, seq_valid=32768)
+    # the key-side kernel's row list: at most 7680 (query head, query block) rows per KV head
+    big = _prob(dtype=P.PSA_BF16, heads_q=32, heads_kv=1, seq_len=16384, seq_valid=16384)
     assert L.psa_attn_bwd(big.ref(), 0.0, *args13(), 1 << 40, None) == P.PSA_ERR_UNSUPPORTED

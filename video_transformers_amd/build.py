@@ -37,7 +37,6 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
 EXTRA = {
     "psa_attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
     "psa_mask.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-    "psa_attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

@@ -30,6 +30,7 @@
 // (global_load_lds_dwordx4), in the swizzled layouts of psa_bf16_tile.h: row-read tiles in
 // the fk layout, transposed-read tiles in the fv layout (K in the dq kernel and Q, dO in the
 // dkv kernel are read both ways, so they are staged twice).
+#include <limits.h>
 #include <math.h>
 
 #include "psa_attn_common.h"
@@ -237,6 +238,9 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_bwd_dq(BwdArgs a, int total_rows)
     const uint32_t lds_vr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Vr[0]));
     const uint32_t kr_base = row_read_base<D>(lds_kr, lane, 0);
     const uint32_t vr_base = row_read_base<D>(lds_vr, lane, 0);
+    uint32_t kt_base[DB];
+#pragma unroll
+    for (int dblk = 0; dblk < DB; ++dblk) kt_base[dblk] = tr_read_base<D>(lds_kt, lane, dblk, 0);
     __syncthreads();   // cols[] visible
 
     for (int l = 0; l < 4; ++l) {
@@ -271,10 +275,17 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_bwd_dq(BwdArgs a, int total_rows)
                     dp[e] = 0.f;
                 }
                 const uint32_t hoff = static_cast<uint32_t>(hh * 32 * D * 2);
+                bf16x8 ka[KK], va[KK];
 #pragma unroll
                 for (int kk = 0; kk < KK; ++kk) {
-                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row(kr_base + hoff, kk), qf[kk], s, 0, 0, 0);
-                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row(vr_base + hoff, kk), gf[kk], dp, 0, 0, 0);
+                    ka[kk] = read_row(kr_base + hoff, kk);
+                    va[kk] = read_row(vr_base + hoff, kk);
+                }
+                __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the products
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) {
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qf[kk], s, 0, 0, 0);
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[kk], gf[kk], dp, 0, 0, 0);
                 }
                 // P and dS of the 16 keys this lane holds: tile key t = 32 hh + 16 j + 8 hi + u
                 // (j = r / 8, u = r % 8); a run of 8 aligned keys lies in one logical block
@@ -286,15 +297,17 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_bwd_dq(BwdArgs a, int total_rows)
                     const bool present = sblk < cnt;
                     const int kb = cols[base + (present ? sblk : 0)];
                     const int last0 = ((kb * rs + (t0 & (rs - 1)) + 1) << l) - 1;   // key t0's last token
-                    const int lim = a.causal ? min(qt, a.Nv - 1) : a.Nv - 1;
+                    // key t0 + x is visible iff its last token <= lim (absent blocks: never)
+                    const int lim = present ? (a.causal ? min(qt, a.Nv - 1) : a.Nv - 1) : -1;
 #pragma unroll
                     for (int u = 0; u < 8; u += 2) {
                         float ds2[2];
 #pragma unroll
                         for (int w = 0; w < 2; ++w) {
                             const int e = 8 * j + u + w;
-                            const bool vis = present && last0 + ((u + w) << l) <= lim;
-                            const float p = vis ? fast_exp2(fmaf(s[e], a.c, static_cast<float>(l) - lse2)) : 0.f;
+                            const bool vis = last0 + ((u + w) << l) <= lim;
+                            // branch-free: an invisible key's exponent is -inf, its P exactly 0
+                            const float p = fast_exp2(vis ? fmaf(s[e], a.c, static_cast<float>(l) - lse2) : -INFINITY);
                             ds2[w] = p * (dp[e] - dd);
                         }
                         dsk[(8 * j + u) >> 1] = pack_bf16x2(ds2[0], ds2[1]);
@@ -304,11 +317,13 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_bwd_dq(BwdArgs a, int total_rows)
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     const bf16x8 df = __builtin_bit_cast(bf16x8, u32x4{dsk[4 * j], dsk[4 * j + 1], dsk[4 * j + 2], dsk[4 * j + 3]});
+                    bf16x8 kt[DB];
 #pragma unroll
-                    for (int dblk = 0; dblk < DB; ++dblk) {
-                        const bf16x8 kt = read_tr<D>(tr_read_base<D>(lds_kt, lane, dblk, 0) + hoff, j);
-                        acc[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt, df, acc[dblk], 0, 0, 0);
-                    }
+                    for (int dblk = 0; dblk < DB; ++dblk) kt[dblk] = read_tr<D>(kt_base[dblk] + hoff, j);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int dblk = 0; dblk < DB; ++dblk)
+                        acc[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kt[dblk], df, acc[dblk], 0, 0, 0);
                 }
             }
         }
@@ -339,9 +354,10 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) k_bwd_dkv(BwdArgs a, in
     constexpr int NW = 4;
     constexpr int KK = D / 16;
     constexpr int DB = D / 32;
-    __shared__ __attribute__((aligned(1024))) bf16_bits Xs[4][64 * D];   // Q rows, Q^T, dO rows, dO^T
-    __shared__ __attribute__((aligned(16))) float Ls[64];
-    __shared__ __attribute__((aligned(16))) float Ds[64];
+    // two buffer sets of the 64-query chunk tiles: Q rows, Q^T, dO rows, dO^T
+    __shared__ __attribute__((aligned(1024))) bf16_bits Xs[2][4][64 * D];
+    __shared__ __attribute__((aligned(16))) float Ls[2][64];
+    __shared__ __attribute__((aligned(16))) float Ds[2][64];
     __shared__ int wsum[NW + 1];
     extern __shared__ int ent[];   // listed rows: (query head in group << 20) | (qb << 8) | blocks
 
@@ -425,94 +441,177 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) k_bwd_dkv(BwdArgs a, in
             dva[i][e] = 0.f;
         }
 
-    uint32_t lx[4];
+    // items: (listed row, 64-query chunk); item it+1's tiles load while item it computes
+    uint32_t lx[2][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lx[i] = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Xs[i][0]));
-    const uint32_t q_rows = row_read_base<D>(lx[0], lane, 32 * qh);
-    const uint32_t g_rows = row_read_base<D>(lx[2], lane, 32 * qh);
-    const uint32_t qs2b = static_cast<uint32_t>(a.qs2) * 2u;
-    const uint32_t os2b = static_cast<uint32_t>(a.os2) * 2u;
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            lx[u][i] = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Xs[u][i][0]));
+    constexpr uint32_t kSetBytes = 4u * 64u * D * 2u;   // one buffer set (Q, Q^T, dO, dO^T)
+    const uint32_t q_rows = row_read_base<D>(lx[0][0], lane, 32 * qh);
+    const uint32_t g_rows = row_read_base<D>(lx[0][2], lane, 32 * qh);
+    uint32_t qt_base[DB], gt_base[DB];
+#pragma unroll
+    for (int dblk = 0; dblk < DB; ++dblk) {
+        qt_base[dblk] = tr_read_base<D>(lx[0][1], lane, dblk, 32 * qh);
+        gt_base[dblk] = tr_read_base<D>(lx[0][3], lane, dblk, 32 * qh);
+    }
+    // direct loads of a chunk: 64 consecutive rows of Q (and dO) of one head, each staged in
+    // the row layout and the transposed-read layout. Instruction mi of this wave covers rows
+    // (wave * IPW + mi) * RPI + rr; its lane offsets are loop invariants, so an instruction
+    // costs one M0 write.
+    constexpr int IPW = LY::INSTR / NW;
+    uint32_t qo_r[IPW], qo_t[IPW], go_r[IPW], go_t[IPW];
+    {
+        const int rr = lane / LY::CH;
+        const int p = lane % LY::CH;
+        const uint32_t qs2b = static_cast<uint32_t>(a.qs2) * 2u;
+        const uint32_t os2b = static_cast<uint32_t>(a.os2) * 2u;
+#pragma unroll
+        for (int mi = 0; mi < IPW; ++mi) {
+            const int trow = (wave * IPW + mi) * LY::RPI + rr;   // tile row of this lane
+            const uint32_t rowq = static_cast<uint32_t>(mi * LY::RPI + rr) * qs2b;
+            const uint32_t rowg = static_cast<uint32_t>(mi * LY::RPI + rr) * os2b;
+            qo_r[mi] = rowq + static_cast<uint32_t>((p ^ LY::fk(trow)) << 4);
+            qo_t[mi] = rowq + static_cast<uint32_t>((p ^ LY::fv(trow)) << 4);
+            go_r[mi] = rowg + static_cast<uint32_t>((p ^ LY::fk(trow)) << 4);
+            go_t[mi] = rowg + static_cast<uint32_t>((p ^ LY::fv(trow)) << 4);
+        }
+    }
+    // items (listed row, 64-query chunk): item it is list entry it >> csh, chunk it & cmask
+    const int csh = a.BQ == 128 ? 1 : 0;
+    const int items = count << csh;
+    auto item_entry = [&](int it) { return __builtin_amdgcn_readfirstlane(ent[it >> csh]); };
+    auto item_head = [&](int en) { return hk * g + (en >> 20); };
+    auto item_q0 = [&](int en, int it) { return ((en >> 8) & 0xfff) * a.BQ + ((it & csh) << 6); };
+    auto issue = [&](int it, int buf) {
+        const int en = item_entry(it);
+        const int h = item_head(en);
+        const int q0 = item_q0(en, it);
+        const int64_t r0 = static_cast<int64_t>(wave * IPW * LY::RPI + q0);
+        const char* qsrc = reinterpret_cast<const char*>(a.q + b * a.qs0 + h * a.qs1 + r0 * a.qs2);
+        const char* gsrc = reinterpret_cast<const char*>(a.dout + b * a.os0 + h * a.os1 + r0 * a.os2);
+        const uint32_t l0 = lx[0][0] + (buf ? kSetBytes : 0u) + static_cast<uint32_t>(wave * IPW) * 1024u;
+#pragma unroll
+        for (int mi = 0; mi < IPW; ++mi) {
+            const uint32_t lo = l0 + static_cast<uint32_t>(mi) * 1024u;
+            dma16(qsrc, qo_r[mi], lo);
+            dma16(qsrc, qo_t[mi], lo + 64u * D * 2u);
+            dma16(gsrc, go_r[mi], lo + 2u * 64u * D * 2u);
+            dma16(gsrc, go_t[mi], lo + 3u * 64u * D * 2u);
+        }
+    };
+    // wave 0 fetches the next item's lse2 and D into registers and stores them after the
+    // current item's products
+    float nl = 0.f, nd = 0.f;
+    auto fetch_ld = [&](int it) {
+        if (tid < 64) {
+            const int en = item_entry(it);
+            const int64_t r = (static_cast<int64_t>(b) * a.H + item_head(en)) * a.N + item_q0(en, it) + tid;
+            nl = a.lse2[r];
+            nd = a.dd[r];
+        }
+    };
+    if (items > 0) {
+        issue(0, 0);
+        fetch_ld(0);
+        if (tid < 64) {
+            Ls[0][tid] = nl;
+            Ds[0][tid] = nd;
+        }
+    }
 
-    for (int it = 0; it < count; ++it) {
-        const int en = ent[it];
-        const int hl = en >> 20;
-        const int qb = (en >> 8) & 0xfff;
+    for (int it = 0; it < items; ++it) {
+        const int buf = it & 1;
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // this item's tiles
+        __syncthreads();   // publish them; every wave is done with the other buffer set
+        if (it + 1 < items) {
+            issue(it + 1, buf ^ 1);
+            fetch_ld(it + 1);
+        }
+        const int en = item_entry(it);
+        const int q0 = item_q0(en, it);
         const int bits = en & 0xff;
-        const int h = hk * g + hl;
+        // query q sees this lane's key iff q >= kmin (an unlisted or invalid key: never)
         const bool sub_ok = key_ok && ((bits >> ksub) & 1);
-        for (int qc = 0; qc < a.BQ; qc += 64) {
-            const int q0 = qb * a.BQ + qc;   // first query of the chunk
-            const char* qsrc = reinterpret_cast<const char*>(a.q + b * a.qs0 + h * a.qs1 + static_cast<int64_t>(q0) * a.qs2);
-            const char* gsrc = reinterpret_cast<const char*>(a.dout + b * a.os0 + h * a.os1 + static_cast<int64_t>(q0) * a.os2);
-            __syncthreads();   // the previous chunk's reads are done
-            load_tile<D, NW, false>(lx[0], wave, lane, qs2b, [&](int t) { return qsrc + static_cast<uint64_t>(t) * qs2b; });
-            load_tile<D, NW, true>(lx[1], wave, lane, qs2b, [&](int t) { return qsrc + static_cast<uint64_t>(t) * qs2b; });
-            load_tile<D, NW, false>(lx[2], wave, lane, os2b, [&](int t) { return gsrc + static_cast<uint64_t>(t) * os2b; });
-            load_tile<D, NW, true>(lx[3], wave, lane, os2b, [&](int t) { return gsrc + static_cast<uint64_t>(t) * os2b; });
-            if (tid < 64) {
-                const int64_t r = (static_cast<int64_t>(b) * a.H + h) * a.N + q0 + tid;
-                Ls[tid] = a.lse2[r];
-                Ds[tid] = a.dd[r];
-            }
-            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-            __syncthreads();
+        const int kmin = sub_ok ? (a.causal ? klast : INT_MIN) : INT_MAX;
+        const uint32_t boff = buf ? kSetBytes : 0u;
 
-            f32x16 s, dp;
+        // every operand row of S and dP first (one wave per SIMD: nothing else hides the
+        // LDS latency), then the two MFMA chains
+        bf16x8 qa[KK], ga[KK];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                s[e] = 0.f;
-                dp[e] = 0.f;
-            }
+        for (int kk = 0; kk < KK; ++kk) {
+            qa[kk] = read_row(q_rows + boff, kk);
+            ga[kk] = read_row(g_rows + boff, kk);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the products
+        f32x16 s, dp;
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) {
-                s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row(q_rows, kk), kf[kk], s, 0, 0, 0);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_row(g_rows, kk), vf[kk], dp, 0, 0, 0);
-            }
-            // register e holds chunk query 32 qh + 16 (e / 8) + 8 hi + e % 8, this lane's key
-            uint32_t pk[8], dsk[8];
+        for (int e = 0; e < 16; ++e) {
+            s[e] = 0.f;
+            dp[e] = 0.f;
+        }
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int qi0 = 32 * qh + 16 * j + 8 * hi;   // 8 consecutive chunk queries
-                const f32x4 la = *reinterpret_cast<const f32x4*>(&Ls[qi0]);
-                const f32x4 lb2 = *reinterpret_cast<const f32x4*>(&Ls[qi0 + 4]);
-                const f32x4 da = *reinterpret_cast<const f32x4*>(&Ds[qi0]);
-                const f32x4 db = *reinterpret_cast<const f32x4*>(&Ds[qi0 + 4]);
+        for (int kk = 0; kk < KK; ++kk) {
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], kf[kk], s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[kk], vf[kk], dp, 0, 0, 0);
+        }
+        // register e holds chunk query 32 qh + 16 (e / 8) + 8 hi + e % 8, this lane's key
+        uint32_t pk[8], dsk[8];
 #pragma unroll
-                for (int u = 0; u < 8; u += 2) {
-                    float pp[2], ds2[2];
+        for (int j = 0; j < 2; ++j) {
+            const int qi0 = 32 * qh + 16 * j + 8 * hi;   // 8 consecutive chunk queries
+            const f32x4 la = *reinterpret_cast<const f32x4*>(&Ls[buf][qi0]);
+            const f32x4 lb2 = *reinterpret_cast<const f32x4*>(&Ls[buf][qi0 + 4]);
+            const f32x4 da = *reinterpret_cast<const f32x4*>(&Ds[buf][qi0]);
+            const f32x4 db = *reinterpret_cast<const f32x4*>(&Ds[buf][qi0 + 4]);
 #pragma unroll
-                    for (int w = 0; w < 2; ++w) {
-                        const int e = 8 * j + u + w;
-                        const int x = u + w;
-                        const float lq = x < 4 ? la[x] : lb2[x - 4];
-                        const float dq = x < 4 ? da[x] : db[x - 4];
-                        const bool vis = sub_ok && (!a.causal || klast <= q0 + qi0 + x);
-                        const float p = vis ? fast_exp2(fmaf(s[e], a.c, static_cast<float>(l) - lq)) : 0.f;
-                        pp[w] = p;
-                        ds2[w] = p * (dp[e] - dq);
-                    }
-                    pk[(8 * j + u) >> 1] = pack_bf16x2(pp[0], pp[1]);
-                    dsk[(8 * j + u) >> 1] = pack_bf16x2(ds2[0], ds2[1]);
+            for (int u = 0; u < 8; u += 2) {
+                float pp[2], ds2[2];
+#pragma unroll
+                for (int w = 0; w < 2; ++w) {
+                    const int e = 8 * j + u + w;
+                    const int x = u + w;
+                    const float lq = x < 4 ? la[x] : lb2[x - 4];
+                    const float dq = x < 4 ? da[x] : db[x - 4];
+                    const bool vis = q0 + qi0 + x >= kmin;
+                    const float p = fast_exp2(vis ? fmaf(s[e], a.c, static_cast<float>(l) - lq) : -INFINITY);
+                    pp[w] = p;
+                    ds2[w] = p * (dp[e] - dq);
                 }
+                pk[(8 * j + u) >> 1] = pack_bf16x2(pp[0], pp[1]);
+                dsk[(8 * j + u) >> 1] = pack_bf16x2(ds2[0], ds2[1]);
             }
+        }
+        // the transposed operands of fragment j are read before its 2 * DB products
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{pk[4 * j], pk[4 * j + 1], pk[4 * j + 2], pk[4 * j + 3]});
-                const bf16x8 df = __builtin_bit_cast(bf16x8, u32x4{dsk[4 * j], dsk[4 * j + 1], dsk[4 * j + 2], dsk[4 * j + 3]});
+        for (int j = 0; j < 2; ++j) {
+            const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{pk[4 * j], pk[4 * j + 1], pk[4 * j + 2], pk[4 * j + 3]});
+            const bf16x8 df = __builtin_bit_cast(bf16x8, u32x4{dsk[4 * j], dsk[4 * j + 1], dsk[4 * j + 2], dsk[4 * j + 3]});
+            bf16x8 gtr[DB], qtr[DB];
 #pragma unroll
-                for (int dblk = 0; dblk < DB; ++dblk) {
-                    const bf16x8 gt = read_tr<D>(tr_read_base<D>(lx[3], lane, dblk, 32 * qh), j);
-                    dva[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gt, pf, dva[dblk], 0, 0, 0);
-                    const bf16x8 qt = read_tr<D>(tr_read_base<D>(lx[1], lane, dblk, 32 * qh), j);
-                    dka[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qt, df, dka[dblk], 0, 0, 0);
-                }
+            for (int dblk = 0; dblk < DB; ++dblk) {
+                gtr[dblk] = read_tr<D>(gt_base[dblk] + boff, j);
+                qtr[dblk] = read_tr<D>(qt_base[dblk] + boff, j);
             }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int dblk = 0; dblk < DB; ++dblk) {
+                dva[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gtr[dblk], pf, dva[dblk], 0, 0, 0);
+                dka[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qtr[dblk], df, dka[dblk], 0, 0, 0);
+            }
+        }
+        if (it + 1 < items && tid < 64) {
+            Ls[buf ^ 1][tid] = nl;
+            Ds[buf ^ 1][tid] = nd;
         }
     }
 
     // ---- add the two query halves (waves 2, 3 hand theirs to waves 0, 1), then write ----
     __syncthreads();
-    float* red = reinterpret_cast<float*>(&Xs[0][0]);   // [kh][2][DB][16][64] floats
+    float* red = reinterpret_cast<float*>(&Xs[0][0][0]);   // [kh][2][DB][16][64] floats
     if (qh == 1) {
 #pragma unroll
         for (int dblk = 0; dblk < DB; ++dblk)
