@@ -21,8 +21,10 @@
 //                per listed row and 64-query chunk: S = Q Kbar^T, dP = dO Vbar^T,
 //                dVbar^T += dO^T P, dKbar^T += Q^T dS. Each wave owns 32 keys of the tile and
 //                half of the chunk's queries; the two query halves are added at the end. The
-//                tile's pooled-row gradients go to an f32 workspace (every row written, zeros
-//                included: no clearing pass).
+//                next chunk's Q, dO, lse2 and D arrive by direct loads while the current one
+//                computes (the loop holds no load the compiler tracks: a compiler-placed wait
+//                would also drain the direct loads in flight). The tile's pooled-row gradients
+//                go to an f32 workspace (every row written, zeros included: no clearing pass).
 //  k_bwd_pool    dK[t] = sum_l 2^-l dKbar_l[t >> l] (and dV), in the input dtype.
 //
 // All products run on v_mfma_f32_32x32x16_bf16 with f32 accumulation; P and dS enter the
@@ -480,6 +482,8 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) k_bwd_dkv(BwdArgs a, in
         }
     }
     // items (listed row, 64-query chunk): item it is list entry it >> csh, chunk it & cmask
+    const uint32_t ls_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Ls[0][0]));
+    const uint32_t ds_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Ds[0][0]));
     const int csh = a.BQ == 128 ? 1 : 0;
     const int items = count << csh;
     auto item_entry = [&](int it) { return __builtin_amdgcn_readfirstlane(ent[it >> csh]); };
@@ -501,35 +505,22 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) k_bwd_dkv(BwdArgs a, in
             dma16(gsrc, go_r[mi], lo + 2u * 64u * D * 2u);
             dma16(gsrc, go_t[mi], lo + 3u * 64u * D * 2u);
         }
-    };
-    // wave 0 fetches the next item's lse2 and D into registers and stores them after the
-    // current item's products
-    float nl = 0.f, nd = 0.f;
-    auto fetch_ld = [&](int it) {
-        if (tid < 64) {
-            const int en = item_entry(it);
-            const int64_t r = (static_cast<int64_t>(b) * a.H + item_head(en)) * a.N + item_q0(en, it) + tid;
-            nl = a.lse2[r];
-            nd = a.dd[r];
+        // lse2 and D of the chunk's 64 queries: 16 lanes x 16 bytes each, also by direct load
+        // (no global load the compiler tracks may sit in the loop: its waits would also
+        // drain the tile loads in flight)
+        if (wave == 0 && lane < 16) {
+            const int64_t r = (static_cast<int64_t>(b) * a.H + h) * a.N + q0;
+            dma16(a.lse2 + r, static_cast<uint32_t>(lane) * 16u, ls_lds + (buf ? 256u : 0u));
+            dma16(a.dd + r, static_cast<uint32_t>(lane) * 16u, ds_lds + (buf ? 256u : 0u));
         }
     };
-    if (items > 0) {
-        issue(0, 0);
-        fetch_ld(0);
-        if (tid < 64) {
-            Ls[0][tid] = nl;
-            Ds[0][tid] = nd;
-        }
-    }
+    if (items > 0) issue(0, 0);
 
     for (int it = 0; it < items; ++it) {
         const int buf = it & 1;
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // this item's tiles
         __syncthreads();   // publish them; every wave is done with the other buffer set
-        if (it + 1 < items) {
-            issue(it + 1, buf ^ 1);
-            fetch_ld(it + 1);
-        }
+        if (it + 1 < items) issue(it + 1, buf ^ 1);
         const int en = item_entry(it);
         const int q0 = item_q0(en, it);
         const int bits = en & 0xff;
@@ -558,8 +549,9 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) k_bwd_dkv(BwdArgs a, in
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], kf[kk], s, 0, 0, 0);
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[kk], vf[kk], dp, 0, 0, 0);
         }
-        // register e holds chunk query 32 qh + 16 (e / 8) + 8 hi + e % 8, this lane's key
-        uint32_t pk[8], dsk[8];
+        // register e holds chunk query 32 qh + 16 (e / 8) + 8 hi + e % 8, this lane's key.
+        // Fragment j (registers 8j..8j+7) is finished, then its 2 * DB products issue and run
+        // while the next fragment's P and dS are computed.
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int qi0 = 32 * qh + 16 * j + 8 * hi;   // 8 consecutive chunk queries
@@ -567,6 +559,13 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) k_bwd_dkv(BwdArgs a, in
             const f32x4 lb2 = *reinterpret_cast<const f32x4*>(&Ls[buf][qi0 + 4]);
             const f32x4 da = *reinterpret_cast<const f32x4*>(&Ds[buf][qi0]);
             const f32x4 db = *reinterpret_cast<const f32x4*>(&Ds[buf][qi0 + 4]);
+            bf16x8 gtr[DB], qtr[DB];
+#pragma unroll
+            for (int dblk = 0; dblk < DB; ++dblk) {
+                gtr[dblk] = read_tr<D>(gt_base[dblk] + boff, j);
+                qtr[dblk] = read_tr<D>(qt_base[dblk] + boff, j);
+            }
+            uint32_t pk[4], dsk[4];
 #pragma unroll
             for (int u = 0; u < 8; u += 2) {
                 float pp[2], ds2[2];
@@ -574,38 +573,25 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) k_bwd_dkv(BwdArgs a, in
                 for (int w = 0; w < 2; ++w) {
                     const int e = 8 * j + u + w;
                     const int x = u + w;
-                    const float lq = x < 4 ? la[x] : lb2[x - 4];
+                    const float lq = static_cast<float>(l) - (x < 4 ? la[x] : lb2[x - 4]);   // l - lse2
                     const float dq = x < 4 ? da[x] : db[x - 4];
                     const bool vis = q0 + qi0 + x >= kmin;
-                    const float p = fast_exp2(vis ? fmaf(s[e], a.c, static_cast<float>(l) - lq) : -INFINITY);
+                    const float p = fast_exp2(vis ? fmaf(s[e], a.c, lq) : -INFINITY);
                     pp[w] = p;
                     ds2[w] = p * (dp[e] - dq);
                 }
-                pk[(8 * j + u) >> 1] = pack_bf16x2(pp[0], pp[1]);
-                dsk[(8 * j + u) >> 1] = pack_bf16x2(ds2[0], ds2[1]);
+                pk[u >> 1] = pack_bf16x2(pp[0], pp[1]);
+                dsk[u >> 1] = pack_bf16x2(ds2[0], ds2[1]);
             }
-        }
-        // the transposed operands of fragment j are read before its 2 * DB products
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{pk[4 * j], pk[4 * j + 1], pk[4 * j + 2], pk[4 * j + 3]});
-            const bf16x8 df = __builtin_bit_cast(bf16x8, u32x4{dsk[4 * j], dsk[4 * j + 1], dsk[4 * j + 2], dsk[4 * j + 3]});
-            bf16x8 gtr[DB], qtr[DB];
-#pragma unroll
-            for (int dblk = 0; dblk < DB; ++dblk) {
-                gtr[dblk] = read_tr<D>(gt_base[dblk] + boff, j);
-                qtr[dblk] = read_tr<D>(qt_base[dblk] + boff, j);
-            }
+            const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+            const bf16x8 df = __builtin_bit_cast(bf16x8, u32x4{dsk[0], dsk[1], dsk[2], dsk[3]});
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int dblk = 0; dblk < DB; ++dblk) {
                 dva[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gtr[dblk], pf, dva[dblk], 0, 0, 0);
                 dka[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qtr[dblk], df, dka[dblk], 0, 0, 0);
             }
-        }
-        if (it + 1 < items && tid < 64) {
-            Ls[buf ^ 1][tid] = nl;
-            Ds[buf ^ 1][tid] = nd;
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
