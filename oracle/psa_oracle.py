@@ -467,7 +467,8 @@ def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, level_map: np.nd
 # ----------------------------------------------------------------------------------------
 
 def attention_backward_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, level_map: np.ndarray,
-                            do: np.ndarray, p: Problem, scale: Optional[float] = None):
+                            do: np.ndarray, p: Problem, scale: Optional[float] = None,
+                            qblocks: Optional[Iterable[int]] = None):
     """Gradients of the PSA forward of one (batch, head) with respect to q, k and v (level 0),
     given the output gradient do [N, d]. Returns (dq [N, d], dk [N, d], dv [N, d]) in fp64.
 
@@ -480,7 +481,8 @@ def attention_backward_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, level_m
     each gathered pooled row's gradient is added to its level's pooled row, and a pooled row
     of level l, the mean of 2**l consecutive tokens, hands 2**-l of its gradient to each of
     them. Pad query rows and rows with no visible key have a constant output (zero): they
-    contribute nothing.
+    contribute nothing. With `qblocks`, only those query blocks are visited: their dq rows
+    are exact, other dq rows stay zero, and dk, dv hold only those blocks' contributions.
     """
     sc = p.scale if scale is None else scale
     lk, lvv = pyramid(k), pyramid(v)
@@ -488,7 +490,7 @@ def attention_backward_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, level_m
     gk = {l: np.zeros_like(lk[l]) for l in range(NUM_LEVELS)}
     gv = {l: np.zeros_like(lvv[l]) for l in range(NUM_LEVELS)}
     dq = np.zeros((n, d))
-    for qb in range(p.n_qblocks):
+    for qb in (range(p.n_qblocks) if qblocks is None else qblocks):
         qi = np.arange(qb * p.block_q, (qb + 1) * p.block_q)
         qi = qi[qi < p.seq_valid]
         if qi.size == 0:
