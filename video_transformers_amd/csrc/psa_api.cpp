@@ -290,8 +290,8 @@ int psa_attn_bwd(const psa_problem* prob, float softmax_scale, const void* q, co
     int rc = check_problem(prob, &s);
     if (rc != PSA_OK) return rc;
     if (s.dtype != PSA_BF16) return PSA_ERR_UNSUPPORTED;
-    // the key-side kernel lists (query head, query block) rows in LDS beside its two tile
-    // buffer sets: 12-bit query block index, at most 7680 rows per KV head
+    // the key-side kernel lists (query head, query block) rows in LDS beside its three chunk
+    // buffer sets and the P/dS exchange: 12-bit query block index, at most 7680 rows per KV head
     const int g = s.H / s.Hkv;
     if (s.NQB >= 4096 || static_cast<int64_t>(g) * s.NQB > 7680) return PSA_ERR_UNSUPPORTED;
     if (!q || !k || !v || !k_pooled || !v_pooled || !level_map || !o || !lse || !dout || !dq ||

@@ -19,19 +19,22 @@
 //                level map for the (query head, query block) rows that list one of the
 //                tile's blocks at that level (ordered, so the sums are deterministic), then
 //                per listed row and 64-query chunk: S = Q Kbar^T, dP = dO Vbar^T,
-//                dVbar^T += dO^T P, dKbar^T += Q^T dS. Each wave owns 32 keys of the tile and
-//                half of the chunk's queries; the two query halves are added at the end. The
-//                next chunk's Q, dO, lse2 and D arrive by direct loads while the current one
-//                computes (the loop holds no load the compiler tracks: a compiler-placed wait
-//                would also drain the direct loads in flight). The tile's pooled-row gradients
-//                go to an f32 workspace (every row written, zeros included: no clearing pass).
+//                dVbar^T += dO^T P, dKbar^T += Q^T dS. Eight waves: four producers (S, dP,
+//                P, dS; each owns 32 keys and half of the chunk's queries) hand P and dS
+//                through LDS to four consumers (the dV / dK products and accumulators), one
+//                chunk behind; a producer and its consumer share a SIMD. Three chunk buffer
+//                sets (producers' chunk, consumers' chunk, the next one loading) by direct
+//                loads, Q and dO staged once each in the fq layout. The loop holds no load the
+//                compiler tracks (a compiler-placed wait would also drain the direct loads in
+//                flight). The tile's pooled-row gradients go to an f32 workspace (every row
+//                written, zeros included: no clearing pass).
 //  k_bwd_pool    dK[t] = sum_l 2^-l dKbar_l[t >> l] (and dV), in the input dtype.
 //
 // All products run on v_mfma_f32_32x32x16_bf16 with f32 accumulation; P and dS enter the
 // products rounded to bf16. Operand tiles are staged in LDS by direct loads
-// (global_load_lds_dwordx4), in the swizzled layouts of psa_bf16_tile.h: row-read tiles in
-// the fk layout, transposed-read tiles in the fv layout (K in the dq kernel and Q, dO in the
-// dkv kernel are read both ways, so they are staged twice).
+// (global_load_lds_dwordx4), in the swizzled layouts of psa_bf16_tile.h: in the dq kernel K
+// rows in the fk layout and a second copy of K in the fv layout for its transposed reads, V
+// in fk; in the dkv kernel Q and dO once each in the fq layout, read both ways.
 #include <limits.h>
 #include <math.h>
 
@@ -345,21 +348,32 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_bwd_dq(BwdArgs a, int total_rows)
 }
 
 // ---------------------------------------------------------------------------------------
-// dKbar, dVbar: one workgroup (4 waves) per (batch, KV head, level, 64-row pooled tile).
-// Wave w owns tile keys 32 (w & 1) + 0..31 and queries 32 (w >> 1) + 0..31 of each 64-query
-// chunk of a listed query block.
+// dKbar, dVbar: one workgroup of 8 waves per (batch, KV head, level, 64-row pooled tile).
+// Waves 0..3 produce: wave p owns tile keys 32 (p & 1) + 0..31 and queries 32 (p >> 1) + 0..31
+// of each 64-query chunk of a listed query block; it computes S = Q Kbar^T, dP = dO Vbar^T,
+// P and dS and hands P, dS to LDS. Wave p + 4 consumes them one chunk later: dVbar^T +=
+// dO^T P, dKbar^T += Q^T dS for the same keys and queries. A producer and its consumer share a
+// SIMD, so one's softmax work runs beside the other's MFMAs. Chunks are staged once each (the
+// fq layout serves the row reads and the transposed reads) in three buffer sets: the chunk
+// the producers work on, the one the consumers work on, and the next one loading.
 // ---------------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t row_read_base_fq_impl(uint32_t lds, int r, int hi, int f, int rowbytes) {
+    return lds + static_cast<uint32_t>(r * rowbytes + 16 * ((hi ^ f) & 1) + 16 * (f & ~1));
+}
+
 template <int D>
-__global__ void __launch_bounds__(256, D == 128 ? 1 : 2) k_bwd_dkv(BwdArgs a, int total_tiles, int tiles_per_bh,
+__global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a, int total_tiles, int tiles_per_bh,
                                                    int t1, int t2, int t3) {
     using LY = Lay<D>;
-    constexpr int NW = 4;
+    constexpr int NW = 8;
     constexpr int KK = D / 16;
     constexpr int DB = D / 32;
-    // two buffer sets of the 64-query chunk tiles: Q rows, Q^T, dO rows, dO^T
-    __shared__ __attribute__((aligned(1024))) bf16_bits Xs[2][4][64 * D];
-    __shared__ __attribute__((aligned(16))) float Ls[2][64];
-    __shared__ __attribute__((aligned(16))) float Ds[2][64];
+    constexpr int NSET = 3;
+    constexpr uint32_t kTileBytes = 64u * D * 2u;
+    __shared__ __attribute__((aligned(1024))) bf16_bits Xs[NSET][2][64 * D];   // [set][Q, dO]
+    __shared__ __attribute__((aligned(16))) float Ls[NSET][64];
+    __shared__ __attribute__((aligned(16))) float Ds[NSET][64];
+    __shared__ __attribute__((aligned(16))) u32x4 Xch[2][4][2][2][64];   // [buf][producer][j][P, dS][lane]
     __shared__ int wsum[NW + 1];
     extern __shared__ int ent[];   // listed rows: (query head in group << 20) | (qb << 8) | blocks
 
@@ -368,8 +382,9 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) k_bwd_dkv(BwdArgs a, in
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31;
     const int hi = lane >> 5;
-    const int kh = wave & 1;
-    const int qh = wave >> 1;
+    const int pw = wave & 3;      // producer / consumer pair index
+    const int kh = pw & 1;
+    const int qh = pw >> 1;
 
     const int nper = (total_tiles + 7) >> 3;
     const int tile = (blockIdx.x & 7) * nper + (blockIdx.x >> 3);
@@ -383,13 +398,12 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) k_bwd_dkv(BwdArgs a, in
     const int g = a.H / a.Hkv;
     const int nb = 1 << l;             // logical blocks per tile
     const int sh = 6 - l;
-    const int nrows = min(64, (a.N >> l) - 64 * m);   // pooled rows of the level in this tile
 
     // ---- the rows (query head, query block) that list one of the tile's blocks at level l,
     //      in ascending order ----
     int count = 0;
     const int cand = g * a.NQB;
-    for (int c0 = 0; c0 < cand; c0 += 256) {
+    for (int c0 = 0; c0 < cand; c0 += 64 * NW) {
         const int e = c0 + tid;
         int bits = 0;
         if (e < cand) {
@@ -414,222 +428,259 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) k_bwd_dkv(BwdArgs a, in
         __syncthreads();
     }
 
-    // ---- this wave's 32 keys, stationary in registers (B operands) ----
-    const int jrow = 64 * m + 32 * kh + l32;          // pooled row of level l
-    const bool in_level = jrow < (a.N >> l);
-    const int jr = in_level ? jrow : 0;
-    const int klast = ((jr + 1) << l) - 1;             // last token the key stands for
-    const bool key_ok = in_level && klast < a.Nv;
-    const int ksub = (32 * kh + l32) >> sh;            // its block inside the tile
-    bf16x8 kf[KK], vf[KK];
-    {
-        const int64_t pbase = (static_cast<int64_t>(b) * a.Hkv + hk) * a.pooled_rows * D;
-        const bf16_bits* kp = l == 0 ? a.k + b * a.ks0 + hk * a.ks1 + static_cast<int64_t>(jr) * a.ks2
-                                     : a.kp + pbase + (level_row_offset(a.N, l) + jr) * D;
-        const bf16_bits* vp = l == 0 ? a.v + b * a.vs0 + hk * a.vs1 + static_cast<int64_t>(jr) * a.vs2
-                                     : a.vp + pbase + (level_row_offset(a.N, l) + jr) * D;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            kf[kk] = *reinterpret_cast<const bf16x8*>(kp + kk * 16 + hi * 8);
-            vf[kk] = *reinterpret_cast<const bf16x8*>(vp + kk * 16 + hi * 8);
-        }
-    }
-    f32x16 dka[DB], dva[DB];
-#pragma unroll
-    for (int i = 0; i < DB; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            dka[i][e] = 0.f;
-            dva[i][e] = 0.f;
-        }
-
-    // items: (listed row, 64-query chunk); item it+1's tiles load while item it computes
-    uint32_t lx[2][4];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            lx[u][i] = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Xs[u][i][0]));
-    constexpr uint32_t kSetBytes = 4u * 64u * D * 2u;   // one buffer set (Q, Q^T, dO, dO^T)
-    const uint32_t q_rows = row_read_base<D>(lx[0][0], lane, 32 * qh);
-    const uint32_t g_rows = row_read_base<D>(lx[0][2], lane, 32 * qh);
-    uint32_t qt_base[DB], gt_base[DB];
-#pragma unroll
-    for (int dblk = 0; dblk < DB; ++dblk) {
-        qt_base[dblk] = tr_read_base<D>(lx[0][1], lane, dblk, 32 * qh);
-        gt_base[dblk] = tr_read_base<D>(lx[0][3], lane, dblk, 32 * qh);
-    }
-    // direct loads of a chunk: 64 consecutive rows of Q (and dO) of one head, each staged in
-    // the row layout and the transposed-read layout. Instruction mi of this wave covers rows
-    // (wave * IPW + mi) * RPI + rr; its lane offsets are loop invariants, so an instruction
-    // costs one M0 write.
-    constexpr int IPW = LY::INSTR / NW;
-    uint32_t qo_r[IPW], qo_t[IPW], go_r[IPW], go_t[IPW];
-    {
-        const int rr = lane / LY::CH;
-        const int p = lane % LY::CH;
-        const uint32_t qs2b = static_cast<uint32_t>(a.qs2) * 2u;
-        const uint32_t os2b = static_cast<uint32_t>(a.os2) * 2u;
-#pragma unroll
-        for (int mi = 0; mi < IPW; ++mi) {
-            const int trow = (wave * IPW + mi) * LY::RPI + rr;   // tile row of this lane
-            const uint32_t rowq = static_cast<uint32_t>(mi * LY::RPI + rr) * qs2b;
-            const uint32_t rowg = static_cast<uint32_t>(mi * LY::RPI + rr) * os2b;
-            qo_r[mi] = rowq + static_cast<uint32_t>((p ^ LY::fk(trow)) << 4);
-            qo_t[mi] = rowq + static_cast<uint32_t>((p ^ LY::fv(trow)) << 4);
-            go_r[mi] = rowg + static_cast<uint32_t>((p ^ LY::fk(trow)) << 4);
-            go_t[mi] = rowg + static_cast<uint32_t>((p ^ LY::fv(trow)) << 4);
-        }
-    }
-    // items (listed row, 64-query chunk): item it is list entry it >> csh, chunk it & cmask
-    const uint32_t ls_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Ls[0][0]));
-    const uint32_t ds_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Ds[0][0]));
+    // items: (listed row, 64-query chunk); item it is entry it >> csh, chunk it & csh
     const int csh = a.BQ == 128 ? 1 : 0;
     const int items = count << csh;
     auto item_entry = [&](int it) { return __builtin_amdgcn_readfirstlane(ent[it >> csh]); };
-    auto item_head = [&](int en) { return hk * g + (en >> 20); };
     auto item_q0 = [&](int en, int it) { return ((en >> 8) & 0xfff) * a.BQ + ((it & csh) << 6); };
-    auto issue = [&](int it, int buf) {
-        const int en = item_entry(it);
-        const int h = item_head(en);
-        const int q0 = item_q0(en, it);
-        const int64_t r0 = static_cast<int64_t>(wave * IPW * LY::RPI + q0);
-        const char* qsrc = reinterpret_cast<const char*>(a.q + b * a.qs0 + h * a.qs1 + r0 * a.qs2);
-        const char* gsrc = reinterpret_cast<const char*>(a.dout + b * a.os0 + h * a.os1 + r0 * a.os2);
-        const uint32_t l0 = lx[0][0] + (buf ? kSetBytes : 0u) + static_cast<uint32_t>(wave * IPW) * 1024u;
+
+    // ---- direct loads of a chunk: Q's 64 rows by waves 0..3, dO's by waves 4..7 (IPW
+    //      instructions each); lse2 and D by wave 0 (16 lanes x 16 bytes) ----
+    constexpr int IPW = LY::INSTR / 4;
+    const bool ld_q = wave < 4;
+    const int m0 = (wave & 3) * IPW;            // the wave's first instruction of its tensor
+    const uint32_t stride = static_cast<uint32_t>(ld_q ? a.qs2 : a.os2) * 2u;
+    uint32_t lo[IPW];
+    {
+        const int rr = lane / LY::CH;
+        const int p = lane % LY::CH;
 #pragma unroll
         for (int mi = 0; mi < IPW; ++mi) {
-            const uint32_t lo = l0 + static_cast<uint32_t>(mi) * 1024u;
-            dma16(qsrc, qo_r[mi], lo);
-            dma16(qsrc, qo_t[mi], lo + 64u * D * 2u);
-            dma16(gsrc, go_r[mi], lo + 2u * 64u * D * 2u);
-            dma16(gsrc, go_t[mi], lo + 3u * 64u * D * 2u);
+            const int trow = (m0 + mi) * LY::RPI + rr;
+            lo[mi] = static_cast<uint32_t>(mi * LY::RPI + rr) * stride + static_cast<uint32_t>((p ^ LY::fq(trow)) << 4);
         }
-        // lse2 and D of the chunk's 64 queries: 16 lanes x 16 bytes each, also by direct load
-        // (no global load the compiler tracks may sit in the loop: its waits would also
-        // drain the tile loads in flight)
+    }
+    const uint32_t xs0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Xs[0][0][0]));
+    const uint32_t ls0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Ls[0][0]));
+    const uint32_t ds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Ds[0][0]));
+    auto issue = [&](int it, int set) {
+        const int en = item_entry(it);
+        const int h = hk * g + (en >> 20);
+        const int q0 = item_q0(en, it);
+        const int64_t r0 = static_cast<int64_t>(q0 + m0 * LY::RPI);
+        const char* src = ld_q ? reinterpret_cast<const char*>(a.q + b * a.qs0 + h * a.qs1 + r0 * a.qs2)
+                               : reinterpret_cast<const char*>(a.dout + b * a.os0 + h * a.os1 + r0 * a.os2);
+        const uint32_t l0 = xs0 + static_cast<uint32_t>(set) * 2u * kTileBytes + (ld_q ? 0u : kTileBytes) +
+                            static_cast<uint32_t>(m0) * 1024u;
+#pragma unroll
+        for (int mi = 0; mi < IPW; ++mi) dma16(src, lo[mi], l0 + static_cast<uint32_t>(mi) * 1024u);
         if (wave == 0 && lane < 16) {
             const int64_t r = (static_cast<int64_t>(b) * a.H + h) * a.N + q0;
-            dma16(a.lse2 + r, static_cast<uint32_t>(lane) * 16u, ls_lds + (buf ? 256u : 0u));
-            dma16(a.dd + r, static_cast<uint32_t>(lane) * 16u, ds_lds + (buf ? 256u : 0u));
+            dma16(a.lse2 + r, static_cast<uint32_t>(lane) * 16u, ls0 + static_cast<uint32_t>(set) * 256u);
+            dma16(a.dd + r, static_cast<uint32_t>(lane) * 16u, ds0 + static_cast<uint32_t>(set) * 256u);
         }
     };
     if (items > 0) issue(0, 0);
-
-    for (int it = 0; it < items; ++it) {
-        const int buf = it & 1;
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);   // this item's tiles
-        __syncthreads();   // publish them; every wave is done with the other buffer set
-        if (it + 1 < items) issue(it + 1, buf ^ 1);
-        const int en = item_entry(it);
-        const int q0 = item_q0(en, it);
-        const int bits = en & 0xff;
-        // query q sees this lane's key iff q >= kmin (an unlisted or invalid key: never)
-        const bool sub_ok = key_ok && ((bits >> ksub) & 1);
-        const int kmin = sub_ok ? (a.causal ? klast : INT_MIN) : INT_MAX;
-        const uint32_t boff = buf ? kSetBytes : 0u;
-
-        // every operand row of S and dP first (one wave per SIMD: nothing else hides the
-        // LDS latency), then the two MFMA chains
-        bf16x8 qa[KK], ga[KK];
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            qa[kk] = read_row(q_rows + boff, kk);
-            ga[kk] = read_row(g_rows + boff, kk);
-        }
-        __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the products
-        f32x16 s, dp;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            s[e] = 0.f;
-            dp[e] = 0.f;
-        }
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], kf[kk], s, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[kk], vf[kk], dp, 0, 0, 0);
-        }
-        // register e holds chunk query 32 qh + 16 (e / 8) + 8 hi + e % 8, this lane's key.
-        // Fragment j (registers 8j..8j+7) is finished, then its 2 * DB products issue and run
-        // while the next fragment's P and dS are computed.
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int qi0 = 32 * qh + 16 * j + 8 * hi;   // 8 consecutive chunk queries
-            const f32x4 la = *reinterpret_cast<const f32x4*>(&Ls[buf][qi0]);
-            const f32x4 lb2 = *reinterpret_cast<const f32x4*>(&Ls[buf][qi0 + 4]);
-            const f32x4 da = *reinterpret_cast<const f32x4*>(&Ds[buf][qi0]);
-            const f32x4 db = *reinterpret_cast<const f32x4*>(&Ds[buf][qi0 + 4]);
-            bf16x8 gtr[DB], qtr[DB];
-#pragma unroll
-            for (int dblk = 0; dblk < DB; ++dblk) {
-                gtr[dblk] = read_tr<D>(gt_base[dblk] + boff, j);
-                qtr[dblk] = read_tr<D>(qt_base[dblk] + boff, j);
-            }
-            uint32_t pk[4], dsk[4];
-#pragma unroll
-            for (int u = 0; u < 8; u += 2) {
-                float pp[2], ds2[2];
-#pragma unroll
-                for (int w = 0; w < 2; ++w) {
-                    const int e = 8 * j + u + w;
-                    const int x = u + w;
-                    const float lq = static_cast<float>(l) - (x < 4 ? la[x] : lb2[x - 4]);   // l - lse2
-                    const float dq = x < 4 ? da[x] : db[x - 4];
-                    const bool vis = q0 + qi0 + x >= kmin;
-                    const float p = fast_exp2(vis ? fmaf(s[e], a.c, lq) : -INFINITY);
-                    pp[w] = p;
-                    ds2[w] = p * (dp[e] - dq);
-                }
-                pk[u >> 1] = pack_bf16x2(pp[0], pp[1]);
-                dsk[u >> 1] = pack_bf16x2(ds2[0], ds2[1]);
-            }
-            const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
-            const bf16x8 df = __builtin_bit_cast(bf16x8, u32x4{dsk[0], dsk[1], dsk[2], dsk[3]});
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int dblk = 0; dblk < DB; ++dblk) {
-                dva[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gtr[dblk], pf, dva[dblk], 0, 0, 0);
-                dka[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qtr[dblk], df, dka[dblk], 0, 0, 0);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-
-    // ---- add the two query halves (waves 2, 3 hand theirs to waves 0, 1), then write ----
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    float* red = reinterpret_cast<float*>(&Xs[0][0][0]);   // [kh][2][DB][16][64] floats
-    if (qh == 1) {
+
+    // per-lane LDS read addresses in set 0 (other sets: + set * 2 * kTileBytes)
+    auto fq_row_base = [&](uint32_t lds) {   // A-operand rows 32 qh + sigma(l % 32)
+        const int r = 32 * qh + sigma(l32);
+        return row_read_base_fq_impl(lds, r, hi, LY::fq(r), D * 2);
+    };
+    // transposed reads of rows 32 qh + 8 (grp >> 1) + (jj >> 2) + 4 s (s = 0, 1: the two
+    // halves of a fragment have different fq swizzles); fragment j adds 16 rows, which leaves
+    // fq unchanged
+    auto fq_tr_base = [&](uint32_t lds, int dblk, int s) {
+        const int grp = lane >> 4;
+        const int jj = lane & 15;
+        const int d = dblk * 32 + 16 * (grp & 1) + 4 * (jj & 3);
+        const int c = d >> 3;
+        const int half = d & 7;
+        const int rA = 32 * qh + 8 * (grp >> 1) + (jj >> 2) + 4 * s;
+        return lds + static_cast<uint32_t>((rA * D + ((c ^ LY::fq(rA)) << 3) + half) * 2);
+    };
+    auto read_tr_fq = [&](uint32_t b0, uint32_t b1, int j) {
+        union {
+            bf16x8 v;
+            v4i16 h[2];
+        } x;
+        x.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)(b0 + static_cast<uint32_t>(j * 16 * D * 2)));
+        x.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)(b1 + static_cast<uint32_t>(j * 16 * D * 2)));
+        return x.v;
+    };
+    const uint32_t xch0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Xch[0][0][0][0][0]));
+
+    if (wave < 4) {
+        // ================= producer =================
+        const int jrow = 64 * m + 32 * kh + l32;          // pooled row of level l
+        const bool in_level = jrow < (a.N >> l);
+        const int jr = in_level ? jrow : 0;
+        const int klast = ((jr + 1) << l) - 1;             // last token the key stands for
+        const bool key_ok = in_level && klast < a.Nv;
+        const int ksub = (32 * kh + l32) >> sh;            // its block inside the tile
+        bf16x8 kf[KK], vf[KK];
+        {
+            const int64_t pbase = (static_cast<int64_t>(b) * a.Hkv + hk) * a.pooled_rows * D;
+            const bf16_bits* kp = l == 0 ? a.k + b * a.ks0 + hk * a.ks1 + static_cast<int64_t>(jr) * a.ks2
+                                         : a.kp + pbase + (level_row_offset(a.N, l) + jr) * D;
+            const bf16_bits* vp = l == 0 ? a.v + b * a.vs0 + hk * a.vs1 + static_cast<int64_t>(jr) * a.vs2
+                                         : a.vp + pbase + (level_row_offset(a.N, l) + jr) * D;
 #pragma unroll
-        for (int dblk = 0; dblk < DB; ++dblk)
+            for (int kk = 0; kk < KK; ++kk) {
+                kf[kk] = *reinterpret_cast<const bf16x8*>(kp + kk * 16 + hi * 8);
+                vf[kk] = *reinterpret_cast<const bf16x8*>(vp + kk * 16 + hi * 8);
+            }
+        }
+        const uint32_t q_rows = fq_row_base(xs0);
+        const uint32_t g_rows = fq_row_base(xs0 + kTileBytes);
+        const uint32_t xw = xch0 + static_cast<uint32_t>(pw) * (2u * 2u * 64u * 16u) + static_cast<uint32_t>(lane) * 16u;
+        int set = 0;
+        for (int k = 0; k <= items; ++k) {
+            if (k + 1 < items) issue(k + 1, set == 2 ? 0 : set + 1);
+            if (k < items) {
+                const int en = item_entry(k);
+                const int q0 = item_q0(en, k);
+                const int bits = en & 0xff;
+                // query q sees this lane's key iff q >= kmin (an unlisted or invalid key: never)
+                const bool sub_ok = key_ok && ((bits >> ksub) & 1);
+                const int kmin = sub_ok ? (a.causal ? klast : INT_MIN) : INT_MAX;
+                const uint32_t soff = static_cast<uint32_t>(set) * 2u * kTileBytes;
+                bf16x8 qa[KK], ga[KK];
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) {
+                    qa[kk] = read_row(q_rows + soff, kk);
+                    ga[kk] = read_row(g_rows + soff, kk);
+                }
+                __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the products
+                f32x16 s, dp;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    s[e] = 0.f;
+                    dp[e] = 0.f;
+                }
+#pragma unroll
+                for (int kk = 0; kk < KK; ++kk) {
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[kk], kf[kk], s, 0, 0, 0);
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga[kk], vf[kk], dp, 0, 0, 0);
+                }
+                // register e holds chunk query 32 qh + 16 (e / 8) + 8 hi + e % 8, this lane's key
+                const uint32_t xb = xw + static_cast<uint32_t>(k & 1) * (4u * 2u * 2u * 64u * 16u);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const int qi0 = 32 * qh + 16 * j + 8 * hi;   // 8 consecutive chunk queries
+                    const f32x4 la = *reinterpret_cast<const f32x4*>(&Ls[set][qi0]);
+                    const f32x4 lb2 = *reinterpret_cast<const f32x4*>(&Ls[set][qi0 + 4]);
+                    const f32x4 da = *reinterpret_cast<const f32x4*>(&Ds[set][qi0]);
+                    const f32x4 db = *reinterpret_cast<const f32x4*>(&Ds[set][qi0 + 4]);
+                    u32x4 pk, dk4;
+#pragma unroll
+                    for (int u = 0; u < 8; u += 2) {
+                        float pp[2], ds2[2];
+#pragma unroll
+                        for (int w = 0; w < 2; ++w) {
+                            const int e = 8 * j + u + w;
+                            const int x = u + w;
+                            const float lq = static_cast<float>(l) - (x < 4 ? la[x] : lb2[x - 4]);
+                            const float dq = x < 4 ? da[x] : db[x - 4];
+                            const bool vis = q0 + qi0 + x >= kmin;
+                            const float p = fast_exp2(vis ? fmaf(s[e], a.c, lq) : -INFINITY);
+                            pp[w] = p;
+                            ds2[w] = p * (dp[e] - dq);
+                        }
+                        pk[u >> 1] = pack_bf16x2(pp[0], pp[1]);
+                        dk4[u >> 1] = pack_bf16x2(ds2[0], ds2[1]);
+                    }
+                    *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(xb + static_cast<uint32_t>(j) * (2u * 64u * 16u)) = pk;
+                    *(__attribute__((address_space(3))) u32x4*)(uintptr_t)(xb + static_cast<uint32_t>(j) * (2u * 64u * 16u) + 64u * 16u) = dk4;
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            __syncthreads();
+            set = set == 2 ? 0 : set + 1;
+        }
+        __syncthreads();   // the consumers' reduction (two barriers, as on their side)
+        __syncthreads();
+    } else {
+        // ================= consumer =================
+        f32x16 dka[DB], dva[DB];
+#pragma unroll
+        for (int i = 0; i < DB; ++i)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                red[(((kh * 2 + 0) * DB + dblk) * 16 + e) * 64 + lane] = dka[dblk][e];
-                red[(((kh * 2 + 1) * DB + dblk) * 16 + e) * 64 + lane] = dva[dblk][e];
+                dka[i][e] = 0.f;
+                dva[i][e] = 0.f;
             }
-    }
-    __syncthreads();
-    if (qh == 0 && in_level) {
-        const int64_t rows15 = static_cast<int64_t>(a.N) + a.pooled_rows;
-        const int64_t grow = (static_cast<int64_t>(b) * a.Hkv + hk) * rows15 +
-                             (l == 0 ? 0 : a.N + level_row_offset(a.N, l)) + jrow;
-        float* gkp = a.gk + grow * D;
-        float* gvp = a.gv + grow * D;
+        uint32_t qt_base[2][DB], gt_base[2][DB];
 #pragma unroll
-        for (int dblk = 0; dblk < DB; ++dblk)
+        for (int sh2 = 0; sh2 < 2; ++sh2)
 #pragma unroll
-            for (int gg = 0; gg < 4; ++gg) {
-                f32x4 wk, wv;
+            for (int dblk = 0; dblk < DB; ++dblk) {
+                qt_base[sh2][dblk] = fq_tr_base(xs0, dblk, sh2);
+                gt_base[sh2][dblk] = fq_tr_base(xs0 + kTileBytes, dblk, sh2);
+            }
+        const uint32_t xr = xch0 + static_cast<uint32_t>(pw) * (2u * 2u * 64u * 16u) + static_cast<uint32_t>(lane) * 16u;
+        int set = 0;        // set of item k
+        int pset = 2;       // set of item k - 1
+        for (int k = 0; k <= items; ++k) {
+            if (k + 1 < items) issue(k + 1, set == 2 ? 0 : set + 1);
+            if (k >= 1) {
+                const uint32_t soff = static_cast<uint32_t>(pset) * 2u * kTileBytes;
+                const uint32_t xb = xr + static_cast<uint32_t>((k - 1) & 1) * (4u * 2u * 2u * 64u * 16u);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int e = 4 * gg + u;
-                    wk[u] = (dka[dblk][e] + red[(((kh * 2 + 0) * DB + dblk) * 16 + e) * 64 + lane]) * a.scale;
-                    wv[u] = dva[dblk][e] + red[(((kh * 2 + 1) * DB + dblk) * 16 + e) * 64 + lane];
+                for (int j = 0; j < 2; ++j) {
+                    const u32x4 pk = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)(xb + static_cast<uint32_t>(j) * (2u * 64u * 16u));
+                    const u32x4 dk4 = *(const __attribute__((address_space(3))) u32x4*)(uintptr_t)(xb + static_cast<uint32_t>(j) * (2u * 64u * 16u) + 64u * 16u);
+                    bf16x8 gtr[DB], qtr[DB];
+#pragma unroll
+                    for (int dblk = 0; dblk < DB; ++dblk) {
+                        gtr[dblk] = read_tr_fq(gt_base[0][dblk] + soff, gt_base[1][dblk] + soff, j);
+                        qtr[dblk] = read_tr_fq(qt_base[0][dblk] + soff, qt_base[1][dblk] + soff, j);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    const bf16x8 pf = __builtin_bit_cast(bf16x8, pk);
+                    const bf16x8 df = __builtin_bit_cast(bf16x8, dk4);
+#pragma unroll
+                    for (int dblk = 0; dblk < DB; ++dblk) {
+                        dva[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gtr[dblk], pf, dva[dblk], 0, 0, 0);
+                        dka[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qtr[dblk], df, dka[dblk], 0, 0, 0);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                *reinterpret_cast<f32x4*>(gkp + dblk * 32 + gg * 8 + hi * 4) = wk;
-                *reinterpret_cast<f32x4*>(gvp + dblk * 32 + gg * 8 + hi * 4) = wv;
             }
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            __syncthreads();
+            pset = set;
+            set = set == 2 ? 0 : set + 1;
+        }
+
+        // ---- add the two query halves (consumers 2, 3 hand theirs to 0, 1), then write ----
+        float* red = reinterpret_cast<float*>(&Xs[0][0][0]);   // [kh][2][DB][16][64] floats
+        __syncthreads();
+        if (qh == 1) {
+#pragma unroll
+            for (int dblk = 0; dblk < DB; ++dblk)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    red[(((kh * 2 + 0) * DB + dblk) * 16 + e) * 64 + lane] = dka[dblk][e];
+                    red[(((kh * 2 + 1) * DB + dblk) * 16 + e) * 64 + lane] = dva[dblk][e];
+                }
+        }
+        __syncthreads();
+        const int jrow = 64 * m + 32 * kh + l32;
+        if (qh == 0 && jrow < (a.N >> l)) {
+            const int64_t rows15 = static_cast<int64_t>(a.N) + a.pooled_rows;
+            const int64_t grow = (static_cast<int64_t>(b) * a.Hkv + hk) * rows15 +
+                                 (l == 0 ? 0 : a.N + level_row_offset(a.N, l)) + jrow;
+            float* gkp = a.gk + grow * D;
+            float* gvp = a.gv + grow * D;
+#pragma unroll
+            for (int dblk = 0; dblk < DB; ++dblk)
+#pragma unroll
+                for (int gg = 0; gg < 4; ++gg) {
+                    f32x4 wk, wv;
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int e = 4 * gg + u;
+                        wk[u] = (dka[dblk][e] + red[(((kh * 2 + 0) * DB + dblk) * 16 + e) * 64 + lane]) * a.scale;
+                        wv[u] = dva[dblk][e] + red[(((kh * 2 + 1) * DB + dblk) * 16 + e) * 64 + lane];
+                    }
+                    *reinterpret_cast<f32x4*>(gkp + dblk * 32 + gg * 8 + hi * 4) = wk;
+                    *reinterpret_cast<f32x4*>(gvp + dblk * 32 + gg * 8 + hi * 4) = wv;
+                }
+        }
     }
-    (void)nrows;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -697,7 +748,7 @@ hipError_t launch_d(const Shape& s, const BwdArgs& a, hipStream_t st) {
     const int tiles = s.B * s.Hkv * tiles_per_bh;
     const int nt = (tiles + 7) / 8;
     const size_t edyn = static_cast<size_t>(s.H / s.Hkv) * s.NQB * sizeof(int);
-    hipLaunchKernelGGL(k_bwd_dkv<D>, dim3(8 * nt), dim3(256), edyn, st, a, tiles, tiles_per_bh,
+    hipLaunchKernelGGL(k_bwd_dkv<D>, dim3(8 * nt), dim3(512), edyn, st, a, tiles, tiles_per_bh,
                        tl[0], tl[0] + tl[1], tl[0] + tl[1] + tl[2]);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -6,7 +6,8 @@
 // A 64-row tile of D bf16 per row sits in LDS row-major with its 16-byte chunks XOR-swizzled
 // per row: fk for tiles read by rows (ds_read_b128 of one chunk of one row per lane), fv for
 // tiles read transposed (ds_read_b64_tr_b16: a 16-lane group reads 4 rows x 16 columns and
-// receives them transposed). Both keep their reads free of bank conflicts.
+// receives them transposed), fq for tiles read both ways. All keep their reads free of bank
+// conflicts.
 #pragma once
 
 #include <type_traits>
@@ -31,6 +32,14 @@ struct Lay {
     static constexpr int INSTR = 64 * D * 2 / 1024;  // instructions per 64-row tile
     static __device__ __forceinline__ int fk(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
     static __device__ __forceinline__ int fv(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+    // One layout for tiles read both ways. Row reads: the 16 rows a 16-lane group reads at
+    // one chunk land on 16 distinct 16-byte bank groups (fq is a bijection of r mod 16 within
+    // each 256-byte bank sweep). Transposed reads: the 4 consecutive rows a 32-lane half
+    // reads over 4 aligned chunks differ in fq's bits 2..3, so the 16 (row, chunk) pairs land
+    // on 16 distinct bank groups.
+    static __device__ __forceinline__ int fq(int r) {
+        return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+    }
 };
 
 // The tile row that MFMA A-operand row r reads: bits 2 and 3 of r swapped. With it, the C
