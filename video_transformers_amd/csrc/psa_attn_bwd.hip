@@ -120,7 +120,14 @@ __global__ void __launch_bounds__(256) k_bwd_rowdot(BwdArgs a) {
 // consecutive with byte stride `stride`). Each of the workgroup's NW waves issues
 // IPW = INSTR / NW instructions; instruction m covers tile rows [m*RPI, (m+1)*RPI).
 // ---------------------------------------------------------------------------------------
-template <int D, int NW, bool FV, typename RunBase>
+// tile layouts of psa_bf16_tile.h
+enum { kLayK = 0, kLayV = 1, kLayQ = 2 };
+template <int D, int LAY>
+__device__ __forceinline__ int swz(int r) {
+    return LAY == kLayK ? Lay<D>::fk(r) : LAY == kLayV ? Lay<D>::fv(r) : Lay<D>::fq(r);
+}
+
+template <int D, int NW, int LAY, typename RunBase>
 __device__ __forceinline__ void load_tile(uint32_t lds, int wave, int lane, uint32_t stride,
                                           RunBase&& run_base) {
     using LY = Lay<D>;
@@ -131,49 +138,50 @@ __device__ __forceinline__ void load_tile(uint32_t lds, int wave, int lane, uint
     for (int mi = 0; mi < IPW; ++mi) {
         const int m = wave * IPW + mi;
         const int trow = m * LY::RPI + rr;
-        const int f = FV ? LY::fv(trow) : LY::fk(trow);
+        const int f = swz<D, LAY>(trow);
         const uint32_t voff = rr * stride + static_cast<uint32_t>((p ^ f) << 4);
         dma16(run_base(m * LY::RPI), voff, lds + static_cast<uint32_t>(m) * 1024u);
     }
 }
 
-// Per-lane LDS byte address of the A-operand row reads (fk tile, rows row0 + sigma(l % 32)):
-// the address of k-step kk is the result XOR 32 kk.
-template <int D>
+// Per-lane LDS byte address of the A-operand row reads (rows row0 + sigma(l % 32)) of a tile
+// in layout LAY: the address of k-step kk is the result XOR 32 kk.
+template <int D, int LAY>
 __device__ __forceinline__ uint32_t row_read_base(uint32_t lds, int lane, int row0) {
     const int r = row0 + sigma(lane & 31);
     const int hi = lane >> 5;
-    const int f = Lay<D>::fk(r);
+    const int f = swz<D, LAY>(r);
     return lds + static_cast<uint32_t>(r * D * 2 + 16 * ((hi ^ f) & 1) + 16 * (f & ~1));
 }
 
-// Per-lane LDS byte address of the transposed A-operand reads (fv tile) of 32-wide d block
-// dblk, for contraction rows row0 + 16 j + ...: add j * 16 * D * 2; the second half of the
-// fragment is 4 rows further.
-template <int D>
-__device__ __forceinline__ uint32_t tr_read_base(uint32_t lds, int lane, int dblk, int row0) {
+// Per-lane LDS byte address of the transposed A-operand reads of 32-wide d block dblk, for
+// contraction rows row0 + 8 (grp / 2) + jj / 4 + 4 s (s = 0, 1: the two halves of a
+// fragment), in layout LAY. Fragment j adds 16 rows (j * 16 * D * 2 bytes), which leaves
+// every layout's swizzle unchanged; so does a row0 that is a multiple of 16.
+template <int D, int LAY>
+__device__ __forceinline__ uint32_t tr_read_base(uint32_t lds, int lane, int dblk, int row0, int s) {
     const int grp = lane >> 4;
     const int jj = lane & 15;
     const int d = dblk * 32 + 16 * (grp & 1) + 4 * (jj & 3);
     const int c = d >> 3;
     const int half = d & 7;
-    const int rA = 8 * (grp >> 1) + (jj >> 2);
-    return lds + static_cast<uint32_t>(((row0 + rA) * D + ((c ^ Lay<D>::fv(rA)) << 3) + half) * 2);
+    const int r = row0 + 8 * (grp >> 1) + (jj >> 2) + 4 * s;
+    return lds + static_cast<uint32_t>((r * D + ((c ^ swz<D, LAY>(r)) << 3) + half) * 2);
 }
 
 __device__ __forceinline__ bf16x8 read_row(uint32_t base, int kk) {
     return *(const lds_bf16x8*)(uintptr_t)(base ^ static_cast<uint32_t>(32 * kk));
 }
 
+// fragment j of a transposed read: the halves at bases b0 (rows + 0) and b1 (rows + 4)
 template <int D>
-__device__ __forceinline__ bf16x8 read_tr(uint32_t base, int j) {
-    const uint32_t pa = base + static_cast<uint32_t>(j * 16 * D * 2);
+__device__ __forceinline__ bf16x8 read_tr(uint32_t b0, uint32_t b1, int j) {
     union {
         bf16x8 v;
         v4i16 h[2];
     } x;
-    x.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)pa);
-    x.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)(pa + 4 * D * 2));
+    x.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)(b0 + static_cast<uint32_t>(j * 16 * D * 2)));
+    x.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)(b1 + static_cast<uint32_t>(j * 16 * D * 2)));
     return x.v;
 }
 
@@ -186,8 +194,7 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_bwd_dq(BwdArgs a, int total_rows)
     constexpr int NW = BQ / 32;
     constexpr int KK = D / 16;
     constexpr int DB = D / 32;
-    __shared__ __attribute__((aligned(1024))) bf16_bits Kr[64 * D];   // K rows (fk)
-    __shared__ __attribute__((aligned(1024))) bf16_bits Kt[64 * D];   // K, transposed reads (fv)
+    __shared__ __attribute__((aligned(1024))) bf16_bits Kr[64 * D];   // K, read both ways (fq)
     __shared__ __attribute__((aligned(1024))) bf16_bits Vr[64 * D];   // V rows (fk)
     extern __shared__ int cols[];
 
@@ -239,13 +246,14 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_bwd_dq(BwdArgs a, int total_rows)
     const char* kpl = reinterpret_cast<const char*>(a.kp + pbase);
     const char* vpl = reinterpret_cast<const char*>(a.vp + pbase);
     const uint32_t lds_kr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Kr[0]));
-    const uint32_t lds_kt = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Kt[0]));
     const uint32_t lds_vr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Vr[0]));
-    const uint32_t kr_base = row_read_base<D>(lds_kr, lane, 0);
-    const uint32_t vr_base = row_read_base<D>(lds_vr, lane, 0);
-    uint32_t kt_base[DB];
+    const uint32_t kr_base = row_read_base<D, kLayQ>(lds_kr, lane, 0);   // + 32 rows: fq unchanged
+    const uint32_t vr_base = row_read_base<D, kLayK>(lds_vr, lane, 0);
+    uint32_t kt_base[2][DB];
 #pragma unroll
-    for (int dblk = 0; dblk < DB; ++dblk) kt_base[dblk] = tr_read_base<D>(lds_kt, lane, dblk, 0);
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int dblk = 0; dblk < DB; ++dblk) kt_base[s2][dblk] = tr_read_base<D, kLayQ>(lds_kr, lane, dblk, 0, s2);
     __syncthreads();   // cols[] visible
 
     for (int l = 0; l < 4; ++l) {
@@ -265,9 +273,8 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_bwd_dq(BwdArgs a, int total_rows)
                 return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(cols[base + s]) * rs + (t & (rs - 1)));
             };
             __syncthreads();   // the previous tile's reads are done
-            load_tile<D, NW, false>(lds_kr, wave, lane, kst, [&](int t) { return kb0 + static_cast<uint64_t>(src_row(t)) * kst; });
-            load_tile<D, NW, true>(lds_kt, wave, lane, kst, [&](int t) { return kb0 + static_cast<uint64_t>(src_row(t)) * kst; });
-            load_tile<D, NW, false>(lds_vr, wave, lane, vst, [&](int t) { return vb0 + static_cast<uint64_t>(src_row(t)) * vst; });
+            load_tile<D, NW, kLayQ>(lds_kr, wave, lane, kst, [&](int t) { return kb0 + static_cast<uint64_t>(src_row(t)) * kst; });
+            load_tile<D, NW, kLayK>(lds_vr, wave, lane, vst, [&](int t) { return vb0 + static_cast<uint64_t>(src_row(t)) * vst; });
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             __syncthreads();
 
@@ -324,7 +331,7 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_bwd_dq(BwdArgs a, int total_rows)
                     const bf16x8 df = __builtin_bit_cast(bf16x8, u32x4{dsk[4 * j], dsk[4 * j + 1], dsk[4 * j + 2], dsk[4 * j + 3]});
                     bf16x8 kt[DB];
 #pragma unroll
-                    for (int dblk = 0; dblk < DB; ++dblk) kt[dblk] = read_tr<D>(kt_base[dblk] + hoff, j);
+                    for (int dblk = 0; dblk < DB; ++dblk) kt[dblk] = read_tr<D>(kt_base[0][dblk] + hoff, kt_base[1][dblk] + hoff, j);
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int dblk = 0; dblk < DB; ++dblk)
@@ -357,10 +364,6 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_bwd_dq(BwdArgs a, int total_rows)
 // fq layout serves the row reads and the transposed reads) in three buffer sets: the chunk
 // the producers work on, the one the consumers work on, and the next one loading.
 // ---------------------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t row_read_base_fq_impl(uint32_t lds, int r, int hi, int f, int rowbytes) {
-    return lds + static_cast<uint32_t>(r * rowbytes + 16 * ((hi ^ f) & 1) + 16 * (f & ~1));
-}
-
 template <int D>
 __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a, int total_tiles, int tiles_per_bh,
                                                    int t1, int t2, int t3) {
@@ -475,31 +478,8 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a, int total_tiles, 
     __syncthreads();
 
     // per-lane LDS read addresses in set 0 (other sets: + set * 2 * kTileBytes)
-    auto fq_row_base = [&](uint32_t lds) {   // A-operand rows 32 qh + sigma(l % 32)
-        const int r = 32 * qh + sigma(l32);
-        return row_read_base_fq_impl(lds, r, hi, LY::fq(r), D * 2);
-    };
-    // transposed reads of rows 32 qh + 8 (grp >> 1) + (jj >> 2) + 4 s (s = 0, 1: the two
-    // halves of a fragment have different fq swizzles); fragment j adds 16 rows, which leaves
-    // fq unchanged
-    auto fq_tr_base = [&](uint32_t lds, int dblk, int s) {
-        const int grp = lane >> 4;
-        const int jj = lane & 15;
-        const int d = dblk * 32 + 16 * (grp & 1) + 4 * (jj & 3);
-        const int c = d >> 3;
-        const int half = d & 7;
-        const int rA = 32 * qh + 8 * (grp >> 1) + (jj >> 2) + 4 * s;
-        return lds + static_cast<uint32_t>((rA * D + ((c ^ LY::fq(rA)) << 3) + half) * 2);
-    };
-    auto read_tr_fq = [&](uint32_t b0, uint32_t b1, int j) {
-        union {
-            bf16x8 v;
-            v4i16 h[2];
-        } x;
-        x.h[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)(b0 + static_cast<uint32_t>(j * 16 * D * 2)));
-        x.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)(b1 + static_cast<uint32_t>(j * 16 * D * 2)));
-        return x.v;
-    };
+    auto fq_row_base = [&](uint32_t lds) { return row_read_base<D, kLayQ>(lds, lane, 32 * qh); };
+    auto fq_tr_base = [&](uint32_t lds, int dblk, int s2) { return tr_read_base<D, kLayQ>(lds, lane, dblk, 32 * qh, s2); };
     const uint32_t xch0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Xch[0][0][0][0][0]));
 
     if (wave < 4) {
@@ -625,8 +605,8 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a, int total_tiles, 
                     bf16x8 gtr[DB], qtr[DB];
 #pragma unroll
                     for (int dblk = 0; dblk < DB; ++dblk) {
-                        gtr[dblk] = read_tr_fq(gt_base[0][dblk] + soff, gt_base[1][dblk] + soff, j);
-                        qtr[dblk] = read_tr_fq(qt_base[0][dblk] + soff, qt_base[1][dblk] + soff, j);
+                        gtr[dblk] = read_tr<D>(gt_base[0][dblk] + soff, gt_base[1][dblk] + soff, j);
+                        qtr[dblk] = read_tr<D>(qt_base[0][dblk] + soff, qt_base[1][dblk] + soff, j);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                     const bf16x8 pf = __builtin_bit_cast(bf16x8, pk);
