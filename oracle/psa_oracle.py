@@ -430,7 +430,13 @@ def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, level_map: np.nd
     blocks not listed in `qblocks` are left as NaN.
     """
     sc = p.scale if scale is None else scale
-    lk, lvv = pyramid(k), pyramid(v)
+    return _attention_from_levels(q, pyramid(k), pyramid(v), level_map, p, sc, qblocks)
+
+
+def _attention_from_levels(q: np.ndarray, lk: Dict[int, np.ndarray], lvv: Dict[int, np.ndarray],
+                           level_map: np.ndarray, p: Problem, sc: float,
+                           qblocks: Optional[Iterable[int]] = None):
+    """The body of attention_head on prepared key/value levels (logit scale sc)."""
     n, d = q.shape
     o = np.full((n, d), np.nan)
     lse = np.full((n,), np.nan)
@@ -460,6 +466,60 @@ def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, level_map: np.nd
         o[qi[pad]] = 0.0
         lse[qi[pad]] = -np.inf
     return o, lse
+
+
+# ----------------------------------------------------------------------------------------
+# 5b. FP8 (e4m3) operands for the QK^T product
+# ----------------------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_round(x) -> np.ndarray:
+    """Nearest e4m3 value (OCP FP8 E4M3: 1 sign, 4 exponent bits with bias 7, 3 mantissa
+    bits, subnormals down to 2^-9, largest finite 448), ties to even. |x| must not exceed
+    464, the midpoint above 448 (which still rounds to 448). Written from the format: in the
+    binade [2^E, 2^(E+1)), E >= -6, the spacing is 2^(E-3); below 2^-6 it is 2^-9."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    if np.any(a > 464.0):
+        raise ValueError("value beyond the e4m3 range")
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6.0)
+    q = 2.0 ** (e - 3.0)
+    return np.sign(x) * (np.round(a / q) * q)   # np.round: ties to even
+
+
+def fp8_scale(x) -> float:
+    """The per-(batch, head) scale of the fp8 reading: s = amax / 448 rounded to float32
+    (amax over the head's level-0 rows, exact for bf16 inputs); an all-zero head gets 1.
+    [ABS] and [NEWS] "Practical": the block-tile design suits FP16/FP8; the pages give no
+    recipe, this one is the plainest (one scale per head, shared by the pooled levels, whose
+    means never exceed the head's amax)."""
+    amax = float(np.max(np.abs(np.asarray(x, dtype=np.float64)))) if np.size(x) else 0.0
+    if amax == 0.0:
+        return 1.0
+    return float(np.float32(np.float32(amax) / np.float32(E4M3_MAX)))
+
+
+def fp8_quantize(x, s: float) -> np.ndarray:
+    """x / s rounded to e4m3 (values, not codes); the fp8 operand is this value, and it
+    stands for (value * s)."""
+    return e4m3_round(np.asarray(x, dtype=np.float64) / s)
+
+
+def attention_fp8qk_head(q8: np.ndarray, k8: np.ndarray, kp8_levels: Dict[int, np.ndarray],
+                         v: np.ndarray, s_q: float, s_k: float, level_map: np.ndarray, p: Problem,
+                         scale: Optional[float] = None, qblocks: Optional[Iterable[int]] = None):
+    """attention_head with the QK^T product taken on the fp8 operands: q8, k8 (level 0) and
+    kp8_levels[l] (the pooled levels, quantized with the same scale s_k) are e4m3 values;
+    logits are scale * s_q * s_k * (q8 . k8) + l ln 2 (exact), V and the rest as in
+    attention_head."""
+    sc = p.scale if scale is None else scale
+    lk = {0: k8}
+    lk.update(kp8_levels)
+    lvv = pyramid(v)
+    return _attention_from_levels(q8, lk, lvv, level_map, p, sc * s_q * s_k, qblocks)
 
 
 # ----------------------------------------------------------------------------------------

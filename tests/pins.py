@@ -489,3 +489,53 @@ def pin_bwd_constant_runs(level=2):
     runsum = lambda x: x.reshape(n // f, f, d).sum(axis=1)
     return max(np.abs(g0[0] - g1[0]).max(), np.abs(runsum(g0[1]) - runsum(g1[1])).max(),
                np.abs(runsum(g0[2]) - runsum(g1[2])).max())
+
+
+# ---------------------------------------------------------------------------------------
+# FP8 pins: the e4m3 rounding against torch's float8_e4m3fn conversion (a library routine;
+# every code, plus random values across the range, ties included); the per-head scale maps
+# the largest magnitude to 448 and keeps every quantized value in range, within half an e4m3
+# step; attention with fp8 QK^T equals plain attention on the dequantized operands.
+# ---------------------------------------------------------------------------------------
+def pin_e4m3_round():
+    codes = torch.arange(256, dtype=torch.int64).to(torch.uint8).view(torch.float8_e4m3fn)
+    vals = codes.to(torch.float64).numpy()
+    vals = vals[np.isfinite(vals)]
+    err = float(np.abs(oracle.e4m3_round(vals) - vals).max())
+    rng = np.random.default_rng(40)
+    x = np.concatenate([rng.uniform(-448, 448, 20000), rng.normal(0, 1e-2, 20000),
+                        rng.normal(0, 1.0, 20000),
+                        (vals[:-1] + np.diff(vals) / 2)[np.abs(vals[:-1]) < 440]])   # midpoints
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return max(err, float(np.abs(oracle.e4m3_round(x) - ref).max()))
+
+
+def pin_fp8_scale():
+    rng = np.random.default_rng(41)
+    x = rng.normal(0, 3.0, (256, 64))
+    s = oracle.fp8_scale(x)
+    q = oracle.fp8_quantize(x, s)
+    amax = np.abs(x).max()
+    step = 2.0 ** (np.maximum(np.floor(np.log2(np.maximum(np.abs(x / s), 1e-300))), -6) - 3)
+    bad = (np.abs(q).max() > 448) or abs(np.abs(q).max() - 448) > 1e-9 or \
+        np.any(np.abs(q - x / s) > step / 2 + 1e-12) or oracle.fp8_scale(np.zeros(4)) != 1.0
+    return float(bad) + abs(s * 448 - amax) / amax * 1e-3
+
+
+def pin_fp8qk_reduces_to_attention(causal=False):
+    n, d = 256, 16
+    p = oracle.Problem(seq_len=n, seq_valid=n - 8, head_dim=d, block_q=64, causal=causal)
+    rng = np.random.default_rng(42)
+    q8 = oracle.e4m3_round(rng.normal(0, 8, (n, d)))
+    k8 = oracle.e4m3_round(rng.normal(0, 8, (n, d)))
+    v = rng.normal(0, 1, (n, d))
+    s_q, s_k = 0.125, 0.0625
+    lm = rng.choice(np.array([0, 1, 2, 3, -1], dtype=np.int8), size=(p.n_qblocks, p.n_kblocks))
+    lm[:, 0] = 0
+    kp = {l: oracle.pool(k8, l) for l in (1, 2, 3)}
+    o8, l8 = oracle.attention_fp8qk_head(q8, k8, kp, v, s_q, s_k, lm, p)
+    o, lse = oracle.attention_head(q8 * s_q, k8 * s_k, v, lm, p)
+    both = np.isfinite(lse) & np.isfinite(l8)
+    same_inf = np.array_equal(np.isfinite(lse), np.isfinite(l8))
+    return max(np.nanmax(np.abs(o8 - o)), np.abs(np.where(both, l8 - lse, 0.0)).max(),
+               0.0 if same_inf else np.inf)

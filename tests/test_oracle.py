@@ -131,3 +131,16 @@ def test_pbwd_all_l0_is_dense_autograd(causal, nv):
 @pytest.mark.parametrize("level", [1, 2, 3])
 def test_pbwd_constant_runs(level):
     assert pins.pin_bwd_constant_runs(level) < 1e-10
+
+
+def test_pfp8_e4m3_round_is_torch_e4m3():
+    assert pins.pin_e4m3_round() == 0.0
+
+
+def test_pfp8_scale():
+    assert pins.pin_fp8_scale() < 1e-9
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_pfp8_qk_reduces_to_attention(causal):
+    assert pins.pin_fp8qk_reduces_to_attention(causal) < 1e-12

@@ -37,6 +37,8 @@ ALL_PINS = {
     "pbwd_l0": lambda: max(pins.pin_bwd_all_l0_autograd(False, 232),
                            pins.pin_bwd_all_l0_autograd(True, 256)),
     "pbwd_runs": lambda: max(pins.pin_bwd_constant_runs(l) for l in (1, 3)),
+    "pfp8": lambda: max(pins.pin_e4m3_round(), pins.pin_fp8_scale(),
+                        pins.pin_fp8qk_reduces_to_attention(True)),
 }
 
 
@@ -76,6 +78,12 @@ MUTANTS = [
     ("bwd_dq_uses_values", "dq[qi] = sc * (dz @ Kb)", "dq[qi] = sc * (dz @ Vb)"),
     ("bwd_gqa_overwrites", "dk[b, h // g] += bk", "dk[b, h // g] = bk"),
     ("bwd_pool_wrong_row", "dv += gv[l][tok >> l] * 2.0 ** -l", "dv += gv[l][np.minimum(tok >> (l - 1 if l else 0), tok.size - 1)] * 2.0 ** -l"),
+    ("e4m3_ties_away", "return np.sign(x) * (np.round(a / q) * q)",
+     "return np.sign(x) * (np.floor(a / q + 0.5) * q)"),
+    ("e4m3_no_subnormals", "e = np.maximum(e, -6.0)", "e = np.maximum(e, -60.0)"),
+    ("e4m3_four_mantissa_bits", "q = 2.0 ** (e - 3.0)", "q = 2.0 ** (e - 4.0)"),
+    ("fp8_scale_unscaled", "return _attention_from_levels(q8, lk, lvv, level_map, p, sc * s_q * s_k, qblocks)",
+     "return _attention_from_levels(q8, lk, lvv, level_map, p, sc * s_q, qblocks)"),
     ("index_descending", "sel = [kb for kb in range(nkb) if rows[r, kb] == l]",
      "sel = [kb for kb in reversed(range(nkb)) if rows[r, kb] == l]"),
 ]
