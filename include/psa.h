@@ -12,13 +12,16 @@
  *   psa_attn_fwd       - the level-weighted flash-style attention;
  *   psa_attn_bwd       - its backward (dq, dk, dv through every pyramid level).
  * plus psa_mask_assign and psa_build_index, the mask's and the attention's integer stages,
- * exported on their own.
+ * exported on their own, and psa_quantize_fp8 / psa_attn_fwd_fp8qk, the forward with its
+ * q . k products on e4m3 operands.
  *
  * Conventions shared by every call
  *  - Pointers named q, k, v, o, k_pooled, v_pooled, level_map, block_mass, block_sim, lse,
- *    row_ptr, col_idx, dev_err, dout, dq, dk, dv and ws are DEVICE pointers owned by the
+ *    row_ptr, col_idx, dev_err, dout, dq, dk, dv, x, x_pooled, q8, k8, k8_pooled, x8,
+ *    x8_pooled, scale, q_scale, k_scale and ws are DEVICE pointers owned by the
  *    caller; the library never allocates or frees device memory and keeps no state between
- *    calls. psa_problem and psa_mask_params are HOST pointers, read during the call only.
+ *    calls. psa_problem, psa_mask_params and x_stride are HOST pointers, read during the call
+ *    only.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). Work is only
  *    enqueued: no call synchronises except psa_check_status.
  *  - Arguments are checked on the host before anything is enqueued. A failed check returns a
@@ -209,6 +212,50 @@ int psa_attn_fwd_unpacked(const psa_problem* prob, float softmax_scale, const vo
                           const void* k, const void* v, const void* k_pooled,
                           const void* v_pooled, const int32_t* row_ptr, const int32_t* col_idx,
                           void* o, float* lse, void* stream);
+
+/*
+ * Per-head e4m3 quantization for the fp8 QK^T reading (PSA paper abstract and the news summary
+ * at euno.news, "Practical": the block-tile kernel suits FP16 and FP8 arithmetic; the pages fix
+ * no quantization recipe, this one keeps one scale per (batch, head)). For each of the
+ * batch*heads heads of x (bf16 [batch, heads, seq_len, head_dim], element strides x_stride[3]
+ * for the batch, head and token axes, head_dim contiguous):
+ *   amax  = max |x| over the head's seq_len rows;
+ *   scale[b*heads + h] = amax / 448 rounded to float32 (448 = the largest finite e4m3), or 1
+ *           when amax = 0;
+ *   x8    = the e4m3 (OCP FP8 E4M3, bias 7, with subnormals) code nearest to x / scale, ties to
+ *           even (the quotient is formed in float64, which makes the rounding exact), written
+ *           contiguous [batch, heads, seq_len, head_dim] bytes; the code stands for
+ *           value(code) * scale.
+ * With x_pooled (bf16 [batch, heads, 7*seq_len/8, head_dim], contiguous, the layout of
+ * psa_build_pyramid's outputs) the pooled rows are quantized with the same scale into
+ * x8_pooled (contiguous, same shape, bytes); x_pooled and x8_pooled are both null or both set.
+ * x must be finite. seq_len and head_dim multiples of 8, batch*heads <= 65535; x, x_pooled
+ * 16-byte aligned, x8, x8_pooled 8-byte aligned. All pointers are device pointers; x_stride
+ * is a host array.
+ */
+int psa_quantize_fp8(int32_t batch, int32_t heads, int32_t seq_len, int32_t head_dim,
+                     const void* x, const int64_t* x_stride, const void* x_pooled, uint8_t* x8,
+                     uint8_t* x8_pooled, float* scale, void* stream);
+
+/*
+ * psa_attn_fwd with the q . k products taken on e4m3 operands (paper abstract and news
+ * summary, "Practical": FP8 arithmetic on the block-tile kernel): q8 (scale q_scale), k8 and
+ * k8_pooled (one scale k_scale per KV head, shared by the pooled levels) as written by
+ * psa_quantize_fp8 from Q, K and psa_build_pyramid's k_pooled. The logits are
+ *   z_j = softmax_scale * q_scale[b,h] * k_scale[b,hkv] * (q8_i . k8bar_j) + l_j ln 2
+ * with the products exact and summed in float32 (v_mfma_f32_32x32x64_f8f6f4); everything else
+ * (levels, masking, softmax, P V in bf16, o, lse, the workspace and its status) is as in
+ * psa_attn_fwd. q8 [batch, heads_q, seq_len, 128], k8 [batch, heads_kv, seq_len, 128] and
+ * k8_pooled [batch, heads_kv, 7*seq_len/8, 128] are contiguous bytes (prob->q_stride and
+ * prob->k_stride are not used); q_scale [batch*heads_q], k_scale [batch*heads_kv] float32.
+ * v, v_pooled, o follow the problem (dtype PSA_BF16). head_dim 128 only; anything else returns
+ * PSA_ERR_UNSUPPORTED. Workspace: psa_attn_workspace_bytes.
+ */
+int psa_attn_fwd_fp8qk(const psa_problem* prob, float softmax_scale, const uint8_t* q8,
+                       const float* q_scale, const uint8_t* k8, const uint8_t* k8_pooled,
+                       const float* k_scale, const void* v, const void* v_pooled,
+                       const int8_t* level_map, void* o, float* lse, void* ws, size_t ws_bytes,
+                       void* stream);
 
 /* Device workspace psa_attn_bwd needs; 0 on a bad problem. */
 size_t psa_attn_bwd_workspace_bytes(const psa_problem* prob);

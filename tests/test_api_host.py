@@ -161,3 +161,48 @@ def test_attn_bwd_host_checks():
     # the key-side kernel's row list: at most 7680 (query head, query block) rows per KV head
     big = _prob(dtype=P.PSA_BF16, heads_q=32, heads_kv=1, seq_len=16384, seq_valid=16384)
     assert L.psa_attn_bwd(big.ref(), 0.0, *args13(), 1 << 40, None) == P.PSA_ERR_UNSUPPORTED
+
+
+def test_quantize_fp8_host_checks():
+    L = psa.lib()
+    d = ctypes.c_void_p(256)
+    st = lambda *v: (ctypes.c_int64 * 3)(*v)
+    ok = st(2 * 1024 * 128, 1024 * 128, 128)
+    q = lambda B=1, H=2, N=1024, D=128, x=d, s=ok, xp=None, x8=d, x8p=None, sc=d: \
+        L.psa_quantize_fp8(B, H, N, D, x, s, xp, x8, x8p, sc, None)
+    assert q(H=0) == P.PSA_ERR_INVALID_ARG
+    assert q(N=-8) == P.PSA_ERR_INVALID_ARG
+    assert q(N=1020) == P.PSA_ERR_UNSUPPORTED          # pooled rows need N % 8 == 0
+    assert q(D=100) == P.PSA_ERR_UNSUPPORTED
+    assert q(B=300, H=300) == P.PSA_ERR_UNSUPPORTED   # grid y holds the heads
+    assert q(s=st(0, 1024 * 128, 128)) == P.PSA_ERR_INVALID_ARG
+    assert q(s=st(2 * 1024 * 128, 1024 * 128, 64)) == P.PSA_ERR_INVALID_ARG   # row stride < d
+    assert q(x=None) == P.PSA_ERR_INVALID_ARG
+    assert q(sc=None) == P.PSA_ERR_INVALID_ARG
+    assert q(xp=d) == P.PSA_ERR_INVALID_ARG            # pooled input without pooled output
+    assert q(x8p=d) == P.PSA_ERR_INVALID_ARG
+    assert q(x=ctypes.c_void_p(264)) == P.PSA_ERR_INVALID_ARG   # 16-byte alignment
+    assert q(x8=ctypes.c_void_p(260)) == P.PSA_ERR_INVALID_ARG  # 8-byte alignment
+    assert q(sc=ctypes.c_void_p(258)) == P.PSA_ERR_INVALID_ARG
+
+
+def test_attn_fwd_fp8qk_host_checks():
+    L = psa.lib()
+    d = ctypes.c_void_p(256)
+    args11 = lambda **o: [o.get(n, d) for n in ("q8", "qs", "k8", "kp8", "ks", "v", "vp", "map",
+                                                 "o", "lse", "ws")]
+    q = torch.zeros(1, 2, 1024, 128)
+    p = psa.make_problem(q, q, q, block_q=64)
+    p.c.dtype = P.PSA_BF16
+    need = L.psa_attn_workspace_bytes(p.ref())
+    call = lambda prob, n=need, sc=0.0, **o: L.psa_attn_fwd_fp8qk(prob.ref(), sc, *args11(**o), n, None)
+    assert call(p, n=need - 1) == P.PSA_ERR_WORKSPACE
+    assert call(p, ws=None) == P.PSA_ERR_WORKSPACE
+    for name in ("q8", "qs", "k8", "kp8", "ks", "v", "vp", "map", "o"):
+        assert call(p, **{name: None}) == P.PSA_ERR_INVALID_ARG, name
+    assert call(p, k8=ctypes.c_void_p(264)) == P.PSA_ERR_INVALID_ARG
+    assert call(p, sc=float("inf")) == P.PSA_ERR_INVALID_ARG
+    p.c.dtype = P.PSA_F32
+    assert call(p) == P.PSA_ERR_UNSUPPORTED
+    p64 = _prob(dtype=P.PSA_BF16)                      # head_dim 64: no fp8 kernel
+    assert call(p64, n=1 << 30) == P.PSA_ERR_UNSUPPORTED

@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpsa.so")
 
 SOURCES = ["psa_api.cpp", "psa_pyramid.hip", "psa_index.hip", "psa_attn.hip", "psa_attn_bf16.hip",
-           "psa_attn_bwd.hip", "psa_mask.hip"]
+           "psa_attn_bwd.hip", "psa_mask.hip", "psa_fp8.hip"]
 HEADERS = ["psa_internal.h", "psa_device.h", "psa_attn_common.h", "psa_bf16_tile.h"]
 
 ARCH = "gfx950"

@@ -276,6 +276,56 @@ int psa_attn_fwd_unpacked(const psa_problem* prob, float softmax_scale, const vo
                         lse, false, stream);
 }
 
+int psa_quantize_fp8(int32_t batch, int32_t heads, int32_t seq_len, int32_t head_dim,
+                     const void* x, const int64_t* x_stride, const void* x_pooled, uint8_t* x8,
+                     uint8_t* x8_pooled, float* scale, void* stream) {
+    if (batch < 0 || heads <= 0 || seq_len < 0 || head_dim <= 0 || x_stride == nullptr)
+        return PSA_ERR_INVALID_ARG;
+    if (head_dim % 8 != 0 || seq_len % 8 != 0) return PSA_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(batch) * heads > 65535) return PSA_ERR_UNSUPPORTED;
+    for (int i = 0; i < 3; ++i)
+        if (x_stride[i] <= 0 || x_stride[i] % 8 != 0) return PSA_ERR_INVALID_ARG;
+    if (x_stride[2] < head_dim) return PSA_ERR_INVALID_ARG;
+    if (!x || !x8 || !scale || (x_pooled == nullptr) != (x8_pooled == nullptr)) return PSA_ERR_INVALID_ARG;
+    if (!aligned16(x) || (x_pooled && !aligned16(x_pooled)) ||
+        (reinterpret_cast<uintptr_t>(x8) & 7u) != 0 ||
+        (x8_pooled && (reinterpret_cast<uintptr_t>(x8_pooled) & 7u) != 0) ||
+        (reinterpret_cast<uintptr_t>(scale) & 3u) != 0)
+        return PSA_ERR_INVALID_ARG;
+    return hip_status(psa::launch_quantize_fp8(batch, heads, seq_len, head_dim, x, x_stride,
+                                               x_pooled, x8, x8_pooled, scale,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int psa_attn_fwd_fp8qk(const psa_problem* prob, float softmax_scale, const uint8_t* q8,
+                       const float* q_scale, const uint8_t* k8, const uint8_t* k8_pooled,
+                       const float* k_scale, const void* v, const void* v_pooled,
+                       const int8_t* level_map, void* o, float* lse, void* ws, size_t ws_bytes,
+                       void* stream) {
+    psa::Shape s;
+    int rc = check_problem(prob, &s);
+    if (rc != PSA_OK) return rc;
+    if (s.dtype != PSA_BF16 || s.D != 128) return PSA_ERR_UNSUPPORTED;
+    if (!q8 || !q_scale || !k8 || !k8_pooled || !k_scale || !v || !v_pooled || !level_map || !o)
+        return PSA_ERR_INVALID_ARG;
+    if (!aligned16(q8) || !aligned16(k8) || !aligned16(k8_pooled) || !aligned16(v) ||
+        !aligned16(v_pooled) || !aligned16(o) || (reinterpret_cast<uintptr_t>(q_scale) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(k_scale) & 3u) != 0)
+        return PSA_ERR_INVALID_ARG;
+    if (!std::isfinite(softmax_scale)) return PSA_ERR_INVALID_ARG;
+    const size_t need = attn_ws_layout(s, nullptr).bytes;
+    if (ws == nullptr || ws_bytes < need) return PSA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return PSA_ERR_WORKSPACE;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(s.D));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    AttnWs w = attn_ws_layout(s, ws);
+    psa::IndexBufs ib{w.row_ptr, w.col_idx, w.dev_err};
+    hipError_t e = psa::launch_build_index(s, level_map, ib, st);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(psa::launch_attn_fwd_fp8qk(s, scale, q8, q_scale, k8, k8_pooled, k_scale, v,
+                                                 v_pooled, w.row_ptr, w.col_idx, o, lse, st));
+}
+
 size_t psa_attn_bwd_workspace_bytes(const psa_problem* prob) {
     psa::Shape s;
     if (check_problem(prob, &s) != PSA_OK) return 0;

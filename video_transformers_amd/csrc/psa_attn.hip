@@ -217,10 +217,11 @@ hipError_t launch(Kern kern, int threads, const AttnArgs& a, int64_t rows, hipSt
 
 }  // namespace
 
-hipError_t launch_attn_fwd(const Shape& s, float scale, const void* q, const void* k,
-                           const void* v, const void* kp, const void* vp,
-                           const int32_t* row_ptr, const int32_t* col_idx, void* o, float* lse,
-                           bool pack, hipStream_t st) {
+namespace {
+
+AttnArgs make_args(const Shape& s, float scale, const void* q, const void* k, const void* v,
+                   const void* kp, const void* vp, const int32_t* row_ptr,
+                   const int32_t* col_idx, void* o, float* lse) {
     AttnArgs a;
     a.q = q;
     a.k = k;
@@ -243,6 +244,18 @@ hipError_t launch_attn_fwd(const Shape& s, float scale, const void* q, const voi
     a.os0 = s.os[0]; a.os1 = s.os[1]; a.os2 = s.os[2];
     a.pooled_rows = s.pooled_rows;
     a.c = scale * kLog2e;
+    a.q_scale = nullptr;
+    a.k_scale = nullptr;
+    return a;
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd(const Shape& s, float scale, const void* q, const void* k,
+                           const void* v, const void* kp, const void* vp,
+                           const int32_t* row_ptr, const int32_t* col_idx, void* o, float* lse,
+                           bool pack, hipStream_t st) {
+    const AttnArgs a = make_args(s, scale, q, k, v, kp, vp, row_ptr, col_idx, o, lse);
     const int64_t rows = static_cast<int64_t>(s.B) * s.H * s.NQB;
     if (rows == 0) return hipSuccess;
     if (s.dtype == PSA_BF16) {
@@ -255,6 +268,22 @@ hipError_t launch_attn_fwd(const Shape& s, float scale, const void* q, const voi
         if (s.D == 64 && s.BQ == 64) return launch(k_attn_fwd_f32<64, 64>, 128, a, rows, st);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_fwd_fp8qk(const Shape& s, float scale, const uint8_t* q8,
+                                 const float* q_scale, const uint8_t* k8, const uint8_t* kp8,
+                                 const float* k_scale, const void* v, const void* vp,
+                                 const int32_t* row_ptr, const int32_t* col_idx, void* o,
+                                 float* lse, hipStream_t st) {
+    if (s.dtype != PSA_BF16) return hipErrorNotSupported;
+    AttnArgs a = make_args(s, scale, q8, k8, v, kp8, vp, row_ptr, col_idx, o, lse);
+    // the e4m3 operands are contiguous [batch, head, token, head_dim] bytes
+    const int64_t nd = static_cast<int64_t>(s.N) * s.D;
+    a.qs0 = s.H * nd; a.qs1 = nd; a.qs2 = s.D;
+    a.ks0 = s.Hkv * nd; a.ks1 = nd; a.ks2 = s.D;
+    a.q_scale = q_scale;
+    a.k_scale = k_scale;
+    return launch_attn_fp8qk(s, a, st);
 }
 
 }  // namespace psa

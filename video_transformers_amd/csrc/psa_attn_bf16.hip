@@ -65,14 +65,26 @@ struct Tile {
 // PACK: a tile packs 2^l logical blocks of level l (the decoupled block-tile). Without it
 // every tile holds one logical block and its other rows are masked: the naive layout, kept
 // as the ablation baseline the packing is measured against.
-template <int D, int BQ, bool CONTIG, bool PACK>
+// F8: Q and K (level 0 and pooled) are e4m3 bytes with one scale per (batch, head); S comes
+// from v_mfma_f32_32x32x64_f8f6f4 (A: lane l holds row l % 32, bytes 32 * (l / 32) + 0..31 of
+// the 64-wide k-step; B likewise per column; C as in the bf16 product). A K row of D bytes has
+// the byte layout of a bf16 row of D / 2 elements and travels with that layout's direct loads
+// and swizzle; P, V and O stay bf16.
+template <int D, int BQ, bool CONTIG, bool PACK, bool F8>
 __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int total_rows) {
     constexpr int NW = BQ / 32;
-    using LY = Lay<D>;
-    constexpr int IPW = LY::INSTR / NW;  // direct-load instructions per wave per tensor
-    constexpr int KK = D / 16;           // k-steps of the S product
+    using LY = Lay<D>;                   // V tiles (and K tiles in bf16)
+    using KL = Lay<F8 ? D / 2 : D>;      // K tiles
+    constexpr int EK = F8 ? 1 : 2;       // bytes per K element
+    constexpr int RBK = D * EK;          // bytes per K row
+    constexpr int KK = D / 16;           // pipeline slots per step (k-steps of the bf16 S product)
+    constexpr int KS = F8 ? D / 64 : KK; // k-steps of the S product
+    constexpr int KSL = KK / KS;         // slots per k-step
     constexpr int DB = D / 32;           // 32-wide d blocks of the O product
-    __shared__ __attribute__((aligned(1024))) bf16_bits Kt[2][64 * D];
+    using KT = std::conditional_t<F8, uint8_t, bf16_bits>;
+    using KOp = std::conditional_t<F8, i32x8, bf16x8>;   // one lane's S operand of a k-step
+    static_assert(!F8 || D == 128, "fp8 K rows of 128 bytes");
+    __shared__ __attribute__((aligned(1024))) uint8_t Kt[2][64 * RBK];
     __shared__ __attribute__((aligned(1024))) bf16_bits Vt[2][64 * D];
     extern __shared__ int cols[];   // the row's block list (LDS reads do not wait on vmcnt)
 
@@ -92,10 +104,10 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
     const int b = bh / a.H;
     const int hk = h / (a.H / a.Hkv);
 
-    const bf16_bits* __restrict__ Q = static_cast<const bf16_bits*>(a.q);
-    const bf16_bits* __restrict__ K = static_cast<const bf16_bits*>(a.k);
+    const KT* __restrict__ Q = static_cast<const KT*>(a.q);
+    const KT* __restrict__ K = static_cast<const KT*>(a.k);
     const bf16_bits* __restrict__ V = static_cast<const bf16_bits*>(a.v);
-    const bf16_bits* __restrict__ KP = static_cast<const bf16_bits*>(a.kp);
+    const KT* __restrict__ KP = static_cast<const KT*>(a.kp);
     const bf16_bits* __restrict__ VP = static_cast<const bf16_bits*>(a.vp);
 
     // ---- the row's block list -> LDS ----
@@ -112,14 +124,16 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
     const bool any_valid_query = blk_first < a.Nv;
     const int limit = a.causal ? min(qt, a.Nv - 1) : a.Nv - 1;
 
-    // ---- Q fragments (B operand of S^T = K Q^T) ----
-    bf16x8 qf[KK];
+    // ---- Q fragments (B operand of S^T = K Q^T): 16 bytes (bf16) or 32 bytes (fp8) per k-step ----
+    KOp qf[KS];
     {
-        const bf16_bits* qp = Q + b * a.qs0 + h * a.qs1 + static_cast<int64_t>(qt) * a.qs2;
+        const KT* qp = Q + b * a.qs0 + h * a.qs1 + static_cast<int64_t>(qt) * a.qs2;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-            qf[kk] = *reinterpret_cast<const bf16x8*>(qp + kk * 16 + hi * 8);
+        for (int ks = 0; ks < KS; ++ks)
+            qf[ks] = *reinterpret_cast<const KOp*>(qp + (ks * 2 + hi) * (sizeof(KOp) / sizeof(KT)));
     }
+    // logit scale in log2 units (fp8: times the two operand scales)
+    const float cs = F8 ? a.c * a.q_scale[b * a.H + h] * a.k_scale[b * a.Hkv + hk] : a.c;
 
     f32x16 oacc[DB];
 #pragma unroll
@@ -130,7 +144,7 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
 
     const int64_t kbase = b * a.ks0 + hk * a.ks1;
     const int64_t vbase = b * a.vs0 + hk * a.vs1;
-    const int64_t pbase = (static_cast<int64_t>(b) * a.Hkv + hk) * a.pooled_rows * D;
+    const int64_t pbase = (static_cast<int64_t>(b) * a.Hkv + hk) * a.pooled_rows * D;  // elements
 
     // walk state (uniform): first tile, then next_tile() per tile; level changes are rare
     auto enter_level = [&](Tile& t) {   // t.l set, list position at the level's start
@@ -161,34 +175,37 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
     // first row minus the rows of the instructions before it. Instruction mi's lane offsets
     // (row inside the instruction, swizzled 16-byte chunk, plus mi instructions of rows) are
     // then loop invariants, and no per-instruction address work remains but the LDS
-    // destination in M0.
-    constexpr int KVAR = D == 128 ? 4 : 2;   // distinct K chunk swizzles across instructions
-    static_assert(IPW % KVAR == 0, "instruction m and its index inside the wave agree mod KVAR");
-    constexpr int IPWK = 64 / LY::RPI / NW;       // K instructions per wave per tile
+    // destination in M0. K and V differ in rows per instruction (KL, LY) when K is fp8.
+    constexpr int KVAR = KL::CH == 16 ? 4 : 2;   // distinct K chunk swizzles across instructions
+    constexpr int IPWK = 64 / KL::RPI / NW;       // K instructions per wave per tile
     constexpr int IPWV = 32 / LY::RPI / NW;       // V instructions per wave per half tile
-    constexpr int IPG = 8 / LY::RPI;              // instructions per 8-row group
-    static_assert(IPWK % KVAR == 0 && IPWV % IPG == 0 && IPWK / IPG <= 4, "direct-load groups");
+    constexpr int IPGK = 8 / KL::RPI;             // instructions per 8-row group (K)
+    constexpr int IPGV = 8 / LY::RPI;             // instructions per 8-row group (V)
+    static_assert(IPWK % KVAR == 0, "instruction m and its index inside the wave agree mod KVAR");
+    static_assert(IPGK >= 1 && IPWK % IPGK == 0 && IPWV % IPGV == 0 && IPWK / IPGK <= 4, "direct-load groups");
     constexpr int NSTR = CONTIG ? 1 : 2;          // lane offset sets: pooled stride (and level 0)
     uint32_t lok[NSTR][IPWK], lov[NSTR][IPWV];
     {
-        const int rr = lane / LY::CH;   // row inside the instruction
-        const int p = lane % LY::CH;    // LDS chunk position
+        const int rk = lane / KL::CH;   // row inside the instruction
+        const int pk = lane % KL::CH;   // LDS chunk position
+        const int rv = lane / LY::CH;
+        const int pv = lane % LY::CH;
 #pragma unroll
         for (int i = 0; i < NSTR; ++i) {
-            const uint32_t sk = i == 1 ? static_cast<uint32_t>(a.ks2) * 2u : static_cast<uint32_t>(D) * 2u;
+            const uint32_t sk = (i == 1 ? static_cast<uint32_t>(a.ks2) : static_cast<uint32_t>(D)) * EK;
             const uint32_t sv = i == 1 ? static_cast<uint32_t>(a.vs2) * 2u : static_cast<uint32_t>(D) * 2u;
 #pragma unroll
             for (int mi = 0; mi < IPWK; ++mi)
-                lok[i][mi] = (rr + mi * LY::RPI) * sk + static_cast<uint32_t>((p ^ LY::fk((mi % KVAR) * LY::RPI + rr)) << 4);
+                lok[i][mi] = (rk + mi * KL::RPI) * sk + static_cast<uint32_t>((pk ^ KL::fk((mi % KVAR) * KL::RPI + rk)) << 4);
 #pragma unroll
             for (int mi = 0; mi < IPWV; ++mi)
-                lov[i][mi] = (rr + mi * LY::RPI) * sv + static_cast<uint32_t>((p ^ LY::fv(rr)) << 4);
+                lov[i][mi] = (rv + mi * LY::RPI) * sv + static_cast<uint32_t>((pv ^ LY::fv(rv)) << 4);
         }
     }
     // LDS byte offsets of the tile buffers (32-bit local-address-space pointers)
     const uint32_t lds_k0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Kt[0][0]));
     const uint32_t lds_v0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Vt[0][0]));
-    constexpr uint32_t kBufBytes = 64 * D * 2;
+    constexpr uint32_t kBufBytes = 64 * RBK;   // one K buffer
     struct Dma {
         uint64_t b[4];   // SGPR bases of the wave's 8-row groups
         uint32_t lds;    // LDS byte address of the wave's first instruction
@@ -198,74 +215,85 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
     struct Pend {
         int c[4];
     };
+    // A wave's share of NR tile rows from R0 on: NR / NW rows, in groups of 8.
     auto pend = [&](const Tile& t, auto R0, auto NR) {
-        constexpr int ipw = decltype(NR)::value / LY::RPI / NW;
+        constexpr int rpw = decltype(NR)::value / NW;
         const int sh = 6 - t.l;
         const int clast = t.cnt - 1;
-        const int key0 = decltype(R0)::value + wave * ipw * LY::RPI;
+        const int key0 = decltype(R0)::value + wave * rpw;
         // an absent block of a level's partial last tile is replaced by the last one (masked)
         Pend pd;
 #pragma unroll
-        for (int j = 0; j < ipw / IPG; ++j) pd.c[j] = cols[t.base + min((key0 + 8 * j) >> sh, clast)];
+        for (int j = 0; j < rpw / 8; ++j) pd.c[j] = cols[t.base + min((key0 + 8 * j) >> sh, clast)];
         return pd;
     };
     auto resolve = [&](const Tile& t, const Pend& pd, uint32_t lds_dst, bool is_v, auto R0, auto NR) {
-        constexpr int ipw = decltype(NR)::value / LY::RPI / NW;
+        constexpr int rpw = decltype(NR)::value / NW;
+        const uint32_t rb = is_v ? D * 2u : static_cast<uint32_t>(RBK);   // bytes per row
         const int l = t.l;
         const int sh = 6 - l;
         const int rsm1 = (1 << sh) - 1;   // rows per logical block - 1
         // pooled level l starts at row N - N / 2^(l-1) (0 for l = 1 and, by the same formula
         // with shift 0, for l = 0); the level-0 / pooled tensor choice is a mask, not a branch
         const uint32_t lvl_off = static_cast<uint32_t>(a.N - (a.N >> max(l - 1, 0)));
-        const uint64_t l0 = reinterpret_cast<uint64_t>(is_v ? V + vbase : K + kbase);
-        const uint64_t pl = reinterpret_cast<uint64_t>(is_v ? VP + pbase : KP + pbase);
+        const uint64_t l0 = is_v ? reinterpret_cast<uint64_t>(V + vbase) : reinterpret_cast<uint64_t>(K + kbase);
+        const uint64_t pl = is_v ? reinterpret_cast<uint64_t>(VP + pbase) : reinterpret_cast<uint64_t>(KP + pbase);
         const uint64_t m0 = 0ull - static_cast<uint64_t>(l == 0);
-        const uint64_t base = ((l0 & m0) | (pl & ~m0)) + static_cast<uint64_t>(lvl_off * (D * 2u));
+        const uint64_t base = ((l0 & m0) | (pl & ~m0)) + static_cast<uint64_t>(lvl_off * rb);
         // byte offsets inside one (batch, head) of one level fit 32 bits (checked on the host)
-        const uint32_t stride = static_cast<uint32_t>(l == 0 && !CONTIG ? (is_v ? a.vs2 : a.ks2) : D) * 2u;
-        const int key0 = decltype(R0)::value + wave * ipw * LY::RPI;
+        const uint32_t stride = static_cast<uint32_t>(l == 0 && !CONTIG ? (is_v ? a.vs2 : a.ks2) : D) * (is_v ? 2u : EK);
+        const int key0 = decltype(R0)::value + wave * rpw;
         Dma d;
 #pragma unroll
-        for (int j = 0; j < ipw / IPG; ++j) {
+        for (int j = 0; j < rpw / 8; ++j) {
             const uint32_t r = (static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(pd.c[j])) << sh) +
                                static_cast<uint32_t>((key0 + 8 * j) & rsm1);
             d.b[j] = base + static_cast<uint64_t>(r * stride) - static_cast<uint64_t>(8 * j * stride);
         }
-        d.lds = lds_dst + static_cast<uint32_t>(wave * ipw) * 1024u;
+        d.lds = lds_dst + static_cast<uint32_t>(wave * rpw) * rb;
         return d;
     };
     // instruction mi of the wave (level-0 / pooled lane offsets by `pooled`)
     auto fire = [&](const Dma& d, bool is_v, int pooled, int mi) {
         const int s = CONTIG ? 0 : (pooled ? 0 : 1);
         const uint32_t lo = is_v ? lov[s][mi] : lok[s][mi];
-        dma16(reinterpret_cast<const void*>(d.b[mi / IPG]), lo, d.lds + static_cast<uint32_t>(mi) * 1024u);
+        dma16(reinterpret_cast<const void*>(d.b[mi / (is_v ? IPGV : IPGK)]), lo, d.lds + static_cast<uint32_t>(mi) * 1024u);
     };
-    auto issue = [&](const Tile& t, uint32_t lds_dst, bool is_v, auto R0, auto NR) {
-        constexpr int ipw = decltype(NR)::value / LY::RPI / NW;
+    auto issue = [&](const Tile& t, uint32_t lds_dst, auto ISV, auto R0, auto NR) {
+        constexpr bool is_v = decltype(ISV)::value != 0;
+        constexpr int ipw = decltype(NR)::value / (is_v ? LY::RPI : KL::RPI) / NW;
         const Dma d = resolve(t, pend(t, R0, NR), lds_dst, is_v, R0, NR);
 #pragma unroll
         for (int mi = 0; mi < ipw; ++mi) fire(d, is_v, t.l > 0, mi);
     };
     constexpr uint32_t kSlotBytes = 32 * D * 2;   // one 32-row V slot
     auto issue_k = [&](const Tile& t, int buf) {
-        issue(t, lds_k0 + (buf ? kBufBytes : 0u), false, IC<0>{}, IC<64>{});
+        issue(t, lds_k0 + (buf ? kBufBytes : 0u), IC<0>{}, IC<0>{}, IC<64>{});
     };
     auto issue_vh = [&](const Tile& t, int half, int slot) {
         if (half == 0)
-            issue(t, lds_v0 + slot * kSlotBytes, true, IC<0>{}, IC<32>{});
+            issue(t, lds_v0 + slot * kSlotBytes, IC<1>{}, IC<0>{}, IC<32>{});
         else
-            issue(t, lds_v0 + slot * kSlotBytes, true, IC<32>{}, IC<32>{});
+            issue(t, lds_v0 + slot * kSlotBytes, IC<1>{}, IC<32>{}, IC<32>{});
     };
 
     // Loop-invariant per-lane LDS byte addresses of the operand reads (buffer 0; buffer 1 and
     // the kh / j steps are instruction immediates).
-    // K: chunk position (2kk + hi) ^ fk(r) -> byte address ka_base ^ (32 kk): the row start and
+    // K, bf16: chunk (2kk + hi) ^ fk(r) -> byte address ka_base ^ (32 kk): the row start and
     // the hi / low-swizzle chunk bit occupy other bits than 32 kk (rows are D*2 >= 128 bytes).
-    uint32_t ka_base;
+    // K, fp8: chunks (4ks + 2hi + e) ^ fk(r), e = 0, 1 -> ka_base[e] ^ (64 ks), for the same
+    // reason (rows of 128 bytes; 2hi + e and fk(r) < 8 stay below bit 6).
+    uint32_t ka_base[F8 ? 2 : 1];
     {
         const int r = sigma(l32);          // kh = 1 adds 32 rows: an immediate
-        const int f = LY::fk(r);
-        ka_base = lds_k0 + static_cast<uint32_t>(r * D * 2 + 16 * ((hi ^ f) & 1) + 16 * (f & ~1));
+        const int f = KL::fk(r);
+        if constexpr (F8) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                ka_base[e] = lds_k0 + static_cast<uint32_t>(r * RBK + 16 * ((2 * hi + e) ^ f));
+        } else {
+            ka_base[0] = lds_k0 + static_cast<uint32_t>(r * D * 2 + 16 * ((hi ^ f) & 1) + 16 * (f & ~1));
+        }
     }
     const int grp = lane >> 4;   // 16-lane group: d half (grp & 1), key half (grp >> 1)
     const int jj = lane & 15;
@@ -282,22 +310,42 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
     f32x16 sacc[2];   // S of two consecutive 32-key half tiles (index: the half)
     float psum0 = 0.f, psum1 = 0.f;
 
+    // K operand address of k-step ks: a loop-invariant register per k-step (and fp8 half)
+    // plus an immediate (buffer and half); every operand read of the loop then takes its
+    // offset from the instruction
+    constexpr int KX = F8 ? 2 : 1;
+    uint32_t kx[KS][KX];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int e = 0; e < KX; ++e) kx[ks][e] = ka_base[e] ^ static_cast<uint32_t>((F8 ? 64 : 32) * ks);
+    auto read_kx = [&](int ks, uint32_t off) -> KOp {
+        if constexpr (F8) {
+            union {
+                i32x8 v;
+                u32x4 h[2];
+            } r;
+            r.h[0] = *(const lds_u32x4*)(uintptr_t)(kx[ks][0] + off);
+            r.h[1] = *(const lds_u32x4*)(uintptr_t)(kx[ks][1] + off);
+            return r.v;
+        } else {
+            return *(const lds_bf16x8*)(uintptr_t)(kx[ks][0] + off);
+        }
+    };
+    auto mfma_s = [&](const KOp& ka, int ks, const f32x16& acc) {
+        if constexpr (F8)
+            return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka, qf[ks], acc, 0, 0, 0, 0, 0, 0);
+        else
+            return __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], acc, 0, 0, 0);
+    };
     // S^T of half H of the K tile at LDS byte offset kbuf (0 or one buffer) into sacc[H]
     auto compute_s = [&](auto H, uint32_t kbuf) {
         constexpr int hh = decltype(H)::value;
-        constexpr uint32_t boff = hh * 32 * D * 2;
-        // the buffer offset (bit 14 and up) and the XOR of 32 kk (bits 5..7) do not interact;
-        // the per-k-step addresses stay inside the loop (one XOR each) instead of KK registers
-        uint32_t kb_opaque = ka_base + kbuf;
-        asm volatile("" : "+v"(kb_opaque));
+        const uint32_t off = kbuf + hh * 32 * RBK;
 #pragma unroll
         for (int e = 0; e < 16; ++e) sacc[hh][e] = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            const uint32_t kaddr = kb_opaque ^ static_cast<uint32_t>(32 * kk);
-            const bf16x8 ka = *(const lds_bf16x8*)(uintptr_t)(kaddr + boff);
-            sacc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], sacc[hh], 0, 0, 0);
-        }
+        for (int ks = 0; ks < KS; ++ks) sacc[hh] = mfma_s(read_kx(ks, off), ks, sacc[hh]);
     };
     // P fragment j (0/1) of sacc[H]: 16 keys 16j + 8*hi + e of that half; exp2 offset `off`
     auto make_p = [&](auto H, int j, float off) {
@@ -308,8 +356,8 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
         } pk;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-            const float p0 = fast_exp2(fmaf(sacc[hh][j * 8 + 2 * t], a.c, off));
-            const float p1 = fast_exp2(fmaf(sacc[hh][j * 8 + 2 * t + 1], a.c, off));
+            const float p0 = fast_exp2(fmaf(sacc[hh][j * 8 + 2 * t], cs, off));
+            const float p1 = fast_exp2(fmaf(sacc[hh][j * 8 + 2 * t + 1], cs, off));
             pk.u[t] = pack_bf16x2(p0, p1);
             if (t & 1)
                 psum1 = add_bf16x2(pk.u[t], psum1);
@@ -362,7 +410,7 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
                      fmaxf(fmaxf(sacc[hh][e0 + 4], sacc[hh][e0 + 5]), fmaxf(sacc[hh][e0 + 6], sacc[hh][e0 + 7])));
     };
     auto half_max = [&](float x0, float x1, int lvl) {
-        return fmaf(pair32_max(fmaxf(x0, x1)), a.c, static_cast<float>(lvl));  // log2 units
+        return fmaf(pair32_max(fmaxf(x0, x1)), cs, static_cast<float>(lvl));  // log2 units
     };
     // lazy running max: rescale the O accumulators and row sums only when the max in use is
     // exceeded by more than kLazyRescale (after the O products issued so far)
@@ -397,23 +445,14 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
 #pragma unroll
         for (int q = 0; q < PAIRS; ++q) {
             const int pr = c * PAIRS + q;   // pair 0..7: fragment pr / 4, dword pr % 4
-            const float p0 = fast_exp2(fmaf(sacc[hh][2 * pr], a.c, off));
-            const float p1 = fast_exp2(fmaf(sacc[hh][2 * pr + 1], a.c, off));
+            const float p0 = fast_exp2(fmaf(sacc[hh][2 * pr], cs, off));
+            const float p1 = fast_exp2(fmaf(sacc[hh][2 * pr + 1], cs, off));
             pk[pr] = pack_bf16x2(p0, p1);
             if (pr & 1)
                 psum1 = add_bf16x2(pk[pr], psum1);
             else
                 psum0 = add_bf16x2(pk[pr], psum0);
         }
-    };
-    // K operand address of k-step kk: a loop-invariant register per k-step plus an immediate
-    // (buffer and half); every operand read of the loop then takes its offset from the
-    // instruction
-    uint32_t kx[KK];
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) kx[kk] = ka_base ^ static_cast<uint32_t>(32 * kk);
-    auto read_kx = [&](int kk, uint32_t off) {
-        return *(const lds_bf16x8*)(uintptr_t)(kx[kk] + off);
     };
     auto read_v = [&](uint32_t vslot, int j, int dblk) {
         const uint32_t pa = va_addr[dblk] + vslot + j * 16 * D * 2;
@@ -425,34 +464,36 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
         va.h[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(uintptr_t)(pa + 4 * D * 2));
         return va.v;
     };
-    // One pipeline step, in a fixed issue order (a scheduling barrier after each MFMA):
-    //   S(h) MFMAs 0..KK-1, K reads three MFMAs ahead; after each, 1/KK of the exp work of the
-    //   previous half (sacc[H^1], level lvl_p); from MFMA KK/2 on, the O MFMAs of its first 16
-    //   keys alternate with them; then the O MFMAs of its last 16 keys, alongside the row max
-    //   of S(h).
+    // One pipeline step of KK slots, in a fixed issue order (a scheduling barrier after each
+    // MFMA):
+    //   S(h) MFMAs: bf16 one per slot, K reads three MFMAs ahead; fp8 one per KSL slots, K
+    //   reads all at the start. In each slot 1/KK of the exp work of the previous half
+    //   (sacc[H^1], level lvl_p); from slot KK/2 on, the O MFMAs of its first 16 keys; then the
+    //   O MFMAs of its last 16 keys, alongside the row max of S(h).
     // Returns the half's unmasked max (log2 units).
     auto step = [&](auto H, uint32_t kbuf, uint32_t vslot, int lvl_p, int lvl_h, auto&& dma) {
         constexpr int hh = decltype(H)::value;
+        constexpr int KPRE = F8 ? KS : 3;   // K reads issued before the first slot
         const float off = exp_off(lvl_p);
-        const uint32_t koff = kbuf + hh * 32 * D * 2;   // an immediate: no carry into the XORed bits
+        const uint32_t koff = kbuf + hh * 32 * RBK;   // an immediate: no carry into the XORed bits
         uint32_t pk[8];
-        bf16x8 kr[KK];
+        KOp kr[KS];
         bf16x8 vr0[DB], vr1[DB];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 3 && i < KK; ++i) kr[i] = read_kx(i, koff);
+        for (int i = 0; i < KPRE && i < KS; ++i) kr[i] = read_kx(i, koff);
 #pragma unroll
         for (int e = 0; e < 16; ++e) sacc[hh][e] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            if (kk + 3 < KK) kr[kk + 3] = read_kx(kk + 3, koff);
+            if (!F8 && kk + KPRE < KS) kr[kk + KPRE] = read_kx(kk + KPRE, koff);
             if (kk == 0)
 #pragma unroll
                 for (int d = 0; d < DB; ++d) vr0[d] = read_v(vslot, 0, d);
             if (kk == KK / 2)
 #pragma unroll
                 for (int d = 0; d < DB; ++d) vr1[d] = read_v(vslot, 1, d);
-            sacc[hh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kr[kk], qf[kk], sacc[hh], 0, 0, 0);
+            if (kk % KSL == 0) sacc[hh] = mfma_s(kr[kk / KSL], kk / KSL, sacc[hh]);
             exp_chunk(IC<hh ^ 1>{}, kk, off, pk);
             dma(kk);   // the next tiles' direct loads ride along with the MFMAs
             if (kk >= KK / 2) {
@@ -609,15 +650,15 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
     }
 }
 
-template <int D, int BQ, bool PACK>
+template <int D, int BQ, bool PACK, bool F8 = false>
 hipError_t launch_one(const Shape& s, const AttnArgs& a, hipStream_t st) {
     const int rows = s.B * s.H * s.NQB;
     const int nper = (rows + 7) / 8;
     const size_t dyn = static_cast<size_t>(s.NKB) * sizeof(int);
     if (a.ks2 == D && a.vs2 == D)
-        hipLaunchKernelGGL((k_attn_fwd_bf16<D, BQ, true, PACK>), dim3(8 * nper), dim3(2 * BQ), dyn, st, a, rows);
+        hipLaunchKernelGGL((k_attn_fwd_bf16<D, BQ, true, PACK, F8>), dim3(8 * nper), dim3(2 * BQ), dyn, st, a, rows);
     else
-        hipLaunchKernelGGL((k_attn_fwd_bf16<D, BQ, false, PACK>), dim3(8 * nper), dim3(2 * BQ), dyn, st, a, rows);
+        hipLaunchKernelGGL((k_attn_fwd_bf16<D, BQ, false, PACK, F8>), dim3(8 * nper), dim3(2 * BQ), dyn, st, a, rows);
     return hipGetLastError();
 }
 
@@ -634,6 +675,14 @@ hipError_t launch_packed(const Shape& s, const AttnArgs& a, hipStream_t st) {
 
 hipError_t launch_attn_bf16(const Shape& s, const AttnArgs& a, bool pack, hipStream_t st) {
     return pack ? launch_packed<true>(s, a, st) : launch_packed<false>(s, a, st);
+}
+
+hipError_t launch_attn_fp8qk(const Shape& s, const AttnArgs& a, hipStream_t st) {
+    if (s.B * s.H * s.NQB == 0) return hipSuccess;
+    if (a.q_scale == nullptr || a.k_scale == nullptr) return hipErrorInvalidValue;
+    if (s.D == 128 && s.BQ == 128) return launch_one<128, 128, true, true>(s, a, st);
+    if (s.D == 128 && s.BQ == 64) return launch_one<128, 64, true, true>(s, a, st);
+    return hipErrorNotSupported;
 }
 
 }  // namespace psa

@@ -26,6 +26,10 @@ struct AttnArgs {
     int64_t qs0, qs1, qs2, ks0, ks1, ks2, vs0, vs1, vs2, os0, os1, os2;
     int64_t pooled_rows;
     float c;  // softmax scale * log2(e)
+    // fp8 QK^T reading only (null otherwise): per (batch, head) scales of the e4m3 operands,
+    // q_scale [B*H] and k_scale [B*Hkv]; the logit of q8 . k8 is c * q_scale * k_scale times it
+    const float* q_scale;
+    const float* k_scale;
 };
 
 // Level-by-level walk over a row's block index. Uniform across the workgroup. Only the
@@ -100,5 +104,9 @@ __device__ __forceinline__ RowSrc tile_row(const AttnArgs& a, const TileWalk& tw
 
 // pack = false: one logical block per hardware tile (the unpacked ablation baseline).
 hipError_t launch_attn_bf16(const Shape& s, const AttnArgs& a, bool pack, hipStream_t st);
+
+// Q and K (level 0 and pooled) as e4m3 bytes, contiguous, with a.q_scale / a.k_scale set
+// (head_dim 128 only; hipErrorNotSupported otherwise). V, O and the index as in the bf16 path.
+hipError_t launch_attn_fp8qk(const Shape& s, const AttnArgs& a, hipStream_t st);
 
 }  // namespace psa

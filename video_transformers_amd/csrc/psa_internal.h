@@ -37,6 +37,21 @@ hipError_t launch_attn_fwd(const Shape& s, float scale, const void* q, const voi
                            const int32_t* row_ptr, const int32_t* col_idx, void* o, float* lse,
                            bool pack, hipStream_t st);
 
+// Forward with Q and K (level 0 and pooled) as contiguous e4m3 bytes and one float scale per
+// (batch, head) of each (q_scale [B*H], k_scale [B*Hkv]); V, O as in launch_attn_fwd (bf16).
+hipError_t launch_attn_fwd_fp8qk(const Shape& s, float scale, const uint8_t* q8,
+                                 const float* q_scale, const uint8_t* k8, const uint8_t* kp8,
+                                 const float* k_scale, const void* v, const void* vp,
+                                 const int32_t* row_ptr, const int32_t* col_idx, void* o,
+                                 float* lse, hipStream_t st);
+
+// Per-head e4m3 quantization of one bf16 tensor [B, Hx, N, D] (strides xs, elements) and,
+// when xp is not null, of its packed pooled rows [B, Hx, 7N/8, D] with the same scale.
+// Writes x8 / xp8 contiguous and scale [B*Hx]; see psa_quantize_fp8.
+hipError_t launch_quantize_fp8(int B, int Hx, int N, int D, const void* x, const int64_t xs[3],
+                               const void* xp, uint8_t* x8, uint8_t* xp8, float* scale,
+                               hipStream_t st);
+
 // Backward (bf16 only; hipErrorNotSupported otherwise). `scratch` holds
 // attn_bwd_scratch_bytes(s): per-row lse2 and D, and the f32 gradients of every level's rows.
 size_t attn_bwd_scratch_bytes(const Shape& s);

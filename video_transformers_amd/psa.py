@@ -34,7 +34,8 @@ SKIP = -1
 EXPORTS = ("psa_pooled_rows", "psa_build_pyramid", "psa_mask_workspace_bytes", "psa_mask",
            "psa_mask_assign", "psa_build_index", "psa_attn_workspace_bytes", "psa_attn_fwd",
            "psa_attn_fwd_indexed", "psa_attn_fwd_unpacked", "psa_attn_bwd_workspace_bytes",
-           "psa_attn_bwd", "psa_check_status", "psa_status_string", "psa_last_hip_error")
+           "psa_attn_bwd", "psa_quantize_fp8", "psa_attn_fwd_fp8qk", "psa_check_status",
+           "psa_status_string", "psa_last_hip_error")
 
 
 class PsaError(RuntimeError):
@@ -93,6 +94,10 @@ def lib() -> ctypes.CDLL:
         L.psa_attn_bwd_workspace_bytes.restype = SZ
         L.psa_attn_bwd.argtypes = [P, ctypes.c_float] + [V] * 13 + [SZ, V]
         L.psa_attn_bwd.restype = I32
+        L.psa_quantize_fp8.argtypes = [I32, I32, I32, I32, V, ctypes.POINTER(I64), V, V, V, V, V]
+        L.psa_quantize_fp8.restype = I32
+        L.psa_attn_fwd_fp8qk.argtypes = [P, ctypes.c_float] + [V] * 11 + [SZ, V]
+        L.psa_attn_fwd_fp8qk.restype = I32
         L.psa_check_status.argtypes, L.psa_check_status.restype = [V, V], I32
         L.psa_status_string.argtypes, L.psa_status_string.restype = [I32], ctypes.c_char_p
         L.psa_last_hip_error.argtypes, L.psa_last_hip_error.restype = [], I32
@@ -327,6 +332,49 @@ def attn_bwd(q, k, v, k_pooled, v_pooled, level_map, o, lse, dout, prob: Problem
                               _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws),
                               ws.numel(), _stream(stream)), "psa_attn_bwd")
     return dq, dk, dv
+
+
+def quantize_fp8(x: torch.Tensor, x_pooled: Optional[torch.Tensor] = None, stream=None):
+    """Per-head e4m3 codes of a bf16 [B, Hx, N, d] tensor (and of its packed pooled rows, same
+    scale). Returns (x8 [B,Hx,N,d] uint8, x8_pooled or None, scale [B*Hx] float32); the codes
+    view as torch.float8_e4m3fn."""
+    if x.dtype != torch.bfloat16 or x.dim() != 4 or x.stride(3) != 1:
+        raise ValueError("x must be bf16 [B, Hx, N, d] with a contiguous last axis")
+    B, Hx, N, d = x.shape
+    x8 = torch.empty((B, Hx, N, d), dtype=torch.uint8, device=x.device)
+    x8p = None
+    if x_pooled is not None:
+        if x_pooled.dtype != torch.bfloat16 or not x_pooled.is_contiguous():
+            raise ValueError("x_pooled must be contiguous bf16")
+        x8p = torch.empty(x_pooled.shape, dtype=torch.uint8, device=x.device)
+    scale = torch.empty(B * Hx, dtype=torch.float32, device=x.device)
+    st = (ctypes.c_int64 * 3)(*x.stride()[:3])
+    _check(lib().psa_quantize_fp8(B, Hx, N, d, _ptr(x), st, _ptr(x_pooled), _ptr(x8), _ptr(x8p),
+                                  _ptr(scale), _stream(stream)), "psa_quantize_fp8")
+    return x8, x8p, scale
+
+
+def attn_fwd_fp8qk(q8, q_scale, k8, k8_pooled, k_scale, v, v_pooled, level_map, prob: Problem, *,
+                   scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                   ws: Optional[torch.Tensor] = None, stream=None):
+    """attn_fwd with the q . k products on e4m3 operands from quantize_fp8 (q8, k8, k8_pooled
+    contiguous uint8). `prob` is the bf16 problem of Q, K, V (its o_stride applies to out).
+    Returns (o, lse or None)."""
+    for t in (q8, k8, k8_pooled):
+        if t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError("q8, k8, k8_pooled must be contiguous uint8 codes")
+    if out is None:
+        out = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
+    if lse is None and want_lse:
+        lse = torch.empty(q8.shape[:3], dtype=torch.float32, device=q8.device)
+    if ws is None:
+        ws = attn_workspace(prob, q8.device)
+    _check(lib().psa_attn_fwd_fp8qk(prob.ref(), ctypes.c_float(scale), _ptr(q8), _ptr(q_scale),
+                                    _ptr(k8), _ptr(k8_pooled), _ptr(k_scale), _ptr(v),
+                                    _ptr(v_pooled), _ptr(level_map), _ptr(out), _ptr(lse),
+                                    _ptr(ws), ws.numel(), _stream(stream)), "psa_attn_fwd_fp8qk")
+    return out, lse
 
 
 def check_status(ws: torch.Tensor, stream=None) -> None:
