@@ -222,10 +222,9 @@ int psa_attn_fwd_unpacked(const psa_problem* prob, float softmax_scale, const vo
  *   amax  = max |x| over the head's seq_len rows;
  *   scale[b*heads + h] = amax / 448 rounded to float32 (448 = the largest finite e4m3), or 1
  *           when amax = 0;
- *   x8    = the e4m3 (OCP FP8 E4M3, bias 7, with subnormals) code nearest to x / scale, ties to
- *           even (the quotient is formed in float64, which makes the rounding exact), written
- *           contiguous [batch, heads, seq_len, head_dim] bytes; the code stands for
- *           value(code) * scale.
+ *   x8    = the e4m3 (OCP FP8 E4M3, bias 7, with subnormals) code nearest to the exact
+ *           quotient x / scale, ties to even, written contiguous [batch, heads, seq_len,
+ *           head_dim] bytes; the code stands for value(code) * scale.
  * With x_pooled (bf16 [batch, heads, 7*seq_len/8, head_dim], contiguous, the layout of
  * psa_build_pyramid's outputs) the pooled rows are quantized with the same scale into
  * x8_pooled (contiguous, same shape, bytes); x_pooled and x8_pooled are both null or both set.

@@ -71,31 +71,51 @@ def pack_levels(levels):
 # ---------------------------------------------------------------------------------------
 # quantization
 # ---------------------------------------------------------------------------------------
+def every_bf16_upto(amax: float, n: int) -> torch.Tensor:
+    """Every bf16 value v with |v| <= amax (both signs, amax itself included), zero-padded to
+    n values."""
+    bits = torch.arange(0, 0x7F80, dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+    pos = bits[bits.float() <= amax].float()
+    vals = torch.cat([pos, -pos])
+    assert vals.numel() <= n and float(pos.max()) == amax
+    out = torch.zeros(n)
+    out[:vals.numel()] = vals
+    return out
+
+
+# amax values whose scale amax / 448 makes a float32 estimate of x / s round to the wrong code
+# for some bf16 x (found by enumerating the bf16 amax values in [2^-8, 2^8])
+AMAX_ESTIMATE_MISSES = (0.00396728515625, 0.00408935546875, 0.0045166015625)
+
+
 def test_quantize_every_bf16_value():
-    """Every finite bf16 of magnitude <= 448 (every e4m3 value and every midpoint between two
-    of them among them) in a head whose amax is 448 (scale exactly 1); the same values times
-    2^-20 (scale exactly 2^-20, same codes; values below 2^-100 left out so that the product
-    stays exact); an all-zero head (scale 1, all codes zero)."""
+    """Heads holding every finite bf16 up to their amax: amax 448 (scale exactly 1; every e4m3
+    value and every midpoint between two of them appear), the same values times 2^-20 (scale
+    exactly 2^-20, same codes; values below 2^-100 left out so that the product stays exact),
+    an all-zero head (scale 1, all codes zero), amax values whose scale defeats a float32
+    estimate of the quotient, and amax 448 * 2^-120 (scale 2^-120, below the float32 path's
+    range)."""
     announce("quantize_fp8 every bf16 value")
-    pos = torch.arange(0, 0x43E0 + 1, dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
-    vals = torch.cat([pos, -pos]).float()
     N, D = 272, 128
-    head = torch.zeros(N * D)
-    head[:vals.numel()] = vals
-    head = head.view(N, D)
+    head = every_bf16_upto(448.0, N * D)
     big = torch.where(head.abs() >= 2.0 ** -100, head, torch.zeros_like(head))
-    x = torch.stack([head, big * 2.0 ** -20, torch.zeros(N, D)])[None].to(torch.bfloat16)
-    assert torch.equal(x[0, 1].float() * 2.0 ** 20, big)
+    heads = [head, big * 2.0 ** -20, torch.zeros(N * D)]
+    heads += [every_bf16_upto(a, N * D) for a in AMAX_ESTIMATE_MISSES]
+    heads.append(every_bf16_upto(448.0 * 2.0 ** -120, N * D))
+    x = torch.stack(heads).view(1, len(heads), N, D).to(torch.bfloat16)
+    assert torch.equal(x[0, 1].float().flatten() * 2.0 ** 20, big)
     x8, _, sc = psa.quantize_fp8(x.to(DEV))
     torch.cuda.synchronize()
     got_s = sc.cpu().numpy()
     got = decode(x8)
-    for h in range(3):
+    for h in range(len(heads)):
         xh = oracle.as_f64(x[0, h])
         s = oracle.fp8_scale(xh)
         assert np.float32(s) == got_s[h], (h, s, got_s[h])
-        assert np.array_equal(got[0, h], oracle.fp8_quantize(xh, s)), h
+        ref = oracle.fp8_quantize(xh, s)
+        assert np.array_equal(got[0, h], ref), (h, int(np.sum(got[0, h] != ref)))
     assert got_s[0] == 1.0 and got_s[1] == 2.0 ** -20 and got_s[2] == 1.0
+    assert got_s[-1] == 2.0 ** -120
     assert np.count_nonzero(got[0, 2]) == 0
 
 
