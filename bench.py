@@ -15,7 +15,9 @@ FLOPs (4*d per executed (valid query, visible pooled key) pair) per second of st
 MFMA peak, speedup over the same kernel on an all-level-0 map, and over the unpacked layout
 with one logical block per hardware tile on the same map). `roofline` is for that
 kernel, timed with HIP events on the stream it runs on. `bwd` times psa_attn_bwd on the same
-map with a seeded output gradient (not part of `value`). `cpu_baseline` times the CPU oracle
+map with a seeded output gradient (not part of `value`). `fp8qk` times the forward with its
+q . k products on e4m3 operands (psa_quantize_fp8 of Q and of K with its pooled rows, then
+psa_attn_fwd_fp8qk on the same map; not part of `value`). `cpu_baseline` times the CPU oracle
 (fp64 numpy) on a bounded sample of the same workload on this host's cores.
 """
 from __future__ import annotations
@@ -35,6 +37,7 @@ sys.path.insert(0, ROOT)
 import workloads as W  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, TFLOP/s
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, GB/s
 METRIC = "psa_attn_fwd ms/layer + effective TFLOP/s (% bf16 MFMA peak), Wan-like 32k"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_fwd_bf16_traffic.txt")
@@ -281,6 +284,12 @@ def run(args) -> dict:
     frac = {("skip" if int(a) < 0 else f"L{int(a)}"): round(float(c) / lm_host.size, 4)
             for a, c in zip(lv, cnt)}
 
+    # the e4m3 QK^T forward on the same map, timed next to the step (same clocks)
+    fp8 = None
+    if not args.no_fp8 and wl.dtype == "bf16" and d == 128:
+        lm_dev = lm_buf if computed_map else drawn
+        fp8 = _fp8_run(wl, prob, L, ptr, st, check, q, k, v, kp, vp, lm_dev, stream, flops,
+                       float(st_ms[2]), attn_ms_mean)
     # same kernel, all-level-0 map (causal: the lower triangle)
     dense_ms = float("nan")
     if not args.no_dense:
@@ -289,17 +298,11 @@ def run(args) -> dict:
     # same map, same index, one logical block per hardware tile (the unpacked ablation)
     unpacked_ms = float("nan")
     if not args.no_unpacked and wl.dtype == "bf16":
-        ue = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        times = []
-        for i in range(4):
-            ue[0].record(stream)
+        def unpacked():
             check(L.psa_attn_fwd_unpacked(prob.ref(), ctypes.c_float(0.0), ptr(q), ptr(k), ptr(v),
                                           ptr(kp), ptr(vp), ptr(row_ptr), ptr(col_idx), ptr(o),
                                           ptr(lse), st), "attn unpacked")
-            ue[1].record(stream)
-            torch.cuda.synchronize()
-            times.append(ue[0].elapsed_time(ue[1]))
-        unpacked_ms = float(np.median(times[1:]))
+        unpacked_ms = _timed_back_to_back(unpacked, stream, reps=4, warm=1)
     bwd = None
     if not args.no_bwd and wl.dtype == "bf16":
         bwd = _bwd_run(wl, prob, L, ptr, st, check, q, k, v, kp, vp, lm_host, o, lse, stream, flops)
@@ -307,15 +310,33 @@ def run(args) -> dict:
                   attn_ms_mean, st_ms, dense_ms, wall)
     if bwd is not None:
         out["bwd"] = bwd
+    if fp8 is not None:
+        out["fp8qk"] = fp8
     out["attn"]["unpacked_same_map_ms"] = None if unpacked_ms != unpacked_ms else round(unpacked_ms, 3)
     out["attn"]["speedup_vs_unpacked"] = (None if unpacked_ms != unpacked_ms
                                           else round(unpacked_ms / attn_ms_mean, 2))
     return out
 
 
+def _timed_back_to_back(fn, stream, reps: int = 10, warm: int = 2) -> float:
+    """Mean ms per call of `reps` calls enqueued back to back (as the step loop runs), after
+    `warm` untimed calls; HIP events on the launch stream bracket the whole run."""
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        fn()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    return ev[0].elapsed_time(ev[1]) / reps
+
+
 def _bwd_run(wl, prob, L, ptr, st, check, q, k, v, kp, vp, lm_host, o, lse, stream, fwd_flops):
-    """psa_attn_bwd on the step's map, o and lse with a seeded output gradient: median of 5
-    timed launches (the call builds its block index and runs its four kernels). Work is
+    """psa_attn_bwd on the step's map, o and lse with a seeded output gradient: mean of 5 calls
+    run back to back (the call builds its block index and runs its four kernels). Work is
     counted as 2.5x the forward's executed FLOPs (recomputed S, then dP, dV, dK, dQ: 10*d per
     executed pair)."""
     import ctypes
@@ -331,24 +352,63 @@ def _bwd_run(wl, prob, L, ptr, st, check, q, k, v, kp, vp, lm_host, o, lse, stre
         check(L.psa_attn_bwd(prob.ref(), ctypes.c_float(0.0), ptr(q), ptr(k), ptr(v), ptr(kp),
                              ptr(vp), ptr(lm), ptr(o), ptr(lse), ptr(dout), ptr(dq), ptr(dk),
                              ptr(dv), ptr(ws), n, st), "attn bwd")
-    for _ in range(2):
-        call()
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    times = []
-    for _ in range(5):
-        ev[0].record(stream)
-        call()
-        ev[1].record(stream)
-        torch.cuda.synchronize()
-        times.append(ev[0].elapsed_time(ev[1]))
+    ms = _timed_back_to_back(call, stream, reps=5)
     check(L.psa_check_status(ptr(ws), st), "attn bwd status")
-    ms = float(np.median(times))
     tf = 2.5 * fwd_flops / (ms * 1e-3) / 1e12
-    return {"ms_per_layer_median": round(ms, 4), "tflops_algorithmic": round(tf, 2),
+    return {"ms_per_layer": round(ms, 4), "tflops_algorithmic": round(tf, 2),
             "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
             "work": "2.5x the forward's executed FLOP (10*d per executed pair)",
             "workspace_bytes": n}
+
+
+def _fp8_run(wl, prob, L, ptr, st, check, q, k, v, kp, vp, lm, stream, fwd_flops, index_ms,
+             bf16_attn_ms):
+    """The e4m3 QK^T forward on the step's map: psa_quantize_fp8 of K (with its pooled rows)
+    and of Q, then psa_attn_fwd_fp8qk (which builds its block index, then runs the kernel);
+    mean of 10 calls run back to back each. The kernel's own time is estimated as the call minus the
+    index build timed in the step (same map, same kernels). Its bound mixes two peaks: the
+    q . k half of the executed FLOP (2*d per pair) at the fp8 MFMA peak and the P V half at
+    the bf16 one."""
+    import ctypes
+    import torch
+    dev = q.device
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    k8 = torch.empty((B, Hkv, N, d), dtype=torch.uint8, device=dev)
+    kp8 = torch.empty(kp.shape, dtype=torch.uint8, device=dev)
+    q8 = torch.empty((B, H, N, d), dtype=torch.uint8, device=dev)
+    sk = torch.empty(B * Hkv, dtype=torch.float32, device=dev)
+    sq = torch.empty(B * H, dtype=torch.float32, device=dev)
+    o8 = torch.empty_like(q)
+    lse8 = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    n = L.psa_attn_workspace_bytes(prob.ref())
+    ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    kst = (ctypes.c_int64 * 3)(*k.stride()[:3])
+    qst = (ctypes.c_int64 * 3)(*q.stride()[:3])
+
+    def quant():
+        check(L.psa_quantize_fp8(B, Hkv, N, d, ptr(k), kst, ptr(kp), ptr(k8), ptr(kp8), ptr(sk), st),
+              "quantize k")
+        check(L.psa_quantize_fp8(B, H, N, d, ptr(q), qst, None, ptr(q8), None, ptr(sq), st),
+              "quantize q")
+
+    def attn():
+        check(L.psa_attn_fwd_fp8qk(prob.ref(), ctypes.c_float(0.0), ptr(q8), ptr(sq), ptr(k8),
+                                   ptr(kp8), ptr(sk), ptr(v), ptr(vp), ptr(lm), ptr(o8), ptr(lse8),
+                                   ptr(ws), n, st), "attn fp8qk")
+
+    q_ms = _timed_back_to_back(quant, stream)
+    a_ms = _timed_back_to_back(attn, stream)
+    check(L.psa_check_status(ptr(ws), st), "attn fp8qk status")
+    kern_ms = a_ms - index_ms
+    tf = fwd_flops / (kern_ms * 1e-3) / 1e12
+    bound_ms = (fwd_flops / 2 / PEAK_FP8_TFLOPS + fwd_flops / 2 / PEAK_BF16_TFLOPS) / 1e12 * 1e3
+    return {"quantize_q_k_ms": round(q_ms, 4), "attn_call_ms": round(a_ms, 4),
+            "attn_kernel_ms_est": round(kern_ms, 4), "tflops_executed": round(tf, 2),
+            "speedup_vs_bf16_kernel": round(bf16_attn_ms / kern_ms, 3),
+            "roofline": {"bound": "mfma", "peak": "fp8 5000 TFLOP/s for q.k, bf16 2500 for P V",
+                         "min_ms": round(bound_ms, 4), "frac": round(bound_ms / kern_ms, 4)},
+            "quantization": "e4m3, one scale per (batch, head), K and pooled K share it"}
 
 
 def _dense_run(args, wl, prob, L, ptr, st, check, q, k, v, kp, vp, o, lse, row_ptr, col_idx,
@@ -366,17 +426,11 @@ def _dense_run(args, wl, prob, L, ptr, st, check, q, k, v, kp, vp, o, lse, row_p
     rp_d = torch.empty_like(row_ptr)
     ci_d = torch.empty_like(col_idx)
     check(L.psa_build_index(prob.ref(), ptr(dense), ptr(rp_d), ptr(ci_d), ptr(dev_err), st), "index")
-    de = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    times = []
-    for i in range(3):
-        de[0].record(stream)
+    def dense_call():
         check(L.psa_attn_fwd_indexed(prob.ref(), ctypes.c_float(0.0), ptr(q), ptr(k), ptr(v),
                                      ptr(kp), ptr(vp), ptr(rp_d), ptr(ci_d), ptr(o), ptr(lse), st),
               "attn dense")
-        de[1].record(stream)
-        torch.cuda.synchronize()
-        times.append(de[0].elapsed_time(de[1]))
-    return float(np.median(times[1:]))
+    return _timed_back_to_back(dense_call, stream, reps=3, warm=1)
 
 
 def _report(args, wl, flops, pairs, dpairs, frac, d, B, H, N, computed_map, attn_ms,
@@ -436,6 +490,8 @@ def main():
                     help="skip the unpacked-layout comparison run (one logical block per tile)")
     ap.add_argument("--no-bwd", action="store_true",
                     help="skip the psa_attn_bwd timing (reported beside the forward metric)")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the e4m3 QK^T forward timing (reported beside the forward metric)")
     ap.add_argument("--mask-mode", choices=("sampling", "antidiag", "meankey"), default=None,
                     help="score with this psa_mask mode instead of the workload's own")
     ap.add_argument("--cpu-budget", type=float, default=15.0)

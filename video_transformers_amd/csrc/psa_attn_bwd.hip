@@ -33,8 +33,8 @@
 // All products run on v_mfma_f32_32x32x16_bf16 with f32 accumulation; P and dS enter the
 // products rounded to bf16. Operand tiles are staged in LDS by direct loads
 // (global_load_lds_dwordx4), in the swizzled layouts of psa_bf16_tile.h: in the dq kernel K
-// rows in the fk layout and a second copy of K in the fv layout for its transposed reads, V
-// in fk; in the dkv kernel Q and dO once each in the fq layout, read both ways.
+// once in the fq layout (read by rows for S and transposed for dQ) and V in fk; in the dkv
+// kernel Q and dO once each in the fq layout, read both ways.
 #include <limits.h>
 #include <math.h>
 
