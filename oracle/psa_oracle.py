@@ -469,7 +469,7 @@ def _attention_from_levels(q: np.ndarray, lk: Dict[int, np.ndarray], lvv: Dict[i
 
 
 # ----------------------------------------------------------------------------------------
-# 5b. FP8 (e4m3) operands for the QK^T product
+# 5b. FP8 (e4m3) operands for the QK^T product (and for P V)
 # ----------------------------------------------------------------------------------------
 
 E4M3_MAX = 448.0
@@ -520,6 +520,51 @@ def attention_fp8qk_head(q8: np.ndarray, k8: np.ndarray, kp8_levels: Dict[int, n
     lk.update(kp8_levels)
     lvv = pyramid(v)
     return _attention_from_levels(q8, lk, lvv, level_map, p, sc * s_q * s_k, qblocks)
+
+
+def attention_fp8_head(q8: np.ndarray, k8: np.ndarray, kp8_levels: Dict[int, np.ndarray],
+                       v8: np.ndarray, vp8_levels: Dict[int, np.ndarray], s_q: float, s_k: float,
+                       s_v: float, level_map: np.ndarray, p: Problem,
+                       scale: Optional[float] = None, qblocks: Optional[Iterable[int]] = None):
+    """attention_fp8qk_head with the P V product on e4m3 operands as well ([ABS], [NEWS]
+    "Practical": FP8 arithmetic on the block-tile kernel; the pages give no recipe). V and its
+    pooled levels are e4m3 values with one scale s_v per head (v8 stands for v8 * s_v). For
+    each valid query, in log2 units t_j = z_j / ln 2 (z_j as in attention_fp8qk_head):
+      M = ceil(max_j t_j), an integer;  p_j = 2^(t_j - M) in (0, 1];  P8_j = e4m3(p_j);
+      o = s_v * sum_j P8_j v8_j / sum_j P8_j;  lse = (M + log2 sum_j P8_j) * ln 2.
+    The weights that multiply V are the quantized P8_j, normalised by their own sum. An
+    integer reference keeps P8 independent of which integer is used, as long as the values
+    stay in e4m3's normal range (rounding commutes with scaling by a power of two). Rows with
+    no visible key and pad rows give o = 0 and lse = -inf."""
+    sc = p.scale if scale is None else scale
+    lk = {0: k8}
+    lk.update(kp8_levels)
+    lvv = {0: v8}
+    lvv.update(vp8_levels)
+    n, d = q8.shape
+    o = np.full((n, d), np.nan)
+    lse = np.full((n,), np.nan)
+    for qb in (range(p.n_qblocks) if qblocks is None else qblocks):
+        qi = np.arange(qb * p.block_q, (qb + 1) * p.block_q)
+        Kb, Vb, lv, last = gather_row_keys(lk, lvv, level_map[qb], p)
+        o[qi] = 0.0
+        lse[qi] = -np.inf
+        if Kb.shape[0] == 0:
+            continue
+        t = (sc * s_q * s_k * (q8[qi] @ Kb.T) + lv[None, :] * LN2) / LN2
+        vis = np.broadcast_to(last[None, :] < p.seq_valid, t.shape)
+        if p.causal:
+            vis = vis & (last[None, :] <= qi[:, None])
+        for r in range(qi.size):
+            if qi[r] >= p.seq_valid or not np.any(vis[r]):
+                continue
+            tr = t[r][vis[r]]
+            M = math.ceil(float(np.max(tr)))
+            P8 = e4m3_round(2.0 ** (tr - M))
+            l8 = float(np.sum(P8))
+            o[qi[r]] = s_v * (P8 @ Vb[vis[r]]) / l8
+            lse[qi[r]] = (M + math.log2(l8)) * LN2
+    return o, lse
 
 
 # ----------------------------------------------------------------------------------------

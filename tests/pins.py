@@ -539,3 +539,60 @@ def pin_fp8qk_reduces_to_attention(causal=False):
     same_inf = np.array_equal(np.isfinite(lse), np.isfinite(l8))
     return max(np.nanmax(np.abs(o8 - o)), np.abs(np.where(both, l8 - lse, 0.0)).max(),
                0.0 if same_inf else np.inf)
+
+
+def pin_fp8pv_worked_rows():
+    """Hand-worked rows of attention_fp8_head. Causal, 8 valid tokens, unit query vectors,
+    scale ln 2 and unit q/k scales, so the log2-unit logits are t = k8[:, 0]: key 0 at 0.5,
+    key 1 at 13/64. Query 0 sees key 0 only: M = 1, p = 2^-0.5 = 0.7071 lies between 11/16
+    and 12/16 (e4m3 spacing 1/16 on [1/2, 1)) and rounds to 11/16; one weight, so o = s_v v8[0]
+    and lse = (1 + log2(11/16)) ln 2. Query 1 sees keys 0 and 1: p = (2^-0.5, 2^(13/64 - 1) =
+    0.5756) -> (11/16, 9/16); o = s_v (11/16 v8[0] + 9/16 v8[1]) / (20/16) and
+    lse = (1 + log2(20/16)) ln 2. With v8[0] = e_0, v8[1] = -3 e_1, s_v = 3/4: query 1's o
+    starts (0.4125, -1.0125)."""
+    n, d = 64, 16
+    p = oracle.Problem(seq_len=n, seq_valid=8, head_dim=d, block_q=64, causal=True)
+    q8 = np.zeros((n, d))
+    q8[:, 0] = 1.0
+    k8 = np.zeros((n, d))
+    k8[0, 0], k8[1, 0] = 0.5, 13.0 / 64.0
+    k8[2:8, 0] = -2.0
+    v8 = np.zeros((n, d))
+    v8[0, 0], v8[1, 1] = 1.0, -3.0
+    v8[2:8, 2] = 1.0
+    lm = np.zeros((1, 1), dtype=np.int8)
+    kp = {l: oracle.pool(k8, l) for l in (1, 2, 3)}
+    vp = {l: oracle.pool(v8, l) for l in (1, 2, 3)}
+    o, lse = oracle.attention_fp8_head(q8, k8, kp, v8, vp, 1.0, 1.0, 0.75, lm, p, scale=math.log(2.0))
+    want0 = np.zeros(d)
+    want0[0] = 0.75
+    want1 = np.zeros(d)
+    want1[0], want1[1] = 0.4125, -1.0125
+    errs = [np.abs(o[0] - want0).max(), np.abs(o[1] - want1).max(),
+            abs(lse[0] - (1 + math.log2(11 / 16)) * math.log(2)),
+            abs(lse[1] - (1 + math.log2(20 / 16)) * math.log(2)),
+            np.abs(o[8:]).max(), 0.0 if np.all(np.isneginf(lse[8:])) else 1.0]
+    return float(max(errs))
+
+
+def pin_fp8pv_powers_of_two(causal=False):
+    """Zero queries make every logit l ln 2: the p_j are powers of two, e4m3 holds them exactly,
+    and attention_fp8_head must equal attention_head (pinned above) on the dequantized values
+    v8 * s_v, with mixed levels, padding and (optionally) causal masking."""
+    n, d = 256, 16
+    p = oracle.Problem(seq_len=n, seq_valid=n - 16, head_dim=d, block_q=64, causal=causal)
+    rng = np.random.default_rng(43)
+    k8 = oracle.e4m3_round(rng.normal(0, 4, (n, d)))
+    v8 = oracle.e4m3_round(rng.normal(0, 4, (n, d)))
+    s_v = 0.3
+    lm = rng.choice(np.array([0, 1, 2, 3, -1], dtype=np.int8), size=(p.n_qblocks, p.n_kblocks))
+    lm[:, 0] = 0
+    q8 = np.zeros((n, d))
+    kp = {l: oracle.pool(k8, l) for l in (1, 2, 3)}
+    vp = {l: oracle.pool(v8, l) for l in (1, 2, 3)}
+    o8, l8 = oracle.attention_fp8_head(q8, k8, kp, v8, vp, 0.5, 2.0, s_v, lm, p)
+    o, lse = oracle.attention_head(q8, k8, v8 * s_v, lm, p)
+    both = np.isfinite(lse) & np.isfinite(l8)
+    same_inf = np.array_equal(np.isfinite(lse), np.isfinite(l8))
+    return max(np.nanmax(np.abs(o8 - o)), np.abs(np.where(both, l8 - lse, 0.0)).max(),
+               0.0 if same_inf else np.inf)

@@ -144,3 +144,12 @@ def test_pfp8_scale():
 @pytest.mark.parametrize("causal", [False, True])
 def test_pfp8_qk_reduces_to_attention(causal):
     assert pins.pin_fp8qk_reduces_to_attention(causal) < 1e-12
+
+
+def test_pfp8_pv_worked_rows():
+    assert pins.pin_fp8pv_worked_rows() < 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_pfp8_pv_powers_of_two(causal):
+    assert pins.pin_fp8pv_powers_of_two(causal) < 1e-12

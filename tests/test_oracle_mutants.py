@@ -39,6 +39,7 @@ ALL_PINS = {
     "pbwd_runs": lambda: max(pins.pin_bwd_constant_runs(l) for l in (1, 3)),
     "pfp8": lambda: max(pins.pin_e4m3_round(), pins.pin_fp8_scale(),
                         pins.pin_fp8qk_reduces_to_attention(True)),
+    "pfp8pv": lambda: max(pins.pin_fp8pv_worked_rows(), pins.pin_fp8pv_powers_of_two(True)),
 }
 
 
@@ -84,6 +85,10 @@ MUTANTS = [
     ("e4m3_four_mantissa_bits", "q = 2.0 ** (e - 3.0)", "q = 2.0 ** (e - 4.0)"),
     ("fp8_scale_unscaled", "return _attention_from_levels(q8, lk, lvv, level_map, p, sc * s_q * s_k, qblocks)",
      "return _attention_from_levels(q8, lk, lvv, level_map, p, sc * s_q, qblocks)"),
+    ("fp8pv_p_unquantized", "P8 = e4m3_round(2.0 ** (tr - M))", "P8 = 2.0 ** (tr - M)"),
+    ("fp8pv_sum_unquantized", "l8 = float(np.sum(P8))", "l8 = float(np.sum(2.0 ** (tr - M)))"),
+    ("fp8pv_reference_not_integer", "M = math.ceil(float(np.max(tr)))", "M = float(np.max(tr))"),
+    ("fp8pv_v_unscaled", "o[qi[r]] = s_v * (P8 @ Vb[vis[r]]) / l8", "o[qi[r]] = (P8 @ Vb[vis[r]]) / l8"),
     ("index_descending", "sel = [kb for kb in range(nkb) if rows[r, kb] == l]",
      "sel = [kb for kb in reversed(range(nkb)) if rows[r, kb] == l]"),
 ]
