@@ -12,13 +12,13 @@
  *   psa_attn_fwd       - the level-weighted flash-style attention;
  *   psa_attn_bwd       - its backward (dq, dk, dv through every pyramid level).
  * plus psa_mask_assign and psa_build_index, the mask's and the attention's integer stages,
- * exported on their own, and psa_quantize_fp8 / psa_attn_fwd_fp8qk, the forward with its
- * q . k products on e4m3 operands.
+ * exported on their own, and psa_quantize_fp8 / psa_attn_fwd_fp8qk / psa_attn_fwd_fp8, the
+ * forward with its q . k products (and its P V product) on e4m3 operands.
  *
  * Conventions shared by every call
  *  - Pointers named q, k, v, o, k_pooled, v_pooled, level_map, block_mass, block_sim, lse,
- *    row_ptr, col_idx, dev_err, dout, dq, dk, dv, x, x_pooled, q8, k8, k8_pooled, x8,
- *    x8_pooled, scale, q_scale, k_scale and ws are DEVICE pointers owned by the
+ *    row_ptr, col_idx, dev_err, dout, dq, dk, dv, x, x_pooled, q8, k8, k8_pooled, v8,
+ *    v8_pooled, x8, x8_pooled, scale, q_scale, k_scale, v_scale and ws are DEVICE pointers owned by the
  *    caller; the library never allocates or frees device memory and keeps no state between
  *    calls. psa_problem, psa_mask_params and x_stride are HOST pointers, read during the call
  *    only.
@@ -255,6 +255,27 @@ int psa_attn_fwd_fp8qk(const psa_problem* prob, float softmax_scale, const uint8
                        const float* k_scale, const void* v, const void* v_pooled,
                        const int8_t* level_map, void* o, float* lse, void* ws, size_t ws_bytes,
                        void* stream);
+
+/*
+ * psa_attn_fwd_fp8qk with the P V product on e4m3 operands as well (paper abstract and news
+ * summary, "Practical"): v8 and v8_pooled are psa_quantize_fp8's codes of V and of
+ * psa_build_pyramid's v_pooled (one scale v_scale per KV head), contiguous like k8 and
+ * k8_pooled. For each valid query, in log2 units t_j = z_j / ln 2 (z_j as in
+ * psa_attn_fwd_fp8qk), with M an integer no less than max_j t_j - 8 (the kernel's running
+ * maximum, rounded up to an integer):
+ *   P8_j = e4m3(2^(t_j - M)) (round to nearest even),
+ *   o = v_scale * sum_j P8_j v8_j / sum_j P8_j,   lse = (M + log2 sum_j P8_j) ln 2.
+ * e4m3 rounding commutes with the power-of-two change of M except for values in e4m3's
+ * subnormal range, so the result depends on the running maximum only at that level. Both
+ * products run on v_mfma_f32_32x32x64_f8f6f4 with float32 accumulation (the sum of P8 by a
+ * ones-row product). head_dim 128, dtype PSA_BF16 (o) only; anything else returns
+ * PSA_ERR_UNSUPPORTED. Workspace: psa_attn_workspace_bytes.
+ */
+int psa_attn_fwd_fp8(const psa_problem* prob, float softmax_scale, const uint8_t* q8,
+                     const float* q_scale, const uint8_t* k8, const uint8_t* k8_pooled,
+                     const float* k_scale, const uint8_t* v8, const uint8_t* v8_pooled,
+                     const float* v_scale, const int8_t* level_map, void* o, float* lse, void* ws,
+                     size_t ws_bytes, void* stream);
 
 /* Device workspace psa_attn_bwd needs; 0 on a bad problem. */
 size_t psa_attn_bwd_workspace_bytes(const psa_problem* prob);

@@ -530,12 +530,14 @@ def attention_fp8_head(q8: np.ndarray, k8: np.ndarray, kp8_levels: Dict[int, np.
     "Practical": FP8 arithmetic on the block-tile kernel; the pages give no recipe). V and its
     pooled levels are e4m3 values with one scale s_v per head (v8 stands for v8 * s_v). For
     each valid query, in log2 units t_j = z_j / ln 2 (z_j as in attention_fp8qk_head):
-      M = ceil(max_j t_j), an integer;  p_j = 2^(t_j - M) in (0, 1];  P8_j = e4m3(p_j);
-      o = s_v * sum_j P8_j v8_j / sum_j P8_j;  lse = (M + log2 sum_j P8_j) * ln 2.
-    The weights that multiply V are the quantized P8_j, normalised by their own sum. An
-    integer reference keeps P8 independent of which integer is used, as long as the values
-    stay in e4m3's normal range (rounding commutes with scaling by a power of two). Rows with
-    no visible key and pad rows give o = 0 and lse = -inf."""
+      M = ceil(max_j t_j), an integer;  P8_j = e4m3(2^(t_j - M + 7));
+      o = s_v * sum_j P8_j v8_j / sum_j P8_j;  lse = (M - 7 + log2 sum_j P8_j) * ln 2.
+    The weights that multiply V are the quantized P8_j, normalised by their own sum. The
+    reference 2^(M - 7) puts the largest weight in (64, 128], so every weight down to 2^-13 of
+    it stays in e4m3's normal range (>= 2^-6; below, the subnormal spacing 2^-9 would cost
+    relative precision). Rounding commutes with scaling by a power of two in the normal range,
+    so any integer reference between M - 8 and M - 7 gives the same codes there. Rows with no
+    visible key and pad rows give o = 0 and lse = -inf."""
     sc = p.scale if scale is None else scale
     lk = {0: k8}
     lk.update(kp8_levels)
@@ -560,10 +562,10 @@ def attention_fp8_head(q8: np.ndarray, k8: np.ndarray, kp8_levels: Dict[int, np.
                 continue
             tr = t[r][vis[r]]
             M = math.ceil(float(np.max(tr)))
-            P8 = e4m3_round(2.0 ** (tr - M))
+            P8 = e4m3_round(2.0 ** (tr - M + 7))
             l8 = float(np.sum(P8))
             o[qi[r]] = s_v * (P8 @ Vb[vis[r]]) / l8
-            lse[qi[r]] = (M + math.log2(l8)) * LN2
+            lse[qi[r]] = (M - 7 + math.log2(l8)) * LN2
     return o, lse
 
 

@@ -544,12 +544,15 @@ def pin_fp8qk_reduces_to_attention(causal=False):
 def pin_fp8pv_worked_rows():
     """Hand-worked rows of attention_fp8_head. Causal, 8 valid tokens, unit query vectors,
     scale ln 2 and unit q/k scales, so the log2-unit logits are t = k8[:, 0]: key 0 at 0.5,
-    key 1 at 13/64. Query 0 sees key 0 only: M = 1, p = 2^-0.5 = 0.7071 lies between 11/16
-    and 12/16 (e4m3 spacing 1/16 on [1/2, 1)) and rounds to 11/16; one weight, so o = s_v v8[0]
-    and lse = (1 + log2(11/16)) ln 2. Query 1 sees keys 0 and 1: p = (2^-0.5, 2^(13/64 - 1) =
-    0.5756) -> (11/16, 9/16); o = s_v (11/16 v8[0] + 9/16 v8[1]) / (20/16) and
+    key 1 at 13/64. Query 0 sees key 0 only: M = 1, 2^(0.5 - 1 + 7) = 90.51 lies between 88 and
+    96 (e4m3 spacing 8 on [64, 128)) and rounds to 88; one weight, so o = s_v v8[0] and
+    lse = (1 - 7 + log2 88) ln 2 = (1 + log2(11/16)) ln 2. Query 1 sees keys 0 and 1:
+    (2^6.5, 2^(13/64 + 6) = 73.67) -> (88, 72); o = s_v (88 v8[0] + 72 v8[1]) / 160 and
     lse = (1 + log2(20/16)) ln 2. With v8[0] = e_0, v8[1] = -3 e_1, s_v = 3/4: query 1's o
-    starts (0.4125, -1.0125)."""
+    starts (0.4125, -1.0125). A second row puts key 1 at -6.5: 2^(-6.5 - 1 + 7) = 0.7071 rounds
+    to 11/16 (spacing 1/16 on [1/2, 1)), so o = s_v (88 v8[0] + 11/16 v8[1]) / (88 + 11/16);
+    relative to 2^M instead of 2^(M - 7) that weight, 2^-7.5, would fall in e4m3's subnormal
+    range and round to 3 * 2^-9."""
     n, d = 64, 16
     p = oracle.Problem(seq_len=n, seq_valid=8, head_dim=d, block_q=64, causal=True)
     q8 = np.zeros((n, d))
@@ -572,6 +575,11 @@ def pin_fp8pv_worked_rows():
             abs(lse[0] - (1 + math.log2(11 / 16)) * math.log(2)),
             abs(lse[1] - (1 + math.log2(20 / 16)) * math.log(2)),
             np.abs(o[8:]).max(), 0.0 if np.all(np.isneginf(lse[8:])) else 1.0]
+    k8[1, 0] = -6.5
+    o, lse = oracle.attention_fp8_head(q8, k8, kp, v8, vp, 1.0, 1.0, 0.75, lm, p, scale=math.log(2.0))
+    want1 = np.zeros(d)
+    want1[0], want1[1] = 0.75 * 88 / 88.6875, 0.75 * (-3) * 0.6875 / 88.6875
+    errs += [np.abs(o[1] - want1).max(), abs(lse[1] - (1 - 7 + math.log2(88.6875)) * math.log(2))]
     return float(max(errs))
 
 

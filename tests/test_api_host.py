@@ -206,3 +206,25 @@ def test_attn_fwd_fp8qk_host_checks():
     assert call(p) == P.PSA_ERR_UNSUPPORTED
     p64 = _prob(dtype=P.PSA_BF16)                      # head_dim 64: no fp8 kernel
     assert call(p64, n=1 << 30) == P.PSA_ERR_UNSUPPORTED
+
+
+def test_attn_fwd_fp8_host_checks():
+    L = psa.lib()
+    d = ctypes.c_void_p(256)
+    names = ("q8", "qs", "k8", "kp8", "ks", "v8", "vp8", "vs", "map", "o", "lse", "ws")
+    args = lambda **o: [o.get(n, d) for n in names]
+    q = torch.zeros(1, 2, 1024, 128)
+    p = psa.make_problem(q, q, q, block_q=64)
+    p.c.dtype = P.PSA_BF16
+    need = L.psa_attn_workspace_bytes(p.ref())
+    call = lambda prob, n=need, sc=0.0, **o: L.psa_attn_fwd_fp8(prob.ref(), sc, *args(**o), n, None)
+    assert call(p, n=need - 1) == P.PSA_ERR_WORKSPACE
+    assert call(p, ws=None) == P.PSA_ERR_WORKSPACE
+    for name in ("q8", "qs", "k8", "kp8", "ks", "v8", "vp8", "vs", "map", "o"):
+        assert call(p, **{name: None}) == P.PSA_ERR_INVALID_ARG, name
+    assert call(p, v8=ctypes.c_void_p(264)) == P.PSA_ERR_INVALID_ARG
+    assert call(p, vs=ctypes.c_void_p(258)) == P.PSA_ERR_INVALID_ARG
+    assert call(p, sc=float("nan")) == P.PSA_ERR_INVALID_ARG
+    p.c.dtype = P.PSA_F32
+    assert call(p) == P.PSA_ERR_UNSUPPORTED
+    assert call(_prob(dtype=P.PSA_BF16), n=1 << 30) == P.PSA_ERR_UNSUPPORTED   # head_dim 64

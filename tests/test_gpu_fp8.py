@@ -338,3 +338,173 @@ def test_fp8qk_fullsize_wan():
         assert mx <= 2e-2 and rel <= 5e-3 and ld <= 3e-2
         pad = rows[rows >= wl.seq_valid]
         assert torch.count_nonzero(o[0, h, pad]).item() == 0
+
+
+# ---------------------------------------------------------------------------------------
+# attention with the P V product on e4m3 operands as well
+# ---------------------------------------------------------------------------------------
+# Bars. P is rounded to e4m3 on both sides from values computed in different precisions (fp32
+# logits and exp2 on the GPU, fp64 in the oracle); a value within rounding of an e4m3 midpoint
+# can land on either neighbouring code. One code step moves that weight w_j by at most w_j / 8,
+# so o_i by at most w_j / 8 * |v_j - o_i| and the lse by at most ln(1 + 1/8) = 0.118. Such
+# flips are sparse (a pair's value must lie within ~2^-22 relative of a midpoint), so the
+# relative L2 bar stays that of bf16 (5e-3); max-abs allows a flip on a key of weight 0.05
+# at |v_j - o_i| = 8 (N(0,1) values): 5e-2; lse 0.125.
+FP8PV_MAX_ABS = 5e-2
+FP8PV_REL_L2 = 5e-3
+FP8PV_LSE = 0.125
+
+
+def check_fp8pv(o, lse, o_ref, lse_ref, nv, what):
+    a = o[..., :nv, :].double().cpu().numpy()
+    r = o_ref[..., :nv, :]
+    mx = float(np.abs(a - r).max())
+    rel = float(np.linalg.norm(a - r) / np.linalg.norm(r))
+    lg = lse[..., :nv].double().cpu().numpy()
+    lr = lse_ref[..., :nv]
+    assert np.array_equal(np.isneginf(lg), np.isneginf(lr)), f"{what}: empty-row sets differ"
+    ld = float(np.abs(np.where(np.isneginf(lr), 0.0, lg - lr)).max(initial=0.0))
+    print(f"[{what}] max_abs={mx:.3e} rel_l2={rel:.3e} lse={ld:.3e}", flush=True)
+    assert mx <= FP8PV_MAX_ABS and rel <= FP8PV_REL_L2 and ld <= FP8PV_LSE, what
+    assert torch.count_nonzero(o[..., nv:, :]).item() == 0, f"{what}: non-zero pad rows"
+def _oracle_v_fp8(wl, v):
+    """Per-KV-head oracle quantization of V and its pooled levels (the pyramid's bf16 means)."""
+    B, Hkv = wl.batch, wl.heads_kv
+    sv = np.zeros((B, Hkv))
+    v8 = np.zeros(v.shape)
+    vp8 = [[None] * Hkv for _ in range(B)]
+    for b in range(B):
+        for h in range(Hkv):
+            sv[b, h], v8[b, h], vp8[b][h] = oracle_head_fp8(oracle.as_f64(v[b, h]))
+    return sv, v8, vp8
+
+
+def _oracle_fp8pv_attention(wl, q8, sq, k8, kp8, sk, v8, vp8, sv, lm, qblocks=None, heads=None):
+    p = oracle_problem(wl)
+    g = wl.group
+    o = np.zeros(q8.shape)
+    lse = np.zeros(q8.shape[:3])
+    for b in range(wl.batch):
+        for h in (range(wl.heads_q) if heads is None else heads):
+            hk = h // g
+            o[b, h], lse[b, h] = oracle.attention_fp8_head(
+                q8[b, h], k8[b, hk], kp8[b][hk], v8[b, hk], vp8[b][hk], sq[b, h], sk[b, hk],
+                sv[b, hk], lm[b, h], p, qblocks=qblocks)
+    return o, lse
+
+
+def _packed_levels(wl, levels):
+    return np.stack([np.stack([pack_levels(levels[b][h]) for h in range(wl.heads_kv)])
+                     for b in range(wl.batch)])
+
+
+@pytest.mark.parametrize("wl", ATTN, ids=[w.name for w in ATTN])
+def test_fp8_kernel_parity(wl):
+    """The fp8 Q K^T + P V kernel on the oracle's own e4m3 codes and scales."""
+    announce(f"fp8 kernel {wl.name}")
+    q, k, v = W.make_qkv(wl)
+    lm = oracle_map(wl, q, k)
+    sq, q8, sk, k8, kp8 = _oracle_fp8_inputs(wl, q, k)
+    sv, v8, vp8 = _oracle_v_fp8(wl, v)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    prob = problem_for(wl, qd, kd, vd)
+    up = lambda x: torch.from_numpy(np.ascontiguousarray(x).ravel()).float().to(DEV)
+    o, lse = psa.attn_fwd_fp8(encode(q8).to(DEV), up(sq), encode(k8).to(DEV),
+                              encode(_packed_levels(wl, kp8)).to(DEV), up(sk), encode(v8).to(DEV),
+                              encode(_packed_levels(wl, vp8)).to(DEV), up(sv),
+                              torch.from_numpy(lm).to(DEV), prob)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = _oracle_fp8pv_attention(wl, q8, sq, k8, kp8, sk, v8, vp8, sv, lm)
+    check_fp8pv(o, lse, o_ref, lse_ref, wl.seq_valid, f"{wl.name} fp8 kernel")
+
+
+def _gpu_fp8pv_path(qd, kd, vd, lm_dev, prob):
+    kp, vp = psa.build_pyramid(kd, vd, prob)
+    k8, kp8, sk = psa.quantize_fp8(kd, kp)
+    v8, vp8, sv = psa.quantize_fp8(vd, vp)
+    q8, _, sq = psa.quantize_fp8(qd)
+    o, lse = psa.attn_fwd_fp8(q8, sq, k8, kp8, sk, v8, vp8, sv, lm_dev, prob)
+    return o, lse
+
+
+@pytest.mark.parametrize("wl", ATTN, ids=[w.name for w in ATTN])
+def test_fp8_path_parity(wl):
+    """Pyramid, quantization of Q, K and V, and the fp8 attention on the GPU against the
+    oracle's fp8 reading of the same bf16 inputs."""
+    announce(f"fp8 path {wl.name}")
+    q, k, v = W.make_qkv(wl)
+    lm = oracle_map(wl, q, k)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    prob = problem_for(wl, qd, kd, vd)
+    o, lse = _gpu_fp8pv_path(qd, kd, vd, torch.from_numpy(lm).to(DEV), prob)
+    torch.cuda.synchronize()
+    sq, q8, sk, k8, kp8 = _oracle_fp8_inputs(wl, q, k)
+    sv, v8, vp8 = _oracle_v_fp8(wl, v)
+    o_ref, lse_ref = _oracle_fp8pv_attention(wl, q8, sq, k8, kp8, sk, v8, vp8, sv, lm)
+    check_fp8pv(o, lse, o_ref, lse_ref, wl.seq_valid, f"{wl.name} fp8 path")
+    o_exact, _ = oracle.attention(q, k, v, lm, oracle_problem(wl))
+    n = wl.seq_valid
+    a = o[..., :n, :].double().cpu().numpy()
+    rel = np.linalg.norm(a - o_exact[..., :n, :]) / np.linalg.norm(o_exact[..., :n, :])
+    print(f"[{wl.name}] fp8 Q K^T and P V vs exact attention: rel L2 {rel:.3e}", flush=True)
+    assert rel < 0.12
+
+
+def test_fp8_deterministic_and_rejects_d64():
+    announce("fp8 determinism, d64 rejected")
+    wl = W.small(W.QWEN25VL_32K)
+    q, k, v = W.make_qkv(wl)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    lm = torch.from_numpy(W.make_map(wl.replace(map_source="iid",
+                                                map_probs=(.3, .2, .2, .1, .2)))).to(DEV)
+    prob = problem_for(wl, qd, kd, vd)
+    r1 = _gpu_fp8pv_path(qd, kd, vd, lm, prob)
+    r2 = _gpu_fp8pv_path(qd, kd, vd, lm, prob)
+    assert all(torch.equal(a, b) for a, b in zip(r1, r2))
+    wl64 = W.small(W.COGVIDEOX5B_17K)
+    q, k, v = W.make_qkv(wl64)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    prob = problem_for(wl64, qd, kd, vd)
+    lm64 = torch.from_numpy(W.make_map(wl64.replace(map_source="iid",
+                                                    map_probs=(.3, .2, .2, .1, .2)))).to(DEV)
+    with pytest.raises(psa.PsaError) as ei:
+        _gpu_fp8pv_path(qd, kd, vd, lm64, prob)
+    assert ei.value.status == psa.psa.PSA_ERR_UNSUPPORTED
+
+
+def test_fp8_fullsize_wan():
+    """The fp8 Q K^T + P V path on the full Wan2.1-1.3B-like 32k layer with the mask's own
+    map; sampled heads and query blocks against the oracle's fp8 reading on the GPU map rows."""
+    wl = W.WAN13B_32K
+    announce(f"fp8 full size {wl.name}")
+    from gpu_util import mask_params
+    q, k, v = W.make_qkv(wl)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    prob = problem_for(wl, qd, kd, vd)
+    lm, _, _ = psa.mask(qd, kd, prob, mask_params(wl))
+    o, lse = _gpu_fp8pv_path(qd, kd, vd, lm, prob)
+    torch.cuda.synchronize()
+    lm = lm.cpu().numpy()
+    p = oracle_problem(wl)
+    n = wl.n_qblocks
+    rng = np.random.default_rng(wl.seed + 1)
+    for h in (0, wl.heads_q - 1):
+        qh, kh, vh = (oracle.as_f64(t[0, h]) for t in (q, k, v))
+        s_q = oracle.fp8_scale(qh)
+        s_k, k8h, kp8h = oracle_head_fp8(kh)
+        s_v, v8h, vp8h = oracle_head_fp8(vh)
+        qbs = sorted({0, n // 2, n - 1, int(rng.integers(1, n - 1))})
+        o_ref, lse_ref = oracle.attention_fp8_head(oracle.fp8_quantize(qh, s_q), k8h, kp8h, v8h,
+                                                   vp8h, s_q, s_k, s_v, lm[0, h], p, qblocks=qbs)
+        rows = np.concatenate([np.arange(qb * wl.block_q, (qb + 1) * wl.block_q) for qb in qbs])
+        valid = rows[rows < wl.seq_valid]
+        og = o[0, h, valid].double().cpu().numpy()
+        d = og - o_ref[valid]
+        rel = np.linalg.norm(d) / np.linalg.norm(o_ref[valid])
+        mx = np.abs(d).max()
+        ld = np.abs(lse[0, h, valid].double().cpu().numpy() - lse_ref[valid]).max()
+        print(f"[{wl.name}] fp8 head {h} blocks {qbs}: max_abs={mx:.3e} rel_l2={rel:.3e} "
+              f"lse={ld:.3e}", flush=True)
+        assert mx <= FP8PV_MAX_ABS and rel <= FP8PV_REL_L2 and ld <= FP8PV_LSE
+        pad = rows[rows >= wl.seq_valid]
+        assert torch.count_nonzero(o[0, h, pad]).item() == 0

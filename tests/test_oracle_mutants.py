@@ -85,8 +85,9 @@ MUTANTS = [
     ("e4m3_four_mantissa_bits", "q = 2.0 ** (e - 3.0)", "q = 2.0 ** (e - 4.0)"),
     ("fp8_scale_unscaled", "return _attention_from_levels(q8, lk, lvv, level_map, p, sc * s_q * s_k, qblocks)",
      "return _attention_from_levels(q8, lk, lvv, level_map, p, sc * s_q, qblocks)"),
-    ("fp8pv_p_unquantized", "P8 = e4m3_round(2.0 ** (tr - M))", "P8 = 2.0 ** (tr - M)"),
-    ("fp8pv_sum_unquantized", "l8 = float(np.sum(P8))", "l8 = float(np.sum(2.0 ** (tr - M)))"),
+    ("fp8pv_p_unquantized", "P8 = e4m3_round(2.0 ** (tr - M + 7))", "P8 = 2.0 ** (tr - M + 7)"),
+    ("fp8pv_sum_unquantized", "l8 = float(np.sum(P8))", "l8 = float(np.sum(2.0 ** (tr - M + 7)))"),
+    ("fp8pv_reference_at_max", "P8 = e4m3_round(2.0 ** (tr - M + 7))", "P8 = e4m3_round(2.0 ** (tr - M)) * 128.0"),
     ("fp8pv_reference_not_integer", "M = math.ceil(float(np.max(tr)))", "M = float(np.max(tr))"),
     ("fp8pv_v_unscaled", "o[qi[r]] = s_v * (P8 @ Vb[vis[r]]) / l8", "o[qi[r]] = (P8 @ Vb[vis[r]]) / l8"),
     ("index_descending", "sel = [kb for kb in range(nkb) if rows[r, kb] == l]",

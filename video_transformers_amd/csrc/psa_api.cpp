@@ -326,6 +326,36 @@ int psa_attn_fwd_fp8qk(const psa_problem* prob, float softmax_scale, const uint8
                                                  v_pooled, w.row_ptr, w.col_idx, o, lse, st));
 }
 
+int psa_attn_fwd_fp8(const psa_problem* prob, float softmax_scale, const uint8_t* q8,
+                     const float* q_scale, const uint8_t* k8, const uint8_t* k8_pooled,
+                     const float* k_scale, const uint8_t* v8, const uint8_t* v8_pooled,
+                     const float* v_scale, const int8_t* level_map, void* o, float* lse, void* ws,
+                     size_t ws_bytes, void* stream) {
+    psa::Shape s;
+    int rc = check_problem(prob, &s);
+    if (rc != PSA_OK) return rc;
+    if (s.dtype != PSA_BF16 || s.D != 128) return PSA_ERR_UNSUPPORTED;
+    if (!q8 || !q_scale || !k8 || !k8_pooled || !k_scale || !v8 || !v8_pooled || !v_scale ||
+        !level_map || !o)
+        return PSA_ERR_INVALID_ARG;
+    if (!aligned16(q8) || !aligned16(k8) || !aligned16(k8_pooled) || !aligned16(v8) ||
+        !aligned16(v8_pooled) || !aligned16(o) || (reinterpret_cast<uintptr_t>(q_scale) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(k_scale) & 3u) != 0 || (reinterpret_cast<uintptr_t>(v_scale) & 3u) != 0)
+        return PSA_ERR_INVALID_ARG;
+    if (!std::isfinite(softmax_scale)) return PSA_ERR_INVALID_ARG;
+    const size_t need = attn_ws_layout(s, nullptr).bytes;
+    if (ws == nullptr || ws_bytes < need) return PSA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return PSA_ERR_WORKSPACE;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(s.D));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    AttnWs w = attn_ws_layout(s, ws);
+    psa::IndexBufs ib{w.row_ptr, w.col_idx, w.dev_err};
+    hipError_t e = psa::launch_build_index(s, level_map, ib, st);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(psa::launch_attn_fwd_fp8(s, scale, q8, q_scale, k8, k8_pooled, k_scale, v8,
+                                               v8_pooled, v_scale, w.row_ptr, w.col_idx, o, lse, st));
+}
+
 size_t psa_attn_bwd_workspace_bytes(const psa_problem* prob) {
     psa::Shape s;
     if (check_problem(prob, &s) != PSA_OK) return 0;

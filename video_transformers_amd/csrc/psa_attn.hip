@@ -246,6 +246,7 @@ AttnArgs make_args(const Shape& s, float scale, const void* q, const void* k, co
     a.c = scale * kLog2e;
     a.q_scale = nullptr;
     a.k_scale = nullptr;
+    a.v_scale = nullptr;
     return a;
 }
 
@@ -284,6 +285,24 @@ hipError_t launch_attn_fwd_fp8qk(const Shape& s, float scale, const uint8_t* q8,
     a.q_scale = q_scale;
     a.k_scale = k_scale;
     return launch_attn_fp8qk(s, a, st);
+}
+
+hipError_t launch_attn_fwd_fp8(const Shape& s, float scale, const uint8_t* q8, const float* q_scale,
+                               const uint8_t* k8, const uint8_t* kp8, const float* k_scale,
+                               const uint8_t* v8, const uint8_t* vp8, const float* v_scale,
+                               const int32_t* row_ptr, const int32_t* col_idx, void* o, float* lse,
+                               hipStream_t st) {
+    if (s.dtype != PSA_BF16) return hipErrorNotSupported;
+    AttnArgs a = make_args(s, scale, q8, k8, v8, kp8, vp8, row_ptr, col_idx, o, lse);
+    // every e4m3 operand is contiguous [batch, head, token, head_dim] bytes
+    const int64_t nd = static_cast<int64_t>(s.N) * s.D;
+    a.qs0 = s.H * nd; a.qs1 = nd; a.qs2 = s.D;
+    a.ks0 = s.Hkv * nd; a.ks1 = nd; a.ks2 = s.D;
+    a.vs0 = s.Hkv * nd; a.vs1 = nd; a.vs2 = s.D;
+    a.q_scale = q_scale;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    return launch_attn_fp8(s, a, st);
 }
 
 }  // namespace psa

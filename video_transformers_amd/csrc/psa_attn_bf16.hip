@@ -65,27 +65,37 @@ struct Tile {
 // PACK: a tile packs 2^l logical blocks of level l (the decoupled block-tile). Without it
 // every tile holds one logical block and its other rows are masked: the naive layout, kept
 // as the ablation baseline the packing is measured against.
-// F8: Q and K (level 0 and pooled) are e4m3 bytes with one scale per (batch, head); S comes
-// from v_mfma_f32_32x32x64_f8f6f4 (A: lane l holds row l % 32, bytes 32 * (l / 32) + 0..31 of
-// the 64-wide k-step; B likewise per column; C as in the bf16 product). A K row of D bytes has
-// the byte layout of a bf16 row of D / 2 elements and travels with that layout's direct loads
-// and swizzle; P, V and O stay bf16.
-template <int D, int BQ, bool CONTIG, bool PACK, bool F8>
+// FP8 >= 1: Q and K (level 0 and pooled) are e4m3 bytes with one scale per (batch, head); S
+// comes from v_mfma_f32_32x32x64_f8f6f4 (A: lane l holds row l % 32, bytes 32 * (l / 32) + 0..31
+// of the 64-wide k-step; B likewise per column; C as in the bf16 product). A K row of D bytes
+// has the byte layout of a bf16 row of D / 2 elements and travels with that layout's direct
+// loads and swizzle.
+// FP8 == 2: V is e4m3 too (one scale per (batch, KV head)) and P is quantized to e4m3 for an
+// fp8 P V product over whole 64-key tiles (see the fp8 P V pipeline below). Otherwise P, V and
+// O stay bf16.
+template <int D, int BQ, bool CONTIG, bool PACK, int FP8>
 __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int total_rows) {
+    constexpr bool F8 = FP8 >= 1;
+    constexpr bool PV8 = FP8 == 2;
     constexpr int NW = BQ / 32;
-    using LY = Lay<D>;                   // V tiles (and K tiles in bf16)
+    using LY = Lay<D>;                   // bf16 V tiles (and K tiles in bf16)
     using KL = Lay<F8 ? D / 2 : D>;      // K tiles
+    using VL = Lay<PV8 ? D / 2 : D>;     // V tiles
     constexpr int EK = F8 ? 1 : 2;       // bytes per K element
+    constexpr int EV = PV8 ? 1 : 2;      // bytes per V element
     constexpr int RBK = D * EK;          // bytes per K row
+    constexpr int RBV = D * EV;          // bytes per V row
     constexpr int KK = D / 16;           // pipeline slots per step (k-steps of the bf16 S product)
     constexpr int KS = F8 ? D / 64 : KK; // k-steps of the S product
     constexpr int KSL = KK / KS;         // slots per k-step
     constexpr int DB = D / 32;           // 32-wide d blocks of the O product
     using KT = std::conditional_t<F8, uint8_t, bf16_bits>;
+    using VT = std::conditional_t<PV8, uint8_t, bf16_bits>;
     using KOp = std::conditional_t<F8, i32x8, bf16x8>;   // one lane's S operand of a k-step
     static_assert(!F8 || D == 128, "fp8 K rows of 128 bytes");
     __shared__ __attribute__((aligned(1024))) uint8_t Kt[2][64 * RBK];
-    __shared__ __attribute__((aligned(1024))) bf16_bits Vt[2][64 * D];
+    // bf16: a ring of four 32-row V slots; fp8 P V: three 64-row V tiles
+    __shared__ __attribute__((aligned(1024))) uint8_t Vt[PV8 ? 3 * 64 * RBV : 2 * 64 * RBV];
     extern __shared__ int cols[];   // the row's block list (LDS reads do not wait on vmcnt)
 
     const int tid = threadIdx.x;
@@ -106,9 +116,9 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
 
     const KT* __restrict__ Q = static_cast<const KT*>(a.q);
     const KT* __restrict__ K = static_cast<const KT*>(a.k);
-    const bf16_bits* __restrict__ V = static_cast<const bf16_bits*>(a.v);
+    const VT* __restrict__ V = static_cast<const VT*>(a.v);
     const KT* __restrict__ KP = static_cast<const KT*>(a.kp);
-    const bf16_bits* __restrict__ VP = static_cast<const bf16_bits*>(a.vp);
+    const VT* __restrict__ VP = static_cast<const VT*>(a.vp);
 
     // ---- the row's block list -> LDS ----
     const int32_t* rp = a.row_ptr + static_cast<int64_t>(row) * 4;
@@ -141,6 +151,13 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[i][e] = 0.f;
     float m_use = -INFINITY, l_run = 0.f;
+    // fp8 P V only: the row sums of the quantized P, from a ones-row MFMA (every register of a
+    // lane holds its query's sum), and the fp32 P of a tile's first half, kept until the tile's
+    // P V product
+    f32x16 lacc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) lacc[e] = 0.f;
+    float pAf[16];
 
     const int64_t kbase = b * a.ks0 + hk * a.ks1;
     const int64_t vbase = b * a.vs0 + hk * a.vs1;
@@ -168,6 +185,12 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
         return n;
     };
 
+    // V tile chunk swizzle. bf16: fv, for the 16-bit transposed reads. fp8: 2 ((r >> 1) & 3):
+    // a 16-lane 8-bit transposed read covers 8 aligned rows x 16 bytes (two chunk columns), and
+    // with this swizzle the 32 lanes of a read pass (8 rows x 2 chunks x 2 halves) land on 64
+    // distinct banks. Within a direct-load instruction (8 rows) it depends on the row only
+    // through r mod 8.
+    auto vswz = [](int r) { return PV8 ? 2 * ((r >> 1) & 3) : LY::fv(r); };
     // Direct loads of one tensor of tile t. Instruction m of the tile covers RPI consecutive
     // tile rows; a wave issues ipw consecutive instructions. Logical blocks hold 8 rows or
     // more, so every run of 8 rows (an aligned group of 8 / RPI instructions) lies in one
@@ -177,10 +200,11 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
     // then loop invariants, and no per-instruction address work remains but the LDS
     // destination in M0. K and V differ in rows per instruction (KL, LY) when K is fp8.
     constexpr int KVAR = KL::CH == 16 ? 4 : 2;   // distinct K chunk swizzles across instructions
+    constexpr int VROWS = PV8 ? 64 : 32;          // rows per V load: a whole tile (fp8) or a half
     constexpr int IPWK = 64 / KL::RPI / NW;       // K instructions per wave per tile
-    constexpr int IPWV = 32 / LY::RPI / NW;       // V instructions per wave per half tile
+    constexpr int IPWV = VROWS / VL::RPI / NW;    // V instructions per wave per V load
     constexpr int IPGK = 8 / KL::RPI;             // instructions per 8-row group (K)
-    constexpr int IPGV = 8 / LY::RPI;             // instructions per 8-row group (V)
+    constexpr int IPGV = 8 / VL::RPI;             // instructions per 8-row group (V)
     static_assert(IPWK % KVAR == 0, "instruction m and its index inside the wave agree mod KVAR");
     static_assert(IPGK >= 1 && IPWK % IPGK == 0 && IPWV % IPGV == 0 && IPWK / IPGK <= 4, "direct-load groups");
     constexpr int NSTR = CONTIG ? 1 : 2;          // lane offset sets: pooled stride (and level 0)
@@ -188,23 +212,23 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
     {
         const int rk = lane / KL::CH;   // row inside the instruction
         const int pk = lane % KL::CH;   // LDS chunk position
-        const int rv = lane / LY::CH;
-        const int pv = lane % LY::CH;
+        const int rv = lane / VL::CH;
+        const int pv = lane % VL::CH;
 #pragma unroll
         for (int i = 0; i < NSTR; ++i) {
             const uint32_t sk = (i == 1 ? static_cast<uint32_t>(a.ks2) : static_cast<uint32_t>(D)) * EK;
-            const uint32_t sv = i == 1 ? static_cast<uint32_t>(a.vs2) * 2u : static_cast<uint32_t>(D) * 2u;
+            const uint32_t sv = (i == 1 ? static_cast<uint32_t>(a.vs2) : static_cast<uint32_t>(D)) * EV;
 #pragma unroll
             for (int mi = 0; mi < IPWK; ++mi)
                 lok[i][mi] = (rk + mi * KL::RPI) * sk + static_cast<uint32_t>((pk ^ KL::fk((mi % KVAR) * KL::RPI + rk)) << 4);
 #pragma unroll
             for (int mi = 0; mi < IPWV; ++mi)
-                lov[i][mi] = (rv + mi * LY::RPI) * sv + static_cast<uint32_t>((pv ^ LY::fv(rv)) << 4);
+                lov[i][mi] = (rv + mi * VL::RPI) * sv + static_cast<uint32_t>((pv ^ vswz(rv)) << 4);
         }
     }
     // LDS byte offsets of the tile buffers (32-bit local-address-space pointers)
     const uint32_t lds_k0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Kt[0][0]));
-    const uint32_t lds_v0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Vt[0][0]));
+    const uint32_t lds_v0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)&Vt[0]));
     constexpr uint32_t kBufBytes = 64 * RBK;   // one K buffer
     struct Dma {
         uint64_t b[4];   // SGPR bases of the wave's 8-row groups
@@ -229,7 +253,7 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
     };
     auto resolve = [&](const Tile& t, const Pend& pd, uint32_t lds_dst, bool is_v, auto R0, auto NR) {
         constexpr int rpw = decltype(NR)::value / NW;
-        const uint32_t rb = is_v ? D * 2u : static_cast<uint32_t>(RBK);   // bytes per row
+        const uint32_t rb = static_cast<uint32_t>(is_v ? RBV : RBK);   // bytes per row
         const int l = t.l;
         const int sh = 6 - l;
         const int rsm1 = (1 << sh) - 1;   // rows per logical block - 1
@@ -241,7 +265,7 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
         const uint64_t m0 = 0ull - static_cast<uint64_t>(l == 0);
         const uint64_t base = ((l0 & m0) | (pl & ~m0)) + static_cast<uint64_t>(lvl_off * rb);
         // byte offsets inside one (batch, head) of one level fit 32 bits (checked on the host)
-        const uint32_t stride = static_cast<uint32_t>(l == 0 && !CONTIG ? (is_v ? a.vs2 : a.ks2) : D) * (is_v ? 2u : EK);
+        const uint32_t stride = static_cast<uint32_t>(l == 0 && !CONTIG ? (is_v ? a.vs2 : a.ks2) : D) * (is_v ? EV : EK);
         const int key0 = decltype(R0)::value + wave * rpw;
         Dma d;
 #pragma unroll
@@ -261,7 +285,7 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
     };
     auto issue = [&](const Tile& t, uint32_t lds_dst, auto ISV, auto R0, auto NR) {
         constexpr bool is_v = decltype(ISV)::value != 0;
-        constexpr int ipw = decltype(NR)::value / (is_v ? LY::RPI : KL::RPI) / NW;
+        constexpr int ipw = decltype(NR)::value / (is_v ? VL::RPI : KL::RPI) / NW;
         const Dma d = resolve(t, pend(t, R0, NR), lds_dst, is_v, R0, NR);
 #pragma unroll
         for (int mi = 0; mi < ipw; ++mi) fire(d, is_v, t.l > 0, mi);
@@ -414,13 +438,27 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
     };
     // lazy running max: rescale the O accumulators and row sums only when the max in use is
     // exceeded by more than kLazyRescale (after the O products issued so far)
-    auto update_max = [&](float mt) {
-        if (__builtin_expect(__ballot(mt > m_use + kLazyRescale) != 0ull, 0)) {
-            const float m_new = fmaxf(m_use, mt);
+    // fp8 P V: the max in use is an integer (the ceiling) and is raised as soon as the row max
+    // exceeds it by more than 1, so it stays within [M - 1, M] of the final M = ceil(row max);
+    // P is quantized as 2^(t - m_use + 7) <= 2^8, i.e. relative to 2^(m_use - 7) in
+    // [2^(M - 8), 2^(M - 7)]: every weight down to 2^-13 of the largest stays in e4m3's normal
+    // range, where rounding commutes with the power-of-two rescales. P held in fp32 for a
+    // pending product (`pending`) is rescaled with the accumulators.
+    constexpr float kRescale = PV8 ? 1.0f : kLazyRescale;
+    auto update_max = [&](float mt, bool pending = false) {
+        if (__builtin_expect(__ballot(mt > m_use + kRescale) != 0ull, 0)) {
+            const float m_new = fmaxf(m_use, PV8 ? ceilf(mt) : mt);
             const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_use - m_new);
             m_use = m_new;
-            psum0 *= alpha;
-            psum1 *= alpha;
+            if constexpr (PV8) {
+                lacc[0] *= alpha;
+                if (pending)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) pAf[e] *= alpha;
+            } else {
+                psum0 *= alpha;
+                psum1 *= alpha;
+            }
 #pragma unroll
             for (int i = 0; i < DB; ++i)
 #pragma unroll
@@ -431,7 +469,9 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
         const int kb_max = cols[t.base + t.cnt - 1];
         return (t.cnt < (1 << t.l)) || ((kb_max + 1) * 64 - 1 > min_limit);
     };
-    auto exp_off = [&](int lvl) { return static_cast<float>(lvl) - (m_use == -INFINITY ? 0.f : m_use); };
+    auto exp_off = [&](int lvl) {
+        return static_cast<float>(lvl + (PV8 ? 7 : 0)) - (m_use == -INFINITY ? 0.f : m_use);
+    };
     auto wait_publish = [&]() {
         // this wave's direct loads landed (vmcnt), then the barrier publishes every wave's and
         // retires every wave's reads of the buffers about to be refilled
@@ -532,6 +572,128 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
         update_max(mt);
     };
 
+    // ---- fp8 P V pipeline pieces ----
+    // O^T += V^T P^T on v_mfma_f32_32x32x64_f8f6f4 over a whole 64-key tile. B = P^T: lane l holds
+    // query l % 32 and the 32 bytes kappa = 16 h + 8 j + e (h = the tile's half, j, e as in the
+    // S accumulators: C registers 8j + e of half h hold tile key 32 h + 16 j + 8 (l / 32) + e),
+    // i.e. [P8 of half 0, P8 of half 1] in register order. A = V^T: lane l holds column
+    // d = 32 dblk + l % 32 and the same 32 keys, which four 8-bit transposed reads deliver: a
+    // 16-lane group names 8 aligned rows x 16 bytes (lanes 2m and 2m+1: row m's two 8-byte
+    // halves) and lane i receives byte i of each of the 8 rows, in row order. Read (h, j) of
+    // lane l covers rows 32 h + 16 j + 8 (l / 32) + 0..7 at columns 32 dblk + 16 ((l / 16) & 1)
+    // + 0..15; the swizzle term 2 ((r >> 1) & 3) of those rows depends only on the lane, so
+    // each dblk has one loop-invariant address and (h, j) is an immediate.
+    uint32_t va8[DB];
+#pragma unroll
+    for (int dblk = 0; dblk < DB; ++dblk)
+        va8[dblk] = lds_v0 + static_cast<uint32_t>((8 * hi + (jj >> 1)) * RBV +
+                                                   16 * ((2 * dblk + (grp & 1)) ^ (2 * ((jj >> 2) & 3))) +
+                                                   8 * (jj & 1));
+    auto read_v8 = [&](uint32_t vbuf, int dblk) {
+        union {
+            i32x8 v;
+            i32x2 h[4];
+        } r;
+#pragma unroll
+        for (int hj = 0; hj < 4; ++hj)
+            r.h[hj] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (lds_i32x2*)(uintptr_t)(va8[dblk] + vbuf + static_cast<uint32_t>((32 * (hj >> 1) + 16 * (hj & 1)) * RBV)));
+        return r.v;
+    };
+    // exp chunk c of sacc[H], kept in fp32 (a tile's first half) or packed to e4m3 (its second
+    // half): pair pr = registers 2pr, 2pr + 1 -> bytes 2pr, 2pr + 1 (v_cvt_pk_fp8_f32 rounds to
+    // nearest even, with subnormals; src0 goes to the lower byte)
+    auto exp_f = [&](auto H, int c, float off) {
+        constexpr int hh = decltype(H)::value;
+        constexpr int PAIRS = 8 / KK;
+#pragma unroll
+        for (int q = 0; q < PAIRS; ++q) {
+            const int pr = c * PAIRS + q;
+            pAf[2 * pr] = fast_exp2(fmaf(sacc[hh][2 * pr], cs, off));
+            pAf[2 * pr + 1] = fast_exp2(fmaf(sacc[hh][2 * pr + 1], cs, off));
+        }
+    };
+    auto exp_q = [&](auto H, int c, float off, uint32_t (&pq)[4]) {
+        constexpr int hh = decltype(H)::value;
+        constexpr int PAIRS = 8 / KK;
+#pragma unroll
+        for (int q = 0; q < PAIRS; ++q) {
+            const int pr = c * PAIRS + q;
+            const float p0 = fast_exp2(fmaf(sacc[hh][2 * pr], cs, off));
+            const float p1 = fast_exp2(fmaf(sacc[hh][2 * pr + 1], cs, off));
+            const int old = static_cast<int>(pq[pr >> 1]);   // (the word select must be a constant)
+            pq[pr >> 1] = static_cast<uint32_t>((pr & 1) ? __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, old, true)
+                                                         : __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, old, false));
+        }
+    };
+    // the tile's P V product and its row sums (A = all ones: e4m3 1.0 is 0x38)
+    auto pv8 = [&](const i32x8 (&vf)[DB], const uint32_t (&pq)[4]) {
+        uint32_t qa[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            qa[w] = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(pAf[4 * w], pAf[4 * w + 1], 0, false));
+            qa[w] = static_cast<uint32_t>(
+                __builtin_amdgcn_cvt_pk_fp8_f32(pAf[4 * w + 2], pAf[4 * w + 3], static_cast<int>(qa[w]), true));
+        }
+        const i32x8 pf = {static_cast<int>(qa[0]), static_cast<int>(qa[1]), static_cast<int>(qa[2]),
+                          static_cast<int>(qa[3]), static_cast<int>(pq[0]), static_cast<int>(pq[1]),
+                          static_cast<int>(pq[2]), static_cast<int>(pq[3])};
+        const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                            0x38383838, 0x38383838, 0x38383838, 0x38383838};
+#pragma unroll
+        for (int dblk = 0; dblk < DB; ++dblk) {
+            oacc[dblk] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[dblk], pf, oacc[dblk], 0, 0, 0, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pf, lacc, 0, 0, 0, 0, 0, 0);
+    };
+    // One step of the fp8 P V pipeline (KK slots, a scheduling barrier after each):
+    //   S(h) on the fp8 MFMA in slots 0 and KSL (K reads at the start); in each slot 1/KK of
+    //   the exp work of the other half: H = 0 exponentiates the previous tile's second half
+    //   (to e4m3) and then runs that tile's P V product (V tile reads issued from the middle
+    //   slot, buffer `vprev`); H = 1 exponentiates this tile's first half into pAf (fp32).
+    // Returns the half's unmasked max (log2 units).
+    auto step8 = [&](auto H, uint32_t kbuf, int lvl_p, int lvl_h, auto&& dma, uint32_t vprev) {
+        constexpr int hh = decltype(H)::value;
+        const float off = exp_off(lvl_p);
+        const uint32_t koff = kbuf + hh * 32 * RBK;
+        KOp kr[KS];
+        uint32_t pq[4] = {0u, 0u, 0u, 0u};
+        i32x8 vf[DB];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < KS; ++i) kr[i] = read_kx(i, koff);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sacc[hh][e] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            if (hh == 0 && kk == KK / 2)
+#pragma unroll
+                for (int d = 0; d < DB; ++d) vf[d] = read_v8(vprev, d);
+            if (kk % KSL == 0) sacc[hh] = mfma_s(kr[kk / KSL], kk / KSL, sacc[hh]);
+            if constexpr (hh == 0)
+                exp_q(IC<1>{}, kk, off, pq);
+            else
+                exp_f(IC<0>{}, kk, off);
+            dma(kk);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (hh == 0) pv8(vf, pq);
+        float x0 = half_max_part(H, 0);
+        float x1 = half_max_part(H, 1);
+        return half_max(x0, x1, lvl_h);
+    };
+    auto step8_max = [&](auto H, bool need, uint32_t kbuf, int lvl_p, const Tile& t, auto&& dma,
+                         uint32_t vprev) {
+        constexpr int hh = decltype(H)::value;
+        float mt = step8(H, kbuf, lvl_p, t.l, dma, vprev);
+        if (need) {
+            apply_mask(H, t);
+            mt = half_max(half_max_part(H, 0), half_max_part(H, 1), t.l);
+        }
+        update_max(mt, hh == 1);   // after H = 1 the first half's P waits in pAf
+    };
+
     __syncthreads();  // cols[] visible
 
     Tile cur{0, 0, 0, 0};
@@ -539,7 +701,87 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
     set_cnt(cur);
     if (!any_valid_query) cur.l = 4;
 
-    if (cur.l < 4) {
+    if constexpr (PV8) {
+        // ---- fp8 P V: K(t) in buffer t & 1, V(t) (a whole tile) in buffer t mod 3 ----
+        // Tile t's P V product runs at the end of tile t+1's first step, once its second half
+        // is exponentiated; V(t)'s buffer is refilled (with V(t+3)) only after tile t+2's
+        // barrier. K(t+1) and V(t+1) are loaded during tile t's first step, sharing one list
+        // lookup (both tiles' rows are split over the waves alike).
+        constexpr uint32_t kVTile = 64 * RBV;
+        if (cur.l < 4) {
+            issue_k(cur, 0);
+            issue(cur, lds_v0, IC<1>{}, IC<0>{}, IC<64>{});
+            Tile nxt = next_tile(cur);
+            wait_publish();
+            if (nxt.l < 4) {
+                issue_k(nxt, 1);
+                issue(nxt, lds_v0 + kVTile, IC<1>{}, IC<0>{}, IC<64>{});
+            }
+            const bool nm = tile_needs_mask(cur);
+            compute_s(IC<0>{}, 0u);
+            if (nm) apply_mask(IC<0>{}, cur);
+            update_max(half_max(half_max_part(IC<0>{}, 0), half_max_part(IC<0>{}, 1), cur.l));
+            step8_max(IC<1>{}, nm, 0u, cur.l, cur, [](int) {}, 0u);
+            int lvl_prev = cur.l;
+            cur = nxt;
+            int vb = 1;   // V buffer of tile `cur`
+            auto tile_body8 = [&](auto TT) -> bool {   // false after the row's last tile
+                constexpr int T = decltype(TT)::value;
+                const Tile nx = next_tile(cur);
+                wait_publish();
+                const bool has_nx = nx.l < 4;
+                const bool need = tile_needs_mask(cur);
+                const uint32_t kbuf = T ? kBufBytes : 0u;
+                const Tile nsrc = has_nx ? nx : cur;
+                const uint32_t vprev = static_cast<uint32_t>(vb == 0 ? 2 : vb - 1) * kVTile;
+                const uint32_t vnext = static_cast<uint32_t>(vb == 2 ? 0 : vb + 1) * kVTile;
+                Pend pd{};
+                Dma dk{}, dv{};
+                auto dma = [&](int sl) {
+                    if (sl == 0) {
+                        pd = pend(nsrc, IC<0>{}, IC<64>{});
+                    } else if (sl == 1) {
+                        dk = resolve(nsrc, pd, lds_k0 + (T ? 0u : kBufBytes), false, IC<0>{}, IC<64>{});
+                        dv = resolve(nsrc, pd, lds_v0 + vnext, true, IC<0>{}, IC<64>{});
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < IPWK + IPWV; ++i)
+                            if (i % (KK - 2) == sl - 2) {
+                                if (i < IPWK)
+                                    fire(dk, false, nsrc.l > 0, i);
+                                else
+                                    fire(dv, true, nsrc.l > 0, i - IPWK);
+                            }
+                    }
+                };
+                step8_max(IC<0>{}, need, kbuf, lvl_prev, cur, dma, vprev);
+                step8_max(IC<1>{}, need, kbuf, cur.l, cur, [](int) {}, 0u);
+                lvl_prev = cur.l;
+                cur = nx;
+                vb = vb == 2 ? 0 : vb + 1;
+                return cur.l < 4;
+            };
+            if (cur.l < 4) {
+                for (;;) {
+                    if (!tile_body8(IC<1>{})) break;
+                    if (!tile_body8(IC<0>{})) break;
+                }
+            }
+            // ---- after the last tile: its second half's P, then its P V product ----
+            wait_publish();
+            {
+                const float off = exp_off(lvl_prev);
+                uint32_t pq[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int c = 0; c < KK; ++c) exp_q(IC<1>{}, c, off, pq);
+                const uint32_t vlast = static_cast<uint32_t>(vb == 0 ? 2 : vb - 1) * kVTile;
+                i32x8 vf[DB];
+#pragma unroll
+                for (int d = 0; d < DB; ++d) vf[d] = read_v8(vlast, d);
+                pv8(vf, pq);
+            }
+        }
+    } else if (cur.l < 4) {
         // ---- tile 0: K(0) and V half 0 first; S of half 0 alone, then step(half 1) ----
         issue_k(cur, 0);
         issue_vh(cur, 0, 0);
@@ -631,9 +873,10 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
     l_run += psum0 + psum1;
 
     // ---- epilogue ----
-    const float l_tot = pair32_sum(l_run);
+    const float l_tot = PV8 ? lacc[0] : pair32_sum(l_run);
     const bool valid_q = qt < a.Nv && l_tot > 0.f;
-    const float inv = valid_q ? 1.f / l_tot : 0.f;
+    float inv = valid_q ? 1.f / l_tot : 0.f;
+    if constexpr (PV8) inv *= a.v_scale[b * a.Hkv + hk];
     bf16_bits* O = static_cast<bf16_bits*>(a.o) + b * a.os0 + h * a.os1 + static_cast<int64_t>(qt) * a.os2;
 #pragma unroll
     for (int dblk = 0; dblk < DB; ++dblk)
@@ -645,20 +888,20 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
             *reinterpret_cast<u32x2*>(O + dblk * 32 + gg * 8 + hi * 4) = w;
         }
     if (a.lse != nullptr && hi == 0) {
-        const float lse = valid_q ? (m_use + log2f(l_tot)) * kLn2 : -INFINITY;
+        const float lse = valid_q ? (m_use - (PV8 ? 7.f : 0.f) + log2f(l_tot)) * kLn2 : -INFINITY;
         a.lse[(static_cast<int64_t>(b) * a.H + h) * a.N + qt] = lse;
     }
 }
 
-template <int D, int BQ, bool PACK, bool F8 = false>
+template <int D, int BQ, bool PACK, int FP8 = 0>
 hipError_t launch_one(const Shape& s, const AttnArgs& a, hipStream_t st) {
     const int rows = s.B * s.H * s.NQB;
     const int nper = (rows + 7) / 8;
     const size_t dyn = static_cast<size_t>(s.NKB) * sizeof(int);
     if (a.ks2 == D && a.vs2 == D)
-        hipLaunchKernelGGL((k_attn_fwd_bf16<D, BQ, true, PACK, F8>), dim3(8 * nper), dim3(2 * BQ), dyn, st, a, rows);
+        hipLaunchKernelGGL((k_attn_fwd_bf16<D, BQ, true, PACK, FP8>), dim3(8 * nper), dim3(2 * BQ), dyn, st, a, rows);
     else
-        hipLaunchKernelGGL((k_attn_fwd_bf16<D, BQ, false, PACK, F8>), dim3(8 * nper), dim3(2 * BQ), dyn, st, a, rows);
+        hipLaunchKernelGGL((k_attn_fwd_bf16<D, BQ, false, PACK, FP8>), dim3(8 * nper), dim3(2 * BQ), dyn, st, a, rows);
     return hipGetLastError();
 }
 
@@ -680,8 +923,18 @@ hipError_t launch_attn_bf16(const Shape& s, const AttnArgs& a, bool pack, hipStr
 hipError_t launch_attn_fp8qk(const Shape& s, const AttnArgs& a, hipStream_t st) {
     if (s.B * s.H * s.NQB == 0) return hipSuccess;
     if (a.q_scale == nullptr || a.k_scale == nullptr) return hipErrorInvalidValue;
-    if (s.D == 128 && s.BQ == 128) return launch_one<128, 128, true, true>(s, a, st);
-    if (s.D == 128 && s.BQ == 64) return launch_one<128, 64, true, true>(s, a, st);
+    if (s.D == 128 && s.BQ == 128) return launch_one<128, 128, true, 1>(s, a, st);
+    if (s.D == 128 && s.BQ == 64) return launch_one<128, 64, true, 1>(s, a, st);
+    return hipErrorNotSupported;
+}
+
+hipError_t launch_attn_fp8(const Shape& s, const AttnArgs& a, hipStream_t st) {
+    if (s.B * s.H * s.NQB == 0) return hipSuccess;
+    if (a.q_scale == nullptr || a.k_scale == nullptr || a.v_scale == nullptr) return hipErrorInvalidValue;
+    // the e4m3 K and V are contiguous: only the CONTIG instantiation is used
+    if (a.ks2 != s.D || a.vs2 != s.D) return hipErrorInvalidValue;
+    if (s.D == 128 && s.BQ == 128) return launch_one<128, 128, true, 2>(s, a, st);
+    if (s.D == 128 && s.BQ == 64) return launch_one<128, 64, true, 2>(s, a, st);
     return hipErrorNotSupported;
 }
 

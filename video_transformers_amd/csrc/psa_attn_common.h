@@ -30,6 +30,8 @@ struct AttnArgs {
     // q_scale [B*H] and k_scale [B*Hkv]; the logit of q8 . k8 is c * q_scale * k_scale times it
     const float* q_scale;
     const float* k_scale;
+    // fp8 P V reading only (null otherwise): per (batch, KV head) scale of the e4m3 V [B*Hkv]
+    const float* v_scale;
 };
 
 // Level-by-level walk over a row's block index. Uniform across the workgroup. Only the
@@ -108,5 +110,9 @@ hipError_t launch_attn_bf16(const Shape& s, const AttnArgs& a, bool pack, hipStr
 // Q and K (level 0 and pooled) as e4m3 bytes, contiguous, with a.q_scale / a.k_scale set
 // (head_dim 128 only; hipErrorNotSupported otherwise). V, O and the index as in the bf16 path.
 hipError_t launch_attn_fp8qk(const Shape& s, const AttnArgs& a, hipStream_t st);
+
+// launch_attn_fp8qk with V (level 0 and pooled) as contiguous e4m3 bytes too (a.v_scale set)
+// and P quantized to e4m3 for the P V product.
+hipError_t launch_attn_fp8(const Shape& s, const AttnArgs& a, hipStream_t st);
 
 }  // namespace psa

@@ -45,6 +45,14 @@ hipError_t launch_attn_fwd_fp8qk(const Shape& s, float scale, const uint8_t* q8,
                                  const int32_t* row_ptr, const int32_t* col_idx, void* o,
                                  float* lse, hipStream_t st);
 
+// launch_attn_fwd_fp8qk with V (level 0 and pooled) as contiguous e4m3 bytes too, one scale per
+// (batch, KV head) (v_scale [B*Hkv]), and P quantized to e4m3 for the P V product.
+hipError_t launch_attn_fwd_fp8(const Shape& s, float scale, const uint8_t* q8, const float* q_scale,
+                               const uint8_t* k8, const uint8_t* kp8, const float* k_scale,
+                               const uint8_t* v8, const uint8_t* vp8, const float* v_scale,
+                               const int32_t* row_ptr, const int32_t* col_idx, void* o, float* lse,
+                               hipStream_t st);
+
 // Per-head e4m3 quantization of one bf16 tensor [B, Hx, N, D] (strides xs, elements) and,
 // when xp is not null, of its packed pooled rows [B, Hx, 7N/8, D] with the same scale.
 // Writes x8 / xp8 contiguous and scale [B*Hx]; see psa_quantize_fp8.

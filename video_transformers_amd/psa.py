@@ -34,8 +34,8 @@ SKIP = -1
 EXPORTS = ("psa_pooled_rows", "psa_build_pyramid", "psa_mask_workspace_bytes", "psa_mask",
            "psa_mask_assign", "psa_build_index", "psa_attn_workspace_bytes", "psa_attn_fwd",
            "psa_attn_fwd_indexed", "psa_attn_fwd_unpacked", "psa_attn_bwd_workspace_bytes",
-           "psa_attn_bwd", "psa_quantize_fp8", "psa_attn_fwd_fp8qk", "psa_check_status",
-           "psa_status_string", "psa_last_hip_error")
+           "psa_attn_bwd", "psa_quantize_fp8", "psa_attn_fwd_fp8qk", "psa_attn_fwd_fp8",
+           "psa_check_status", "psa_status_string", "psa_last_hip_error")
 
 
 class PsaError(RuntimeError):
@@ -98,6 +98,8 @@ def lib() -> ctypes.CDLL:
         L.psa_quantize_fp8.restype = I32
         L.psa_attn_fwd_fp8qk.argtypes = [P, ctypes.c_float] + [V] * 11 + [SZ, V]
         L.psa_attn_fwd_fp8qk.restype = I32
+        L.psa_attn_fwd_fp8.argtypes = [P, ctypes.c_float] + [V] * 12 + [SZ, V]
+        L.psa_attn_fwd_fp8.restype = I32
         L.psa_check_status.argtypes, L.psa_check_status.restype = [V, V], I32
         L.psa_status_string.argtypes, L.psa_status_string.restype = [I32], ctypes.c_char_p
         L.psa_last_hip_error.argtypes, L.psa_last_hip_error.restype = [], I32
@@ -374,6 +376,28 @@ def attn_fwd_fp8qk(q8, q_scale, k8, k8_pooled, k_scale, v, v_pooled, level_map, 
                                     _ptr(k8), _ptr(k8_pooled), _ptr(k_scale), _ptr(v),
                                     _ptr(v_pooled), _ptr(level_map), _ptr(out), _ptr(lse),
                                     _ptr(ws), ws.numel(), _stream(stream)), "psa_attn_fwd_fp8qk")
+    return out, lse
+
+
+def attn_fwd_fp8(q8, q_scale, k8, k8_pooled, k_scale, v8, v8_pooled, v_scale, level_map,
+                 prob: Problem, *, scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                 lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                 ws: Optional[torch.Tensor] = None, stream=None):
+    """attn_fwd_fp8qk with the P V product on e4m3 operands too (v8, v8_pooled from
+    quantize_fp8 of V and its pooled rows). Returns (o, lse or None)."""
+    for t in (q8, k8, k8_pooled, v8, v8_pooled):
+        if t.dtype != torch.uint8 or not t.is_contiguous():
+            raise ValueError("q8, k8, k8_pooled, v8, v8_pooled must be contiguous uint8 codes")
+    if out is None:
+        out = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
+    if lse is None and want_lse:
+        lse = torch.empty(q8.shape[:3], dtype=torch.float32, device=q8.device)
+    if ws is None:
+        ws = attn_workspace(prob, q8.device)
+    _check(lib().psa_attn_fwd_fp8(prob.ref(), ctypes.c_float(scale), _ptr(q8), _ptr(q_scale),
+                                  _ptr(k8), _ptr(k8_pooled), _ptr(k_scale), _ptr(v8),
+                                  _ptr(v8_pooled), _ptr(v_scale), _ptr(level_map), _ptr(out),
+                                  _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)), "psa_attn_fwd_fp8")
     return out, lse
 
 
