@@ -15,9 +15,9 @@ FLOPs (4*d per executed (valid query, visible pooled key) pair) per second of st
 MFMA peak, speedup over the same kernel on an all-level-0 map, and over the unpacked layout
 with one logical block per hardware tile on the same map). `roofline` is for that
 kernel, timed with HIP events on the stream it runs on. `bwd` times psa_attn_bwd on the same
-map with a seeded output gradient (not part of `value`). `fp8qk` times the forward with its
-q . k products on e4m3 operands (psa_quantize_fp8 of Q and of K with its pooled rows, then
-psa_attn_fwd_fp8qk on the same map; not part of `value`). `cpu_baseline` times the CPU oracle
+map with a seeded output gradient (not part of `value`). `fp8` times the forward on e4m3
+operands (psa_quantize_fp8 of Q, K, V; psa_attn_fwd_fp8qk with only the q . k products on fp8,
+psa_attn_fwd_fp8 with the P V product too; same map; not part of `value`). `cpu_baseline` times the CPU oracle
 (fp64 numpy) on a bounded sample of the same workload on this host's cores.
 """
 from __future__ import annotations
@@ -311,7 +311,7 @@ def run(args) -> dict:
     if bwd is not None:
         out["bwd"] = bwd
     if fp8 is not None:
-        out["fp8qk"] = fp8
+        out["fp8"] = fp8
     out["attn"]["unpacked_same_map_ms"] = None if unpacked_ms != unpacked_ms else round(unpacked_ms, 3)
     out["attn"]["speedup_vs_unpacked"] = (None if unpacked_ms != unpacked_ms
                                           else round(unpacked_ms / attn_ms_mean, 2))
@@ -363,52 +363,73 @@ def _bwd_run(wl, prob, L, ptr, st, check, q, k, v, kp, vp, lm_host, o, lse, stre
 
 def _fp8_run(wl, prob, L, ptr, st, check, q, k, v, kp, vp, lm, stream, fwd_flops, index_ms,
              bf16_attn_ms):
-    """The e4m3 QK^T forward on the step's map: psa_quantize_fp8 of K (with its pooled rows)
-    and of Q, then psa_attn_fwd_fp8qk (which builds its block index, then runs the kernel);
-    mean of 10 calls run back to back each. The kernel's own time is estimated as the call minus the
-    index build timed in the step (same map, same kernels). Its bound mixes two peaks: the
-    q . k half of the executed FLOP (2*d per pair) at the fp8 MFMA peak and the P V half at
-    the bf16 one."""
+    """The e4m3 forwards on the step's map: psa_quantize_fp8 of Q, of K with its pooled rows and
+    of V with its pooled rows, then psa_attn_fwd_fp8qk (q . k on fp8, P V in bf16) and
+    psa_attn_fwd_fp8 (both products on fp8); each call builds its block index, then runs the
+    kernel. Means of 10 calls run back to back. A kernel's own time is estimated as its call
+    minus the index build timed in the step (same map, same kernels). Bounds: fp8qk mixes two
+    peaks (the q . k half of the executed FLOP, 2*d per pair, at the fp8 MFMA peak, the P V
+    half at the bf16 one); fp8 puts all of it at the fp8 peak."""
     import ctypes
     import torch
     dev = q.device
     B, H, N, d = q.shape
     Hkv = k.shape[1]
-    k8 = torch.empty((B, Hkv, N, d), dtype=torch.uint8, device=dev)
-    kp8 = torch.empty(kp.shape, dtype=torch.uint8, device=dev)
-    q8 = torch.empty((B, H, N, d), dtype=torch.uint8, device=dev)
+    u8 = lambda shape: torch.empty(shape, dtype=torch.uint8, device=dev)  # noqa: E731
+    k8, kp8, v8, vp8, q8 = u8((B, Hkv, N, d)), u8(kp.shape), u8((B, Hkv, N, d)), u8(vp.shape), u8((B, H, N, d))
     sk = torch.empty(B * Hkv, dtype=torch.float32, device=dev)
+    sv = torch.empty(B * Hkv, dtype=torch.float32, device=dev)
     sq = torch.empty(B * H, dtype=torch.float32, device=dev)
     o8 = torch.empty_like(q)
     lse8 = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     n = L.psa_attn_workspace_bytes(prob.ref())
     ws = torch.empty(n, dtype=torch.uint8, device=dev)
     kst = (ctypes.c_int64 * 3)(*k.stride()[:3])
+    vst = (ctypes.c_int64 * 3)(*v.stride()[:3])
     qst = (ctypes.c_int64 * 3)(*q.stride()[:3])
 
-    def quant():
+    def quant_qk():
         check(L.psa_quantize_fp8(B, Hkv, N, d, ptr(k), kst, ptr(kp), ptr(k8), ptr(kp8), ptr(sk), st),
               "quantize k")
         check(L.psa_quantize_fp8(B, H, N, d, ptr(q), qst, None, ptr(q8), None, ptr(sq), st),
               "quantize q")
 
-    def attn():
+    def quant_v():
+        check(L.psa_quantize_fp8(B, Hkv, N, d, ptr(v), vst, ptr(vp), ptr(v8), ptr(vp8), ptr(sv), st),
+              "quantize v")
+
+    def attn_qk():
         check(L.psa_attn_fwd_fp8qk(prob.ref(), ctypes.c_float(0.0), ptr(q8), ptr(sq), ptr(k8),
                                    ptr(kp8), ptr(sk), ptr(v), ptr(vp), ptr(lm), ptr(o8), ptr(lse8),
                                    ptr(ws), n, st), "attn fp8qk")
 
-    q_ms = _timed_back_to_back(quant, stream)
-    a_ms = _timed_back_to_back(attn, stream)
-    check(L.psa_check_status(ptr(ws), st), "attn fp8qk status")
-    kern_ms = a_ms - index_ms
-    tf = fwd_flops / (kern_ms * 1e-3) / 1e12
-    bound_ms = (fwd_flops / 2 / PEAK_FP8_TFLOPS + fwd_flops / 2 / PEAK_BF16_TFLOPS) / 1e12 * 1e3
-    return {"quantize_q_k_ms": round(q_ms, 4), "attn_call_ms": round(a_ms, 4),
-            "attn_kernel_ms_est": round(kern_ms, 4), "tflops_executed": round(tf, 2),
-            "speedup_vs_bf16_kernel": round(bf16_attn_ms / kern_ms, 3),
-            "roofline": {"bound": "mfma", "peak": "fp8 5000 TFLOP/s for q.k, bf16 2500 for P V",
-                         "min_ms": round(bound_ms, 4), "frac": round(bound_ms / kern_ms, 4)},
-            "quantization": "e4m3, one scale per (batch, head), K and pooled K share it"}
+    def attn_all():
+        check(L.psa_attn_fwd_fp8(prob.ref(), ctypes.c_float(0.0), ptr(q8), ptr(sq), ptr(k8),
+                                 ptr(kp8), ptr(sk), ptr(v8), ptr(vp8), ptr(sv), ptr(lm), ptr(o8),
+                                 ptr(lse8), ptr(ws), n, st), "attn fp8")
+
+    qk_ms = _timed_back_to_back(quant_qk, stream)
+    v_ms = _timed_back_to_back(quant_v, stream)
+
+    def report(call_ms, bound_ms, peak):
+        kern_ms = call_ms - index_ms
+        tf = fwd_flops / (kern_ms * 1e-3) / 1e12
+        return {"attn_call_ms": round(call_ms, 4), "attn_kernel_ms_est": round(kern_ms, 4),
+                "tflops_executed": round(tf, 2),
+                "speedup_vs_bf16_kernel": round(bf16_attn_ms / kern_ms, 3),
+                "roofline": {"bound": "mfma", "peak": peak, "min_ms": round(bound_ms, 4),
+                             "frac": round(bound_ms / kern_ms, 4)}}
+    half = fwd_flops / 2
+    out = {"quantize_q_k_ms": round(qk_ms, 4), "quantize_v_ms": round(v_ms, 4),
+           "qk": report(_timed_back_to_back(attn_qk, stream),
+                        (half / PEAK_FP8_TFLOPS + half / PEAK_BF16_TFLOPS) / 1e12 * 1e3,
+                        "fp8 5000 TFLOP/s for q.k, bf16 2500 for P V"),
+           "qk_pv": report(_timed_back_to_back(attn_all, stream),
+                           fwd_flops / PEAK_FP8_TFLOPS / 1e12 * 1e3, "fp8 5000 TFLOP/s"),
+           "quantization": "e4m3, one scale per (batch, head) for Q, K, V (pooled rows share "
+                           "their head's); P relative to 2^(ceil(row max) - 7)"}
+    check(L.psa_check_status(ptr(ws), st), "attn fp8 status")
+    return out
 
 
 def _dense_run(args, wl, prob, L, ptr, st, check, q, k, v, kp, vp, o, lse, row_ptr, col_idx,
@@ -491,7 +512,7 @@ def main():
     ap.add_argument("--no-bwd", action="store_true",
                     help="skip the psa_attn_bwd timing (reported beside the forward metric)")
     ap.add_argument("--no-fp8", action="store_true",
-                    help="skip the e4m3 QK^T forward timing (reported beside the forward metric)")
+                    help="skip the e4m3 forward timings (reported beside the forward metric)")
     ap.add_argument("--mask-mode", choices=("sampling", "antidiag", "meankey"), default=None,
                     help="score with this psa_mask mode instead of the workload's own")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
