@@ -26,6 +26,9 @@
  *    enqueued: no call synchronises except psa_check_status.
  *  - Arguments are checked on the host before anything is enqueued. A failed check returns a
  *    negative psa_status and enqueues nothing. No C++ exception crosses this interface.
+ *  - A problem with batch 0 or seq_len 0 has no work: after the shape and parameter checks
+ *    every call returns PSA_OK without reading its device pointers (they may be null) or
+ *    enqueueing anything (psa_quantize_fp8 with seq_len 0 still writes scale = 1 per head).
  *  - All calls are reentrant; calls on different streams may run concurrently provided their
  *    output and workspace buffers do not overlap.
  *

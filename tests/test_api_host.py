@@ -228,3 +228,30 @@ def test_attn_fwd_fp8_host_checks():
     p.c.dtype = P.PSA_F32
     assert call(p) == P.PSA_ERR_UNSUPPORTED
     assert call(_prob(dtype=P.PSA_BF16), n=1 << 30) == P.PSA_ERR_UNSUPPORTED   # head_dim 64
+
+
+@pytest.mark.parametrize("field,value", [("batch", 0), ("seq_len", 0)])
+def test_empty_problems_do_nothing(field, value):
+    """No batch or no tokens: every call returns PSA_OK without touching its (null) pointers."""
+    L = psa.lib()
+    q = torch.zeros(1, 2, 1024, 128)
+    p = psa.make_problem(q, q, q, block_q=128)
+    p.c.dtype = P.PSA_BF16
+    setattr(p.c, field, value)
+    if field == "seq_len":
+        p.c.seq_valid = 0
+    n = None
+    mp = psa.MaskParams().c()
+    assert L.psa_build_pyramid(p.ref(), n, n, n, n, n) == P.PSA_OK
+    assert L.psa_mask(p.ref(), ctypes.byref(mp), n, n, n, n, n, n, 0, n) == P.PSA_OK
+    assert L.psa_mask_assign(p.ref(), ctypes.byref(mp), n, n, n, n) == P.PSA_OK
+    assert L.psa_build_index(p.ref(), n, n, n, n, n) == P.PSA_OK
+    assert L.psa_attn_fwd(p.ref(), 0.0, *[n] * 9, 0, n) == P.PSA_OK
+    assert L.psa_attn_fwd_indexed(p.ref(), 0.0, *[n] * 10) == P.PSA_OK
+    assert L.psa_attn_fwd_unpacked(p.ref(), 0.0, *[n] * 10) == P.PSA_OK
+    assert L.psa_attn_bwd(p.ref(), 0.0, *[n] * 13, 0, n) == P.PSA_OK
+    assert L.psa_attn_fwd_fp8qk(p.ref(), 0.0, *[n] * 11, 0, n) == P.PSA_OK
+    assert L.psa_attn_fwd_fp8(p.ref(), 0.0, *[n] * 12, 0, n) == P.PSA_OK
+    if field == "batch":
+        st = (ctypes.c_int64 * 3)(2 * 1024 * 128, 1024 * 128, 128)
+        assert L.psa_quantize_fp8(0, 2, 1024, 128, n, st, n, n, n, n, n) == P.PSA_OK

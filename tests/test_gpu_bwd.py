@@ -5,9 +5,12 @@ recomputes everything in float64 from the same bf16 inputs, map and output gradi
 
 Tolerance. The kernels round P and dS to bf16 before the products that use them (relative
 error <= 2^-9 each) and take D_i = dO_i . o_i from the bf16 forward output; everything else is
-bf16 inputs (exact in both) with float32 accumulation. Those roundings are independent across
-the terms of each sum, so the gradient's relative L2 error is a few times 2^-9 ~ 2e-3: the
-bar is rel-L2 <= 1e-2 per tensor, and max-abs <= 2e-2 of the tensor's largest magnitude.
+bf16 inputs (exact in both) with float32 accumulation. Each row of dS sums to exactly zero
+(sum_j P_ij (dP_ij - D_i) = D_i - D_i), so dq_i = s sum_j dS_ij K_j is a cancelling sum: its
+relative error is about 2^-9 times |(dS_ij K_j)_j| / |dq_i|, a ratio that grows when a row sees
+few keys. Applying exactly these roundings to the fp64 oracle gives dq 1.2e-2 from exact at
+64 tokens and <= 7e-3 from 1088 tokens on (the bf16 rounding of dS dominates; exact D changes
+little). Bar: rel-L2 <= 2e-2 per tensor, max-abs <= 4e-2 of the tensor's largest magnitude.
 Pad query rows get dq = 0 and pad tokens dk = dv = 0 exactly; two runs are bit-identical.
 """
 import numpy as np
@@ -21,8 +24,8 @@ from gpu_util import DEV, announce, need_gpu, oracle_map, oracle_problem, proble
 
 pytestmark = pytest.mark.gpu
 
-REL_L2 = 1e-2
-MAX_REL = 2e-2
+REL_L2 = 2e-2
+MAX_REL = 4e-2
 
 BWD = [W.small(w) for w in W.ALL if w.dtype == "bf16"]
 BWD.append(W.small(W.QWEN25VL_32K).replace(name="qwen2.5-vl-7b-small-bq64", block_q=64))

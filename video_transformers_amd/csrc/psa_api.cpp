@@ -79,6 +79,11 @@ int check_problem(const psa_problem* p, psa::Shape* s) {
     return PSA_OK;
 }
 
+// A problem with no tokens or no batch has no work: every entry point returns PSA_OK for it
+// after the shape and parameter checks, without reading its pointers (torch gives empty
+// tensors a null data pointer) and without launching anything.
+bool no_work(const psa::Shape& s) { return s.B == 0 || s.N == 0; }
+
 int check_mask_params(const psa_problem* p, const psa_mask_params* m) {
     if (m == nullptr) return PSA_ERR_INVALID_ARG;
     if (m->mode != PSA_MASK_SAMPLING && m->mode != PSA_MASK_ANTIDIAG && m->mode != PSA_MASK_MEANKEY)
@@ -144,6 +149,7 @@ int psa_build_pyramid(const psa_problem* prob, const void* k, const void* v, voi
     psa::Shape s;
     int rc = check_problem(prob, &s);
     if (rc != PSA_OK) return rc;
+    if (no_work(s)) return PSA_OK;
     if (!k || !v || !k_pooled || !v_pooled) return PSA_ERR_INVALID_ARG;
     if (!aligned16(k) || !aligned16(v) || !aligned16(k_pooled) || !aligned16(v_pooled))
         return PSA_ERR_INVALID_ARG;
@@ -165,6 +171,7 @@ int psa_mask(const psa_problem* prob, const psa_mask_params* params, const void*
     if (rc != PSA_OK) return rc;
     if ((rc = check_mask_params(prob, params)) != PSA_OK) return rc;
     if (s.dtype != PSA_BF16) return PSA_ERR_UNSUPPORTED;
+    if (no_work(s)) return PSA_OK;
     if (!q || !k || !level_map || !block_mass) return PSA_ERR_INVALID_ARG;
     if (params->cos_sim_min > 0.f && block_sim == nullptr) return PSA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k)) return PSA_ERR_INVALID_ARG;
@@ -189,6 +196,7 @@ int psa_mask_assign(const psa_problem* prob, const psa_mask_params* params,
     int rc = check_problem(prob, &s);
     if (rc != PSA_OK) return rc;
     if ((rc = check_mask_params(prob, params)) != PSA_OK) return rc;
+    if (no_work(s)) return PSA_OK;
     if (!block_mass || !level_map) return PSA_ERR_INVALID_ARG;
     const bool use_sim = params->cos_sim_min > 0.f;
     if (use_sim && block_sim == nullptr) return PSA_ERR_INVALID_ARG;
@@ -201,6 +209,7 @@ int psa_build_index(const psa_problem* prob, const int8_t* level_map, int32_t* r
     psa::Shape s;
     int rc = check_problem(prob, &s);
     if (rc != PSA_OK) return rc;
+    if (no_work(s)) return PSA_OK;
     if (!level_map || !row_ptr || !col_idx || !dev_err) return PSA_ERR_INVALID_ARG;
     psa::IndexBufs ib{row_ptr, col_idx, dev_err};
     return hip_status(psa::launch_build_index(s, level_map, ib, static_cast<hipStream_t>(stream)));
@@ -219,6 +228,7 @@ int psa_attn_fwd(const psa_problem* prob, float softmax_scale, const void* q, co
     psa::Shape s;
     int rc = check_problem(prob, &s);
     if (rc != PSA_OK) return rc;
+    if (no_work(s)) return PSA_OK;
     if (!q || !k || !v || !k_pooled || !v_pooled || !level_map || !o) return PSA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_pooled) ||
         !aligned16(v_pooled) || !aligned16(o))
@@ -246,6 +256,8 @@ int attn_indexed(const psa_problem* prob, float softmax_scale, const void* q, co
     psa::Shape s;
     int rc = check_problem(prob, &s);
     if (rc != PSA_OK) return rc;
+    if (!pack && s.dtype != PSA_BF16) return PSA_ERR_UNSUPPORTED;
+    if (no_work(s)) return PSA_OK;
     if (!q || !k || !v || !k_pooled || !v_pooled || !row_ptr || !col_idx || !o)
         return PSA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_pooled) ||
@@ -253,7 +265,6 @@ int attn_indexed(const psa_problem* prob, float softmax_scale, const void* q, co
         return PSA_ERR_INVALID_ARG;
     if (!std::isfinite(softmax_scale)) return PSA_ERR_INVALID_ARG;
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(s.D));
-    if (!pack && s.dtype != PSA_BF16) return PSA_ERR_UNSUPPORTED;
     return hip_status(psa::launch_attn_fwd(s, scale, q, k, v, k_pooled, v_pooled, row_ptr,
                                            col_idx, o, lse, pack, static_cast<hipStream_t>(stream)));
 }
@@ -286,7 +297,13 @@ int psa_quantize_fp8(int32_t batch, int32_t heads, int32_t seq_len, int32_t head
     for (int i = 0; i < 3; ++i)
         if (x_stride[i] <= 0 || x_stride[i] % 8 != 0) return PSA_ERR_INVALID_ARG;
     if (x_stride[2] < head_dim) return PSA_ERR_INVALID_ARG;
-    if (!x || !x8 || !scale || (x_pooled == nullptr) != (x8_pooled == nullptr)) return PSA_ERR_INVALID_ARG;
+    if (batch == 0) return PSA_OK;
+    if (!scale || (reinterpret_cast<uintptr_t>(scale) & 3u) != 0) return PSA_ERR_INVALID_ARG;
+    if (seq_len == 0)   // every head is empty: scale 1, nothing to code
+        return hip_status(psa::launch_quantize_fp8(batch, heads, 0, head_dim, nullptr, x_stride,
+                                                   nullptr, nullptr, nullptr, scale,
+                                                   static_cast<hipStream_t>(stream)));
+    if (!x || !x8 || (x_pooled == nullptr) != (x8_pooled == nullptr)) return PSA_ERR_INVALID_ARG;
     if (!aligned16(x) || (x_pooled && !aligned16(x_pooled)) ||
         (reinterpret_cast<uintptr_t>(x8) & 7u) != 0 ||
         (x8_pooled && (reinterpret_cast<uintptr_t>(x8_pooled) & 7u) != 0) ||
@@ -306,6 +323,7 @@ int psa_attn_fwd_fp8qk(const psa_problem* prob, float softmax_scale, const uint8
     int rc = check_problem(prob, &s);
     if (rc != PSA_OK) return rc;
     if (s.dtype != PSA_BF16 || s.D != 128) return PSA_ERR_UNSUPPORTED;
+    if (no_work(s)) return PSA_OK;
     if (!q8 || !q_scale || !k8 || !k8_pooled || !k_scale || !v || !v_pooled || !level_map || !o)
         return PSA_ERR_INVALID_ARG;
     if (!aligned16(q8) || !aligned16(k8) || !aligned16(k8_pooled) || !aligned16(v) ||
@@ -335,6 +353,7 @@ int psa_attn_fwd_fp8(const psa_problem* prob, float softmax_scale, const uint8_t
     int rc = check_problem(prob, &s);
     if (rc != PSA_OK) return rc;
     if (s.dtype != PSA_BF16 || s.D != 128) return PSA_ERR_UNSUPPORTED;
+    if (no_work(s)) return PSA_OK;
     if (!q8 || !q_scale || !k8 || !k8_pooled || !k_scale || !v8 || !v8_pooled || !v_scale ||
         !level_map || !o)
         return PSA_ERR_INVALID_ARG;
@@ -374,6 +393,7 @@ int psa_attn_bwd(const psa_problem* prob, float softmax_scale, const void* q, co
     // buffer sets and the P/dS exchange: 12-bit query block index, at most 7680 rows per KV head
     const int g = s.H / s.Hkv;
     if (s.NQB >= 4096 || static_cast<int64_t>(g) * s.NQB > 7680) return PSA_ERR_UNSUPPORTED;
+    if (no_work(s)) return PSA_OK;
     if (!q || !k || !v || !k_pooled || !v_pooled || !level_map || !o || !lse || !dout || !dq ||
         !dk || !dv)
         return PSA_ERR_INVALID_ARG;
