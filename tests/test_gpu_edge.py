@@ -1,5 +1,6 @@
 """GPU edge cases of the whole path, through the C ABI: empty inputs, all-padding sequences,
-all-skip maps, and ragged block counts (a single block; an odd number of 64-token blocks).
+all-skip maps, ragged block counts (a single block; an odd number of 64-token blocks), and the
+backward at its maximum row count per KV head.
 
 Expected values: the oracle's (forward, backward, fp8 readings), or what the definitions fix
 exactly (an empty softmax gives o = 0 and lse = -inf; pad query rows and rows with no visible
@@ -139,3 +140,28 @@ def test_ragged_block_counts(n, d, causal):
             o8[0, h], l8[0, h] = oracle.attention_fp8_head(oracle.fp8_quantize(qh, s_q), k8, kp8, v8,
                                                            vp8, s_q, s_k, s_v, lm[0, h], p)
         check_fp8pv(out["o8"], out["lse8"], o8, l8, wl.seq_valid, f"ragged n{n} fp8")
+
+
+@pytest.mark.parametrize("d,heads,n,bq", [(64, 120, 4096, 64), (128, 60, 16384, 128)])
+def test_bwd_row_limit(d, heads, n, bq):
+    """The backward at its row limit: `heads` query heads on one KV head times their query
+    blocks = 7680 (query head, query block) rows, every one listing KV block 0 at level 0 and
+    block 1 at level 2, so two key-side tiles each collect all 7680 rows (at d = 128 the row list
+    nearly fills what the key-side kernel's buffers leave of the LDS). dq, dk and dv against the
+    oracle, every element."""
+    announce(f"backward at 7680 rows per KV head, d={d}")
+    wl = W.Workload(name="rowlimit", seed=313 + d, batch=1, heads_q=heads, heads_kv=1, head_dim=d,
+                    seq_len=n, seq_valid=n - 8, block_q=bq, causal=False, dtype="bf16",
+                    k_dist="clustered", map_source="iid", map_probs=(1.0, 0.0, 0.0, 0.0, 0.0))
+    assert wl.heads_q // wl.heads_kv * wl.n_qblocks == 7680
+    q, k, v = W.make_qkv(wl)
+    lm = np.full((1, wl.heads_q, wl.n_qblocks, wl.n_kblocks), -1, dtype=np.int8)
+    lm[..., 0] = 0
+    lm[..., 1] = 2
+    dout = W.make_dout(wl)
+    dq, dk, dv = _run(wl, q, k, v, lm, dout)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attention_backward(q, k, v, lm, dout, oracle_problem(wl))
+    _compare("dq", dq, rq)
+    _compare("dk", dk, rk)
+    _compare("dv", dv, rv)
