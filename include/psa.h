@@ -12,8 +12,9 @@
  *   psa_attn_fwd       - the level-weighted flash-style attention;
  *   psa_attn_bwd       - its backward (dq, dk, dv through every pyramid level).
  * plus psa_mask_assign and psa_build_index, the mask's and the attention's integer stages,
- * exported on their own, and psa_quantize_fp8 / psa_attn_fwd_fp8qk / psa_attn_fwd_fp8, the
- * forward with its q . k products (and its P V product) on e4m3 operands.
+ * exported on their own, psa_quantize_fp8 / psa_attn_fwd_fp8qk / psa_attn_fwd_fp8, the
+ * forward with its q . k products (and its P V product) on e4m3 operands, and
+ * psa_attn_fwd_meankey, block-mean scoring fused into the attention.
  *
  * Conventions shared by every call
  *  - Pointers named q, k, v, o, k_pooled, v_pooled, level_map, block_mass, block_sim, lse,
@@ -279,6 +280,28 @@ int psa_attn_fwd_fp8(const psa_problem* prob, float softmax_scale, const uint8_t
                      const float* k_scale, const uint8_t* v8, const uint8_t* v8_pooled,
                      const float* v_scale, const int8_t* level_map, void* o, float* lse, void* ws,
                      size_t ws_bytes, void* stream);
+
+/* Device workspace psa_attn_fwd_meankey needs; 0 on a bad problem. */
+size_t psa_attn_fwd_meankey_workspace_bytes(const psa_problem* prob);
+
+/*
+ * Block-mean scoring fused into the attention (skill summary at skillsmp.com,
+ * "Implementation": a query against each KV block's mean key, the cheapest estimator; scored
+ * inside the attention's prologue, no separate mask pass or block index). params->mode must
+ * be PSA_MASK_MEANKEY (else PSA_ERR_INVALID_ARG). Computes exactly what psa_mask (block-mean
+ * mode, same params) followed by psa_attn_fwd computes - the same level map bit for bit, the
+ * same outputs - but each attention workgroup scores its own query block's mean against every
+ * KV block mean (float64 dots), assigns the levels with the same steps as psa_mask_assign and
+ * attends over the resulting list. level_map and block_mass (layouts as in psa_mask) receive
+ * the map and the masses when not null. The cosine check runs when cos_sim_min > 0.
+ * dtype PSA_BF16, block_q 128 and seq_len/64 <= 1792 only (PSA_ERR_UNSUPPORTED otherwise).
+ * Workspace: psa_attn_fwd_meankey_workspace_bytes (the block means and similarities).
+ */
+int psa_attn_fwd_meankey(const psa_problem* prob, const psa_mask_params* params,
+                         float softmax_scale, const void* q, const void* k, const void* v,
+                         const void* k_pooled, const void* v_pooled, int8_t* level_map,
+                         float* block_mass, void* o, float* lse, void* ws, size_t ws_bytes,
+                         void* stream);
 
 /* Device workspace psa_attn_bwd needs; 0 on a bad problem. */
 size_t psa_attn_bwd_workspace_bytes(const psa_problem* prob);

@@ -252,6 +252,38 @@ def test_empty_problems_do_nothing(field, value):
     assert L.psa_attn_bwd(p.ref(), 0.0, *[n] * 13, 0, n) == P.PSA_OK
     assert L.psa_attn_fwd_fp8qk(p.ref(), 0.0, *[n] * 11, 0, n) == P.PSA_OK
     assert L.psa_attn_fwd_fp8(p.ref(), 0.0, *[n] * 12, 0, n) == P.PSA_OK
+    mk = psa.MaskParams(mode="meankey").c()
+    assert L.psa_attn_fwd_meankey(p.ref(), ctypes.byref(mk), 0.0, *[n] * 10, 0, n) == P.PSA_OK
     if field == "batch":
         st = (ctypes.c_int64 * 3)(2 * 1024 * 128, 1024 * 128, 128)
         assert L.psa_quantize_fp8(0, 2, 1024, 128, n, st, n, n, n, n, n) == P.PSA_OK
+
+
+def test_attn_fwd_meankey_host_checks():
+    L = psa.lib()
+    d = ctypes.c_void_p(256)
+    q = torch.zeros(1, 2, 1024, 128)
+    p = psa.make_problem(q, q, q, block_q=128)
+    p.c.dtype = P.PSA_BF16
+    need = L.psa_attn_fwd_meankey_workspace_bytes(p.ref())
+    # query and key block means, block similarities
+    assert need >= (2 * 8 * 128 + 16 * 128 + 16) * 4
+    mk = psa.MaskParams(mode="meankey").c()
+    call = lambda prob, params=mk, n=need, sc=0.0, **o: L.psa_attn_fwd_meankey(
+        prob.ref(), ctypes.byref(params), sc,
+        *[o.get(x, d) for x in ("q", "k", "v", "kp", "vp", "map", "mass", "o", "lse", "ws")], n, None)
+    assert call(p, n=need - 1) == P.PSA_ERR_WORKSPACE
+    assert call(p, ws=None) == P.PSA_ERR_WORKSPACE
+    for name in ("q", "k", "v", "kp", "vp", "o"):
+        assert call(p, **{name: None}) == P.PSA_ERR_INVALID_ARG, name
+    assert call(p, params=psa.MaskParams(mode="sampling").c()) == P.PSA_ERR_INVALID_ARG
+    assert call(p, sc=float("inf")) == P.PSA_ERR_INVALID_ARG
+    p64 = psa.make_problem(q, q, q, block_q=64)
+    p64.c.dtype = P.PSA_BF16
+    assert call(p64, n=1 << 30) == P.PSA_ERR_UNSUPPORTED          # block_q 64
+    big = psa.make_problem(torch.zeros(1, 1, 64 * 1800, 64), torch.zeros(1, 1, 64 * 1800, 64),
+                           torch.zeros(1, 1, 64 * 1800, 64), block_q=128)
+    big.c.dtype = P.PSA_BF16
+    assert call(big, n=1 << 40) == P.PSA_ERR_UNSUPPORTED          # more than 1792 KV blocks
+    p.c.dtype = P.PSA_F32
+    assert call(p, n=1 << 30) == P.PSA_ERR_UNSUPPORTED

@@ -1,0 +1,78 @@
+"""GPU parity of psa_attn_fwd_meankey: block-mean scoring and the threshold assignment fused into
+the attention's prologue.
+
+* Against the two-step GPU path (psa_mask in block-mean mode, then psa_attn_fwd): the same
+  level map, block masses, o and lse bit for bit (same arithmetic, same order, same tiles).
+* Against the oracle: the map rows except at fragile entries (decisions within float rounding of
+  a threshold or tie), and the attention on the GPU's map to the bf16 bars.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+import video_transformers_amd as psa
+from gpu_util import (DEV, announce, assign_params, check_attention, fragile_entries, mask_params,
+                      need_gpu, oracle_problem, problem_for)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+    yield
+    torch.cuda.synchronize()
+
+
+MK = [W.small(W.WAN13B_32K).replace(name="wan2.1-1.3b-small-meankey", mask_mode="meankey"),
+      W.small(W.QWEN25VL_32K).replace(name="qwen2.5-vl-7b-small-meankey", mask_mode="meankey"),
+      W.small(W.COGVIDEOX5B_17K).replace(name="cogvideox-5b-small-meankey", mask_mode="meankey")]
+
+
+def _both(wl, qd, kd, vd):
+    prob = problem_for(wl, qd, kd, vd)
+    kp, vp = psa.build_pyramid(kd, vd, prob)
+    params = mask_params(wl)
+    lm, M, sim = psa.mask(qd, kd, prob, params)
+    o, lse = psa.attn_fwd(qd, kd, vd, kp, vp, lm, prob)
+    of, lsef, lmf, Mf = psa.attn_fwd_meankey(qd, kd, vd, kp, vp, prob, params, want_mass=True)
+    torch.cuda.synchronize()
+    return (lm, M, o, lse), (lmf, Mf, of, lsef)
+
+
+@pytest.mark.parametrize("wl", MK, ids=[w.name for w in MK])
+def test_meankey_fused_parity(wl):
+    announce(f"fused block-mean scoring {wl.name}")
+    q, k, v = W.make_qkv(wl)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    (lm, M, o, lse), (lmf, Mf, of, lsef) = _both(wl, qd, kd, vd)
+    assert torch.equal(lmf, lm), "map differs from psa_mask's"
+    assert torch.equal(Mf, M), "block masses differ from psa_mask's"
+    assert torch.equal(of, o) and torch.equal(lsef, lse), "attention differs from psa_attn_fwd's"
+    # oracle: the map rows, then the attention on the GPU's map
+    p = oracle_problem(wl)
+    a = assign_params(wl)
+    lm_ref, M_ref, sim_ref = oracle.mask(q, k, p, "meankey", a)
+    assert np.abs(Mf.double().cpu().numpy() - M_ref).max() <= 2e-6
+    frag = fragile_entries(M_ref, sim_ref, p, a)
+    diff = lmf.cpu().numpy() != lm_ref
+    print(f"[{wl.name}] map entries differing {int(diff.sum())}, fragile {int(frag.sum())}", flush=True)
+    assert not np.any(diff & ~frag)
+    o_ref, lse_ref = oracle.attention(q, k, v, lmf.cpu().numpy(), p)
+    check_attention(of, lsef, o_ref, lse_ref, wl.seq_valid, False, f"{wl.name} fused")
+
+
+def test_meankey_fused_fullsize_wan():
+    """The Wan2.1-1.3B-like 32k layer: the fused call equals the two-step path bit for bit (the
+    two-step path is held to the oracle at full size by the full-size parity tests)."""
+    wl = W.WAN13B_32K.replace(name="wan2.1-1.3b_32k-meankey", mask_mode="meankey")
+    announce(f"fused block-mean scoring, full size {wl.name}")
+    q, k, v = W.make_qkv(wl)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    (lm, M, o, lse), (lmf, Mf, of, lsef) = _both(wl, qd, kd, vd)
+    dm = (Mf != M)
+    print(f"[{wl.name}] masses differing: {int(dm.sum())} of {M.numel()}", flush=True)
+    assert torch.equal(lmf, lm) and torch.equal(Mf, M)
+    assert torch.equal(of, o) and torch.equal(lsef, lse)

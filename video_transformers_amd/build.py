@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libpsa.so")
 
 SOURCES = ["psa_api.cpp", "psa_pyramid.hip", "psa_index.hip", "psa_attn.hip", "psa_attn_bf16.hip",
            "psa_attn_bwd.hip", "psa_mask.hip", "psa_fp8.hip"]
-HEADERS = ["psa_internal.h", "psa_device.h", "psa_attn_common.h", "psa_bf16_tile.h"]
+HEADERS = ["psa_internal.h", "psa_device.h", "psa_attn_common.h", "psa_bf16_tile.h", "psa_assign.h"]
 
 ARCH = "gfx950"
 # Packed-fp32 VALU forms are disabled for every device compile: the compiler then never
@@ -32,11 +32,12 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE,
           "-Wall", "-Wno-unused-result"] + DEVICE_FLAGS
 # Per-source extras. The bf16 attention and mask-scoring kernels keep their MFMA accumulators
 # in VGPRs (the softmax work reads them with VALU instructions; from AGPRs each value would
-# first need a v_accvgpr_read), and the attention kernel is compiled without NaN semantics so that max reductions of MFMA results need no
-# canonicalisation (the kernel masks with -inf, never with NaN; infinities keep their meaning).
+# first need a v_accvgpr_read). Both are compiled without NaN semantics so that max reductions of MFMA results need no
+# canonicalisation (they mask with -inf, never with NaN; infinities keep their meaning), and so that
+# the threshold assignment they share (psa_assign.h) compiles to the same arithmetic in both.
 EXTRA = {
     "psa_attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
-    "psa_mask.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "psa_mask.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
 }
 
 

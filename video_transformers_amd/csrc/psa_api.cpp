@@ -375,6 +375,69 @@ int psa_attn_fwd_fp8(const psa_problem* prob, float softmax_scale, const uint8_t
                                                v8_pooled, v_scale, w.row_ptr, w.col_idx, o, lse, st));
 }
 
+namespace {
+
+struct MeanKeyWs {
+    float* qbar;
+    float* kbar;
+    float* sim;
+    size_t bytes;
+};
+
+MeanKeyWs meankey_ws_layout(const psa::Shape& s, void* base) {
+    MeanKeyWs w;
+    char* p = static_cast<char*>(base);
+    size_t off = 0;
+    w.qbar = reinterpret_cast<float*>(p + off);
+    off += align_up(static_cast<size_t>(s.B) * s.H * s.NQB * s.D * sizeof(float));
+    w.kbar = reinterpret_cast<float*>(p + off);
+    off += align_up(static_cast<size_t>(s.B) * s.Hkv * s.NKB * s.D * sizeof(float));
+    w.sim = reinterpret_cast<float*>(p + off);
+    off += align_up(static_cast<size_t>(s.B) * s.Hkv * s.NKB * sizeof(float));
+    w.bytes = off;
+    return w;
+}
+
+}  // namespace
+
+size_t psa_attn_fwd_meankey_workspace_bytes(const psa_problem* prob) {
+    psa::Shape s;
+    if (check_problem(prob, &s) != PSA_OK) return 0;
+    return meankey_ws_layout(s, nullptr).bytes;
+}
+
+int psa_attn_fwd_meankey(const psa_problem* prob, const psa_mask_params* params,
+                         float softmax_scale, const void* q, const void* k, const void* v,
+                         const void* k_pooled, const void* v_pooled, int8_t* level_map,
+                         float* block_mass, void* o, float* lse, void* ws, size_t ws_bytes,
+                         void* stream) {
+    psa::Shape s;
+    int rc = check_problem(prob, &s);
+    if (rc != PSA_OK) return rc;
+    if ((rc = check_mask_params(prob, params)) != PSA_OK) return rc;
+    if (params->mode != PSA_MASK_MEANKEY) return PSA_ERR_INVALID_ARG;
+    if (s.dtype != PSA_BF16 || s.BQ != 128 || s.NKB > 1792) return PSA_ERR_UNSUPPORTED;
+    if (no_work(s)) return PSA_OK;
+    if (!q || !k || !v || !k_pooled || !v_pooled || !o) return PSA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_pooled) ||
+        !aligned16(v_pooled) || !aligned16(o))
+        return PSA_ERR_INVALID_ARG;
+    if (!std::isfinite(softmax_scale)) return PSA_ERR_INVALID_ARG;
+    const size_t need = meankey_ws_layout(s, nullptr).bytes;
+    if (ws == nullptr || ws_bytes < need) return PSA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0) return PSA_ERR_WORKSPACE;
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(s.D));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    MeanKeyWs w = meankey_ws_layout(s, ws);
+    hipError_t e = psa::launch_block_means(s, q, k, w.qbar, w.kbar, st);
+    if (e != hipSuccess) return hip_status(e);
+    if (params->cos_sim_min > 0.f && (e = psa::launch_block_sim(s, k, w.sim, st)) != hipSuccess)
+        return hip_status(e);
+    return hip_status(psa::launch_attn_fwd_meankey(s, scale, *params, q, k, v, k_pooled, v_pooled,
+                                                   w.qbar, w.kbar, w.sim, level_map, block_mass,
+                                                   o, lse, st));
+}
+
 size_t psa_attn_bwd_workspace_bytes(const psa_problem* prob) {
     psa::Shape s;
     if (check_problem(prob, &s) != PSA_OK) return 0;

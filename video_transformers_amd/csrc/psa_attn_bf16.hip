@@ -43,8 +43,11 @@
 //    bank conflicts.
 #include <stdlib.h>
 
+#include <cmath>
+
 #include <type_traits>
 
+#include "psa_assign.h"
 #include "psa_attn_common.h"
 #include "psa_bf16_tile.h"
 
@@ -52,6 +55,17 @@ namespace psa {
 namespace {
 
 constexpr float kLazyRescale = 8.0f;  // log2-domain headroom before the accumulators rescale
+
+// Block-mean scoring fused into the prologue (MK): the query block means, KV block means, the
+// assignment's parameters and where the map and masses go (either may be null).
+struct MkArgs {
+    const float* qbar;   // [B*H][NQB][D]
+    const float* kbar;   // [B*Hkv][NKB][D]
+    float* mass_out;     // [B*H*NQB][NKB] or null
+    int8_t* map_out;     // [B*H*NQB][NKB] or null
+    AssignArgs asg;      // RQ = 1, sampling counting, sim set when the cosine check is on
+    double c;            // (1 / sqrt(d)) * log2(e), the scorer's logit scale
+};
 
 struct Tile {
     int l;     // level (4 = walk finished)
@@ -73,8 +87,10 @@ struct Tile {
 // FP8 == 2: V is e4m3 too (one scale per (batch, KV head)) and P is quantized to e4m3 for an
 // fp8 P V product over whole 64-key tiles (see the fp8 P V pipeline below). Otherwise P, V and
 // O stay bf16.
-template <int D, int BQ, bool CONTIG, bool PACK, int FP8>
-__global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int total_rows) {
+// MK: the row's block list comes from block-mean scoring and the threshold assignment run in
+// the prologue (block_q 128: the assignment's 256 threads), instead of the CSR index.
+template <int D, int BQ, bool CONTIG, bool PACK, int FP8, bool MK = false>
+__global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int total_rows, MkArgs mk) {
     constexpr bool F8 = FP8 >= 1;
     constexpr bool PV8 = FP8 == 2;
     constexpr int NW = BQ / 32;
@@ -121,12 +137,107 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
     const VT* __restrict__ VP = static_cast<const VT*>(a.vp);
 
     // ---- the row's block list -> LDS ----
-    const int32_t* rp = a.row_ptr + static_cast<int64_t>(row) * 4;
-    const int r0 = rp[0];
-    const int lb1 = rp[1] - r0, lb2 = rp[2] - r0, lb3 = rp[3] - r0, lb4 = rp[4] - r0;
+    int lb1, lb2, lb3, lb4;
+    if constexpr (MK) {
+        static_assert(!MK || (BQ == 128 && !F8), "fused block-mean scoring: bf16, block_q 128");
+        // Scratch aliased on the tile buffers, which the first tile's loads only fill after the
+        // list is built: the query block mean, the log-masses, masses and levels in Kt, the
+        // sort keys in Vt.
+        const int NKB = mk.asg.NKB;
+        float* qs = reinterpret_cast<float*>(&Kt[0][0]);
+        float* Ls = qs + D;
+        float* Ms = Ls + NKB;
+        int8_t* lvl = reinterpret_cast<int8_t*>(Ms + NKB);
+        uint64_t* keys = reinterpret_cast<uint64_t*>(&Vt[0]);
+        __shared__ int lcnt[4];
+        __shared__ int wtot[2][4][4];   // [chunk parity][level][wave]
+        for (int i = tid; i < D; i += 256) qs[i] = mk.qbar[static_cast<int64_t>(row) * D + i];
+        if (tid < 4) lcnt[tid] = 0;
+        __syncthreads();
+        // log2-masses exactly as the block-mean scorer writes them (float64 dot in d order)
+        const float* kh_bar = mk.kbar + static_cast<int64_t>(b * a.Hkv + hk) * NKB * D;
+        const int qlo = qb * BQ;
+        const int lastk = a.causal ? min((qlo + BQ - 1) / 64, NKB - 1) : NKB - 1;
+        for (int kb = tid; kb < NKB; kb += 256) {
+            const int nv = min(max(a.Nv - kb * 64, 0), 64);
+            const float* kr = kh_bar + static_cast<int64_t>(kb) * D;
+            double dot = 0.0;
+            for (int e = 0; e < D; ++e) dot += static_cast<double>(kr[e]) * static_cast<double>(qs[e]);
+            Ls[kb] = (qlo < a.Nv && nv > 0 && kb <= lastk)
+                         ? static_cast<float>(dot * mk.c + log2(static_cast<double>(nv)))
+                         : -INFINITY;
+        }
+        __syncthreads();
+        assign_masses(mk.asg, qb, Ls, Ms, mk.mass_out != nullptr ? mk.mass_out + static_cast<int64_t>(row) * NKB : nullptr, tid);
+        assign_levels(mk.asg, qb, b, hk, Ms, keys, lvl, tid);
+        if (mk.map_out != nullptr)
+            for (int kb = tid; kb < NKB; kb += 256) mk.map_out[static_cast<int64_t>(row) * NKB + kb] = lvl[kb];
+        // the list: level 0, 1, 2, 3, ascending kb within a level (an ordered compaction)
+        {
+            int cnt[4] = {0, 0, 0, 0};
+            for (int kb = tid; kb < NKB; kb += 256) {
+                const int L = lvl[kb];
+                if (L >= 0) ++cnt[L];
+            }
+#pragma unroll
+            for (int l = 0; l < 4; ++l)
+                if (cnt[l]) atomicAdd(&lcnt[l], cnt[l]);
+        }
+        __syncthreads();
+        lb1 = __builtin_amdgcn_readfirstlane(lcnt[0]);
+        lb2 = lb1 + __builtin_amdgcn_readfirstlane(lcnt[1]);
+        lb3 = lb2 + __builtin_amdgcn_readfirstlane(lcnt[2]);
+        lb4 = lb3 + __builtin_amdgcn_readfirstlane(lcnt[3]);
+        {
+            int run0 = 0, run1 = 0, run2 = 0, run3 = 0;   // entries placed so far per level
+            int par = 0;
+            const uint64_t below = (1ull << lane) - 1ull;
+            for (int c0 = 0; c0 < NKB; c0 += 256) {
+                const int kb = c0 + tid;
+                const int L = kb < NKB ? lvl[kb] : -1;
+                uint64_t bal[4];
+#pragma unroll
+                for (int l = 0; l < 4; ++l) bal[l] = __ballot(L == l);
+                if (lane == 0)
+#pragma unroll
+                    for (int l = 0; l < 4; ++l) wtot[par][l][wave] = __popcll(bal[l]);
+                __syncthreads();
+                int pre[4], tot[4];
+#pragma unroll
+                for (int l = 0; l < 4; ++l) {
+                    pre[l] = 0;
+                    tot[l] = 0;
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const int t = wtot[par][l][w];
+                        tot[l] += t;
+                        if (w < wave) pre[l] += t;
+                    }
+                }
+                if (L >= 0) {
+                    const int base = L == 0 ? run0 : L == 1 ? lb1 + run1 : L == 2 ? lb2 + run2 : lb3 + run3;
+                    const int pl = L == 0 ? pre[0] : L == 1 ? pre[1] : L == 2 ? pre[2] : pre[3];
+                    const uint64_t bl = L == 0 ? bal[0] : L == 1 ? bal[1] : L == 2 ? bal[2] : bal[3];
+                    cols[base + pl + __popcll(bl & below)] = kb;
+                }
+                run0 += tot[0];
+                run1 += tot[1];
+                run2 += tot[2];
+                run3 += tot[3];
+                par ^= 1;
+            }
+        }
+    } else {
+        const int32_t* rp = a.row_ptr + static_cast<int64_t>(row) * 4;
+        const int r0 = rp[0];
+        lb1 = rp[1] - r0;
+        lb2 = rp[2] - r0;
+        lb3 = rp[3] - r0;
+        lb4 = rp[4] - r0;
+        for (int i = tid; i < lb4; i += BQ * 2) cols[i] = a.col_idx[r0 + i];
+    }
     // list offset of level l (l = 0..4), by selects: nothing is indexed dynamically
     auto lb = [&](int l) { return l <= 0 ? 0 : l == 1 ? lb1 : l == 2 ? lb2 : l == 3 ? lb3 : lb4; };
-    for (int i = tid; i < lb4; i += BQ * 2) cols[i] = a.col_idx[r0 + i];
 
     const int blk_first = qb * BQ;
     const int qt = blk_first + wave * 32 + l32;   // this lane's query
@@ -893,15 +1004,15 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
     }
 }
 
-template <int D, int BQ, bool PACK, int FP8 = 0>
-hipError_t launch_one(const Shape& s, const AttnArgs& a, hipStream_t st) {
+template <int D, int BQ, bool PACK, int FP8 = 0, bool MK = false>
+hipError_t launch_one(const Shape& s, const AttnArgs& a, hipStream_t st, const MkArgs& mk = MkArgs{}) {
     const int rows = s.B * s.H * s.NQB;
     const int nper = (rows + 7) / 8;
     const size_t dyn = static_cast<size_t>(s.NKB) * sizeof(int);
     if (a.ks2 == D && a.vs2 == D)
-        hipLaunchKernelGGL((k_attn_fwd_bf16<D, BQ, true, PACK, FP8>), dim3(8 * nper), dim3(2 * BQ), dyn, st, a, rows);
+        hipLaunchKernelGGL((k_attn_fwd_bf16<D, BQ, true, PACK, FP8, MK>), dim3(8 * nper), dim3(2 * BQ), dyn, st, a, rows, mk);
     else
-        hipLaunchKernelGGL((k_attn_fwd_bf16<D, BQ, false, PACK, FP8>), dim3(8 * nper), dim3(2 * BQ), dyn, st, a, rows);
+        hipLaunchKernelGGL((k_attn_fwd_bf16<D, BQ, false, PACK, FP8, MK>), dim3(8 * nper), dim3(2 * BQ), dyn, st, a, rows, mk);
     return hipGetLastError();
 }
 
@@ -925,6 +1036,41 @@ hipError_t launch_attn_fp8qk(const Shape& s, const AttnArgs& a, hipStream_t st) 
     if (a.q_scale == nullptr || a.k_scale == nullptr) return hipErrorInvalidValue;
     if (s.D == 128 && s.BQ == 128) return launch_one<128, 128, true, 1>(s, a, st);
     if (s.D == 128 && s.BQ == 64) return launch_one<128, 64, true, 1>(s, a, st);
+    return hipErrorNotSupported;
+}
+
+hipError_t launch_attn_fwd_meankey(const Shape& s, float scale, const psa_mask_params& mp,
+                                   const void* q, const void* k, const void* v, const void* kp,
+                                   const void* vp, const float* qbar, const float* kbar,
+                                   const float* sim, int8_t* map_out, float* mass_out, void* o,
+                                   float* lse, hipStream_t st) {
+    if (s.dtype != PSA_BF16 || s.BQ != 128 || s.BK != 64 || s.NKB > 1792) return hipErrorNotSupported;
+    if (s.B * s.H * s.NQB == 0) return hipSuccess;
+    AttnArgs a{};
+    a.q = q; a.k = k; a.v = v; a.kp = kp; a.vp = vp; a.o = o; a.lse = lse;
+    a.row_ptr = nullptr;
+    a.col_idx = nullptr;
+    a.H = s.H; a.Hkv = s.Hkv; a.N = s.N; a.Nv = s.Nv; a.NQB = s.NQB; a.causal = s.causal;
+    a.qs0 = s.qs[0]; a.qs1 = s.qs[1]; a.qs2 = s.qs[2];
+    a.ks0 = s.ks[0]; a.ks1 = s.ks[1]; a.ks2 = s.ks[2];
+    a.vs0 = s.vs[0]; a.vs1 = s.vs[1]; a.vs2 = s.vs[2];
+    a.os0 = s.os[0]; a.os1 = s.os[1]; a.os2 = s.os[2];
+    a.pooled_rows = s.pooled_rows;
+    a.c = scale * kLog2e;
+    MkArgs mk;
+    mk.qbar = qbar;
+    mk.kbar = kbar;
+    mk.mass_out = mass_out;
+    mk.map_out = map_out;
+    mk.asg = assign_args_of(s, mp);
+    mk.asg.sim = mp.cos_sim_min > 0.f ? sim : nullptr;
+    mk.asg.RQ = 1;
+    mk.asg.rows_per_head = s.NQB;
+    mk.asg.sampling = 1;   // one scoring row per query block, counted like a sampled row
+    mk.asg.S = 1;
+    mk.c = (1.0 / std::sqrt(static_cast<double>(s.D))) * 1.4426950408889634;
+    if (s.D == 128) return launch_one<128, 128, true, 0, true>(s, a, st, mk);
+    if (s.D == 64) return launch_one<64, 128, true, 0, true>(s, a, st, mk);
     return hipErrorNotSupported;
 }
 

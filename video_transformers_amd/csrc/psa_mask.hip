@@ -27,6 +27,7 @@
 
 #include "psa_device.h"
 #include "psa_internal.h"
+#include "psa_assign.h"
 
 namespace psa {
 namespace {
@@ -748,39 +749,15 @@ __global__ void __launch_bounds__(256)
 }
 
 // ---------------------------------------------------------------------------------------
-// Threshold assignment, one workgroup per (batch, head, query block) row.
+// Threshold assignment, one workgroup per (batch, head, query block) row (psa_assign.h holds
+// the per-row steps, shared with the attention kernel that scores block means in its prologue).
 // ---------------------------------------------------------------------------------------
-constexpr int kAssignThreads = 256;
-
-struct AssignArgs {
-    const float* M;     // given masses [rows][NKB] (psa_mask_assign), or null
-    const float* L;     // log2 masses [B*H][NKB][rows_per_head] (psa_mask), or null
-    float* M_out;       // masses computed from L, written here
-    const float* sim;
-    int8_t* map;
-    int H, Hkv, N, Nv, BQ, BK, NQB, NKB, causal;
-    int P;  // sort length: power of two >= NKB
-    int RQ, rows_per_head, sampling, S;   // scoring rows per query block (L path)
-    double t[4];
-    float cos_min;
-    int force_diag, force_lo, force_hi;
-};
-
-__device__ __forceinline__ uint32_t float_order(float f) {
-    const uint32_t u = __float_as_uint(f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ float float_from_order(uint32_t o) {
-    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
-}
-
 __global__ void __launch_bounds__(kAssignThreads) k_mask_assign(AssignArgs a) {
     // P sort keys, NKB masses, (log-mass path) NKB * RQ staged log-masses, NKB int8 levels
     extern __shared__ uint64_t keys[];
     float* Ms = reinterpret_cast<float*>(keys + a.P);
-    int8_t* lvl = reinterpret_cast<int8_t*>(Ms + a.NKB + (a.L != nullptr ? a.NKB * a.RQ : 0));
-    __shared__ float lse[32];           // per scoring row of the query block (L path)
+    float* Ls = Ms + a.NKB;
+    int8_t* lvl = reinterpret_cast<int8_t*>(Ls + (a.L != nullptr ? a.NKB * a.RQ : 0));
     const int64_t row = blockIdx.x;
     const int qb = static_cast<int>(row % a.NQB);
     const int bh = static_cast<int>(row / a.NQB);
@@ -788,168 +765,28 @@ __global__ void __launch_bounds__(kAssignThreads) k_mask_assign(AssignArgs a) {
     const int b = bh / a.H;
     const int hk = h / (a.H / a.Hkv);
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    int8_t* out = a.map + row * a.NKB;
-
-    const int qlo = qb * a.BQ, qhi = qlo + a.BQ;
-    const bool any_valid = qlo < a.Nv;
-    const int last = a.causal ? min((qhi - 1) / a.BK, a.NKB - 1) : a.NKB - 1;
-    const int ncand = last + 1;
 
     if (a.L != nullptr) {
-        // masses from log-masses: scoring row i of the query block has logsumexp
-        // lse_i = log2 sum_kb exp2(L[kb][i]); mass_kb = mean over the valid rows of
-        // exp2(L[kb][i] - lse_i). Rows with no visible key have L = -inf everywhere.
         // The RQ rows of one block are contiguous in the workspace: the block's values are
         // staged in LDS (Ls[kb * RQ + i]) with independent loads, thread t taking row
         // i = t % RQ of blocks t / RQ + k * (256 / RQ).
-        const int RQ = a.RQ;   // power of two <= 32
+        const int RQ = a.RQ;
         const int i = tid & (RQ - 1);
         const int kstep = kAssignThreads / RQ;
-        float* Ls = Ms + a.NKB;   // NKB * RQ floats, after the masses
-        {
-            const float* Lh = a.L + static_cast<int64_t>(bh) * a.NKB * a.rows_per_head + qb * RQ + i;
+        const float* Lh = a.L + static_cast<int64_t>(bh) * a.NKB * a.rows_per_head + qb * RQ + i;
 #pragma unroll 8
-            for (int kb = tid / RQ; kb < a.NKB; kb += kstep)
-                Ls[kb * RQ + i] = Lh[static_cast<int64_t>(kb) * a.rows_per_head];
-        }
+        for (int kb = tid / RQ; kb < a.NKB; kb += kstep)
+            Ls[kb * RQ + i] = Lh[static_cast<int64_t>(kb) * a.rows_per_head];
         __syncthreads();
-        float m = -INFINITY, sum = 0.f;   // online logsumexp of this thread's values
-        for (int kb = tid / RQ; kb < a.NKB; kb += kstep) {
-            const float v = Ls[kb * RQ + i];
-            const float mn = fmaxf(m, v);
-            if (mn != -INFINITY) sum = sum * fast_exp2(m - mn) + fast_exp2(v - mn);
-            m = mn;
-        }
-        // merge across the lanes of the same row (lane xor RQ, 2 RQ, ... 32), then the waves
-        for (int o = RQ; o < 64; o <<= 1) {
-            const float mo = __shfl_xor(m, o, 64);
-            const float so = __shfl_xor(sum, o, 64);
-            const float mn = fmaxf(m, mo);
-            sum = mn == -INFINITY ? 0.f : sum * fast_exp2(m - mn) + so * fast_exp2(mo - mn);
-            m = mn;
-        }
-        __shared__ float wm[kAssignThreads / 64][32], ws[kAssignThreads / 64][32];
-        if (lane < RQ) {
-            wm[wave][lane] = m;
-            ws[wave][lane] = sum;
-        }
-        __syncthreads();
-        if (tid < RQ) {
-            float mm = -INFINITY, ss = 0.f;
-            for (int w = 0; w < kAssignThreads / 64; ++w) {
-                const float mo = wm[w][tid], so = ws[w][tid];
-                const float mn = fmaxf(mm, mo);
-                ss = mn == -INFINITY ? 0.f : ss * fast_exp2(mm - mn) + so * fast_exp2(mo - mn);
-                mm = mn;
-            }
-            lse[tid] = (mm == -INFINITY || ss <= 0.f) ? -INFINITY : mm + __builtin_amdgcn_logf(ss);
-        }
-        __syncthreads();
-        int den;
-        if (a.sampling)
-            den = min(max(a.Nv - qb * a.BQ, 0), a.BQ) > 0 ? RQ : 0;
-        else
-            den = min(max(a.Nv / a.S - qb * RQ, 0), RQ);
-        const float invd = den > 0 ? 1.f / static_cast<float>(den) : 0.f;
-        float* Mo = a.M_out + row * a.NKB;
-        for (int kb = tid; kb < a.NKB; kb += kAssignThreads) {
-            float acc = 0.f;
-            for (int r = 0; r < RQ; ++r) {
-                const float lr = lse[r];
-                if (lr != -INFINITY) acc += fast_exp2(Ls[kb * RQ + r] - lr);
-            }
-            const float mass = acc * invd;
-            Ms[kb] = mass;
-            Mo[kb] = mass;
-        }
+        assign_masses(a, qb, Ls, Ms, a.M_out + row * a.NKB, tid);
     } else {
         const float* Mrow = a.M + row * a.NKB;
         for (int kb = tid; kb < a.NKB; kb += kAssignThreads) Ms[kb] = Mrow[kb];
     }
     __syncthreads();
-
-    for (int i = tid; i < a.P; i += kAssignThreads) {
-        uint64_t key = ~0ull;
-        if (i < ncand) key = (static_cast<uint64_t>(~float_order(Ms[i])) << 32) | static_cast<uint32_t>(i);
-        keys[i] = key;
-    }
-    for (int i = tid; i < a.NKB; i += kAssignThreads) lvl[i] = -1;
-    __syncthreads();
-    // bitonic sort, ascending keys = mass descending, kb ascending
-    for (int size = 2; size <= a.P; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < a.P / 2; i += kAssignThreads) {
-                const int lo = 2 * i - (i & (stride - 1));
-                const int hi = lo + stride;
-                const bool up = ((lo & size) == 0);
-                const uint64_t x = keys[lo], y = keys[hi];
-                if ((x > y) == up) {
-                    keys[lo] = y;
-                    keys[hi] = x;
-                }
-            }
-            __syncthreads();
-        }
-    }
-    // Exclusive running sum of the sorted masses in float64 (a block scan; the summation
-    // order differs from a left-to-right loop only in float64 rounding, ~1e-16 relative),
-    // then each sorted entry's level from its exclusive sum. The mass comes back out of the
-    // sort key.
-    {
-        const int per = a.P / kAssignThreads > 0 ? a.P / kAssignThreads : 1;   // entries per thread
-        const int i0 = tid * per;
-        double loc = 0.0;
-        for (int u = 0; u < per; ++u) {
-            const int i = i0 + u;
-            if (i < ncand) loc += static_cast<double>(float_from_order(~static_cast<uint32_t>(keys[i] >> 32)));
-        }
-        // inclusive scan of the per-thread totals: within the wave, then across the waves
-        double inc = loc;
-        for (int o = 1; o < 64; o <<= 1) {
-            const double y = __shfl_up(inc, o, 64);
-            if (lane >= o) inc += y;
-        }
-        __shared__ double wsum[kAssignThreads / 64];
-        if (lane == 63) wsum[wave] = inc;
-        __syncthreads();
-        double base = 0.0;
-        for (int w = 0; w < wave; ++w) base += wsum[w];
-        double c = base + inc - loc;   // exclusive sum before entry i0
-        if (any_valid) {
-            for (int u = 0; u < per; ++u) {
-                const int i = i0 + u;
-                if (i >= ncand) break;
-                const uint64_t key = keys[i];
-                const int kb = static_cast<int>(key & 0xffffffffu);
-                int8_t L = -1;
-                if (c < a.t[0]) L = 0;
-                else if (c < a.t[1]) L = 1;
-                else if (c < a.t[2]) L = 2;
-                else if (c < a.t[3]) L = 3;
-                lvl[kb] = L;
-                c += static_cast<double>(float_from_order(~static_cast<uint32_t>(key >> 32)));
-            }
-        }
-    }
-    __syncthreads();
-    for (int kb = tid; kb < a.NKB; kb += kAssignThreads) {
-        int8_t L = any_valid ? lvl[kb] : static_cast<int8_t>(-1);
-        if (any_valid && kb <= last) {
-            const int klo = kb * a.BK, khi = klo + a.BK;
-            bool forced = a.force_diag && klo < qhi && qlo < khi;
-            if (a.force_lo < a.force_hi &&
-                ((qlo < a.force_hi && a.force_lo < qhi) || (klo < a.force_hi && a.force_lo < khi)))
-                forced = true;
-            if (forced)
-                L = 0;
-            else if (a.sim != nullptr && L > 0 &&
-                     a.sim[(static_cast<int64_t>(b) * a.Hkv + hk) * a.NKB + kb] < a.cos_min)
-                L = 0;
-        }
-        out[kb] = L;
-    }
+    assign_levels(a, qb, b, hk, Ms, keys, lvl, tid);
+    int8_t* out = a.map + row * a.NKB;
+    for (int kb = tid; kb < a.NKB; kb += kAssignThreads) out[kb] = lvl[kb];
 }
 
 template <int MODE, int S>
@@ -1028,27 +865,7 @@ ScoreGeom score_geom(const Shape& s, const psa_mask_params& mp) {
     return g;
 }
 
-AssignArgs assign_args(const Shape& s, const psa_mask_params& mp) {
-    AssignArgs a{};
-    a.H = s.H;
-    a.Hkv = s.Hkv;
-    a.N = s.N;
-    a.Nv = s.Nv;
-    a.BQ = s.BQ;
-    a.BK = s.BK;
-    a.NQB = s.NQB;
-    a.NKB = s.NKB;
-    a.causal = s.causal;
-    int P = 1;
-    while (P < s.NKB) P <<= 1;
-    a.P = P;
-    for (int i = 0; i < 4; ++i) a.t[i] = static_cast<double>(mp.thresholds[i]);
-    a.cos_min = mp.cos_sim_min;
-    a.force_diag = mp.force_diag_l0 != 0;
-    a.force_lo = mp.force_l0_begin;
-    a.force_hi = mp.force_l0_end;
-    return a;
-}
+AssignArgs assign_args(const Shape& s, const psa_mask_params& mp) { return assign_args_of(s, mp); }
 
 hipError_t launch_assign(const Shape& s, const AssignArgs& a, hipStream_t st) {
     const int64_t rows = static_cast<int64_t>(s.B) * s.H * s.NQB;
@@ -1090,23 +907,14 @@ hipError_t launch_mask_scores(const Shape& s, const psa_mask_params& mp, const v
     if (mb.ws == nullptr || mb.ws_bytes < g.ws_bytes) return hipErrorInvalidValue;
     if (mp.mode == PSA_MASK_MEANKEY) {
         char* ws = static_cast<char*>(mb.ws);
-        MeanArgs m;
-        m.q = a.q;
-        m.k = a.k;
-        m.qbar = reinterpret_cast<float*>(ws + g.qbar_off);
-        m.kbar = reinterpret_cast<float*>(ws + g.kbar_off);
-        m.B = s.B; m.H = s.H; m.Hkv = s.Hkv; m.N = s.N; m.Nv = s.Nv; m.D = s.D;
-        m.BQ = s.BQ; m.BK = s.BK; m.NQB = s.NQB; m.NKB = s.NKB;
-        m.qs0 = s.qs[0]; m.qs1 = s.qs[1]; m.qs2 = s.qs[2];
-        m.ks0 = s.ks[0]; m.ks1 = s.ks[1]; m.ks2 = s.ks[2];
-        const int64_t items = static_cast<int64_t>(s.B) * (s.H * s.NQB + s.Hkv * s.NKB);
-        if (items == 0) return hipSuccess;
-        hipLaunchKernelGGL(k_block_means, dim3(static_cast<unsigned>(items)), dim3(256), 0, st, m);
-        hipError_t e = hipGetLastError();
+        float* qbar = reinterpret_cast<float*>(ws + g.qbar_off);
+        float* kbar = reinterpret_cast<float*>(ws + g.kbar_off);
+        if (static_cast<int64_t>(s.B) * (s.H * s.NQB + s.Hkv * s.NKB) == 0) return hipSuccess;
+        hipError_t e = launch_block_means(s, q, k, qbar, kbar, st);
         if (e != hipSuccess) return e;
         MeanKeyArgs k;
-        k.qbar = m.qbar;
-        k.kbar = m.kbar;
+        k.qbar = qbar;
+        k.kbar = kbar;
         k.L = static_cast<float*>(mb.ws);
         k.H = s.H; k.Hkv = s.Hkv; k.N = s.N; k.Nv = s.Nv; k.D = s.D; k.BQ = s.BQ; k.BK = s.BK;
         k.NQB = s.NQB; k.NKB = s.NKB; k.causal = s.causal;
@@ -1171,6 +979,23 @@ hipError_t launch_mask_assign_logmass(const Shape& s, const psa_mask_params& mp,
     a.sampling = mp.mode != PSA_MASK_ANTIDIAG;
     a.S = g.S;
     return launch_assign(s, a, st);
+}
+
+hipError_t launch_block_means(const Shape& s, const void* q, const void* k, float* qbar, float* kbar,
+                              hipStream_t st) {
+    MeanArgs m;
+    m.q = static_cast<const bf16_bits*>(q);
+    m.k = static_cast<const bf16_bits*>(k);
+    m.qbar = qbar;
+    m.kbar = kbar;
+    m.B = s.B; m.H = s.H; m.Hkv = s.Hkv; m.N = s.N; m.Nv = s.Nv; m.D = s.D;
+    m.BQ = s.BQ; m.BK = s.BK; m.NQB = s.NQB; m.NKB = s.NKB;
+    m.qs0 = s.qs[0]; m.qs1 = s.qs[1]; m.qs2 = s.qs[2];
+    m.ks0 = s.ks[0]; m.ks1 = s.ks[1]; m.ks2 = s.ks[2];
+    const int64_t items = static_cast<int64_t>(s.B) * (s.H * s.NQB + s.Hkv * s.NKB);
+    if (items == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_block_means, dim3(static_cast<unsigned>(items)), dim3(256), 0, st, m);
+    return hipGetLastError();
 }
 
 hipError_t launch_block_sim(const Shape& s, const void* k, float* block_sim, hipStream_t st) {

@@ -35,7 +35,8 @@ EXPORTS = ("psa_pooled_rows", "psa_build_pyramid", "psa_mask_workspace_bytes", "
            "psa_mask_assign", "psa_build_index", "psa_attn_workspace_bytes", "psa_attn_fwd",
            "psa_attn_fwd_indexed", "psa_attn_fwd_unpacked", "psa_attn_bwd_workspace_bytes",
            "psa_attn_bwd", "psa_quantize_fp8", "psa_attn_fwd_fp8qk", "psa_attn_fwd_fp8",
-           "psa_check_status", "psa_status_string", "psa_last_hip_error")
+           "psa_attn_fwd_meankey_workspace_bytes", "psa_attn_fwd_meankey", "psa_check_status",
+           "psa_status_string", "psa_last_hip_error")
 
 
 class PsaError(RuntimeError):
@@ -100,6 +101,10 @@ def lib() -> ctypes.CDLL:
         L.psa_attn_fwd_fp8qk.restype = I32
         L.psa_attn_fwd_fp8.argtypes = [P, ctypes.c_float] + [V] * 12 + [SZ, V]
         L.psa_attn_fwd_fp8.restype = I32
+        L.psa_attn_fwd_meankey_workspace_bytes.argtypes = [P]
+        L.psa_attn_fwd_meankey_workspace_bytes.restype = SZ
+        L.psa_attn_fwd_meankey.argtypes = [P, MP, ctypes.c_float] + [V] * 10 + [SZ, V]
+        L.psa_attn_fwd_meankey.restype = I32
         L.psa_check_status.argtypes, L.psa_check_status.restype = [V, V], I32
         L.psa_status_string.argtypes, L.psa_status_string.restype = [I32], ctypes.c_char_p
         L.psa_last_hip_error.argtypes, L.psa_last_hip_error.restype = [], I32
@@ -399,6 +404,33 @@ def attn_fwd_fp8(q8, q_scale, k8, k8_pooled, k_scale, v8, v8_pooled, v_scale, le
                                   _ptr(v8_pooled), _ptr(v_scale), _ptr(level_map), _ptr(out),
                                   _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)), "psa_attn_fwd_fp8")
     return out, lse
+
+
+def attn_fwd_meankey(q, k, v, k_pooled, v_pooled, prob: Problem, params: MaskParams, *,
+                     scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                     lse: Optional[torch.Tensor] = None, want_map: bool = True,
+                     want_mass: bool = False, ws: Optional[torch.Tensor] = None, stream=None):
+    """Block-mean scoring fused into the attention (params.mode must be "meankey"). Returns
+    (o, lse, level_map or None, block_mass or None)."""
+    dev = q.device
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=dev)
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    shape = (q.shape[0], q.shape[1], prob.n_qblocks, prob.n_kblocks)
+    lm = torch.empty(shape, dtype=torch.int8, device=dev) if want_map else None
+    mass = torch.empty(shape, dtype=torch.float32, device=dev) if want_mass else None
+    if ws is None:
+        n = lib().psa_attn_fwd_meankey_workspace_bytes(prob.ref())
+        if n == 0:
+            raise PsaError(PSA_ERR_INVALID_ARG, "psa_attn_fwd_meankey_workspace_bytes")
+        ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    cp = params.c()
+    _check(lib().psa_attn_fwd_meankey(prob.ref(), ctypes.byref(cp), ctypes.c_float(scale), _ptr(q),
+                                      _ptr(k), _ptr(v), _ptr(k_pooled), _ptr(v_pooled), _ptr(lm),
+                                      _ptr(mass), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
+                                      _stream(stream)), "psa_attn_fwd_meankey")
+    return out, lse, lm, mass
 
 
 def check_status(ws: torch.Tensor, stream=None) -> None:
