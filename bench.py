@@ -303,6 +303,10 @@ def run(args) -> dict:
                                           ptr(kp), ptr(vp), ptr(row_ptr), ptr(col_idx), ptr(o),
                                           ptr(lse), st), "attn unpacked")
         unpacked_ms = _timed_back_to_back(unpacked, stream, reps=4, warm=1)
+    meankey = None
+    if (not args.no_meankey and computed_map and wl.dtype == "bf16" and wl.block_q == 128
+            and nkb <= 1792):
+        meankey = _meankey_run(wl, prob, params, L, ptr, st, check, q, k, v, kp, vp, stream)
     bwd = None
     if not args.no_bwd and wl.dtype == "bf16":
         bwd = _bwd_run(wl, prob, L, ptr, st, check, q, k, v, kp, vp, lm_host, o, lse, stream, flops)
@@ -312,6 +316,8 @@ def run(args) -> dict:
         out["bwd"] = bwd
     if fp8 is not None:
         out["fp8"] = fp8
+    if meankey is not None:
+        out["meankey_fused"] = meankey
     out["attn"]["unpacked_same_map_ms"] = None if unpacked_ms != unpacked_ms else round(unpacked_ms, 3)
     out["attn"]["speedup_vs_unpacked"] = (None if unpacked_ms != unpacked_ms
                                           else round(unpacked_ms / attn_ms_mean, 2))
@@ -432,6 +438,62 @@ def _fp8_run(wl, prob, L, ptr, st, check, q, k, v, kp, vp, lm, stream, fwd_flops
     return out
 
 
+def _meankey_run(wl, prob, params, L, ptr, st, check, q, k, v, kp, vp, stream):
+    """Block-mean scoring, two ways, on the step's q, k, v and pyramid: psa_mask in block-mean
+    mode, psa_build_index and psa_attn_fwd_indexed (three calls), against psa_attn_fwd_meankey
+    (scoring, assignment and attention in one launch after the block means). Both write the map
+    and the masses; means of 10 calls run back to back. The map is checked equal."""
+    import ctypes
+    import dataclasses
+    import torch
+    dev = q.device
+    B, H, N, d = q.shape
+    nqb, nkb = wl.n_qblocks, wl.n_kblocks
+    mk = dataclasses.replace(params, mode="meankey")
+    cp = mk.c()
+    lm2 = torch.empty((B, H, nqb, nkb), dtype=torch.int8, device=dev)
+    lmf = torch.empty_like(lm2)
+    m2 = torch.empty((B, H, nqb, nkb), dtype=torch.float32, device=dev)
+    mf = torch.empty_like(m2)
+    sim = (torch.empty((B, wl.heads_kv, nkb), dtype=torch.float32, device=dev)
+           if wl.cos_sim_min > 0 else None)
+    nm = L.psa_mask_workspace_bytes(prob.ref(), ctypes.byref(cp))
+    mws = torch.empty(max(nm, 256), dtype=torch.uint8, device=dev)
+    nf = L.psa_attn_fwd_meankey_workspace_bytes(prob.ref())
+    fws = torch.empty(max(nf, 256), dtype=torch.uint8, device=dev)
+    rp = torch.empty(B * H * nqb * 4 + 1, dtype=torch.int32, device=dev)
+    ci = torch.empty(B * H * nqb * nkb, dtype=torch.int32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    o2, of = torch.empty_like(q), torch.empty_like(q)
+    l2 = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    lf = torch.empty_like(l2)
+
+    def two_step():
+        check(L.psa_mask(prob.ref(), ctypes.byref(cp), ptr(q), ptr(k), ptr(lm2), ptr(m2), ptr(sim),
+                         ptr(mws), mws.numel(), st), "mask meankey")
+        check(L.psa_build_index(prob.ref(), ptr(lm2), ptr(rp), ptr(ci), ptr(err), st), "index")
+        check(L.psa_attn_fwd_indexed(prob.ref(), ctypes.c_float(0.0), ptr(q), ptr(k), ptr(v),
+                                     ptr(kp), ptr(vp), ptr(rp), ptr(ci), ptr(o2), ptr(l2), st),
+              "attn")
+
+    def fused():
+        check(L.psa_attn_fwd_meankey(prob.ref(), ctypes.byref(cp), ctypes.c_float(0.0), ptr(q),
+                                     ptr(k), ptr(v), ptr(kp), ptr(vp), ptr(lmf), ptr(mf), ptr(of),
+                                     ptr(lf), ptr(fws), fws.numel(), st), "attn meankey")
+    two_ms = _timed_back_to_back(two_step, stream)
+    fused_ms = _timed_back_to_back(fused, stream)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(lm2, lmf) and torch.equal(o2, of))
+    lm_host = lmf.cpu().numpy()
+    pairs = executed_pairs(lm_host, wl)
+    tf = 4.0 * d * pairs / (fused_ms * 1e-3) / 1e12
+    return {"two_step_ms": round(two_ms, 4), "fused_ms": round(fused_ms, 4),
+            "speedup": round(two_ms / fused_ms, 3), "same_map_and_output": same,
+            "executed_pairs": int(pairs), "fused_tflops_executed": round(tf, 2),
+            "two_step": "psa_mask (block means, scores, assignment) + psa_build_index + psa_attn_fwd_indexed",
+            "fused": "psa_attn_fwd_meankey (block means, then one launch: scores, assignment, attention)"}
+
+
 def _dense_run(args, wl, prob, L, ptr, st, check, q, k, v, kp, vp, o, lse, row_ptr, col_idx,
                dev_err, stream):
     import ctypes
@@ -513,6 +575,8 @@ def main():
                     help="skip the psa_attn_bwd timing (reported beside the forward metric)")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the e4m3 forward timings (reported beside the forward metric)")
+    ap.add_argument("--no-meankey", action="store_true",
+                    help="skip the block-mean scoring comparison (two-step against fused)")
     ap.add_argument("--mask-mode", choices=("sampling", "antidiag", "meankey"), default=None,
                     help="score with this psa_mask mode instead of the workload's own")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
