@@ -582,8 +582,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(every (batch, head) is independent; see the sharding notes). Run with --gpus 1.",
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(every (batch, head) is independent, so heads would shard with no exchange). "
+              "Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
     wl = _workload(args)
