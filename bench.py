@@ -5,7 +5,8 @@
 
 One step = the whole path on one batch of synthetic, seeded input already resident in HBM:
 psa_build_pyramid, psa_mask (block scores, cosine check if any, threshold assignment),
-psa_build_index and the level-weighted attention kernel. The default workload is the
+psa_build_index and the level-weighted attention kernel. The pyramid and the mask are
+independent and run side by side on two streams; the attention waits for both. The default workload is the
 Wan2.1-1.3B-like 32k self-attention layer (12 heads, d 128, 32760 tokens padded to 32768,
 query/KV blocks 128/64, sampling-mode mask with thresholds 0.5/0.7/0.8/0.9).
 
@@ -225,10 +226,23 @@ def run(args) -> dict:
         if rc != 0:
             raise psa.PsaError(rc, what)
 
+    # The pyramid runs on a second stream beside the mask (they are independent: the pyramid
+    # reads K, V and writes the pooled levels; the mask reads Q, K). The fork waits for the
+    # previous step (its attention reads the pooled levels the pyramid overwrites); the
+    # attention waits for the pyramid. Both streams have the default priority.
+    side = torch.cuda.Stream(device=dev)
+    st2 = ctypes.c_void_p(side.cuda_stream)
+    fork, pyr_done = torch.cuda.Event(), torch.cuda.Event()
+
     def step(ev=None):
+        fork.record(stream)
+        side.wait_event(fork)
         if ev:
-            ev[0].record(stream)
-        check(L.psa_build_pyramid(prob.ref(), ptr(k), ptr(v), ptr(kp), ptr(vp), st), "pyramid")
+            ev[5].record(side)
+        check(L.psa_build_pyramid(prob.ref(), ptr(k), ptr(v), ptr(kp), ptr(vp), st2), "pyramid")
+        if ev:
+            ev[6].record(side)
+        pyr_done.record(side)
         if ev:
             ev[1].record(stream)
         if computed_map:
@@ -241,6 +255,7 @@ def run(args) -> dict:
             ev[2].record(stream)
         check(L.psa_build_index(prob.ref(), ptr(lm), ptr(row_ptr), ptr(col_idx), ptr(dev_err), st),
               "index")
+        stream.wait_event(pyr_done)
         if ev:
             ev[3].record(stream)
         check(L.psa_attn_fwd_indexed(prob.ref(), ctypes.c_float(0.0), ptr(q), ptr(k), ptr(v),
@@ -263,14 +278,16 @@ def run(args) -> dict:
     if int(dev_err.item()) != 0:
         raise RuntimeError("level map held invalid entries")
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    stage = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)]
+    # pyramid (side stream), mask, index (with the wait for the pyramid), attention
+    stage = np.array([[evs[i][5].elapsed_time(evs[i][6])] +
+                      [evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(1, 4)]
                       for i in range(args.steps)])
     st_ms = stage.mean(axis=0)
     attn_ms = float(np.median(stage[:, 3]))
