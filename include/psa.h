@@ -166,7 +166,8 @@ int psa_mask_assign(const psa_problem* prob, const psa_mask_params* params,
 /*
  * Block index: a CSR over (row, level) keys, rows r = (b*heads_q + h)*NQB + qb.
  * row_ptr[R*4+1] int32: col_idx[row_ptr[r*4+l] .. row_ptr[r*4+l+1]) lists, in ascending
- * order, the kb with level_map == l. col_idx needs capacity R*NKB int32. Entries outside
+ * order, the kb with level_map == l. col_idx needs capacity R*NKB int32; its entries past
+ * row_ptr[R*4] are unspecified (the call parks scan partial sums there). Entries outside
  * {-1..3} are treated as skip and set *dev_err (device int32) to PSA_ERR_BAD_LEVEL_MAP;
  * the call clears *dev_err first.
  */

@@ -62,7 +62,10 @@ def test_pyramid_parity(wl):
 # ---------------------------------------------------------------------------------------
 # block index
 # ---------------------------------------------------------------------------------------
-@pytest.mark.parametrize("shape", [(1, 3, 16, 16), (2, 5, 65, 130), (1, 1, 1, 1), (1, 4, 33, 66)])
+# (2, 24, 64, 128) and (1, 40, 129, 258): 12288 and 20640 (row, level) counts, i.e. three whole
+# scan tiles of 4096 and six with a ragged last one
+@pytest.mark.parametrize("shape", [(1, 3, 16, 16), (2, 5, 65, 130), (1, 1, 1, 1), (1, 4, 33, 66),
+                                   (2, 24, 64, 128), (1, 40, 129, 258)])
 def test_build_index_exact(shape):
     announce(f"build_index {shape}")
     rng = np.random.default_rng(sum(shape))
@@ -83,6 +86,18 @@ def test_build_index_exact(shape):
     rp = row_ptr.cpu().numpy()
     assert np.array_equal(rp, rp_ref)
     assert np.array_equal(col_idx.cpu().numpy()[:rp[-1]], ci_ref)
+    assert err.item() == 0
+
+
+def test_build_index_all_skip_many_tiles():
+    """An all-skip map over six scan tiles: every row pointer is 0 (nothing listed, fewer
+    listed entries than tiles)."""
+    announce("build_index all skip, many tiles")
+    lm = np.full((1, 40, 129, 258), -1, dtype=np.int8)
+    q = torch.zeros((1, 40, 258 * 64, 64), device=DEV, dtype=torch.bfloat16)
+    prob = psa.make_problem(q, q, q, block_q=128)
+    row_ptr, col_idx, err = psa.build_index(torch.from_numpy(lm).to(DEV), prob)
+    assert not np.any(row_ptr.cpu().numpy())
     assert err.item() == 0
 
 

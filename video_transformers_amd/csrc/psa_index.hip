@@ -4,10 +4,14 @@
 // touches a skipped block (PSA summary article at rg.mbintangr.com, "Method": the least
 // important blocks are skipped entirely).
 //
-// Three launches, all integer and deterministic:
-//   k_index_count  one wave per row: per-level counts via ballots (bad entries -> skip + flag)
-//   k_index_scan   one workgroup: exclusive scan of the R*4 counts into row_ptr
-//   k_index_fill   one wave per row: ballot compaction of each level's kb into col_idx
+// Four launches, all integer and deterministic:
+//   k_index_count       one wave per row: per-level counts via ballots (bad entries -> skip + flag)
+//   k_index_tile_sums   one workgroup per tile of 4096 counts: the tile's total
+//   k_index_scan_tiles  one workgroup per tile: the totals of the tiles before it, then the
+//                       tile's inclusive scan into row_ptr (in place)
+//   k_index_fill        one wave per row: ballot compaction of each level's kb into col_idx
+// The tile totals are parked at the start of col_idx, which the fill overwrites afterwards
+// (its capacity, rows * NKB, is at least the number of tiles).
 #include "psa_device.h"
 #include "psa_internal.h"
 
@@ -49,32 +53,72 @@ __global__ void __launch_bounds__(256)
     }
 }
 
-// Exclusive scan of counts held in row_ptr[1..n] into row_ptr[0..n] (row_ptr[0] = 0).
-// One workgroup of 1024 threads; each thread owns a contiguous chunk.
-__global__ void __launch_bounds__(1024) k_index_scan(int32_t* __restrict__ row_ptr, int64_t n) {
-    __shared__ int64_t part[1024];
-    const int t = threadIdx.x;
-    const int64_t chunk = (n + 1023) / 1024;
-    const int64_t lo = t * chunk;
-    const int64_t hi = lo + chunk < n ? lo + chunk : n;
-    int64_t s = 0;
-    for (int64_t i = lo; i < hi; ++i) s += row_ptr[i + 1];
-    part[t] = s;
+// Scan of the counts held in row_ptr[1..n] into their inclusive prefix sums (row_ptr[0] = 0),
+// in tiles of kScanTile counts, kScanPer consecutive counts per thread.
+constexpr int kScanThreads = 1024;
+constexpr int kScanPer = 4;
+constexpr int kScanTile = kScanThreads * kScanPer;
+
+// Inclusive scan of one value per thread over the workgroup; `total` receives the sum.
+__device__ int64_t block_inclusive_scan(int64_t v, int64_t& total) {
+    __shared__ int64_t wsum[kScanThreads / 64];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int64_t y = __shfl_up(v, o, 64);
+        if (lane >= o) v += y;
+    }
+    if (lane == 63) wsum[wave] = v;
     __syncthreads();
-    // Hillis-Steele inclusive scan over the 1024 partial sums.
-    for (int off = 1; off < 1024; off <<= 1) {
-        int64_t add = t >= off ? part[t - off] : 0;
-        __syncthreads();
-        part[t] += add;
-        __syncthreads();
+    int64_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kScanThreads / 64; ++w) {
+        const int64_t x = wsum[w];
+        if (w < wave) before += x;
+        all += x;
     }
-    int64_t run = part[t] - s;  // exclusive prefix of this chunk
-    for (int64_t i = lo; i < hi; ++i) {
-        const int64_t c = row_ptr[i + 1];
-        run += c;
-        row_ptr[i + 1] = static_cast<int32_t>(run);
+    __syncthreads();   // wsum is reused by the next call
+    total = all;
+    return before + v;
+}
+
+__global__ void __launch_bounds__(kScanThreads)
+    k_index_tile_sums(const int32_t* __restrict__ row_ptr, int64_t n, int32_t* __restrict__ sums) {
+    const int64_t i0 = static_cast<int64_t>(blockIdx.x) * kScanTile + threadIdx.x * kScanPer;
+    int64_t s = 0;
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j)
+        if (i0 + j < n) s += row_ptr[i0 + j + 1];
+    int64_t total;
+    block_inclusive_scan(s, total);
+    if (threadIdx.x == 0) sums[blockIdx.x] = static_cast<int32_t>(total);
+}
+
+__global__ void __launch_bounds__(kScanThreads)
+    k_index_scan_tiles(int32_t* __restrict__ row_ptr, int64_t n, const int32_t* __restrict__ sums) {
+    // the totals of the tiles before this one
+    int64_t b = 0;
+    for (int k = threadIdx.x; k < static_cast<int>(blockIdx.x); k += kScanThreads) b += sums[k];
+    int64_t base;
+    block_inclusive_scan(b, base);
+    const int64_t i0 = static_cast<int64_t>(blockIdx.x) * kScanTile + threadIdx.x * kScanPer;
+    int32_t c[kScanPer];
+    int64_t s = 0;
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) {
+        c[j] = i0 + j < n ? row_ptr[i0 + j + 1] : 0;
+        s += c[j];
     }
-    if (t == 0) row_ptr[0] = 0;
+    int64_t total;
+    int64_t run = base + block_inclusive_scan(s, total) - s;   // exclusive prefix of this thread
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j)
+        if (i0 + j < n) {
+            run += c[j];
+            row_ptr[i0 + j + 1] = static_cast<int32_t>(run);
+        }
+    if (blockIdx.x == 0 && threadIdx.x == 0) row_ptr[0] = 0;
 }
 
 __global__ void __launch_bounds__(256)
@@ -116,7 +160,11 @@ hipError_t launch_build_index(const Shape& s, const int8_t* level_map, const Ind
     hipLaunchKernelGGL(k_index_count, dim3(blocks), dim3(256), 0, st, level_map, rows, s.NKB,
                        ib.row_ptr, ib.dev_err);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(k_index_scan, dim3(1), dim3(1024), 0, st, ib.row_ptr, rows * 4);
+    const int64_t n = rows * 4;
+    const unsigned tiles = static_cast<unsigned>((n + kScanTile - 1) / kScanTile);
+    hipLaunchKernelGGL(k_index_tile_sums, dim3(tiles), dim3(kScanThreads), 0, st, ib.row_ptr, n, ib.col_idx);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_index_scan_tiles, dim3(tiles), dim3(kScanThreads), 0, st, ib.row_ptr, n, ib.col_idx);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k_index_fill, dim3(blocks), dim3(256), 0, st, level_map, rows, s.NKB,
                        ib.row_ptr, ib.col_idx);
