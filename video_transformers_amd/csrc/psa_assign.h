@@ -148,10 +148,14 @@ __device__ inline void assign_levels(const AssignArgs& a, int qb, int b, int hk,
     }
     for (int i = tid; i < a.NKB; i += kAssignThreads) lvl[i] = -1;
     __syncthreads();
-    // bitonic sort, ascending keys = mass descending, kb ascending
-    for (int size = 2; size <= a.P; size <<= 1) {
+    // bitonic sort, ascending keys = mass descending, kb ascending, of the first Pr keys: the
+    // candidates padded to a power of two (causal rows have fewer); the keys past them are
+    // all ~0 and already in place at the end
+    int Pr = 1;
+    while (Pr < ncand) Pr <<= 1;
+    for (int size = 2; size <= Pr; size <<= 1) {
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < a.P / 2; i += kAssignThreads) {
+            for (int i = tid; i < Pr / 2; i += kAssignThreads) {
                 const int lo = 2 * i - (i & (stride - 1));
                 const int hi = lo + stride;
                 const bool up = ((lo & size) == 0);
