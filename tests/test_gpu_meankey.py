@@ -76,3 +76,19 @@ def test_meankey_fused_fullsize_wan():
     print(f"[{wl.name}] masses differing: {int(dm.sum())} of {M.numel()}", flush=True)
     assert torch.equal(lmf, lm) and torch.equal(Mf, M)
     assert torch.equal(of, o) and torch.equal(lsef, lse)
+
+
+def test_meankey_fused_max_blocks():
+    """At the fused call's limit of 1792 KV blocks (114688 tokens, GQA 2:1, 8 pad tokens), where
+    the prologue's scratch (query mean, log-masses, masses, levels; a 2048-key sort) nearly
+    fills the tile buffers it borrows: the same map, masses, o and lse as the two-step path."""
+    wl = W.WAN13B_32K.replace(name="meankey-1792-blocks", heads_q=2, heads_kv=1, seq_len=114688,
+                              seq_valid=114680, mask_mode="meankey")
+    assert wl.n_kblocks == 1792
+    announce(f"fused block-mean scoring at 1792 KV blocks {wl.name}")
+    q, k, v = W.make_qkv(wl)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    (lm, M, o, lse), (lmf, Mf, of, lsef) = _both(wl, qd, kd, vd)
+    assert torch.equal(lmf, lm), "map differs from psa_mask's"
+    assert torch.equal(Mf, M), "block masses differ from psa_mask's"
+    assert torch.equal(of, o) and torch.equal(lsef, lse), "attention differs from psa_attn_fwd's"
