@@ -50,7 +50,13 @@
  * Supported domain (anything else returns PSA_ERR_UNSUPPORTED): dtype f32 or bf16;
  * head_dim 64 or 128; block_k 64; block_q 64 or 128; seq_len a multiple of block_q;
  * 0 <= seq_valid <= seq_len with (seq_len - seq_valid) a multiple of 8 (so that every pooled
- * token is either wholly valid or wholly padding).
+ * token is either wholly valid or wholly padding). The attention calls (forward, fp8,
+ * backward) need seq_len/64 <= 16384: a row's block list is staged in LDS. psa_mask and
+ * psa_mask_assign need one row's assignment to fit 64 KB of LDS: 8*P + 5*NKB bytes, plus
+ * 4*NKB*RQ when scoring (P = NKB rounded up to a power of two, NKB = seq_len/64, RQ = the
+ * scoring rows per query block: samples_per_qblock, block_q/antidiag_stride, or 1 for block
+ * means), e.g. NKB <= 1328 with 8 samples, NKB <= 831 with antidiagonal stride 8 and block_q
+ * 128. Checked on the host before anything is enqueued.
  */
 #ifndef PSA_H_
 #define PSA_H_

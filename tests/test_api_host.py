@@ -287,3 +287,41 @@ def test_attn_fwd_meankey_host_checks():
     assert call(big, n=1 << 40) == P.PSA_ERR_UNSUPPORTED          # more than 1792 KV blocks
     p.c.dtype = P.PSA_F32
     assert call(p, n=1 << 30) == P.PSA_ERR_UNSUPPORTED
+
+
+def _big(nkb, block_q=128):
+    q = torch.zeros(1, 1, 64, 128)
+    p = psa.make_problem(q, q, q, block_q=64)
+    p.c.seq_len = p.c.seq_valid = nkb * 64
+    p.c.block_q = block_q
+    for st in (p.c.q_stride, p.c.k_stride, p.c.v_stride, p.c.o_stride):
+        st[0] = st[1] = nkb * 64 * 128
+        st[2] = 128
+    p.c.dtype = P.PSA_BF16
+    return p
+
+
+# sampling, 8 samples: 8 * 2048 + 37 * NKB <= 65536 up to NKB = 1328 (block_q 64 keeps every
+# NKB a whole number of query blocks); antidiagonal, stride 8, block_q 128 (16 scoring rows):
+# 8 * 1024 + 69 * NKB <= 65536 up to NKB = 831, i.e. 830 with whole 128-token query blocks
+@pytest.mark.parametrize("mode,nkb,bq,ok", [("sampling", 1328, 64, True), ("sampling", 1329, 64, False),
+                                            ("antidiag", 830, 128, True), ("antidiag", 832, 128, False)])
+def test_mask_assignment_lds_limit(mode, nkb, bq, ok):
+    """psa_mask refuses, before enqueueing anything, a problem whose per-row assignment would
+    not fit 64 KB of LDS (sort keys, masses, staged log-masses, levels)."""
+    p = _big(nkb, bq)
+    mp = psa.MaskParams(mode=mode).c()
+    L = psa.lib()
+    d = ctypes.c_void_p(256)
+    rc = L.psa_mask(p.ref(), ctypes.byref(mp), d, d, d, d, d, d, 0, None)
+    # within the limit the call gets as far as the workspace check (none given)
+    assert rc == (P.PSA_ERR_WORKSPACE if ok else P.PSA_ERR_UNSUPPORTED)
+
+
+def test_attention_block_limit():
+    """The attention calls refuse seq_len/64 > 16384 (a row's block list is staged in LDS)."""
+    L = psa.lib()
+    d = ctypes.c_void_p(256)
+    for nkb, want in ((16385, P.PSA_ERR_UNSUPPORTED), (16384, P.PSA_ERR_WORKSPACE)):
+        p = _big(nkb)
+        assert L.psa_attn_fwd(p.ref(), 0.0, d, d, d, d, d, d, d, None, d, 0, None) == want

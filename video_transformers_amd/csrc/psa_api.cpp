@@ -171,6 +171,7 @@ int psa_mask(const psa_problem* prob, const psa_mask_params* params, const void*
     if (rc != PSA_OK) return rc;
     if ((rc = check_mask_params(prob, params)) != PSA_OK) return rc;
     if (s.dtype != PSA_BF16) return PSA_ERR_UNSUPPORTED;
+    if (psa::assign_lds_bytes(s, *params, true) > psa::kAssignMaxLds) return PSA_ERR_UNSUPPORTED;
     if (no_work(s)) return PSA_OK;
     if (!q || !k || !level_map || !block_mass) return PSA_ERR_INVALID_ARG;
     if (params->cos_sim_min > 0.f && block_sim == nullptr) return PSA_ERR_INVALID_ARG;
@@ -196,6 +197,7 @@ int psa_mask_assign(const psa_problem* prob, const psa_mask_params* params,
     int rc = check_problem(prob, &s);
     if (rc != PSA_OK) return rc;
     if ((rc = check_mask_params(prob, params)) != PSA_OK) return rc;
+    if (psa::assign_lds_bytes(s, *params, false) > psa::kAssignMaxLds) return PSA_ERR_UNSUPPORTED;
     if (no_work(s)) return PSA_OK;
     if (!block_mass || !level_map) return PSA_ERR_INVALID_ARG;
     const bool use_sim = params->cos_sim_min > 0.f;
@@ -228,6 +230,7 @@ int psa_attn_fwd(const psa_problem* prob, float softmax_scale, const void* q, co
     psa::Shape s;
     int rc = check_problem(prob, &s);
     if (rc != PSA_OK) return rc;
+    if (s.NKB > psa::kAttnMaxKBlocks) return PSA_ERR_UNSUPPORTED;
     if (no_work(s)) return PSA_OK;
     if (!q || !k || !v || !k_pooled || !v_pooled || !level_map || !o) return PSA_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_pooled) ||
@@ -256,6 +259,7 @@ int attn_indexed(const psa_problem* prob, float softmax_scale, const void* q, co
     psa::Shape s;
     int rc = check_problem(prob, &s);
     if (rc != PSA_OK) return rc;
+    if (s.NKB > psa::kAttnMaxKBlocks) return PSA_ERR_UNSUPPORTED;
     if (!pack && s.dtype != PSA_BF16) return PSA_ERR_UNSUPPORTED;
     if (no_work(s)) return PSA_OK;
     if (!q || !k || !v || !k_pooled || !v_pooled || !row_ptr || !col_idx || !o)
@@ -322,6 +326,7 @@ int psa_attn_fwd_fp8qk(const psa_problem* prob, float softmax_scale, const uint8
     psa::Shape s;
     int rc = check_problem(prob, &s);
     if (rc != PSA_OK) return rc;
+    if (s.NKB > psa::kAttnMaxKBlocks) return PSA_ERR_UNSUPPORTED;
     if (s.dtype != PSA_BF16 || s.D != 128) return PSA_ERR_UNSUPPORTED;
     if (no_work(s)) return PSA_OK;
     if (!q8 || !q_scale || !k8 || !k8_pooled || !k_scale || !v || !v_pooled || !level_map || !o)
@@ -352,6 +357,7 @@ int psa_attn_fwd_fp8(const psa_problem* prob, float softmax_scale, const uint8_t
     psa::Shape s;
     int rc = check_problem(prob, &s);
     if (rc != PSA_OK) return rc;
+    if (s.NKB > psa::kAttnMaxKBlocks) return PSA_ERR_UNSUPPORTED;
     if (s.dtype != PSA_BF16 || s.D != 128) return PSA_ERR_UNSUPPORTED;
     if (no_work(s)) return PSA_OK;
     if (!q8 || !q_scale || !k8 || !k8_pooled || !k_scale || !v8 || !v8_pooled || !v_scale ||
@@ -451,6 +457,7 @@ int psa_attn_bwd(const psa_problem* prob, float softmax_scale, const void* q, co
     psa::Shape s;
     int rc = check_problem(prob, &s);
     if (rc != PSA_OK) return rc;
+    if (s.NKB > psa::kAttnMaxKBlocks) return PSA_ERR_UNSUPPORTED;
     if (s.dtype != PSA_BF16) return PSA_ERR_UNSUPPORTED;
     // the key-side kernel lists (query head, query block) rows in LDS beside its three chunk
     // buffer sets and the P/dS exchange: 12-bit query block index, at most 7680 rows per KV head

@@ -77,6 +77,12 @@ struct MaskBufs {
 };
 
 size_t mask_workspace_bytes(const Shape& s, const psa_mask_params& mp);
+// LDS of one threshold-assignment workgroup (sort keys, masses, staged log-masses when the
+// masses come from log-masses, levels); it must not exceed kAssignMaxLds.
+constexpr size_t kAssignMaxLds = 64 * 1024;
+size_t assign_lds_bytes(const Shape& s, const psa_mask_params& mp, bool from_log_masses);
+// Attention and its backward stage a row's block list (NKB int32) in LDS beside the tiles.
+constexpr int kAttnMaxKBlocks = 16384;
 
 hipError_t launch_mask_scores(const Shape& s, const psa_mask_params& mp, const void* q,
                               const void* k, const MaskBufs& mb, hipStream_t st);

@@ -867,14 +867,18 @@ ScoreGeom score_geom(const Shape& s, const psa_mask_params& mp) {
 
 AssignArgs assign_args(const Shape& s, const psa_mask_params& mp) { return assign_args_of(s, mp); }
 
+// sort keys, masses, (log-mass path) the staged log-masses, levels
+size_t assign_bytes(const Shape& s, int P, int RQ, bool from_log_masses) {
+    return static_cast<size_t>(P) * sizeof(uint64_t) + static_cast<size_t>(s.NKB) * sizeof(float) +
+           (from_log_masses ? static_cast<size_t>(s.NKB) * RQ * sizeof(float) : 0) +
+           static_cast<size_t>(s.NKB);
+}
+
 hipError_t launch_assign(const Shape& s, const AssignArgs& a, hipStream_t st) {
     const int64_t rows = static_cast<int64_t>(s.B) * s.H * s.NQB;
     if (rows == 0) return hipSuccess;
-    // sort keys, masses, (log-mass path) the staged log-masses, levels
-    const size_t lds = static_cast<size_t>(a.P) * sizeof(uint64_t) + static_cast<size_t>(s.NKB) * sizeof(float) +
-                       (a.L != nullptr ? static_cast<size_t>(s.NKB) * a.RQ * sizeof(float) : 0) +
-                       static_cast<size_t>(s.NKB);
-    if (lds > 64 * 1024) return hipErrorNotSupported;
+    const size_t lds = assign_bytes(s, a.P, a.RQ, a.L != nullptr);
+    if (lds > kAssignMaxLds) return hipErrorNotSupported;
     hipLaunchKernelGGL(k_mask_assign, dim3(static_cast<unsigned>(rows)), dim3(kAssignThreads), lds, st, a);
     return hipGetLastError();
 }
@@ -883,6 +887,10 @@ hipError_t launch_assign(const Shape& s, const AssignArgs& a, hipStream_t st) {
 
 size_t mask_workspace_bytes(const Shape& s, const psa_mask_params& mp) {
     return score_geom(s, mp).ws_bytes;
+}
+
+size_t assign_lds_bytes(const Shape& s, const psa_mask_params& mp, bool from_log_masses) {
+    return assign_bytes(s, assign_args_of(s, mp).P, score_geom(s, mp).RQ, from_log_masses);
 }
 
 hipError_t launch_mask_scores(const Shape& s, const psa_mask_params& mp, const void* q,
