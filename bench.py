@@ -571,6 +571,11 @@ def _report(args, wl, flops, pairs, dpairs, frac, d, B, H, N, computed_map, attn
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic,
+                     # the counted bytes over this run's kernel time: what the L2s fetch from
+                     # the fabric (HBM or the Infinity Cache), against the HBM peak
+                     "traffic_gbs": None if traffic is None else round(traffic / (attn_ms_mean * 1e-3) / 1e9, 1),
+                     "traffic_vs_hbm_peak": (None if traffic is None
+                                             else round(traffic / (attn_ms_mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)),
                      "kernel": "k_attn_fwd_bf16" if wl.dtype == "bf16" else "k_attn_fwd_f32",
                      "per_launch": f"{flops:.4e} executed FLOP (4*d per executed pair)"},
     }
