@@ -537,7 +537,7 @@ def pin_fp8qk_reduces_to_attention(causal=False):
     o, lse = oracle.attention_head(q8 * s_q, k8 * s_k, v, lm, p)
     both = np.isfinite(lse) & np.isfinite(l8)
     same_inf = np.array_equal(np.isfinite(lse), np.isfinite(l8))
-    return max(np.nanmax(np.abs(o8 - o)), np.abs(np.where(both, l8 - lse, 0.0)).max(),
+    return max(np.nanmax(np.abs(o8 - o)), np.abs(l8[both] - lse[both]).max(initial=0.0),
                0.0 if same_inf else np.inf)
 
 
@@ -602,5 +602,130 @@ def pin_fp8pv_powers_of_two(causal=False):
     o, lse = oracle.attention_head(q8, k8, v8 * s_v, lm, p)
     both = np.isfinite(lse) & np.isfinite(l8)
     same_inf = np.array_equal(np.isfinite(lse), np.isfinite(l8))
-    return max(np.nanmax(np.abs(o8 - o)), np.abs(np.where(both, l8 - lse, 0.0)).max(),
+    return max(np.nanmax(np.abs(o8 - o)), np.abs(l8[both] - lse[both]).max(initial=0.0),
                0.0 if same_inf else np.inf)
+
+
+# ---------------------------------------------------------------------------------------
+# Sampling scores with padding: every valid row of every query block sampled exactly twice
+# (S = BQ on blocks of BQ valid rows; the last block holds BQ / 2 valid rows, so the offsets
+# floor(s * r / S) name each of them twice). The scores then equal the dense softmax block
+# mass over the valid keys only, averaged over each block's valid rows (torch, fp64). The pad
+# keys hold random non-zero values, so a pad key that stays visible takes mass.
+# ---------------------------------------------------------------------------------------
+def pin_sampling_padded(causal=False):
+    n, d, bq = 512, 16, 64
+    nv = n - bq // 2
+    p = oracle.Problem(seq_len=n, seq_valid=nv, head_dim=d, block_q=bq, block_k=64,
+                       causal=causal)
+    q, k, _ = rand_qkv(n, d, seed=15)
+    M = oracle.mask_scores_sampling(q, k, p, samples=bq)
+    z = (_t(q) @ _t(k).T) / math.sqrt(d)
+    i = torch.arange(n)
+    keep = (i[None, :] < nv).expand(n, n)
+    if causal:
+        keep = keep & (i[None, :] <= i[:, None])
+    pr = torch.softmax(z.masked_fill(~keep, float("-inf")), dim=-1).numpy()
+    mass = pr.reshape(n, p.n_kblocks, 64).sum(-1)
+    ref = np.stack([mass[qb * bq: min((qb + 1) * bq, nv)].mean(axis=0)
+                    for qb in range(p.n_qblocks)])
+    return max(np.abs(M - ref).max(), np.abs(M.sum(1) - 1).max())
+
+
+# ---------------------------------------------------------------------------------------
+# GQA grouping (4 query heads on 2 KV heads). The whole-tensor wrappers are held to
+# library routines that fix the grouping independently of the oracle: torch's
+# scaled_dot_product_attention with enable_gqa (query heads 2j and 2j + 1 read KV head j)
+# for the all-level-0 forward, torch autograd through it for the backward (a KV head's
+# gradient sums its query heads), and dense block masses from torch for the scores (sampling
+# with every row, antidiagonal with stride 1). For a mixed-level map each query head is held
+# to attention_head on the KV head the table KV_OF names. The similarity check is pinned by
+# keys built so that KV head 0's blocks pass it (identical keys) and KV head 1's fail it
+# (orthogonal keys): only query heads 0 and 1 may keep pooled levels.
+# ---------------------------------------------------------------------------------------
+KV_OF = (0, 0, 1, 1)
+
+
+def _gqa_inputs(n=256, d=16, seed=40, nv=None):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((1, 4, n, d))
+    k = rng.standard_normal((1, 2, n, d))
+    v = rng.standard_normal((1, 2, n, d))
+    return q, k, v
+
+
+def pin_gqa_attention(causal=False):
+    n, d = 256, 16
+    nv = n - 8
+    p = oracle.Problem(seq_len=n, seq_valid=nv, head_dim=d, block_q=64, block_k=64,
+                       causal=causal)
+    q, k, v = _gqa_inputs(n, d)
+    lm0 = np.zeros((1, 4, p.n_qblocks, p.n_kblocks), dtype=np.int8)
+    o, lse = oracle.attention(q, k, v, lm0, p)
+    i = torch.arange(n)
+    keep = (i[None, :] < nv).expand(n, n)
+    if causal:
+        keep = keep & (i[None, :] <= i[:, None])
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        _t(q), _t(k), _t(v), attn_mask=keep[None, None], scale=1.0 / math.sqrt(d),
+        enable_gqa=True).numpy()
+    err = np.abs(o[..., :nv, :] - ref[..., :nv, :]).max()
+    rng = np.random.default_rng(41)
+    lm = rng.choice(np.array([0, 1, 2, 3, -1], dtype=np.int8), size=lm0.shape)
+    for qb in range(p.n_qblocks):
+        lm[..., qb, (qb * 64) // 64] = 0
+    o2, l2 = oracle.attention(q, k, v, lm, p)
+    for h in range(4):
+        oh, lh = oracle.attention_head(q[0, h], k[0, KV_OF[h]], v[0, KV_OF[h]], lm[0, h], p)
+        fin = np.isfinite(lh)
+        if not np.array_equal(fin, np.isfinite(l2[0, h])):
+            return np.inf
+        err = max(err, np.abs(o2[0, h] - oh).max(), np.abs(l2[0, h][fin] - lh[fin]).max())
+    return err
+
+
+def pin_gqa_backward(causal=False):
+    n, d = 128, 8
+    p = oracle.Problem(seq_len=n, seq_valid=n, head_dim=d, block_q=64, block_k=64,
+                       causal=causal)
+    q, k, v = _gqa_inputs(n, d, seed=42)
+    do = np.random.default_rng(43).standard_normal(q.shape)
+    lm = np.zeros((1, 4, p.n_qblocks, p.n_kblocks), dtype=np.int8)
+    dq, dk, dv = oracle.attention_backward(q, k, v, lm, do, p)
+    tq, tk, tv = (_t(x).clone().requires_grad_(True) for x in (q, k, v))
+    i = torch.arange(n)
+    keep = torch.ones(n, n, dtype=torch.bool)
+    if causal:
+        keep = i[None, :] <= i[:, None]
+    o = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, attn_mask=keep[None, None], scale=1.0 / math.sqrt(d), enable_gqa=True)
+    (o * _t(do)).sum().backward()
+    return max(np.abs(dq - tq.grad.numpy()).max(), np.abs(dk - tk.grad.numpy()).max(),
+               np.abs(dv - tv.grad.numpy()).max())
+
+
+def pin_gqa_mask():
+    n, d = 256, 16
+    p = oracle.Problem(seq_len=n, seq_valid=n, head_dim=d, block_q=64, block_k=64)
+    q, k, _ = _gqa_inputs(n, d, seed=44)
+    a = oracle.AssignParams((0.5, 0.7, 0.8, 0.9))
+    err = 0.0
+    z = (_t(q) @ _t(k)[:, [0, 0, 1, 1]].transpose(-1, -2)) / math.sqrt(d)
+    pr = torch.softmax(z, dim=-1).numpy()[0]
+    ref = pr.reshape(4, n, p.n_kblocks, 64).sum(-1).reshape(4, p.n_qblocks, 64, -1).mean(2)
+    _, Ms, _ = oracle.mask(q, k, p, "sampling", a, samples=64)
+    _, Ma, _ = oracle.mask(q, k, p, "antidiag", a, stride=1)
+    err = max(err, np.abs(Ms[0] - ref).max(), np.abs(Ma[0] - ref).max())
+    # similarity: KV head 0 blocks of identical keys (similarity 1), KV head 1 blocks of
+    # independent Gaussian keys (similarity near 0); with the cosine bound 0.8 only KV head 0
+    # may pool
+    ks = np.zeros((1, 2, n, d))
+    rng = np.random.default_rng(45)
+    for kb in range(p.n_kblocks):
+        ks[0, 0, kb * 64:(kb + 1) * 64] = rng.standard_normal(d)
+    ks[0, 1] = rng.standard_normal((n, d))
+    ac = oracle.AssignParams((0.3, 0.6, 0.8, 1.0), cos_sim_min=0.8)
+    lm, _, sim = oracle.mask(q, ks, p, "sampling", ac, samples=8)
+    pooled = [bool((lm[0, h] > 0).any()) for h in range(4)]
+    ok = sim[0, 0].min() > 0.99 and sim[0, 1].max() < 0.5 and pooled == [True, True, False, False]
+    return err if ok else np.inf

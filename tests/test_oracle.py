@@ -45,6 +45,25 @@ def test_p8_sampling_all_rows(causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+def test_p8_sampling_padded(causal):
+    assert pins.pin_sampling_padded(causal) < TOL
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_attention_grouping(causal):
+    assert pins.pin_gqa_attention(causal) < TOL
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_backward_grouping(causal):
+    assert pins.pin_gqa_backward(causal) < TOL
+
+
+def test_gqa_mask_grouping():
+    assert pins.pin_gqa_mask() < TOL
+
+
+@pytest.mark.parametrize("causal", [False, True])
 def test_p8_antidiag_stride1(causal):
     assert pins.pin_antidiag_stride1(causal) < TOL
 

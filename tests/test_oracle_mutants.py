@@ -25,6 +25,10 @@ ALL_PINS = {
     "p6": pins.pin_weight_multiplicity,
     "p7": pins.pin_pyramid,
     "p8s": lambda: max(pins.pin_sampling_all_rows(False), pins.pin_sampling_all_rows(True)),
+    "p8s_pad": lambda: max(pins.pin_sampling_padded(False), pins.pin_sampling_padded(True)),
+    "gqa": lambda: max(pins.pin_gqa_attention(False), pins.pin_gqa_attention(True),
+                       pins.pin_gqa_mask()),
+    "gqa_bwd": lambda: max(pins.pin_gqa_backward(False), pins.pin_gqa_backward(True)),
     "p8a": lambda: max(pins.pin_antidiag_stride1(False), pins.pin_antidiag_stride1(True),
                        pins.pin_antidiag_orientation_and_sum()),
     "p8c": pins.pin_cossim,
@@ -59,6 +63,19 @@ MUTANTS = [
      "vis = last[None, :] < p.seq_len\n        if p.causal"),
     ("antidiag_no_reverse", "qs = q.reshape(R, S, d)[:, ::-1, :]", "qs = q.reshape(R, S, d)[:, :, :]"),
     ("antidiag_mean", "A = p.scale * (qs @ ks.T)", "A = p.scale * (qs @ ks.T) / S"),
+    ("sampling_pad_keys_visible", "vis = keys[None, :] < p.seq_valid", "vis = keys[None, :] < p.seq_len"),
+    ("gqa_modulo_attention", "attention_head(q[b, h], k[b, h // g], v[b, h // g],",
+     "attention_head(q[b, h], k[b, h % k.shape[1]], v[b, h % k.shape[1]],"),
+    ("gqa_modulo_backward", "attention_backward_head(q[b, h], k[b, h // g], v[b, h // g],",
+     "attention_backward_head(q[b, h], k[b, h % k.shape[1]], v[b, h % k.shape[1]],"),
+    ("gqa_modulo_backward_sum", "dk[b, h // g] += bk\n            dv[b, h // g] += bv",
+     "dk[b, h % k.shape[1]] += bk\n            dv[b, h % k.shape[1]] += bv"),
+    ("gqa_modulo_mask_sampling", "mask_scores_sampling(q[b, h], k[b, h // g], p, samples)",
+     "mask_scores_sampling(q[b, h], k[b, h % Hkv], p, samples)"),
+    ("gqa_modulo_mask_antidiag", "mask_scores_antidiag(q[b, h], k[b, h // g], p, stride)",
+     "mask_scores_antidiag(q[b, h], k[b, h % Hkv], p, stride)"),
+    ("gqa_modulo_mask_sim", "None if sim is None else sim[b, h // g], p, a)",
+     "None if sim is None else sim[b, h % Hkv], p, a)"),
     ("sampling_no_causal", "vis = vis & (keys[None, :] <= rows[:, None])", "vis = vis"),
     ("cossim_keeps_diagonal", "sim[kb] = cos[off].sum()", "sim[kb] = cos.sum()"),
     ("meankey_no_count", "p.scale * (kbar[ok] @ qbar) + np.log(nv[ok])", "p.scale * (kbar[ok] @ qbar)"),
