@@ -4,4 +4,4 @@ from .psa_oracle import (Problem, AssignParams, as_f64, pool, pyramid, pack_pyra
                          packed_level_offset, mask_scores_sampling, mask_scores_antidiag,
                          block_cossim, assign_row, assign_levels, build_index, attention_head,
                          attention, attention_backward_head, attention_backward, mask,
-                         e4m3_round, fp8_scale, fp8_quantize, attention_fp8qk_head, attention_fp8_head, sample_offsets, kb_diag, SKIP, NUM_LEVELS)
+                         e4m3_round, bf16_round, fp8_scale, fp8_quantize, attention_fp8qk_head, attention_fp8_head, sample_offsets, kb_diag, SKIP, NUM_LEVELS)

@@ -95,9 +95,30 @@ def pool(x: np.ndarray, level: int) -> np.ndarray:
     return x.reshape(*x.shape[:-2], n // f, f, x.shape[-1]).mean(axis=-2)
 
 
-def pyramid(x: np.ndarray) -> Dict[int, np.ndarray]:
-    """All levels 0..3 of one tensor (K or V); level 0 is the input itself."""
-    return {l: (x if l == 0 else pool(x, l)) for l in range(NUM_LEVELS)}
+def pyramid(x: np.ndarray, pooled_round: Optional[str] = None) -> Dict[int, np.ndarray]:
+    """All levels 0..3 of one tensor (K or V); level 0 is the input itself. With
+    pooled_round="bf16" the pooled levels (1..3) are the exact means rounded once to bfloat16
+    (bf16_round): the levels a bf16 pyramid stores for the attention to read."""
+    out = {l: (x if l == 0 else pool(x, l)) for l in range(NUM_LEVELS)}
+    if pooled_round == "bf16":
+        out = {l: (v if l == 0 else bf16_round(v)) for l, v in out.items()}
+    elif pooled_round is not None:
+        raise ValueError(pooled_round)
+    return out
+
+
+def bf16_round(x) -> np.ndarray:
+    """Nearest bfloat16 value of float64 x, ties to even (bfloat16: 8 exponent bits with bias
+    127, 7 stored mantissa bits, subnormals below 2^-126). Written from the format: in the
+    binade [2^E, 2^(E+1)), E >= -126, the spacing is 2^(E-7); below 2^-126 it is 2^-133.
+    Finite inputs whose rounding stays below the largest finite bfloat16 only."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -126.0)
+    q = np.ldexp(1.0, (e - 7.0).astype(np.int64))
+    r = np.round(a / q) * q   # np.round: ties to even
+    return np.sign(x) * r
 
 
 def packed_level_offset(seq_len: int, level: int) -> int:
@@ -422,15 +443,19 @@ def attention_weights_row(q_rows: np.ndarray, query_idx: np.ndarray, Kb, lv, las
 
 def attention_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, level_map: np.ndarray,
                    p: Problem, scale: Optional[float] = None,
-                   qblocks: Optional[Iterable[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+                   qblocks: Optional[Iterable[int]] = None,
+                   pooled_round: Optional[str] = None) -> Tuple[np.ndarray, np.ndarray]:
     """PSA forward for one (batch, head). q: [N, d]; k, v: [N, d] of its KV head (level 0);
     level_map: [NQB, NKB]. Returns (o [N, d], lse [N]) in fp64. For each valid query i:
       z_j = s * q_i . K̄_j + l_j * ln2,  o_i = sum_j softmax(z)_j V̄_j,  lse_i = logsumexp(z).
     Query rows >= Nv, and rows with no visible key, give o = 0 and lse = -inf. Rows of query
-    blocks not listed in `qblocks` are left as NaN.
+    blocks not listed in `qblocks` are left as NaN. pooled_round="bf16" reads the pooled
+    levels as a bf16 pyramid stores them (each exact mean rounded once to bfloat16); the rest
+    of the arithmetic stays fp64.
     """
     sc = p.scale if scale is None else scale
-    return _attention_from_levels(q, pyramid(k), pyramid(v), level_map, p, sc, qblocks)
+    return _attention_from_levels(q, pyramid(k, pooled_round), pyramid(v, pooled_round),
+                                  level_map, p, sc, qblocks)
 
 
 def _attention_from_levels(q: np.ndarray, lk: Dict[int, np.ndarray], lvv: Dict[int, np.ndarray],
@@ -640,7 +665,8 @@ def attention_backward_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, level_m
 # Whole-tensor wrappers ([B, H, N, d] inputs, GQA: KV head = h // (H / Hkv))
 # ----------------------------------------------------------------------------------------
 
-def attention(q, k, v, level_map, p: Problem, scale: Optional[float] = None):
+def attention(q, k, v, level_map, p: Problem, scale: Optional[float] = None,
+              pooled_round: Optional[str] = None):
     q, k, v = as_f64(q), as_f64(k), as_f64(v)
     B, H = q.shape[:2]
     g = H // k.shape[1]
@@ -649,7 +675,8 @@ def attention(q, k, v, level_map, p: Problem, scale: Optional[float] = None):
     for b in range(B):
         for h in range(H):
             o[b, h], lse[b, h] = attention_head(q[b, h], k[b, h // g], v[b, h // g],
-                                                level_map[b, h], p, scale)
+                                                level_map[b, h], p, scale,
+                                                pooled_round=pooled_round)
     return o, lse
 
 

@@ -729,3 +729,63 @@ def pin_gqa_mask():
     pooled = [bool((lm[0, h] > 0).any()) for h in range(4)]
     ok = sim[0, 0].min() > 0.99 and sim[0, 1].max() < 0.5 and pooled == [True, True, False, False]
     return err if ok else np.inf
+
+
+# ---------------------------------------------------------------------------------------
+# bfloat16 rounding (the pooled levels a bf16 pyramid stores): bf16_round against torch's
+# float32 -> bfloat16 conversion (a library routine, round to nearest even) on float32
+# values: random magnitudes across the range, every midpoint between neighbouring bf16
+# values of a few binades (ties), and subnormals. Then the attention reading on bf16-rounded
+# pooled levels against nearest-neighbour upsampling + torch SDPA on levels rounded by torch
+# (inputs chosen so that every exact mean is a float32 value, so torch rounds it once).
+# ---------------------------------------------------------------------------------------
+def pin_bf16_round():
+    rng = np.random.default_rng(50)
+    x = (rng.standard_normal(50000) * np.exp2(rng.integers(-40, 40, 50000))).astype(np.float32)
+    mids = []
+    for e in (-3, 0, 5):
+        for m in range(128, 256):
+            mids.append((2 * m + 1) * 2.0 ** (e - 8))       # halfway between m and m + 1 ulps
+    sub = (rng.integers(1, 1 << 16, 2000) * 2.0 ** -149).astype(np.float32)
+    xs = np.concatenate([x, np.asarray(mids, np.float32), -np.asarray(mids, np.float32), sub])
+    ref = torch.from_numpy(xs).to(torch.bfloat16).double().numpy()
+    got = oracle.bf16_round(xs.astype(np.float64))
+    return float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), 2.0 ** -140)))
+
+
+def pin_bf16_pooled_attention(seed=51):
+    n, d, bq, bk = 512, 16, 64, 64
+    p = oracle.Problem(seq_len=n, seq_valid=n, head_dim=d, block_q=bq, block_k=bk)
+    rng = np.random.default_rng(seed)
+    # k, v: 10-bit integers / 64: sums of <= 8 of them and their means are float32 values
+    q = rng.standard_normal((n, d))
+    k = rng.integers(-512, 512, (n, d)) / 64.0
+    v = rng.integers(-512, 512, (n, d)) / 64.0
+    lm = rng.choice(np.array([0, 1, 2, 3, -1], dtype=np.int8), size=(p.n_qblocks, p.n_kblocks))
+    lm[:, 0] = 3
+    o, lse = oracle.attention_head(q, k, v, lm, p, pooled_round="bf16")
+
+    def torch_round(x):
+        return torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    err = 0.0
+    for qb in range(p.n_qblocks):
+        qi = slice(qb * bq, (qb + 1) * bq)
+        ks, vs, keep = [], [], []
+        for kb, l in enumerate(lm[qb]):
+            blk = slice(kb * bk, (kb + 1) * bk)
+            f = 1 << max(int(l), 0)
+            kp = k[blk].reshape(bk // f, f, d).mean(axis=1)
+            vp = v[blk].reshape(bk // f, f, d).mean(axis=1)
+            if l > 0:
+                kp, vp = torch_round(kp), torch_round(vp)
+            ks.append(np.repeat(kp, f, axis=0))
+            vs.append(np.repeat(vp, f, axis=0))
+            keep.append(np.full(bk, l >= 0))
+        ku, vu, km = np.concatenate(ks), np.concatenate(vs), np.concatenate(keep)
+        km = np.broadcast_to(km, (bq, n))
+        ref = sdpa(q[qi], ku, vu, km, 1.0 / math.sqrt(d))
+        ref_lse = torch_lse(q[qi], ku, km, 1.0 / math.sqrt(d))
+        err = max(err, np.abs(o[qi] - ref).max(), np.abs(lse[qi] - ref_lse).max())
+    # the rounding must matter on these inputs (else the pin would not see it dropped)
+    o_exact, _ = oracle.attention_head(q, k, v, lm, p)
+    return err if np.abs(o_exact - o).max() > 1e-6 else np.inf

@@ -172,3 +172,11 @@ def test_pfp8_pv_worked_rows():
 @pytest.mark.parametrize("causal", [False, True])
 def test_pfp8_pv_powers_of_two(causal):
     assert pins.pin_fp8pv_powers_of_two(causal) < 1e-12
+
+
+def test_bf16_round_matches_torch():
+    assert pins.pin_bf16_round() == 0.0
+
+
+def test_bf16_pooled_attention_reading():
+    assert pins.pin_bf16_pooled_attention() < TOL

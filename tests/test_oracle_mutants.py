@@ -43,6 +43,7 @@ ALL_PINS = {
     "pbwd_runs": lambda: max(pins.pin_bwd_constant_runs(l) for l in (1, 3)),
     "pfp8": lambda: max(pins.pin_e4m3_round(), pins.pin_fp8_scale(),
                         pins.pin_fp8qk_reduces_to_attention(True)),
+    "pbf16": lambda: max(pins.pin_bf16_round(), pins.pin_bf16_pooled_attention()),
     "pfp8pv": lambda: max(pins.pin_fp8pv_worked_rows(), pins.pin_fp8pv_powers_of_two(True)),
 }
 
@@ -96,6 +97,14 @@ MUTANTS = [
     ("bwd_dq_uses_values", "dq[qi] = sc * (dz @ Kb)", "dq[qi] = sc * (dz @ Vb)"),
     ("bwd_gqa_overwrites", "dk[b, h // g] += bk", "dk[b, h // g] = bk"),
     ("bwd_pool_wrong_row", "dv += gv[l][tok >> l] * 2.0 ** -l", "dv += gv[l][np.minimum(tok >> (l - 1 if l else 0), tok.size - 1)] * 2.0 ** -l"),
+    ("bf16_ties_away", "r = np.round(a / q) * q   # np.round: ties to even", "r = np.floor(a / q + 0.5) * q"),
+    ("bf16_eight_mantissa_bits", "q = np.ldexp(1.0, (e - 7.0).astype(np.int64))",
+     "q = np.ldexp(1.0, (e - 8.0).astype(np.int64))"),
+    ("bf16_no_subnormals", "e = np.maximum(e, -126.0)", "e = np.maximum(e, -1260.0)"),
+    ("bf16_pooled_not_rounded", "out = {l: (v if l == 0 else bf16_round(v)) for l, v in out.items()}",
+     "out = {l: v for l, v in out.items()}"),
+    ("bf16_level0_rounded", "out = {l: (v if l == 0 else bf16_round(v)) for l, v in out.items()}",
+     "out = {l: bf16_round(v) for l, v in out.items()}"),
     ("e4m3_ties_away", "return np.sign(x) * (np.round(a / q) * q)",
      "return np.sign(x) * (np.floor(a / q + 0.5) * q)"),
     ("e4m3_no_subnormals", "e = np.maximum(e, -6.0)", "e = np.maximum(e, -60.0)"),
