@@ -121,11 +121,16 @@ int64_t psa_pooled_rows(const psa_problem* prob);
  * pooling; skill summary at skillsmp.com, "Implementation": level l pools by 2^l).
  * k_pooled/v_pooled row j of level l = mean of full-resolution rows [j*2^l, (j+1)*2^l).
  * Accumulation is a pairwise float32 tree (each level is the pairwise mean of the one
- * below), which equals the direct mean up to one rounding; bf16 outputs are rounded to
- * nearest-even. Level 0 is not copied: the attention reads K and V directly.
+ * below), which equals the direct mean up to one rounding per addition.
+ * out_dtype: the problem's dtype (bf16 outputs are the tree's float32 values rounded to
+ * nearest even; this is what the attention calls read), or PSA_F32 for float32 levels of a
+ * bf16 problem (parity runs: the tree's values before rounding). A float32 problem with a
+ * bf16 out_dtype returns PSA_ERR_UNSUPPORTED; any other value PSA_ERR_INVALID_ARG.
+ * k_pooled/v_pooled: [batch][heads_kv][7*seq_len/8][head_dim] contiguous, in out_dtype,
+ * 16-byte aligned, caller-owned. Level 0 is not copied: the attention reads K and V directly.
  */
 int psa_build_pyramid(const psa_problem* prob, const void* k, const void* v,
-                      void* k_pooled, void* v_pooled, void* stream);
+                      void* k_pooled, void* v_pooled, int32_t out_dtype, void* stream);
 
 /* Device workspace psa_mask needs for `params`; 0 on a bad argument. */
 size_t psa_mask_workspace_bytes(const psa_problem* prob, const psa_mask_params* params);
@@ -153,6 +158,24 @@ size_t psa_mask_workspace_bytes(const psa_problem* prob, const psa_mask_params* 
 int psa_mask(const psa_problem* prob, const psa_mask_params* params, const void* q,
              const void* k, int8_t* level_map, float* block_mass, float* block_sim,
              void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Certification inside psa_mask (the level map's threshold decisions are discontinuous in the
+ * masses, so float32 scores could flip a decision that sits at their rounding level). The
+ * scores and the assignment run in float32 (the assignment's running sum in float64); a row
+ * with a decision within 1e-5 of a threshold, or with two sorted masses within 1e-5 (relative)
+ * of each other on either side of a level change, is rescored in float64 on the device
+ * (logits as float64 dots of the bf16 inputs, float64 softmax and block masses; in block-mean
+ * mode float64 means) and reassigned in float64; its block_mass row then holds those masses
+ * rounded to float. The similarity check compares the float64 similarity (block_sim holds it
+ * rounded to float). At most a workspace-bounded number of rows per call (all rows of the
+ * usual shapes; at least 16) are rescored; rows beyond it keep the float32 decisions.
+ * psa_mask_certified_rows reads the counters of the last psa_mask call on `ws`:
+ * counts[0] = rows flagged, counts[1] = flagged rows left uncertified (beyond the capacity).
+ * It synchronizes `stream` (the stream psa_mask ran on). counts: host memory, 2 int32.
+ */
+int psa_mask_certified_rows(const psa_problem* prob, const psa_mask_params* params,
+                            const void* ws, int32_t* counts, void* stream);
 
 /*
  * Threshold assignment (summary article, "Results": threshold-based levels with a cosine
@@ -345,6 +368,15 @@ int psa_check_status(const void* ws, void* stream);
 
 /* Static string for a status code. */
 const char* psa_status_string(int status);
+
+/*
+ * Diagnostics (no part of the path): enqueues workgroups that fill the LDS of every CU with
+ * the 32-bit `pattern` (e.g. a NaN), so that the kernels enqueued next start on LDS holding
+ * it. A kernel that read LDS it had not written would then show the pattern in its outputs;
+ * the tests run the path after such a fill and require outputs bit-identical to a run
+ * without it.
+ */
+int psa_debug_fill_lds(uint32_t pattern, void* stream);
 
 /* The hipError_t of the last PSA_ERR_HIP returned on this thread (0 if none). */
 int psa_last_hip_error(void);

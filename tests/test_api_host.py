@@ -59,7 +59,21 @@ def test_problem_checks(field, value, status):
     rc = L.psa_attn_fwd(p.ref(), 0.0, dummy, dummy, dummy, dummy, dummy, dummy, dummy, None,
                         dummy, 1 << 20, None)
     assert rc == status
-    assert L.psa_build_pyramid(p.ref(), dummy, dummy, dummy, dummy, None) == status
+    assert L.psa_build_pyramid(p.ref(), dummy, dummy, dummy, dummy, P.PSA_BF16, None) == status
+
+
+def test_pyramid_out_dtype_checks():
+    """out_dtype: the problem's dtype or float32; a bf16 level of a float32 problem is
+    unsupported, anything else is an invalid argument (nothing is launched)."""
+    L = psa.lib()
+    d = ctypes.c_void_p(256)
+    pb = _prob(dtype=P.PSA_BF16)
+    pf = _prob(dtype=P.PSA_F32)
+    assert L.psa_build_pyramid(pb.ref(), d, d, d, d, 7, None) == P.PSA_ERR_INVALID_ARG
+    assert L.psa_build_pyramid(pb.ref(), d, d, d, d, -1, None) == P.PSA_ERR_INVALID_ARG
+    assert L.psa_build_pyramid(pf.ref(), d, d, d, d, P.PSA_BF16, None) == P.PSA_ERR_UNSUPPORTED
+    assert L.psa_build_pyramid(pb.ref(), None, d, d, d, P.PSA_F32, None) == P.PSA_ERR_INVALID_ARG
+    assert L.psa_build_pyramid(pf.ref(), d, d, d, None, P.PSA_F32, None) == P.PSA_ERR_INVALID_ARG
 
 
 def test_bad_stride_rejected():
@@ -107,18 +121,27 @@ def test_mask_param_checks(kw, status):
 
 def test_mask_workspace_per_mode():
     """Every scoring mode is accepted and sizes its workspace: the log-masses (scoring rows x
-    blocks, float32) plus, for block means, the query and key means."""
+    blocks, float32; for block means also the query and key means), then the certification
+    area: two counters (256 bytes), the flagged-row list and the float64 log-masses of the
+    certifiable rows (all 32 rows of this small problem: scoring rows per query block x
+    blocks x 8 bytes each), plus the float64 similarities when the cosine check is on."""
     p = _prob(dtype=P.PSA_BF16)
     L = psa.lib()
     B, H, Hkv, N, D = 1, 2, 2, 1024, 64   # the _prob() shape
     nqb, nkb = N // 64, N // 64
+    R = B * H * nqb
+    a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
     sizes = {}
     for mode in ("sampling", "antidiag", "meankey"):
         mp = psa.MaskParams(mode=mode, samples_per_qblock=8, antidiag_stride=8).c()
         sizes[mode] = L.psa_mask_workspace_bytes(p.ref(), ctypes.byref(mp))
-    assert sizes["sampling"] == B * H * nkb * nqb * 8 * 4
-    assert sizes["antidiag"] == B * H * nkb * (N // 8) * 4
-    assert sizes["meankey"] >= B * H * nkb * nqb * 4 + B * H * nqb * D * 4 + B * Hkv * nkb * D * 4
+    cert = lambda rq: 256 + a256(R * 4) + R * rq * nkb * 8  # noqa: E731
+    assert sizes["sampling"] == a256(B * H * nkb * nqb * 8 * 4) + cert(8)
+    assert sizes["antidiag"] == a256(B * H * nkb * (N // 8) * 4) + cert(64 // 8)
+    assert sizes["meankey"] >= B * H * nkb * nqb * 4 + B * H * nqb * D * 4 + B * Hkv * nkb * D * 4 + cert(1)
+    mp = psa.MaskParams(mode="antidiag", antidiag_stride=8, cos_sim_min=0.8).c()
+    assert (L.psa_mask_workspace_bytes(p.ref(), ctypes.byref(mp))
+            == sizes["antidiag"] + a256(B * Hkv * nkb * 8))
     with pytest.raises(ValueError):
         psa.MaskParams(mode="bogus").c()
 
@@ -242,7 +265,7 @@ def test_empty_problems_do_nothing(field, value):
         p.c.seq_valid = 0
     n = None
     mp = psa.MaskParams().c()
-    assert L.psa_build_pyramid(p.ref(), n, n, n, n, n) == P.PSA_OK
+    assert L.psa_build_pyramid(p.ref(), n, n, n, n, P.PSA_BF16, n) == P.PSA_OK
     assert L.psa_mask(p.ref(), ctypes.byref(mp), n, n, n, n, n, n, 0, n) == P.PSA_OK
     assert L.psa_mask_assign(p.ref(), ctypes.byref(mp), n, n, n, n) == P.PSA_OK
     assert L.psa_build_index(p.ref(), n, n, n, n, n) == P.PSA_OK

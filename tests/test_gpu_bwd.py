@@ -10,7 +10,10 @@ bf16 inputs (exact in both) with float32 accumulation. Each row of dS sums to ex
 relative error is about 2^-9 times |(dS_ij K_j)_j| / |dq_i|, a ratio that grows when a row sees
 few keys. Applying exactly these roundings to the fp64 oracle gives dq 1.2e-2 from exact at
 64 tokens and <= 7e-3 from 1088 tokens on (the bf16 rounding of dS dominates; exact D changes
-little). Bar: rel-L2 <= 2e-2 per tensor, max-abs <= 4e-2 of the tensor's largest magnitude.
+little). Bars: where rows see about a thousand tokens or more (every workload here, and the
+ragged 1080-token case) rel-L2 <= 1e-2 per tensor and max-abs <= 2e-2 of the tensor's largest
+magnitude; where they see few (64 tokens; the row-limit case, two blocks per row) rel-L2 <= 2e-2
+and max-abs <= 4e-2.
 Pad query rows get dq = 0 and pad tokens dk = dv = 0 exactly; two runs are bit-identical.
 """
 import numpy as np
@@ -26,6 +29,14 @@ pytestmark = pytest.mark.gpu
 
 REL_L2 = 2e-2
 MAX_REL = 4e-2
+# rows that see about a thousand tokens or more: the derivation's <= 7e-3 with headroom
+REL_L2_LONG = 1e-2
+MAX_REL_LONG = 2e-2
+LONG_TOKENS = 1024
+
+
+def _bars(nv):
+    return (REL_L2_LONG, MAX_REL_LONG) if nv >= LONG_TOKENS else (REL_L2, MAX_REL)
 
 BWD = [W.small(w) for w in W.ALL if w.dtype == "bf16"]
 BWD.append(W.small(W.QWEN25VL_32K).replace(name="qwen2.5-vl-7b-small-bq64", block_q=64))
@@ -53,15 +64,17 @@ def _run(wl, q, k, v, lm, dout):
     return dq, dk, dv
 
 
-def _compare(name, got, ref):
+def _compare(name, got, ref, nv):
+    bar_rel, bar_max = _bars(nv)
     g = got.double().cpu().numpy()
     diff = g - ref
     scale = max(np.abs(ref).max(), 1e-30)
     rel = float(np.linalg.norm(diff) / max(np.linalg.norm(ref), 1e-30))
     mx = float(np.abs(diff).max() / scale)
-    print(f"  {name}: rel_l2={rel:.3e} max_abs/max|ref|={mx:.3e} max|ref|={scale:.3e}", flush=True)
-    assert rel <= REL_L2, f"{name}: rel L2 {rel}"
-    assert mx <= MAX_REL, f"{name}: max abs {mx} of max|ref|"
+    print(f"  {name}: rel_l2={rel:.3e} max_abs/max|ref|={mx:.3e} max|ref|={scale:.3e} "
+          f"(bars {bar_rel:.0e} / {bar_max:.0e})", flush=True)
+    assert rel <= bar_rel, f"{name}: rel L2 {rel}"
+    assert mx <= bar_max, f"{name}: max abs {mx} of max|ref|"
 
 
 @pytest.mark.parametrize("wl", BWD, ids=[w.name for w in BWD])
@@ -74,10 +87,10 @@ def test_bwd_parity(wl):
     dq, dk, dv = _run(wl, q, k, v, lm, dout)
     torch.cuda.synchronize()
     rq, rk, rv = oracle.attention_backward(q, k, v, lm, dout, oracle_problem(wl))
-    _compare("dq", dq, rq)
-    _compare("dk", dk, rk)
-    _compare("dv", dv, rv)
     nv = wl.seq_valid
+    _compare("dq", dq, rq, nv)
+    _compare("dk", dk, rk, nv)
+    _compare("dv", dv, rv, nv)
     assert torch.count_nonzero(dq[..., nv:, :]).item() == 0
     assert torch.count_nonzero(dk[..., nv:, :]).item() == 0
     assert torch.count_nonzero(dv[..., nv:, :]).item() == 0
@@ -112,9 +125,9 @@ def test_bwd_all_l0_matches_autograd():
     o = torch.softmax(z, dim=-1) @ tv
     rows = (torch.arange(wl.seq_len, device=DEV) < nv)[:, None]
     (o * dout.to(DEV).float() * rows).sum().backward()
-    _compare("dq", dq, tq.grad.double().cpu().numpy())
-    _compare("dk", dk, tk.grad.double().cpu().numpy())
-    _compare("dv", dv, tv.grad.double().cpu().numpy())
+    _compare("dq", dq, tq.grad.double().cpu().numpy(), nv)
+    _compare("dk", dk, tk.grad.double().cpu().numpy(), nv)
+    _compare("dv", dv, tv.grad.double().cpu().numpy(), nv)
 
 
 def test_bwd_token_major_layout():
@@ -147,10 +160,12 @@ FULL = [w for w in W.ALL if w.dtype == "bf16"]
 def test_bwd_fullsize(wl):
     """Full size, as the benchmark runs it. dq of sampled query blocks (first, last, middle,
     a random one) against the oracle, which computes those rows one block at a time. dk and dv
-    need every row of a column, so at full size they are checked by properties that hold at
-    any size: each row's P sums to 1 and a pooled row hands out exactly its gradient, so per
-    KV head sum_t dv[t] = sum of dO over the rows that see a key; and rowsum(dS) = 0 gives
-    sum_t dk[t] = 0."""
+    element by element on sampled KV blocks (a middle one and the last, ragged one) of one KV
+    head: only the (query head, query block) rows that list a KV block at some level reach its
+    tokens, so the oracle visits just those rows of the group's query heads. Also properties
+    that hold at any size: each row's P sums to 1 and a pooled row hands out exactly its
+    gradient, so per KV head sum_t dv[t] = sum of dO over the rows that see a key; and
+    rowsum(dS) = 0 gives sum_t dk[t] = 0."""
     announce(f"backward full size {wl.name}: H{wl.heads_q}/{wl.heads_kv} N{wl.seq_len} d{wl.head_dim}")
     q, k, v = W.make_qkv(wl)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
@@ -183,7 +198,27 @@ def test_bwd_fullsize(wl):
             oracle.as_f64(dout[0, h]), p, qblocks=qbs)
         rows = np.concatenate([np.arange(b * wl.block_q, (b + 1) * wl.block_q) for b in qbs])
         print(f"[{wl.name}] head {h} query blocks {qbs}", flush=True)
-        _compare("dq", dq[0, h, rows], rq[rows])
+        _compare("dq", dq[0, h, rows], rq[rows], wl.seq_valid)
+    # dk, dv of sampled KV blocks of the last KV head, from the rows that list them
+    hk = wl.heads_kv - 1
+    kbs = sorted({wl.n_kblocks // 2 + 1, (wl.seq_valid - 1) // 64})
+    rk = np.zeros((wl.seq_len, wl.head_dim))
+    rv = np.zeros_like(rk)
+    kf, vf = oracle.as_f64(k[0, hk]), oracle.as_f64(v[0, hk])
+    nrows = 0
+    for h in range(hk * g, (hk + 1) * g):
+        qbs = [qb for qb in range(n) if np.any(lm[0, h, qb, kbs] >= 0)]
+        nrows += len(qbs)
+        if not qbs:
+            continue
+        _, a_k, a_v = oracle.attention_backward_head(
+            oracle.as_f64(q[0, h]), kf, vf, lm[0, h], oracle.as_f64(dout[0, h]), p, qblocks=qbs)
+        rk += a_k
+        rv += a_v
+    toks = np.concatenate([np.arange(kb * 64, (kb + 1) * 64) for kb in kbs])
+    print(f"[{wl.name}] kv head {hk} KV blocks {kbs}: {nrows} listing rows", flush=True)
+    _compare("dk", dk[0, hk, toks], rk[toks], wl.seq_valid)
+    _compare("dv", dv[0, hk, toks], rv[toks], wl.seq_valid)
     # sums over tokens, per KV head
     seen = torch.isfinite(lse) & (torch.arange(wl.seq_len, device=DEV) < wl.seq_valid)
     dsum = (do.float() * seen[..., None]).sum(dim=2)                      # [B, H, d]

@@ -125,9 +125,9 @@ def test_ragged_block_counts(n, d, causal):
     dout = W.make_dout(wl)
     dq, dk, dv = _run(wl, q, k, v, lm, dout)
     rq, rk, rv = oracle.attention_backward(q, k, v, lm, dout, p)
-    _compare("dq", dq, rq)
-    _compare("dk", dk, rk)
-    _compare("dv", dv, rv)
+    _compare("dq", dq, rq, wl.seq_valid)
+    _compare("dk", dk, rk, wl.seq_valid)
+    _compare("dv", dv, rv, wl.seq_valid)
     if d == 128:
         o8 = np.zeros(o_ref.shape)
         l8 = np.zeros(lse_ref.shape)
@@ -162,6 +162,7 @@ def test_bwd_row_limit(d, heads, n, bq):
     dq, dk, dv = _run(wl, q, k, v, lm, dout)
     torch.cuda.synchronize()
     rq, rk, rv = oracle.attention_backward(q, k, v, lm, dout, oracle_problem(wl))
-    _compare("dq", dq, rq)
-    _compare("dk", dk, rk)
-    _compare("dv", dv, rv)
+    # every row sees two blocks (80 pooled keys): the few-keys bars
+    _compare("dq", dq, rq, 0)
+    _compare("dk", dk, rk, 0)
+    _compare("dv", dv, rv, 0)

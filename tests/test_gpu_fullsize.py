@@ -5,10 +5,13 @@ The whole path runs on the full tensors exactly as the benchmark's step does
 stream, into preallocated buffers). The oracle cannot run a full layer in seconds, so it
 checks outputs it can compute one by one, on sampled heads and query blocks:
   * pooled K/V rows of the sampled KV heads (every level);
+  * float32 pooled rows (out_dtype float32) at the 1e-5 bar, and the bf16 levels the
+    attention reads;
   * mask rows: block masses, similarities and the level map row of each sampled query block,
-    recomputed by the oracle from the same inputs (map rows exact but for fragile entries);
+    recomputed by the oracle from the same inputs (bit for bit but at decisions within the
+    oracle's own 1e-12 margin; near-threshold rows are certified in float64 on the GPU);
   * the attention output and lse of every query of each sampled block, on the oracle's own
-    level map row (blocks whose map row differs at a fragile entry are counted, not compared).
+    level map row, against the exact-mean reading and the bf16-pooled-level reading (lse 1e-3).
 Sampled blocks include the first block, the last one (ragged: it holds the pad rows) and, for
 the causal workload, blocks whose diagonal split the query block.
 """
@@ -19,8 +22,8 @@ import torch
 import oracle
 import workloads as W
 import video_transformers_amd as psa
-from gpu_util import (DEV, announce, assign_params, check_attention, fragile_entries,
-                      mask_params, need_gpu)
+from gpu_util import (DEV, announce, assign_params, check_attention, check_map,
+                      mask_params, need_gpu, oracle_margin_entries)
 
 pytestmark = pytest.mark.gpu
 
@@ -52,15 +55,16 @@ def _run_path(wl, qd, kd, vd):
                             causal=wl.causal, seq_valid=wl.seq_valid)
     kp, vp = psa.build_pyramid(kd, vd, prob)
     M = sim = None
+    cert = []
     if wl.map_source == "mask":
-        lm, M, sim = psa.mask(qd, kd, prob, mask_params(wl))
+        lm, M, sim = psa.mask(qd, kd, prob, mask_params(wl), cert_counts=cert)
     else:
         lm = torch.from_numpy(W.make_map(wl)).to(DEV)
     row_ptr, col_idx, err = psa.build_index(lm, prob)
     o, lse = psa.attn_fwd_indexed(qd, kd, vd, kp, vp, row_ptr, col_idx, prob)
     torch.cuda.synchronize()
     assert err.item() == 0
-    return kp, vp, lm, M, sim, o, lse
+    return kp, vp, lm, M, sim, o, lse, cert
 
 
 # the five workloads, plus block-mean scoring on the Wan-like 32k layer
@@ -73,7 +77,17 @@ def test_fullsize_sampled_parity(wl):
              f"d{wl.head_dim}")
     q, k, v = W.make_qkv(wl)
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
-    kp, vp, lm, M, sim, o, lse = _run_path(wl, qd, kd, vd)
+    kp, vp, lm, M, sim, o, lse, cert = _run_path(wl, qd, kd, vd)
+    if cert:
+        print(f"[{wl.name}] certification: {cert[0]} rows rescored in float64, {cert[1]} left "
+              f"(of {wl.batch * wl.heads_q * wl.n_qblocks})", flush=True)
+        assert cert[1] == 0
+    kp32 = vp32 = None
+    if wl.dtype == "bf16":
+        prob = psa.make_problem(qd, kd, vd, block_q=wl.block_q, block_k=wl.block_k,
+                                causal=wl.causal, seq_valid=wl.seq_valid)
+        kp32, vp32 = psa.build_pyramid(kd, vd, prob, out_dtype=torch.float32)
+        assert torch.equal(kp32.to(torch.bfloat16), kp) and torch.equal(vp32.to(torch.bfloat16), vp)
     p = oracle.Problem.of(wl)
     a = assign_params(wl)
     g = wl.group
@@ -90,17 +104,20 @@ def test_fullsize_sampled_parity(wl):
         ref = oracle.pack_pyramid(kh)
         got = kp[0, hk].double().cpu().numpy()
         tol = 1e-5 * np.abs(ref).max() if f32 else None
-        for name, r, gt in (("k", ref, got),
-                            ("v", oracle.pack_pyramid(vh), vp[0, hk].double().cpu().numpy())):
+        for name, r, gt, g32 in (("k", ref, got, kp32), ("v", oracle.pack_pyramid(vh),
+                                 vp[0, hk].double().cpu().numpy(), vp32)):
             if f32:
                 assert np.abs(gt - r).max() <= tol, f"pooled {name} head {hk}"
             else:
                 assert np.all(np.abs(gt - r) <= np.abs(r) * 2.0 ** -7 + 1e-30), \
                     f"pooled {name} head {hk}: beyond one bf16 ulp of the exact mean"
+                x32 = g32[0, hk].double().cpu().numpy()
+                assert np.abs(x32 - r).max() <= 1e-5 * np.abs(r).max(), f"f32 pooled {name} head {hk}"
+                assert np.linalg.norm(x32 - r) <= 1e-5 * np.linalg.norm(r), f"f32 pooled {name} head {hk}"
 
         # the level map rows the oracle assigns
         lm_ref = np.full((p.n_qblocks, p.n_kblocks), oracle.SKIP, dtype=np.int8)
-        frag = np.zeros_like(lm_ref, dtype=bool)
+        marg = np.zeros_like(lm_ref, dtype=bool)
         lm_gpu = lm[0, h].cpu().numpy()
         if wl.map_source == "mask":
             if wl.mask_mode == "sampling":
@@ -120,31 +137,35 @@ def test_fullsize_sampled_parity(wl):
                 assert ds <= 1e-6
             for qb in qbs:
                 lm_ref[qb] = oracle.assign_row(Mr[qb], simr, p, a, qb)
-            frag = fragile_entries(Mr[None, None], None if simr is None else simr[None, None],
-                                   p, a, qblocks=qbs)[0, 0]
+            marg = oracle_margin_entries(Mr[None, None], None if simr is None else simr[None, None],
+                                         p, a, qblocks=qbs)[0, 0]
         else:
             lm_ref = W.make_map(wl, [h])[0, 0]
-        for qb in qbs:
-            diff = lm_gpu[qb] != lm_ref[qb]
-            assert not np.any(diff & ~frag[qb]), \
-                f"head {h} qblock {qb}: map differs at non-fragile blocks {np.nonzero(diff)[0]}"
+        check_map(lm_gpu[qbs], lm_ref[qbs], marg[qbs], f"{wl.name} head {h} qblocks {qbs}")
 
-        # attention of the sampled blocks whose map rows agree exactly
+        # attention of the sampled blocks on the oracle's map rows (a row may differ only at a
+        # decision within the oracle's own 1e-12 margin: such a block is counted, not compared)
         agree = [qb for qb in qbs if np.array_equal(lm_gpu[qb], lm_ref[qb])]
         skipped += len(qbs) - len(agree)
         if not agree:
             continue
         o_ref, lse_ref = oracle.attention_head(qh, kh, vh, lm_ref, p, qblocks=agree)
+        rnd = None
+        if not f32:
+            o_r, lse_r = oracle.attention_head(qh, kh, vh, lm_ref, p, qblocks=agree,
+                                               pooled_round="bf16")
         rows = np.concatenate([np.arange(qb * wl.block_q, (qb + 1) * wl.block_q) for qb in agree])
         valid = rows < wl.seq_valid
         og = o[0, h, rows].double().cpu().numpy()
         lg = lse[0, h, rows].double().cpu().numpy()
+        if not f32:
+            rnd = (o_r[rows][valid][None], lse_r[rows][valid][None])
         check_attention(torch.from_numpy(og[valid][None]), torch.from_numpy(lg[valid][None]),
                         o_ref[rows][valid][None], lse_ref[rows][valid][None],
-                        int(valid.sum()), f32, f"{wl.name} head {h} qblocks {agree}")
+                        int(valid.sum()), f32, f"{wl.name} head {h} qblocks {agree}", rnd)
         assert np.all(og[~valid] == 0.0), "pad query rows must be zero"
         assert np.all(np.isneginf(lg[~valid]))
         compared += len(agree)
-    print(f"[{wl.name}] compared {compared} query blocks, {skipped} left out on fragile map "
-          f"entries", flush=True)
-    assert compared >= 3 * skipped and compared > 0
+    print(f"[{wl.name}] compared {compared} query blocks, {skipped} left out (map row differing "
+          f"within the oracle's 1e-12 margin)", flush=True)
+    assert compared > 0

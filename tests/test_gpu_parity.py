@@ -12,8 +12,9 @@ import torch
 import oracle
 import workloads as W
 import video_transformers_amd as psa
-from gpu_util import (DEV, announce, assign_params, check_attention, fragile_entries,
-                      mask_params, need_gpu, oracle_map, oracle_problem, problem_for)
+from gpu_util import (DEV, announce, assign_params, check_attention, check_map,
+                      mask_params, need_gpu, oracle_map, oracle_margin_entries, oracle_problem,
+                      problem_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,25 +39,38 @@ def _inputs(wl):
 # ---------------------------------------------------------------------------------------
 @pytest.mark.parametrize("wl", SMALL, ids=IDS)
 def test_pyramid_parity(wl):
+    """float32 levels (out_dtype f32, also for bf16 inputs) against the fp64 means at the 1e-5
+    bar; the bf16 levels are exactly the bf16 rounding of those float32 values; and wherever a
+    bf16 level differs from the rounding of the exact mean, the exact mean lies within the
+    float32 tree's error (3 roundings: 2^-22 relative) of a bf16 rounding midpoint."""
     announce(f"pyramid {wl.name}")
     q, k, v, qd, kd, vd = _inputs(wl)
     prob = problem_for(wl, qd, kd, vd)
+    kp32, vp32 = psa.build_pyramid(kd, vd, prob, out_dtype=torch.float32)
     kp, vp = psa.build_pyramid(kd, vd, prob)
     torch.cuda.synchronize()
-    for name, x, xp in (("k", k, kp), ("v", v, vp)):
+    for name, x, xp32, xp in (("k", k, kp32, kp), ("v", v, vp32, vp)):
         ref = oracle.pack_pyramid(oracle.as_f64(x))
-        got = xp.double().cpu().numpy()
+        got = xp32.double().cpu().numpy()
+        d = np.abs(got - ref)
+        print(f"[{wl.name} {name}] f32 levels: max abs {d.max():.3e} "
+              f"(max |ref| {np.abs(ref).max():.3e})", flush=True)
+        assert d.max() <= 1e-5 * np.abs(ref).max(), name
+        assert np.linalg.norm(got - ref) <= 1e-5 * np.linalg.norm(ref), name
         if wl.dtype == "f32":
-            d = np.abs(got - ref)
-            assert d.max() <= 1e-5 * np.abs(ref).max(), name
-            assert np.linalg.norm(got - ref) <= 1e-5 * np.linalg.norm(ref), name
-        else:
-            # bf16 output: the correctly rounded mean, within one bf16 ulp of the exact mean
-            ref_bf = torch.from_numpy(ref).to(torch.float32).to(torch.bfloat16).double().numpy()
-            exact = np.mean(got == ref_bf)
-            ulp = np.abs(ref) * 2.0 ** -7 + 1e-30
-            assert np.all(np.abs(got - ref) <= ulp), name
-            assert exact > 0.999, f"{name}: only {exact:.5f} of pooled values equal RNE(mean)"
+            assert torch.equal(xp, xp32), name
+            continue
+        assert torch.equal(xp, xp32.to(torch.bfloat16)), f"{name}: bf16 levels != RNE(f32 levels)"
+        rne = oracle.bf16_round(ref)
+        b = xp.double().cpu().numpy()
+        off = b != rne
+        # a bf16 rounding midpoint next to the exact mean: halfway between rne and its neighbour
+        # on the side of b
+        mid = (b + rne) / 2.0
+        near = np.abs(ref - mid) <= 2.0 ** -22 * np.abs(ref)
+        print(f"[{wl.name} {name}] bf16 levels differing from RNE(exact mean): {int(off.sum())} "
+              f"of {off.size}", flush=True)
+        assert np.all(near[off]), f"{name}: a bf16 level off RNE(mean) away from a midpoint"
 
 
 # ---------------------------------------------------------------------------------------
@@ -145,7 +159,9 @@ def test_attention_parity(wl):
     o, lse = psa.attn_fwd(qd, kd, vd, kp, vp, torch.from_numpy(lm).to(DEV), prob)
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attention(q, k, v, lm, oracle_problem(wl))
-    check_attention(o, lse, o_ref, lse_ref, wl.seq_valid, wl.dtype == "f32", wl.name)
+    rnd = (oracle.attention(q, k, v, lm, oracle_problem(wl), pooled_round="bf16")
+           if wl.dtype == "bf16" else None)
+    check_attention(o, lse, o_ref, lse_ref, wl.seq_valid, wl.dtype == "f32", wl.name, rnd)
 
 
 BF16_SMALL = [w for w in SMALL if w.dtype == "bf16"]
@@ -197,7 +213,9 @@ def test_attention_shapes(causal, dtype, d, bq):
     o, lse = psa.attn_fwd(qd, kd, vd, kp, vp, torch.from_numpy(lm).to(DEV), prob)
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attention(q, k, v, lm, oracle_problem(wl))
-    check_attention(o, lse, o_ref, lse_ref, wl.seq_valid, dtype == "f32", f"shape d{d} bq{bq}")
+    rnd = (oracle.attention(q, k, v, lm, oracle_problem(wl), pooled_round="bf16")
+           if dtype == "bf16" else None)
+    check_attention(o, lse, o_ref, lse_ref, wl.seq_valid, dtype == "f32", f"shape d{d} bq{bq}", rnd)
 
 
 TOKEN_MAJOR = [W.small(W.WAN13B_32K), W.small(W.QWEN25VL_32K)]
@@ -215,7 +233,8 @@ def test_path_on_token_major_layout(wl):
     assert qd.stride(2) == wl.heads_q * wl.head_dim and kd.stride(2) == wl.heads_kv * wl.head_dim
     prob = problem_for(wl, qd, kd, vd)
     kp, vp = psa.build_pyramid(kd, vd, prob)
-    lm, M, sim = psa.mask(qd, kd, prob, mask_params(wl))
+    cert = []
+    lm, M, sim = psa.mask(qd, kd, prob, mask_params(wl), cert_counts=cert)
     o, lse = psa.attn_fwd(qd, kd, vd, kp, vp, lm, prob)
     torch.cuda.synchronize()
     assert o.stride() == qd.stride()
@@ -223,9 +242,8 @@ def test_path_on_token_major_layout(wl):
     lm_ref, M_ref, sim_ref = oracle.mask(q, k, p, wl.mask_mode, assign_params(wl),
                                          samples=wl.samples_per_qblock, stride=wl.antidiag_stride)
     assert np.abs(M.double().cpu().numpy() - M_ref).max() <= 2e-6
-    frag = fragile_entries(M_ref, sim_ref, p, assign_params(wl))
-    diff = lm.cpu().numpy() != lm_ref
-    assert not np.any(diff & ~frag)
+    check_map(lm.cpu().numpy(), lm_ref, oracle_margin_entries(M_ref, sim_ref, p, assign_params(wl)),
+              f"{wl.name} token-major", cert)
     o_ref, lse_ref = oracle.attention(q, k, v, lm.cpu().numpy(), p)
     check_attention(o, lse, o_ref, lse_ref, wl.seq_valid, False, f"{wl.name} token-major")
     # the attention on this layout equals the attention on the contiguous copies
@@ -329,6 +347,10 @@ MASKED = [w for w in SMALL if w.map_source == "mask"]
 # tiles) next to its fast path above
 MASKED.append(W.small(W.QWEN25VL_32K).replace(name="qwen2.5-vl-7b-small-1536", seq_len=1536,
                                                   seq_valid=1536))
+# a last tile of compressed columns that is partial (2176 / 8 = 272 columns = 4.25 tiles of 64),
+# with padding: a regression case for the general path's last tile
+MASKED.append(W.small(W.QWEN25VL_32K).replace(name="qwen2.5-vl-7b-small-partial-tile", seq_len=2176,
+                                                  seq_valid=2168))
 # block-mean scoring on the sampling workloads' inputs, non-causal with padding and causal
 MASKED.append(W.small(W.WAN13B_32K).replace(name="wan2.1-1.3b-small-meankey", mask_mode="meankey"))
 MASKED.append(W.small(W.QWEN25VL_32K).replace(name="qwen2.5-vl-7b-small-meankey", mask_mode="meankey"))
@@ -343,19 +365,18 @@ def test_mask_parity(wl):
     lm_ref, M_ref, sim_ref = oracle.mask(q, k, p, wl.mask_mode, a, samples=wl.samples_per_qblock,
                                          stride=wl.antidiag_stride)
     prob = problem_for(wl, qd, kd, vd)
-    lm, M, sim = psa.mask(qd, kd, prob, mask_params(wl))
+    cert = []
+    lm, M, sim = psa.mask(qd, kd, prob, mask_params(wl), cert_counts=cert)
     torch.cuda.synchronize()
     Mg = M.double().cpu().numpy()
     dM = np.abs(Mg - M_ref)
-    print(f"[{wl.name}] mass max abs diff {dM.max():.3e}", flush=True)
+    big = M_ref > 1e-3
+    rel = (dM[big] / M_ref[big]).max(initial=0.0)
+    print(f"[{wl.name}] mass max abs diff {dM.max():.3e}, max rel diff (masses > 1e-3) {rel:.3e}",
+          flush=True)
     assert dM.max() <= 2e-6
     if sim_ref is not None:
         ds = np.abs(sim.double().cpu().numpy() - sim_ref)
         print(f"[{wl.name}] sim max abs diff {ds.max():.3e}", flush=True)
         assert ds.max() <= 1e-6
-    got = lm.cpu().numpy()
-    diff = got != lm_ref
-    frag = fragile_entries(M_ref, sim_ref, p, a)
-    print(f"[{wl.name}] map entries differing {int(diff.sum())}, fragile {int(frag.sum())} "
-          f"of {diff.size}", flush=True)
-    assert not np.any(diff & ~frag)
+    check_map(lm.cpu().numpy(), lm_ref, oracle_margin_entries(M_ref, sim_ref, p, a), wl.name, cert)

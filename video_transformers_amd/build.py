@@ -62,8 +62,53 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+# A second build of the host side of the C ABI (psa_api.cpp: argument checks, workspace
+# layout, dispatch) with AddressSanitizer and UndefinedBehaviorSanitizer on the host code only,
+# linked with the same device objects into _build/libpsa_hostsan.so. The CPU tests run the
+# argument checks against it (no GPU needed). Device code is never built with a sanitizer.
+HOSTSAN_LIB = os.path.join(BUILD, "libpsa_hostsan.so")
+HOSTSAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    """The clang AddressSanitizer runtime the host-sanitized library links against."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    base = os.path.join(rocm, "llvm", "lib", "clang")
+    for ver in sorted(os.listdir(base), reverse=True) if os.path.isdir(base) else []:
+        p = os.path.join(base, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if os.path.exists(p):
+            return p
+    raise FileNotFoundError("clang AddressSanitizer runtime not found under " + base)
+
+
+def build_host_sanitized(verbose: bool = False, objs=None) -> str:
+    """Compile psa_api.cpp with host sanitizers and link _build/libpsa_hostsan.so with the other
+    objects of the last build (compiling them first if absent)."""
+    os.makedirs(BUILD, exist_ok=True)
+    if objs is None:
+        objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        if not all(os.path.exists(o) for o in objs):
+            build(verbose)
+    obj = os.path.join(BUILD, "psa_api_hostsan.o")
+    cmd = ([hipcc(), "-x", "hip", "-c", os.path.join(CSRC, "psa_api.cpp"), "-o", obj, "-g"] +
+           [f for f in CFLAGS if f != "-O3"] + ["-O1"] + HOSTSAN_FLAGS)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on psa_api.cpp (host sanitizers):\n{r.stdout}\n{r.stderr}")
+    others = [o for o in objs if not o.endswith("psa_api.o")]
+    cmd = ([hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-shared-libasan", "-o",
+            HOSTSAN_LIB + ".tmp", obj] + others + HOSTSAN_FLAGS[:4])
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed (host sanitizers):\n{r.stdout}\n{r.stderr}")
+    os.replace(HOSTSAN_LIB + ".tmp", HOSTSAN_LIB)
+    return HOSTSAN_LIB
+
+
 def build(verbose: bool = False, jobs: int = 0) -> str:
-    """Compile every source and link libpsa.so. Always recompiles. Returns the library path."""
+    """Compile every source and link libpsa.so (and the host-sanitized build of the C ABI's
+    host side). Always recompiles. Returns the library path."""
     os.makedirs(BUILD, exist_ok=True)
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 1)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
@@ -76,6 +121,7 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_host_sanitized(verbose, objs)
     return LIB
 
 

@@ -120,16 +120,22 @@ struct AttnWs {
     size_t bytes;
 };
 
+// The address `off` bytes into a workspace, or null when only the size is being computed
+// (base null): no arithmetic on a null pointer.
+template <typename T>
+T* ws_at(void* base, size_t off) {
+    return base == nullptr ? nullptr : reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
 AttnWs attn_ws_layout(const psa::Shape& s, void* base) {
     const size_t R = static_cast<size_t>(s.B) * s.H * s.NQB;
     AttnWs w;
-    char* p = static_cast<char*>(base);
     size_t off = 0;
-    w.dev_err = reinterpret_cast<int32_t*>(p + off);
+    w.dev_err = ws_at<int32_t>(base, off);
     off += kAlign;
-    w.row_ptr = reinterpret_cast<int32_t*>(p + off);
+    w.row_ptr = ws_at<int32_t>(base, off);
     off += align_up((R * 4 + 1) * sizeof(int32_t));
-    w.col_idx = reinterpret_cast<int32_t*>(p + off);
+    w.col_idx = ws_at<int32_t>(base, off);
     off += align_up(R * s.NKB * sizeof(int32_t));
     w.bytes = off;
     return w;
@@ -145,15 +151,17 @@ int64_t psa_pooled_rows(const psa_problem* prob) {
 }
 
 int psa_build_pyramid(const psa_problem* prob, const void* k, const void* v, void* k_pooled,
-                      void* v_pooled, void* stream) {
+                      void* v_pooled, int32_t out_dtype, void* stream) {
     psa::Shape s;
     int rc = check_problem(prob, &s);
     if (rc != PSA_OK) return rc;
+    if (out_dtype != PSA_F32 && out_dtype != PSA_BF16) return PSA_ERR_INVALID_ARG;
+    if (out_dtype != s.dtype && out_dtype != PSA_F32) return PSA_ERR_UNSUPPORTED;
     if (no_work(s)) return PSA_OK;
     if (!k || !v || !k_pooled || !v_pooled) return PSA_ERR_INVALID_ARG;
     if (!aligned16(k) || !aligned16(v) || !aligned16(k_pooled) || !aligned16(v_pooled))
         return PSA_ERR_INVALID_ARG;
-    return hip_status(psa::launch_pyramid(s, k, v, k_pooled, v_pooled,
+    return hip_status(psa::launch_pyramid(s, k, v, k_pooled, v_pooled, out_dtype,
                                           static_cast<hipStream_t>(stream)));
 }
 
@@ -180,14 +188,34 @@ int psa_mask(const psa_problem* prob, const psa_mask_params* params, const void*
     if (need > 0 && (ws == nullptr || ws_bytes < need)) return PSA_ERR_WORKSPACE;
     hipStream_t st = static_cast<hipStream_t>(stream);
     psa::MaskBufs mb{block_mass, block_sim, ws, ws_bytes};
-    hipError_t e = psa::launch_mask_scores(s, *params, q, k, mb, st);
+    hipError_t e = psa::launch_clear_i32(psa::mask_cert_counters(s, *params, ws), 2, st);
     if (e != hipSuccess) return hip_status(e);
+    if ((e = psa::launch_mask_scores(s, *params, q, k, mb, st)) != hipSuccess) return hip_status(e);
     const bool use_sim = params->cos_sim_min > 0.f;
     if (use_sim) {
-        e = psa::launch_block_sim(s, k, block_sim, st);
+        e = psa::launch_block_sim(s, k, block_sim, psa::mask_sim64(s, *params, mb), st);
         if (e != hipSuccess) return hip_status(e);
     }
-    return hip_status(psa::launch_mask_assign_logmass(s, *params, mb, level_map, st));
+    if ((e = psa::launch_mask_assign_logmass(s, *params, mb, level_map, st)) != hipSuccess)
+        return hip_status(e);
+    return hip_status(psa::launch_mask_certify(s, *params, q, k, mb, level_map, st));
+}
+
+int psa_mask_certified_rows(const psa_problem* prob, const psa_mask_params* params,
+                            const void* ws, int32_t* counts, void* stream) {
+    psa::Shape s;
+    int rc = check_problem(prob, &s);
+    if (rc != PSA_OK) return rc;
+    if ((rc = check_mask_params(prob, params)) != PSA_OK) return rc;
+    if (counts == nullptr) return PSA_ERR_INVALID_ARG;
+    counts[0] = counts[1] = 0;
+    if (no_work(s)) return PSA_OK;
+    if (ws == nullptr) return PSA_ERR_INVALID_ARG;
+    const int* c = psa::mask_cert_counters(s, *params, const_cast<void*>(ws));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(counts, c, 2 * sizeof(int32_t), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    return hip_status(e);
 }
 
 int psa_mask_assign(const psa_problem* prob, const psa_mask_params* params,
@@ -387,19 +415,21 @@ struct MeanKeyWs {
     float* qbar;
     float* kbar;
     float* sim;
+    double* sim64;
     size_t bytes;
 };
 
 MeanKeyWs meankey_ws_layout(const psa::Shape& s, void* base) {
     MeanKeyWs w;
-    char* p = static_cast<char*>(base);
     size_t off = 0;
-    w.qbar = reinterpret_cast<float*>(p + off);
+    w.qbar = ws_at<float>(base, off);
     off += align_up(static_cast<size_t>(s.B) * s.H * s.NQB * s.D * sizeof(float));
-    w.kbar = reinterpret_cast<float*>(p + off);
+    w.kbar = ws_at<float>(base, off);
     off += align_up(static_cast<size_t>(s.B) * s.Hkv * s.NKB * s.D * sizeof(float));
-    w.sim = reinterpret_cast<float*>(p + off);
+    w.sim = ws_at<float>(base, off);
     off += align_up(static_cast<size_t>(s.B) * s.Hkv * s.NKB * sizeof(float));
+    w.sim64 = ws_at<double>(base, off);
+    off += align_up(static_cast<size_t>(s.B) * s.Hkv * s.NKB * sizeof(double));
     w.bytes = off;
     return w;
 }
@@ -437,11 +467,11 @@ int psa_attn_fwd_meankey(const psa_problem* prob, const psa_mask_params* params,
     MeanKeyWs w = meankey_ws_layout(s, ws);
     hipError_t e = psa::launch_block_means(s, q, k, w.qbar, w.kbar, st);
     if (e != hipSuccess) return hip_status(e);
-    if (params->cos_sim_min > 0.f && (e = psa::launch_block_sim(s, k, w.sim, st)) != hipSuccess)
+    if (params->cos_sim_min > 0.f && (e = psa::launch_block_sim(s, k, w.sim, w.sim64, st)) != hipSuccess)
         return hip_status(e);
     return hip_status(psa::launch_attn_fwd_meankey(s, scale, *params, q, k, v, k_pooled, v_pooled,
-                                                   w.qbar, w.kbar, w.sim, level_map, block_mass,
-                                                   o, lse, st));
+                                                   w.qbar, w.kbar, w.sim, w.sim64, level_map,
+                                                   block_mass, o, lse, st));
 }
 
 size_t psa_attn_bwd_workspace_bytes(const psa_problem* prob) {
@@ -511,5 +541,9 @@ const char* psa_status_string(int status) {
 }
 
 int psa_last_hip_error(void) { return g_last_hip_error; }
+
+int psa_debug_fill_lds(uint32_t pattern, void* stream) {
+    return hip_status(psa::launch_fill_lds(pattern, static_cast<hipStream_t>(stream)));
+}
 
 }  // extern "C"

@@ -65,6 +65,7 @@ struct MkArgs {
     int8_t* map_out;     // [B*H*NQB][NKB] or null
     AssignArgs asg;      // RQ = 1, sampling counting, sim set when the cosine check is on
     double c;            // (1 / sqrt(d)) * log2(e), the scorer's logit scale
+    double scale;        // 1 / sqrt(d), the certification's (natural-log) logit scale
 };
 
 struct Tile {
@@ -167,9 +168,44 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
                          ? static_cast<float>(dot * mk.c + log2(static_cast<double>(nv)))
                          : -INFINITY;
         }
+        __shared__ int cflag;
+        if (tid == 0) cflag = 0;
         __syncthreads();
         assign_masses(mk.asg, qb, Ls, Ms, mk.mass_out != nullptr ? mk.mass_out + static_cast<int64_t>(row) * NKB : nullptr, tid);
-        assign_levels(mk.asg, qb, b, hk, Ms, keys, lvl, tid);
+        assign_levels(mk.asg, qb, b, hk, Ms, keys, lvl, tid, &cflag);
+        if (cflag) {
+            // Certification, as psa_mask does it: a decision within the margins of the float32
+            // assignment is redone from float64 block-mean scores (same functions, same order as
+            // psa_mask's rescoring). Scratch: the float64 log-masses and then the sort keys in
+            // place of the float32 keys; q_bar and the sort's kb column after the levels when
+            // they fit in the K buffers, else over the dead float32 log-masses and masses.
+            char* kt = reinterpret_cast<char*>(&Kt[0][0]);
+            const int used = (4 * D + 9 * NKB + 7) & ~7;
+            const int need = 8 * D + 2 * mk.asg.P;
+            char* scr = used + need <= static_cast<int>(sizeof(Kt)) ? kt + used : reinterpret_cast<char*>(Ls);
+            double* qbar64 = reinterpret_cast<double*>(scr);
+            uint16_t* idx = reinterpret_cast<uint16_t*>(scr + 8 * D);
+            double* Ld = reinterpret_cast<double*>(keys);
+            cert_qbar_f64(Q + b * a.qs0 + h * a.qs1, a.qs2, qb, BQ, a.Nv, D, qbar64, tid);
+            __syncthreads();
+            const bf16_bits* kh = K + b * a.ks0 + hk * a.ks1;
+            for (int kb = tid; kb < NKB; kb += 256)
+                Ld[kb] = cert_meankey_logmass(kh, a.ks2, qbar64, D, kb, a.Nv, qlo < a.Nv && kb <= lastk, mk.scale);
+            __syncthreads();
+            __shared__ double clse[32], cwm[4][32], cws[4][32];
+            cert_lse(Ld, 1, NKB, clse, cwm, cws, tid);
+            const int den = cert_den(mk.asg, qb);
+            for (int kb = tid; kb < NKB; kb += 256) {
+                const double mass = cert_mass(Ld, clse, 1, NKB, kb, den);
+                if (mk.mass_out != nullptr) mk.mass_out[static_cast<int64_t>(row) * NKB + kb] = static_cast<float>(mass);
+                if (kb <= lastk) {
+                    keys[kb] = ~double_order(mass);
+                    idx[kb] = static_cast<uint16_t>(kb);
+                }
+            }
+            __syncthreads();
+            assign_levels_f64(mk.asg, qb, b, hk, keys, idx, lvl, tid);
+        }
         if (mk.map_out != nullptr)
             for (int kb = tid; kb < NKB; kb += 256) mk.map_out[static_cast<int64_t>(row) * NKB + kb] = lvl[kb];
         // the list: level 0, 1, 2, 3, ascending kb within a level (an ordered compaction)
@@ -1042,8 +1078,8 @@ hipError_t launch_attn_fp8qk(const Shape& s, const AttnArgs& a, hipStream_t st) 
 hipError_t launch_attn_fwd_meankey(const Shape& s, float scale, const psa_mask_params& mp,
                                    const void* q, const void* k, const void* v, const void* kp,
                                    const void* vp, const float* qbar, const float* kbar,
-                                   const float* sim, int8_t* map_out, float* mass_out, void* o,
-                                   float* lse, hipStream_t st) {
+                                   const float* sim, const double* sim64, int8_t* map_out,
+                                   float* mass_out, void* o, float* lse, hipStream_t st) {
     if (s.dtype != PSA_BF16 || s.BQ != 128 || s.BK != 64 || s.NKB > 1792) return hipErrorNotSupported;
     if (s.B * s.H * s.NQB == 0) return hipSuccess;
     AttnArgs a{};
@@ -1064,11 +1100,13 @@ hipError_t launch_attn_fwd_meankey(const Shape& s, float scale, const psa_mask_p
     mk.map_out = map_out;
     mk.asg = assign_args_of(s, mp);
     mk.asg.sim = mp.cos_sim_min > 0.f ? sim : nullptr;
+    mk.asg.sim64 = mp.cos_sim_min > 0.f ? sim64 : nullptr;
     mk.asg.RQ = 1;
     mk.asg.rows_per_head = s.NQB;
     mk.asg.sampling = 1;   // one scoring row per query block, counted like a sampled row
     mk.asg.S = 1;
     mk.c = (1.0 / std::sqrt(static_cast<double>(s.D))) * 1.4426950408889634;
+    mk.scale = 1.0 / std::sqrt(static_cast<double>(s.D));
     if (s.D == 128) return launch_one<128, 128, true, 0, true>(s, a, st, mk);
     if (s.D == 64) return launch_one<64, 128, true, 0, true>(s, a, st, mk);
     return hipErrorNotSupported;

@@ -30,6 +30,19 @@ __global__ void __launch_bounds__(256) k_clear_i32(int32_t* p, int n) {
     if (i < n) p[i] = 0;
 }
 
+// Diagnostics: every word of the workgroup's 32 KB of LDS set to `pattern`. Launched with
+// enough workgroups to cover every CU's LDS several times over, so the next kernels on the
+// stream start on CUs whose LDS holds the pattern (LDS is not cleared between kernels).
+constexpr int kFillLdsWords = 32 * 1024 / 4;
+
+__global__ void __launch_bounds__(256) k_fill_lds(uint32_t pattern, int32_t* sink) {
+    __shared__ uint32_t lds[kFillLdsWords];
+    for (int i = threadIdx.x; i < kFillLdsWords; i += 256) lds[i] = pattern;
+    __syncthreads();
+    // one read keeps the stores (never true for a pattern the host passes with sink null)
+    if (sink != nullptr && threadIdx.x == 0 && lds[blockIdx.x % kFillLdsWords] == ~pattern) sink[0] = 1;
+}
+
 __global__ void __launch_bounds__(256)
     k_index_count(const int8_t* __restrict__ map, int64_t rows, int nkb,
                   int32_t* __restrict__ row_ptr, int32_t* __restrict__ dev_err) {
@@ -148,6 +161,17 @@ __global__ void __launch_bounds__(256)
 
 hipError_t launch_clear_i32(int32_t* p, int n, hipStream_t st) {
     hipLaunchKernelGGL(k_clear_i32, dim3((n + 255) / 256), dim3(256), 0, st, p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_lds(uint32_t pattern, hipStream_t st) {
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    // 160 KB of LDS per CU = 5 workgroups of 32 KB; four times that many
+    hipLaunchKernelGGL(k_fill_lds, dim3(static_cast<unsigned>(cus) * 20), dim3(256), 0, st, pattern,
+                       static_cast<int32_t*>(nullptr));
     return hipGetLastError();
 }
 

@@ -25,8 +25,9 @@ struct IndexBufs {
 
 // ---- launchers (each returns the launch's hipError_t) ----
 
+// out_dtype: the problem's dtype, or PSA_F32 (float32 levels of a bf16 problem)
 hipError_t launch_pyramid(const Shape& s, const void* k, const void* v, void* kp, void* vp,
-                          hipStream_t st);
+                          int out_dtype, hipStream_t st);
 
 hipError_t launch_build_index(const Shape& s, const int8_t* level_map, const IndexBufs& ib,
                               hipStream_t st);
@@ -87,7 +88,19 @@ constexpr int kAttnMaxKBlocks = 16384;
 hipError_t launch_mask_scores(const Shape& s, const psa_mask_params& mp, const void* q,
                               const void* k, const MaskBufs& mb, hipStream_t st);
 
-hipError_t launch_block_sim(const Shape& s, const void* k, float* block_sim, hipStream_t st);
+// sim64 (nullable): the same similarities in float64
+hipError_t launch_block_sim(const Shape& s, const void* k, float* block_sim, double* sim64,
+                            hipStream_t st);
+
+// Inside psa_mask's workspace: the float64 similarities (null without the cosine check) and the
+// two certification counters (rows flagged for float64 rescoring, rows beyond the capacity).
+double* mask_sim64(const Shape& s, const psa_mask_params& mp, const MaskBufs& mb);
+int* mask_cert_counters(const Shape& s, const psa_mask_params& mp, void* ws);
+
+// Float64 rescoring and reassignment of the rows the assignment flagged (after
+// launch_mask_assign_logmass; the counters must have been cleared before it).
+hipError_t launch_mask_certify(const Shape& s, const psa_mask_params& mp, const void* q,
+                               const void* k, const MaskBufs& mb, int8_t* level_map, hipStream_t st);
 
 // Mean of each query block's valid rows (qbar [B*H][NQB][D]) and of each KV block's valid keys
 // (kbar [B*Hkv][NKB][D]), float32.
@@ -102,8 +115,8 @@ hipError_t launch_block_means(const Shape& s, const void* q, const void* k, floa
 hipError_t launch_attn_fwd_meankey(const Shape& s, float scale, const psa_mask_params& mp,
                                    const void* q, const void* k, const void* v, const void* kp,
                                    const void* vp, const float* qbar, const float* kbar,
-                                   const float* sim, int8_t* map_out, float* mass_out, void* o,
-                                   float* lse, hipStream_t st);
+                                   const float* sim, const double* sim64, int8_t* map_out,
+                                   float* mass_out, void* o, float* lse, hipStream_t st);
 
 hipError_t launch_mask_assign(const Shape& s, const psa_mask_params& mp, const float* block_mass,
                               const float* block_sim, int8_t* level_map, hipStream_t st);
@@ -115,5 +128,8 @@ hipError_t launch_mask_assign_logmass(const Shape& s, const psa_mask_params& mp,
 // Clears one int32 on the device with a kernel (no memset node, so the call stays safe to
 // capture in a graph).
 hipError_t launch_clear_i32(int32_t* p, int n, hipStream_t st);
+
+// Diagnostics: fills the LDS of every CU with `pattern` (see psa_debug_fill_lds).
+hipError_t launch_fill_lds(uint32_t pattern, hipStream_t st);
 
 }  // namespace psa

@@ -107,8 +107,10 @@ __global__ void __launch_bounds__(kScoreThreads) k_mask_logmass(ScoreArgs a) {
     };
     if (MODE == 0) load_q(0);
 
+    // 64-column tiles; in antidiagonal mode the last one may be partial (N/S not a multiple
+    // of 64): its columns past ncols read no key and are masked like padding
     const int ncols = MODE == 0 ? a.N : a.N / S;
-    const int ntiles = ncols / 64;
+    const int ntiles = (ncols + 63) / 64;
     // tiles past the causal frontier of the workgroup's rows are fully masked
     int tiles_needed = ntiles;
     if (MODE == 1 && a.causal) tiles_needed = min(ntiles, r_last / 64 + 1);
@@ -129,7 +131,10 @@ __global__ void __launch_bounds__(kScoreThreads) k_mask_logmass(ScoreArgs a) {
             const int col = (cidx % (D / 8)) * 8;
             const int64_t key = MODE == 0 ? static_cast<int64_t>(j) * 64 + row
                                           : (static_cast<int64_t>(j) * 64 + row) * S + t;
-            kreg[i] = *reinterpret_cast<const u32x4*>(kbase + key * a.ks2 + col);
+            if (MODE == 1 && j * 64 + row >= ncols)
+                kreg[i] = u32x4{0u, 0u, 0u, 0u};
+            else
+                kreg[i] = *reinterpret_cast<const u32x4*>(kbase + key * a.ks2 + col);
         }
     };
     auto store_k = [&]() {
@@ -213,14 +218,16 @@ __global__ void __launch_bounds__(kScoreThreads) k_mask_logmass(ScoreArgs a) {
         }
         if (hi == 0 && row_in) {
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt) Lh[static_cast<int64_t>(j * KT + kt) * a.rows_per_head + r] = Lk[kt];
+            for (int kt = 0; kt < KT; ++kt)
+                if (j * KT + kt < a.NKB) Lh[static_cast<int64_t>(j * KT + kt) * a.rows_per_head + r] = Lk[kt];
         }
     }
     // tiles of this range past the causal frontier: no mass
     if (hi == 0 && row_in)
         for (int j = max(j_lo, j_end); j < j_hi; ++j)
 #pragma unroll
-            for (int kt = 0; kt < KT; ++kt) Lh[static_cast<int64_t>(j * KT + kt) * a.rows_per_head + r] = -INFINITY;
+            for (int kt = 0; kt < KT; ++kt)
+                if (j * KT + kt < a.NKB) Lh[static_cast<int64_t>(j * KT + kt) * a.rows_per_head + r] = -INFINITY;
 }
 
 // Sampling mode, the fast path: 64 rows per wave (two groups of 32 sharing every K operand
@@ -706,7 +713,7 @@ __global__ void __launch_bounds__(256) k_meankey_logmass(MeanKeyArgs a) {
 template <int D>
 __global__ void __launch_bounds__(256)
     k_block_sim(const bf16_bits* __restrict__ k, int64_t ks0, int64_t ks1, int64_t ks2, int Hkv,
-                int NKB, int Nv, int64_t items, float* __restrict__ sim) {
+                int NKB, int Nv, int64_t items, float* __restrict__ sim, double* __restrict__ sim64) {
     const int64_t item = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (item >= items) return;
@@ -717,7 +724,10 @@ __global__ void __launch_bounds__(256)
     const int lo = kb * 64;
     const int nv = min(max(Nv - lo, 0), 64);
     if (nv < 2) {
-        if (lane == 0) sim[item] = 1.f;
+        if (lane == 0) {
+            sim[item] = 1.f;
+            if (sim64 != nullptr) sim64[item] = 1.0;
+        }
         return;
     }
     // lane t owns key lo + t: its norm, then every lane accumulates head-dim slices of the
@@ -745,7 +755,11 @@ __global__ void __launch_bounds__(256)
         sq += s * s;
     }
     sq = wave_sum_f64(sq);
-    if (lane == 0) sim[item] = static_cast<float>((sq - self_sum) / (static_cast<double>(nv) * (nv - 1)));
+    const double sv = (sq - self_sum) / (static_cast<double>(nv) * (nv - 1));
+    if (lane == 0) {
+        sim[item] = static_cast<float>(sv);
+        if (sim64 != nullptr) sim64[item] = sv;
+    }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -783,10 +797,291 @@ __global__ void __launch_bounds__(kAssignThreads) k_mask_assign(AssignArgs a) {
         const float* Mrow = a.M + row * a.NKB;
         for (int kb = tid; kb < a.NKB; kb += kAssignThreads) Ms[kb] = Mrow[kb];
     }
+    __shared__ int cflag;
+    if (tid == 0) cflag = 0;
     __syncthreads();
-    assign_levels(a, qb, b, hk, Ms, keys, lvl, tid);
+    assign_levels(a, qb, b, hk, Ms, keys, lvl, tid, a.cert != nullptr ? &cflag : nullptr);
     int8_t* out = a.map + row * a.NKB;
     for (int kb = tid; kb < a.NKB; kb += kAssignThreads) out[kb] = lvl[kb];
+    if (a.cert != nullptr && tid == 0 && cflag) {
+        const int slot = atomicAdd(&a.cert[0], 1);
+        if (slot < a.cert_cap)
+            a.cert_rows[slot] = static_cast<int>(row);
+        else
+            atomicAdd(&a.cert[1], 1);
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Certification: float64 rescoring of the rows the float32 assignment flagged (a decision
+// within kCertAbs of a threshold, or a tie within kCertRel across a level change). Each
+// rescoring kernel walks (flagged row, column chunk) items over a fixed grid and writes, per
+// scoring row i of the query block and KV block kb, the natural log of the row's
+// unnormalised softmax mass on the block in float64 (logits are float64 dots of the bf16
+// inputs). k_cert_assign then forms the block masses in float64 (each scoring row normalised
+// by its logsumexp, averaged over the valid rows), runs the float64 assignment and overwrites
+// the row's levels and masses. Rows beyond the capacity keep the float32 decisions and are
+// counted in cert[1].
+// ---------------------------------------------------------------------------------------
+struct CertArgs {
+    const bf16_bits* q;
+    const bf16_bits* k;
+    int H, Hkv, N, Nv, BQ, NQB, NKB, causal;
+    int S;        // samples per query block (sampling) or stride (antidiagonal)
+    int RQ;       // scoring rows per query block
+    int64_t qs0, qs1, qs2, ks0, ks1, ks2;
+    double scale; // 1 / sqrt(d)
+    const int* cert;
+    const int* rows;
+    double* Lg;   // [cap][RQ][NKB]
+    int cap;
+    int nchunks;  // column chunks per row
+};
+
+// log of sum_t exp(z_t) over the lanes of a group of G consecutive lanes (a power of two
+// <= 64); -inf when every z is -inf. Every lane of the group gets the value.
+template <int G>
+__device__ __forceinline__ double group_logsumexp(double z) {
+    double m = z;
+#pragma unroll
+    for (int o = 1; o < G; o <<= 1) m = fmax(m, __shfl_xor(m, o, 64));
+    double e = m == -INFINITY ? 0.0 : exp(z - m);
+#pragma unroll
+    for (int o = 1; o < G; o <<= 1) e += __shfl_xor(e, o, 64);
+    return m == -INFINITY ? -INFINITY : m + log(e);
+}
+
+struct RowIds {
+    int qb, h, b, hk;
+};
+
+__device__ __forceinline__ RowIds row_ids(int row, int NQB, int H, int Hkv) {
+    RowIds r;
+    r.qb = row % NQB;
+    const int bh = row / NQB;
+    r.h = bh % H;
+    r.b = bh / H;
+    r.hk = r.h / (H / Hkv);
+    return r;
+}
+
+// Sampling mode: items (flagged row, chunk of 256 * KPT keys); thread = KPT keys (256 apart),
+// every sampled row of the query block against each (float64 dots over d); the sampled rows sit
+// in LDS as float64, [e][s], read two at a time. For key group j one wave covers one KV block.
+template <int D, int S>
+__global__ void __launch_bounds__(256) k_cert_sampling(CertArgs a) {
+    constexpr int KPT = S <= 8 ? 4 : (S == 16 ? 2 : 1);   // keys per thread (KPT * S <= 32 sums)
+    constexpr int SP = S < 2 ? 2 : S;                      // LDS row of one e: even length
+    __shared__ __attribute__((aligned(16))) double qs[D * SP];
+    const int tid = threadIdx.x;
+    const int nrows = min(a.cert[0], a.cap);
+    const int64_t items = static_cast<int64_t>(nrows) * a.nchunks;
+    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+        const int slot = static_cast<int>(it / a.nchunks);
+        const int chunk = static_cast<int>(it % a.nchunks);
+        const RowIds r = row_ids(a.rows[slot], a.NQB, a.H, a.Hkv);
+        const int rv = min(max(a.Nv - r.qb * a.BQ, 0), a.BQ);
+        __syncthreads();   // the previous item's reads of qs are done
+        const bf16_bits* qh = a.q + r.b * a.qs0 + r.h * a.qs1;
+        for (int i = tid; i < D * SP; i += 256) {
+            const int e = i / SP, si = i % SP;
+            const int qrow = r.qb * a.BQ + (si * rv) / S;
+            qs[i] = (rv > 0 && si < S) ? static_cast<double>(bf16_to_f32(qh[static_cast<int64_t>(qrow) * a.qs2 + e])) : 0.0;
+        }
+        __syncthreads();
+        const int t0 = chunk * 256 * KPT + tid;
+        double acc[KPT][S];
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+#pragma unroll
+            for (int si = 0; si < S; ++si) acc[j][si] = 0.0;
+        const bf16_bits* kh = a.k + r.b * a.ks0 + r.hk * a.ks1;
+        if (rv > 0 && t0 < a.Nv) {
+            for (int e0 = 0; e0 < D; e0 += 8) {
+                double kv[KPT][8];
+#pragma unroll
+                for (int j = 0; j < KPT; ++j) {
+                    const int t = t0 + 256 * j;
+                    u32x4 w = u32x4{0u, 0u, 0u, 0u};
+                    if (t < a.Nv) w = *reinterpret_cast<const u32x4*>(kh + static_cast<int64_t>(t) * a.ks2 + e0);
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) {
+                        kv[j][2 * x] = static_cast<double>(__uint_as_float(w[x] << 16));
+                        kv[j][2 * x + 1] = static_cast<double>(__uint_as_float(w[x] & 0xffff0000u));
+                    }
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const double* qe = &qs[(e0 + e) * SP];
+#pragma unroll
+                    for (int si = 0; si < S; si += 2) {
+                        const double2 q2 = *reinterpret_cast<const double2*>(qe + si);
+#pragma unroll
+                        for (int j = 0; j < KPT; ++j) {
+                            acc[j][si] = fma(q2.x, kv[j][e], acc[j][si]);
+                            if (si + 1 < S) acc[j][si + 1] = fma(q2.y, kv[j][e], acc[j][si + 1]);
+                        }
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) {
+            const int t = t0 + 256 * j;
+            const int kb = t >> 6;
+#pragma unroll
+            for (int si = 0; si < S; ++si) {
+                const int qrow = r.qb * a.BQ + (si * rv) / S;
+                const bool vis = rv > 0 && t < a.Nv && (!a.causal || t <= qrow);
+                const double L = group_logsumexp<64>(vis ? acc[j][si] * a.scale : -INFINITY);
+                if ((tid & 63) == 0 && kb < a.NKB)
+                    a.Lg[(static_cast<int64_t>(slot) * a.RQ + si) * a.NKB + kb] = L;
+            }
+        }
+    }
+}
+
+// Antidiagonal mode, stride S: items (flagged row, chunk of 512 compressed columns); thread =
+// columns c and c + 256, every compressed row i < RQ of the query block against each: the
+// float64 sum over t < S of q[(qb*RQ + i)*S + S-1-t] . k[c*S + t]. The query block's rows sit
+// in LDS as float32 (exact for bf16 values), [t][e][i], read four at a time. A KV block is
+// 64/S consecutive columns.
+template <int D, int S, int RQ>
+__global__ void __launch_bounds__(256) k_cert_antidiag(CertArgs a) {
+    constexpr int G = 64 / S;                 // columns per KV block
+    constexpr int CPT = 2;                    // columns per thread
+    __shared__ __attribute__((aligned(16))) float qs[S * D * RQ];   // qs[(t*D + e)*RQ + i]
+    const int tid = threadIdx.x;
+    const int ncols = a.N / S;
+    const int nrows = min(a.cert[0], a.cap);
+    const int64_t items = static_cast<int64_t>(nrows) * a.nchunks;
+    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+        const int slot = static_cast<int>(it / a.nchunks);
+        const int chunk = static_cast<int>(it % a.nchunks);
+        const RowIds r = row_ids(a.rows[slot], a.NQB, a.H, a.Hkv);
+        __syncthreads();
+        const bf16_bits* qh = a.q + r.b * a.qs0 + r.h * a.qs1;
+        for (int x = tid; x < S * D * RQ; x += 256) {
+            const int i = x % RQ, te = x / RQ, e = te % D, t = te / D;
+            qs[x] = bf16_to_f32(qh[static_cast<int64_t>(r.qb * a.BQ + i * S + S - 1 - t) * a.qs2 + e]);
+        }
+        __syncthreads();
+        const int c0 = chunk * 256 * CPT + tid;
+        const int rlast = r.qb * RQ + RQ - 1;   // last compressed row of the query block
+        double acc[CPT][RQ];
+#pragma unroll
+        for (int j = 0; j < CPT; ++j)
+#pragma unroll
+            for (int i = 0; i < RQ; ++i) acc[j][i] = 0.0;
+        bool any = false;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const int c = c0 + 256 * j;
+            any = any || (c < ncols && c * S + S - 1 < a.Nv && (!a.causal || c <= rlast));
+        }
+        if (any) {
+            const bf16_bits* kh = a.k + r.b * a.ks0 + r.hk * a.ks1;
+            for (int t = 0; t < S; ++t) {
+                for (int e0 = 0; e0 < D; e0 += 8) {
+                    double kv[CPT][8];
+#pragma unroll
+                    for (int j = 0; j < CPT; ++j) {
+                        const int c = c0 + 256 * j;
+                        u32x4 w = u32x4{0u, 0u, 0u, 0u};
+                        if (c < ncols) w = *reinterpret_cast<const u32x4*>(kh + static_cast<int64_t>(c * S + t) * a.ks2 + e0);
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) {
+                            kv[j][2 * x] = static_cast<double>(__uint_as_float(w[x] << 16));
+                            kv[j][2 * x + 1] = static_cast<double>(__uint_as_float(w[x] & 0xffff0000u));
+                        }
+                    }
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float* qe = &qs[(t * D + e0 + e) * RQ];
+#pragma unroll
+                        for (int i = 0; i < RQ; i += 4) {
+                            const f32x4 q4 = *reinterpret_cast<const f32x4*>(qe + i);
+#pragma unroll
+                            for (int u = 0; u < 4; ++u) {
+                                const double qd = static_cast<double>(q4[u]);
+#pragma unroll
+                                for (int j = 0; j < CPT; ++j) acc[j][i + u] = fma(qd, kv[j][e], acc[j][i + u]);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+            const int c = c0 + 256 * j;
+            const bool col_ok = c < ncols && c * S + S - 1 < a.Nv;
+            const int kb = c / G;
+#pragma unroll
+            for (int i = 0; i < RQ; ++i) {
+                const int rg = r.qb * RQ + i;
+                const bool row_ok = rg * S + S - 1 < a.Nv;
+                const bool vis = col_ok && row_ok && (!a.causal || c <= rg);
+                const double L = group_logsumexp<G>(vis ? acc[j][i] * a.scale : -INFINITY);
+                if ((tid % G) == 0 && c < ncols)
+                    a.Lg[(static_cast<int64_t>(slot) * RQ + i) * a.NKB + kb] = L;
+            }
+        }
+    }
+}
+
+// Block-mean mode: one workgroup per flagged row: q_bar and each KV block's log-mass in
+// float64 (the same functions as the fused prologue).
+template <int D>
+__global__ void __launch_bounds__(256) k_cert_meankey(CertArgs a) {
+    __shared__ double qbar[D];
+    const int tid = threadIdx.x;
+    const int nrows = min(a.cert[0], a.cap);
+    for (int slot = blockIdx.x; slot < nrows; slot += gridDim.x) {
+        const RowIds r = row_ids(a.rows[slot], a.NQB, a.H, a.Hkv);
+        __syncthreads();
+        cert_qbar_f64(a.q + r.b * a.qs0 + r.h * a.qs1, a.qs2, r.qb, a.BQ, a.Nv, D, qbar, tid);
+        __syncthreads();
+        const bool anyq = r.qb * a.BQ < a.Nv;
+        const int last = a.causal ? min((r.qb * a.BQ + a.BQ - 1) / 64, a.NKB - 1) : a.NKB - 1;
+        const bf16_bits* kh = a.k + r.b * a.ks0 + r.hk * a.ks1;
+        for (int kb = tid; kb < a.NKB; kb += 256)
+            a.Lg[static_cast<int64_t>(slot) * a.NKB + kb] =
+                cert_meankey_logmass(kh, a.ks2, qbar, D, kb, a.Nv, anyq && kb <= last, a.scale);
+    }
+}
+
+// One workgroup per flagged row: the float64 masses from Lg, the float64 assignment, then the
+// row's levels and masses (as float) overwrite the float32 ones.
+__global__ void __launch_bounds__(kAssignThreads) k_cert_assign(AssignArgs a, CertArgs c) {
+    extern __shared__ uint64_t ckeys[];               // a.P
+    uint16_t* idx = reinterpret_cast<uint16_t*>(ckeys + a.P);   // a.P
+    int8_t* lvl = reinterpret_cast<int8_t*>(idx + a.P);         // NKB
+    __shared__ double lse[32];
+    __shared__ double wm[kAssignThreads / 64][32], wsum[kAssignThreads / 64][32];
+    const int tid = threadIdx.x;
+    const int nrows = min(c.cert[0], c.cap);
+    for (int slot = blockIdx.x; slot < nrows; slot += gridDim.x) {
+        const int row = c.rows[slot];
+        const RowIds r = row_ids(row, a.NQB, a.H, a.Hkv);
+        const double* L = c.Lg + static_cast<int64_t>(slot) * a.RQ * a.NKB;
+        __syncthreads();
+        cert_lse(L, a.RQ, a.NKB, lse, wm, wsum, tid);
+        const int den = cert_den(a, r.qb);
+        const int last = a.causal ? min((r.qb * a.BQ + a.BQ - 1) / a.BK, a.NKB - 1) : a.NKB - 1;
+        for (int kb = tid; kb < a.NKB; kb += kAssignThreads) {
+            const double mass = cert_mass(L, lse, a.RQ, a.NKB, kb, den);
+            if (a.M_out != nullptr) a.M_out[static_cast<int64_t>(row) * a.NKB + kb] = static_cast<float>(mass);
+            if (kb <= last) {
+                ckeys[kb] = ~double_order(mass);
+                idx[kb] = static_cast<uint16_t>(kb);
+            }
+        }
+        __syncthreads();
+        assign_levels_f64(a, r.qb, r.b, r.hk, ckeys, idx, lvl, tid);
+        int8_t* out = a.map + static_cast<int64_t>(row) * a.NKB;
+        for (int kb = tid; kb < a.NKB; kb += kAssignThreads) out[kb] = lvl[kb];
+    }
 }
 
 template <int MODE, int S>
@@ -824,9 +1119,39 @@ struct ScoreGeom {
     int S, rows_per_head, RQ, rows_per_wg, wg_per_head, ntiles, nsplit, tiles_per_split;
     size_t ws_bytes;
     size_t qbar_off = 0, kbar_off = 0;   // block-mean mode: offsets of the means in the workspace
+    // certification: counters, flagged row list, float64 similarities, float64 log-masses
+    size_t cert_off = 0, rows_off = 0, sim64_off = 0, lg_off = 0;
+    int cap = 0;
 };
 
+// Float64 log-masses of the flagged rows take at most this much workspace; the rows that fit
+// (at least 16, at most all) are the certification capacity.
+constexpr size_t kCertLgBytes = size_t(64) << 20;
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+ScoreGeom score_geom_base(const Shape& s, const psa_mask_params& mp);
+
 ScoreGeom score_geom(const Shape& s, const psa_mask_params& mp) {
+    ScoreGeom g = score_geom_base(s, mp);
+    const int64_t R = static_cast<int64_t>(s.B) * s.H * s.NQB;
+    const size_t per_row = static_cast<size_t>(g.RQ) * s.NKB * sizeof(double);
+    const int64_t fit = per_row > 0 ? static_cast<int64_t>(kCertLgBytes / per_row) : R;
+    g.cap = static_cast<int>(std::min<int64_t>(R, std::max<int64_t>(16, fit)));
+    size_t off = align256(g.ws_bytes);
+    g.cert_off = off;
+    off += 256;
+    g.rows_off = off;
+    off = align256(off + static_cast<size_t>(g.cap) * sizeof(int));
+    g.sim64_off = off;
+    if (mp.cos_sim_min > 0.f) off = align256(off + static_cast<size_t>(s.B) * s.Hkv * s.NKB * sizeof(double));
+    g.lg_off = off;
+    off += static_cast<size_t>(g.cap) * per_row;
+    g.ws_bytes = off;
+    return g;
+}
+
+ScoreGeom score_geom_base(const Shape& s, const psa_mask_params& mp) {
     ScoreGeom g;
     if (mp.mode == PSA_MASK_MEANKEY) {
         // one scoring row per query block; workspace: log-masses, query and key block means
@@ -854,7 +1179,9 @@ ScoreGeom score_geom(const Shape& s, const psa_mask_params& mp) {
     g.rows_per_wg = sampling ? kSampRows : 128;
     g.wg_per_head = (g.rows_per_head + g.rows_per_wg - 1) / g.rows_per_wg;
     // column tiles: 64 columns (sampling), 128 compressed columns (antidiagonal fast path)
-    g.ntiles = sampling ? s.N / 64 : (s.N / g.S) / (antidiag_fast(s, g.S) ? kAdCols : 64);
+    // (the general antidiagonal path ends in a partial tile when N/S is not a multiple of 64)
+    g.ntiles = sampling ? s.N / 64
+                        : antidiag_fast(s, g.S) ? (s.N / g.S) / kAdCols : (s.N / g.S + 63) / 64;
     // enough workgroups to fill the chip several times over; at least 4 tiles per range
     const int64_t groups = static_cast<int64_t>(s.B) * s.H * g.wg_per_head;
     int64_t want = groups > 0 ? (2048 + groups - 1) / groups : 1;
@@ -980,7 +1307,11 @@ hipError_t launch_mask_assign_logmass(const Shape& s, const psa_mask_params& mp,
     a.L = static_cast<const float*>(mb.ws);
     a.M_out = mb.block_mass;
     a.sim = mp.cos_sim_min > 0.f ? mb.block_sim : nullptr;
+    a.sim64 = mask_sim64(s, mp, mb);
     a.map = level_map;
+    a.cert = reinterpret_cast<int*>(static_cast<char*>(mb.ws) + g.cert_off);
+    a.cert_rows = reinterpret_cast<int*>(static_cast<char*>(mb.ws) + g.rows_off);
+    a.cert_cap = g.cap;
     a.RQ = g.RQ;
     a.rows_per_head = g.rows_per_head;
     // block-mean mode: one row per query block, counted like a sampled row
@@ -1006,7 +1337,8 @@ hipError_t launch_block_means(const Shape& s, const void* q, const void* k, floa
     return hipGetLastError();
 }
 
-hipError_t launch_block_sim(const Shape& s, const void* k, float* block_sim, hipStream_t st) {
+hipError_t launch_block_sim(const Shape& s, const void* k, float* block_sim, double* sim64,
+                            hipStream_t st) {
     if (s.dtype != PSA_BF16) return hipErrorNotSupported;
     const int64_t items = static_cast<int64_t>(s.B) * s.Hkv * s.NKB;
     if (items == 0) return hipSuccess;
@@ -1014,11 +1346,96 @@ hipError_t launch_block_sim(const Shape& s, const void* k, float* block_sim, hip
     if (s.D == 128)
         hipLaunchKernelGGL(k_block_sim<128>, dim3(blocks), dim3(256), 0, st,
                            static_cast<const bf16_bits*>(k), s.ks[0], s.ks[1], s.ks[2], s.Hkv,
-                           s.NKB, s.Nv, items, block_sim);
+                           s.NKB, s.Nv, items, block_sim, sim64);
     else
         hipLaunchKernelGGL(k_block_sim<64>, dim3(blocks), dim3(256), 0, st,
                            static_cast<const bf16_bits*>(k), s.ks[0], s.ks[1], s.ks[2], s.Hkv,
-                           s.NKB, s.Nv, items, block_sim);
+                           s.NKB, s.Nv, items, block_sim, sim64);
+    return hipGetLastError();
+}
+
+double* mask_sim64(const Shape& s, const psa_mask_params& mp, const MaskBufs& mb) {
+    if (mp.cos_sim_min <= 0.f) return nullptr;
+    return reinterpret_cast<double*>(static_cast<char*>(mb.ws) + score_geom(s, mp).sim64_off);
+}
+
+int* mask_cert_counters(const Shape& s, const psa_mask_params& mp, void* ws) {
+    return reinterpret_cast<int*>(static_cast<char*>(ws) + score_geom(s, mp).cert_off);
+}
+
+hipError_t launch_mask_certify(const Shape& s, const psa_mask_params& mp, const void* q,
+                               const void* k, const MaskBufs& mb, int8_t* level_map, hipStream_t st) {
+    const ScoreGeom g = score_geom(s, mp);
+    char* ws = static_cast<char*>(mb.ws);
+    CertArgs c;
+    c.q = static_cast<const bf16_bits*>(q);
+    c.k = static_cast<const bf16_bits*>(k);
+    c.H = s.H; c.Hkv = s.Hkv; c.N = s.N; c.Nv = s.Nv; c.BQ = s.BQ; c.NQB = s.NQB; c.NKB = s.NKB;
+    c.causal = s.causal;
+    c.S = g.S;
+    c.RQ = g.RQ;
+    c.qs0 = s.qs[0]; c.qs1 = s.qs[1]; c.qs2 = s.qs[2];
+    c.ks0 = s.ks[0]; c.ks1 = s.ks[1]; c.ks2 = s.ks[2];
+    c.scale = 1.0 / std::sqrt(static_cast<double>(s.D));
+    c.cert = reinterpret_cast<const int*>(ws + g.cert_off);
+    c.rows = reinterpret_cast<const int*>(ws + g.rows_off);
+    c.Lg = reinterpret_cast<double*>(ws + g.lg_off);
+    c.cap = g.cap;
+    if (c.cap == 0) return hipSuccess;
+    // fixed grids walking the device-side count of flagged rows
+    const bool sampling = mp.mode == PSA_MASK_SAMPLING, antidiag = mp.mode == PSA_MASK_ANTIDIAG;
+    const int ncols = sampling ? s.N : antidiag ? s.N / g.S : 0;
+    const int per_item = sampling ? 256 * (g.S <= 8 ? 4 : (g.S == 16 ? 2 : 1)) : 512;
+    c.nchunks = (ncols + per_item - 1) / per_item;
+    const unsigned score_grid = static_cast<unsigned>(
+        std::min<int64_t>(2048, std::max<int64_t>(1, static_cast<int64_t>(c.cap) * std::max(1, c.nchunks))));
+    hipError_t e = hipSuccess;
+    const int D = s.D;
+#define PSA_CERT_SAMP(DD, SS) hipLaunchKernelGGL((k_cert_sampling<DD, SS>), dim3(score_grid), dim3(256), 0, st, c)
+#define PSA_CERT_AD(DD, SS, RR) hipLaunchKernelGGL((k_cert_antidiag<DD, SS, RR>), dim3(score_grid), dim3(256), 0, st, c)
+    if (sampling) {
+        switch (g.S) {
+            case 1: if (D == 128) PSA_CERT_SAMP(128, 1); else PSA_CERT_SAMP(64, 1); break;
+            case 2: if (D == 128) PSA_CERT_SAMP(128, 2); else PSA_CERT_SAMP(64, 2); break;
+            case 4: if (D == 128) PSA_CERT_SAMP(128, 4); else PSA_CERT_SAMP(64, 4); break;
+            case 8: if (D == 128) PSA_CERT_SAMP(128, 8); else PSA_CERT_SAMP(64, 8); break;
+            case 16: if (D == 128) PSA_CERT_SAMP(128, 16); else PSA_CERT_SAMP(64, 16); break;
+            case 32: if (D == 128) PSA_CERT_SAMP(128, 32); else PSA_CERT_SAMP(64, 32); break;
+            default: return hipErrorNotSupported;
+        }
+    } else if (antidiag) {
+        const int key = g.S * 100 + g.RQ;
+        switch (key) {
+            case 232: if (D == 128) PSA_CERT_AD(128, 2, 32); else PSA_CERT_AD(64, 2, 32); break;
+            case 416: if (D == 128) PSA_CERT_AD(128, 4, 16); else PSA_CERT_AD(64, 4, 16); break;
+            case 432: if (D == 128) PSA_CERT_AD(128, 4, 32); else PSA_CERT_AD(64, 4, 32); break;
+            case 808: if (D == 128) PSA_CERT_AD(128, 8, 8); else PSA_CERT_AD(64, 8, 8); break;
+            case 816: if (D == 128) PSA_CERT_AD(128, 8, 16); else PSA_CERT_AD(64, 8, 16); break;
+            default: return hipErrorNotSupported;
+        }
+    } else {
+        const unsigned grid = static_cast<unsigned>(std::min(c.cap, 1024));
+        if (D == 128)
+            hipLaunchKernelGGL(k_cert_meankey<128>, dim3(grid), dim3(256), 0, st, c);
+        else
+            hipLaunchKernelGGL(k_cert_meankey<64>, dim3(grid), dim3(256), 0, st, c);
+    }
+#undef PSA_CERT_SAMP
+#undef PSA_CERT_AD
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    AssignArgs a = assign_args(s, mp);
+    a.M_out = mb.block_mass;
+    a.sim = mp.cos_sim_min > 0.f ? mb.block_sim : nullptr;
+    a.sim64 = mask_sim64(s, mp, mb);
+    a.map = level_map;
+    a.RQ = g.RQ;
+    a.rows_per_head = g.rows_per_head;
+    a.sampling = mp.mode != PSA_MASK_ANTIDIAG;
+    a.S = g.S;
+    const size_t lds = static_cast<size_t>(a.P) * (sizeof(uint64_t) + sizeof(uint16_t)) + s.NKB;
+    if (lds > kAssignMaxLds) return hipErrorNotSupported;
+    hipLaunchKernelGGL(k_cert_assign, dim3(static_cast<unsigned>(std::min(c.cap, 1024))),
+                       dim3(kAssignThreads), lds, st, a, c);
     return hipGetLastError();
 }
 

@@ -6,9 +6,11 @@
 // the 8 rows once (16 B per row for bf16, 32 B for f32), forms level 1 as pairwise means of
 // the rows, level 2 as pairwise means of level 1, level 3 as the mean of the two level-2 rows,
 // and writes 4 + 2 + 1 output rows. Scaling by 1/2 is exact, so this "progressive" tree gives
-// the same bits as the direct mean summed pairwise. HBM-bound: it reads K and V once and
-// writes 7/8 of their size. Consecutive threads walk head_dim first, then windows, so each
-// wave reads whole contiguous rows.
+// the same bits as the direct mean summed pairwise. The output is either the input dtype
+// (bf16 rounded to nearest even) or float32 (the tree's values themselves, for parity runs).
+// HBM-bound: it reads K and V once and writes 7/8 of their size (in the output dtype).
+// Consecutive threads walk head_dim first, then windows, so each wave reads whole contiguous
+// rows.
 #include "psa_device.h"
 #include "psa_internal.h"
 
@@ -68,7 +70,7 @@ struct PyrArgs {
     int64_t work;         // windows * chunks per tensor = B*Hkv*(N/8)*(D/8)
 };
 
-template <typename T>
+template <typename T, typename TO>
 __global__ void __launch_bounds__(256) k_pyramid(PyrArgs a) {
     const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     const int tensor = blockIdx.y;  // 0 = K, 1 = V
@@ -101,22 +103,22 @@ __global__ void __launch_bounds__(256) k_pyramid(PyrArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) l3[e] = (l2[0][e] + l2[1][e]) * 0.5f;
 
-    T* dst = static_cast<T*>(a.dst[tensor]) +
+    TO* dst = static_cast<TO*>(a.dst[tensor]) +
              (static_cast<int64_t>(b) * a.Hkv + h) * a.pooled_rows * a.D + c * 8;
     const int64_t D = a.D;
     const int64_t off2 = a.N >> 1, off3 = (a.N >> 1) + (a.N >> 2);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) Vec8<T>::store(dst + (static_cast<int64_t>(w) * 4 + j) * D, l1[j]);
+    for (int j = 0; j < 4; ++j) Vec8<TO>::store(dst + (static_cast<int64_t>(w) * 4 + j) * D, l1[j]);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-        Vec8<T>::store(dst + (off2 + static_cast<int64_t>(w) * 2 + j) * D, l2[j]);
-    Vec8<T>::store(dst + (off3 + w) * D, l3);
+        Vec8<TO>::store(dst + (off2 + static_cast<int64_t>(w) * 2 + j) * D, l2[j]);
+    Vec8<TO>::store(dst + (off3 + w) * D, l3);
 }
 
 }  // namespace
 
 hipError_t launch_pyramid(const Shape& s, const void* k, const void* v, void* kp, void* vp,
-                          hipStream_t st) {
+                          int out_dtype, hipStream_t st) {
     PyrArgs a;
     a.src[0] = k;
     a.src[1] = v;
@@ -133,10 +135,14 @@ hipError_t launch_pyramid(const Shape& s, const void* k, const void* v, void* kp
     a.work = static_cast<int64_t>(s.B) * s.Hkv * (s.N / 8) * (s.D / 8);
     if (a.work == 0) return hipSuccess;
     dim3 grid(static_cast<unsigned>((a.work + 255) / 256), 2);
-    if (s.dtype == PSA_BF16)
-        hipLaunchKernelGGL(k_pyramid<bf16_bits>, grid, dim3(256), 0, st, a);
+    if (s.dtype == PSA_BF16 && out_dtype == PSA_BF16)
+        hipLaunchKernelGGL((k_pyramid<bf16_bits, bf16_bits>), grid, dim3(256), 0, st, a);
+    else if (s.dtype == PSA_BF16 && out_dtype == PSA_F32)
+        hipLaunchKernelGGL((k_pyramid<bf16_bits, float>), grid, dim3(256), 0, st, a);
+    else if (s.dtype == PSA_F32 && out_dtype == PSA_F32)
+        hipLaunchKernelGGL((k_pyramid<float, float>), grid, dim3(256), 0, st, a);
     else
-        hipLaunchKernelGGL(k_pyramid<float>, grid, dim3(256), 0, st, a);
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

@@ -14,7 +14,9 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpsa.so")
+# PSA_LIBRARY selects another build of the same library (the host-sanitized one the CPU tests
+# run the argument checks under); by default the in-tree libpsa.so.
+LIB_PATH = os.environ.get("PSA_LIBRARY") or os.path.join(_HERE, "libpsa.so")
 
 PSA_OK = 0
 PSA_ERR_INVALID_ARG = -1
@@ -32,11 +34,11 @@ SKIP = -1
 
 # every symbol include/psa.h declares
 EXPORTS = ("psa_pooled_rows", "psa_build_pyramid", "psa_mask_workspace_bytes", "psa_mask",
-           "psa_mask_assign", "psa_build_index", "psa_attn_workspace_bytes", "psa_attn_fwd",
+           "psa_mask_assign", "psa_mask_certified_rows", "psa_build_index", "psa_attn_workspace_bytes", "psa_attn_fwd",
            "psa_attn_fwd_indexed", "psa_attn_fwd_unpacked", "psa_attn_bwd_workspace_bytes",
            "psa_attn_bwd", "psa_quantize_fp8", "psa_attn_fwd_fp8qk", "psa_attn_fwd_fp8",
            "psa_attn_fwd_meankey_workspace_bytes", "psa_attn_fwd_meankey", "psa_check_status",
-           "psa_status_string", "psa_last_hip_error")
+           "psa_status_string", "psa_last_hip_error", "psa_debug_fill_lds")
 
 
 class PsaError(RuntimeError):
@@ -79,10 +81,12 @@ def lib() -> ctypes.CDLL:
                               ctypes.c_int64, ctypes.c_size_t)
         MP = ctypes.POINTER(CMaskParams)
         L.psa_pooled_rows.argtypes, L.psa_pooled_rows.restype = [P], I64
-        L.psa_build_pyramid.argtypes, L.psa_build_pyramid.restype = [P, V, V, V, V, V], I32
+        L.psa_build_pyramid.argtypes, L.psa_build_pyramid.restype = [P, V, V, V, V, I32, V], I32
         L.psa_mask_workspace_bytes.argtypes, L.psa_mask_workspace_bytes.restype = [P, MP], SZ
         L.psa_mask.argtypes, L.psa_mask.restype = [P, MP, V, V, V, V, V, V, SZ, V], I32
         L.psa_mask_assign.argtypes, L.psa_mask_assign.restype = [P, MP, V, V, V, V], I32
+        L.psa_mask_certified_rows.argtypes = [P, MP, V, ctypes.POINTER(I32), V]
+        L.psa_mask_certified_rows.restype = I32
         L.psa_build_index.argtypes, L.psa_build_index.restype = [P, V, V, V, V, V], I32
         L.psa_attn_workspace_bytes.argtypes, L.psa_attn_workspace_bytes.restype = [P], SZ
         L.psa_attn_fwd.argtypes = [P, ctypes.c_float, V, V, V, V, V, V, V, V, V, SZ, V]
@@ -108,6 +112,7 @@ def lib() -> ctypes.CDLL:
         L.psa_check_status.argtypes, L.psa_check_status.restype = [V, V], I32
         L.psa_status_string.argtypes, L.psa_status_string.restype = [I32], ctypes.c_char_p
         L.psa_last_hip_error.argtypes, L.psa_last_hip_error.restype = [], I32
+        L.psa_debug_fill_lds.argtypes, L.psa_debug_fill_lds.restype = [ctypes.c_uint32, V], I32
         _LIB = L
     return _LIB
 
@@ -205,21 +210,27 @@ def pooled_rows(prob: Problem) -> int:
 
 
 def build_pyramid(k: torch.Tensor, v: torch.Tensor, prob: Problem,
-                  out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None, stream=None):
-    """Levels 1..3 of K and V packed as [B, Hkv, 7N/8, d] (level l at row N - 2N/2^l)."""
+                  out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None, stream=None,
+                  out_dtype: Optional[torch.dtype] = None):
+    """Levels 1..3 of K and V packed as [B, Hkv, 7N/8, d] (level l at row N - 2N/2^l), in
+    `out_dtype` (default: the input dtype; torch.float32 gives the unrounded levels)."""
     B, Hkv, _, d = k.shape
     if out is None:
+        dt = k.dtype if out_dtype is None else out_dtype
         shape = (B, Hkv, pooled_rows(prob), d)
-        out = (torch.empty(shape, dtype=k.dtype, device=k.device),
-               torch.empty(shape, dtype=v.dtype, device=v.device))
+        out = (torch.empty(shape, dtype=dt, device=k.device),
+               torch.empty(shape, dtype=dt, device=v.device))
     kp, vp = out
     _check(lib().psa_build_pyramid(prob.ref(), _ptr(k), _ptr(v), _ptr(kp), _ptr(vp),
-                                   _stream(stream)), "psa_build_pyramid")
+                                   _dtype_code(kp.dtype), _stream(stream)), "psa_build_pyramid")
     return kp, vp
 
 
-def mask(q: torch.Tensor, k: torch.Tensor, prob: Problem, params: MaskParams, stream=None):
-    """Returns (level_map int8 [B,H,NQB,NKB], block_mass f32 [B,H,NQB,NKB], block_sim or None)."""
+def mask(q: torch.Tensor, k: torch.Tensor, prob: Problem, params: MaskParams, stream=None,
+         cert_counts: Optional[list] = None):
+    """Returns (level_map int8 [B,H,NQB,NKB], block_mass f32 [B,H,NQB,NKB], block_sim or None).
+    With a list `cert_counts`, the call's certification counters are appended to it (rows
+    rescored in float64, flagged rows left uncertified); reading them synchronizes the stream."""
     B, H = q.shape[:2]
     Hkv = k.shape[1]
     nqb, nkb = prob.n_qblocks, prob.n_kblocks
@@ -232,6 +243,11 @@ def mask(q: torch.Tensor, k: torch.Tensor, prob: Problem, params: MaskParams, st
     ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     _check(lib().psa_mask(prob.ref(), ctypes.byref(cp), _ptr(q), _ptr(k), _ptr(lm), _ptr(mass),
                           _ptr(sim), _ptr(ws), nbytes, _stream(stream)), "psa_mask")
+    if cert_counts is not None:
+        c = (ctypes.c_int32 * 2)()
+        _check(lib().psa_mask_certified_rows(prob.ref(), ctypes.byref(cp), _ptr(ws), c,
+                                             _stream(stream)), "psa_mask_certified_rows")
+        cert_counts.extend([int(c[0]), int(c[1])])
     return lm, mass, sim
 
 
@@ -445,3 +461,9 @@ def forward(q, k, v, *, block_q: int, params: MaskParams, causal: bool = False,
     lm, _, _ = mask(q, k, prob, params)
     o, lse = attn_fwd(q, k, v, kp, vp, lm, prob, scale=scale)
     return o, lse, lm
+
+
+def debug_fill_lds(pattern: int, stream=None) -> None:
+    """Diagnostics: fill every CU's LDS with the 32-bit `pattern` on the stream."""
+    _check(lib().psa_debug_fill_lds(ctypes.c_uint32(pattern & 0xffffffff), _stream(stream)),
+           "psa_debug_fill_lds")
