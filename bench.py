@@ -18,8 +18,11 @@ with one logical block per hardware tile on the same map). `roofline` is for tha
 kernel, timed with HIP events on the stream it runs on. `bwd` times psa_attn_bwd on the same
 map with a seeded output gradient (not part of `value`). `fp8` times the forward on e4m3
 operands (psa_quantize_fp8 of Q, K, V; psa_attn_fwd_fp8qk with only the q . k products on fp8,
-psa_attn_fwd_fp8 with the P V product too; same map; not part of `value`). `cpu_baseline` times the CPU oracle
-(fp64 numpy) on a bounded sample of the same workload on this host's cores.
+psa_attn_fwd_fp8 with the P V product too; same map; not part of `value`). `workloads` times the
+attention kernel on each of the five workloads (its own inputs and map; not part of `value`).
+`roofline.mfma` carries the MFMA busy fraction from the committed counter summary of the same
+kernel source. `cpu_baseline` times the CPU oracle (fp64 numpy) on a bounded sample of the same
+workload on this host's cores.
 """
 from __future__ import annotations
 
@@ -39,6 +42,7 @@ import workloads as W  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, TFLOP/s
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, TFLOP/s
+PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA, TFLOP/s
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, GB/s
 METRIC = "psa_attn_fwd ms/layer + effective TFLOP/s (% bf16 MFMA peak), Wan-like 32k"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_fwd_bf16_traffic.txt")
@@ -140,6 +144,7 @@ def cpu_baseline(wl: W.Workload, budget_s: float = 15.0) -> dict:
     pairs = executed_pairs(lm[None, None, :n_rows], wl.replace(heads_q=1, batch=1))
     flops = 4.0 * wl.head_dim * pairs
     return {"value": round(flops / wall / 1e12, 6), "unit": "TFLOP/s", "cores": workers,
+            "cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0)),
             "kind": "oracle",
             "sample": f"fp64 numpy oracle attention over query blocks 0..{n_rows - 1} of head 0 "
                       f"(of {wl.heads_q} heads x {wl.n_qblocks} blocks), its own level map; "
@@ -168,6 +173,36 @@ def _traffic_from_profile(workload: str):
         return float(kv["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "psa_path_wan2.1-1.3b_32k_counters.txt")
+ATTN_KERNEL_BF16 = "k_attn_fwd_bf16<128, 128, true, true, 0, false>"
+
+
+def _attn_counters(workload: str):
+    """The bf16 attention kernel's rocprofv3 counters (mean per dispatch) from the committed
+    summary, or None if the attention source changed since they were taken or the workload
+    differs."""
+    if workload != "wan2.1-1.3b_32k" or not os.path.exists(COUNTERS_FILE):
+        return None
+    sha = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
+    text = open(COUNTERS_FILE).read()
+    if f"sha256: {sha}" not in text:
+        return None
+    out, cur = {}, None
+    for line in text.splitlines():
+        if line.startswith("#") or not line.strip():
+            continue
+        if not line.startswith(" "):
+            cur = line.strip()
+            continue
+        if cur == ATTN_KERNEL_BF16:
+            parts = line.split()
+            try:
+                out[parts[0]] = float(parts[1])
+            except (IndexError, ValueError):
+                pass
+    return out or None
 
 
 def _workload(args) -> W.Workload:
@@ -239,7 +274,8 @@ def run(args) -> dict:
         side.wait_event(fork)
         if ev:
             ev[5].record(side)
-        check(L.psa_build_pyramid(prob.ref(), ptr(k), ptr(v), ptr(kp), ptr(vp), st2), "pyramid")
+        check(L.psa_build_pyramid(prob.ref(), ptr(k), ptr(v), ptr(kp), ptr(vp),
+                                  psa.psa._dtype_code(kp.dtype), st2), "pyramid")
         if ev:
             ev[6].record(side)
         pyr_done.record(side)
@@ -335,9 +371,78 @@ def run(args) -> dict:
         out["fp8"] = fp8
     if meankey is not None:
         out["meankey_fused"] = meankey
+    if not args.no_workloads:
+        # every workload's attention kernel, driver-observed in this same line (the step
+        # above is the metric's workload; these are reported beside it)
+        out["workloads"] = {w.name: _workload_attention(w, dev) for w in W.ALL}
     out["attn"]["unpacked_same_map_ms"] = None if unpacked_ms != unpacked_ms else round(unpacked_ms, 3)
     out["attn"]["speedup_vs_unpacked"] = (None if unpacked_ms != unpacked_ms
                                           else round(unpacked_ms / attn_ms_mean, 2))
+    return out
+
+
+def _workload_attention(wl, dev, reps: int = 10) -> dict:
+    """One workload's attention on its own map (psa_mask, or the drawn map), inputs resident:
+    mean of `reps` back-to-back psa_attn_fwd_indexed calls after two untimed ones (sustained
+    attention load, unlike the step, where the pyramid and the mask run between attention
+    calls), executed level-weighted FLOP over that time, and the pyramid and psa_mask calls
+    timed once each (the first calls of the process)."""
+    import ctypes
+    import torch
+    import video_transformers_amd as psa
+    L = psa.lib()
+    ptr = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    stream = torch.cuda.current_stream()
+    st = ctypes.c_void_p(stream.cuda_stream)
+    q, k, v = (t.to(dev) for t in W.make_qkv(wl))
+    prob = psa.make_problem(q, k, v, block_q=wl.block_q, block_k=wl.block_k, causal=wl.causal,
+                            seq_valid=wl.seq_valid)
+    drawn = None if wl.map_source == "mask" else torch.from_numpy(W.make_map(wl)).to(dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record(stream)
+    kp, vp = psa.build_pyramid(k, v, prob)
+    ev[1].record(stream)
+    if wl.map_source == "mask":
+        params = psa.MaskParams(mode=wl.mask_mode, thresholds=tuple(wl.thresholds),
+                                samples_per_qblock=wl.samples_per_qblock,
+                                antidiag_stride=wl.antidiag_stride, cos_sim_min=wl.cos_sim_min,
+                                force_diag_l0=wl.force_diag_l0, force_l0_begin=wl.text_begin,
+                                force_l0_end=wl.text_end)
+        lm, _, _ = psa.mask(q, k, prob, params)
+    else:
+        lm = drawn
+    ev[2].record(stream)
+    rp, ci, err = psa.build_index(lm, prob)
+    ev[3].record(stream)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+
+    def call():
+        rc = L.psa_attn_fwd_indexed(prob.ref(), ctypes.c_float(0.0), ptr(q), ptr(k), ptr(v),
+                                    ptr(kp), ptr(vp), ptr(rp), ptr(ci), ptr(o), ptr(lse), st)
+        if rc != 0:
+            raise psa.PsaError(rc, f"attn {wl.name}")
+    ms = _timed_back_to_back(call, stream, reps=reps)
+    torch.cuda.synchronize()
+    if int(err.item()) != 0:
+        raise RuntimeError(f"{wl.name}: level map held invalid entries")
+    lm_host = lm.cpu().numpy()
+    pairs = executed_pairs(lm_host, wl)
+    d = wl.head_dim
+    tf = 4.0 * d * pairs / (ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_TFLOPS
+    out = {"attn_ms": round(ms, 4), "tflops_executed": round(tf, 2),
+           "pct_peak": round(100 * tf / peak, 2),
+           "peak": f"{'bf16' if wl.dtype == 'bf16' else 'fp32'} MFMA {peak:.1f} TFLOP/s",
+           "executed_pairs": int(pairs),
+           "effective_sparsity": round(1.0 - pairs / dense_pairs(wl), 4),
+           "pyramid_ms": round(ev[0].elapsed_time(ev[1]), 4),
+           "mask_ms": (round(ev[1].elapsed_time(ev[2]), 4) if wl.map_source == "mask" else None),
+           "map": (f"psa_mask {wl.mask_mode}" if wl.map_source == "mask" else f"drawn ({wl.map_source})"),
+           "shape": f"B{wl.batch} H{wl.heads_q}/{wl.heads_kv} N{wl.seq_len} (valid {wl.seq_valid}) "
+                    f"d{d} {wl.dtype} block_q {wl.block_q}{' causal' if wl.causal else ''}"}
+    del q, k, v, kp, vp, lm, rp, ci, o, lse
+    torch.cuda.empty_cache()
     return out
 
 
@@ -538,6 +643,19 @@ def _report(args, wl, flops, pairs, dpairs, frac, d, B, H, N, computed_map, attn
     ms_per_step = wall * 1e3 / args.steps
     attn_tflops = flops / (attn_ms_mean * 1e-3) / 1e12
     traffic = _traffic_from_profile(wl.name)
+    ctr = _attn_counters(wl.name) if wl.dtype == "bf16" else None
+    mfma = None
+    if ctr and "SQ_VALU_MFMA_BUSY_CYCLES" in ctr and "SQ_INSTS_MFMA" in ctr:
+        # busy cycles summed over the 1024 SIMDs, against this run's kernel time at the 2.4 GHz
+        # the peak is quoted at (the clock under MFMA load is lower, so this understates it)
+        simd_cycles = 1024 * attn_ms_mean * 1e-3 * 2.4e9
+        issued = ctr["SQ_INSTS_MFMA"] * 2 * 32 * 32 * 16
+        mfma = {"busy_pct": round(100 * ctr["SQ_VALU_MFMA_BUSY_CYCLES"] / simd_cycles, 1),
+                "issued_tflop_per_launch": round(issued / 1e12, 4),
+                "issued_tflops": round(issued / (attn_ms_mean * 1e-3) / 1e12, 1),
+                "executed_over_issued": round(flops / issued, 4),
+                "source": os.path.relpath(COUNTERS_FILE, ROOT) + " (SQ_VALU_MFMA_BUSY_CYCLES, "
+                          "SQ_INSTS_MFMA; this run's kernel time; 1024 SIMDs at 2.4 GHz)"}
     out = {
         "metric": METRIC,
         "value": round(flops / (ms_per_step * 1e-3) / 1e12, 3),
@@ -576,6 +694,7 @@ def _report(args, wl, flops, pairs, dpairs, frac, d, B, H, N, computed_map, attn
                      "traffic_gbs": None if traffic is None else round(traffic / (attn_ms_mean * 1e-3) / 1e9, 1),
                      "traffic_vs_hbm_peak": (None if traffic is None
                                              else round(traffic / (attn_ms_mean * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)),
+                     "mfma": mfma,
                      "kernel": "k_attn_fwd_bf16" if wl.dtype == "bf16" else "k_attn_fwd_f32",
                      "per_launch": f"{flops:.4e} executed FLOP (4*d per executed pair)"},
     }
@@ -599,6 +718,8 @@ def main():
                     help="skip the e4m3 forward timings (reported beside the forward metric)")
     ap.add_argument("--no-meankey", action="store_true",
                     help="skip the block-mean scoring comparison (two-step against fused)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the attention timings of all five workloads (reported beside the metric)")
     ap.add_argument("--mask-mode", choices=("sampling", "antidiag", "meankey"), default=None,
                     help="score with this psa_mask mode instead of the workload's own")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
