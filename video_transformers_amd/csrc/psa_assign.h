@@ -26,12 +26,13 @@ struct AssignArgs {
     const float* sim;
     const double* sim64;  // the similarities in float64 (psa_mask), used instead of sim if set
     int8_t* map;
-    // Certification (psa_mask): rows whose float32 decisions lie within kCertAbs of a threshold
-    // or kCertRel of a tie across a level change are listed here for float64 rescoring.
+    // Certification (psa_mask): rows whose float32 decisions lie within cert_abs of a threshold
+    // or cert_rel of a tie across a level change are listed here for float64 rescoring.
     // cert[0] counts flagged rows, cert[1] those beyond cert_cap (left as float32 decides).
     int* cert;          // null: no certification (given masses are exact by definition)
     int* cert_rows;     // [cert_cap]
     int cert_cap;
+    double cert_abs, cert_rel;   // the margins (cert_margins: per scoring mode)
     int H, Hkv, N, Nv, BQ, BK, NQB, NKB, causal;
     int P;  // sort length: power of two >= NKB
     int RQ, rows_per_head, sampling, S;   // scoring rows per query block (L path)
@@ -39,6 +40,19 @@ struct AssignArgs {
     float cos_min;
     int force_diag, force_lo, force_hi;
 };
+
+// Certification margins of a float32 assignment, per scoring mode: about five times the
+// largest relative error of its float32 block masses against float64 (measured on the GPU:
+// sampling and block-mean masses within 9e-7, antidiagonal within 6.3e-6: its logits sum
+// S*d = 1024 products, eight times the sampling mode's). The running sums then carry at
+// most that error times c <= 1, so a decision further than `cert_abs` from every threshold,
+// with no tie closer than `cert_rel` (relative) across a level change, is the float64 decision.
+struct CertMargins {
+    double abs, rel;
+};
+inline CertMargins cert_margins(int mode) {
+    return mode == PSA_MASK_ANTIDIAG ? CertMargins{3e-5, 3e-5} : CertMargins{4e-6, 4e-6};
+}
 
 // The arguments every assignment shares for one problem and mask parameters (the per-call
 // sources and destinations, M / L / M_out / sim / map and the log-mass geometry, are set by
@@ -62,16 +76,11 @@ inline AssignArgs assign_args_of(const Shape& s, const psa_mask_params& mp) {
     a.force_diag = mp.force_diag_l0 != 0;
     a.force_lo = mp.force_l0_begin;
     a.force_hi = mp.force_l0_end;
+    const CertMargins cm = cert_margins(mp.mode);
+    a.cert_abs = cm.abs;
+    a.cert_rel = cm.rel;
     return a;
 }
-
-// Certification margins of a float32 assignment. The float32 block masses agree with their
-// float64 values to a few 1e-6 relative (float32 logits of exact bf16 products, exp2 and the
-// per-row logsumexp), so the running sums to a few 1e-6 absolute: a decision further than
-// kCertAbs from every threshold, with no tie closer than kCertRel (relative) across a level
-// change, is the float64 decision.
-constexpr double kCertAbs = 1e-5;
-constexpr double kCertRel = 1e-5;
 
 // float <-> uint32 order-preserving maps (for a 64-bit sort key of mass and kb)
 __device__ __forceinline__ uint32_t float_order(float f) {
@@ -273,8 +282,8 @@ __device__ inline void assign_levels(const AssignArgs& a, int qb, int b, int hk,
                 if (cflag != nullptr) {
 #pragma unroll
                     for (int l = 0; l < 4; ++l)
-                        if (fabs(c - a.t[l]) < kCertAbs) flag = true;
-                    if (i > 0 && L != lprev && mprev - m <= kCertRel * mprev) flag = true;
+                        if (fabs(c - a.t[l]) < a.cert_abs) flag = true;
+                    if (i > 0 && L != lprev && mprev - m <= a.cert_rel * mprev) flag = true;
                     mprev = m;
                     lprev = L;
                 }

@@ -814,7 +814,7 @@ __global__ void __launch_bounds__(kAssignThreads) k_mask_assign(AssignArgs a) {
 
 // ---------------------------------------------------------------------------------------
 // Certification: float64 rescoring of the rows the float32 assignment flagged (a decision
-// within kCertAbs of a threshold, or a tie within kCertRel across a level change). Each
+// within the mode's margin of a threshold, or a tie within it across a level change). Each
 // rescoring kernel walks (flagged row, column chunk) items over a fixed grid and writes, per
 // scoring row i of the query block and KV block kb, the natural log of the row's
 // unnormalised softmax mass on the block in float64 (logits are float64 dots of the bf16
