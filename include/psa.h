@@ -75,6 +75,7 @@ extern "C" {
 #define PSA_ERR_WORKSPACE (-3)     /* workspace null or smaller than the *_workspace_bytes query */
 #define PSA_ERR_HIP (-4)           /* a HIP runtime call or kernel launch failed; see psa_last_hip_error */
 #define PSA_ERR_BAD_LEVEL_MAP (-5) /* a level map entry outside {-1,0,1,2,3} was seen on the device */
+#define PSA_ERR_SCRATCH (-6)       /* the allocation-free call's fixed scratch cannot hold the index */
 
 /* Element types. */
 #define PSA_F32 0
@@ -370,6 +371,26 @@ int psa_check_status(const void* ws, void* stream);
 
 /* Static string for a status code. */
 const char* psa_status_string(int status);
+
+/*
+ * Allocation-free psa_attn_fwd, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation). Same math, kernels
+ * and outputs as psa_attn_fwd; the block index it builds lives in a file-scope device array of
+ * psa_attn_fwd_noalloc_max_bytes() bytes (128 MiB) that each GPU holds from the library's load
+ * until the process ends, instead of a caller workspace. The call allocates and frees nothing.
+ * Needs 4*(R*4 + 1) + 4*R*NKB bytes (rounded up to 256 each; R = batch*heads_q*NQB) of it,
+ * else returns PSA_ERR_SCRATCH with nothing enqueued. dev_err: caller-owned device int32,
+ * cleared by the call and set to PSA_ERR_BAD_LEVEL_MAP on an invalid map entry (read it after
+ * the stream completes). Calls on one GPU share the array: calls that overlap on one GPU (two
+ * streams, two host threads) race; serialize them.
+ */
+int psa_attn_fwd_noalloc(const psa_problem* prob, float softmax_scale, const void* q, const void* k,
+                         const void* v, const void* k_pooled, const void* v_pooled,
+                         const int8_t* level_map, void* o, float* lse, int32_t* dev_err,
+                         void* stream);
+
+/* Size in bytes of psa_attn_fwd_noalloc's per-GPU scratch array. */
+size_t psa_attn_fwd_noalloc_max_bytes(void);
 
 /*
  * Diagnostics (no part of the path): enqueues workgroups that fill the LDS of every CU with

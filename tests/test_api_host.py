@@ -348,3 +348,26 @@ def test_attention_block_limit():
     for nkb, want in ((16385, P.PSA_ERR_UNSUPPORTED), (16384, P.PSA_ERR_WORKSPACE)):
         p = _big(nkb)
         assert L.psa_attn_fwd(p.ref(), 0.0, d, d, d, d, d, d, d, None, d, 0, None) == want
+
+
+def test_noalloc_host_checks():
+    """The allocation-free attention: the fixed scratch's size, a problem whose block index does
+    not fit it (PSA_ERR_SCRATCH), a missing output or error word (PSA_ERR_INVALID_ARG), an empty
+    problem (PSA_OK); nothing is launched in any of these."""
+    L = psa.lib()
+    cap = L.psa_attn_fwd_noalloc_max_bytes()
+    assert cap == 128 << 20
+    d = ctypes.c_void_p(256)
+    p = _prob(dtype=P.PSA_BF16)
+    assert L.psa_attn_fwd_noalloc(p.ref(), 0.0, d, d, d, d, d, d, d, None, None, None) == P.PSA_ERR_INVALID_ARG
+    assert L.psa_attn_fwd_noalloc(p.ref(), 0.0, d, d, d, d, d, d, None, None, d, None) == P.PSA_ERR_INVALID_ARG
+    # 40 heads x 1024 query blocks x 2048 KV blocks: a 335 MB index
+    big = torch.zeros(1, 40, 131072, 64)
+    pb = psa.make_problem(big, big, big, block_q=128)
+    pb.c.dtype = P.PSA_BF16
+    assert L.psa_attn_fwd_noalloc(pb.ref(), 0.0, d, d, d, d, d, d, d, None, d, None) == P.PSA_ERR_SCRATCH
+    pe = _prob(dtype=P.PSA_BF16)
+    pe.c.batch = 0
+    n = None
+    assert L.psa_attn_fwd_noalloc(pe.ref(), 0.0, *[n] * 9, n) == P.PSA_OK
+    assert b"SCRATCH" in L.psa_status_string(P.PSA_ERR_SCRATCH)

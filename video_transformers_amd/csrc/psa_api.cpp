@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "psa.h"
 #include "psa_internal.h"
@@ -536,6 +537,8 @@ const char* psa_status_string(int status) {
         case PSA_ERR_WORKSPACE: return "PSA_ERR_WORKSPACE: workspace missing, misaligned or too small";
         case PSA_ERR_HIP: return "PSA_ERR_HIP: HIP runtime or launch failure";
         case PSA_ERR_BAD_LEVEL_MAP: return "PSA_ERR_BAD_LEVEL_MAP: level map entry outside {-1,0,1,2,3}";
+        case PSA_ERR_SCRATCH:
+            return "PSA_ERR_SCRATCH: block index larger than the allocation-free call's fixed scratch";
         default: return "unknown psa status";
     }
 }
@@ -544,6 +547,80 @@ int psa_last_hip_error(void) { return g_last_hip_error; }
 
 int psa_debug_fill_lds(uint32_t pattern, void* stream) {
     return hip_status(psa::launch_fill_lds(pattern, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------------
+// Allocation-free attention: psa_attn_fwd with its block index (row_ptr, col_idx) in a
+// file-scope device array instead of a caller workspace. Each GPU holds its own copy of the
+// array from the library's load until the process ends; its device address is looked up once
+// per device (hipGetSymbolAddress, with that device current) and only that address is passed
+// to kernels. Every call on one GPU shares the array: calls that overlap on one GPU race.
+// ---------------------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = size_t(128) << 20;   // 128 MiB per GPU
+static __device__ __attribute__((aligned(256))) char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on its first use on that device).
+hipError_t scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t psa_attn_fwd_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+int psa_attn_fwd_noalloc(const psa_problem* prob, float softmax_scale, const void* q, const void* k,
+                         const void* v, const void* k_pooled, const void* v_pooled,
+                         const int8_t* level_map, void* o, float* lse, int32_t* dev_err,
+                         void* stream) {
+    psa::Shape s;
+    int rc = check_problem(prob, &s);
+    if (rc != PSA_OK) return rc;
+    if (s.NKB > psa::kAttnMaxKBlocks) return PSA_ERR_UNSUPPORTED;
+    if (no_work(s)) return PSA_OK;
+    if (!q || !k || !v || !k_pooled || !v_pooled || !level_map || !o || !dev_err)
+        return PSA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_pooled) ||
+        !aligned16(v_pooled) || !aligned16(o))
+        return PSA_ERR_INVALID_ARG;
+    if (!std::isfinite(softmax_scale)) return PSA_ERR_INVALID_ARG;
+    // the index: row_ptr [R*4 + 1] then col_idx [R*NKB], as in the workspace of psa_attn_fwd
+    const size_t R = static_cast<size_t>(s.B) * s.H * s.NQB;
+    const size_t rp_bytes = align_up((R * 4 + 1) * sizeof(int32_t));
+    const size_t need = rp_bytes + align_up(R * s.NKB * sizeof(int32_t));
+    if (need > kNoAllocScratchBytes) return PSA_ERR_SCRATCH;
+    void* base = nullptr;
+    hipError_t e = scratch_address(&base);
+    if (e != hipSuccess) return hip_status(e);
+    int32_t* row_ptr = static_cast<int32_t*>(base);
+    int32_t* col_idx = reinterpret_cast<int32_t*>(static_cast<char*>(base) + rp_bytes);
+    const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(s.D));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    psa::IndexBufs ib{row_ptr, col_idx, dev_err};
+    if ((e = psa::launch_build_index(s, level_map, ib, st)) != hipSuccess) return hip_status(e);
+    return hip_status(psa::launch_attn_fwd(s, scale, q, k, v, k_pooled, v_pooled, row_ptr, col_idx,
+                                           o, lse, true, st));
 }
 
 }  // extern "C"

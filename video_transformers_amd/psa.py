@@ -24,6 +24,7 @@ PSA_ERR_UNSUPPORTED = -2
 PSA_ERR_WORKSPACE = -3
 PSA_ERR_HIP = -4
 PSA_ERR_BAD_LEVEL_MAP = -5
+PSA_ERR_SCRATCH = -6
 PSA_F32 = 0
 PSA_BF16 = 1
 PSA_MASK_SAMPLING = 0
@@ -38,7 +39,8 @@ EXPORTS = ("psa_pooled_rows", "psa_build_pyramid", "psa_mask_workspace_bytes", "
            "psa_attn_fwd_indexed", "psa_attn_fwd_unpacked", "psa_attn_bwd_workspace_bytes",
            "psa_attn_bwd", "psa_quantize_fp8", "psa_attn_fwd_fp8qk", "psa_attn_fwd_fp8",
            "psa_attn_fwd_meankey_workspace_bytes", "psa_attn_fwd_meankey", "psa_check_status",
-           "psa_status_string", "psa_last_hip_error", "psa_debug_fill_lds")
+           "psa_status_string", "psa_last_hip_error", "psa_debug_fill_lds",
+           "psa_attn_fwd_noalloc", "psa_attn_fwd_noalloc_max_bytes")
 
 
 class PsaError(RuntimeError):
@@ -113,6 +115,9 @@ def lib() -> ctypes.CDLL:
         L.psa_status_string.argtypes, L.psa_status_string.restype = [I32], ctypes.c_char_p
         L.psa_last_hip_error.argtypes, L.psa_last_hip_error.restype = [], I32
         L.psa_debug_fill_lds.argtypes, L.psa_debug_fill_lds.restype = [ctypes.c_uint32, V], I32
+        L.psa_attn_fwd_noalloc.argtypes = [P, ctypes.c_float] + [V] * 9 + [V]
+        L.psa_attn_fwd_noalloc.restype = I32
+        L.psa_attn_fwd_noalloc_max_bytes.argtypes, L.psa_attn_fwd_noalloc_max_bytes.restype = [], SZ
         _LIB = L
     return _LIB
 
@@ -467,3 +472,15 @@ def debug_fill_lds(pattern: int, stream=None) -> None:
     """Diagnostics: fill every CU's LDS with the 32-bit `pattern` on the stream."""
     _check(lib().psa_debug_fill_lds(ctypes.c_uint32(pattern & 0xffffffff), _stream(stream)),
            "psa_debug_fill_lds")
+
+
+def attn_fwd_noalloc(q, k, v, k_pooled, v_pooled, level_map, prob: Problem, *, scale: float = 0.0,
+                     out: torch.Tensor, lse: Optional[torch.Tensor], dev_err: torch.Tensor,
+                     stream=None) -> None:
+    """psa_attn_fwd without a workspace: the block index lives in the library's fixed per-GPU
+    scratch array. Every output (o, lse, the int32 device error word) is caller-provided; the
+    call allocates nothing."""
+    _check(lib().psa_attn_fwd_noalloc(prob.ref(), ctypes.c_float(scale), _ptr(q), _ptr(k), _ptr(v),
+                                      _ptr(k_pooled), _ptr(v_pooled), _ptr(level_map), _ptr(out),
+                                      _ptr(lse), _ptr(dev_err), _stream(stream)),
+           "psa_attn_fwd_noalloc")
