@@ -245,7 +245,7 @@ def run(args) -> dict:
     cp0 = params.c()
     mask_ws_bytes = psa.lib().psa_mask_workspace_bytes(prob.ref(), ctypes.byref(cp0)) if computed_map else 0
     mask_ws = torch.empty(max(mask_ws_bytes, 256), dtype=torch.uint8, device=dev)
-    row_ptr = torch.empty(B * H * nqb * 4 + 1, dtype=torch.int32, device=dev)
+    row_ptr = torch.empty(B * H * nqb * 5 + 1, dtype=torch.int32, device=dev)
     col_idx = torch.empty(B * H * nqb * nkb, dtype=torch.int32, device=dev)
     dev_err = torch.empty(1, dtype=torch.int32, device=dev)
     o = torch.empty_like(q)
@@ -583,7 +583,7 @@ def _meankey_run(wl, prob, params, L, ptr, st, check, q, k, v, kp, vp, stream):
     mws = torch.empty(max(nm, 256), dtype=torch.uint8, device=dev)
     nf = L.psa_attn_fwd_meankey_workspace_bytes(prob.ref())
     fws = torch.empty(max(nf, 256), dtype=torch.uint8, device=dev)
-    rp = torch.empty(B * H * nqb * 4 + 1, dtype=torch.int32, device=dev)
+    rp = torch.empty(B * H * nqb * 5 + 1, dtype=torch.int32, device=dev)
     ci = torch.empty(B * H * nqb * nkb, dtype=torch.int32, device=dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     o2, of = torch.empty_like(q), torch.empty_like(q)

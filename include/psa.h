@@ -197,8 +197,12 @@ int psa_mask_assign(const psa_problem* prob, const psa_mask_params* params,
 
 /*
  * Block index: a CSR over (row, level) keys, rows r = (b*heads_q + h)*NQB + qb.
- * row_ptr[R*4+1] int32: col_idx[row_ptr[r*4+l] .. row_ptr[r*4+l+1]) lists, in ascending
- * order, the kb with level_map == l. col_idx needs capacity R*NKB int32; its entries past
+ * row_ptr[R*5+1] int32: col_idx[row_ptr[r*4+l] .. row_ptr[r*4+l+1]) lists, in ascending
+ * order, the kb with level_map == l; then row_ptr[R*4+1 + p], p < R, is the row the attention
+ * runs in dispatch slot p (a permutation of the rows: slot p runs on XCD p / ceil(R/8), each
+ * XCD's contiguous range of rows listed by their count of 64-row tiles, sum over l of
+ * ceil(n_l / 2^l), largest first; a stable counting sort over 32 buckets of the range's span of
+ * counts, exact when that span is at most 32). col_idx needs capacity R*NKB int32; its entries past
  * row_ptr[R*4] are unspecified (the call parks scan partial sums there). Entries outside
  * {-1..3} are treated as skip and set *dev_err (device int32) to PSA_ERR_BAD_LEVEL_MAP;
  * the call clears *dev_err first.
@@ -378,7 +382,7 @@ const char* psa_status_string(int status);
  * and outputs as psa_attn_fwd; the block index it builds lives in a file-scope device array of
  * psa_attn_fwd_noalloc_max_bytes() bytes (128 MiB) that each GPU holds from the library's load
  * until the process ends, instead of a caller workspace. The call allocates and frees nothing.
- * Needs 4*(R*4 + 1) + 4*R*NKB bytes (rounded up to 256 each; R = batch*heads_q*NQB) of it,
+ * Needs 4*(R*5 + 1) + 4*R*NKB bytes (rounded up to 256 each; R = batch*heads_q*NQB) of it,
  * else returns PSA_ERR_SCRATCH with nothing enqueued. dev_err: caller-owned device int32,
  * cleared by the call and set to PSA_ERR_BAD_LEVEL_MAP on an invalid map entry (read it after
  * the stream completes). Calls on one GPU share the array: calls that overlap on one GPU (two

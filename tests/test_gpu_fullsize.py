@@ -22,7 +22,7 @@ import torch
 import oracle
 import workloads as W
 import video_transformers_amd as psa
-from gpu_util import (DEV, announce, assign_params, check_attention, check_map,
+from gpu_util import (DEV, announce, assign_params, check_attention, check_map, dispatch_order,
                       mask_params, need_gpu, oracle_margin_entries)
 
 pytestmark = pytest.mark.gpu
@@ -64,6 +64,11 @@ def _run_path(wl, qd, kd, vd):
     o, lse = psa.attn_fwd_indexed(qd, kd, vd, kp, vp, row_ptr, col_idx, prob)
     torch.cuda.synchronize()
     assert err.item() == 0
+    # the dispatch order at full size: a permutation, from its definition bit for bit
+    rows = lm.numel() // prob.n_kblocks
+    rp = row_ptr.cpu().numpy()
+    assert np.array_equal(np.sort(rp[rows * 4 + 1:]), np.arange(rows))
+    assert np.array_equal(rp[rows * 4 + 1:], dispatch_order(rp, rows))
     return kp, vp, lm, M, sim, o, lse, cert
 
 

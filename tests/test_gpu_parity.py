@@ -12,7 +12,7 @@ import torch
 import oracle
 import workloads as W
 import video_transformers_amd as psa
-from gpu_util import (DEV, announce, assign_params, check_attention, check_map,
+from gpu_util import (DEV, announce, assign_params, check_attention, check_index, check_map,
                       mask_params, need_gpu, oracle_map, oracle_margin_entries, oracle_problem,
                       problem_for)
 
@@ -97,9 +97,7 @@ def test_build_index_exact(shape):
     prob = psa.make_problem(q, q, q, block_q=bq)
     row_ptr, col_idx, err = psa.build_index(torch.from_numpy(lm).to(DEV), prob)
     rp_ref, ci_ref = oracle.build_index(lm)
-    rp = row_ptr.cpu().numpy()
-    assert np.array_equal(rp, rp_ref)
-    assert np.array_equal(col_idx.cpu().numpy()[:rp[-1]], ci_ref)
+    check_index(row_ptr, col_idx, rp_ref, ci_ref)
     assert err.item() == 0
 
 
@@ -111,7 +109,10 @@ def test_build_index_all_skip_many_tiles():
     q = torch.zeros((1, 40, 258 * 64, 64), device=DEV, dtype=torch.bfloat16)
     prob = psa.make_problem(q, q, q, block_q=128)
     row_ptr, col_idx, err = psa.build_index(torch.from_numpy(lm).to(DEV), prob)
-    assert not np.any(row_ptr.cpu().numpy())
+    rows = 40 * 129
+    rp = row_ptr.cpu().numpy()
+    assert not np.any(rp[:rows * 4 + 1])
+    assert np.array_equal(rp[rows * 4 + 1:], np.arange(rows))   # equal counts: rows in order
     assert err.item() == 0
 
 
@@ -126,8 +127,7 @@ def test_build_index_flags_bad_entries():
     assert err.item() == psa.psa.PSA_ERR_BAD_LEVEL_MAP
     clean = np.where((lm < -1) | (lm > 3), -1, lm).astype(np.int8)
     rp_ref, ci_ref = oracle.build_index(clean)
-    assert np.array_equal(row_ptr.cpu().numpy(), rp_ref)
-    assert np.array_equal(col_idx.cpu().numpy()[:rp_ref[-1]], ci_ref)
+    check_index(row_ptr, col_idx, rp_ref, ci_ref)
 
 
 def test_attn_reports_bad_level_map():

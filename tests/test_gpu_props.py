@@ -17,7 +17,7 @@ from hypothesis import strategies as st
 import oracle
 import workloads as W
 import video_transformers_amd as psa
-from gpu_util import (DEV, announce, check_attention, check_map, need_gpu, oracle_margin_entries,
+from gpu_util import (DEV, announce, check_attention, check_index, check_map, need_gpu, oracle_margin_entries,
                       problem_for)
 
 pytestmark = pytest.mark.gpu
@@ -66,8 +66,7 @@ def test_prop_attention_and_index(wl, skip_row):
     lmd = torch.from_numpy(lm).to(DEV)
     row_ptr, col_idx, err = psa.build_index(lmd, prob)
     rp_ref, ci_ref = oracle.build_index(lm)
-    rp = row_ptr.cpu().numpy()
-    assert np.array_equal(rp, rp_ref) and np.array_equal(col_idx.cpu().numpy()[:rp[-1]], ci_ref)
+    check_index(row_ptr, col_idx, rp_ref, ci_ref)
     assert err.item() == 0
     kp, vp = psa.build_pyramid(kd, vd, prob)
     o, lse = psa.attn_fwd_indexed(qd, kd, vd, kp, vp, row_ptr, col_idx, prob)

@@ -55,7 +55,7 @@ int check_problem(const psa_problem* p, psa::Shape* s) {
         return PSA_ERR_UNSUPPORTED;
     // every index the kernels form per (batch, head) row stays in int32 range
     const int64_t R = static_cast<int64_t>(p->batch) * p->heads_q * (p->seq_len / p->block_q);
-    if (R * 4 + 1 > INT32_MAX || R * (p->seq_len / 64) > INT32_MAX) return PSA_ERR_UNSUPPORTED;
+    if (R * 5 + 1 > INT32_MAX || R * (p->seq_len / 64) > INT32_MAX) return PSA_ERR_UNSUPPORTED;
     if (s != nullptr) {
         s->B = p->batch;
         s->H = p->heads_q;
@@ -135,7 +135,7 @@ AttnWs attn_ws_layout(const psa::Shape& s, void* base) {
     w.dev_err = ws_at<int32_t>(base, off);
     off += kAlign;
     w.row_ptr = ws_at<int32_t>(base, off);
-    off += align_up((R * 4 + 1) * sizeof(int32_t));
+    off += align_up((R * 5 + 1) * sizeof(int32_t));   // CSR offsets, then the dispatch order
     w.col_idx = ws_at<int32_t>(base, off);
     off += align_up(R * s.NKB * sizeof(int32_t));
     w.bytes = off;
@@ -605,9 +605,9 @@ int psa_attn_fwd_noalloc(const psa_problem* prob, float softmax_scale, const voi
         !aligned16(v_pooled) || !aligned16(o))
         return PSA_ERR_INVALID_ARG;
     if (!std::isfinite(softmax_scale)) return PSA_ERR_INVALID_ARG;
-    // the index: row_ptr [R*4 + 1] then col_idx [R*NKB], as in the workspace of psa_attn_fwd
+    // the index: row_ptr [R*5 + 1] then col_idx [R*NKB], as in the workspace of psa_attn_fwd
     const size_t R = static_cast<size_t>(s.B) * s.H * s.NQB;
-    const size_t rp_bytes = align_up((R * 4 + 1) * sizeof(int32_t));
+    const size_t rp_bytes = align_up((R * 5 + 1) * sizeof(int32_t));
     const size_t need = rp_bytes + align_up(R * s.NKB * sizeof(int32_t));
     if (need > kNoAllocScratchBytes) return PSA_ERR_SCRATCH;
     void* base = nullptr;

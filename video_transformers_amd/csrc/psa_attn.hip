@@ -232,6 +232,7 @@ AttnArgs make_args(const Shape& s, float scale, const void* q, const void* k, co
     a.lse = lse;
     a.row_ptr = row_ptr;
     a.col_idx = col_idx;
+    a.row_order = row_ptr != nullptr ? row_ptr + static_cast<int64_t>(s.B) * s.H * s.NQB * 4 + 1 : nullptr;
     a.H = s.H;
     a.Hkv = s.Hkv;
     a.N = s.N;

@@ -121,10 +121,12 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 
-    // XCD-aware row order: workgroup i runs on XCD i % 8; give each XCD a contiguous range.
+    // XCD-aware row order: workgroup i runs on XCD i % 8; give each XCD a contiguous range of
+    // rows, taken in the index's dispatch order (largest first) when it has one.
     const int nper = (total_rows + 7) >> 3;
-    const int row = (blockIdx.x & 7) * nper + (blockIdx.x >> 3);
-    if (row >= total_rows) return;
+    const int slot = (blockIdx.x & 7) * nper + (blockIdx.x >> 3);
+    if (slot >= total_rows) return;
+    const int row = a.row_order != nullptr ? a.row_order[slot] : slot;
     const int qb = row % a.NQB;
     const int bh = row / a.NQB;
     const int h = bh % a.H;

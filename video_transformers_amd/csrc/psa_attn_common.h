@@ -22,6 +22,9 @@ struct AttnArgs {
     float* lse;
     const int32_t* row_ptr;
     const int32_t* col_idx;
+    // dispatch order [R] (slot -> row; psa_build_index writes it after the CSR offsets), or
+    // null: slot = row
+    const int32_t* row_order;
     int H, Hkv, N, Nv, NQB, causal;
     int64_t qs0, qs1, qs2, ks0, ks1, ks2, vs0, vs1, vs2, os0, os1, os2;
     int64_t pooled_rows;

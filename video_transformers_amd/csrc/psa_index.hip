@@ -4,12 +4,14 @@
 // touches a skipped block (PSA summary article at rg.mbintangr.com, "Method": the least
 // important blocks are skipped entirely).
 //
-// Four launches, all integer and deterministic:
+// Five launches, all integer and deterministic:
 //   k_index_count       one wave per row: per-level counts via ballots (bad entries -> skip + flag)
 //   k_index_tile_sums   one workgroup per tile of 4096 counts: the tile's total
 //   k_index_scan_tiles  one workgroup per tile: the totals of the tiles before it, then the
 //                       tile's inclusive scan into row_ptr (in place)
 //   k_index_fill        one wave per row: ballot compaction of each level's kb into col_idx
+//   k_index_order       one workgroup per XCD range: the attention's dispatch order of the rows
+//                       (after the offsets in row_ptr)
 // The tile totals are parked at the start of col_idx, which the fill overwrites afterwards
 // (its capacity, rows * NKB, is at least the number of tiles).
 #include "psa_device.h"
@@ -157,6 +159,110 @@ __global__ void __launch_bounds__(256)
     }
 }
 
+// Dispatch order of the attention workgroups. Workgroup i runs on XCD i % 8, and the attention
+// kernels give XCD x the rows of one contiguous range [x * nper, (x + 1) * nper), nper =
+// ceil(rows / 8), so that neighbouring query blocks of a head share that XCD's L2. Inside a
+// range the rows are listed by their number of 64-row tiles (sum over levels l of
+// ceil(n_l / 2^l)), largest first: the workgroups an XCD starts last are then short ones and its
+// CUs run out of work together (longest-processing-time-first list scheduling). A stable
+// counting sort over kOrderBuckets buckets spanning the range's tile counts (exact for spans up
+// to kOrderBuckets, bucketed beyond); deterministic.
+constexpr int kOrderThreads = 256;
+constexpr int kOrderBuckets = 32;
+
+__device__ __forceinline__ int row_tiles(const int32_t* rp, int64_t r) {
+    const int32_t* p = rp + r * 4;
+    int t = 0;
+#pragma unroll
+    for (int l = 0; l < 4; ++l) t += (p[l + 1] - p[l] + (1 << l) - 1) >> l;
+    return t;
+}
+
+// exclusive scan of one value per thread over kOrderThreads threads
+__device__ int order_exclusive_scan(int v, int* wsum) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    int before = 0;
+#pragma unroll
+    for (int w = 0; w < kOrderThreads / 64; ++w)
+        if (w < wave) before += wsum[w];
+    __syncthreads();
+    return before + x - v;
+}
+
+__global__ void __launch_bounds__(kOrderThreads)
+    k_index_order(const int32_t* __restrict__ row_ptr, int64_t rows, int64_t nper,
+                  int32_t* __restrict__ order) {
+    __shared__ int hist[kOrderBuckets * kOrderThreads];   // [bucket][thread]
+    __shared__ int wred[2][kOrderThreads / 64];
+    __shared__ int wsum[kOrderThreads / 64];
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = t >> 6;
+    const int64_t lo = static_cast<int64_t>(blockIdx.x) * nper;
+    const int64_t hi = lo + nper < rows ? lo + nper : rows;
+    if (lo >= hi) return;   // uniform: an empty range
+    // thread t takes the consecutive rows [s0, s1) of the range
+    const int64_t seg = (hi - lo + kOrderThreads - 1) / kOrderThreads;
+    const int64_t s0 = lo + t * seg < hi ? lo + t * seg : hi;
+    const int64_t s1 = s0 + seg < hi ? s0 + seg : hi;
+    // the span of the tile counts
+    int cmin = 0x7fffffff, cmax = 0;
+    for (int64_t r = s0; r < s1; ++r) {
+        const int c = row_tiles(row_ptr, r);
+        cmin = min(cmin, c);
+        cmax = max(cmax, c);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        cmin = min(cmin, __shfl_xor(cmin, o, 64));
+        cmax = max(cmax, __shfl_xor(cmax, o, 64));
+    }
+    if (lane == 0) {
+        wred[0][wave] = cmin;
+        wred[1][wave] = cmax;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kOrderThreads / 64; ++w) {
+        cmin = min(cmin, wred[0][w]);
+        cmax = max(cmax, wred[1][w]);
+    }
+    const int span = cmax - cmin + 1;
+    auto bucket = [&](int c) { return static_cast<int>((static_cast<int64_t>(cmax - c) * kOrderBuckets) / span); };
+    // per (bucket, thread) counts, then their exclusive scan in bucket-major order: the first
+    // position of each thread's rows of each bucket (stable: bucket, then thread, then row)
+#pragma unroll
+    for (int b = 0; b < kOrderBuckets; ++b) hist[b * kOrderThreads + t] = 0;
+    for (int64_t r = s0; r < s1; ++r) ++hist[bucket(row_tiles(row_ptr, r)) * kOrderThreads + t];
+    __syncthreads();
+    constexpr int PER = kOrderBuckets;   // entries per thread: kOrderBuckets * kOrderThreads / kOrderThreads
+    int loc = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) loc += hist[t * PER + j];
+    int run = order_exclusive_scan(loc, wsum);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int c = hist[t * PER + j];
+        hist[t * PER + j] = run;
+        run += c;
+    }
+    __syncthreads();
+    for (int64_t r = s0; r < s1; ++r) {
+        int* slot = &hist[bucket(row_tiles(row_ptr, r)) * kOrderThreads + t];
+        order[lo + *slot] = static_cast<int32_t>(r);
+        ++*slot;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_clear_i32(int32_t* p, int n, hipStream_t st) {
@@ -192,6 +298,9 @@ hipError_t launch_build_index(const Shape& s, const int8_t* level_map, const Ind
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(k_index_fill, dim3(blocks), dim3(256), 0, st, level_map, rows, s.NKB,
                        ib.row_ptr, ib.col_idx);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_index_order, dim3(8), dim3(kOrderThreads), 0, st, ib.row_ptr, rows, (rows + 7) / 8,
+                       ib.row_ptr + rows * 4 + 1);
     return hipGetLastError();
 }
 

@@ -18,7 +18,7 @@ struct Shape {
 };
 
 struct IndexBufs {
-    int32_t* row_ptr;  // [R*4 + 1]
+    int32_t* row_ptr;  // [R*5 + 1]: the CSR offsets [R*4 + 1], then the dispatch order [R]
     int32_t* col_idx;  // [R*NKB]
     int32_t* dev_err;  // [1]
 };

@@ -266,10 +266,11 @@ def mask_assign(block_mass: torch.Tensor, block_sim: Optional[torch.Tensor], pro
 
 
 def build_index(level_map: torch.Tensor, prob: Problem, stream=None):
-    """Returns (row_ptr int32 [R*4+1], col_idx int32 [R*NKB] (prefix valid), dev_err int32 [1])."""
+    """Returns (row_ptr int32 [R*5+1]: the CSR offsets [R*4+1] then the attention's dispatch
+    order [R], col_idx int32 [R*NKB] (prefix valid), dev_err int32 [1])."""
     rows = level_map.numel() // prob.n_kblocks
     dev = level_map.device
-    row_ptr = torch.empty(rows * 4 + 1, dtype=torch.int32, device=dev)
+    row_ptr = torch.empty(rows * 5 + 1, dtype=torch.int32, device=dev)
     col_idx = torch.empty(max(rows * prob.n_kblocks, 1), dtype=torch.int32, device=dev)
     dev_err = torch.empty(1, dtype=torch.int32, device=dev)
     _check(lib().psa_build_index(prob.ref(), _ptr(level_map), _ptr(row_ptr), _ptr(col_idx),
