@@ -199,9 +199,10 @@ int psa_mask_assign(const psa_problem* prob, const psa_mask_params* params,
  * Block index: a CSR over (row, level) keys, rows r = (b*heads_q + h)*NQB + qb.
  * row_ptr[R*5+1] int32: col_idx[row_ptr[r*4+l] .. row_ptr[r*4+l+1]) lists, in ascending
  * order, the kb with level_map == l; then row_ptr[R*4+1 + p], p < R, is the row the attention
- * runs in dispatch slot p (a permutation of the rows: slot p runs on XCD p / ceil(R/8), each
- * XCD's contiguous range of rows listed by their count of 64-row tiles, sum over l of
- * ceil(n_l / 2^l), largest first; a stable counting sort over 32 buckets of the range's span of
+ * runs in dispatch slot p (a permutation of the rows: slot p runs on XCD p / ceil(R/8); each
+ * XCD's contiguous range of rows is grouped by KV head, r / (NQB*heads_q/heads_kv), groups in
+ * ascending order, each group listed by its rows' count of 64-row tiles, sum over l of
+ * ceil(n_l / 2^l), largest first; a stable counting sort over 32 buckets of the group's span of
  * counts, exact when that span is at most 32). col_idx needs capacity R*NKB int32; its entries past
  * row_ptr[R*4] are unspecified (the call parks scan partial sums there). Entries outside
  * {-1..3} are treated as skip and set *dev_err (device int32) to PSA_ERR_BAD_LEVEL_MAP;

@@ -180,29 +180,34 @@ def check_map(got: np.ndarray, ref: np.ndarray, marg: np.ndarray, what: str, cer
         assert cert[1] == 0, f"{what}: {cert[1]} flagged rows left uncertified"
 
 
-def dispatch_order(row_ptr, rows):
+def dispatch_order(row_ptr, rows, unit):
     """The attention's dispatch order that psa_build_index writes after the CSR offsets
     (row_ptr[rows*4+1 + p] = the row of dispatch slot p), from its definition: slot p belongs to
-    XCD range p // ceil(rows/8); inside a range the rows are listed by tile count (sum over
-    levels l of ceil(n_l / 2^l)), largest first, stably, over 32 buckets of the range's span of
-    counts. A scheduling choice of the library, not part of the method: no oracle function."""
+    XCD range p // ceil(rows/8); inside a range the rows are grouped by KV head (row // unit,
+    unit = NQB * heads_q / heads_kv), groups ascending, and inside a group listed by tile count
+    (sum over levels l of ceil(n_l / 2^l)), largest first, stably, over 32 buckets of the
+    group's span of counts. A scheduling choice of the library, not part of the method: no
+    oracle function."""
     cnt = np.diff(np.asarray(row_ptr[:rows * 4 + 1], dtype=np.int64)).reshape(rows, 4)
     tiles = sum((cnt[:, l] + (1 << l) - 1) >> l for l in range(4))
     nper = (rows + 7) // 8
     out = np.empty(rows, dtype=np.int64)
     for x in range(8):
         lo, hi = x * nper, min((x + 1) * nper, rows)
-        if lo >= hi:
-            continue
-        t = tiles[lo:hi]
-        bucket = ((t.max() - t) * 32) // (t.max() - t.min() + 1)
-        out[lo:hi] = lo + np.argsort(bucket, kind="stable")
+        g = lo
+        while g < hi:
+            g_hi = min((g // unit + 1) * unit, hi)
+            t = tiles[g:g_hi]
+            bucket = ((t.max() - t) * 32) // (t.max() - t.min() + 1)
+            out[g:g_hi] = g + np.argsort(bucket, kind="stable")
+            g = g_hi
     return out
 
 
-def check_index(row_ptr, col_idx, rp_ref, ci_ref):
+def check_index(row_ptr, col_idx, rp_ref, ci_ref, unit):
     """psa_build_index's output against the oracle's CSR (bit for bit) and the dispatch order
-    against its definition (bit for bit, and a permutation of the rows)."""
+    against its definition (bit for bit, and a permutation of the rows); unit = the rows per KV
+    head (NQB * heads_q / heads_kv)."""
     rp = row_ptr.cpu().numpy() if hasattr(row_ptr, "cpu") else np.asarray(row_ptr)
     rows = (len(rp_ref) - 1) // 4
     assert len(rp) == rows * 5 + 1
@@ -211,4 +216,4 @@ def check_index(row_ptr, col_idx, rp_ref, ci_ref):
     assert np.array_equal(ci[:rp_ref[-1]], ci_ref)
     order = rp[rows * 4 + 1:]
     assert np.array_equal(np.sort(order), np.arange(rows))
-    assert np.array_equal(order, dispatch_order(rp_ref, rows))
+    assert np.array_equal(order, dispatch_order(rp_ref, rows, unit))

@@ -68,7 +68,7 @@ def _run_path(wl, qd, kd, vd):
     rows = lm.numel() // prob.n_kblocks
     rp = row_ptr.cpu().numpy()
     assert np.array_equal(np.sort(rp[rows * 4 + 1:]), np.arange(rows))
-    assert np.array_equal(rp[rows * 4 + 1:], dispatch_order(rp, rows))
+    assert np.array_equal(rp[rows * 4 + 1:], dispatch_order(rp, rows, wl.n_qblocks * wl.group))
     return kp, vp, lm, M, sim, o, lse, cert
 
 

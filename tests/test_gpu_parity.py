@@ -97,7 +97,7 @@ def test_build_index_exact(shape):
     prob = psa.make_problem(q, q, q, block_q=bq)
     row_ptr, col_idx, err = psa.build_index(torch.from_numpy(lm).to(DEV), prob)
     rp_ref, ci_ref = oracle.build_index(lm)
-    check_index(row_ptr, col_idx, rp_ref, ci_ref)
+    check_index(row_ptr, col_idx, rp_ref, ci_ref, nqb)
     assert err.item() == 0
 
 
@@ -127,7 +127,7 @@ def test_build_index_flags_bad_entries():
     assert err.item() == psa.psa.PSA_ERR_BAD_LEVEL_MAP
     clean = np.where((lm < -1) | (lm > 3), -1, lm).astype(np.int8)
     rp_ref, ci_ref = oracle.build_index(clean)
-    check_index(row_ptr, col_idx, rp_ref, ci_ref)
+    check_index(row_ptr, col_idx, rp_ref, ci_ref, 16)
 
 
 def test_attn_reports_bad_level_map():

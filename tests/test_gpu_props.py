@@ -66,7 +66,7 @@ def test_prop_attention_and_index(wl, skip_row):
     lmd = torch.from_numpy(lm).to(DEV)
     row_ptr, col_idx, err = psa.build_index(lmd, prob)
     rp_ref, ci_ref = oracle.build_index(lm)
-    check_index(row_ptr, col_idx, rp_ref, ci_ref)
+    check_index(row_ptr, col_idx, rp_ref, ci_ref, wl.n_qblocks * wl.group)
     assert err.item() == 0
     kp, vp = psa.build_pyramid(kd, vd, prob)
     o, lse = psa.attn_fwd_indexed(qd, kd, vd, kp, vp, row_ptr, col_idx, prob)

@@ -162,11 +162,14 @@ __global__ void __launch_bounds__(256)
 // Dispatch order of the attention workgroups. Workgroup i runs on XCD i % 8, and the attention
 // kernels give XCD x the rows of one contiguous range [x * nper, (x + 1) * nper), nper =
 // ceil(rows / 8), so that neighbouring query blocks of a head share that XCD's L2. Inside a
-// range the rows are listed by their number of 64-row tiles (sum over levels l of
-// ceil(n_l / 2^l)), largest first: the workgroups an XCD starts last are then short ones and its
-// CUs run out of work together (longest-processing-time-first list scheduling). A stable
-// counting sort over kOrderBuckets buckets spanning the range's tile counts (exact for spans up
-// to kOrderBuckets, bucketed beyond); deterministic.
+// range the rows are grouped by KV head (rows / unit, unit = NQB * heads_q / heads_kv: the
+// query heads that read one KV head), groups in ascending order, and inside a group listed by
+// their number of 64-row tiles (sum over levels l of ceil(n_l / 2^l)), largest first. The rows
+// an XCD runs at one time then read one KV head's blocks, mostly the same ones (rows of
+// similar tile counts have similar maps), and the workgroups it starts last are short ones
+// (longest-processing-time-first list scheduling). Each group: a stable counting sort over
+// kOrderBuckets buckets spanning the group's tile counts (exact for spans up to
+// kOrderBuckets, bucketed beyond); deterministic.
 constexpr int kOrderThreads = 256;
 constexpr int kOrderBuckets = 32;
 
@@ -199,7 +202,7 @@ __device__ int order_exclusive_scan(int v, int* wsum) {
 }
 
 __global__ void __launch_bounds__(kOrderThreads)
-    k_index_order(const int32_t* __restrict__ row_ptr, int64_t rows, int64_t nper,
+    k_index_order(const int32_t* __restrict__ row_ptr, int64_t rows, int64_t nper, int64_t unit,
                   int32_t* __restrict__ order) {
     __shared__ int hist[kOrderBuckets * kOrderThreads];   // [bucket][thread]
     __shared__ int wred[2][kOrderThreads / 64];
@@ -209,57 +212,63 @@ __global__ void __launch_bounds__(kOrderThreads)
     const int wave = t >> 6;
     const int64_t lo = static_cast<int64_t>(blockIdx.x) * nper;
     const int64_t hi = lo + nper < rows ? lo + nper : rows;
-    if (lo >= hi) return;   // uniform: an empty range
-    // thread t takes the consecutive rows [s0, s1) of the range
-    const int64_t seg = (hi - lo + kOrderThreads - 1) / kOrderThreads;
-    const int64_t s0 = lo + t * seg < hi ? lo + t * seg : hi;
-    const int64_t s1 = s0 + seg < hi ? s0 + seg : hi;
-    // the span of the tile counts
-    int cmin = 0x7fffffff, cmax = 0;
-    for (int64_t r = s0; r < s1; ++r) {
-        const int c = row_tiles(row_ptr, r);
-        cmin = min(cmin, c);
-        cmax = max(cmax, c);
-    }
+    // the KV-head groups of the range, one after another (uniform loop)
+    for (int64_t g_lo = lo; g_lo < hi;) {
+        const int64_t g_end = (g_lo / unit + 1) * unit;
+        const int64_t g_hi = g_end < hi ? g_end : hi;
+        // thread t takes the consecutive rows [s0, s1) of the group
+        const int64_t seg = (g_hi - g_lo + kOrderThreads - 1) / kOrderThreads;
+        const int64_t s0 = g_lo + t * seg < g_hi ? g_lo + t * seg : g_hi;
+        const int64_t s1 = s0 + seg < g_hi ? s0 + seg : g_hi;
+        // the span of the tile counts
+        int cmin = 0x7fffffff, cmax = 0;
+        for (int64_t r = s0; r < s1; ++r) {
+            const int c = row_tiles(row_ptr, r);
+            cmin = min(cmin, c);
+            cmax = max(cmax, c);
+        }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        cmin = min(cmin, __shfl_xor(cmin, o, 64));
-        cmax = max(cmax, __shfl_xor(cmax, o, 64));
-    }
-    if (lane == 0) {
-        wred[0][wave] = cmin;
-        wred[1][wave] = cmax;
-    }
-    __syncthreads();
+        for (int o = 32; o > 0; o >>= 1) {
+            cmin = min(cmin, __shfl_xor(cmin, o, 64));
+            cmax = max(cmax, __shfl_xor(cmax, o, 64));
+        }
+        if (lane == 0) {
+            wred[0][wave] = cmin;
+            wred[1][wave] = cmax;
+        }
+        __syncthreads();
 #pragma unroll
-    for (int w = 0; w < kOrderThreads / 64; ++w) {
-        cmin = min(cmin, wred[0][w]);
-        cmax = max(cmax, wred[1][w]);
-    }
-    const int span = cmax - cmin + 1;
-    auto bucket = [&](int c) { return static_cast<int>((static_cast<int64_t>(cmax - c) * kOrderBuckets) / span); };
-    // per (bucket, thread) counts, then their exclusive scan in bucket-major order: the first
-    // position of each thread's rows of each bucket (stable: bucket, then thread, then row)
+        for (int w = 0; w < kOrderThreads / 64; ++w) {
+            cmin = min(cmin, wred[0][w]);
+            cmax = max(cmax, wred[1][w]);
+        }
+        const int span = cmax - cmin + 1;
+        auto bucket = [&](int c) { return static_cast<int>((static_cast<int64_t>(cmax - c) * kOrderBuckets) / span); };
+        // per (bucket, thread) counts, then their exclusive scan in bucket-major order: the
+        // first position of each thread's rows of each bucket (stable: bucket, thread, row)
 #pragma unroll
-    for (int b = 0; b < kOrderBuckets; ++b) hist[b * kOrderThreads + t] = 0;
-    for (int64_t r = s0; r < s1; ++r) ++hist[bucket(row_tiles(row_ptr, r)) * kOrderThreads + t];
-    __syncthreads();
-    constexpr int PER = kOrderBuckets;   // entries per thread: kOrderBuckets * kOrderThreads / kOrderThreads
-    int loc = 0;
+        for (int b = 0; b < kOrderBuckets; ++b) hist[b * kOrderThreads + t] = 0;
+        for (int64_t r = s0; r < s1; ++r) ++hist[bucket(row_tiles(row_ptr, r)) * kOrderThreads + t];
+        __syncthreads();
+        constexpr int PER = kOrderBuckets;   // entries per thread
+        int loc = 0;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) loc += hist[t * PER + j];
-    int run = order_exclusive_scan(loc, wsum);
+        for (int j = 0; j < PER; ++j) loc += hist[t * PER + j];
+        int run = order_exclusive_scan(loc, wsum);
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        const int c = hist[t * PER + j];
-        hist[t * PER + j] = run;
-        run += c;
-    }
-    __syncthreads();
-    for (int64_t r = s0; r < s1; ++r) {
-        int* slot = &hist[bucket(row_tiles(row_ptr, r)) * kOrderThreads + t];
-        order[lo + *slot] = static_cast<int32_t>(r);
-        ++*slot;
+        for (int j = 0; j < PER; ++j) {
+            const int c = hist[t * PER + j];
+            hist[t * PER + j] = run;
+            run += c;
+        }
+        __syncthreads();
+        for (int64_t r = s0; r < s1; ++r) {
+            int* slot = &hist[bucket(row_tiles(row_ptr, r)) * kOrderThreads + t];
+            order[g_lo + *slot] = static_cast<int32_t>(r);
+            ++*slot;
+        }
+        __syncthreads();   // hist and wred are reused by the next group
+        g_lo = g_hi;
     }
 }
 
@@ -299,8 +308,9 @@ hipError_t launch_build_index(const Shape& s, const int8_t* level_map, const Ind
     hipLaunchKernelGGL(k_index_fill, dim3(blocks), dim3(256), 0, st, level_map, rows, s.NKB,
                        ib.row_ptr, ib.col_idx);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t unit = static_cast<int64_t>(s.NQB) * (s.H / s.Hkv);   // rows per KV head
     hipLaunchKernelGGL(k_index_order, dim3(8), dim3(kOrderThreads), 0, st, ib.row_ptr, rows, (rows + 7) / 8,
-                       ib.row_ptr + rows * 4 + 1);
+                       unit, ib.row_ptr + rows * 4 + 1);
     return hipGetLastError();
 }
 
