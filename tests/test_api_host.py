@@ -122,9 +122,10 @@ def test_mask_param_checks(kw, status):
 def test_mask_workspace_per_mode():
     """Every scoring mode is accepted and sizes its workspace: the log-masses (scoring rows x
     blocks, float32; for block means also the query and key means), then the certification
-    area: two counters (256 bytes), the flagged-row list and the float64 log-masses of the
-    certifiable rows (all 32 rows of this small problem: scoring rows per query block x
-    blocks x 8 bytes each), plus the float64 similarities when the cosine check is on."""
+    area: the counters (256 bytes), the flagged-row list, the batches of flagged rows (16 int32
+    slots per certifiable row) and the float64 log-masses of the certifiable rows (all 32 rows
+    of this small problem: scoring rows per query block x blocks x 8 bytes each), plus the
+    float64 similarities when the cosine check is on."""
     p = _prob(dtype=P.PSA_BF16)
     L = psa.lib()
     B, H, Hkv, N, D = 1, 2, 2, 1024, 64   # the _prob() shape
@@ -135,7 +136,7 @@ def test_mask_workspace_per_mode():
     for mode in ("sampling", "antidiag", "meankey"):
         mp = psa.MaskParams(mode=mode, samples_per_qblock=8, antidiag_stride=8).c()
         sizes[mode] = L.psa_mask_workspace_bytes(p.ref(), ctypes.byref(mp))
-    cert = lambda rq: 256 + a256(R * 4) + R * rq * nkb * 8  # noqa: E731
+    cert = lambda rq: 256 + a256(R * 4) + a256(R * 16 * 4) + R * rq * nkb * 8  # noqa: E731
     assert sizes["sampling"] == a256(B * H * nkb * nqb * 8 * 4) + cert(8)
     assert sizes["antidiag"] == a256(B * H * nkb * (N // 8) * 4) + cert(64 // 8)
     assert sizes["meankey"] >= B * H * nkb * nqb * 4 + B * H * nqb * D * 4 + B * Hkv * nkb * D * 4 + cert(1)

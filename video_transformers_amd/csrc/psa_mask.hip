@@ -941,6 +941,221 @@ __global__ void __launch_bounds__(256) k_cert_sampling(CertArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Sampling mode on float64 MFMA (v_mfma_f64_16x16x4_f64): the flagged rows are first grouped
+// by KV head into batches of 16 / S rows (k_cert_batches), so that the 16 MFMA rows hold the
+// S sampled queries of every row of a batch and one K read serves them all. Operand layouts
+// of the instruction (16x16x4, one double per lane): A[i][k] in lane i + 16k, B[k][j] in lane
+// j + 16k; the result D[4r + (l >> 4)][l & 15] in lane l, register r. The contraction index
+// k of k-step ks maps to head dimension (D / 4) * k + ks, so a lane's operands are D / 4
+// consecutive dimensions of one query (A) or one key (B).
+// ---------------------------------------------------------------------------------------
+constexpr int kBatchThreads = 1024;
+constexpr int kBatchSortMax = 16384;   // flagged rows sorted in LDS; beyond, one row per batch
+
+struct BatchArgs {
+    int* cert;         // cert[0] flagged rows, cert[2] <- batches
+    const int* rows;   // [cap] the flagged rows, in the order they were flagged
+    int* bat;          // [cap][16] slots of each batch (-1: none)
+    int cap, unit, BR; // unit: rows per KV head (NQB * heads_q / heads_kv); BR: rows per batch
+};
+
+// exclusive sum over the workgroup of one value per thread (kBatchThreads threads)
+__device__ int batch_exclusive_sum(int v, int* wsum) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    __syncthreads();
+    return before + x - v;
+}
+
+__global__ void __launch_bounds__(kBatchThreads) k_cert_batches(BatchArgs b) {
+    extern __shared__ uint64_t skeys[];   // (KV head << 32) | slot, sorted
+    __shared__ int wsum[kBatchThreads / 64];
+    const int tid = threadIdx.x;
+    const int n = min(b.cert[0], b.cap);
+    if (n > kBatchSortMax) {   // (uniform) no grouping: one row per batch
+        for (int i = tid; i < n; i += kBatchThreads)
+            for (int j = 0; j < 16; ++j) b.bat[i * 16 + j] = j == 0 ? i : -1;
+        if (tid == 0) b.cert[2] = n;
+        return;
+    }
+    int P = 1;
+    while (P < n) P <<= 1;
+    for (int i = tid; i < P; i += kBatchThreads)
+        skeys[i] = i < n ? (static_cast<uint64_t>(b.rows[i] / b.unit) << 32) | static_cast<uint32_t>(i) : ~0ull;
+    __syncthreads();
+    // bitonic sort, ascending
+    for (int size = 2; size <= P; size <<= 1)
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = tid; i < P; i += kBatchThreads) {
+                const int jx = i ^ stride;
+                if (jx > i) {
+                    const bool up = (i & size) == 0;
+                    const uint64_t x = skeys[i], y = skeys[jx];
+                    if ((x > y) == up) {
+                        skeys[i] = y;
+                        skeys[jx] = x;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    // batch heads: every BR-th position of each KV head's run (the run's start by binary search)
+    constexpr int PER = kBatchSortMax / kBatchThreads;
+    int head[PER];
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        const int p = tid * PER + e;
+        head[e] = 0;
+        if (p < n) {
+            const uint32_t key = static_cast<uint32_t>(skeys[p] >> 32);
+            int lo = 0, hi = p;   // first position with this key
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (static_cast<uint32_t>(skeys[mid] >> 32) < key) lo = mid + 1; else hi = mid;
+            }
+            head[e] = (p - lo) % b.BR == 0;
+            cnt += head[e];
+        }
+    }
+    int bidx = batch_exclusive_sum(cnt, wsum);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+        const int p = tid * PER + e;
+        if (head[e]) {
+            const uint32_t key = static_cast<uint32_t>(skeys[p] >> 32);
+            for (int j = 0; j < 16; ++j) {
+                const int q = p + j;
+                const bool in = j < b.BR && q < n && static_cast<uint32_t>(skeys[q] >> 32) == key;
+                b.bat[bidx * 16 + j] = in ? static_cast<int>(skeys[q] & 0xffffffffu) : -1;
+            }
+            ++bidx;
+        }
+    }
+    if (tid == kBatchThreads - 1) b.cert[2] = bidx;   // the last thread ends past every head
+}
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// items (batch, 4 KV blocks); wave w of the workgroup takes KV block 4 * (item % ceil(NKB/4)) + w:
+// 4 column tiles of 16 keys, D / 4 k-steps each, then per sampled query the block's log-mass.
+template <int D, int S>
+__global__ void __launch_bounds__(256) k_cert_sampling_mfma(CertArgs a, const int* bat) {
+    constexpr int BR = 16 / S;
+    constexpr int KST = D / 4;   // k-steps; a lane's D / 4 consecutive dimensions
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    const int j = lane & 15;
+    const int nb = a.cert[2];
+    const int nkb4 = (a.NKB + 3) / 4;
+    const int64_t items = static_cast<int64_t>(nb) * nkb4;
+    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+        const int batch = static_cast<int>(it / nkb4);
+        const int kb = static_cast<int>(it % nkb4) * 4 + wave;
+        if (kb >= a.NKB) continue;   // wave-uniform
+        const int* bs = bat + static_cast<int64_t>(batch) * 16;
+        const RowIds r0 = row_ids(a.rows[bs[0]], a.NQB, a.H, a.Hkv);   // the batch's KV head
+        // A operand: sampled query j (batch row j / S, sample j % S), dimensions g*KST ...
+        double av[KST];
+        {
+            const int slot = bs[j / S];
+            const int si = j % S;
+            bool ok = slot >= 0 && j / S < BR;
+            int qrow = 0;
+            const bf16_bits* qh = a.q;
+            if (ok) {
+                const RowIds r = row_ids(a.rows[slot], a.NQB, a.H, a.Hkv);
+                const int rv = min(max(a.Nv - r.qb * a.BQ, 0), a.BQ);
+                ok = rv > 0;
+                qrow = r.qb * a.BQ + (si * rv) / S;
+                qh = a.q + r.b * a.qs0 + r.h * a.qs1 + static_cast<int64_t>(qrow) * a.qs2 + g * KST;
+            }
+#pragma unroll
+            for (int c = 0; c < KST / 8; ++c) {
+                u32x4 w = u32x4{0u, 0u, 0u, 0u};
+                if (ok) w = *reinterpret_cast<const u32x4*>(qh + 8 * c);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    av[8 * c + 2 * x] = static_cast<double>(__uint_as_float(w[x] << 16));
+                    av[8 * c + 2 * x + 1] = static_cast<double>(__uint_as_float(w[x] & 0xffff0000u));
+                }
+            }
+        }
+        // the sampled queries of this lane's results: m = 4 rr + g
+        int mslot[4], msi[4], mqrow[4];
+        bool mok[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int m = 4 * rr + g;
+            mslot[rr] = bs[m / S];
+            msi[rr] = m % S;
+            mok[rr] = false;
+            mqrow[rr] = 0;
+            if (mslot[rr] >= 0) {
+                const RowIds r = row_ids(a.rows[mslot[rr]], a.NQB, a.H, a.Hkv);
+                const int rv = min(max(a.Nv - r.qb * a.BQ, 0), a.BQ);
+                mok[rr] = rv > 0;
+                mqrow[rr] = r.qb * a.BQ + (msi[rr] * rv) / S;
+            }
+        }
+        const bf16_bits* kh = a.k + r0.b * a.ks0 + r0.hk * a.ks1 + g * KST;
+        double mx[4], zt[4][4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) mx[rr] = -INFINITY;
+#pragma unroll
+        for (int tile = 0; tile < 4; ++tile) {
+            const int t = kb * 64 + tile * 16 + j;   // this lane's key (B operand and results)
+            u32x4 kw[KST / 8];
+#pragma unroll
+            for (int c = 0; c < KST / 8; ++c) {
+                kw[c] = u32x4{0u, 0u, 0u, 0u};
+                if (t < a.Nv) kw[c] = *reinterpret_cast<const u32x4*>(kh + static_cast<int64_t>(t) * a.ks2 + 8 * c);
+            }
+            f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+            for (int ks = 0; ks < KST; ++ks) {
+                const uint32_t w = kw[ks / 8][(ks % 8) / 2];
+                const double bv = static_cast<double>(__uint_as_float((ks & 1) ? (w & 0xffff0000u) : (w << 16)));
+                acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av[ks], bv, acc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const bool vis = mok[rr] && t < a.Nv && (!a.causal || t <= mqrow[rr]);
+                zt[rr][tile] = vis ? acc[rr] * a.scale : -INFINITY;
+                mx[rr] = fmax(mx[rr], zt[rr][tile]);
+            }
+        }
+        // each sampled query's log-mass on the block: logsumexp over 4 tiles x 16 lanes
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            double m = mx[rr];
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) m = fmax(m, __shfl_xor(m, o, 64));
+            double e = 0.0;
+            if (m != -INFINITY)
+#pragma unroll
+                for (int tile = 0; tile < 4; ++tile) e += exp(zt[rr][tile] - m);
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) e += __shfl_xor(e, o, 64);
+            const double L = m == -INFINITY ? -INFINITY : m + log(e);
+            if (j == 0 && mslot[rr] >= 0)
+                a.Lg[(static_cast<int64_t>(mslot[rr]) * a.RQ + msi[rr]) * a.NKB + kb] = L;
+        }
+    }
+}
+
 // Antidiagonal mode, stride S: items (flagged row, chunk of 512 compressed columns); thread =
 // columns c and c + 256, every compressed row i < RQ of the query block against each: the
 // float64 sum over t < S of q[(qb*RQ + i)*S + S-1-t] . k[c*S + t]. The query block's rows sit
@@ -1119,8 +1334,9 @@ struct ScoreGeom {
     int S, rows_per_head, RQ, rows_per_wg, wg_per_head, ntiles, nsplit, tiles_per_split;
     size_t ws_bytes;
     size_t qbar_off = 0, kbar_off = 0;   // block-mean mode: offsets of the means in the workspace
-    // certification: counters, flagged row list, float64 similarities, float64 log-masses
-    size_t cert_off = 0, rows_off = 0, sim64_off = 0, lg_off = 0;
+    // certification: counters, flagged row list, batches (16 slots each), float64
+    // similarities, float64 log-masses
+    size_t cert_off = 0, rows_off = 0, bat_off = 0, sim64_off = 0, lg_off = 0;
     int cap = 0;
 };
 
@@ -1143,6 +1359,8 @@ ScoreGeom score_geom(const Shape& s, const psa_mask_params& mp) {
     off += 256;
     g.rows_off = off;
     off = align256(off + static_cast<size_t>(g.cap) * sizeof(int));
+    g.bat_off = off;
+    off = align256(off + static_cast<size_t>(g.cap) * 16 * sizeof(int));
     g.sim64_off = off;
     if (mp.cos_sim_min > 0.f) off = align256(off + static_cast<size_t>(s.B) * s.Hkv * s.NKB * sizeof(double));
     g.lg_off = off;
@@ -1393,7 +1611,35 @@ hipError_t launch_mask_certify(const Shape& s, const psa_mask_params& mp, const 
     const int D = s.D;
 #define PSA_CERT_SAMP(DD, SS) hipLaunchKernelGGL((k_cert_sampling<DD, SS>), dim3(score_grid), dim3(256), 0, st, c)
 #define PSA_CERT_AD(DD, SS, RR) hipLaunchKernelGGL((k_cert_antidiag<DD, SS, RR>), dim3(score_grid), dim3(256), 0, st, c)
-    if (sampling) {
+    if (sampling && g.S <= 16) {
+        // group the flagged rows by KV head into batches, then rescore on float64 MFMA
+        BatchArgs b;
+        b.cert = reinterpret_cast<int*>(ws + g.cert_off);
+        b.rows = c.rows;
+        b.bat = reinterpret_cast<int*>(ws + g.bat_off);
+        b.cap = c.cap;
+        b.unit = s.NQB * (s.H / s.Hkv);
+        b.BR = 16 / g.S;
+        int P = 1;
+        while (P < std::min(c.cap, kBatchSortMax)) P <<= 1;
+        hipLaunchKernelGGL(k_cert_batches, dim3(1), dim3(kBatchThreads), static_cast<size_t>(P) * sizeof(uint64_t),
+                           st, b);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        const int nkb4 = (s.NKB + 3) / 4;
+        const unsigned grid = static_cast<unsigned>(
+            std::min<int64_t>(4096, std::max<int64_t>(1, static_cast<int64_t>(c.cap) * nkb4)));
+        const int* bat = b.bat;
+#define PSA_CERT_SM(DD, SS) hipLaunchKernelGGL((k_cert_sampling_mfma<DD, SS>), dim3(grid), dim3(256), 0, st, c, bat)
+        switch (g.S) {
+            case 1: if (D == 128) PSA_CERT_SM(128, 1); else PSA_CERT_SM(64, 1); break;
+            case 2: if (D == 128) PSA_CERT_SM(128, 2); else PSA_CERT_SM(64, 2); break;
+            case 4: if (D == 128) PSA_CERT_SM(128, 4); else PSA_CERT_SM(64, 4); break;
+            case 8: if (D == 128) PSA_CERT_SM(128, 8); else PSA_CERT_SM(64, 8); break;
+            case 16: if (D == 128) PSA_CERT_SM(128, 16); else PSA_CERT_SM(64, 16); break;
+            default: return hipErrorNotSupported;
+        }
+#undef PSA_CERT_SM
+    } else if (sampling) {
         switch (g.S) {
             case 1: if (D == 128) PSA_CERT_SAMP(128, 1); else PSA_CERT_SAMP(64, 1); break;
             case 2: if (D == 128) PSA_CERT_SAMP(128, 2); else PSA_CERT_SAMP(64, 2); break;
