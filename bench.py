@@ -47,6 +47,17 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, GB/s
 METRIC = "psa_attn_fwd ms/layer + effective TFLOP/s (% bf16 MFMA peak), Wan-like 32k"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_attn_fwd_bf16_traffic.txt")
 ATTN_SOURCE = os.path.join(ROOT, "video_transformers_amd", "csrc", "psa_attn_bf16.hip")
+# the attention's traffic also depends on the dispatch order the index builder writes
+INDEX_SOURCE = os.path.join(ROOT, "video_transformers_amd", "csrc", "psa_index.hip")
+
+
+def attn_sources_sha256() -> str:
+    """sha256 over the attention kernel source and the index builder source, in that order:
+    the counter summaries under profiles/ hold for this pair only."""
+    h = hashlib.sha256()
+    for path in (ATTN_SOURCE, INDEX_SOURCE):
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
 
 
 # ---------------------------------------------------------------------------------------
@@ -166,8 +177,8 @@ def _traffic_from_profile(workload: str):
         if ":" in line and not line.lstrip().startswith("#"):
             key, val = line.split(":", 1)
             kv[key.strip()] = val.strip()
-    sha = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
-    if kv.get("attn_source_sha256") != sha or kv.get("workload") != workload:
+    sha = attn_sources_sha256()
+    if kv.get("sources_sha256") != sha or kv.get("workload") != workload:
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -185,9 +196,9 @@ def _attn_counters(workload: str):
     differs."""
     if workload != "wan2.1-1.3b_32k" or not os.path.exists(COUNTERS_FILE):
         return None
-    sha = hashlib.sha256(open(ATTN_SOURCE, "rb").read()).hexdigest()
+    sha = attn_sources_sha256()
     text = open(COUNTERS_FILE).read()
-    if f"sha256: {sha}" not in text:
+    if f"sources sha256: {sha}" not in text:
         return None
     out, cur = {}, None
     for line in text.splitlines():
@@ -356,6 +367,13 @@ def run(args) -> dict:
                                           ptr(kp), ptr(vp), ptr(row_ptr), ptr(col_idx), ptr(o),
                                           ptr(lse), st), "attn unpacked")
         unpacked_ms = _timed_back_to_back(unpacked, stream, reps=4, warm=1)
+    sustained = None
+    if not args.no_sustained:
+        def attn_call():
+            check(L.psa_attn_fwd_indexed(prob.ref(), ctypes.c_float(0.0), ptr(q), ptr(k), ptr(v),
+                                         ptr(kp), ptr(vp), ptr(row_ptr), ptr(col_idx), ptr(o),
+                                         ptr(lse), st), "attn sustained")
+        sustained = _sustained_attention(attn_call, stream, flops)
     meankey = None
     if (not args.no_meankey and computed_map and wl.dtype == "bf16" and wl.block_q == 128
             and nkb <= 1792):
@@ -375,6 +393,8 @@ def run(args) -> dict:
         # every workload's attention kernel, driver-observed in this same line (the step
         # above is the metric's workload; these are reported beside it)
         out["workloads"] = {w.name: _workload_attention(w, dev) for w in W.ALL}
+    if sustained is not None:
+        out["attn"]["sustained"] = sustained
     out["attn"]["unpacked_same_map_ms"] = None if unpacked_ms != unpacked_ms else round(unpacked_ms, 3)
     out["attn"]["speedup_vs_unpacked"] = (None if unpacked_ms != unpacked_ms
                                           else round(unpacked_ms / attn_ms_mean, 2))
@@ -443,6 +463,64 @@ def _workload_attention(wl, dev, reps: int = 10) -> dict:
                     f"d{d} {wl.dtype} block_q {wl.block_q}{' causal' if wl.causal else ''}"}
     del q, k, v, kp, vp, lm, rp, ci, o, lse
     torch.cuda.empty_cache()
+    return out
+
+
+def _smi_sample() -> dict:
+    """Graphics clocks (MHz, one per XCD) and socket power (W) as amd-smi reports them now, or
+    an empty dict when amd-smi is not installed or its output is not understood."""
+    import re
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-c", "-p"], capture_output=True, text=True, timeout=15)
+    except (OSError, subprocess.SubprocessError):
+        return {}
+    clks = [int(x) for x in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", r.stdout)]
+    pw = re.findall(r"SOCKET_POWER:\s*(\d+)", r.stdout)
+    out = {}
+    if clks:
+        out["gfx_clock_mhz"] = {"min": min(clks), "mean": round(sum(clks) / len(clks)), "max": max(clks)}
+    if pw:
+        out["socket_power_w"] = int(pw[0])
+    return out
+
+
+def _sustained_attention(fn, stream, flops: float, seconds: float = 3.0) -> dict:
+    """The attention call back to back for about `seconds` (long enough for the GPU to settle
+    at its power limit, as in a model's layer loop), timed over the last third in batches of
+    20 calls bracketed by HIP events on the launch stream; clocks and power sampled once in
+    that last third."""
+    import threading
+    import time
+
+    import torch
+    t0 = time.time()
+    smi = {}
+    sampler = None
+    times = []
+    while True:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(20):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        el = time.time() - t0
+        if el > seconds * 2 / 3:
+            times.append(ev[0].elapsed_time(ev[1]) / 20)
+            if sampler is None:
+                sampler = threading.Thread(target=lambda: smi.update(_smi_sample()))
+                sampler.start()
+        if el > seconds and sampler is not None and not sampler.is_alive():
+            break
+        if el > 4 * seconds:
+            break
+    ms = sorted(times)[len(times) // 2]
+    out = {"ms_per_layer_median": round(ms, 4), "tflops_executed": round(flops / (ms * 1e-3) / 1e12, 2),
+           "pct_bf16_peak": round(100 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+           "calls_timed": 20 * len(times),
+           "note": "back-to-back calls for about 3 s; the median batch of the last third"}
+    out.update(smi)
     return out
 
 
@@ -656,6 +734,11 @@ def _report(args, wl, flops, pairs, dpairs, frac, d, B, H, N, computed_map, attn
                 "executed_over_issued": round(flops / issued, 4),
                 "source": os.path.relpath(COUNTERS_FILE, ROOT) + " (SQ_VALU_MFMA_BUSY_CYCLES, "
                           "SQ_INSTS_MFMA; this run's kernel time; 1024 SIMDs at 2.4 GHz)"}
+        if "GRBM_GUI_ACTIVE" in ctr:
+            # the same busy cycles against the cycles the GPU was active in the profiled
+            # launches at the clock it actually ran (GRBM_GUI_ACTIVE sums the 8 XCDs)
+            active = ctr["GRBM_GUI_ACTIVE"] / 8
+            mfma["busy_pct_of_active_cycles"] = round(100 * ctr["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * active), 1)
     out = {
         "metric": METRIC,
         "value": round(flops / (ms_per_step * 1e-3) / 1e12, 3),
@@ -706,6 +789,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-sustained", action="store_true",
+                    help="skip the sustained (power-limited) attention measurement")
     ap.add_argument("--workload", default=W.WAN13B_32K.name, choices=sorted(W.BY_NAME))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true",

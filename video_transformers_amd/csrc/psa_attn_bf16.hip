@@ -628,15 +628,21 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
         __syncthreads();
     };
     // exp chunk c (of KK) of the P fragments of sacc[H]: 8 / KK * 4 ... pairs of keys
-    auto exp_chunk = [&](auto H, int c, float off, uint32_t (&pk)[8]) {
+    constexpr int PAIRS = 8 / KK;   // key pairs per chunk (1 for D = 128, 2 for D = 64)
+    auto exp_a = [&](auto H, int c, float off, float (&ef)[2 * PAIRS]) {
         constexpr int hh = decltype(H)::value;
-        constexpr int PAIRS = 8 / KK;   // key pairs per chunk (1 for D = 128, 2 for D = 64)
 #pragma unroll
         for (int q = 0; q < PAIRS; ++q) {
-            const int pr = c * PAIRS + q;   // pair 0..7: fragment pr / 4, dword pr % 4
-            const float p0 = fast_exp2(fmaf(sacc[hh][2 * pr], cs, off));
-            const float p1 = fast_exp2(fmaf(sacc[hh][2 * pr + 1], cs, off));
-            pk[pr] = pack_bf16x2(p0, p1);
+            const int pr = c * PAIRS + q;
+            ef[2 * q] = fast_exp2(fmaf(sacc[hh][2 * pr], cs, off));
+            ef[2 * q + 1] = fast_exp2(fmaf(sacc[hh][2 * pr + 1], cs, off));
+        }
+    };
+    auto exp_b = [&](int c, const float (&ef)[2 * PAIRS], uint32_t (&pk)[8]) {
+#pragma unroll
+        for (int q = 0; q < PAIRS; ++q) {
+            const int pr = c * PAIRS + q;
+            pk[pr] = pack_bf16x2(ef[2 * q], ef[2 * q + 1]);
             if (pr & 1)
                 psum1 = add_bf16x2(pk[pr], psum1);
             else
@@ -654,7 +660,11 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
         return va.v;
     };
     // One pipeline step of KK slots, in a fixed issue order (a scheduling barrier after each
-    // MFMA):
+    // MFMA). The exp work is software-pipelined: slot kk issues the fma and exp2 of chunk kk and
+    // the bf16 packing and row sums of chunk kk-1, whose exp2 results arrived meanwhile. The
+    // wave raises its issue priority for the MFMA-dense second half of the step (S and O
+    // MFMAs per slot) and drops it for the exp-heavy first half, so that the two waves sharing
+    // a SIMD tend to alternate between the two kinds of work.
     //   S(h) MFMAs: bf16 one per slot, K reads three MFMAs ahead; fp8 one per KSL slots, K
     //   reads all at the start. In each slot 1/KK of the exp work of the previous half
     //   (sacc[H^1], level lvl_p); from slot KK/2 on, the O MFMAs of its first 16 keys; then the
@@ -666,6 +676,7 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
         const float off = exp_off(lvl_p);
         const uint32_t koff = kbuf + hh * 32 * RBK;   // an immediate: no carry into the XORed bits
         uint32_t pk[8];
+        float ef[2][2 * PAIRS];   // exp results of chunks kk and kk - 1
         KOp kr[KS];
         bf16x8 vr0[DB], vr1[DB];
         __builtin_amdgcn_sched_barrier(0);
@@ -679,11 +690,14 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
             if (kk == 0)
 #pragma unroll
                 for (int d = 0; d < DB; ++d) vr0[d] = read_v(vslot, 0, d);
-            if (kk == KK / 2)
+            if (kk == KK / 2) {
+                __builtin_amdgcn_s_setprio(1);
 #pragma unroll
                 for (int d = 0; d < DB; ++d) vr1[d] = read_v(vslot, 1, d);
+            }
             if (kk % KSL == 0) sacc[hh] = mfma_s(kr[kk / KSL], kk / KSL, sacc[hh]);
-            exp_chunk(IC<hh ^ 1>{}, kk, off, pk);
+            if (kk > 0) exp_b(kk - 1, ef[(kk - 1) & 1], pk);
+            exp_a(IC<hh ^ 1>{}, kk, off, ef[kk & 1]);
             dma(kk);   // the next tiles' direct loads ride along with the MFMAs
             if (kk >= KK / 2) {
                 const int d = kk - KK / 2;
@@ -692,6 +706,7 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        exp_b(KK - 1, ef[(KK - 1) & 1], pk);
         float x0 = -INFINITY, x1 = -INFINITY;
 #pragma unroll
         for (int d = 0; d < DB; ++d) {
@@ -708,6 +723,7 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+        __builtin_amdgcn_s_setprio(0);
         return half_max(x0, x1, lvl_h);
     };
     // step, then (tiles that need it) the mask and the max again, then the lazy max update
