@@ -15,7 +15,8 @@
 //  k_bwd_dq      one workgroup per (batch, head, query block) row, walking the row's block
 //                index in packed tiles like the forward: S^T = Kbar Q^T, dP^T = Vbar dO^T,
 //                dQ^T += Kbar^T dS^T. 32 queries per wave; each wave owns its queries' dq.
-//  k_bwd_dkv     one workgroup per (batch, KV head, level, 64-row pooled tile): scans the
+//  k_bwd_dkv     one workgroup per (batch, KV head, level, 64-row pooled tile; the tiles are
+//                claimed per XCD range with spill-over to the next ranges): scans the
 //                level map for the (query head, query block) rows that list one of the
 //                tile's blocks at that level (ordered, so the sums are deterministic), then
 //                per listed row and 64-query chunk: S = Q Kbar^T, dP = dO Vbar^T,
@@ -63,6 +64,7 @@ struct BwdArgs {
     bf16_bits* dq;
     bf16_bits* dk;
     bf16_bits* dv;
+    int* claim;    // [8] next unclaimed pooled tile of each XCD's range (k_bwd_dkv), zeroed per call
     int B, H, Hkv, N, Nv, NQB, NKB, BQ, causal;
     int64_t qs0, qs1, qs2, ks0, ks1, ks2, vs0, vs1, vs2, os0, os1, os2;
     int64_t pooled_rows;   // 7N/8
@@ -204,9 +206,12 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_bwd_dq(BwdArgs a, int total_rows)
     const int l32 = lane & 31;
     const int hi = lane >> 5;
 
+    // XCD-aware row order: XCD x = i % 8 takes a contiguous range of rows in the index's
+    // dispatch order (grouped by KV head, largest first), as the forward does
     const int nper = (total_rows + 7) >> 3;
-    const int row = (blockIdx.x & 7) * nper + (blockIdx.x >> 3);
-    if (row >= total_rows) return;
+    const int slot = (blockIdx.x & 7) * nper + (blockIdx.x >> 3);
+    if (slot >= total_rows) return;
+    const int row = a.row_ptr[static_cast<int64_t>(total_rows) * 4 + 1 + slot];
     const int qb = row % a.NQB;
     const int bh = row / a.NQB;
     const int h = bh % a.H;
@@ -389,9 +394,29 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a, int total_tiles, 
     const int kh = pw & 1;
     const int qh = pw >> 1;
 
+    // Tile claim. Workgroup i runs on XCD x = i % 8; it takes the next unclaimed tile of XCD
+    // x's contiguous range of tiles (neighbouring tiles of a KV head share that XCD's L2) and,
+    // once that range is exhausted, the next tile of the first following range that has one
+    // left, so an XCD whose tiles happen to be cheap takes over tiles of a busier one. The
+    // grid has one workgroup per tile: every claim succeeds and every tile is processed once.
+    // (The tiles are independent, so the assignment does not change any result.)
     const int nper = (total_tiles + 7) >> 3;
-    const int tile = (blockIdx.x & 7) * nper + (blockIdx.x >> 3);
-    if (tile >= total_tiles) return;
+    __shared__ int claimed;
+    if (tid == 0) {
+        int t = -1;
+        for (int d = 0; d < 8 && t < 0; ++d) {
+            const int x = (static_cast<int>(blockIdx.x & 7) + d) & 7;
+            const int lo = x * nper;
+            const int hi = min(lo + nper, total_tiles);
+            if (lo >= hi) continue;
+            const int c = atomicAdd(&a.claim[x], 1);
+            if (lo + c < hi) t = lo + c;
+        }
+        claimed = t;
+    }
+    __syncthreads();
+    const int tile = claimed;
+    if (tile < 0) return;
     const int bhk = tile / tiles_per_bh;
     int m = tile % tiles_per_bh;
     const int l = m < t1 ? 0 : m < t2 ? 1 : m < t3 ? 2 : 3;
@@ -707,8 +732,10 @@ __global__ void __launch_bounds__(256) k_bwd_pool(BwdArgs a) {
 template <int D>
 hipError_t launch_d(const Shape& s, const BwdArgs& a, hipStream_t st) {
     const int64_t rows = static_cast<int64_t>(s.B) * s.H * s.N;
+    hipError_t e = launch_clear_i32(a.claim, 8, st);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_bwd_rowdot<D>, dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(256), 0, st, a);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
 
     const int qrows = s.B * s.H * s.NQB;
@@ -726,9 +753,8 @@ hipError_t launch_d(const Shape& s, const BwdArgs& a, hipStream_t st) {
     for (int l = 0; l < 4; ++l) tl[l] = ((s.N >> l) + 63) / 64;
     const int tiles_per_bh = tl[0] + tl[1] + tl[2] + tl[3];
     const int tiles = s.B * s.Hkv * tiles_per_bh;
-    const int nt = (tiles + 7) / 8;
     const size_t edyn = static_cast<size_t>(s.H / s.Hkv) * s.NQB * sizeof(int);
-    hipLaunchKernelGGL(k_bwd_dkv<D>, dim3(8 * nt), dim3(512), edyn, st, a, tiles, tiles_per_bh,
+    hipLaunchKernelGGL(k_bwd_dkv<D>, dim3(tiles), dim3(512), edyn, st, a, tiles, tiles_per_bh,
                        tl[0], tl[0] + tl[1], tl[0] + tl[1] + tl[2]);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -743,7 +769,7 @@ hipError_t launch_d(const Shape& s, const BwdArgs& a, hipStream_t st) {
 size_t attn_bwd_scratch_bytes(const Shape& s) {
     const size_t rows = static_cast<size_t>(s.B) * s.H * s.N;
     const size_t grows = static_cast<size_t>(s.B) * s.Hkv * (static_cast<size_t>(s.N) + s.pooled_rows);
-    return 2 * rows * sizeof(float) + 2 * grows * s.D * sizeof(float);
+    return 2 * rows * sizeof(float) + 2 * grows * s.D * sizeof(float) + 8 * sizeof(int);
 }
 
 hipError_t launch_attn_bwd(const Shape& s, float scale, const void* q, const void* k,
@@ -771,6 +797,7 @@ hipError_t launch_attn_bwd(const Shape& s, float scale, const void* q, const voi
     a.dd = f + rows;
     a.gk = f + 2 * rows;
     a.gv = a.gk + grows * s.D;
+    a.claim = reinterpret_cast<int*>(a.gv + grows * s.D);
     a.dq = static_cast<bf16_bits*>(dq);
     a.dk = static_cast<bf16_bits*>(dk);
     a.dv = static_cast<bf16_bits*>(dv);
