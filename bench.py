@@ -405,8 +405,8 @@ def _workload_attention(wl, dev, reps: int = 10) -> dict:
     """One workload's attention on its own map (psa_mask, or the drawn map), inputs resident:
     mean of `reps` back-to-back psa_attn_fwd_indexed calls after two untimed ones (sustained
     attention load, unlike the step, where the pyramid and the mask run between attention
-    calls), executed level-weighted FLOP over that time, and the pyramid and psa_mask calls
-    timed once each (the first calls of the process)."""
+    calls), executed level-weighted FLOP over that time, and the pyramid, psa_mask and
+    psa_build_index calls, each the mean of 5 back-to-back calls after its first."""
     import ctypes
     import torch
     import video_transformers_amd as psa
@@ -418,10 +418,9 @@ def _workload_attention(wl, dev, reps: int = 10) -> dict:
     prob = psa.make_problem(q, k, v, block_q=wl.block_q, block_k=wl.block_k, causal=wl.causal,
                             seq_valid=wl.seq_valid)
     drawn = None if wl.map_source == "mask" else torch.from_numpy(W.make_map(wl)).to(dev)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    ev[0].record(stream)
     kp, vp = psa.build_pyramid(k, v, prob)
-    ev[1].record(stream)
+    pyramid_ms = _timed_back_to_back(lambda: psa.build_pyramid(k, v, prob), stream, reps=5, warm=0)
+    mask_ms = None
     if wl.map_source == "mask":
         params = psa.MaskParams(mode=wl.mask_mode, thresholds=tuple(wl.thresholds),
                                 samples_per_qblock=wl.samples_per_qblock,
@@ -429,11 +428,11 @@ def _workload_attention(wl, dev, reps: int = 10) -> dict:
                                 force_diag_l0=wl.force_diag_l0, force_l0_begin=wl.text_begin,
                                 force_l0_end=wl.text_end)
         lm, _, _ = psa.mask(q, k, prob, params)
+        mask_ms = _timed_back_to_back(lambda: psa.mask(q, k, prob, params), stream, reps=5, warm=0)
     else:
         lm = drawn
-    ev[2].record(stream)
     rp, ci, err = psa.build_index(lm, prob)
-    ev[3].record(stream)
+    index_ms = _timed_back_to_back(lambda: psa.build_index(lm, prob), stream, reps=5, warm=0)
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
 
@@ -456,8 +455,9 @@ def _workload_attention(wl, dev, reps: int = 10) -> dict:
            "peak": f"{'bf16' if wl.dtype == 'bf16' else 'fp32'} MFMA {peak:.1f} TFLOP/s",
            "executed_pairs": int(pairs),
            "effective_sparsity": round(1.0 - pairs / dense_pairs(wl), 4),
-           "pyramid_ms": round(ev[0].elapsed_time(ev[1]), 4),
-           "mask_ms": (round(ev[1].elapsed_time(ev[2]), 4) if wl.map_source == "mask" else None),
+           "pyramid_ms": round(pyramid_ms, 4),
+           "mask_ms": None if mask_ms is None else round(mask_ms, 4),
+           "index_ms": round(index_ms, 4),
            "map": (f"psa_mask {wl.mask_mode}" if wl.map_source == "mask" else f"drawn ({wl.map_source})"),
            "shape": f"B{wl.batch} H{wl.heads_q}/{wl.heads_kv} N{wl.seq_len} (valid {wl.seq_valid}) "
                     f"d{d} {wl.dtype} block_q {wl.block_q}{' causal' if wl.causal else ''}"}

@@ -380,3 +380,83 @@ def test_mask_parity(wl):
         print(f"[{wl.name}] sim max abs diff {ds.max():.3e}", flush=True)
         assert ds.max() <= 1e-6
     check_map(lm.cpu().numpy(), lm_ref, oracle_margin_entries(M_ref, sim_ref, p, a), wl.name, cert)
+
+
+# ---------------------------------------------------------------------------------------
+# float64 certification of near-threshold rows, forced
+# ---------------------------------------------------------------------------------------
+def _prefix_sums(Mr, last):
+    """Exclusive cumulative masses of one row in the assignment's order (mass descending, ties
+    by block index)."""
+    order = sorted(range(last + 1), key=lambda kb: (-float(Mr[kb]), kb))
+    return np.cumsum([0.0] + [float(Mr[kb]) for kb in order])[:-1]
+
+
+def _near_thresholds(rows_c, delta):
+    """Four increasing thresholds, the l-th `delta` above an exclusive cumulative mass in the
+    l-th quarter of (0.3, 0.97) of row l of `rows_c` (else of row 0)."""
+    edges = np.linspace(0.3, 0.97, 5)
+    t = []
+    for l in range(4):
+        for c in (rows_c[l], rows_c[0]):
+            inside = c[(c > edges[l]) & (c < edges[l + 1] - 2 * delta)]
+            if inside.size:
+                t.append(float(np.float32(inside[inside.size // 2] + delta)))
+                break
+        else:
+            raise AssertionError("row too concentrated for the test")
+    assert all(t[i] < t[i + 1] for i in range(3))
+    return tuple(t)
+
+
+_QW = W.small(W.QWEN25VL_32K)
+FORCED = [
+    # sampling, every query block of head 0 a copy of the first: all its rows flagged
+    ("sampling-repeated", W.small(W.WAN13B_32K).replace(seq_valid=2048), True, 1.5e-6),
+    # antidiagonal S = 8, 16 compressed rows per query block (the float64 MFMA rescoring)
+    ("antidiag-s8-repeated", _QW.replace(causal=False, force_diag_l0=False), True, 1e-5),
+    # antidiagonal S = 4 with 64-row query blocks (16 compressed rows again)
+    ("antidiag-s4-repeated", _QW.replace(causal=False, force_diag_l0=False, block_q=64,
+                                         antidiag_stride=4), True, 1e-5),
+    # causal antidiagonal S = 8: each threshold next to a cumulative mass of another query block
+    ("antidiag-s8-causal", _QW, False, 1e-5),
+]
+
+
+@pytest.mark.parametrize("case", FORCED, ids=[c[0] for c in FORCED])
+def test_certification_forced(case):
+    """Thresholds placed `delta` above cumulative masses of chosen rows (inside the float32 margin
+    that flags a row for float64 rescoring, far outside the oracle's own 1e-12 margin): the
+    flagged rows are rescored in float64 and the map must equal the oracle's bit for bit. With
+    every query block of head 0 a copy of the first (non-causal), all of head 0's rows are
+    flagged."""
+    name, wl, repeated, delta = case
+    announce(f"forced certification {name}")
+    q, k, v = W.make_qkv(wl)
+    if repeated:
+        B, H, N, D = q.shape
+        q = q.clone()
+        q[:, 0] = q[:, 0, :wl.block_q].repeat(1, N // wl.block_q, 1)
+    p = oracle_problem(wl)
+    a0 = assign_params(wl)
+    _, M_ref, sim_ref = oracle.mask(q, k, p, wl.mask_mode, a0, samples=wl.samples_per_qblock,
+                                    stride=wl.antidiag_stride)
+    nq = p.n_qblocks
+    rows = (nq - 1,) * 4 if repeated else (nq - 1, nq - 3, nq // 2 + 1, nq // 2 - 1)
+    t = _near_thresholds([_prefix_sums(M_ref[0, 0, r], oracle.kb_diag(p, r) if p.causal else
+                                       p.n_kblocks - 1) for r in rows], delta)
+    wl_t = wl.replace(thresholds=t)
+    a = assign_params(wl_t)
+    lm_ref = np.stack([np.stack([oracle.assign_levels(M_ref[b, h], None if sim_ref is None else
+                                                      sim_ref[b, h // (q.shape[1] // k.shape[1])], p, a)
+                                 for h in range(q.shape[1])]) for b in range(q.shape[0])])
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    prob = problem_for(wl_t, qd, kd, vd)
+    cert = []
+    lm, M, sim = psa.mask(qd, kd, prob, mask_params(wl_t), cert_counts=cert)
+    torch.cuda.synchronize()
+    need = p.n_qblocks if repeated else 4
+    print(f"[{name}] thresholds {t}: {cert[0]} rows rescored in float64 (at least {need} expected)",
+          flush=True)
+    assert cert[1] == 0 and cert[0] >= need
+    check_map(lm.cpu().numpy(), lm_ref, oracle_margin_entries(M_ref, sim_ref, p, a), name, cert)

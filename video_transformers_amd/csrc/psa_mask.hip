@@ -1156,6 +1156,101 @@ __global__ void __launch_bounds__(256) k_cert_sampling_mfma(CertArgs a, const in
     }
 }
 
+// Antidiagonal mode on float64 MFMA, RQ = 16 compressed rows per query block (the 16 MFMA
+// rows): items (256 compressed columns, flagged row), column-chunk major; wave w takes columns
+// 64 w .. 64 w + 63 of the item as 4 column tiles of 16. The contraction runs over kdim = t * D + d (t < S, d < D):
+// A[i][kdim] = q[(qb * RQ + i) * S + S - 1 - t][d], B[kdim][c] = k[c * S + t][d]; lane group
+// g = lane / 16 holds kdims g * (S * D / 4) + ks, streamed in chunks of 32 (64 bytes of one
+// query row and one key row per lane). Column tiles that lie wholly past the block's last
+// compressed row (causal) or past the valid keys are skipped.
+template <int D, int S>
+__global__ void __launch_bounds__(256) k_cert_antidiag_mfma(CertArgs a) {
+    constexpr int RQ = 16;
+    constexpr int G = 64 / S;            // compressed columns per KV block
+    constexpr int KSP = S * D / 4;       // k-steps; lane group g holds kdims g * KSP + ks
+    constexpr int CH = 32;               // k-steps per chunk (64 bytes of one row)
+    static_assert(KSP % CH == 0 && D % CH == 0, "chunks inside one row");
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int g = lane >> 4;
+    const int j = lane & 15;
+    const int ncols = a.N / S;
+    const int nrows = min(a.cert[0], a.cap);
+    const int nchunk = (ncols + 255) / 256;
+    const int64_t items = static_cast<int64_t>(nrows) * nchunk;
+    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+        // column-chunk major: the workgroups in flight share one chunk's keys in L2
+        const int slot = static_cast<int>(it % nrows);
+        const int c0 = static_cast<int>(it / nrows) * 256 + wave * 64;
+        const RowIds r = row_ids(a.rows[slot], a.NQB, a.H, a.Hkv);
+        const int rlast = r.qb * RQ + RQ - 1;   // last compressed row of the query block
+        // the wave's column tiles that hold a visible column at all (wave-uniform); the others
+        // are not computed, and their log-masses are written as -inf below like any invisible one
+        const int cvis_end = min(ncols, (a.causal ? rlast + 1 : ncols));
+        const int ntiles = (c0 >= cvis_end || c0 * S >= a.Nv) ? 0 : min(4, (cvis_end - c0 + 15) / 16);
+        const bf16_bits* qh = a.q + r.b * a.qs0 + r.h * a.qs1;
+        const bf16_bits* kh = a.k + r.b * a.ks0 + r.hk * a.ks1;
+        f64x4 acc[4];
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) acc[nt] = f64x4{0.0, 0.0, 0.0, 0.0};
+        for (int kc = 0; ntiles > 0 && kc < KSP; kc += CH) {
+            const int kd = g * KSP + kc;   // first kdim of the chunk
+            const int t = kd / D;
+            const int d0 = kd % D;
+            // A chunk: compressed row j of the block, query row (qb RQ + j) S + S - 1 - t
+            const int qrow = (r.qb * RQ + j) * S + S - 1 - t;
+            u32x4 qa[CH / 8];
+#pragma unroll
+            for (int x = 0; x < CH / 8; ++x)
+                qa[x] = *reinterpret_cast<const u32x4*>(qh + static_cast<int64_t>(qrow) * a.qs2 + d0 + 8 * x);
+#pragma unroll
+            for (int nt = 0; nt < 4; ++nt) {
+                if (nt >= ntiles) break;   // wave-uniform
+                const int c = c0 + nt * 16 + j;
+                u32x4 kb4[CH / 8];
+#pragma unroll
+                for (int x = 0; x < CH / 8; ++x) {
+                    kb4[x] = u32x4{0u, 0u, 0u, 0u};
+                    if (c < ncols) kb4[x] = *reinterpret_cast<const u32x4*>(kh + static_cast<int64_t>(c * S + t) * a.ks2 + d0 + 8 * x);
+                }
+#pragma unroll
+                for (int ks = 0; ks < CH; ++ks) {
+                    const uint32_t wa = qa[ks / 8][(ks % 8) / 2];
+                    const uint32_t wb = kb4[ks / 8][(ks % 8) / 2];
+                    const double av = static_cast<double>(__uint_as_float((ks & 1) ? (wa & 0xffff0000u) : (wa << 16)));
+                    const double bv = static_cast<double>(__uint_as_float((ks & 1) ? (wb & 0xffff0000u) : (wb << 16)));
+                    acc[nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[nt], 0, 0, 0);
+                }
+            }
+        }
+        // results: D[4 rr + g][j] of tile nt = compressed row 4 rr + g, column c0 + 16 nt + j;
+        // each KV block is G = 8 consecutive columns, i.e. 8 lanes of one tile
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+            const int c = c0 + nt * 16 + j;
+            const bool col_ok = c < ncols && c * S + S - 1 < a.Nv;
+            const int kb = c / G;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int i = 4 * rr + g;
+                const int rg = r.qb * RQ + i;
+                const bool row_ok = rg * S + S - 1 < a.Nv;
+                const bool vis = nt < ntiles && col_ok && row_ok && (!a.causal || c <= rg);
+                const double z = vis ? acc[nt][rr] * a.scale : -INFINITY;
+                double m = z;
+#pragma unroll
+                for (int o = 1; o < G; o <<= 1) m = fmax(m, __shfl_xor(m, o, 64));
+                double e = m == -INFINITY ? 0.0 : exp(z - m);
+#pragma unroll
+                for (int o = 1; o < G; o <<= 1) e += __shfl_xor(e, o, 64);
+                const double L = m == -INFINITY ? -INFINITY : m + log(e);
+                if ((j % G) == 0 && c < ncols)
+                    a.Lg[(static_cast<int64_t>(slot) * RQ + i) * a.NKB + kb] = L;
+            }
+        }
+    }
+}
+
 // Antidiagonal mode, stride S: items (flagged row, chunk of 512 compressed columns); thread =
 // columns c and c + 256, every compressed row i < RQ of the query block against each: the
 // float64 sum over t < S of q[(qb*RQ + i)*S + S-1-t] . k[c*S + t]. The query block's rows sit
@@ -1648,6 +1743,18 @@ hipError_t launch_mask_certify(const Shape& s, const psa_mask_params& mp, const 
             case 16: if (D == 128) PSA_CERT_SAMP(128, 16); else PSA_CERT_SAMP(64, 16); break;
             case 32: if (D == 128) PSA_CERT_SAMP(128, 32); else PSA_CERT_SAMP(64, 32); break;
             default: return hipErrorNotSupported;
+        }
+    } else if (antidiag && g.RQ == 16 && (g.S == 8 || g.S == 4)) {
+        // float64 MFMA: the query block's 16 compressed rows are the 16 MFMA rows
+        const int nchunk = (s.N / g.S + 255) / 256;
+        const unsigned grid = static_cast<unsigned>(
+            std::min<int64_t>(4096, std::max<int64_t>(1, static_cast<int64_t>(c.cap) * nchunk)));
+        if (g.S == 8) {
+            if (D == 128) hipLaunchKernelGGL((k_cert_antidiag_mfma<128, 8>), dim3(grid), dim3(256), 0, st, c);
+            else hipLaunchKernelGGL((k_cert_antidiag_mfma<64, 8>), dim3(grid), dim3(256), 0, st, c);
+        } else {
+            if (D == 128) hipLaunchKernelGGL((k_cert_antidiag_mfma<128, 4>), dim3(grid), dim3(256), 0, st, c);
+            else hipLaunchKernelGGL((k_cert_antidiag_mfma<64, 4>), dim3(grid), dim3(256), 0, st, c);
         }
     } else if (antidiag) {
         const int key = g.S * 100 + g.RQ;
