@@ -575,15 +575,21 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
             }
         }
     };
-    // row max over the 16 values of sacc[H] in two chains (max3 each): part 0 / part 1 / final
+    // max over the 8 values of part `part` of sacc[H]: a chain of three max3 and one max
     auto half_max_part = [&](auto H, int part) {
         constexpr int hh = decltype(H)::value;
         const int e0 = part * 8;
-        return fmaxf(fmaxf(fmaxf(sacc[hh][e0], sacc[hh][e0 + 1]), fmaxf(sacc[hh][e0 + 2], sacc[hh][e0 + 3])),
-                     fmaxf(fmaxf(sacc[hh][e0 + 4], sacc[hh][e0 + 5]), fmaxf(sacc[hh][e0 + 6], sacc[hh][e0 + 7])));
+        float m = __builtin_fmaxf(__builtin_fmaxf(sacc[hh][e0], sacc[hh][e0 + 1]), sacc[hh][e0 + 2]);
+        asm volatile("" : "+v"(m));
+        m = __builtin_fmaxf(__builtin_fmaxf(m, sacc[hh][e0 + 3]), sacc[hh][e0 + 4]);
+        asm volatile("" : "+v"(m));
+        m = __builtin_fmaxf(__builtin_fmaxf(m, sacc[hh][e0 + 5]), sacc[hh][e0 + 6]);
+        return __builtin_fmaxf(m, sacc[hh][e0 + 7]);
     };
+    // this lane's max over its half of the step's keys (the other half of each query's keys
+    // sits in lane l ^ 32; the two are combined only when the max in use is raised), log2 units
     auto half_max = [&](float x0, float x1, int lvl) {
-        return fmaf(pair32_max(fmaxf(x0, x1)), cs, static_cast<float>(lvl));  // log2 units
+        return fmaf(fmaxf(x0, x1), cs, static_cast<float>(lvl));
     };
     // lazy running max: rescale the O accumulators and row sums only when the max in use is
     // exceeded by more than kLazyRescale (after the O products issued so far)
@@ -595,8 +601,11 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
     // pending product (`pending`) is rescaled with the accumulators.
     constexpr float kRescale = PV8 ? 1.0f : kLazyRescale;
     auto update_max = [&](float mt, bool pending = false) {
+        // mt is this lane's half of the query's keys: the query's max exceeds the bound iff
+        // one of its two lanes' does, and the new max is taken over both
         if (__builtin_expect(__ballot(mt > m_use + kRescale) != 0ull, 0)) {
-            const float m_new = fmaxf(m_use, PV8 ? ceilf(mt) : mt);
+            const float mt_all = pair32_max(mt);
+            const float m_new = fmaxf(m_use, PV8 ? ceilf(mt_all) : mt_all);
             const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_use - m_new);
             m_use = m_new;
             if constexpr (PV8) {
