@@ -1164,12 +1164,12 @@ __global__ void __launch_bounds__(256) k_cert_sampling_mfma(CertArgs a, const in
 // query row and one key row per lane). Column tiles that lie wholly past the block's last
 // compressed row (causal) or past the valid keys are skipped.
 template <int D, int S>
-__global__ void __launch_bounds__(256) k_cert_antidiag_mfma(CertArgs a) {
+__global__ void __launch_bounds__(256, 2) k_cert_antidiag_mfma(CertArgs a) {
     constexpr int RQ = 16;
     constexpr int G = 64 / S;            // compressed columns per KV block
     constexpr int KSP = S * D / 4;       // k-steps; lane group g holds kdims g * KSP + ks
-    constexpr int CH = 32;               // k-steps per chunk (64 bytes of one row)
-    static_assert(KSP % CH == 0 && D % CH == 0, "chunks inside one row");
+    constexpr int CH = 16;               // k-steps per chunk (32 bytes of one row)
+    static_assert(KSP % (2 * CH) == 0 && D % CH == 0, "chunks inside one row, in pairs");
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int g = lane >> 4;
@@ -1193,34 +1193,68 @@ __global__ void __launch_bounds__(256) k_cert_antidiag_mfma(CertArgs a) {
         f64x4 acc[4];
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) acc[nt] = f64x4{0.0, 0.0, 0.0, 0.0};
-        for (int kc = 0; ntiles > 0 && kc < KSP; kc += CH) {
+        // a chunk's operands: A = 32 bytes of one query row, B = 32 bytes of one key row per
+        // live tile (a column past the last is clamped to it; its results are not used); the
+        // next chunk's loads are issued before the current chunk's MFMAs
+        auto load = [&](int kc, u32x4 (&qa)[CH / 8], u32x4 (&kb)[4][CH / 8]) {
             const int kd = g * KSP + kc;   // first kdim of the chunk
             const int t = kd / D;
             const int d0 = kd % D;
-            // A chunk: compressed row j of the block, query row (qb RQ + j) S + S - 1 - t
             const int qrow = (r.qb * RQ + j) * S + S - 1 - t;
-            u32x4 qa[CH / 8];
 #pragma unroll
             for (int x = 0; x < CH / 8; ++x)
                 qa[x] = *reinterpret_cast<const u32x4*>(qh + static_cast<int64_t>(qrow) * a.qs2 + d0 + 8 * x);
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt) {
                 if (nt >= ntiles) break;   // wave-uniform
-                const int c = c0 + nt * 16 + j;
-                u32x4 kb4[CH / 8];
+                const int c = min(c0 + nt * 16 + j, ncols - 1);
 #pragma unroll
-                for (int x = 0; x < CH / 8; ++x) {
-                    kb4[x] = u32x4{0u, 0u, 0u, 0u};
-                    if (c < ncols) kb4[x] = *reinterpret_cast<const u32x4*>(kh + static_cast<int64_t>(c * S + t) * a.ks2 + d0 + 8 * x);
-                }
+                for (int x = 0; x < CH / 8; ++x)
+                    kb[nt][x] = *reinterpret_cast<const u32x4*>(kh + static_cast<int64_t>(c * S + t) * a.ks2 + d0 + 8 * x);
+            }
+        };
+        auto mul = [&](const u32x4 (&qa)[CH / 8], const u32x4 (&kb)[4][CH / 8]) {
+            double av[CH];   // converted once, used by every tile
+#pragma unroll
+            for (int ks = 0; ks < CH; ++ks) {
+                const uint32_t wa = qa[ks / 8][(ks % 8) / 2];
+                av[ks] = static_cast<double>(__uint_as_float((ks & 1) ? (wa & 0xffff0000u) : (wa << 16)));
+            }
+            auto bval = [&](int nt, int ks) {
+                const uint32_t wb = kb[nt][ks / 8][(ks % 8) / 2];
+                return static_cast<double>(__uint_as_float((ks & 1) ? (wb & 0xffff0000u) : (wb << 16)));
+            };
+            if (ntiles == 4) {
+                // the four tiles' accumulation chains interleaved: consecutive MFMAs are
+                // independent
 #pragma unroll
                 for (int ks = 0; ks < CH; ++ks) {
-                    const uint32_t wa = qa[ks / 8][(ks % 8) / 2];
-                    const uint32_t wb = kb4[ks / 8][(ks % 8) / 2];
-                    const double av = static_cast<double>(__uint_as_float((ks & 1) ? (wa & 0xffff0000u) : (wa << 16)));
-                    const double bv = static_cast<double>(__uint_as_float((ks & 1) ? (wb & 0xffff0000u) : (wb << 16)));
-                    acc[nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[nt], 0, 0, 0);
+#pragma unroll
+                    for (int nt = 0; nt < 4; ++nt)
+                        acc[nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[ks], bval(nt, ks), acc[nt], 0, 0, 0);
+                    // (keeps each conversion next to its MFMA: hoisted, they exhaust the VGPRs)
+                    __builtin_amdgcn_sched_barrier(0);
                 }
+            } else {
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    if (nt >= ntiles) break;   // wave-uniform
+#pragma unroll
+                    for (int ks = 0; ks < CH; ++ks) {
+                        acc[nt] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[ks], bval(nt, ks), acc[nt], 0, 0, 0);
+                        if (ks % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+            }
+        };
+        if (ntiles > 0) {
+            u32x4 qa0[CH / 8], qa1[CH / 8], kb0[4][CH / 8], kb1[4][CH / 8];
+            load(0, qa0, kb0);
+            for (int kc = 0; kc < KSP; kc += 2 * CH) {
+                load(kc + CH, qa1, kb1);
+                mul(qa0, kb0);
+                if (kc + 2 * CH < KSP) load(kc + 2 * CH, qa0, kb0);
+                mul(qa1, kb1);
             }
         }
         // results: D[4 rr + g][j] of tile nt = compressed row 4 rr + g, column c0 + 16 nt + j;
