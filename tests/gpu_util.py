@@ -180,20 +180,32 @@ def check_map(got: np.ndarray, ref: np.ndarray, marg: np.ndarray, what: str, cer
         assert cert[1] == 0, f"{what}: {cert[1]} flagged rows left uncertified"
 
 
-def dispatch_order(row_ptr, rows, unit):
+def order_interleaved(wl: W.Workload) -> bool:
+    """Whether psa_build_index lays its dispatch list over the XCDs interleaved: the K and V
+    rows of all levels (N + 7N/8 rows each) of eight KV heads exceed 256 MB, and there is more
+    than one (batch, KV head)."""
+    elem = 4 if wl.dtype == "f32" else 2
+    per_head = (wl.seq_len + 7 * wl.seq_len // 8) * wl.head_dim * elem * 2
+    return wl.batch * wl.heads_kv > 1 and 8 * per_head > (256 << 20)
+
+
+def dispatch_order(row_ptr, rows, unit, interleaved=False):
     """The attention's dispatch order that psa_build_index writes after the CSR offsets
-    (row_ptr[rows*4+1 + p] = the row of dispatch slot p), from its definition: slot p belongs to
-    XCD range p // ceil(rows/8); inside a range the rows are grouped by KV head (row // unit,
-    unit = NQB * heads_q / heads_kv), groups ascending, and inside a group listed by tile count
-    (sum over levels l of ceil(n_l / 2^l)), largest first, stably, over 32 buckets of the
-    group's span of counts. A scheduling choice of the library, not part of the method: no
-    oracle function."""
+    (row_ptr[rows*4+1 + p] = the row of dispatch slot p), from its definition: the rows grouped
+    by KV head (row // unit, unit = NQB * heads_q / heads_kv), groups ascending, and inside a
+    group listed by tile count (sum over levels l of ceil(n_l / 2^l)), largest first, stably,
+    over 32 buckets of the group's span of counts. Contiguous layout: slot p belongs to XCD
+    range p // ceil(rows/8), and a group cut by a range boundary is sorted in two parts.
+    Interleaved layout: whole groups, list position i at slot (i % 8) * ceil(rows/8) + i // 8
+    while every range has a slot left (m = rows - 7 ceil(rows/8) each), then the list's tail
+    in the remaining slots of ranges 0..6, in order.
+    A scheduling choice of the library, not part of the method: no oracle function."""
     cnt = np.diff(np.asarray(row_ptr[:rows * 4 + 1], dtype=np.int64)).reshape(rows, 4)
     tiles = sum((cnt[:, l] + (1 << l) - 1) >> l for l in range(4))
     nper = (rows + 7) // 8
     out = np.empty(rows, dtype=np.int64)
-    for x in range(8):
-        lo, hi = x * nper, min((x + 1) * nper, rows)
+    ranges = [(0, rows)] if interleaved else [(x * nper, min((x + 1) * nper, rows)) for x in range(8)]
+    for lo, hi in ranges:
         g = lo
         while g < hi:
             g_hi = min((g // unit + 1) * unit, hi)
@@ -201,10 +213,19 @@ def dispatch_order(row_ptr, rows, unit):
             bucket = ((t.max() - t) * 32) // (t.max() - t.min() + 1)
             out[g:g_hi] = g + np.argsort(bucket, kind="stable")
             g = g_hi
+    if interleaved:
+        m = max(rows - 7 * nper, 0)   # slots of the last range (every range has as many)
+        i = np.arange(rows)
+        j = i - 8 * m
+        w = max(nper - m, 1)
+        slot = np.where(i < 8 * m, (i % 8) * nper + i // 8, (j // w) * nper + m + j % w)
+        laid = np.empty(rows, dtype=np.int64)
+        laid[slot] = out
+        return laid
     return out
 
 
-def check_index(row_ptr, col_idx, rp_ref, ci_ref, unit):
+def check_index(row_ptr, col_idx, rp_ref, ci_ref, unit, interleaved=False):
     """psa_build_index's output against the oracle's CSR (bit for bit) and the dispatch order
     against its definition (bit for bit, and a permutation of the rows); unit = the rows per KV
     head (NQB * heads_q / heads_kv)."""
@@ -216,4 +237,4 @@ def check_index(row_ptr, col_idx, rp_ref, ci_ref, unit):
     assert np.array_equal(ci[:rp_ref[-1]], ci_ref)
     order = rp[rows * 4 + 1:]
     assert np.array_equal(np.sort(order), np.arange(rows))
-    assert np.array_equal(order, dispatch_order(rp_ref, rows, unit))
+    assert np.array_equal(order, dispatch_order(rp_ref, rows, unit, interleaved))

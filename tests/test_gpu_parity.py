@@ -116,6 +116,26 @@ def test_build_index_all_skip_many_tiles():
     assert err.item() == 0
 
 
+def test_build_index_interleaved_order():
+    """A problem whose eight KV heads' K and V (all levels) exceed 256 MB (Wan2.1-14B-like
+    length, GQA 2:1): psa_build_index lays the dispatch list over the XCDs interleaved. CSR bit
+    for bit against the oracle, the order against its definition. Only the map and the shape
+    are read, so Q, K, V are zeros."""
+    announce("build_index interleaved order")
+    B, H, Hkv, N, D = 1, 4, 2, 75648, 128
+    nqb, nkb = N // 128, N // 64
+    rng = np.random.default_rng(75648)
+    lm = rng.choice(np.array([0, 1, 2, 3, -1], dtype=np.int8), size=(B, H, nqb, nkb),
+                    p=[0.05, 0.05, 0.05, 0.05, 0.8])
+    q = torch.zeros((B, H, N, D), device=DEV, dtype=torch.bfloat16)
+    k = torch.zeros((B, Hkv, N, D), device=DEV, dtype=torch.bfloat16)
+    prob = psa.make_problem(q, k, k, block_q=128)
+    row_ptr, col_idx, err = psa.build_index(torch.from_numpy(lm).to(DEV), prob)
+    rp_ref, ci_ref = oracle.build_index(lm)
+    check_index(row_ptr, col_idx, rp_ref, ci_ref, nqb * (H // Hkv), interleaved=True)
+    assert err.item() == 0
+
+
 def test_build_index_flags_bad_entries():
     announce("build_index bad entries")
     lm = np.zeros((1, 2, 16, 16), dtype=np.int8)

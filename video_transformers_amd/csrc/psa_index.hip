@@ -160,18 +160,34 @@ __global__ void __launch_bounds__(256)
 }
 
 // Dispatch order of the attention workgroups. Workgroup i runs on XCD i % 8, and the attention
-// kernels give XCD x the rows of one contiguous range [x * nper, (x + 1) * nper), nper =
-// ceil(rows / 8), so that neighbouring query blocks of a head share that XCD's L2. Inside a
-// range the rows are grouped by KV head (rows / unit, unit = NQB * heads_q / heads_kv: the
-// query heads that read one KV head), groups in ascending order, and inside a group listed by
-// their number of 64-row tiles (sum over levels l of ceil(n_l / 2^l)), largest first. The rows
-// an XCD runs at one time then read one KV head's blocks, mostly the same ones (rows of
-// similar tile counts have similar maps), and the workgroups it starts last are short ones
-// (longest-processing-time-first list scheduling). Each group: a stable counting sort over
-// kOrderBuckets buckets spanning the group's tile counts (exact for spans up to
-// kOrderBuckets, bucketed beyond); deterministic.
+// kernels give XCD x the slots of one contiguous range [x * nper, (x + 1) * nper), nper =
+// ceil(rows / 8). The rows are grouped by KV head (rows / unit, unit = NQB * heads_q /
+// heads_kv: the query heads that read one KV head), groups in ascending order, and inside a
+// group listed by their number of 64-row tiles (sum over levels l of ceil(n_l / 2^l)), largest
+// first: rows of similar tile counts have similar maps and fetch mostly the same blocks, and
+// the workgroups started last are short ones (longest-processing-time-first list scheduling).
+// Two ways to lay that list over the XCDs:
+//  * contiguous (the default): slot ranges follow the row numbering, so each XCD takes whole
+//    KV heads (a group cut by a range boundary is sorted in two parts) and neighbouring query
+//    blocks of a head share that XCD's L2;
+//  * interleaved, when the K and V rows (all levels) of eight KV heads exceed the 256 MB
+//    last-level cache: list position i goes to slot (i mod 8) * nper + i / 8, so the eight
+//    XCDs work through the same KV head at the same time and that cache holds its blocks.
+//    (The last range has m = rows - 7 nper slots; positions from 8m on, the list's tail, fill
+//    the other ranges' remaining slots in order.)
+// Each group: a stable counting sort over kOrderBuckets buckets spanning the group's tile
+// counts (exact for spans up to kOrderBuckets, bucketed beyond); deterministic.
 constexpr int kOrderThreads = 256;
 constexpr int kOrderBuckets = 32;
+
+// slot of list position i in the interleaved layout (see above)
+__device__ __forceinline__ int64_t interleaved_slot(int64_t i, int64_t rows, int64_t nper) {
+    const int64_t m = rows - 7 * nper > 0 ? rows - 7 * nper : 0;   // slots of every range
+    if (i < 8 * m) return (i & 7) * nper + (i >> 3);
+    const int64_t j = i - 8 * m;
+    const int64_t w = nper - m;   // remaining slots of ranges 0..6 (j < 7 w)
+    return (j / w) * nper + m + j % w;
+}
 
 __device__ __forceinline__ int row_tiles(const int32_t* rp, int64_t r) {
     const int32_t* p = rp + r * 4;
@@ -203,16 +219,17 @@ __device__ int order_exclusive_scan(int v, int* wsum) {
 
 __global__ void __launch_bounds__(kOrderThreads)
     k_index_order(const int32_t* __restrict__ row_ptr, int64_t rows, int64_t nper, int64_t unit,
-                  int32_t* __restrict__ order) {
+                  int interleave, int32_t* __restrict__ order) {
     __shared__ int hist[kOrderBuckets * kOrderThreads];   // [bucket][thread]
     __shared__ int wred[2][kOrderThreads / 64];
     __shared__ int wsum[kOrderThreads / 64];
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = t >> 6;
-    const int64_t lo = static_cast<int64_t>(blockIdx.x) * nper;
-    const int64_t hi = lo + nper < rows ? lo + nper : rows;
-    // the KV-head groups of the range, one after another (uniform loop)
+    // contiguous: the KV-head groups (or parts) of range blockIdx.x, one after another;
+    // interleaved: the whole groups blockIdx.x, blockIdx.x + 8, ... (uniform loops)
+    const int64_t lo = interleave ? static_cast<int64_t>(blockIdx.x) * unit : static_cast<int64_t>(blockIdx.x) * nper;
+    const int64_t hi = interleave ? rows : (lo + nper < rows ? lo + nper : rows);
     for (int64_t g_lo = lo; g_lo < hi;) {
         const int64_t g_end = (g_lo / unit + 1) * unit;
         const int64_t g_hi = g_end < hi ? g_end : hi;
@@ -264,11 +281,12 @@ __global__ void __launch_bounds__(kOrderThreads)
         __syncthreads();
         for (int64_t r = s0; r < s1; ++r) {
             int* slot = &hist[bucket(row_tiles(row_ptr, r)) * kOrderThreads + t];
-            order[g_lo + *slot] = static_cast<int32_t>(r);
+            const int64_t i = g_lo + *slot;   // list position
+            order[interleave ? interleaved_slot(i, rows, nper) : i] = static_cast<int32_t>(r);
             ++*slot;
         }
         __syncthreads();   // hist and wred are reused by the next group
-        g_lo = g_hi;
+        g_lo = interleave ? g_hi + 7 * unit : g_hi;
     }
 }
 
@@ -288,6 +306,14 @@ hipError_t launch_fill_lds(uint32_t pattern, hipStream_t st) {
     hipLaunchKernelGGL(k_fill_lds, dim3(static_cast<unsigned>(cus) * 20), dim3(256), 0, st, pattern,
                        static_cast<int32_t*>(nullptr));
     return hipGetLastError();
+}
+
+// The interleaved dispatch order: the K and V rows of all levels (N + 7N/8 rows each) of eight
+// KV heads exceed the 256 MB last-level cache.
+bool order_interleaved(const Shape& s) {
+    const int64_t elem = s.dtype == PSA_F32 ? 4 : 2;
+    const int64_t per_head = (static_cast<int64_t>(s.N) + s.pooled_rows) * s.D * elem * 2;
+    return static_cast<int64_t>(s.B) * s.Hkv > 1 && 8 * per_head > (int64_t{256} << 20);
 }
 
 hipError_t launch_build_index(const Shape& s, const int8_t* level_map, const IndexBufs& ib,
@@ -310,7 +336,7 @@ hipError_t launch_build_index(const Shape& s, const int8_t* level_map, const Ind
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t unit = static_cast<int64_t>(s.NQB) * (s.H / s.Hkv);   // rows per KV head
     hipLaunchKernelGGL(k_index_order, dim3(8), dim3(kOrderThreads), 0, st, ib.row_ptr, rows, (rows + 7) / 8,
-                       unit, ib.row_ptr + rows * 4 + 1);
+                       unit, order_interleaved(s) ? 1 : 0, ib.row_ptr + rows * 4 + 1);
     return hipGetLastError();
 }
 
