@@ -199,11 +199,15 @@ int psa_mask_assign(const psa_problem* prob, const psa_mask_params* params,
  * Block index: a CSR over (row, level) keys, rows r = (b*heads_q + h)*NQB + qb.
  * row_ptr[R*5+1] int32: col_idx[row_ptr[r*4+l] .. row_ptr[r*4+l+1]) lists, in ascending
  * order, the kb with level_map == l; then row_ptr[R*4+1 + p], p < R, is the row the attention
- * runs in dispatch slot p (a permutation of the rows: slot p runs on XCD p / ceil(R/8); each
- * XCD's contiguous range of rows is grouped by KV head, r / (NQB*heads_q/heads_kv), groups in
- * ascending order, each group listed by its rows' count of 64-row tiles, sum over l of
- * ceil(n_l / 2^l), largest first; a stable counting sort over 32 buckets of the group's span of
- * counts, exact when that span is at most 32). col_idx needs capacity R*NKB int32; its entries past
+ * runs in dispatch slot p (a permutation of the rows: slot p runs on XCD p / ceil(R/8)). The
+ * rows are grouped by KV head, r / (NQB*heads_q/heads_kv), groups in ascending order, each
+ * group listed by its rows' count of 64-row tiles, sum over l of ceil(n_l / 2^l), largest
+ * first (a stable counting sort over 32 buckets of the group's span of counts, exact when that
+ * span is at most 32). That list fills the slots in order (each XCD's contiguous range sorted
+ * on its own where it cuts a group), or, when the K and V rows of all levels ((N + 7N/8) * d
+ * elements each) of eight KV heads exceed 256 MB and B*heads_kv > 1, interleaved: list
+ * position i in slot (i mod 8)*ceil(R/8) + i/8 while every XCD range has slots left, the rest
+ * in the remaining slots in order. col_idx needs capacity R*NKB int32; its entries past
  * row_ptr[R*4] are unspecified (the call parks scan partial sums there). Entries outside
  * {-1..3} are treated as skip and set *dev_err (device int32) to PSA_ERR_BAD_LEVEL_MAP;
  * the call clears *dev_err first.
