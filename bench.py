@@ -403,9 +403,9 @@ def run(args) -> dict:
 
 def _workload_attention(wl, dev, reps: int = 10) -> dict:
     """One workload's attention on its own map (psa_mask, or the drawn map), inputs resident:
-    mean of `reps` back-to-back psa_attn_fwd_indexed calls after two untimed ones (sustained
-    attention load, unlike the step, where the pyramid and the mask run between attention
-    calls), executed level-weighted FLOP over that time, and the pyramid, psa_mask and
+    mean of about 0.3 s (at least `reps`) of back-to-back psa_attn_fwd_indexed calls after about
+    0.2 s of untimed ones (sustained attention load, unlike the step, where the pyramid and the
+    mask run between attention calls), executed level-weighted FLOP over that time, and the pyramid, psa_mask and
     psa_build_index calls, each the mean of 5 back-to-back calls after its first."""
     import ctypes
     import torch
@@ -441,7 +441,11 @@ def _workload_attention(wl, dev, reps: int = 10) -> dict:
                                     ptr(kp), ptr(vp), ptr(rp), ptr(ci), ptr(o), ptr(lse), st)
         if rc != 0:
             raise psa.PsaError(rc, f"attn {wl.name}")
-    ms = _timed_back_to_back(call, stream, reps=reps)
+    # warm up for about 0.2 s (the clocks settle under a sustained load), then time about 0.3 s
+    # of calls (at least `reps`)
+    est = _timed_back_to_back(call, stream, reps=2, warm=1)
+    warm = max(2, int(200.0 / max(est, 1e-3)))
+    ms = _timed_back_to_back(call, stream, reps=max(reps, int(300.0 / max(est, 1e-3))), warm=warm)
     torch.cuda.synchronize()
     if int(err.item()) != 0:
         raise RuntimeError(f"{wl.name}: level map held invalid entries")
