@@ -203,11 +203,12 @@ int psa_mask_assign(const psa_problem* prob, const psa_mask_params* params,
  * rows are grouped by KV head, r / (NQB*heads_q/heads_kv), groups in ascending order, each
  * group listed by its rows' count of 64-row tiles, sum over l of ceil(n_l / 2^l), largest
  * first (a stable counting sort over 32 buckets of the group's span of counts, exact when that
- * span is at most 32). That list fills the slots in order (each XCD's contiguous range sorted
- * on its own where it cuts a group), or, when the K and V rows of all levels ((N + 7N/8) * d
- * elements each) of eight KV heads exceed 256 MB and B*heads_kv > 1, interleaved: list
- * position i in slot (i mod 8)*ceil(R/8) + i/8 while every XCD range has slots left, the rest
- * in the remaining slots in order. col_idx needs capacity R*NKB int32; its entries past
+ * span is at most 32). That list is laid over chunks of f consecutive XCD ranges, f the
+ * smallest of 1, 2, 4, 8 with (8/f) * 2 * (N + 7N/8) * d * sizeof(element) <= 128 MB (1 when
+ * B*heads_kv == 1): inside a chunk, position j goes to range (first + j mod f), slot j/f of that
+ * range, while every range of the chunk has slots left, the chunk's tail to the remaining slots
+ * in order. For f < 8 each range is sorted on its own where it cuts a group; for f = 8 whole
+ * groups are sorted. col_idx needs capacity R*NKB int32; its entries past
  * row_ptr[R*4] are unspecified (the call parks scan partial sums there). Entries outside
  * {-1..3} are treated as skip and set *dev_err (device int32) to PSA_ERR_BAD_LEVEL_MAP;
  * the call clears *dev_err first.

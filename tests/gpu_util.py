@@ -180,31 +180,57 @@ def check_map(got: np.ndarray, ref: np.ndarray, marg: np.ndarray, what: str, cer
         assert cert[1] == 0, f"{what}: {cert[1]} flagged rows left uncertified"
 
 
-def order_interleaved(wl: W.Workload) -> bool:
-    """Whether psa_build_index lays its dispatch list over the XCDs interleaved: the K and V
-    rows of all levels (N + 7N/8 rows each) of eight KV heads exceed 256 MB, and there is more
-    than one (batch, KV head)."""
+def order_share(wl: W.Workload) -> int:
+    """XCD ranges per chunk of psa_build_index's dispatch order: the smallest f of 1, 2, 4, 8
+    for which the K and V rows of all levels (N + 7N/8 rows each) of 8 / f KV heads fit in
+    128 MB; 1 with a single (batch, KV head)."""
+    if wl.batch * wl.heads_kv <= 1:
+        return 1
     elem = 4 if wl.dtype == "f32" else 2
     per_head = (wl.seq_len + 7 * wl.seq_len // 8) * wl.head_dim * elem * 2
-    return wl.batch * wl.heads_kv > 1 and 8 * per_head > (256 << 20)
+    f = 1
+    while f < 8 and (8 // f) * per_head > (128 << 20):
+        f *= 2
+    return f
 
 
-def dispatch_order(row_ptr, rows, unit, interleaved=False):
+def chunk_slots(rows, nper, f):
+    """Slot of each list position with f XCD ranges per chunk: inside a chunk, position j to
+    range (first + j mod f), local slot j // f, while every range of the chunk has slots left;
+    the chunk's tail then fills the ranges' remaining slots in order."""
+    lens = [min(max(rows - x * nper, 0), nper) for x in range(8)]
+    out = np.empty(rows, dtype=np.int64)
+    for i in range(rows):
+        x0 = (i // (f * nper)) * f
+        j = i - x0 * nper
+        m = min(lens[x0 + k] for k in range(f))
+        if j < f * m:
+            out[i] = (x0 + j % f) * nper + j // f
+            continue
+        j -= f * m
+        for k in range(f):
+            rem = lens[x0 + k] - m
+            if j < rem:
+                out[i] = (x0 + k) * nper + m + j
+                break
+            j -= rem
+    return out
+
+
+def dispatch_order(row_ptr, rows, unit, share=1):
     """The attention's dispatch order that psa_build_index writes after the CSR offsets
     (row_ptr[rows*4+1 + p] = the row of dispatch slot p), from its definition: the rows grouped
     by KV head (row // unit, unit = NQB * heads_q / heads_kv), groups ascending, and inside a
     group listed by tile count (sum over levels l of ceil(n_l / 2^l)), largest first, stably,
-    over 32 buckets of the group's span of counts. Contiguous layout: slot p belongs to XCD
-    range p // ceil(rows/8), and a group cut by a range boundary is sorted in two parts.
-    Interleaved layout: whole groups, list position i at slot (i % 8) * ceil(rows/8) + i // 8
-    while every range has a slot left (m = rows - 7 ceil(rows/8) each), then the list's tail
-    in the remaining slots of ranges 0..6, in order.
-    A scheduling choice of the library, not part of the method: no oracle function."""
+    over 32 buckets of the group's span of counts. With share f < 8 each XCD range of
+    ceil(rows/8) positions is sorted on its own where it cuts a group; with f = 8 whole groups
+    are sorted. List positions then go to slots by chunk_slots. A scheduling choice of the
+    library, not part of the method: no oracle function."""
     cnt = np.diff(np.asarray(row_ptr[:rows * 4 + 1], dtype=np.int64)).reshape(rows, 4)
     tiles = sum((cnt[:, l] + (1 << l) - 1) >> l for l in range(4))
     nper = (rows + 7) // 8
     out = np.empty(rows, dtype=np.int64)
-    ranges = [(0, rows)] if interleaved else [(x * nper, min((x + 1) * nper, rows)) for x in range(8)]
+    ranges = [(0, rows)] if share == 8 else [(x * nper, min((x + 1) * nper, rows)) for x in range(8)]
     for lo, hi in ranges:
         g = lo
         while g < hi:
@@ -213,19 +239,14 @@ def dispatch_order(row_ptr, rows, unit, interleaved=False):
             bucket = ((t.max() - t) * 32) // (t.max() - t.min() + 1)
             out[g:g_hi] = g + np.argsort(bucket, kind="stable")
             g = g_hi
-    if interleaved:
-        m = max(rows - 7 * nper, 0)   # slots of the last range (every range has as many)
-        i = np.arange(rows)
-        j = i - 8 * m
-        w = max(nper - m, 1)
-        slot = np.where(i < 8 * m, (i % 8) * nper + i // 8, (j // w) * nper + m + j % w)
-        laid = np.empty(rows, dtype=np.int64)
-        laid[slot] = out
-        return laid
-    return out
+    if share == 1:
+        return out
+    laid = np.empty(rows, dtype=np.int64)
+    laid[chunk_slots(rows, nper, share)] = out
+    return laid
 
 
-def check_index(row_ptr, col_idx, rp_ref, ci_ref, unit, interleaved=False):
+def check_index(row_ptr, col_idx, rp_ref, ci_ref, unit, share=1):
     """psa_build_index's output against the oracle's CSR (bit for bit) and the dispatch order
     against its definition (bit for bit, and a permutation of the rows); unit = the rows per KV
     head (NQB * heads_q / heads_kv)."""
@@ -237,4 +258,4 @@ def check_index(row_ptr, col_idx, rp_ref, ci_ref, unit, interleaved=False):
     assert np.array_equal(ci[:rp_ref[-1]], ci_ref)
     order = rp[rows * 4 + 1:]
     assert np.array_equal(np.sort(order), np.arange(rows))
-    assert np.array_equal(order, dispatch_order(rp_ref, rows, unit, interleaved))
+    assert np.array_equal(order, dispatch_order(rp_ref, rows, unit, share))

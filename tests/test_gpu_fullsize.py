@@ -23,7 +23,7 @@ import oracle
 import workloads as W
 import video_transformers_amd as psa
 from gpu_util import (DEV, announce, assign_params, check_attention, check_map, dispatch_order,
-                      mask_params, need_gpu, oracle_margin_entries, order_interleaved)
+                      mask_params, need_gpu, oracle_margin_entries, order_share)
 
 pytestmark = pytest.mark.gpu
 
@@ -68,7 +68,7 @@ def _run_path(wl, qd, kd, vd):
     rows = lm.numel() // prob.n_kblocks
     rp = row_ptr.cpu().numpy()
     assert np.array_equal(np.sort(rp[rows * 4 + 1:]), np.arange(rows))
-    assert np.array_equal(rp[rows * 4 + 1:], dispatch_order(rp, rows, wl.n_qblocks * wl.group, order_interleaved(wl)))
+    assert np.array_equal(rp[rows * 4 + 1:], dispatch_order(rp, rows, wl.n_qblocks * wl.group, order_share(wl)))
     return kp, vp, lm, M, sim, o, lse, cert
 
 

@@ -14,7 +14,7 @@ import workloads as W
 import video_transformers_amd as psa
 from gpu_util import (DEV, announce, assign_params, check_attention, check_index, check_map,
                       mask_params, need_gpu, oracle_map, oracle_margin_entries, oracle_problem,
-                      problem_for)
+                      order_share, problem_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -116,15 +116,25 @@ def test_build_index_all_skip_many_tiles():
     assert err.item() == 0
 
 
-def test_build_index_interleaved_order():
-    """A problem whose eight KV heads' K and V (all levels) exceed 256 MB (Wan2.1-14B-like
-    length, GQA 2:1): psa_build_index lays the dispatch list over the XCDs interleaved. CSR bit
-    for bit against the oracle, the order against its definition. Only the map and the shape
-    are read, so Q, K, V are zeros."""
-    announce("build_index interleaved order")
-    B, H, Hkv, N, D = 1, 4, 2, 75648, 128
+# (N, heads_q, heads_kv, XCD ranges per chunk of the dispatch order): lengths at which the K
+# and V of the KV heads in flight outgrow half the last-level cache (ragged row counts for
+# f = 2 and 4)
+SHARES = [(75648, 4, 2, 8), (32896, 4, 4, 2), (49280, 3, 3, 4)]
+
+
+@pytest.mark.parametrize("case", SHARES, ids=[f"N{c[0]}-f{c[3]}" for c in SHARES])
+def test_build_index_shared_order(case):
+    """Long problems: psa_build_index lays the dispatch list over chunks of f XCD ranges
+    (f = 2, 4, 8). CSR bit for bit against the oracle, the order against its definition. Only
+    the map and the shape are read, so Q, K, V are zeros."""
+    N, H, Hkv, f = case
+    announce(f"build_index order, N {N}, f {f}")
+    B, D = 1, 128
     nqb, nkb = N // 128, N // 64
-    rng = np.random.default_rng(75648)
+    wl = W.Workload(name="shape", seed=0, batch=B, heads_q=H, heads_kv=Hkv, head_dim=D,
+                    seq_len=N, seq_valid=N, block_q=128, block_k=64, dtype="bf16")
+    assert order_share(wl) == f
+    rng = np.random.default_rng(N)
     lm = rng.choice(np.array([0, 1, 2, 3, -1], dtype=np.int8), size=(B, H, nqb, nkb),
                     p=[0.05, 0.05, 0.05, 0.05, 0.8])
     q = torch.zeros((B, H, N, D), device=DEV, dtype=torch.bfloat16)
@@ -132,7 +142,7 @@ def test_build_index_interleaved_order():
     prob = psa.make_problem(q, k, k, block_q=128)
     row_ptr, col_idx, err = psa.build_index(torch.from_numpy(lm).to(DEV), prob)
     rp_ref, ci_ref = oracle.build_index(lm)
-    check_index(row_ptr, col_idx, rp_ref, ci_ref, nqb * (H // Hkv), interleaved=True)
+    check_index(row_ptr, col_idx, rp_ref, ci_ref, nqb * (H // Hkv), share=f)
     assert err.item() == 0
 
 

@@ -65,7 +65,7 @@ struct BwdArgs {
     bf16_bits* dk;
     bf16_bits* dv;
     int* claim;    // [8] next unclaimed pooled tile of each XCD's range (k_bwd_dkv), zeroed per call
-    int interleave;   // k_bwd_dkv's XCD ranges interleaved (tiles x, x + 8, ...), as the index's order
+    int interleave;   // k_bwd_dkv's XCD ranges interleaved (tiles x, x + 8, ...), as the index's order (f = 8)
     int B, H, Hkv, N, Nv, NQB, NKB, BQ, causal;
     int64_t qs0, qs1, qs2, ks0, ks1, ks2, vs0, vs1, vs2, os0, os1, os2;
     int64_t pooled_rows;   // 7N/8
@@ -400,8 +400,9 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a, int total_tiles, 
     // following range that has one left, so an XCD whose tiles happen to be cheap takes over
     // tiles of a busier one. Range x is the contiguous tiles [x nper, (x + 1) nper)
     // (neighbouring tiles of a KV head share that XCD's L2), or, when the block index lays its
-    // dispatch order interleaved (eight KV heads' K and V exceed the last-level cache), the
-    // tiles x, x + 8, x + 16, ... (the XCDs work through one KV head at a time). The grid has
+    // dispatch order over all eight XCDs at once (one KV head's K and V at a time fill half the
+    // last-level cache), the tiles x, x + 8, x + 16, ... (the XCDs work through one KV head at
+    // a time). The grid has
     // one workgroup per tile: every claim succeeds and every tile is processed once. (The
     // tiles are independent, so the assignment does not change any result.)
     const int nper = (total_tiles + 7) >> 3;
@@ -809,7 +810,7 @@ hipError_t launch_attn_bwd(const Shape& s, float scale, const void* q, const voi
     a.gk = f + 2 * rows;
     a.gv = a.gk + grows * s.D;
     a.claim = reinterpret_cast<int*>(a.gv + grows * s.D);
-    a.interleave = order_interleaved(s) ? 1 : 0;
+    a.interleave = order_share(s) == 8 ? 1 : 0;
     a.dq = static_cast<bf16_bits*>(dq);
     a.dk = static_cast<bf16_bits*>(dk);
     a.dv = static_cast<bf16_bits*>(dv);

@@ -166,27 +166,40 @@ __global__ void __launch_bounds__(256)
 // group listed by their number of 64-row tiles (sum over levels l of ceil(n_l / 2^l)), largest
 // first: rows of similar tile counts have similar maps and fetch mostly the same blocks, and
 // the workgroups started last are short ones (longest-processing-time-first list scheduling).
-// Two ways to lay that list over the XCDs:
-//  * contiguous (the default): slot ranges follow the row numbering, so each XCD takes whole
-//    KV heads (a group cut by a range boundary is sorted in two parts) and neighbouring query
-//    blocks of a head share that XCD's L2;
-//  * interleaved, when the K and V rows (all levels) of eight KV heads exceed the 256 MB
-//    last-level cache: list position i goes to slot (i mod 8) * nper + i / 8, so the eight
-//    XCDs work through the same KV head at the same time and that cache holds its blocks.
-//    (The last range has m = rows - 7 nper slots; positions from 8m on, the list's tail, fill
-//    the other ranges' remaining slots in order.)
+// The list is laid over the XCDs in chunks: f consecutive XCD ranges form a chunk, and
+// inside a chunk list position j goes to XCD (chunk's first + j mod f), its local slot j / f,
+// so the f XCDs work through the same rows, and the same KV head, at the same time (while
+// each range has slots left; the list's tail then fills the remaining slots in order). f is
+// the smallest of 1, 2, 4, 8 for which the K and V rows of all levels of the 8 / f KV heads
+// in flight fit in half the 256 MB last-level cache (f = 1 when there is one (batch, KV
+// head) only):
+//  * f = 1 (contiguous ranges): each XCD takes whole KV heads (a group cut by a range
+//    boundary is sorted in two parts) and neighbouring query blocks of a head share its L2;
+//  * f = 2, 4: as f = 1 inside each range, the chunk's ranges interleaved;
+//  * f = 8: whole groups sorted, the whole list interleaved over the eight XCDs.
 // Each group: a stable counting sort over kOrderBuckets buckets spanning the group's tile
 // counts (exact for spans up to kOrderBuckets, bucketed beyond); deterministic.
 constexpr int kOrderThreads = 256;
 constexpr int kOrderBuckets = 32;
 
-// slot of list position i in the interleaved layout (see above)
-__device__ __forceinline__ int64_t interleaved_slot(int64_t i, int64_t rows, int64_t nper) {
-    const int64_t m = rows - 7 * nper > 0 ? rows - 7 * nper : 0;   // slots of every range
-    if (i < 8 * m) return (i & 7) * nper + (i >> 3);
-    const int64_t j = i - 8 * m;
-    const int64_t w = nper - m;   // remaining slots of ranges 0..6 (j < 7 w)
-    return (j / w) * nper + m + j % w;
+// slot of list position i with f XCD ranges per chunk (see above); f = 1 is the identity
+__device__ __forceinline__ int64_t chunk_slot(int64_t i, int64_t rows, int64_t nper, int f) {
+    auto len = [&](int64_t x) {   // slots of XCD range x
+        const int64_t n = rows - x * nper;
+        return n < 0 ? int64_t{0} : (n < nper ? n : nper);
+    };
+    const int64_t x0 = (i / (f * nper)) * f;   // the chunk's first range
+    int64_t j = i - x0 * nper;                 // position inside the chunk
+    int64_t m = nper;                          // slots every range of the chunk has
+    for (int k = 0; k < f; ++k) m = len(x0 + k) < m ? len(x0 + k) : m;
+    if (j < f * m) return (x0 + j % f) * nper + j / f;
+    j -= f * m;
+    for (int k = 0; k < f; ++k) {   // the tail: the ranges' remaining slots, in order
+        const int64_t rem = len(x0 + k) - m;
+        if (j < rem) return (x0 + k) * nper + m + j;
+        j -= rem;
+    }
+    return -1;   // not reached: the chunk has as many slots as positions
 }
 
 __device__ __forceinline__ int row_tiles(const int32_t* rp, int64_t r) {
@@ -219,17 +232,18 @@ __device__ int order_exclusive_scan(int v, int* wsum) {
 
 __global__ void __launch_bounds__(kOrderThreads)
     k_index_order(const int32_t* __restrict__ row_ptr, int64_t rows, int64_t nper, int64_t unit,
-                  int interleave, int32_t* __restrict__ order) {
+                  int f, int32_t* __restrict__ order) {
     __shared__ int hist[kOrderBuckets * kOrderThreads];   // [bucket][thread]
     __shared__ int wred[2][kOrderThreads / 64];
     __shared__ int wsum[kOrderThreads / 64];
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = t >> 6;
-    // contiguous: the KV-head groups (or parts) of range blockIdx.x, one after another;
-    // interleaved: the whole groups blockIdx.x, blockIdx.x + 8, ... (uniform loops)
-    const int64_t lo = interleave ? static_cast<int64_t>(blockIdx.x) * unit : static_cast<int64_t>(blockIdx.x) * nper;
-    const int64_t hi = interleave ? rows : (lo + nper < rows ? lo + nper : rows);
+    // f < 8: the KV-head groups (or parts) of range blockIdx.x, one after another; f = 8: the
+    // whole groups blockIdx.x, blockIdx.x + 8, ... (uniform loops)
+    const bool whole = f == 8;
+    const int64_t lo = whole ? static_cast<int64_t>(blockIdx.x) * unit : static_cast<int64_t>(blockIdx.x) * nper;
+    const int64_t hi = whole ? rows : (lo + nper < rows ? lo + nper : rows);
     for (int64_t g_lo = lo; g_lo < hi;) {
         const int64_t g_end = (g_lo / unit + 1) * unit;
         const int64_t g_hi = g_end < hi ? g_end : hi;
@@ -282,11 +296,11 @@ __global__ void __launch_bounds__(kOrderThreads)
         for (int64_t r = s0; r < s1; ++r) {
             int* slot = &hist[bucket(row_tiles(row_ptr, r)) * kOrderThreads + t];
             const int64_t i = g_lo + *slot;   // list position
-            order[interleave ? interleaved_slot(i, rows, nper) : i] = static_cast<int32_t>(r);
+            order[f == 1 ? i : chunk_slot(i, rows, nper, f)] = static_cast<int32_t>(r);
             ++*slot;
         }
         __syncthreads();   // hist and wred are reused by the next group
-        g_lo = interleave ? g_hi + 7 * unit : g_hi;
+        g_lo = whole ? g_hi + 7 * unit : g_hi;
     }
 }
 
@@ -308,12 +322,16 @@ hipError_t launch_fill_lds(uint32_t pattern, hipStream_t st) {
     return hipGetLastError();
 }
 
-// The interleaved dispatch order: the K and V rows of all levels (N + 7N/8 rows each) of eight
-// KV heads exceed the 256 MB last-level cache.
-bool order_interleaved(const Shape& s) {
+// XCD ranges per chunk of the dispatch order: the smallest f of 1, 2, 4, 8 for which the K
+// and V rows of all levels (N + 7N/8 rows each) of the 8 / f KV heads in flight fit in half the
+// 256 MB last-level cache; 1 with a single (batch, KV head).
+int order_share(const Shape& s) {
+    if (static_cast<int64_t>(s.B) * s.Hkv <= 1) return 1;
     const int64_t elem = s.dtype == PSA_F32 ? 4 : 2;
     const int64_t per_head = (static_cast<int64_t>(s.N) + s.pooled_rows) * s.D * elem * 2;
-    return static_cast<int64_t>(s.B) * s.Hkv > 1 && 8 * per_head > (int64_t{256} << 20);
+    int f = 1;
+    while (f < 8 && (8 / f) * per_head > (int64_t{128} << 20)) f *= 2;
+    return f;
 }
 
 hipError_t launch_build_index(const Shape& s, const int8_t* level_map, const IndexBufs& ib,
@@ -336,7 +354,7 @@ hipError_t launch_build_index(const Shape& s, const int8_t* level_map, const Ind
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t unit = static_cast<int64_t>(s.NQB) * (s.H / s.Hkv);   // rows per KV head
     hipLaunchKernelGGL(k_index_order, dim3(8), dim3(kOrderThreads), 0, st, ib.row_ptr, rows, (rows + 7) / 8,
-                       unit, order_interleaved(s) ? 1 : 0, ib.row_ptr + rows * 4 + 1);
+                       unit, order_share(s), ib.row_ptr + rows * 4 + 1);
     return hipGetLastError();
 }
 

@@ -32,9 +32,10 @@ hipError_t launch_pyramid(const Shape& s, const void* k, const void* v, void* kp
 hipError_t launch_build_index(const Shape& s, const int8_t* level_map, const IndexBufs& ib,
                               hipStream_t st);
 
-// Whether the block index lays its dispatch order interleaved over the XCDs: the K and V rows
-// of all levels of eight KV heads exceed the 256 MB last-level cache (and B * heads_kv > 1).
-bool order_interleaved(const Shape& s);
+// XCD ranges per chunk of the block index's dispatch order (1, 2, 4 or 8): the smallest for
+// which the K and V rows of all levels of the KV heads in flight fit in half the 256 MB
+// last-level cache.
+int order_share(const Shape& s);
 
 // pack = false selects the unpacked ablation layout (bf16 only; hipErrorNotSupported for f32)
 hipError_t launch_attn_fwd(const Shape& s, float scale, const void* q, const void* k,
