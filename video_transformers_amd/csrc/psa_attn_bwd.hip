@@ -65,7 +65,7 @@ struct BwdArgs {
     bf16_bits* dk;
     bf16_bits* dv;
     int* claim;    // [8] next unclaimed pooled tile of each XCD's range (k_bwd_dkv), zeroed per call
-    int interleave;   // k_bwd_dkv's XCD ranges interleaved (tiles x, x + 8, ...), as the index's order (f = 8)
+    int share;        // k_bwd_dkv's XCD ranges per chunk of tiles (1, 2, 4, 8), as the index's order
     int B, H, Hkv, N, Nv, NQB, NKB, BQ, causal;
     int64_t qs0, qs1, qs2, ks0, ks1, ks2, vs0, vs1, vs2, os0, os1, os2;
     int64_t pooled_rows;   // 7N/8
@@ -398,11 +398,12 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a, int total_tiles, 
     // Tile claim. Workgroup i runs on XCD x = i % 8; it takes the next unclaimed tile of XCD
     // x's range of tiles and, once that range is exhausted, the next tile of the first
     // following range that has one left, so an XCD whose tiles happen to be cheap takes over
-    // tiles of a busier one. Range x is the contiguous tiles [x nper, (x + 1) nper)
-    // (neighbouring tiles of a KV head share that XCD's L2), or, when the block index lays its
-    // dispatch order over all eight XCDs at once (one KV head's K and V at a time fill half the
-    // last-level cache), the tiles x, x + 8, x + 16, ... (the XCDs work through one KV head at
-    // a time). The grid has
+    // tiles of a busier one. The tiles are cut in chunks of f nper (f = the block index's XCD
+    // ranges per chunk: the KV heads in flight fit in half the last-level cache), and range x
+    // of its chunk is every f-th tile from the chunk's start + (x mod f): with f = 1 the
+    // contiguous tiles [x nper, (x + 1) nper) (neighbouring tiles of a KV head share that
+    // XCD's L2), with f = 8 the tiles x, x + 8, ... (the XCDs work through one KV head at a
+    // time). The grid has
     // one workgroup per tile: every claim succeeds and every tile is processed once. (The
     // tiles are independent, so the assignment does not change any result.)
     const int nper = (total_tiles + 7) >> 3;
@@ -411,18 +412,13 @@ __global__ void __launch_bounds__(512, 1) k_bwd_dkv(BwdArgs a, int total_tiles, 
         int t = -1;
         for (int d = 0; d < 8 && t < 0; ++d) {
             const int x = (static_cast<int>(blockIdx.x & 7) + d) & 7;
-            if (a.interleave) {
-                const int nx = (total_tiles - x + 7) >> 3;   // tiles x + 8 c < total_tiles
-                if (nx <= 0) continue;
-                const int c = atomicAdd(&a.claim[x], 1);
-                if (c < nx) t = x + 8 * c;
-            } else {
-                const int lo = x * nper;
-                const int hi = min(lo + nper, total_tiles);
-                if (lo >= hi) continue;
-                const int c = atomicAdd(&a.claim[x], 1);
-                if (lo + c < hi) t = lo + c;
-            }
+            const int f = a.share;
+            const int x0 = x - x % f;                                // the chunk's first range
+            const int lo = x0 * nper + (x - x0);                     // range x's first tile
+            const int end = min((x0 + f) * nper, total_tiles);       // the chunk's end
+            if (lo >= end) continue;
+            const int c = atomicAdd(&a.claim[x], 1);
+            if (lo + c * f < end) t = lo + c * f;
         }
         claimed = t;
     }
@@ -810,7 +806,7 @@ hipError_t launch_attn_bwd(const Shape& s, float scale, const void* q, const voi
     a.gk = f + 2 * rows;
     a.gv = a.gk + grows * s.D;
     a.claim = reinterpret_cast<int*>(a.gv + grows * s.D);
-    a.interleave = order_share(s) == 8 ? 1 : 0;
+    a.share = order_share(s);
     a.dq = static_cast<bf16_bits*>(dq);
     a.dk = static_cast<bf16_bits*>(dk);
     a.dv = static_cast<bf16_bits*>(dv);
