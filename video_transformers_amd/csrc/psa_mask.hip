@@ -1010,14 +1010,13 @@ __global__ void __launch_bounds__(kBatchThreads) k_cert_batches(BatchArgs b) {
             }
             __syncthreads();
         }
-    // batch heads: every BR-th position of each KV head's run (the run's start by binary search)
-    constexpr int PER = kBatchSortMax / kBatchThreads;
-    int head[PER];
+    // batch heads: every BR-th position of each KV head's run (the run's start by binary search);
+    // thread t takes the positions [t per, (t + 1) per), per = ceil(n / threads) <= 16
+    const int per = (n + kBatchThreads - 1) / kBatchThreads;
+    uint32_t heads = 0;   // bit e: position t per + e starts a batch
     int cnt = 0;
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-        const int p = tid * PER + e;
-        head[e] = 0;
+    for (int e = 0; e < per; ++e) {
+        const int p = tid * per + e;
         if (p < n) {
             const uint32_t key = static_cast<uint32_t>(skeys[p] >> 32);
             int lo = 0, hi = p;   // first position with this key
@@ -1025,15 +1024,16 @@ __global__ void __launch_bounds__(kBatchThreads) k_cert_batches(BatchArgs b) {
                 const int mid = (lo + hi) >> 1;
                 if (static_cast<uint32_t>(skeys[mid] >> 32) < key) lo = mid + 1; else hi = mid;
             }
-            head[e] = (p - lo) % b.BR == 0;
-            cnt += head[e];
+            if ((p - lo) % b.BR == 0) {
+                heads |= 1u << e;
+                ++cnt;
+            }
         }
     }
     int bidx = batch_exclusive_sum(cnt, wsum);
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-        const int p = tid * PER + e;
-        if (head[e]) {
+    for (int e = 0; e < per; ++e) {
+        if ((heads >> e) & 1u) {
+            const int p = tid * per + e;
             const uint32_t key = static_cast<uint32_t>(skeys[p] >> 32);
             for (int j = 0; j < 16; ++j) {
                 const int q = p + j;
