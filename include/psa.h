@@ -167,9 +167,10 @@ int psa_mask(const psa_problem* prob, const psa_mask_params* params, const void*
  * with a decision within a margin of a threshold, or with two sorted masses within the margin
  * (relative) of each other on either side of a level change, is rescored in float64 on the
  * device (logits as float64 dots of the bf16 inputs, float64 softmax and block masses; in
- * block-mean mode float64 means) and reassigned in float64 (margin: 4e-6 for sampling and
- * block-mean scores, 3e-5 for antidiagonal scores, about five times their float32 masses'
- * largest measured relative error); its block_mass row then holds those masses
+ * block-mean mode float64 means) and reassigned in float64 (margins, from the float32 masses'
+ * largest errors measured against float64 at full size: 4e-6 absolute and 8e-6 relative for
+ * sampling and block-mean scores, 5e-6 and 3.3e-5 for antidiagonal scores); its block_mass
+ * row then holds those masses
  * rounded to float. The similarity check compares the float64 similarity (block_sim holds it
  * rounded to float). At most a workspace-bounded number of rows per call (all rows of the
  * usual shapes; at least 16) are rescored; rows beyond it keep the float32 decisions.

@@ -444,12 +444,12 @@ FORCED = [
     # sampling, every query block of head 0 a copy of the first: all its rows flagged
     ("sampling-repeated", W.small(W.WAN13B_32K).replace(seq_valid=2048), True, 1.5e-6),
     # antidiagonal S = 8, 16 compressed rows per query block (the float64 MFMA rescoring)
-    ("antidiag-s8-repeated", _QW.replace(causal=False, force_diag_l0=False), True, 1e-5),
+    ("antidiag-s8-repeated", _QW.replace(causal=False, force_diag_l0=False), True, 2e-6),
     # antidiagonal S = 4 with 64-row query blocks (16 compressed rows again)
     ("antidiag-s4-repeated", _QW.replace(causal=False, force_diag_l0=False, block_q=64,
-                                         antidiag_stride=4), True, 1e-5),
+                                         antidiag_stride=4), True, 2e-6),
     # causal antidiagonal S = 8: each threshold next to a cumulative mass of another query block
-    ("antidiag-s8-causal", _QW, False, 1e-5),
+    ("antidiag-s8-causal", _QW, False, 2e-6),
 ]
 
 
