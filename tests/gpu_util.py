@@ -37,6 +37,9 @@ LSE_ABS_F32 = 1e-5
 # within ln(1 + 2^-9) = 1.95e-3 (reached when one key dominates a row); float32 accumulation of
 # the logits and exp2 add ~1e-6. Bar: 2e-3.
 LSE_ABS_BF16_POOLED = 2e-3
+# The library's certification margins per scoring mode (absolute, relative): a row whose
+# float32 threshold decisions lie within them is rescored in float64.
+CERT_MARGINS = {"sampling": (4e-6, 8e-6), "meankey": (4e-6, 8e-6), "antidiag": (5e-6, 3.3e-5)}
 
 
 def need_gpu():

@@ -22,8 +22,8 @@ import torch
 import oracle
 import workloads as W
 import video_transformers_amd as psa
-from gpu_util import (DEV, announce, assign_params, check_attention, check_map, dispatch_order,
-                      mask_params, need_gpu, oracle_margin_entries, order_share)
+from gpu_util import (CERT_MARGINS, DEV, announce, assign_params, check_attention, check_map,
+                      dispatch_order, mask_params, need_gpu, oracle_margin_entries, order_share)
 
 pytestmark = pytest.mark.gpu
 
@@ -136,6 +136,17 @@ def test_fullsize_sampled_parity(wl):
             dM = np.abs(Mg[qbs] - Mr[qbs]).max()
             print(f"[{wl.name}] head {h}: block mass max abs diff {dM:.3e}", flush=True)
             assert dM <= 2e-6
+            # the premise of the certification margins (absolute, relative): a row's running
+            # sums are off by at most its summed absolute mass error, which must stay below the
+            # absolute margin, and two masses can trade places only within the sum of their
+            # relative errors, each of which must stay below half the relative margin
+            m_abs, m_rel = CERT_MARGINS[wl.mask_mode]
+            row_abs = np.abs(Mg[qbs] - Mr[qbs]).sum(-1).max()
+            big = Mr[qbs] > 1e-9
+            rel = (np.abs(Mg[qbs] - Mr[qbs])[big] / Mr[qbs][big]).max()
+            print(f"[{wl.name}] head {h}: summed abs mass error per row <= {row_abs:.3e} "
+                  f"(margin {m_abs:g}), relative <= {rel:.3e} (half margin {m_rel / 2:g})", flush=True)
+            assert row_abs < m_abs and rel < m_rel / 2
             if simr is not None:
                 ds = np.abs(sim[0, hk].double().cpu().numpy() - simr).max()
                 print(f"[{wl.name}] kv head {hk}: similarity max abs diff {ds:.3e}", flush=True)
