@@ -15,12 +15,13 @@ arXiv 2512.04025, as described on the web pages):
 
 Where the pages leave a step open, the reading taken is stated in the function's docstring
 (and listed with the rest of the design notes). Pins that tie each function to something other
-than itself live in tests/test_oracle.py. Functions whose definition is this project's own
-reading with no closed form or special case on the pages to pin against say so:
-  mask_scores_sampling, mask_scores_antidiag, mask_scores_meankey, block_cossim,
-  assign_levels — pinned only by
-  reductions and hand-computed special cases of our own readings ("parity unpinned" against
-  the pages, which print no worked example for the mask generator).
+than itself live in tests/test_oracle.py. The pages print no worked example for the mask
+generator, so its functions (mask_scores_sampling, mask_scores_antidiag, mask_scores_meankey,
+block_cossim, assign_levels) are pinned by special cases that reduce them to a plain definition
+(every query row sampled gives the dense block mass; stride 1 gives the full logits; constant
+key blocks give the exact block-mean logit), by brute force (the similarity over all key
+pairs equals its closed form) and by hand-computed assignment cases, not by values printed on
+the pages.
 
 Notation: N padded length, Nv valid length, d head dim, BQ/BK query/KV block size,
 NQB = N/BQ, NKB = N/BK, level l in {0,1,2,3}, skip = -1, s = 1/sqrt(d).
