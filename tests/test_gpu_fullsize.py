@@ -1,4 +1,5 @@
-"""GPU parity at the workloads' full sizes, in the launch configuration the benchmark times.
+"""GPU parity at the workloads' full sizes, in the launch configuration the benchmark times, and at
+the largest sizes psa_mask accepts.
 
 The whole path runs on the full tensors exactly as the benchmark's step does
 (psa_build_pyramid, psa_mask or the drawn map, psa_build_index, psa_attn_fwd_indexed, on one
@@ -72,8 +73,17 @@ def _run_path(wl, qd, kd, vd):
     return kp, vp, lm, M, sim, o, lse, cert
 
 
-# the five workloads, plus block-mean scoring on the Wan-like 32k layer
-FULL = list(W.ALL) + [W.WAN13B_32K.replace(name="wan2.1-1.3b_32k-meankey", mask_mode="meankey")]
+# the five workloads, plus block-mean scoring on the Wan-like 32k layer, plus two layers at the
+# largest NKB whose per-row assignment fits its 64 KB of LDS (sampling with 8 samples: 1328
+# blocks; antidiagonal with stride 8 and 128-token query blocks: 830 blocks, which also runs
+# the general antidiagonal scorer: N / 8 is not a whole number of 128-column tiles)
+FULL = list(W.ALL) + [
+    W.WAN13B_32K.replace(name="wan2.1-1.3b_32k-meankey", mask_mode="meankey"),
+    W.WAN13B_32K.replace(name="wan-like-sampling-nkb1328", heads_q=2, heads_kv=2, seq_len=1328 * 64,
+                         seq_valid=1328 * 64 - 8, block_q=64),
+    W.QWEN25VL_32K.replace(name="qwen-like-antidiag-nkb830", heads_q=2, heads_kv=1, seq_len=830 * 64,
+                           seq_valid=830 * 64),
+]
 
 
 @pytest.mark.parametrize("wl", FULL, ids=[w.name for w in FULL])
