@@ -66,6 +66,7 @@ struct MkArgs {
     AssignArgs asg;      // RQ = 1, sampling counting, sim set when the cosine check is on
     double c;            // (1 / sqrt(d)) * log2(e), the scorer's logit scale
     double scale;        // 1 / sqrt(d), the certification's (natural-log) logit scale
+    int share;           // XCD ranges per chunk of the row order (1, 2, 4, 8)
 };
 
 struct Tile {
@@ -124,9 +125,24 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
     // XCD-aware row order: workgroup i runs on XCD i % 8; give each XCD a contiguous range of
     // rows, taken in the index's dispatch order (largest first) when it has one.
     const int nper = (total_rows + 7) >> 3;
-    const int slot = (blockIdx.x & 7) * nper + (blockIdx.x >> 3);
-    if (slot >= total_rows) return;
-    const int row = a.row_order != nullptr ? a.row_order[slot] : slot;
+    int row;
+    if constexpr (MK) {
+        // No block index (the map is made in the prologue), so no sort by tile count: rows in
+        // natural order (a KV head's query heads are consecutive), laid over the XCDs in chunks
+        // of f ranges as the index's dispatch order is: range x of its chunk takes every f-th
+        // row from the chunk's start + (x mod f), so the f XCDs of a chunk work through one KV
+        // head together. Each XCD's slots cover at most nper rows; every row is taken once.
+        const int x = blockIdx.x & 7;
+        const int f = mk.share;
+        const int x0 = x - x % f;
+        const int pos = x0 * nper + (x - x0) + static_cast<int>(blockIdx.x >> 3) * f;
+        if (pos >= min((x0 + f) * nper, total_rows)) return;
+        row = pos;
+    } else {
+        const int slot = (blockIdx.x & 7) * nper + (blockIdx.x >> 3);
+        if (slot >= total_rows) return;
+        row = a.row_order != nullptr ? a.row_order[slot] : slot;
+    }
     const int qb = row % a.NQB;
     const int bh = row / a.NQB;
     const int h = bh % a.H;
@@ -1134,6 +1150,7 @@ hipError_t launch_attn_fwd_meankey(const Shape& s, float scale, const psa_mask_p
     mk.asg.S = 1;
     mk.c = (1.0 / std::sqrt(static_cast<double>(s.D))) * 1.4426950408889634;
     mk.scale = 1.0 / std::sqrt(static_cast<double>(s.D));
+    mk.share = order_share(s);
     if (s.D == 128) return launch_one<128, 128, true, 0, true>(s, a, st, mk);
     if (s.D == 64) return launch_one<64, 128, true, 0, true>(s, a, st, mk);
     return hipErrorNotSupported;
