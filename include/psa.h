@@ -339,7 +339,8 @@ size_t psa_attn_fwd_meankey_workspace_bytes(const psa_problem* prob);
  * attends over the resulting list. level_map and block_mass (layouts as in psa_mask) receive
  * the map and the masses when not null. The cosine check runs when cos_sim_min > 0.
  * dtype PSA_BF16, block_q 128 and seq_len/64 <= 1792 only (PSA_ERR_UNSUPPORTED otherwise).
- * Workspace: psa_attn_fwd_meankey_workspace_bytes (the block means and similarities).
+ * Workspace: psa_attn_fwd_meankey_workspace_bytes (the block means, the float64 key sums of each
+ * KV block and the similarities).
  */
 int psa_attn_fwd_meankey(const psa_problem* prob, const psa_mask_params* params,
                          float softmax_scale, const void* q, const void* k, const void* v,

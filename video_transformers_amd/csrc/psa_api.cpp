@@ -415,6 +415,7 @@ namespace {
 struct MeanKeyWs {
     float* qbar;
     float* kbar;
+    double* ksum;
     float* sim;
     double* sim64;
     size_t bytes;
@@ -427,6 +428,8 @@ MeanKeyWs meankey_ws_layout(const psa::Shape& s, void* base) {
     off += align_up(static_cast<size_t>(s.B) * s.H * s.NQB * s.D * sizeof(float));
     w.kbar = ws_at<float>(base, off);
     off += align_up(static_cast<size_t>(s.B) * s.Hkv * s.NKB * s.D * sizeof(float));
+    w.ksum = ws_at<double>(base, off);
+    off += align_up(static_cast<size_t>(s.B) * s.Hkv * s.NKB * s.D * sizeof(double));
     w.sim = ws_at<float>(base, off);
     off += align_up(static_cast<size_t>(s.B) * s.Hkv * s.NKB * sizeof(float));
     w.sim64 = ws_at<double>(base, off);
@@ -466,12 +469,12 @@ int psa_attn_fwd_meankey(const psa_problem* prob, const psa_mask_params* params,
     const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt(float(s.D));
     hipStream_t st = static_cast<hipStream_t>(stream);
     MeanKeyWs w = meankey_ws_layout(s, ws);
-    hipError_t e = psa::launch_block_means(s, q, k, w.qbar, w.kbar, st);
+    hipError_t e = psa::launch_block_means(s, q, k, w.qbar, w.kbar, w.ksum, st);
     if (e != hipSuccess) return hip_status(e);
     if (params->cos_sim_min > 0.f && (e = psa::launch_block_sim(s, k, w.sim, w.sim64, st)) != hipSuccess)
         return hip_status(e);
     return hip_status(psa::launch_attn_fwd_meankey(s, scale, *params, q, k, v, k_pooled, v_pooled,
-                                                   w.qbar, w.kbar, w.sim, w.sim64, level_map,
+                                                   w.qbar, w.kbar, w.ksum, w.sim, w.sim64, level_map,
                                                    block_mass, o, lse, st));
 }
 

@@ -386,19 +386,16 @@ __device__ inline void cert_qbar_f64(const bf16_bits* qh, int64_t qs2, int qb, i
 }
 
 // Block-mean log-mass of KV block kb in float64: scale * q_bar . (sum_t k_t) / n + ln n over
-// the block's n valid keys (each key's dot with q_bar in d order, keys summed in order); -inf
-// for a non-candidate, a block with no valid key or a query block with no valid row.
-__device__ inline double cert_meankey_logmass(const bf16_bits* kh, int64_t ks2, const double* qbar,
-                                              int D, int kb, int Nv, bool usable, double scale) {
+// the block's n valid keys, from the block's float64 key sums ksum[e] = sum_t k_t[e] (one row
+// of D, written by the block-means kernel; the dot in d order); -inf for a non-candidate, a
+// block with no valid key or a query block with no valid row.
+__device__ inline double cert_meankey_logmass(const double* ksum, const double* qbar, int D, int kb,
+                                              int Nv, bool usable, double scale) {
     const int nv = min(max(Nv - kb * 64, 0), 64);
     if (!usable || nv == 0) return -INFINITY;
+    const double* kr = ksum + static_cast<int64_t>(kb) * D;
     double dot = 0.0;
-    for (int t = 0; t < nv; ++t) {
-        const bf16_bits* kr = kh + static_cast<int64_t>(kb * 64 + t) * ks2;
-        double d1 = 0.0;
-        for (int e = 0; e < D; ++e) d1 = fma(qbar[e], static_cast<double>(bf16_to_f32(kr[e])), d1);
-        dot += d1;
-    }
+    for (int e = 0; e < D; ++e) dot = fma(qbar[e], kr[e], dot);
     return scale * dot / nv + log(static_cast<double>(nv));
 }
 

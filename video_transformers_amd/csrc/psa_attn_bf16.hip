@@ -61,6 +61,7 @@ constexpr float kLazyRescale = 8.0f;  // log2-domain headroom before the accumul
 struct MkArgs {
     const float* qbar;   // [B*H][NQB][D]
     const float* kbar;   // [B*Hkv][NKB][D]
+    const double* ksum;  // [B*Hkv][NKB][D] float64 key sums (the certification)
     float* mass_out;     // [B*H*NQB][NKB] or null
     int8_t* map_out;     // [B*H*NQB][NKB] or null
     AssignArgs asg;      // RQ = 1, sampling counting, sim set when the cosine check is on
@@ -206,9 +207,9 @@ __global__ void __launch_bounds__(2 * BQ, 2) k_attn_fwd_bf16(AttnArgs a, int tot
             double* Ld = reinterpret_cast<double*>(keys);
             cert_qbar_f64(Q + b * a.qs0 + h * a.qs1, a.qs2, qb, BQ, a.Nv, D, qbar64, tid);
             __syncthreads();
-            const bf16_bits* kh = K + b * a.ks0 + hk * a.ks1;
+            const double* ks = mk.ksum + static_cast<int64_t>(b * a.Hkv + hk) * NKB * D;
             for (int kb = tid; kb < NKB; kb += 256)
-                Ld[kb] = cert_meankey_logmass(kh, a.ks2, qbar64, D, kb, a.Nv, qlo < a.Nv && kb <= lastk, mk.scale);
+                Ld[kb] = cert_meankey_logmass(ks, qbar64, D, kb, a.Nv, qlo < a.Nv && kb <= lastk, mk.scale);
             __syncthreads();
             __shared__ double clse[32], cwm[4][32], cws[4][32];
             cert_lse(Ld, 1, NKB, clse, cwm, cws, tid);
@@ -1121,8 +1122,9 @@ hipError_t launch_attn_fp8qk(const Shape& s, const AttnArgs& a, hipStream_t st) 
 hipError_t launch_attn_fwd_meankey(const Shape& s, float scale, const psa_mask_params& mp,
                                    const void* q, const void* k, const void* v, const void* kp,
                                    const void* vp, const float* qbar, const float* kbar,
-                                   const float* sim, const double* sim64, int8_t* map_out,
-                                   float* mass_out, void* o, float* lse, hipStream_t st) {
+                                   const double* ksum, const float* sim, const double* sim64,
+                                   int8_t* map_out, float* mass_out, void* o, float* lse,
+                                   hipStream_t st) {
     if (s.dtype != PSA_BF16 || s.BQ != 128 || s.BK != 64 || s.NKB > 1792) return hipErrorNotSupported;
     if (s.B * s.H * s.NQB == 0) return hipSuccess;
     AttnArgs a{};
@@ -1139,6 +1141,7 @@ hipError_t launch_attn_fwd_meankey(const Shape& s, float scale, const psa_mask_p
     MkArgs mk;
     mk.qbar = qbar;
     mk.kbar = kbar;
+    mk.ksum = ksum;
     mk.mass_out = mass_out;
     mk.map_out = map_out;
     mk.asg = assign_args_of(s, mp);

@@ -108,19 +108,20 @@ hipError_t launch_mask_certify(const Shape& s, const psa_mask_params& mp, const 
                                const void* k, const MaskBufs& mb, int8_t* level_map, hipStream_t st);
 
 // Mean of each query block's valid rows (qbar [B*H][NQB][D]) and of each KV block's valid keys
-// (kbar [B*Hkv][NKB][D]), float32.
+// (kbar [B*Hkv][NKB][D]), float32; and the float64 sum of each KV block's valid keys (ksum
+// [B*Hkv][NKB][D]), which the certification of block-mean scores reads.
 hipError_t launch_block_means(const Shape& s, const void* q, const void* k, float* qbar, float* kbar,
-                              hipStream_t st);
+                              double* ksum, hipStream_t st);
 
 // Block-mean scoring, threshold assignment and the attention in one kernel (bf16, block_q 128,
 // NKB <= 1792): each workgroup scores its query block's mean against every KV block mean,
 // assigns the levels (the same steps as the mask's assignment) and attends over the resulting
-// list. qbar / kbar from launch_block_means; sim (or null) from launch_block_sim; map_out and
-// mass_out (or null) receive the level map and block masses.
+// list. qbar / kbar / ksum from launch_block_means; sim (or null) from launch_block_sim; map_out
+// and mass_out (or null) receive the level map and block masses.
 hipError_t launch_attn_fwd_meankey(const Shape& s, float scale, const psa_mask_params& mp,
                                    const void* q, const void* k, const void* v, const void* kp,
                                    const void* vp, const float* qbar, const float* kbar,
-                                   const float* sim, const double* sim64, int8_t* map_out,
+                                   const double* ksum, const float* sim, const double* sim64, int8_t* map_out,
                                    float* mass_out, void* o, float* lse, hipStream_t st);
 
 hipError_t launch_mask_assign(const Shape& s, const psa_mask_params& mp, const float* block_mass,

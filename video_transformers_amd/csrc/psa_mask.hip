@@ -615,6 +615,7 @@ struct MeanArgs {
     const bf16_bits* k;
     float* qbar;   // [B*H][NQB][D]
     float* kbar;   // [B*Hkv][NKB][D]
+    double* ksum;  // [B*Hkv][NKB][D] float64 sums of each KV block's valid keys (certification)
     int B, H, Hkv, N, Nv, D, BQ, BK, NQB, NKB;
     int64_t qs0, qs1, qs2, ks0, ks1, ks2;
 };
@@ -622,6 +623,7 @@ struct MeanArgs {
 __global__ void __launch_bounds__(256) k_block_means(MeanArgs a) {
     // 16-byte loads: thread t reads 8 columns (t % (D/8)) of rows t / (D/8), t / (D/8) + 256/(D/8), ..
     __shared__ float part[256 * 8];
+    __shared__ double part64[256 * 8];
     const int64_t nq = static_cast<int64_t>(a.B) * a.H * a.NQB;
     const int64_t item = blockIdx.x;
     const bool is_q = item < nq;
@@ -650,16 +652,27 @@ __global__ void __launch_bounds__(256) k_block_means(MeanArgs a) {
     const int ch = threadIdx.x % cpr;
     const int ph = threadIdx.x / cpr;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    // KV blocks: the certification's float64 key sums beside the float32 means (64 bf16 values
+    // sum exactly in float64 unless their exponents span more than about 45 bits)
+    double acc64[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
     for (int r = ph; r < rows; r += phases) {
         const u32x4 w = *reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(r) * rs + ch * 8);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             acc[2 * i] += __uint_as_float(w[i] << 16);
             acc[2 * i + 1] += __uint_as_float(w[i] & 0xffff0000u);
+            if (!is_q) {
+                acc64[2 * i] += static_cast<double>(__uint_as_float(w[i] << 16));
+                acc64[2 * i + 1] += static_cast<double>(__uint_as_float(w[i] & 0xffff0000u));
+            }
         }
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) part[threadIdx.x * 8 + i] = acc[i];
+    if (!is_q) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part64[threadIdx.x * 8 + i] = acc64[i];
+    }
     __syncthreads();
     if (threadIdx.x < a.D) {
         const int e = threadIdx.x;
@@ -668,6 +681,11 @@ __global__ void __launch_bounds__(256) k_block_means(MeanArgs a) {
         const float mean = rows > 0 ? sum / static_cast<float>(rows) : 0.f;
         float* dst = is_q ? a.qbar + item * a.D : a.kbar + (item - nq) * a.D;
         dst[e] = mean;
+        if (!is_q) {
+            double s64 = 0.0;
+            for (int p = 0; p < phases; ++p) s64 += part64[(p * cpr + e / 8) * 8 + e % 8];
+            a.ksum[(item - nq) * a.D + e] = s64;
+        }
     }
 }
 
@@ -852,6 +870,7 @@ struct CertArgs {
     const int* cert;
     const int* rows;
     double* Lg;   // [cap][RQ][NKB]
+    const double* ksum;   // block-mean mode: float64 key sums per KV block [B*Hkv][NKB][D]
     int cap;
     int nchunks;  // column chunks per row
 };
@@ -1406,10 +1425,10 @@ __global__ void __launch_bounds__(256) k_cert_meankey(CertArgs a) {
         __syncthreads();
         const bool anyq = r.qb * a.BQ < a.Nv;
         const int last = a.causal ? min((r.qb * a.BQ + a.BQ - 1) / 64, a.NKB - 1) : a.NKB - 1;
-        const bf16_bits* kh = a.k + r.b * a.ks0 + r.hk * a.ks1;
+        const double* ks = a.ksum + static_cast<int64_t>(r.b * a.Hkv + r.hk) * a.NKB * D;
         for (int kb = tid; kb < a.NKB; kb += 256)
             a.Lg[static_cast<int64_t>(slot) * a.NKB + kb] =
-                cert_meankey_logmass(kh, a.ks2, qbar, D, kb, a.Nv, anyq && kb <= last, a.scale);
+                cert_meankey_logmass(ks, qbar, D, kb, a.Nv, anyq && kb <= last, a.scale);
     }
 }
 
@@ -1480,7 +1499,7 @@ hipError_t launch_antidiag(const ScoreArgs& a, int D, int blocks, hipStream_t st
 struct ScoreGeom {
     int S, rows_per_head, RQ, rows_per_wg, wg_per_head, ntiles, nsplit, tiles_per_split;
     size_t ws_bytes;
-    size_t qbar_off = 0, kbar_off = 0;   // block-mean mode: offsets of the means in the workspace
+    size_t qbar_off = 0, kbar_off = 0, ksum_off = 0;   // block-mean mode: means, float64 key sums
     // certification: counters, flagged row list, batches (16 slots each), float64
     // similarities, float64 log-masses
     size_t cert_off = 0, rows_off = 0, bat_off = 0, sim64_off = 0, lg_off = 0;
@@ -1535,6 +1554,9 @@ ScoreGeom score_geom_base(const Shape& s, const psa_mask_params& mp) {
         g.ws_bytes = (g.ws_bytes + 255) & ~static_cast<size_t>(255);
         g.kbar_off = g.ws_bytes;
         g.ws_bytes += static_cast<size_t>(s.B) * s.Hkv * s.NKB * s.D * sizeof(float);
+        g.ws_bytes = (g.ws_bytes + 255) & ~static_cast<size_t>(255);
+        g.ksum_off = g.ws_bytes;
+        g.ws_bytes += static_cast<size_t>(s.B) * s.Hkv * s.NKB * s.D * sizeof(double);
         return g;
     }
     const bool sampling = mp.mode == PSA_MASK_SAMPLING;
@@ -1609,8 +1631,9 @@ hipError_t launch_mask_scores(const Shape& s, const psa_mask_params& mp, const v
         char* ws = static_cast<char*>(mb.ws);
         float* qbar = reinterpret_cast<float*>(ws + g.qbar_off);
         float* kbar = reinterpret_cast<float*>(ws + g.kbar_off);
+        double* ksum = reinterpret_cast<double*>(ws + g.ksum_off);
         if (static_cast<int64_t>(s.B) * (s.H * s.NQB + s.Hkv * s.NKB) == 0) return hipSuccess;
-        hipError_t e = launch_block_means(s, q, k, qbar, kbar, st);
+        hipError_t e = launch_block_means(s, q, k, qbar, kbar, ksum, st);
         if (e != hipSuccess) return e;
         MeanKeyArgs k;
         k.qbar = qbar;
@@ -1686,12 +1709,13 @@ hipError_t launch_mask_assign_logmass(const Shape& s, const psa_mask_params& mp,
 }
 
 hipError_t launch_block_means(const Shape& s, const void* q, const void* k, float* qbar, float* kbar,
-                              hipStream_t st) {
+                              double* ksum, hipStream_t st) {
     MeanArgs m;
     m.q = static_cast<const bf16_bits*>(q);
     m.k = static_cast<const bf16_bits*>(k);
     m.qbar = qbar;
     m.kbar = kbar;
+    m.ksum = ksum;
     m.B = s.B; m.H = s.H; m.Hkv = s.Hkv; m.N = s.N; m.Nv = s.Nv; m.D = s.D;
     m.BQ = s.BQ; m.BK = s.BK; m.NQB = s.NQB; m.NKB = s.NKB;
     m.qs0 = s.qs[0]; m.qs1 = s.qs[1]; m.qs2 = s.qs[2];
@@ -1745,6 +1769,7 @@ hipError_t launch_mask_certify(const Shape& s, const psa_mask_params& mp, const 
     c.cert = reinterpret_cast<const int*>(ws + g.cert_off);
     c.rows = reinterpret_cast<const int*>(ws + g.rows_off);
     c.Lg = reinterpret_cast<double*>(ws + g.lg_off);
+    c.ksum = mp.mode == PSA_MASK_MEANKEY ? reinterpret_cast<const double*>(ws + g.ksum_off) : nullptr;
     c.cap = g.cap;
     if (c.cap == 0) return hipSuccess;
     // fixed grids walking the device-side count of flagged rows
