@@ -450,6 +450,9 @@ FORCED = [
                                          antidiag_stride=4), True, 2e-6),
     # causal antidiagonal S = 8: each threshold next to a cumulative mass of another query block
     ("antidiag-s8-causal", _QW, False, 2e-6),
+    # block-mean scoring (float64 key sums per KV block), also through the fused attention
+    ("meankey-repeated", W.small(W.WAN13B_32K).replace(seq_valid=2048, mask_mode="meankey"), True,
+     1.5e-6),
 ]
 
 
@@ -490,3 +493,10 @@ def test_certification_forced(case):
           flush=True)
     assert cert[1] == 0 and cert[0] >= need
     check_map(lm.cpu().numpy(), lm_ref, oracle_margin_entries(M_ref, sim_ref, p, a), name, cert)
+    if wl.mask_mode == "meankey":
+        # the fused call certifies the same rows in its prologue: the same map and masses
+        kp, vp = psa.build_pyramid(kd, vd, prob)
+        _, _, lmf, Mf = psa.attn_fwd_meankey(qd, kd, vd, kp, vp, prob, mask_params(wl_t),
+                                             want_mass=True)
+        torch.cuda.synchronize()
+        assert torch.equal(lmf, lm) and torch.equal(Mf, M), "fused call differs from psa_mask"
