@@ -525,6 +525,13 @@ def _sustained_attention(fn, stream, flops: float, seconds: float = 3.0) -> dict
            "calls_timed": 20 * len(times),
            "note": "back-to-back calls for about 3 s; the median batch of the last third"}
     out.update(smi)
+    clk = smi.get("gfx_clock_mhz")
+    if clk:
+        # the bf16 MFMA peak scales with the graphics clock (2.5 PFLOP/s at 2.4 GHz); under this
+        # sustained load the power limit holds the clock below that
+        peak_at_clock = PEAK_BF16_TFLOPS * clk["mean"] / 2400.0
+        out["bf16_peak_at_mean_clock"] = round(peak_at_clock, 1)
+        out["pct_of_peak_at_mean_clock"] = round(100 * flops / (ms * 1e-3) / 1e12 / peak_at_clock, 2)
     return out
 
 
