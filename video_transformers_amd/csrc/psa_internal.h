@@ -121,8 +121,9 @@ hipError_t launch_block_means(const Shape& s, const void* q, const void* k, floa
 hipError_t launch_attn_fwd_meankey(const Shape& s, float scale, const psa_mask_params& mp,
                                    const void* q, const void* k, const void* v, const void* kp,
                                    const void* vp, const float* qbar, const float* kbar,
-                                   const double* ksum, const float* sim, const double* sim64, int8_t* map_out,
-                                   float* mass_out, void* o, float* lse, hipStream_t st);
+                                   const double* ksum, const float* sim, const double* sim64,
+                                   int8_t* map_out, float* mass_out, void* o, float* lse,
+                                   hipStream_t st);
 
 hipError_t launch_mask_assign(const Shape& s, const psa_mask_params& mp, const float* block_mass,
                               const float* block_sim, int8_t* level_map, hipStream_t st);
